@@ -1,0 +1,224 @@
+/*
+ * moe.h -- C ABI of the token-choice mixture-of-experts forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (page titles and sections of the sources it follows):
+ *   "Lab 18 -- Mixture of experts" s.1 (layer equation, gate values),
+ *   s.2 (load balancing, router z-loss), s.3 (capacity and dropped tokens),
+ *   "What to implement"; "Lab 01 -- Router, Load Balancing, Capacity & the
+ *   MoE Layer" ("Where to start", "The traps"); "Mixture of Experts --
+ *   parameters without the FLOPs" s.2 (the router) and s.3 (capacity);
+ *   "Mixture of experts" lecture field map (fp32 router, DeepSeek-V3 sigmoid
+ *   affinities and selection bias).
+ *
+ *   z   = x W_r + logit_bias                      float32, [T,E]
+ *   key = z (+ select_bias)          (softmax scores)
+ *       = fp32 sigmoid(z) + select_bias  (sigmoid scores)
+ *   idx = the k largest keys per token, best first, equal keys to the lower
+ *         expert index (-0 equals +0)
+ *   g   = softmax over the selected logits (renormalised), or the full
+ *         softmax probability (raw, the k = 1 default), or the selected
+ *         sigmoid scores normalised over the k (sigmoid)
+ *   C   = ceil(cf * T * k / E), or capacity_override when > 0
+ *   slot= queue position of (token, choice) in its expert, in priority order
+ *         (rank-major: every first choice, then every second choice, token
+ *         order inside a rank; or token-major); dropped iff slot >= C
+ *   y_t = sum over kept choices of g * FFN_e(x_t)  (+ shared experts);
+ *         a token with no kept choice and no shared expert gets y_t = x_t
+ *         (or 0 when dropped_output = 1)
+ *   L_aux = E * sum_i f_i P_i, f_i = (choices routed to i) / (T k),
+ *         P_i = mean full router probability of i;   L_z = mean_t LSE_t^2.
+ *         Both are returned without their alpha coefficients.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked [host]. Tensors are dense,
+ *     row-major, and at least 16-byte aligned.
+ *   - Storage type of x, expert weights, expert biases and y: MOE_F32 or
+ *     MOE_BF16 (raw bf16 bits). The router weight, biases of the router,
+ *     logits, probabilities, gates and losses are always float32.
+ *   - Expert weights follow the [out_features, in_features] layout:
+ *     w_in/w_gate/w_up [E, F, d], w_out [E, d, F], b_in [E, F], b_out [E, d].
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it; nothing blocks the host, nothing is copied to
+ *     the host, and no device memory is allocated or freed. Results are valid
+ *     once the stream has been synchronised.
+ *   - The caller owns every buffer, including the workspace `ws` of
+ *     moe_workspace_bytes() bytes (256-byte aligned).
+ *   - Errors: inputs are validated on the host before anything is launched.
+ *     MOE_EINVAL for a bad configuration or argument (capacity_factor < 1,
+ *     k < 1, k > E, k > 32, E > 256, T*k >= 2^31, d or F not a multiple of 8,
+ *     a required pointer NULL or misaligned); MOE_EUNSUPPORTED for a
+ *     combination that is not built; MOE_EHIP when a launch fails.
+ *     moe_last_error() returns a message for the calling thread's last
+ *     non-OK status.
+ *   - Same inputs on the same GPU give bit-identical outputs (no result
+ *     depends on the order of atomic operations).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_OK = 0, MOE_EINVAL = 1, MOE_EUNSUPPORTED = 2, MOE_EHIP = 3 } moe_status;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
+typedef enum { MOE_GELU = 0, MOE_SWIGLU = 1 } moe_act;
+typedef enum { MOE_RANK_MAJOR = 0, MOE_TOKEN_MAJOR = 1 } moe_priority;
+
+typedef struct moe_config {
+  int64_t T;                  /* tokens (B*S flattened by the caller)                 */
+  int32_t d;                  /* model width                                           */
+  int32_t E;                  /* routed experts, 1..256                                */
+  int32_t k;                  /* experts per token, 1..min(E,32)                       */
+  int32_t d_ff;               /* routed expert hidden width F                          */
+  int32_t n_shared;           /* shared experts (GELU MLPs), 0 = none                  */
+  int32_t d_ff_shared;        /* hidden width of ONE shared expert                     */
+  double capacity_factor;     /* >= 1.0, else MOE_EINVAL                               */
+  int64_t capacity_override;  /* > 0: use as the capacity C; 0: ceil(cf*T*k/E)         */
+  int32_t renormalize;        /* -1: renormalise iff k > 1; 0: raw gates; 1: renorm.   */
+  int32_t score;              /* moe_score                                             */
+  int32_t act;                /* moe_act of the routed experts                         */
+  int32_t dtype;              /* moe_dtype of x, expert weights/biases, y              */
+  int32_t priority;           /* moe_priority of the capacity queue                    */
+  int32_t dropped_output;     /* 0: fully dropped token -> y = x; 1: y = 0             */
+} moe_config;
+
+/* Check a configuration; on MOE_OK store the capacity C in *capacity [host]
+ * (may be NULL). Runs on the host only. ["Lab 18" s.3; "Lab 01" traps] */
+MOE_API moe_status moe_validate(const moe_config* cfg, int64_t* capacity);
+
+/* Bytes of workspace moe_forward needs for cfg (0 if cfg is invalid).
+ * moe_route, moe_dispatch and moe_aux_losses need at most this much. */
+MOE_API size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Router: logits, probabilities, top-k and gates ["Lab 18" s.1 and "What to
+ * implement" 1; "Parameters without the FLOPs" s.2].
+ *   x           [T,d] storage type; NULL => `logits` is an INPUT [T,E]
+ *   w_router    [d,E] float32 (ignored when x is NULL)
+ *   logit_bias  [E] float32 added to the logits, or NULL
+ *   select_bias [E] float32 added to the selection key only, or NULL
+ *   logits      [T,E] float32: output when x != NULL (may then be NULL)
+ *   probs       [T,E] float32 full softmax (or sigmoid scores normalised over
+ *               all E), or NULL
+ *   idx         [T,k] int32 selected experts, best first          (required)
+ *   gates       [T,k] float32 gate of each selected expert        (required)
+ *   lse         [T] float32 log-sum-exp of the logits, or NULL
+ *   ws          workspace (may be NULL: then no loss partials are kept) */
+MOE_API moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router,
+                     const float* logit_bias, const float* select_bias, float* logits,
+                     float* probs, int32_t* idx, float* gates, float* lse, void* ws,
+                     void* stream);
+
+/* Capacity and dispatch ["Lab 18" s.3 GShard priority and Tips; "Lab 01"
+ * "Where to start" 4; "Parameters without the FLOPs" s.3 static shapes].
+ *   x          [T,d] storage type, or NULL (slots only)
+ *   idx        [T,k] int32 expert ids (each row distinct, 0..E-1)
+ *   slot       [T,k] int32 queue position of each choice
+ *   dropped    [T,k] uint8 1 iff slot >= C
+ *   counts     [E] int32 choices routed to each expert (before capacity)
+ *   row_token  [E,C] int32 token held by each kept slot (rows >= kept_e of
+ *              expert e are left untouched), or NULL
+ *   xe         [E,C,d] storage type: xe[e,slot] = x[t] for every kept choice
+ *              (rows >= kept_e untouched), or NULL
+ *   ws         workspace (required) */
+MOE_API moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx, int32_t* slot,
+                        uint8_t* dropped, int32_t* counts, int32_t* row_token, void* xe,
+                        void* ws, void* stream);
+
+/* Grouped expert FFN on bf16 MFMA (float32 FMA for MOE_F32)
+ * ["Lab 18" s.1 experts, Tips (one grouped matrix multiply over all
+ * experts); "Mixture of experts" lecture, expert geometry].
+ *   groups          number of experts in this call
+ *   rows_per_group  row stride between groups in a, h and out (C for the
+ *                   dispatched buffer; T for shared experts with groups = 1)
+ *   rows            [groups] int32 rows to compute in each group (e.g. the
+ *                   counts of moe_dispatch, clamped to rows_per_group), or
+ *                   NULL for all rows_per_group rows
+ *   a               [groups*rows_per_group, d] storage type
+ *   act             moe_act: GELU  h = GELU(a w_in^T + b_in), out = h w_out^T + b_out
+ *                            SwiGLU h = SiLU(a w_gate^T) * (a w_up^T), out = h w_out^T
+ *   w_in            [groups,F,d] (GELU: w_in; SwiGLU: w_up)
+ *   w_gate          [groups,F,d] SwiGLU gate projection, NULL for GELU
+ *   b_in            [groups,F] or NULL;   w_out [groups,d,F];  b_out [groups,d] or NULL
+ *   h               [groups*rows_per_group, F] hidden activations (storage type)
+ *   out             [groups*rows_per_group, d] expert outputs (storage type)
+ * Rows at or beyond rows[g] are neither read nor written. */
+MOE_API moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups,
+                          int64_t rows_per_group, const int32_t* rows, const void* a,
+                          const void* w_in, const void* w_gate, const void* b_in,
+                          const void* w_out, const void* b_out, int32_t F, void* h, void* out,
+                          void* stream);
+
+/* Gate-weighted combine with residual fallback ["Lab 18" s.1 layer equation
+ * and s.3; "Lab 01" "Where to start" 5; "Phase 02" concept map].
+ *   y_t = sum_{j not dropped} gates[t,j] * ye[idx[t,j], slot[t,j]] + shared_out[t]
+ *   accumulated in float32 in j order, rounded once to the storage type.
+ *   With shared_out NULL, a token with every choice dropped gets x_t (or 0).
+ *   x [T,d]; ye [E,C,d]; shared_out [T,d] or NULL; y [T,d] (storage type). */
+MOE_API moe_status moe_combine(const moe_config* cfg, const void* x, const void* ye,
+                       const void* shared_out, const int32_t* idx, const float* gates,
+                       const int32_t* slot, const uint8_t* dropped, void* y, void* stream);
+
+/* Auxiliary losses from given logits and choices ["Lab 18" s.2 and "What to
+ * implement" 2-3; "Lab 01" traps]: losses[0] = E * sum_i f_i P_i,
+ * losses[1] = mean_t logsumexp(z_t)^2 (no alpha applied).
+ *   logits [T,E] float32; idx [T,k] int32; losses [2] float32; ws required. */
+MOE_API moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int32_t* idx,
+                          float* losses, void* ws, void* stream);
+
+typedef struct moe_weights {
+  const float* w_router;      /* [d,E] float32                                      */
+  const float* logit_bias;    /* [E] float32 or NULL                                */
+  const float* select_bias;   /* [E] float32 or NULL                                */
+  const void* w_in;           /* GELU: [E,F,d]; SwiGLU: w_up [E,F,d]                */
+  const void* w_gate;         /* SwiGLU gate [E,F,d]; NULL for GELU                 */
+  const void* b_in;           /* [E,F] or NULL                                      */
+  const void* w_out;          /* [E,d,F]                                            */
+  const void* b_out;          /* [E,d] or NULL                                      */
+  const void* ws_in;          /* shared experts concatenated: [n_shared*Fs, d]      */
+  const void* bs_in;          /* [n_shared*Fs] or NULL                              */
+  const void* ws_out;         /* [d, n_shared*Fs]                                   */
+  const void* bs_out;         /* [d] (sum of the shared experts' output biases) or NULL */
+} moe_weights;
+
+typedef struct moe_outputs {
+  void* y;                    /* [T,d] storage type                        (required) */
+  int32_t* idx;               /* [T,k]                                     (required) */
+  float* gates;               /* [T,k]                                     (required) */
+  int32_t* slot;              /* [T,k]                                     (required) */
+  uint8_t* dropped;           /* [T,k]                                     (required) */
+  int32_t* counts;            /* [E]                                       (required) */
+  float* losses;              /* [2] {L_aux, L_z}                          (required) */
+  int32_t* stats;             /* [4] {kept, dropped, fallback tokens, pad slots} or NULL */
+  float* logits;              /* [T,E] or NULL                                        */
+  float* probs;               /* [T,E] or NULL                                        */
+  float* lse;                 /* [T] or NULL                                          */
+} moe_outputs;
+
+/* The whole layer: route -> capacity -> dispatch -> routed (and shared)
+ * expert FFNs -> combine, with the losses beside, all on `stream`
+ * ["Lab 18" "What to implement" 5: MoE.forward(x) -> (y, aux)].
+ * Shared experts: pass them concatenated along their hidden dimension
+ * (GELU is elementwise, so the sum of the shared experts equals one MLP
+ * whose hidden layer is the concatenation of theirs). */
+MOE_API moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
+                       moe_outputs* out, void* ws, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+MOE_API const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,493 @@
+// Host side of the C ABI: validation, capacity arithmetic, workspace layout
+// and the launch sequence of the layer on the caller's stream.  Nothing here
+// allocates device memory, synchronises or copies to the host.
+//
+// Sources: "Lab 18 -- Mixture of experts" s.3 (C = ceil(cf*T*k/E)) and "What
+// to implement" (route, load_balancing_loss, router_z_loss, capacity_mask,
+// MoE.forward); "Lab 01" "The traps" (capacity_factor < 1 must raise).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+thread_local std::string g_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int64_t capacity_of(const moe_config& c) {
+  if (c.capacity_override > 0) return c.capacity_override;
+  // evaluated in IEEE double in this order, then rounded up
+  return static_cast<int64_t>(ceil(c.capacity_factor * static_cast<double>(c.T) *
+                                   static_cast<double>(c.k) / static_cast<double>(c.E)));
+}
+
+size_t dsize(const moe_config& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status check_ptr(const void* p, const char* name, size_t align, bool required = true) {
+  if (p == nullptr) {
+    if (required) return fail(MOE_EINVAL, "%s must not be NULL", name);
+    return MOE_OK;
+  }
+  if (!aligned(p, align)) return fail(MOE_EINVAL, "%s must be %zu-byte aligned", name, align);
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                  \
+  do {                                 \
+    moe_status _s = (expr);            \
+    if (_s != MOE_OK) return _s;       \
+  } while (0)
+
+moe_status validate(const moe_config* cfg, int64_t* cap) {
+  if (!cfg) return fail(MOE_EINVAL, "config is NULL");
+  const moe_config& c = *cfg;
+  if (c.T < 0) return fail(MOE_EINVAL, "T must be >= 0 (got %lld)", static_cast<long long>(c.T));
+  if (c.d < 8 || c.d % 8) return fail(MOE_EINVAL, "d must be a positive multiple of 8 (got %d)", c.d);
+  if (c.E < 1 || c.E > 256) return fail(MOE_EINVAL, "E must be in [1, 256] (got %d)", c.E);
+  if (c.k < 1 || c.k > c.E || c.k > 32)
+    return fail(MOE_EINVAL, "k must be in [1, min(E, 32)] (got k=%d, E=%d)", c.k, c.E);
+  if (c.d_ff < 8 || c.d_ff % 8) return fail(MOE_EINVAL, "d_ff must be a positive multiple of 8 (got %d)", c.d_ff);
+  if (c.n_shared < 0) return fail(MOE_EINVAL, "n_shared must be >= 0");
+  if (c.n_shared > 0 && (c.d_ff_shared < 8 || c.d_ff_shared % 8))
+    return fail(MOE_EINVAL, "d_ff_shared must be a positive multiple of 8 (got %d)", c.d_ff_shared);
+  if (c.T * static_cast<int64_t>(c.k) >= (int64_t{1} << 31))
+    return fail(MOE_EINVAL, "T*k must be < 2^31");
+  if (c.capacity_override < 0) return fail(MOE_EINVAL, "capacity_override must be >= 0");
+  if (c.capacity_override == 0 && !(c.capacity_factor >= 1.0))
+    return fail(MOE_EINVAL,
+                "capacity_factor must be >= 1.0 (got %g): below 1 it drops tokens even under "
+                "perfect balance",
+                c.capacity_factor);
+  if (c.renormalize < -1 || c.renormalize > 1) return fail(MOE_EINVAL, "renormalize must be -1, 0 or 1");
+  if (c.score != MOE_SOFTMAX && c.score != MOE_SIGMOID) return fail(MOE_EINVAL, "unknown score %d", c.score);
+  if (c.act != MOE_GELU && c.act != MOE_SWIGLU) return fail(MOE_EINVAL, "unknown act %d", c.act);
+  if (c.dtype != MOE_F32 && c.dtype != MOE_BF16) return fail(MOE_EINVAL, "unknown dtype %d", c.dtype);
+  if (c.priority != MOE_RANK_MAJOR && c.priority != MOE_TOKEN_MAJOR)
+    return fail(MOE_EINVAL, "unknown priority %d", c.priority);
+  if (c.dropped_output != 0 && c.dropped_output != 1) return fail(MOE_EINVAL, "dropped_output must be 0 or 1");
+  const int64_t C = capacity_of(c);
+  if (C > (int64_t{1} << 31) / c.E) return fail(MOE_EINVAL, "capacity %lld too large", static_cast<long long>(C));
+  if (cap) *cap = C;
+  return MOE_OK;
+}
+
+int resolved_renorm(const moe_config& c) { return c.renormalize < 0 ? (c.k > 1) : c.renormalize; }
+
+// ------------------------------------------------------------------ workspace
+struct Workspace {
+  int32_t* hist;
+  int32_t* kept;
+  int32_t* counts_tmp;
+  double* p_partial;
+  double* lse2_partial;
+  int32_t* fallback_partial;
+  int32_t* idx_tmp;
+  float* gates_tmp;
+  int32_t* row_token;
+  void* xe;
+  void* h;
+  void* ye;
+  void* hs;
+  void* s;
+  size_t bytes;
+};
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t{255}; }
+
+Workspace carve(const moe_config& c, int64_t C, void* base) {
+  const int64_t n_tiles = (c.T + kTileTokens - 1) / kTileTokens;
+  const int64_t n_rtiles = (c.T + kRouteTokens - 1) / kRouteTokens;
+  const size_t ds = dsize(c);
+  const int64_t fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
+  Workspace w{};
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t n) -> void* {
+    void* p = b ? b + off : nullptr;
+    off += align_up(n);
+    return p;
+  };
+  w.hist = static_cast<int32_t*>(take(sizeof(int32_t) * c.k * n_tiles * c.E));
+  w.kept = static_cast<int32_t*>(take(sizeof(int32_t) * c.E));
+  w.counts_tmp = static_cast<int32_t*>(take(sizeof(int32_t) * c.E));
+  w.p_partial = static_cast<double*>(take(sizeof(double) * n_rtiles * c.E));
+  w.lse2_partial = static_cast<double*>(take(sizeof(double) * n_rtiles));
+  w.fallback_partial = static_cast<int32_t*>(take(sizeof(int32_t) * n_tiles));
+  w.idx_tmp = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
+  w.gates_tmp = static_cast<float*>(take(sizeof(float) * c.T * c.k));
+  w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * c.E * C));
+  w.xe = take(ds * c.E * C * c.d);
+  w.h = take(ds * c.E * C * c.d_ff);
+  w.ye = take(ds * c.E * C * c.d);
+  w.hs = fs > 0 ? take(ds * c.T * fs) : nullptr;
+  w.s = fs > 0 ? take(ds * c.T * c.d) : nullptr;
+  w.bytes = off;
+  return w;
+}
+
+RouteArgs route_args(const moe_config& c, Workspace* w) {
+  RouteArgs r{};
+  r.T = c.T;
+  r.d = c.d;
+  r.E = c.E;
+  r.k = c.k;
+  r.score = c.score;
+  r.renorm = resolved_renorm(c);
+  if (w) {
+    r.p_partial = w->p_partial;
+    r.lse2_partial = w->lse2_partial;
+  }
+  return r;
+}
+
+CapArgs cap_args(const moe_config& c, int64_t C, const Workspace& w) {
+  CapArgs a{};
+  a.hist = w.hist;
+  a.kept = w.kept;
+  a.fallback_partial = w.fallback_partial;
+  a.T = c.T;
+  a.C = C;
+  a.E = c.E;
+  a.k = c.k;
+  a.d = c.d;
+  a.n_tiles = static_cast<int>((c.T + kTileTokens - 1) / kTileTokens);
+  a.token_major = c.priority == MOE_TOKEN_MAJOR;
+  return a;
+}
+
+LossArgs loss_args(const moe_config& c, int64_t C, const Workspace& w, const int32_t* counts) {
+  LossArgs l{};
+  l.p_partial = w.p_partial;
+  l.lse2_partial = w.lse2_partial;
+  l.counts = counts;
+  l.fallback_partial = w.fallback_partial;
+  l.T = c.T;
+  l.C = C;
+  l.E = c.E;
+  l.k = c.k;
+  l.n_rtiles = static_cast<int>((c.T + kRouteTokens - 1) / kRouteTokens);
+  l.n_tiles = static_cast<int>((c.T + kTileTokens - 1) / kTileTokens);
+  l.has_shared = c.n_shared > 0;
+  return l;
+}
+
+moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int32_t* rows, const void* a,
+               const void* w_in, const void* w_gate, const void* b_in, const void* w_out, const void* b_out,
+               int F, void* h, void* out, hipStream_t s) {
+  // element offsets inside one group are 32-bit in the GEMM kernels
+  const int64_t lim = int64_t{1} << 31;
+  if (rpg * c.d >= lim || rpg * F >= lim || static_cast<int64_t>(F) * c.d >= lim)
+    return fail(MOE_EINVAL, "one expert's operands must hold < 2^31 elements");
+  GemmArgs g1{};
+  g1.A = a;
+  g1.B0 = w_in;
+  g1.B1 = w_gate;
+  g1.bias = act == MOE_SWIGLU ? nullptr : b_in;
+  g1.C = h;
+  g1.rows = rows;
+  g1.rows_per_group = rpg;
+  g1.groups = groups;
+  g1.N = F;
+  g1.K = c.d;
+  g1.act = act == MOE_SWIGLU ? 2 : 1;
+  MOE_TRY(hip_status(launch_gemm(g1, c.dtype, s), "expert GEMM 1"));
+  GemmArgs g2{};
+  g2.A = h;
+  g2.B0 = w_out;
+  g2.bias = b_out;
+  g2.C = out;
+  g2.rows = rows;
+  g2.rows_per_group = rpg;
+  g2.groups = groups;
+  g2.N = c.d;
+  g2.K = F;
+  g2.act = 0;
+  return hip_status(launch_gemm(g2, c.dtype, s), "expert GEMM 2");
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_error.c_str(); }
+
+moe_status moe_validate(const moe_config* cfg, int64_t* capacity) { return validate(cfg, capacity); }
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+  int64_t C = 0;
+  if (validate(cfg, &C) != MOE_OK) return 0;
+  return carve(*cfg, C, nullptr).bytes;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router, const float* logit_bias,
+                     const float* select_bias, float* logits, float* probs, int32_t* idx, float* gates,
+                     float* lse, void* ws, void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  const bool needT = c.T > 0;   // T-sized buffers may be NULL when T == 0
+  MOE_TRY(check_ptr(idx, "idx", 4, needT));
+  MOE_TRY(check_ptr(gates, "gates", 4, needT));
+  MOE_TRY(check_ptr(logit_bias, "logit_bias", 4, false));
+  MOE_TRY(check_ptr(select_bias, "select_bias", 4, false));
+  MOE_TRY(check_ptr(probs, "probs", 4, false));
+  MOE_TRY(check_ptr(lse, "lse", 4, false));
+  MOE_TRY(check_ptr(ws, "ws", 256, false));
+  if (x) {
+    MOE_TRY(check_ptr(x, "x", 16));
+    MOE_TRY(check_ptr(w_router, "w_router", 4));
+    MOE_TRY(check_ptr(logits, "logits", 4, false));
+  } else {
+    MOE_TRY(check_ptr(logits, "logits (input when x is NULL)", 4, needT));
+  }
+  Workspace w = carve(c, C, ws);
+  RouteArgs r = route_args(c, ws ? &w : nullptr);
+  r.x = x;
+  r.w_router = w_router;
+  r.logit_bias = logit_bias;
+  r.select_bias = select_bias;
+  r.logits = logits;
+  r.probs = probs;
+  r.idx = idx;
+  r.gates = gates;
+  r.lse = lse;
+  return hip_status(launch_route(r, c.dtype, static_cast<hipStream_t>(stream)), "router");
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx, int32_t* slot, uint8_t* dropped,
+                        int32_t* counts, int32_t* row_token, void* xe, void* ws, void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  const bool needT = c.T > 0;
+  MOE_TRY(check_ptr(idx, "idx", 4, needT));
+  MOE_TRY(check_ptr(slot, "slot", 4, needT));
+  MOE_TRY(check_ptr(dropped, "dropped", 1, needT));
+  MOE_TRY(check_ptr(counts, "counts", 4));
+  MOE_TRY(check_ptr(row_token, "row_token", 4, false));
+  MOE_TRY(check_ptr(ws, "ws", 256));
+  if ((xe || x) && needT) {
+    MOE_TRY(check_ptr(x, "x", 16));
+    MOE_TRY(check_ptr(xe, "xe", 16, C > 0));
+  }
+  Workspace w = carve(c, C, ws);
+  CapArgs a = cap_args(c, C, w);
+  a.idx = idx;
+  a.slot = slot;
+  a.dropped = dropped;
+  a.counts = counts;
+  a.row_token = row_token;
+  a.x = x;
+  a.xe = xe;
+  return hip_status(launch_capacity(a, c.dtype, static_cast<hipStream_t>(stream)), "capacity");
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups, int64_t rows_per_group,
+                          const int32_t* rows, const void* a, const void* w_in, const void* w_gate,
+                          const void* b_in, const void* w_out, const void* b_out, int32_t F, void* h, void* out,
+                          void* stream) {
+  MOE_TRY(validate(cfg, nullptr));
+  const moe_config& c = *cfg;
+  if (act != MOE_GELU && act != MOE_SWIGLU) return fail(MOE_EINVAL, "unknown act %d", act);
+  if (groups < 0 || rows_per_group < 0) return fail(MOE_EINVAL, "groups and rows_per_group must be >= 0");
+  if (F < 8 || F % 8) return fail(MOE_EINVAL, "F must be a positive multiple of 8 (got %d)", F);
+  if (static_cast<int64_t>(groups) * rows_per_group >= (int64_t{1} << 31))
+    return fail(MOE_EINVAL, "groups*rows_per_group must be < 2^31");
+  MOE_TRY(check_ptr(a, "a", 16));
+  MOE_TRY(check_ptr(w_in, "w_in", 16));
+  MOE_TRY(check_ptr(w_out, "w_out", 16));
+  MOE_TRY(check_ptr(h, "h", 16));
+  MOE_TRY(check_ptr(out, "out", 16));
+  MOE_TRY(check_ptr(rows, "rows", 4, false));
+  MOE_TRY(check_ptr(b_in, "b_in", dsize(c), false));
+  MOE_TRY(check_ptr(b_out, "b_out", dsize(c), false));
+  if (act == MOE_SWIGLU) {
+    MOE_TRY(check_ptr(w_gate, "w_gate", 16));
+    if (b_in) return fail(MOE_EUNSUPPORTED, "SwiGLU experts take no b_in");
+  }
+  return ffn(c, act, groups, rows_per_group, rows, a, w_in, w_gate, b_in, w_out, b_out, F, h, out,
+             static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_config* cfg, const void* x, const void* ye, const void* shared_out,
+                       const int32_t* idx, const float* gates, const int32_t* slot, const uint8_t* dropped, void* y,
+                       void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  const bool needT = c.T > 0;
+  MOE_TRY(check_ptr(x, "x", 16, needT));
+  MOE_TRY(check_ptr(ye, "ye", 16, needT && C > 0));
+  MOE_TRY(check_ptr(shared_out, "shared_out", 16, false));
+  MOE_TRY(check_ptr(idx, "idx", 4, needT));
+  MOE_TRY(check_ptr(gates, "gates", 4, needT));
+  MOE_TRY(check_ptr(slot, "slot", 4, needT));
+  MOE_TRY(check_ptr(dropped, "dropped", 1, needT));
+  MOE_TRY(check_ptr(y, "y", 16, needT));
+  CombineArgs a{};
+  a.x = x;
+  a.ye = ye;
+  a.shared_out = shared_out;
+  a.idx = idx;
+  a.gates = gates;
+  a.slot = slot;
+  a.dropped = dropped;
+  a.y = y;
+  a.T = c.T;
+  a.C = C;
+  a.d = c.d;
+  a.k = c.k;
+  a.E = c.E;
+  a.zero_fallback = c.dropped_output;
+  return hip_status(launch_combine(a, c.dtype, static_cast<hipStream_t>(stream)), "combine");
+}
+
+moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int32_t* idx, float* losses, void* ws,
+                          void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  MOE_TRY(check_ptr(logits, "logits", 4, c.T > 0));
+  MOE_TRY(check_ptr(idx, "idx", 4, c.T > 0));
+  MOE_TRY(check_ptr(losses, "losses", 4));
+  MOE_TRY(check_ptr(ws, "ws", 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace w = carve(c, C, ws);
+  // probabilities and LSE partials from the given logits (the re-derived
+  // selection goes to scratch and is not used)
+  RouteArgs r = route_args(c, &w);
+  r.logits = const_cast<float*>(logits);
+  r.idx = w.idx_tmp;
+  r.gates = w.gates_tmp;
+  MOE_TRY(hip_status(launch_route(r, c.dtype, s), "aux-loss statistics"));
+  // f_i from the given choices: the capacity histogram + scan (no dispatch)
+  CapArgs a = cap_args(c, C, w);
+  a.idx = idx;
+  a.counts = w.counts_tmp;
+  a.slot = w.idx_tmp;                         // scratch, overwritten
+  a.dropped = reinterpret_cast<uint8_t*>(w.gates_tmp);
+  a.fallback_partial = nullptr;
+  MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "aux-loss counts"));
+  LossArgs l = loss_args(c, C, w, w.counts_tmp);
+  l.fallback_partial = nullptr;
+  l.losses = losses;
+  return hip_status(launch_losses(l, s), "aux-loss finaliser");
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* x, moe_outputs* out, void* ws,
+                       void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  if (!wt || !out) return fail(MOE_EINVAL, "weights and outputs must not be NULL");
+  const bool needT = c.T > 0;   // T-sized buffers may be NULL when T == 0
+  MOE_TRY(check_ptr(x, "x", 16, needT));
+  MOE_TRY(check_ptr(ws, "ws", 256));
+  MOE_TRY(check_ptr(wt->w_router, "w_router", 4));
+  MOE_TRY(check_ptr(wt->logit_bias, "logit_bias", 4, false));
+  MOE_TRY(check_ptr(wt->select_bias, "select_bias", 4, false));
+  MOE_TRY(check_ptr(wt->w_in, "w_in", 16));
+  MOE_TRY(check_ptr(wt->w_out, "w_out", 16));
+  MOE_TRY(check_ptr(wt->b_in, "b_in", dsize(c), false));
+  MOE_TRY(check_ptr(wt->b_out, "b_out", dsize(c), false));
+  if (c.act == MOE_SWIGLU) {
+    MOE_TRY(check_ptr(wt->w_gate, "w_gate", 16));
+    if (wt->b_in) return fail(MOE_EUNSUPPORTED, "SwiGLU experts take no b_in");
+  }
+  if (c.n_shared > 0) {
+    MOE_TRY(check_ptr(wt->ws_in, "ws_in", 16));
+    MOE_TRY(check_ptr(wt->ws_out, "ws_out", 16));
+    MOE_TRY(check_ptr(wt->bs_in, "bs_in", dsize(c), false));
+    MOE_TRY(check_ptr(wt->bs_out, "bs_out", dsize(c), false));
+  }
+  MOE_TRY(check_ptr(out->y, "y", 16, needT));
+  MOE_TRY(check_ptr(out->idx, "idx", 4, needT));
+  MOE_TRY(check_ptr(out->gates, "gates", 4, needT));
+  MOE_TRY(check_ptr(out->slot, "slot", 4, needT));
+  MOE_TRY(check_ptr(out->dropped, "dropped", 1, needT));
+  MOE_TRY(check_ptr(out->counts, "counts", 4));
+  MOE_TRY(check_ptr(out->losses, "losses", 4));
+  MOE_TRY(check_ptr(out->stats, "stats", 4, false));
+  MOE_TRY(check_ptr(out->logits, "logits", 4, false));
+  MOE_TRY(check_ptr(out->probs, "probs", 4, false));
+  MOE_TRY(check_ptr(out->lse, "lse", 4, false));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace w = carve(c, C, ws);
+
+  RouteArgs r = route_args(c, &w);
+  r.x = x;
+  r.w_router = wt->w_router;
+  r.logit_bias = wt->logit_bias;
+  r.select_bias = wt->select_bias;
+  r.logits = out->logits;
+  r.probs = out->probs;
+  r.idx = out->idx;
+  r.gates = out->gates;
+  r.lse = out->lse;
+  MOE_TRY(hip_status(launch_route(r, c.dtype, s), "router"));
+
+  CapArgs a = cap_args(c, C, w);
+  a.idx = out->idx;
+  a.counts = out->counts;
+  a.slot = out->slot;
+  a.dropped = out->dropped;
+  a.row_token = w.row_token;
+  a.x = x;
+  a.xe = w.xe;
+  MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "capacity"));
+
+  if (C > 0)
+    MOE_TRY(ffn(c, c.act, c.E, C, w.kept, w.xe, wt->w_in, wt->w_gate, wt->b_in, wt->w_out, wt->b_out, c.d_ff, w.h,
+                w.ye, s));
+  if (c.n_shared > 0 && c.T > 0)
+    MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, wt->ws_in, nullptr, wt->bs_in, wt->ws_out, wt->bs_out,
+                c.n_shared * c.d_ff_shared, w.hs, w.s, s));
+
+  CombineArgs cb{};
+  cb.x = x;
+  cb.ye = w.ye;
+  cb.shared_out = c.n_shared > 0 ? w.s : nullptr;
+  cb.idx = out->idx;
+  cb.gates = out->gates;
+  cb.slot = out->slot;
+  cb.dropped = out->dropped;
+  cb.y = out->y;
+  cb.T = c.T;
+  cb.C = C;
+  cb.d = c.d;
+  cb.k = c.k;
+  cb.E = c.E;
+  cb.zero_fallback = c.dropped_output;
+  MOE_TRY(hip_status(launch_combine(cb, c.dtype, s), "combine"));
+
+  LossArgs l = loss_args(c, C, w, out->counts);
+  l.losses = out->losses;
+  l.stats = out->stats;
+  return hip_status(launch_losses(l, s), "loss finaliser");
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 storage, wave-64
+// reductions, and the internal launch descriptors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kTileTokens = 64;      // tokens per capacity tile (one wavefront)
+
+using bf16_t = uint16_t;             // raw bf16 bits in memory
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// float32 -> bf16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Storage;
+template <> struct Storage<float> {
+  __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Storage<bf16_t> {
+  __device__ static __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ static __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Monotone map of a float32 key to uint32 (larger key -> larger code);
+// -0 is first folded to +0 so that the two compare equal.
+__device__ __forceinline__ uint32_t order_code(float key) {
+  uint32_t b = __float_as_uint(key);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+// Packed selection code: key first, then the LOWER expert index wins a tie.
+__device__ __forceinline__ uint64_t select_code(float key, int e) {
+  return (static_cast<uint64_t>(order_code(key)) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
+}
+__device__ __forceinline__ int code_expert(uint64_t c) {
+  return static_cast<int>(~static_cast<uint32_t>(c & 0xFFFFFFFFull));
+}
+
+// ---------------------------------------------------------------- descriptors
+struct RouteArgs {
+  const void* x;              // [T,d] or null (logits given)
+  const float* w_router;      // [d,E]
+  const float* logit_bias;    // [E] | null
+  const float* select_bias;   // [E] | null
+  float* logits;              // [T,E] in (x null) or out | null
+  float* probs;               // [T,E] | null
+  int32_t* idx;               // [T,k]
+  float* gates;               // [T,k]
+  float* lse;                 // [T] | null
+  double* p_partial;          // [n_rtiles, E] | null
+  double* lse2_partial;       // [n_rtiles] | null
+  int64_t T;
+  int d, E, k;
+  int score;                  // moe_score
+  int renorm;                 // resolved: 0 / 1
+};
+
+struct CapArgs {
+  const int32_t* idx;         // [T,k]
+  int32_t* hist;              // [k, n_tiles, E]: counts, then exclusive offsets
+  int32_t* counts;            // [E]
+  int32_t* kept;              // [E] min(counts, C) | null
+  int32_t* slot;              // [T,k]
+  uint8_t* dropped;           // [T,k]
+  int32_t* row_token;         // [E,C] | null
+  int32_t* fallback_partial;  // [n_tiles] | null
+  const void* x;              // [T,d] | null
+  void* xe;                   // [E,C,d] | null
+  int64_t T, C;
+  int E, k, d, n_tiles;
+  int token_major;
+};
+
+struct GemmArgs {
+  const void* A;              // [groups*rows_per_group, K]
+  const void* B0;             // [groups, N, K]
+  const void* B1;             // [groups, N, K] (SwiGLU gate) | null
+  const void* bias;           // [groups, N] | null
+  void* C;                    // [groups*rows_per_group, N]
+  const int32_t* rows;        // [groups] | null
+  int64_t rows_per_group;
+  int groups, N, K;
+  int act;                    // 0 none (bias only), 1 GELU, 2 SwiGLU (B1 = gate)
+};
+
+struct CombineArgs {
+  const void* x;              // [T,d]
+  const void* ye;             // [E,C,d]
+  const void* shared_out;     // [T,d] | null
+  const int32_t* idx;
+  const float* gates;
+  const int32_t* slot;
+  const uint8_t* dropped;
+  void* y;                    // [T,d]
+  int64_t T, C;
+  int d, k, E;
+  int zero_fallback;
+};
+
+struct LossArgs {
+  const double* p_partial;    // [n_rtiles, E]
+  const double* lse2_partial; // [n_rtiles]
+  const int32_t* counts;      // [E]
+  const int32_t* fallback_partial;  // [n_tiles] | null
+  float* losses;              // [2]
+  int32_t* stats;             // [4] | null
+  int64_t T, C;
+  int E, k, n_rtiles, n_tiles;
+  int has_shared;
+};
+
+// host-side launchers (defined in the kernel translation units)
+hipError_t launch_route(const RouteArgs& a, int dtype, hipStream_t s);
+hipError_t launch_capacity(const CapArgs& a, int dtype, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
+hipError_t launch_losses(const LossArgs& a, hipStream_t s);
+
+// router tile (tokens per router workgroup), shared by launcher and host sizing
+constexpr int kRouteTokens = 32;
+
+}  // namespace moe

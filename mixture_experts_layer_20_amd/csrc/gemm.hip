@@ -1,0 +1,321 @@
+// Grouped expert GEMMs for gfx950: C[g] = act(A[g] B[g]^T + bias[g]) for every
+// expert g, with ragged row counts read on the device.
+//
+// Sources: "Lab 18 -- Mixture of experts" s.1 (an expert is a 2-matrix GELU
+// MLP, or Mixtral's 3-matrix SwiGLU FFN) and Tips (production kernels run one
+// grouped matrix multiply over all experts); "Mixture of experts" lecture
+// field map, systems section (small ragged per-expert matmuls).
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16 with float32 accumulation.
+//   * Workgroup tile: 256 token rows x 256 weight rows x 64 (k), 4 wavefronts,
+//     each owning 128 x 128 of the output (4 x 4 MFMA blocks, 256 float32
+//     accumulators per lane).  For SwiGLU the 256 weight rows are 128 gate
+//     rows and the 128 matching up rows, so the epilogue has g and u of the
+//     same output element in the same lane and register.
+//   * The MFMA's first operand is the weight tile and its second the token
+//     tile, so each lane ends with four consecutive output columns of one
+//     token row: 8-byte bf16 stores.
+//   * Global -> registers -> LDS, double-buffered, one barrier per k-step;
+//     16-byte chunks XOR-swizzled by row so fragment reads spread over banks.
+//   * Tile order: blocks are dealt round-robin to the 8 XCDs, so block b is
+//     remapped to logical tile (b mod 8) * (grid/8) + b/8; logical tiles walk
+//     groups of 4 row-tiles column by column, so the ~32 tiles an XCD runs at
+//     once share 4 token panels and 8 weight panels in its L2.
+//   * Rows at or past rows[g] are never stored; their loads are clamped to a
+//     valid row.  Columns past N are clamped and not stored; k past K reads 0.
+// float32 path: a plain LDS-tiled FMA kernel (small layers only).
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kBM = 256;     // token rows per tile
+constexpr int kBW = 256;     // weight rows per tile
+constexpr int kBK = 64;      // k per stage
+constexpr int kRowBytes = kBK * 2;                         // 128
+constexpr int kStageBytes = (kBM + kBW) * kRowBytes;       // 64 KiB
+constexpr int kChunksPerTile = kBM * kBK / 8;              // 2048 16-byte chunks per operand tile
+constexpr int kLoadsPerThread = kChunksPerTile / kThreads; // 8
+
+__device__ __forceinline__ float gelu_erf(float v) {
+  return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+}
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+}
+
+struct TileCoord {
+  int g, mt, nt;
+  bool valid;
+};
+
+// logical tile -> (group, row tile, column tile): groups of 4 row tiles,
+// walked column by column
+__device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntiles, int groups) {
+  TileCoord c;
+  const int64_t per_group = static_cast<int64_t>(mt_max) * ntiles;
+  c.valid = L < per_group * groups;
+  if (!c.valid) { c.g = c.mt = c.nt = 0; return c; }
+  c.g = static_cast<int>(L / per_group);
+  const int r = static_cast<int>(L % per_group);
+  constexpr int kGM = 4;
+  const int band = r / (kGM * ntiles);
+  const int first = band * kGM;
+  const int gm = min(kGM, mt_max - first);
+  const int within = r % (kGM * ntiles);
+  c.mt = first + within % gm;
+  c.nt = within / gm;
+  return c;
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr bool kGlu = ACT == 2;
+  constexpr int kNOut = kGlu ? kBW / 2 : kBW;   // output columns per tile
+  __shared__ __align__(16) uint8_t lds[2 * kStageBytes];
+
+  const int N = a.N, K = a.K;
+  const int ntiles = (N + kNOut - 1) / kNOut;
+  const int mt_max = static_cast<int>((a.rows_per_group + kBM - 1) / kBM);
+  const int64_t nb8 = gridDim.x / 8;
+  const int64_t L = static_cast<int64_t>(blockIdx.x % 8) * nb8 + blockIdx.x / 8;
+  const TileCoord tc = decode_tile(L, mt_max, ntiles, a.groups);
+  if (!tc.valid) return;
+  const int64_t rows_g = a.rows ? min<int64_t>(a.rows[tc.g], a.rows_per_group) : a.rows_per_group;
+  const int m0 = tc.mt * kBM;
+  if (m0 >= rows_g) return;
+  const int n0 = tc.nt * kNOut;
+
+  const bf16_t* A = static_cast<const bf16_t*>(a.A) + static_cast<int64_t>(tc.g) * a.rows_per_group * K;
+  const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + static_cast<int64_t>(tc.g) * N * K;
+  const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + static_cast<int64_t>(tc.g) * N * K : nullptr;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  // per-thread element offsets of the 8 + 8 chunks it stages each k-step:
+  // chunk q = tid + 256 i sits at row q/8 = tid/8 + 32 i, column chunk tid%8,
+  // so its swizzled LDS offset is the i = 0 offset + 32 i rows
+  const int c8 = tid & 7;
+  const int lds_x0 = swz(tid >> 3, c8);
+  uint32_t xo[kLoadsPerThread], wo[kLoadsPerThread];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerThread; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    const int64_t m = min<int64_t>(m0 + row, rows_g - 1);
+    xo[i] = static_cast<uint32_t>(m * K + c8 * 8);
+    int n;
+    if (kGlu) {
+      // rows 0..127 (i < 4) come from the gate matrix B1, rows 128..255 from B0
+      n = min(n0 + (row & 127), N - 1);
+    } else {
+      n = min(n0 + row, N - 1);
+    }
+    wo[i] = static_cast<uint32_t>(static_cast<int64_t>(n) * K + c8 * 8);
+  }
+  const int kchunk = c8 * 8;
+
+  uint4 px[kLoadsPerThread], pw[kLoadsPerThread];
+  auto gload = [&](int kt) {
+    const int k0 = kt * kBK;
+    const bool ok = k0 + kchunk < K;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      const bf16_t* wb = kGlu ? (i < kLoadsPerThread / 2 ? B1 : B0) : B0;
+      px[i] = ok ? *reinterpret_cast<const uint4*>(A + xo[i] + k0) : make_uint4(0, 0, 0, 0);
+      pw[i] = ok ? *reinterpret_cast<const uint4*>(wb + wo[i] + k0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* s = lds + buf * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      *reinterpret_cast<uint4*>(s + lds_x0 + i * 32 * kRowBytes) = px[i];
+      *reinterpret_cast<uint4*>(s + kBM * kRowBytes + lds_x0 + i * 32 * kRowBytes) = pw[i];
+    }
+  };
+
+  // wave layout: 2 x 2 wavefronts, each 128 weight rows x 128 token rows
+  const int wn = wave & 1, wm = wave >> 1;
+  int wrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    wrow[i] = kGlu ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + (lane & 31))
+                   : (wn * 128 + i * 32 + (lane & 31));
+  int xrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xrow[j] = wm * 128 + j * 32 + (lane & 31);
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (K + kBK - 1) / kBK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint8_t* s = lds + buf * kStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      bf16x8_t wf[4], xf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + kBM * kRowBytes + swz(wrow[i], c)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + swz(xrow[j], c)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds, for block (i, j), output columns
+  // nbase + 8q + 4*(lane/32) + {0..3} of token row mbase + lane%32
+  bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;
+  const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
+  constexpr int kIB = kGlu ? 2 : 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
+    if (m >= rows_g) continue;
+#pragma unroll
+    for (int i = 0; i < kIB; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + (kGlu ? wn * 64 : wn * 128) + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (n >= N) continue;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[i][j][4 * q + r];
+          if (ACT == 2) {
+            const float up = acc[i + 2][j][4 * q + r];
+            x = silu(x) * up;
+          } else {
+            if (bias) x += bf16_to_f32(bias[n + r]);
+            if (ACT == 1) x = gelu_erf(x);
+          }
+          v[r] = x;
+        }
+        uint2 packed;
+        packed.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        packed.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2*>(C + m * N + n) = packed;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ float32
+constexpr int kFT = 32;   // 32 x 32 output tile, 256 threads x 4 outputs
+
+template <int ACT>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
+  __shared__ float as[kFT][kFT + 1];
+  __shared__ float bs[2][kFT][kFT + 1];
+  const int N = a.N, K = a.K;
+  const int ntiles = (N + kFT - 1) / kFT;
+  const int mt_max = static_cast<int>((a.rows_per_group + kFT - 1) / kFT);
+  const int64_t L = blockIdx.x;
+  const int g = static_cast<int>(L / (static_cast<int64_t>(mt_max) * ntiles));
+  if (g >= a.groups) return;
+  const int r = static_cast<int>(L % (static_cast<int64_t>(mt_max) * ntiles));
+  const int mt = r / ntiles, nt = r % ntiles;
+  const int64_t rows_g = a.rows ? min<int64_t>(a.rows[g], a.rows_per_group) : a.rows_per_group;
+  const int m0 = mt * kFT, n0 = nt * kFT;
+  if (m0 >= rows_g) return;
+  const float* A = static_cast<const float*>(a.A) + static_cast<int64_t>(g) * a.rows_per_group * K;
+  const float* B0 = static_cast<const float*>(a.B0) + static_cast<int64_t>(g) * N * K;
+  const float* B1 = ACT == 2 ? static_cast<const float*>(a.B1) + static_cast<int64_t>(g) * N * K : nullptr;
+  const int tx = threadIdx.x % kFT, ty = threadIdx.x / kFT;   // ty 0..7
+  float acc0[4] = {0, 0, 0, 0}, acc1[4] = {0, 0, 0, 0};
+  for (int k0 = 0; k0 < K; k0 += kFT) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kFT * kFT; i += kThreads) {
+      const int rr = i / kFT, cc = i % kFT;
+      const int64_t m = m0 + rr;
+      const int n = n0 + rr;
+      const int kk = k0 + cc;
+      as[rr][cc] = (m < rows_g && kk < K) ? A[m * K + kk] : 0.0f;
+      bs[0][rr][cc] = (n < N && kk < K) ? B0[static_cast<int64_t>(n) * K + kk] : 0.0f;
+      if (ACT == 2) bs[1][rr][cc] = (n < N && kk < K) ? B1[static_cast<int64_t>(n) * K + kk] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < kFT; ++kk) {
+      const float b0 = bs[0][tx][kk];
+      const float b1 = ACT == 2 ? bs[1][tx][kk] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float av = as[ty + 8 * q][kk];
+        acc0[q] += av * b0;
+        if (ACT == 2) acc1[q] += av * b1;
+      }
+    }
+  }
+  float* C = static_cast<float*>(a.C) + static_cast<int64_t>(g) * a.rows_per_group * N;
+  const float* bias = a.bias ? static_cast<const float*>(a.bias) + static_cast<int64_t>(g) * N : nullptr;
+  const int n = n0 + tx;
+  if (n >= N) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t m = m0 + ty + 8 * q;
+    if (m >= rows_g) continue;
+    float v = acc0[q];
+    if (ACT == 2) {
+      v = silu(acc1[q]) * v;          // B0 = up, B1 = gate
+    } else {
+      if (bias) v += bias[n];
+      if (ACT == 1) v = gelu_erf(v);
+    }
+    C[m * N + n] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
+  if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
+  if (dtype == MOE_BF16) {
+    const int nout = a.act == 2 ? kBW / 2 : kBW;
+    const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kBM - 1) / kBM) *
+                          ((a.N + nout - 1) / nout);
+    const unsigned grid = static_cast<unsigned>((tiles + 7) / 8 * 8);
+    switch (a.act) {
+      case 0: gemm_bf16_kernel<0><<<grid, kThreads, 0, s>>>(a); break;
+      case 1: gemm_bf16_kernel<1><<<grid, kThreads, 0, s>>>(a); break;
+      default: gemm_bf16_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
+    }
+  } else {
+    const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kFT - 1) / kFT) *
+                          ((a.N + kFT - 1) / kFT);
+    const unsigned grid = static_cast<unsigned>(tiles);
+    switch (a.act) {
+      case 0: gemm_f32_kernel<0><<<grid, kThreads, 0, s>>>(a); break;
+      case 1: gemm_f32_kernel<1><<<grid, kThreads, 0, s>>>(a); break;
+      default: gemm_f32_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -253,3 +253,15 @@ def random_indices(T: int, E: int, k: int, seed: int, skew: float = 0.0) -> np.n
 def tiny(name: str, **kw) -> Workload:
     """A small variant of a named workload (for tests on CPU or quick GPU checks)."""
     return WORKLOADS[name].with_(name=name + '_small', **kw)
+
+
+def to_torch(a, device='cuda'):
+    """A stored input tensor as a torch tensor on `device`: bf16 bit patterns
+    become torch.bfloat16 (same bits), float32 stays float32."""
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
