@@ -1,0 +1,257 @@
+"""Benchmark of the MoE layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--phase-reps R]
+
+A step is one whole forward pass of the layer (router, capacity, dispatch,
+routed and shared expert FFNs, combine, losses) over one batch of T synthetic
+tokens that are already resident in HBM, through moe_forward on torch's
+current stream.  `value` is tokens per second over the K timed steps.
+
+Besides the headline line, the run times each phase of the same layer
+through the public entry points (moe_route, moe_dispatch, moe_expert_ffn,
+moe_combine) with HIP events recorded on the stream the kernels run on, after
+flushing the caches, and reports
+  * roofline: the expert grouped GEMM (the dominant kernel: its gate/up and
+    down launches) against the bf16 MFMA peak, from algorithmic FLOPs
+    2 * kept_assignments * (3 or 2) * d * d_ff (+ shared experts);
+  * phases: router, dispatch and combine against the HBM peak, from their
+    algorithmic bytes;
+  * cpu_baseline: the CPU oracle (tests' reference implementation) timed on a
+    bounded sample of the same workload.
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (vector / matrix)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = 'MoE layer tokens/sec at 1 GPU; expert-GEMM % MFMA peak; route/combine % HBM'
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument('--gpus', type=int, default=1)
+    p.add_argument('--steps', type=int, default=20)
+    p.add_argument('--warmup', type=int, default=5)
+    p.add_argument('--workload', default='mixtral_8x_top2')
+    p.add_argument('--no-cpu-baseline', action='store_true')
+    p.add_argument('--cpu-sample-tokens', type=int, default=0)
+    p.add_argument('--phase-reps', type=int, default=10)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({'error': 'this build runs on one GPU only: the MoE layer is measured on a '
+                                   'single MI355X; --gpus must be 1'}), flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_20_amd as moe
+    import synth
+
+    def log(*a):
+        print('[bench]', *a, file=sys.stderr, flush=True)
+
+    w = synth.WORKLOADS[args.workload]
+    dev = 'cuda'
+    t0 = time.time()
+    inp = synth.router_inputs(w)
+    cfg = moe.config_from_workload(w)
+    C = moe.moe_validate(cfg)
+    x = synth.to_torch(inp['x'], dev)
+    weights = dict(w_router=synth.to_torch(inp['w_router'], dev),
+                   logit_bias=synth.to_torch(inp['logit_bias'], dev),
+                   select_bias=synth.to_torch(inp['select_bias'], dev))
+    dt = moe.torch_dtype(cfg)
+    # expert weights generated one expert at a time straight into device tensors
+    F, d, E = w.d_ff, w.d, w.E
+    names = ('w_gate', 'w_up', 'w_out') if w.act == 'swiglu' else ('w_in', 'b_in', 'w_out', 'b_out')
+    host_ex = {}
+    for e in range(E):
+        ew = synth.expert_weights(w, e)
+        for kk in names:
+            v = ew[kk]
+            if kk in ('b_in', 'b_out') and w.dtype == 'bf16':
+                v = synth.bf16_bits(v)
+            if kk not in host_ex:
+                host_ex[kk] = torch.empty((E,) + v.shape, dtype=dt, device=dev)
+            host_ex[kk][e].copy_(synth.to_torch(v, dev))
+    if w.act == 'swiglu':
+        weights.update(w_gate=host_ex['w_gate'], w_in=host_ex['w_up'], w_out=host_ex['w_out'])
+    else:
+        weights.update(host_ex)
+    if w.n_shared:
+        sh = synth.all_expert_weights(w, shared=True)
+        bs_in = np.concatenate(list(sh['b_in']))
+        bs_out = sh['b_out'].sum(0).astype(np.float32)
+        if w.dtype == 'bf16':
+            bs_in, bs_out = synth.bf16_bits(bs_in), synth.bf16_bits(bs_out)
+        weights.update(ws_in=synth.to_torch(np.concatenate(list(sh['w_in']), 0), dev),
+                       ws_out=synth.to_torch(np.concatenate(list(sh['w_out']), 1), dev),
+                       bs_in=synth.to_torch(bs_in, dev), bs_out=synth.to_torch(bs_out, dev))
+    out = moe.alloc_outputs(cfg, dev)
+    ws = moe.workspace(cfg, dev)
+    torch.cuda.synchronize()
+    log(f'inputs ready in {time.time() - t0:.1f}s: {w.name} T={w.T} d={d} E={E} k={w.k} F={F} C={C}')
+
+    # ---------------------------------------------------------------- headline
+    for _ in range(args.warmup):
+        moe.moe_forward(cfg, weights, x, out, ws)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        moe.moe_forward(cfg, weights, x, out, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms = 1e3 * elapsed / max(1, args.steps)
+    tokens_per_s = w.T * args.steps / elapsed
+    stats = out['stats'].cpu().tolist()
+    kept, n_dropped, fallback, pad = stats
+    log(f'forward: {ms:.3f} ms/step, {tokens_per_s:,.0f} tokens/s, kept {kept}, dropped {n_dropped}, '
+        f'fallback {fallback}')
+
+    # ---------------------------------------------------------------- phases
+    T, k = w.T, w.k
+    b = 2 if w.dtype == 'bf16' else 4
+    idx, gates = out['idx'], out['gates']
+    slot = torch.empty_like(out['slot'])
+    dropped = torch.empty_like(out['dropped'])
+    counts = torch.empty_like(out['counts'])
+    xe = torch.empty(E, C, d, dtype=dt, device=dev)
+    h = torch.empty(E, C, F, dtype=dt, device=dev)
+    ye = torch.empty(E, C, d, dtype=dt, device=dev)
+    y = torch.empty_like(out['y'])
+    fs = w.n_shared * w.d_ff_shared
+    hs = torch.empty(T, fs, dtype=dt, device=dev) if fs else None
+    s_out = torch.empty(T, d, dtype=dt, device=dev) if fs else None
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    ph = {'route': [], 'dispatch': [], 'expert_ffn': [], 'shared_ffn': [], 'combine': []}
+
+    def timed(name, fn):
+        flush.zero_()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        z.record()
+        z.synchronize()
+        ph[name].append(a.elapsed_time(z))
+
+    kept_rows = torch.empty(E, dtype=torch.int32, device=dev)
+    for rep in range(args.phase_reps + 1):
+        timed('route', lambda: moe.moe_route(cfg, x, weights['w_router'], weights['logit_bias'],
+                                             weights['select_bias'], None, None, idx, gates, None, ws))
+        timed('dispatch', lambda: moe.moe_dispatch(cfg, x, idx, slot, dropped, counts, None, xe, ws))
+        torch.clamp(counts, max=C, out=kept_rows)
+        if w.act == 'swiglu':
+            timed('expert_ffn', lambda: moe.moe_expert_ffn(cfg, 'swiglu', E, C, kept_rows, xe, weights['w_in'],
+                                                           weights['w_gate'], None, weights['w_out'], None,
+                                                           F, h, ye))
+        else:
+            timed('expert_ffn', lambda: moe.moe_expert_ffn(cfg, 'gelu', E, C, kept_rows, xe, weights['w_in'],
+                                                           None, weights.get('b_in'), weights['w_out'],
+                                                           weights.get('b_out'), F, h, ye))
+        if fs:
+            timed('shared_ffn', lambda: moe.moe_expert_ffn(cfg, 'gelu', 1, T, None, x, weights['ws_in'], None,
+                                                           weights['bs_in'], weights['ws_out'], weights['bs_out'],
+                                                           fs, hs, s_out))
+        timed('combine', lambda: moe.moe_combine(cfg, x, ye, s_out, idx, gates, slot, dropped, y))
+    med = {kk: float(np.median(v[1:])) for kk, v in ph.items() if v}
+    n_kept = int(torch.clamp(counts, max=C).sum().item())
+    any_kept = (dropped == 0).any(dim=1)
+    n_tok_kept = int(any_kept.sum().item())
+    n_fb = T - n_tok_kept
+    mult = 3 if w.act == 'swiglu' else 2
+    ffn_flops = 2.0 * n_kept * mult * d * F
+    sh_flops = 2.0 * T * 2 * d * fs
+    bytes_route = T * d * b + d * E * 4 + T * k * 8 + ((T + 31) // 32) * (E + 1) * 8
+    bytes_dispatch = T * k * 4 + n_tok_kept * d * b + n_kept * d * b + T * k * 5
+    bytes_combine = n_kept * d * b + (0 if fs else n_fb * d * b) + (T * d * b if fs else 0) + T * d * b + T * k * 13
+    peak = PEAK_BF16_TFLOPS if w.dtype == 'bf16' else PEAK_F32_TFLOPS
+
+    def gbs(nbytes, ms_):
+        return nbytes / (ms_ * 1e-3) / 1e9
+
+    phases = {
+        'route': {'ms': med['route'], 'GB/s': gbs(bytes_route, med['route']),
+                  'hbm_frac': gbs(bytes_route, med['route']) / PEAK_HBM_GBS, 'bytes': bytes_route},
+        'dispatch': {'ms': med['dispatch'], 'GB/s': gbs(bytes_dispatch, med['dispatch']),
+                     'hbm_frac': gbs(bytes_dispatch, med['dispatch']) / PEAK_HBM_GBS, 'bytes': bytes_dispatch},
+        'expert_ffn': {'ms': med['expert_ffn'], 'TFLOP/s': ffn_flops / (med['expert_ffn'] * 1e-3) / 1e12,
+                       'mfma_frac': ffn_flops / (med['expert_ffn'] * 1e-3) / 1e12 / peak, 'flops': ffn_flops},
+        'combine': {'ms': med['combine'], 'GB/s': gbs(bytes_combine, med['combine']),
+                    'hbm_frac': gbs(bytes_combine, med['combine']) / PEAK_HBM_GBS, 'bytes': bytes_combine},
+    }
+    if fs:
+        phases['shared_ffn'] = {'ms': med['shared_ffn'], 'TFLOP/s': sh_flops / (med['shared_ffn'] * 1e-3) / 1e12,
+                                'mfma_frac': sh_flops / (med['shared_ffn'] * 1e-3) / 1e12 / peak,
+                                'flops': sh_flops}
+    for kk, v in phases.items():
+        log(f'phase {kk}: ' + ', '.join(f'{a}={bb:.4g}' if isinstance(bb, float) else f'{a}={bb}'
+                                      for a, bb in v.items()))
+    ach = ffn_flops / (med['expert_ffn'] * 1e-3) / 1e12
+    roofline = {'kernel': 'expert grouped GEMM (gate/up launch + down launch)',
+                'bound': 'mfma', 'achieved': round(ach, 2), 'peak': peak, 'unit': 'TFLOP/s',
+                'frac': round(ach / peak, 4), 'traffic': None,
+                'algorithmic': f'2*kept*{mult}*d*d_ff = {ffn_flops:.4e} flop per launch pair, '
+                               f'kept={n_kept}'}
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_sample_tokens, log)
+
+    line = {'metric': METRIC, 'value': round(tokens_per_s, 1), 'unit': 'tokens/s', 'n_gpus': 1,
+            'steps': args.steps, 'warmup': args.warmup, 'ms_per_step': round(ms, 4),
+            'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None, 'dtype': w.dtype,
+            'data': 'synthetic (seeded; random-init weights of the named shape)',
+            'config': {'workload': w.name, 'T': w.T, 'd': d, 'E': E, 'k': k, 'd_ff': F, 'act': w.act,
+                       'score': w.score, 'capacity_factor': w.cf, 'capacity': C,
+                       'n_shared': w.n_shared, 'kept_assignments': kept, 'dropped_assignments': n_dropped},
+            'roofline': roofline,
+            'phases': {kk: {a: (round(bb, 5) if isinstance(bb, float) else bb) for a, bb in v.items()}
+                       for kk, v in phases.items()},
+            'cpu_baseline': cpu}
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, sample_tokens, log):
+    """The oracle as it stands, on the first `sample_tokens` tokens of the same
+    workload taken as a batch of their own (routing, capacity, every expert
+    FFN and the combine, in float64 on the host cores)."""
+    import numpy as np
+    import synth
+    from oracle import moe as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get('num_threads', 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n = sample_tokens or {'mixtral_8x_top2': 256, 'sigmoid_stress': 256}.get(w.name, min(w.T, 1024))
+    ws_ = w.with_(T=n)
+    inp = synth.router_inputs(w)
+    inp = dict(inp, x=inp['x'][:n])
+    experts = [synth.expert_weights(w, e) for e in range(w.E)]
+    shared = [synth.expert_weights(w, s, shared=True) for s in range(w.n_shared)] or None
+    t = time.perf_counter()
+    O.moe_forward(ws_, inp, lambda e: experts[e], (lambda s: shared[s]) if shared else None)
+    el = time.perf_counter() - t
+    log(f'cpu oracle: {n} tokens in {el:.1f}s on {threads} threads')
+    return {'value': round(n / el, 2), 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',
+            'sample': f'the first {n} tokens of the {w.name} workload as one batch (T={n}, same d, E, k, '
+                      f'd_ff and capacity factor); routing, capacity, all expert FFNs and the combine '
+                      f'in float64 numpy; wall {el:.1f}s'}
+
+
+if __name__ == '__main__':
+    main()

@@ -260,8 +260,9 @@ def gelu(u):
 
 
 def silu(u):
+    """SiLU(u) = u * sigmoid(u), with sigmoid(u) = (1 + tanh(u/2)) / 2 (no overflow)."""
     u = np.asarray(u, F64)
-    return u / (1.0 + np.exp(-u))
+    return 0.5 * u * (1.0 + np.tanh(0.5 * u))
 
 
 def expert_ffn(a, wts, act, dtype):

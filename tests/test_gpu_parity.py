@@ -12,8 +12,8 @@ import torch
 import synth
 from oracle import moe as O
 
-from gpu_helpers import (DEV, check_capacity_valid, device_layer, f64_of, forward,
-                         logit_error_bound, maxrel, near_tie_tokens, np_of)
+from gpu_helpers import (DEV, assert_propagated, check_capacity_valid, device_layer, f64_of,
+                         forward, logit_error_bound, maxrel, near_tie_tokens, np_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -306,7 +306,8 @@ def _compare_forward(moe, w, rows=None, **over):
     zg = np_of(out['logits'])
     bound = logit_error_bound(x, inp['w_router'], inp['logit_bias']) + 2.0 ** -24 * np.abs(zr.astype(np.float64))
     assert (np.abs(zg.astype(np.float64) - zr) <= bound).all()
-    near = near_tie_tokens(zr, w.k, w.score, inp['select_bias'], bound)
+    near = near_tie_tokens(zr, zg, w.k, w.score, inp['select_bias'])
+    dz = np.abs(zg.astype(np.float64) - zr).max(axis=1)
     gi = np_of(out['idx'])
     same = (gi == ref['idx']).all(axis=1)
     assert same[~near].all(), np.nonzero(~same & ~near)[0][:10]
@@ -319,14 +320,19 @@ def _compare_forward(moe, w, rows=None, **over):
         np.testing.assert_array_equal(gc, ref['counts'])
         st = np_of(out['stats'])
         assert st.tolist() == [ref['stats'][kk] for kk in ('kept', 'dropped', 'fallback', 'pad')]
-        l = np_of(out['losses'])
-        assert abs(l[0] - ref['l_aux']) <= 1e-5 * abs(ref['l_aux'])
-        assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z'])
+        l = np_of(out['losses']).astype(np.float64)
+        # P_i and LSE^2 move with the logits: first-order propagation of dz
+        slack = 2 * float(dz.mean())
+        assert abs(l[0] - ref['l_aux']) <= (1e-5 + slack) * abs(ref['l_aux'])
+        lse_abs = np.abs(ref['lse'])
+        assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z']) + 2 * float((lse_abs * dz).mean()) + float((dz * dz).mean())
+        say(f'  L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}, L_z {l[1]:.6f} vs {ref["l_z"]:.6f}, max dz {dz.max():.2e}')
     else:
         check_capacity_valid(gi, gs, gd, gc, C, w.E, pr)
-    assert maxrel(np_of(out['gates'])[same], ref['gates'][same]) <= 1e-5
-    assert maxrel(np_of(out['lse']), ref['lse']) <= 1e-5
-    assert maxrel(np_of(out['probs']), ref['probs']) <= 1e-5
+    assert_propagated(np_of(out['gates'])[same], ref['gates'][same], dz[same], what='gates')
+    assert_propagated(np_of(out['probs']), ref['probs'], dz, what='probs')
+    lse_g = np_of(out['lse']).astype(np.float64)
+    assert (np.abs(lse_g - ref['lse']) <= 1e-5 * np.abs(ref['lse']).max() + dz).all()
     rws = ref['rows']
     # rows whose routing and drops match the oracle's are compared
     cmp = same[rws] & (gd[rws] == ref['dropped'][rws]).all(1)
