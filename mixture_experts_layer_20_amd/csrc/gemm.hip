@@ -35,19 +35,38 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kBM = 256;     // token rows per tile
 constexpr int kBW = 256;     // weight rows per tile
-constexpr int kBK = 64;      // k per stage
-constexpr int kRowBytes = kBK * 2;                         // 128
-constexpr int kStageBytes = (kBM + kBW) * kRowBytes;       // 64 KiB
-constexpr int kChunksPerTile = kBM * kBK / 8;              // 2048 16-byte chunks per operand tile
-constexpr int kLoadsPerThread = kChunksPerTile / kThreads; // 8
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 4
+#endif
+constexpr int kBK = MOE_GEMM_BK;          // k per pipeline stage
+constexpr int kStages = MOE_GEMM_STAGES;  // LDS pipeline depth
+constexpr int kRowBytes = kBK * 2;                         // 64
+constexpr int kChunks = kRowBytes / 16;                    // 16-byte k-chunks per row
+constexpr int kStageBytes = (kBM + kBW) * kRowBytes;       // 32 KiB
+constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows one wave instruction fills
+constexpr int kLoadsPerWave = (kBM + kBW) / kRowsPerLoad / 4;  // per stage
 
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
 }
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
+// Byte offset of logical 16-byte k-chunk `chunk` of tile row `row` in LDS:
+// the chunk index is XORed with the row bits above the ones that already
+// separate rows within 128 bytes, so the 16 lanes a 128-bit LDS read serves
+// at once (16 consecutive rows, one logical chunk) hit 16 distinct 16-byte
+// bank groups.
+constexpr int kSwzShift = kRowBytes == 64 ? 2 : 1;
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
+  return row * kRowBytes + ((chunk ^ ((row >> kSwzShift) & (kChunks - 1))) << 4);
+}
+
+// s_waitcnt immediate: vmcnt(n), lgkmcnt(0), expcnt unchanged (gfx9 layout)
+__device__ __forceinline__ constexpr int wait_vm_lgkm0(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4);
 }
 
 struct TileCoord {
@@ -74,11 +93,18 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntil
   return c;
 }
 
+// Buffer resource word 3 for raw (unswizzled, untyped) buffers on gfx9.
+constexpr int kRsrcWord3 = 0x00020000;
+// An offset no buffer reaches: loads from it return zero.
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <int ACT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr bool kGlu = ACT == 2;
   constexpr int kNOut = kGlu ? kBW / 2 : kBW;   // output columns per tile
-  __shared__ __align__(16) uint8_t lds[2 * kStageBytes];
+  __shared__ __align__(1024) uint8_t lds[kStages * kStageBytes];
 
   const int N = a.N, K = a.K;
   const int ntiles = (N + kNOut - 1) / kNOut;
@@ -94,63 +120,93 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 
   const bf16_t* A = static_cast<const bf16_t*>(a.A) + static_cast<int64_t>(tc.g) * a.rows_per_group * K;
   const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + static_cast<int64_t>(tc.g) * N * K;
-  const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + static_cast<int64_t>(tc.g) * N * K : nullptr;
+  const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + static_cast<int64_t>(tc.g) * N * K : B0;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: say so, so that descriptors and LDS bases live
+  // in scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // per-thread element offsets of the 8 + 8 chunks it stages each k-step:
-  // chunk q = tid + 256 i sits at row q/8 = tid/8 + 32 i, column chunk tid%8,
-  // so its swizzled LDS offset is the i = 0 offset + 32 i rows
-  const int c8 = tid & 7;
-  const int lds_x0 = swz(tid >> 3, c8);
-  uint32_t xo[kLoadsPerThread], wo[kLoadsPerThread];
+  // ---- staging: direct global -> LDS, 16 bytes per lane, 1 KiB per
+  // wavefront instruction (kRowsPerLoad rows of kBK k).  Waves 0-1 stage the
+  // 256 token rows, waves 2-3 the 256 weight rows (for SwiGLU: wave 2 the
+  // gate rows, wave 3 the up rows).  Lane i of an instruction fills LDS bytes
+  // [16i, 16i+16) of its row block: row i/kChunks, physical chunk i%kChunks,
+  // which holds logical k-chunk (i%kChunks) ^ swizzle(row).  Rows past the
+  // operand's end (ragged expert rows, columns past N) and k past K read as
+  // zero through the buffer bounds.
+  const bool stage_x = wave < 2;
+  const int lr = lane / kChunks, pc = lane % kChunks;
+  const int row0 = (wave & 1) * 128;               // first tile row this wave stages
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[kLoadsPerWave];
+  int kcol[kLoadsPerWave];
+  {
+    const bf16_t* base = stage_x ? A : ((kGlu && wave == 2) ? B1 : B0);
+    const int64_t nbytes = stage_x ? rows_g * K * 2 : static_cast<int64_t>(N) * K * 2;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0,
+                                             static_cast<int>(nbytes), kRsrcWord3);
+    // first operand row of this wave's block 0 (token rows: m0; weight rows:
+    // n0, plus 128 for the second half when not SwiGLU)
+    const int orow0 = stage_x ? m0 + row0 : (kGlu ? n0 : n0 + row0);
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    const int64_t m = min<int64_t>(m0 + row, rows_g - 1);
-    xo[i] = static_cast<uint32_t>(m * K + c8 * 8);
-    int n;
-    if (kGlu) {
-      // rows 0..127 (i < 4) come from the gate matrix B1, rows 128..255 from B0
-      n = min(n0 + (row & 127), N - 1);
-    } else {
-      n = min(n0 + row, N - 1);
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+      const int trow = row0 + j * kRowsPerLoad + lr;             // tile row (sets the swizzle)
+      const int c = pc ^ ((trow >> kSwzShift) & (kChunks - 1));
+      kcol[j] = c * 8;
+      // weight rows past N land past the buffer's end and read as zero
+      voff[j] = static_cast<uint32_t>((orow0 + j * kRowsPerLoad + lr) * K + c * 8) * 2u;
     }
-    wo[i] = static_cast<uint32_t>(static_cast<int64_t>(n) * K + c8 * 8);
   }
-  const int kchunk = c8 * 8;
+  uint8_t* stage_region = lds + (stage_x ? 0 : kBM * kRowBytes) + row0 * kRowBytes;
 
-  uint4 px[kLoadsPerThread], pw[kLoadsPerThread];
-  auto gload = [&](int kt) {
+  // stage kt goes to LDS buffer kt % kStages; a stage past the end (valid
+  // false) loads zeros so that every iteration has the same shape
+  // When K is a multiple of kBK no chunk passes K, so the k offset goes in
+  // the scalar offset (the bounds check sees only the row offset, which is
+  // what separates valid rows) and the per-lane offsets stay fixed.
+  const bool k_full = (K % kBK) == 0;
+  auto issue_stage = [&](int kt, bool valid) {
     const int k0 = kt * kBK;
-    const bool ok = k0 + kchunk < K;
+    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+    uint8_t* dst = stage_region + (kt % kStages) * kStageBytes;
+    if (k_full) {
+      const int soff = valid ? static_cast<int>(kb) : 0;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      const bf16_t* wb = kGlu ? (i < kLoadsPerThread / 2 ? B1 : B0) : B0;
-      px[i] = ok ? *reinterpret_cast<const uint4*>(A + xo[i] + k0) : make_uint4(0, 0, 0, 0);
-      pw[i] = ok ? *reinterpret_cast<const uint4*>(wb + wo[i] + k0) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* s = lds + buf * kStageBytes;
+      for (int j = 0; j < kLoadsPerWave; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
+                                                 valid ? voff[j] : kOutOfRange, soff, 0, 0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      *reinterpret_cast<uint4*>(s + lds_x0 + i * 32 * kRowBytes) = px[i];
-      *reinterpret_cast<uint4*>(s + kBM * kRowBytes + lds_x0 + i * 32 * kRowBytes) = pw[i];
+      for (int j = 0; j < kLoadsPerWave; ++j) {
+        const bool ok = valid && k0 + kcol[j] < K;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
+                                                 ok ? voff[j] + kb : kOutOfRange, 0, 0, 0);
+      }
     }
   };
 
-  // wave layout: 2 x 2 wavefronts, each 128 weight rows x 128 token rows
+  // ---- fragments: wave (wn, wm) owns 128 weight rows x 128 token rows
   const int wn = wave & 1, wm = wave >> 1;
-  int wrow[4];
+  int wrow[4], xrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     wrow[i] = kGlu ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + (lane & 31))
                    : (wn * 128 + i * 32 + (lane & 31));
-  int xrow[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) xrow[j] = wm * 128 + j * 32 + (lane & 31);
+
+  bf16x8_t wf[2][4], xf[2][4];
+  auto load_frags = [&](int stage, int ks, int slot) {
+    const uint8_t* s = lds + (stage % kStages) * kStageBytes;
+    const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wf[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + kBM * kRowBytes + swz(wrow[i], c)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xf[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + swz(xrow[j], c)));
+  };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -160,33 +216,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (K + kBK - 1) / kBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* s = lds + buf * kStageBytes;
+  auto mfmas = [&](int slot) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
-      bf16x8_t wf[4], xf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + kBM * kRowBytes + swz(wrow[i], c)));
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + swz(xrow[j], c)));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][i], xf[slot][j], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- pipeline: stages kt+1 .. kt+kStages-1 are in flight while stage kt
+  // is multiplied.
+  constexpr int kSteps = kBK / 16;
+  static_assert(kSteps % 2 == 0, "fragment slots alternate per 16-k step");
+  const int nk = (K + kBK - 1) / kBK;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int st = 0; st < kStages - 1; ++st) issue_stage(st, st < nk);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
+  __builtin_amdgcn_s_barrier();
+  load_frags(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    issue_stage(kt + kStages - 1, kt + kStages - 1 < nk);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < kSteps) {
+        load_frags(kt, ks + 1, cur ^ 1);
+        mfmas(cur);
+        // interleave: one fragment read after each of the first 8 MFMAs
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      } else {
+        // last step of the stage: wait for stage kt+1 (own loads), make
+        // everyone's visible, start reading it, and multiply meanwhile
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
+        __builtin_amdgcn_s_barrier();
+        load_frags(kt + 1, 0, cur ^ 1);
+        mfmas(cur);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
+  // the last issue_stage calls loaded zeros past the end; drain them
+  __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane holds, for block (i, j), output columns
   // nbase + 8q + 4*(lane/32) + {0..3} of token row mbase + lane%32
