@@ -128,7 +128,7 @@ def main():
     slot = torch.empty_like(out['slot'])
     dropped = torch.empty_like(out['dropped'])
     counts = torch.empty_like(out['counts'])
-    xe = torch.empty(E, C, d, dtype=dt, device=dev)
+    row_token = torch.empty(E, C, dtype=torch.int32, device=dev)
     h = torch.empty(E, C, F, dtype=dt, device=dev)
     ye = torch.empty(E, C, d, dtype=dt, device=dev)
     y = torch.empty_like(out['y'])
@@ -151,16 +151,18 @@ def main():
     for rep in range(args.phase_reps + 1):
         timed('route', lambda: moe.moe_route(cfg, x, weights['w_router'], weights['logit_bias'],
                                              weights['select_bias'], None, None, idx, gates, None, ws))
-        timed('dispatch', lambda: moe.moe_dispatch(cfg, x, idx, slot, dropped, counts, None, xe, ws))
+        # capacity slots and the token list of every expert (the layer gathers
+        # token rows inside the expert GEMM, so nothing is copied here)
+        timed('dispatch', lambda: moe.moe_dispatch(cfg, None, idx, slot, dropped, counts, row_token, None, ws))
         torch.clamp(counts, max=C, out=kept_rows)
         if w.act == 'swiglu':
-            timed('expert_ffn', lambda: moe.moe_expert_ffn(cfg, 'swiglu', E, C, kept_rows, xe, weights['w_in'],
+            timed('expert_ffn', lambda: moe.moe_expert_ffn(cfg, 'swiglu', E, C, kept_rows, x, weights['w_in'],
                                                            weights['w_gate'], None, weights['w_out'], None,
-                                                           F, h, ye))
+                                                           F, h, ye, gather=row_token))
         else:
-            timed('expert_ffn', lambda: moe.moe_expert_ffn(cfg, 'gelu', E, C, kept_rows, xe, weights['w_in'],
+            timed('expert_ffn', lambda: moe.moe_expert_ffn(cfg, 'gelu', E, C, kept_rows, x, weights['w_in'],
                                                            None, weights.get('b_in'), weights['w_out'],
-                                                           weights.get('b_out'), F, h, ye))
+                                                           weights.get('b_out'), F, h, ye, gather=row_token))
         if fs:
             timed('shared_ffn', lambda: moe.moe_expert_ffn(cfg, 'gelu', 1, T, None, x, weights['ws_in'], None,
                                                            weights['bs_in'], weights['ws_out'], weights['bs_out'],
@@ -175,7 +177,8 @@ def main():
     ffn_flops = 2.0 * n_kept * mult * d * F
     sh_flops = 2.0 * T * 2 * d * fs
     bytes_route = T * d * b + d * E * 4 + T * k * 8 + ((T + 31) // 32) * (E + 1) * 8
-    bytes_dispatch = T * k * 4 + n_tok_kept * d * b + n_kept * d * b + T * k * 5
+    # slots only: idx in; slot, dropped, row_token out (+ the tile histograms)
+    bytes_dispatch = T * k * 4 + T * k * 5 + n_kept * 4
     bytes_combine = n_kept * d * b + (0 if fs else n_fb * d * b) + (T * d * b if fs else 0) + T * d * b + T * k * 13
     peak = PEAK_BF16_TFLOPS if w.dtype == 'bf16' else PEAK_F32_TFLOPS
 

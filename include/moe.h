@@ -140,25 +140,34 @@ MOE_API moe_status moe_dispatch(const moe_config* cfg, const void* x, const int3
  * ["Lab 18" s.1 experts, Tips (one grouped matrix multiply over all
  * experts); "Mixture of experts" lecture, expert geometry].
  *   groups          number of experts in this call
- *   rows_per_group  row stride between groups in a, h and out (C for the
- *                   dispatched buffer; T for shared experts with groups = 1)
+ *   rows_per_group  row stride between groups in h and out (and in a when
+ *                   not gathered): C for dispatched buffers, T for shared
+ *                   experts with groups = 1
  *   rows            [groups] int32 rows to compute in each group (e.g. the
- *                   counts of moe_dispatch, clamped to rows_per_group), or
+ *                   counts of moe_dispatch; clamped to rows_per_group), or
  *                   NULL for all rows_per_group rows
- *   a               [groups*rows_per_group, d] storage type
+ *   a               the input rows, storage type: [groups*rows_per_group, d],
+ *                   or, with `gather`, the whole [a_rows, d] token matrix
+ *   gather          [groups*rows_per_group] int32 or NULL: row m of group g
+ *                   is a[gather[g*rows_per_group + m]] (e.g. the row_token
+ *                   of moe_dispatch), read straight into the GEMM tiles so
+ *                   no dispatched copy of x is needed; entries at or past
+ *                   rows[g] are not read
+ *   a_rows          rows of a when gathered (ignored otherwise)
  *   act             moe_act: GELU  h = GELU(a w_in^T + b_in), out = h w_out^T + b_out
- *                            SwiGLU h = SiLU(a w_gate^T) * (a w_up^T), out = h w_out^T
- *   w_in            [groups,F,d] (GELU: w_in; SwiGLU: w_up)
+ *                            SwiGLU h = SiLU(a w_gate^T) * (a w_in^T), out = h w_out^T
+ *   w_in            [groups,F,d] (GELU: w_in; SwiGLU: the up projection)
  *   w_gate          [groups,F,d] SwiGLU gate projection, NULL for GELU
  *   b_in            [groups,F] or NULL;   w_out [groups,d,F];  b_out [groups,d] or NULL
  *   h               [groups*rows_per_group, F] hidden activations (storage type)
  *   out             [groups*rows_per_group, d] expert outputs (storage type)
- * Rows at or beyond rows[g] are neither read nor written. */
+ * Rows at or beyond rows[g] are neither read nor written.  Every operand one
+ * launch addresses must hold < 2^30 elements per group (MOE_EINVAL). */
 MOE_API moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups,
-                          int64_t rows_per_group, const int32_t* rows, const void* a,
-                          const void* w_in, const void* w_gate, const void* b_in,
-                          const void* w_out, const void* b_out, int32_t F, void* h, void* out,
-                          void* stream);
+                                  int64_t rows_per_group, const int32_t* rows, const void* a,
+                                  const int32_t* gather, int64_t a_rows, const void* w_in,
+                                  const void* w_gate, const void* b_in, const void* w_out,
+                                  const void* b_out, int32_t F, void* h, void* out, void* stream);
 
 /* Gate-weighted combine with residual fallback ["Lab 18" s.1 layer equation
  * and s.3; "Lab 01" "Where to start" 5; "Phase 02" concept map].

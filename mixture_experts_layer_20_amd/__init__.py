@@ -64,8 +64,8 @@ def _load():
         'moe_workspace_bytes': (ctypes.c_size_t, [cfgp]),
         'moe_route': (st, [cfgp] + [_P] * 11),
         'moe_dispatch': (st, [cfgp] + [_P] * 9),
-        'moe_expert_ffn': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P,
-                                _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
+        'moe_expert_ffn': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
+                                ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
         'moe_combine': (st, [cfgp] + [_P] * 9),
         'moe_aux_losses': (st, [cfgp, _P, _P, _P, _P, _P]),
         'moe_forward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs),
@@ -192,10 +192,14 @@ def moe_dispatch(cfg, x, idx, slot, dropped, counts, row_token, xe, ws, stream=N
 
 
 def moe_expert_ffn(cfg, act, groups, rows_per_group, rows, a, w_in, w_gate, b_in, w_out, b_out, F,
-                   h, out, stream=None):
+                   h, out, stream=None, gather=None):
+    """``gather`` (optional, int32 [groups*rows_per_group]): row m of group g is
+    a[gather[g*rows_per_group + m]]; ``a`` is then the whole token matrix."""
     dt = torch_dtype(cfg)
+    a_rows = a.shape[0] if gather is not None else 0
     _check(_lib.moe_expert_ffn(ctypes.byref(cfg), _enum('act', act), groups, rows_per_group,
                                _ptr(rows, 'rows', torch.int32), _ptr(a, 'a', dt),
+                               _ptr(gather, 'gather', torch.int32), a_rows,
                                _ptr(w_in, 'w_in', dt), _ptr(w_gate, 'w_gate', dt),
                                _ptr(b_in, 'b_in', dt), _ptr(w_out, 'w_out', dt),
                                _ptr(b_out, 'b_out', dt), F, _ptr(h, 'h', dt), _ptr(out, 'out', dt),

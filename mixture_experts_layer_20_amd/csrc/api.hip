@@ -102,10 +102,10 @@ struct Workspace {
   double* p_partial;
   double* lse2_partial;
   int32_t* fallback_partial;
+  double* psum;
   int32_t* idx_tmp;
   float* gates_tmp;
   int32_t* row_token;
-  void* xe;
   void* h;
   void* ye;
   void* hs;
@@ -134,10 +134,11 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   w.p_partial = static_cast<double*>(take(sizeof(double) * n_rtiles * c.E));
   w.lse2_partial = static_cast<double*>(take(sizeof(double) * n_rtiles));
   w.fallback_partial = static_cast<int32_t*>(take(sizeof(int32_t) * n_tiles));
+  w.psum = static_cast<double*>(take(sizeof(double) * (c.E + 1)));
   w.idx_tmp = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
   w.gates_tmp = static_cast<float*>(take(sizeof(float) * c.T * c.k));
   w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * c.E * C));
-  w.xe = take(ds * c.E * C * c.d);
+
   w.h = take(ds * c.E * C * c.d_ff);
   w.ye = take(ds * c.E * C * c.d);
   w.hs = fs > 0 ? take(ds * c.T * fs) : nullptr;
@@ -172,35 +173,42 @@ CapArgs cap_args(const moe_config& c, int64_t C, const Workspace& w) {
   a.k = c.k;
   a.d = c.d;
   a.n_tiles = static_cast<int>((c.T + kTileTokens - 1) / kTileTokens);
+  a.n_rtiles = static_cast<int>((c.T + kRouteTokens - 1) / kRouteTokens);
   a.token_major = c.priority == MOE_TOKEN_MAJOR;
   return a;
 }
 
 LossArgs loss_args(const moe_config& c, int64_t C, const Workspace& w, const int32_t* counts) {
   LossArgs l{};
-  l.p_partial = w.p_partial;
-  l.lse2_partial = w.lse2_partial;
+  l.psum = w.psum;
   l.counts = counts;
   l.fallback_partial = w.fallback_partial;
   l.T = c.T;
   l.C = C;
   l.E = c.E;
   l.k = c.k;
-  l.n_rtiles = static_cast<int>((c.T + kRouteTokens - 1) / kRouteTokens);
   l.n_tiles = static_cast<int>((c.T + kTileTokens - 1) / kTileTokens);
   l.has_shared = c.n_shared > 0;
   return l;
 }
 
+// Expert FFN on `groups` groups of rows: h = act(a w_in^T (+ b_in)) (or the
+// SwiGLU pair), out = h w_out^T (+ b_out).  With `gather`, row m of group g
+// is row gather[g*rpg + m] of a ([a_rows, d]).
 moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int32_t* rows, const void* a,
-               const void* w_in, const void* w_gate, const void* b_in, const void* w_out, const void* b_out,
-               int F, void* h, void* out, hipStream_t s) {
-  // element offsets inside one group are 32-bit in the GEMM kernels
-  const int64_t lim = int64_t{1} << 31;
-  if (rpg * c.d >= lim || rpg * F >= lim || static_cast<int64_t>(F) * c.d >= lim)
-    return fail(MOE_EINVAL, "one expert's operands must hold < 2^31 elements");
+               const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate,
+               const void* b_in, const void* w_out, const void* b_out, int F, void* h, void* out,
+               hipStream_t s) {
+  // each operand a GEMM launch addresses through one buffer descriptor stays
+  // below 2^30 elements (2^31 bytes)
+  const int64_t lim = int64_t{1} << 30;
+  if (rpg * c.d >= lim || rpg * F >= lim || static_cast<int64_t>(F) * c.d >= lim ||
+      (gather && a_rows * c.d >= lim))
+    return fail(MOE_EINVAL, "one expert's operands must hold < 2^30 elements");
   GemmArgs g1{};
   g1.A = a;
+  g1.gather = gather;
+  g1.a_rows = a_rows;
   g1.B0 = w_in;
   g1.B1 = w_gate;
   g1.bias = act == MOE_SWIGLU ? nullptr : b_in;
@@ -307,9 +315,9 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups, int64_t rows_per_group,
-                          const int32_t* rows, const void* a, const void* w_in, const void* w_gate,
-                          const void* b_in, const void* w_out, const void* b_out, int32_t F, void* h, void* out,
-                          void* stream) {
+                          const int32_t* rows, const void* a, const int32_t* gather, int64_t a_rows,
+                          const void* w_in, const void* w_gate, const void* b_in, const void* w_out,
+                          const void* b_out, int32_t F, void* h, void* out, void* stream) {
   MOE_TRY(validate(cfg, nullptr));
   const moe_config& c = *cfg;
   if (act != MOE_GELU && act != MOE_SWIGLU) return fail(MOE_EINVAL, "unknown act %d", act);
@@ -323,14 +331,16 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups, in
   MOE_TRY(check_ptr(h, "h", 16));
   MOE_TRY(check_ptr(out, "out", 16));
   MOE_TRY(check_ptr(rows, "rows", 4, false));
+  MOE_TRY(check_ptr(gather, "gather", 4, false));
+  if (gather && a_rows <= 0) return fail(MOE_EINVAL, "a_rows must be > 0 when gathering");
   MOE_TRY(check_ptr(b_in, "b_in", dsize(c), false));
   MOE_TRY(check_ptr(b_out, "b_out", dsize(c), false));
   if (act == MOE_SWIGLU) {
     MOE_TRY(check_ptr(w_gate, "w_gate", 16));
     if (b_in) return fail(MOE_EUNSUPPORTED, "SwiGLU experts take no b_in");
   }
-  return ffn(c, act, groups, rows_per_group, rows, a, w_in, w_gate, b_in, w_out, b_out, F, h, out,
-             static_cast<hipStream_t>(stream));
+  return ffn(c, act, groups, rows_per_group, rows, a, gather, a_rows, w_in, w_gate, b_in, w_out, b_out, F, h,
+             out, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_config* cfg, const void* x, const void* ye, const void* shared_out,
@@ -391,6 +401,9 @@ moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int3
   a.slot = w.idx_tmp;                         // scratch, overwritten
   a.dropped = reinterpret_cast<uint8_t*>(w.gates_tmp);
   a.fallback_partial = nullptr;
+  a.p_partial = w.p_partial;
+  a.lse2_partial = w.lse2_partial;
+  a.psum = w.psum;
   MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "aux-loss counts"));
   LossArgs l = loss_args(c, C, w, w.counts_tmp);
   l.fallback_partial = nullptr;
@@ -456,16 +469,21 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   a.slot = out->slot;
   a.dropped = out->dropped;
   a.row_token = w.row_token;
-  a.x = x;
-  a.xe = w.xe;
+  a.p_partial = w.p_partial;
+  a.lse2_partial = w.lse2_partial;
+  a.psum = w.psum;
+  // the up-projection gathers token rows straight into its tiles through
+  // row_token, so no dispatched copy of x is made
+  a.x = nullptr;
+  a.xe = nullptr;
   MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "capacity"));
 
   if (C > 0)
-    MOE_TRY(ffn(c, c.act, c.E, C, w.kept, w.xe, wt->w_in, wt->w_gate, wt->b_in, wt->w_out, wt->b_out, c.d_ff, w.h,
-                w.ye, s));
+    MOE_TRY(ffn(c, c.act, c.E, C, w.kept, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in, wt->w_out,
+                wt->b_out, c.d_ff, w.h, w.ye, s));
   if (c.n_shared > 0 && c.T > 0)
-    MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, wt->ws_in, nullptr, wt->bs_in, wt->ws_out, wt->bs_out,
-                c.n_shared * c.d_ff_shared, w.hs, w.s, s));
+    MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt->ws_in, nullptr, wt->bs_in, wt->ws_out,
+                wt->bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s));
 
   CombineArgs cb{};
   cb.x = x;

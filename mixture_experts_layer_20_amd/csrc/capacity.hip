@@ -107,6 +107,30 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(CapArgs a) {
     a.counts[e] = total;
     if (a.kept) a.kept[e] = static_cast<int>(min<int64_t>(total, a.C));
   }
+  // the router's per-workgroup partial sums of P_e (and, in block 0, of
+  // LSE^2), reduced in a fixed order: strided per thread, then a fixed tree
+  if (a.p_partial) {
+    __shared__ double dred[kThreads];
+    auto reduce = [&](auto load) {
+      double v = 0.0;
+      for (int r = tid; r < a.n_rtiles; r += kThreads) v += load(r);
+      dred[tid] = v;
+      __syncthreads();
+      for (int o = kThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) dred[tid] += dred[tid + o];
+        __syncthreads();
+      }
+      const double out = dred[0];
+      __syncthreads();
+      return out;
+    };
+    const double P = reduce([&](int r) { return a.p_partial[static_cast<int64_t>(r) * a.E + e]; });
+    if (tid == 0) a.psum[e] = P;
+    if (e == 0) {
+      const double z2 = reduce([&](int r) { return a.lse2_partial[r]; });
+      if (tid == 0) a.psum[a.E] = z2;
+    }
+  }
 }
 
 template <typename XT>

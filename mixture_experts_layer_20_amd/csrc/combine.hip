@@ -12,7 +12,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokensPerBlock = 4;
+constexpr int kTokensPerBlock = 8;
 
 template <typename T>
 struct Vec;  // 16 bytes of storage as float32 lanes
@@ -50,31 +50,48 @@ template <> struct Vec<float> {
 
 // y_t = sum_{j kept} g_tj * ye[e_tj, s_tj] (+ shared_t), float32 in j order,
 // one rounding; fallback x_t (or 0) when nothing was kept and no shared expert.
+// A workgroup takes kTokensPerBlock tokens; their (row, gate) lists are staged
+// in LDS first, then every thread streams 16-byte chunks: all kept rows of a
+// token are loaded before they are summed.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   constexpr int V = Vec<T>::N;
+  __shared__ int64_t rows[kTokensPerBlock][32];
+  __shared__ float gts[kTokensPerBlock][32];
+  __shared__ int nkept[kTokensPerBlock];
   const int nvec = a.d / V;
   const int64_t rowbytes = static_cast<int64_t>(a.d) * sizeof(T);
-  const char* ye = static_cast<const char*>(a.ye);
-  const char* x = static_cast<const char*>(a.x);
-  const char* sh = static_cast<const char*>(a.shared_out);
-  char* y = static_cast<char*>(a.y);
-  for (int i = 0; i < kTokensPerBlock; ++i) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + i;
-    if (t >= a.T) return;
-    const int64_t tk = t * a.k;
-    // a choice counts only if it is kept and its (expert, slot) is in range
-    auto kept = [&](int j) {
-      const int e = a.idx[tk + j];
-      const int s = a.slot[tk + j];
-      return !a.dropped[tk + j] && e >= 0 && e < a.E && s >= 0 && s < a.C;
-    };
-    bool any = false;
-    for (int j = 0; j < a.k; ++j) any = any || kept(j);
+  const char* __restrict__ ye = static_cast<const char*>(a.ye);
+  const char* __restrict__ x = static_cast<const char*>(a.x);
+  const char* __restrict__ sh = static_cast<const char*>(a.shared_out);
+  char* __restrict__ y = static_cast<char*>(a.y);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock;
+  const int nt = static_cast<int>(min<int64_t>(kTokensPerBlock, a.T - t0));
+  if (threadIdx.x < kTokensPerBlock) {
+    const int i = threadIdx.x;
+    int n = 0;
+    if (i < nt) {
+      const int64_t tk = (t0 + i) * a.k;
+      for (int j = 0; j < a.k; ++j) {
+        // a choice counts only if it is kept and its (expert, slot) is in range
+        const int e = a.idx[tk + j];
+        const int sl = a.slot[tk + j];
+        if (a.dropped[tk + j] || e < 0 || e >= a.E || sl < 0 || sl >= a.C) continue;
+        rows[i][n] = static_cast<int64_t>(e) * a.C + sl;
+        gts[i][n] = a.gates[tk + j];
+        ++n;
+      }
+    }
+    nkept[i] = n;
+  }
+  __syncthreads();
+  for (int i = 0; i < nt; ++i) {
+    const int64_t t = t0 + i;
+    const int n = nkept[i];
     for (int c = threadIdx.x; c < nvec; c += kThreads) {
       const int64_t off = static_cast<int64_t>(c) * 16;
       float acc[V];
-      if (!any && sh == nullptr) {
+      if (n == 0 && sh == nullptr) {
         if (a.zero_fallback) {
 #pragma unroll
           for (int q = 0; q < V; ++q) acc[q] = 0.0f;
@@ -84,14 +101,19 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       } else {
 #pragma unroll
         for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-        for (int j = 0; j < a.k; ++j) {
-          if (!kept(j)) continue;
-          const int64_t row = static_cast<int64_t>(a.idx[tk + j]) * a.C + a.slot[tk + j];
-          const float g = a.gates[tk + j];
-          float v[V];
-          Vec<T>::load(ye + row * rowbytes + off, v);
+        for (int j0 = 0; j0 < n; j0 += 4) {
+          float v[4][V];
 #pragma unroll
-          for (int q = 0; q < V; ++q) acc[q] += g * v[q];
+          for (int u = 0; u < 4; ++u)
+            if (j0 + u < n) Vec<T>::load(ye + rows[i][j0 + u] * rowbytes + off, v[u]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (j0 + u < n) {
+              const float g = gts[i][j0 + u];
+#pragma unroll
+              for (int q = 0; q < V; ++q) acc[q] += g * v[u][q];
+            }
+          }
         }
         if (sh) {
           float v[V];
@@ -105,53 +127,44 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
-// One workgroup: fixed-order float64 reductions of the router partials and
-// the capacity counts into L_aux, L_z and the drop statistics.
+// One workgroup: L_aux = E * sum_i f_i P_i and L_z from the per-expert sums
+// the capacity scan reduced, plus the drop statistics; fixed-order trees.
 __global__ __launch_bounds__(kThreads) void losses_kernel(LossArgs a) {
   __shared__ double red[kThreads];
   __shared__ long long ired[kThreads];
+  __shared__ long long fred[kThreads];
   const int tid = threadIdx.x;
-  // per-expert mean probability P_i, times f_i
+  const double T = static_cast<double>(a.T);
   double fp = 0.0;
   long long kept = 0;
-  for (int e = tid; e < a.E && a.T > 0; e += kThreads) {
-    double P = 0.0;
-    for (int r = 0; r < a.n_rtiles; ++r) P += a.p_partial[static_cast<int64_t>(r) * a.E + e];
-    const double T = static_cast<double>(a.T);
-    const double f = static_cast<double>(a.counts[e]) / (T * a.k);
-    fp += f * (P / T);
+  for (int e = tid; e < a.E; e += kThreads) {
+    if (a.T > 0) fp += (static_cast<double>(a.counts[e]) / (T * a.k)) * (a.psum[e] / T);
     kept += min<long long>(a.counts[e], a.C);
   }
-  red[tid] = fp;
-  ired[tid] = kept;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) { red[tid] += red[tid + o]; ired[tid] += ired[tid + o]; }
-    __syncthreads();
-  }
-  const double l_aux = static_cast<double>(a.E) * red[0];
-  const long long n_kept = ired[0];
-  __syncthreads();
-  double z2 = 0.0;
   long long fb = 0;
-  for (int r = tid; r < a.n_rtiles; r += kThreads) z2 += a.lse2_partial[r];
   if (a.fallback_partial)
     for (int r = tid; r < a.n_tiles; r += kThreads) fb += a.fallback_partial[r];
-  red[tid] = z2;
-  ired[tid] = fb;
+  red[tid] = fp;
+  ired[tid] = kept;
+  fred[tid] = fb;
   __syncthreads();
   for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) { red[tid] += red[tid + o]; ired[tid] += ired[tid + o]; }
+    if (tid < o) {
+      red[tid] += red[tid + o];
+      ired[tid] += ired[tid + o];
+      fred[tid] += fred[tid + o];
+    }
     __syncthreads();
   }
   if (tid == 0) {
-    a.losses[0] = static_cast<float>(l_aux);
-    a.losses[1] = a.T > 0 ? static_cast<float>(red[0] / static_cast<double>(a.T)) : 0.0f;
+    const long long n_kept = ired[0];
+    a.losses[0] = static_cast<float>(static_cast<double>(a.E) * red[0]);
+    a.losses[1] = a.T > 0 ? static_cast<float>(a.psum[a.E] / T) : 0.0f;
     if (a.stats) {
       const long long total = a.T * a.k;
       a.stats[0] = static_cast<int32_t>(n_kept);
       a.stats[1] = static_cast<int32_t>(total - n_kept);
-      a.stats[2] = a.has_shared ? 0 : static_cast<int32_t>(ired[0]);
+      a.stats[2] = a.has_shared ? 0 : static_cast<int32_t>(fred[0]);
       a.stats[3] = static_cast<int32_t>(static_cast<long long>(a.E) * a.C - n_kept);
     }
   }

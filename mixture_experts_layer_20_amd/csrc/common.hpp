@@ -109,13 +109,18 @@ struct CapArgs {
   int32_t* fallback_partial;  // [n_tiles] | null
   const void* x;              // [T,d] | null
   void* xe;                   // [E,C,d] | null
+  const double* p_partial;    // [n_rtiles, E] router partial sums of P_i | null
+  const double* lse2_partial; // [n_rtiles] | null
+  double* psum;               // [E + 1]: sum_t P_ti per expert, then sum_t LSE_t^2
   int64_t T, C;
-  int E, k, d, n_tiles;
+  int E, k, d, n_tiles, n_rtiles;
   int token_major;
 };
 
 struct GemmArgs {
-  const void* A;              // [groups*rows_per_group, K]
+  const void* A;              // [groups*rows_per_group, K], or [a_rows, K] when gathered
+  const int32_t* gather;      // [groups*rows_per_group] row of A for each (group, row) | null
+  int64_t a_rows;             // rows of A when gathered
   const void* B0;             // [groups, N, K]
   const void* B1;             // [groups, N, K] (SwiGLU gate) | null
   const void* bias;           // [groups, N] | null
@@ -141,14 +146,13 @@ struct CombineArgs {
 };
 
 struct LossArgs {
-  const double* p_partial;    // [n_rtiles, E]
-  const double* lse2_partial; // [n_rtiles]
+  const double* psum;         // [E + 1] from the capacity scan
   const int32_t* counts;      // [E]
   const int32_t* fallback_partial;  // [n_tiles] | null
   float* losses;              // [2]
   int32_t* stats;             // [4] | null
   int64_t T, C;
-  int E, k, n_rtiles, n_tiles;
+  int E, k, n_tiles;
   int has_shared;
 };
 

@@ -15,12 +15,17 @@
 //   * The MFMA's first operand is the weight tile and its second the token
 //     tile, so each lane ends with four consecutive output columns of one
 //     token row: 8-byte bf16 stores.
-//   * Global -> registers -> LDS, double-buffered, one barrier per k-step;
-//     16-byte chunks XOR-swizzled by row so fragment reads spread over banks.
-//   * Tile order: blocks are dealt round-robin to the 8 XCDs, so block b is
-//     remapped to logical tile (b mod 8) * (grid/8) + b/8; logical tiles walk
-//     groups of 4 row-tiles column by column, so the ~32 tiles an XCD runs at
-//     once share 4 token panels and 8 weight panels in its L2.
+//   * Direct global -> LDS loads (buffer_load ... lds), kStages k-stages of
+//     kBK in flight, one barrier per stage; 16-byte chunks XOR-swizzled by row
+//     so fragment reads spread over the LDS banks.  Token rows may be
+//     gathered through a row list (the dispatch is fused into this load).
+//   * Tile order: logical tiles walk groups of 4 row tiles column by column,
+//     and 32-tile chunks of them are dealt round-robin to the 8 XCDs (blocks
+//     reach XCDs round-robin), so the ~32 tiles an XCD runs at once share 4
+//     token panels and 8 weight panels in its L2 while every XCD gets an even
+//     share of every expert.
+//   * A tail tile (at most 128 valid token rows) splits the weight rows four
+//     ways across the waves and skips empty 32-row token blocks.
 //   * Rows at or past rows[g] are never stored; their loads are clamped to a
 //     valid row.  Columns past N are clamped and not stored; k past K reads 0.
 // float32 path: a plain LDS-tiled FMA kernel (small layers only).
@@ -95,8 +100,9 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntil
 
 // Buffer resource word 3 for raw (unswizzled, untyped) buffers on gfx9.
 constexpr int kRsrcWord3 = 0x00020000;
-// An offset no buffer reaches: loads from it return zero.
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+// An offset past every operand (operands are kept below 2^31 bytes), which
+// stays past them after a stage's k offset is added: loads from it read zero.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -109,8 +115,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int N = a.N, K = a.K;
   const int ntiles = (N + kNOut - 1) / kNOut;
   const int mt_max = static_cast<int>((a.rows_per_group + kBM - 1) / kBM);
-  const int64_t nb8 = gridDim.x / 8;
-  const int64_t L = static_cast<int64_t>(blockIdx.x % 8) * nb8 + blockIdx.x / 8;
+  // blocks are dealt round-robin to the 8 XCDs: block b runs on XCD b%8 as
+  // that XCD's (b/8)-th block.  XCD x takes the 32-tile chunks x, x+8, x+16,
+  // ... in turn, so each XCD works on one chunk (4 row tiles x 8 column
+  // tiles, sharing 4 token panels and 8 weight panels in its L2) at a time
+  // and every XCD gets an even share of every expert.  The grid is a multiple
+  // of 256 blocks.
+  const int64_t p = blockIdx.x / 8;
+  const int64_t L = ((p / 32) * 8 + blockIdx.x % 8) * 32 + p % 32;
   const TileCoord tc = decode_tile(L, mt_max, ntiles, a.groups);
   if (!tc.valid) return;
   const int64_t rows_g = a.rows ? min<int64_t>(a.rows[tc.g], a.rows_per_group) : a.rows_per_group;
@@ -118,7 +130,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   if (m0 >= rows_g) return;
   const int n0 = tc.nt * kNOut;
 
-  const bf16_t* A = static_cast<const bf16_t*>(a.A) + static_cast<int64_t>(tc.g) * a.rows_per_group * K;
+  // token rows: contiguous per group, or gathered through a.gather (then A
+  // is the whole [a_rows, K] input and row m of group g is A[gather[g*rpg+m]])
+  const bool gathered = a.gather != nullptr;
+  const bf16_t* A = static_cast<const bf16_t*>(a.A) +
+                    (gathered ? 0 : static_cast<int64_t>(tc.g) * a.rows_per_group * K);
   const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + static_cast<int64_t>(tc.g) * N * K;
   const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + static_cast<int64_t>(tc.g) * N * K : B0;
 
@@ -143,7 +159,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   int kcol[kLoadsPerWave];
   {
     const bf16_t* base = stage_x ? A : ((kGlu && wave == 2) ? B1 : B0);
-    const int64_t nbytes = stage_x ? rows_g * K * 2 : static_cast<int64_t>(N) * K * 2;
+    const int64_t nbytes = stage_x ? (gathered ? a.a_rows : rows_g) * K * 2
+                                   : static_cast<int64_t>(N) * K * 2;
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0,
                                              static_cast<int>(nbytes), kRsrcWord3);
     // first operand row of this wave's block 0 (token rows: m0; weight rows:
@@ -154,8 +171,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
       const int trow = row0 + j * kRowsPerLoad + lr;             // tile row (sets the swizzle)
       const int c = pc ^ ((trow >> kSwzShift) & (kChunks - 1));
       kcol[j] = c * 8;
-      // weight rows past N land past the buffer's end and read as zero
-      voff[j] = static_cast<uint32_t>((orow0 + j * kRowsPerLoad + lr) * K + c * 8) * 2u;
+      int orow = orow0 + j * kRowsPerLoad + lr;
+      if (stage_x && gathered) {
+        // gathered rows past rows_g read as zero; others come from their token
+        orow = orow < rows_g ? a.gather[static_cast<int64_t>(tc.g) * a.rows_per_group + orow] : -1;
+      }
+      // weight rows past N (and token rows past rows_g) land past the
+      // buffer's end and read as zero
+      voff[j] = orow < 0 ? kOutOfRange : static_cast<uint32_t>(orow * K + c * 8) * 2u;
     }
   }
   uint8_t* stage_region = lds + (stage_x ? 0 : kBM * kRowBytes) + row0 * kRowBytes;
@@ -179,22 +202,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < kLoadsPerWave; ++j) {
-        const bool ok = valid && k0 + kcol[j] < K;
+        const bool ok = valid && k0 + kcol[j] < K && voff[j] != kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
                                                  ok ? voff[j] + kb : kOutOfRange, 0, 0, 0);
       }
     }
   };
 
-  // ---- fragments: wave (wn, wm) owns 128 weight rows x 128 token rows
+  // ---- fragments.  A full tile: wave (wn, wm) owns 128 weight rows x 128
+  // token rows (4 x 4 MFMA blocks).  A tail tile with at most 128 valid token
+  // rows: the four waves split the weight rows four ways and all take the
+  // valid 32-row token blocks, so an expert's last, mostly empty tile costs
+  // about (valid blocks)/8 of a full one instead of all of it.
+  // Block i of a wave: weight rows wrow[i] (+ lane%32), output columns
+  // ncol[i]; for SwiGLU blocks 0-1 are gate rows, 2-3 the matching up rows.
   const int wn = wave & 1, wm = wave >> 1;
-  int wrow[4], xrow[4];
+  const int valid_rows = static_cast<int>(min<int64_t>(rows_g - m0, kBM));
+  const bool tail = valid_rows <= 128;
+  const int mblocks = (valid_rows + 31) / 32;          // valid 32-row token blocks
+  int wrow[4], ncol[4], xrow[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    wrow[i] = kGlu ? ((i >> 1) * 128 + wn * 64 + (i & 1) * 32 + (lane & 31))
-                   : (wn * 128 + i * 32 + (lane & 31));
+  for (int i = 0; i < 4; ++i) {
+    if (!tail) {
+      ncol[i] = kGlu ? wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+      wrow[i] = kGlu ? (i >> 1) * 128 + ncol[i] : ncol[i];
+    } else {
+      // blocks 0 and (SwiGLU: 2, else 1) are used
+      ncol[i] = kGlu ? wave * 32 : wave * 64 + (i & 1) * 32;
+      wrow[i] = kGlu ? (i >> 1) * 128 + ncol[i] : ncol[i];
+    }
+    wrow[i] += lane & 31;
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) xrow[j] = wm * 128 + j * 32 + (lane & 31);
+  for (int j = 0; j < 4; ++j) xrow[j] = (tail ? 0 : wm * 128) + j * 32 + (lane & 31);
+  constexpr int kTailB = kGlu ? 2 : 1;                 // second weight block of a tail tile
 
   bf16x8_t wf[2][4], xf[2][4];
   auto load_frags = [&](int stage, int ks, int slot) {
@@ -202,7 +243,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int c = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      wf[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + kBM * kRowBytes + swz(wrow[i], c)));
+      if (!tail || i == 0 || i == kTailB)
+        wf[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + kBM * kRowBytes + swz(wrow[i], c)));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       xf[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + swz(xrow[j], c)));
@@ -223,6 +265,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][i], xf[slot][j], acc[i][j], 0, 0, 0);
   };
+  auto mfmas_tail = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < mblocks) {
+        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][0], xf[slot][j], acc[0][j], 0, 0, 0);
+        acc[kTailB][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][kTailB], xf[slot][j], acc[kTailB][j], 0, 0, 0);
+      }
+    }
+  };
 
   // ---- pipeline: stages kt+1 .. kt+kStages-1 are in flight while stage kt
   // is multiplied.
@@ -234,13 +285,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    issue_stage(kt + kStages - 1, kt + kStages - 1 < nk);
+  if (!tail) {
+    for (int kt = 0; kt < nk; ++kt) {
+      issue_stage(kt + kStages - 1, kt + kStages - 1 < nk);
 #pragma unroll
-    for (int ks = 0; ks < kSteps; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < kSteps) {
-        load_frags(kt, ks + 1, cur ^ 1);
+      for (int ks = 0; ks < kSteps; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < kSteps) {
+          load_frags(kt, ks + 1, cur ^ 1);
+        } else {
+          // last step of the stage: wait for stage kt+1 (own loads), make
+          // everyone's visible, start reading it, and multiply meanwhile
+          __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
+          __builtin_amdgcn_s_barrier();
+          load_frags(kt + 1, 0, cur ^ 1);
+        }
         mfmas(cur);
         // interleave: one fragment read after each of the first 8 MFMAs
 #pragma unroll
@@ -249,19 +308,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      } else {
-        // last step of the stage: wait for stage kt+1 (own loads), make
-        // everyone's visible, start reading it, and multiply meanwhile
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
-        __builtin_amdgcn_s_barrier();
-        load_frags(kt + 1, 0, cur ^ 1);
-        mfmas(cur);
+      }
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      issue_stage(kt + kStages - 1, kt + kStages - 1 < nk);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int ks = 0; ks < kSteps; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < kSteps) {
+          load_frags(kt, ks + 1, cur ^ 1);
+        } else {
+          __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
+          __builtin_amdgcn_s_barrier();
+          load_frags(kt + 1, 0, cur ^ 1);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        mfmas_tail(cur);
       }
     }
   }
@@ -275,13 +337,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int kIB = kGlu ? 2 : 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
+    const int64_t m = m0 + xrow[j];
     if (m >= rows_g) continue;
 #pragma unroll
     for (int i = 0; i < kIB; ++i) {
+      if (tail && i != 0 && i != kTailB) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + (kGlu ? wn * 64 : wn * 128) + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
         if (n >= N) continue;
         float v[4];
 #pragma unroll
@@ -323,7 +386,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
   const int64_t rows_g = a.rows ? min<int64_t>(a.rows[g], a.rows_per_group) : a.rows_per_group;
   const int m0 = mt * kFT, n0 = nt * kFT;
   if (m0 >= rows_g) return;
-  const float* A = static_cast<const float*>(a.A) + static_cast<int64_t>(g) * a.rows_per_group * K;
+  const bool gathered = a.gather != nullptr;
+  const float* A = static_cast<const float*>(a.A) + (gathered ? 0 : static_cast<int64_t>(g) * a.rows_per_group * K);
+  const int32_t* grow = gathered ? a.gather + static_cast<int64_t>(g) * a.rows_per_group : nullptr;
   const float* B0 = static_cast<const float*>(a.B0) + static_cast<int64_t>(g) * N * K;
   const float* B1 = ACT == 2 ? static_cast<const float*>(a.B1) + static_cast<int64_t>(g) * N * K : nullptr;
   const int tx = threadIdx.x % kFT, ty = threadIdx.x / kFT;   // ty 0..7
@@ -335,7 +400,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
       const int64_t m = m0 + rr;
       const int n = n0 + rr;
       const int kk = k0 + cc;
-      as[rr][cc] = (m < rows_g && kk < K) ? A[m * K + kk] : 0.0f;
+      const int64_t ar = (m < rows_g && gathered) ? grow[m] : m;
+      as[rr][cc] = (m < rows_g && kk < K) ? A[ar * K + kk] : 0.0f;
       bs[0][rr][cc] = (n < N && kk < K) ? B0[static_cast<int64_t>(n) * K + kk] : 0.0f;
       if (ACT == 2) bs[1][rr][cc] = (n < N && kk < K) ? B1[static_cast<int64_t>(n) * K + kk] : 0.0f;
     }
@@ -379,7 +445,7 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
     const int nout = a.act == 2 ? kBW / 2 : kBW;
     const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kBM - 1) / kBM) *
                           ((a.N + nout - 1) / nout);
-    const unsigned grid = static_cast<unsigned>((tiles + 7) / 8 * 8);
+    const unsigned grid = static_cast<unsigned>((tiles + 255) / 256 * 256);
     switch (a.act) {
       case 0: gemm_bf16_kernel<0><<<grid, kThreads, 0, s>>>(a); break;
       case 1: gemm_bf16_kernel<1><<<grid, kThreads, 0, s>>>(a); break;

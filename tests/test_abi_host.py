@@ -146,12 +146,15 @@ def test_null_and_misaligned_pointers_rejected_before_launch(moe):
     assert st == moe.MOE_EINVAL
     st = lib.moe_dispatch(ctypes.byref(c), None, 16, 16, 16, 16, None, None, None, None)
     assert st == moe.MOE_EINVAL and b'ws' in lib.moe_last_error()
-    st = lib.moe_expert_ffn(ctypes.byref(c), 1, 4, 40, None, 16, 16, None, None, 16, None, 12, 16,
-                            16, None)
+    st = lib.moe_expert_ffn(ctypes.byref(c), 1, 4, 40, None, 16, None, 0, 16, None, None, 16, None, 12,
+                            16, 16, None)
     assert st == moe.MOE_EINVAL and b'F must be' in lib.moe_last_error()
-    st = lib.moe_expert_ffn(ctypes.byref(c), moe.MOE_SWIGLU, 4, 40, None, 16, 16, 16, 16, 16, None,
-                            64, 16, 16, None)
+    st = lib.moe_expert_ffn(ctypes.byref(c), moe.MOE_SWIGLU, 4, 40, None, 16, None, 0, 16, 16, 16, 16,
+                            None, 64, 16, 16, None)
     assert st == moe.MOE_EUNSUPPORTED
+    st = lib.moe_expert_ffn(ctypes.byref(c), 1, 4, 40, None, 16, 16, 0, 16, None, None, 16, None, 64,
+                            16, 16, None)
+    assert st == moe.MOE_EINVAL and b'a_rows' in lib.moe_last_error()
 
 
 def test_workspace_grows_with_capacity(moe):

@@ -178,6 +178,8 @@ def test_dispatch_bit_exact(moe, case, dtype):
 FFN_CASES = [
     # (groups, rows_per_group, rows, d, F, act, dtype)
     (5, 320, [0, 1, 37, 256, 300], 256, 384, 'gelu', 'bf16'),
+    (3, 520, [520, 129, 128], 256, 256, 'swiglu', 'bf16'),
+    (4, 300, [300, 257, 5, 97], 512, 384, 'gelu', 'bf16'),
     (3, 600, [600, 513, 255], 512, 256, 'swiglu', 'bf16'),
     (2, 130, [130, 64], 1024, 1408, 'swiglu', 'bf16'),
     (1, 700, None, 136, 200, 'gelu', 'bf16'),
@@ -219,14 +221,34 @@ def test_expert_ffn_parity(moe, case):
     hn, on = f64_of(h), f64_of(out)
     af = synth.as_f32(a).astype(np.float64)
     tol = 1e-5 if dtype == 'f32' else 2e-2
-    for g in range(G):
-        n = R if rows is None else rows[g]
-        wts = {kk: synth.as_f32(v[g]) for kk, v in ex.items()}
-        if n:
-            rh, ro = O.expert_ffn(af[g * R:g * R + n], wts, act, dtype)
-            assert maxrel(hn[g * R:g * R + n], rh) <= tol
-            assert maxrel(on[g * R:g * R + n], ro) <= tol
-        assert (hn[g * R + n:(g + 1) * R] == 7.0).all() and (on[g * R + n:(g + 1) * R] == 7.0).all()
+
+    def check(hn, on, src_rows):
+        for g in range(G):
+            n = R if rows is None else rows[g]
+            wts = {kk: synth.as_f32(v[g]) for kk, v in ex.items()}
+            if n:
+                rh, ro = O.expert_ffn(af[src_rows(g, n)], wts, act, dtype)
+                assert maxrel(hn[g * R:g * R + n], rh) <= tol
+                assert maxrel(on[g * R:g * R + n], ro) <= tol
+            assert (hn[g * R + n:(g + 1) * R] == 7.0).all() and (on[g * R + n:(g + 1) * R] == 7.0).all()
+    check(hn, on, lambda g, n: slice(g * R, g * R + n))
+    # the same FFN with rows gathered from a shuffled token matrix
+    perm = np.random.default_rng(G + R).permutation(G * R)
+    a_sh = np.ascontiguousarray(a[np.argsort(perm)])          # a_sh[perm[i]] = a[i]
+    gather = perm.astype(np.int32)
+    # entries at or past rows[g] are never read; give them a harmless valid row
+    gather[np.arange(G * R) % R >= (np.array(rows)[np.arange(G * R) // R] if rows is not None else R)] = 0
+    h.fill_(7.0)
+    out.fill_(7.0)
+    kw = dict(gather=torch.from_numpy(gather).to(DEV))
+    if act == 'gelu':
+        moe.moe_expert_ffn(cfg, act, G, R, rows_t, synth.to_torch(a_sh, DEV), tt(ex['w_in']), None,
+                           tt(ex['b_in']), tt(ex['w_out']), tt(ex['b_out']), F, h, out, **kw)
+    else:
+        moe.moe_expert_ffn(cfg, act, G, R, rows_t, synth.to_torch(a_sh, DEV), tt(ex['w_up']),
+                           tt(ex['w_gate']), None, tt(ex['w_out']), None, F, h, out, **kw)
+    torch.cuda.synchronize()
+    check(f64_of(h), f64_of(out), lambda g, n: slice(g * R, g * R + n))
 
 
 # ----------------------------------------------------------------------------- combine and losses
