@@ -103,6 +103,7 @@ struct Workspace {
   double* lse2_partial;
   int32_t* fallback_partial;
   double* psum;
+  bf16_t* wsplit;
   int32_t* idx_tmp;
   float* gates_tmp;
   int32_t* row_token;
@@ -117,7 +118,7 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t{255}; }
 
 Workspace carve(const moe_config& c, int64_t C, void* base) {
   const int64_t n_tiles = (c.T + kTileTokens - 1) / kTileTokens;
-  const int64_t n_rtiles = (c.T + kRouteTokens - 1) / kRouteTokens;
+  const int64_t n_rtiles = (c.T + kMinRouteTile - 1) / kMinRouteTile;
   const size_t ds = dsize(c);
   const int64_t fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
   Workspace w{};
@@ -135,6 +136,7 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   w.lse2_partial = static_cast<double*>(take(sizeof(double) * n_rtiles));
   w.fallback_partial = static_cast<int32_t*>(take(sizeof(int32_t) * n_tiles));
   w.psum = static_cast<double*>(take(sizeof(double) * (c.E + 1)));
+  w.wsplit = static_cast<bf16_t*>(take(sizeof(bf16_t) * 3 * ((c.E + 15) / 16 * 16) * c.d));
   w.idx_tmp = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
   w.gates_tmp = static_cast<float*>(take(sizeof(float) * c.T * c.k));
   w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * c.E * C));
@@ -158,8 +160,15 @@ RouteArgs route_args(const moe_config& c, Workspace* w) {
   if (w) {
     r.p_partial = w->p_partial;
     r.lse2_partial = w->lse2_partial;
+    r.wsplit = w->wsplit;
   }
   return r;
+}
+
+// router partial sums come in one row per router workgroup
+int router_tiles(const moe_config& c, bool from_x) {
+  const int tb = route_tile_tokens(c.E, c.dtype, from_x);
+  return static_cast<int>((c.T + tb - 1) / tb);
 }
 
 CapArgs cap_args(const moe_config& c, int64_t C, const Workspace& w) {
@@ -269,6 +278,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router
     MOE_TRY(check_ptr(x, "x", 16));
     MOE_TRY(check_ptr(w_router, "w_router", 4));
     MOE_TRY(check_ptr(logits, "logits", 4, false));
+    if (c.dtype == MOE_BF16 && !ws)
+      return fail(MOE_EINVAL, "ws must not be NULL when routing bf16 x (it holds the split router weight)");
   } else {
     MOE_TRY(check_ptr(logits, "logits (input when x is NULL)", 4, needT));
   }
@@ -404,6 +415,7 @@ moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int3
   a.p_partial = w.p_partial;
   a.lse2_partial = w.lse2_partial;
   a.psum = w.psum;
+  a.n_rtiles = router_tiles(c, false);
   MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "aux-loss counts"));
   LossArgs l = loss_args(c, C, w, w.counts_tmp);
   l.fallback_partial = nullptr;
@@ -472,6 +484,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   a.p_partial = w.p_partial;
   a.lse2_partial = w.lse2_partial;
   a.psum = w.psum;
+  a.n_rtiles = router_tiles(c, true);
   // the up-projection gathers token rows straight into its tiles through
   // row_token, so no dispatched copy of x is made
   a.x = nullptr;

@@ -12,7 +12,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokensPerBlock = 8;
+constexpr int kTokensPerBlock = 4;
 
 template <typename T>
 struct Vec;  // 16 bytes of storage as float32 lanes
@@ -51,8 +51,8 @@ template <> struct Vec<float> {
 // y_t = sum_{j kept} g_tj * ye[e_tj, s_tj] (+ shared_t), float32 in j order,
 // one rounding; fallback x_t (or 0) when nothing was kept and no shared expert.
 // A workgroup takes kTokensPerBlock tokens; their (row, gate) lists are staged
-// in LDS first, then every thread streams 16-byte chunks: all kept rows of a
-// token are loaded before they are summed.
+// in LDS first, then every thread streams 16-byte chunks of two (token,
+// chunk) items at a time, loading all their kept rows before summing.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   constexpr int V = Vec<T>::N;
@@ -85,11 +85,31 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     nkept[i] = n;
   }
   __syncthreads();
-  for (int i = 0; i < nt; ++i) {
-    const int64_t t = t0 + i;
-    const int n = nkept[i];
-    for (int c = threadIdx.x; c < nvec; c += kThreads) {
-      const int64_t off = static_cast<int64_t>(c) * 16;
+  // work items (token i, chunk c), two per thread at a time: every row of
+  // both items is loaded before either is summed
+  const int items = nt * nvec;
+  for (int w0 = threadIdx.x; w0 < items; w0 += 2 * kThreads) {
+    int it[2], ic[2], in[2];
+    bool live[2];
+    float v[2][4][V];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int w = w0 + u * kThreads;
+      live[u] = w < items;
+      it[u] = live[u] ? w / nvec : 0;
+      ic[u] = live[u] ? w % nvec : 0;
+      in[u] = live[u] ? nkept[it[u]] : 0;
+      const int64_t off = static_cast<int64_t>(ic[u]) * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < in[u]) Vec<T>::load(ye + rows[it[u]][j] * rowbytes + off, v[u][j]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!live[u]) continue;
+      const int i = it[u], n = in[u];
+      const int64_t t = t0 + i;
+      const int64_t off = static_cast<int64_t>(ic[u]) * 16;
       float acc[V];
       if (n == 0 && sh == nullptr) {
         if (a.zero_fallback) {
@@ -101,25 +121,27 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       } else {
 #pragma unroll
         for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-        for (int j0 = 0; j0 < n; j0 += 4) {
-          float v[4][V];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (j0 + u < n) Vec<T>::load(ye + rows[i][j0 + u] * rowbytes + off, v[u]);
+        for (int j = 0; j < 4; ++j) {
+          if (j < n) {
+            const float g = gts[i][j];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (j0 + u < n) {
-              const float g = gts[i][j0 + u];
-#pragma unroll
-              for (int q = 0; q < V; ++q) acc[q] += g * v[u][q];
-            }
+            for (int q = 0; q < V; ++q) acc[q] += g * v[u][j][q];
           }
         }
-        if (sh) {
-          float v[V];
-          Vec<T>::load(sh + t * rowbytes + off, v);
+        // choices beyond the fourth (k > 4), in order
+        for (int j = 4; j < n; ++j) {
+          float vv[V];
+          Vec<T>::load(ye + rows[i][j] * rowbytes + off, vv);
+          const float g = gts[i][j];
 #pragma unroll
-          for (int q = 0; q < V; ++q) acc[q] += v[q];
+          for (int q = 0; q < V; ++q) acc[q] += g * vv[q];
+        }
+        if (sh) {
+          float vv[V];
+          Vec<T>::load(sh + t * rowbytes + off, vv);
+#pragma unroll
+          for (int q = 0; q < V; ++q) acc[q] += vv[q];
         }
       }
       Vec<T>::store(y + t * rowbytes + off, acc);

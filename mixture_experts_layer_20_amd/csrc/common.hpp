@@ -92,6 +92,7 @@ struct RouteArgs {
   float* lse;                 // [T] | null
   double* p_partial;          // [n_rtiles, E] | null
   double* lse2_partial;       // [n_rtiles] | null
+  bf16_t* wsplit;             // [3, round16(E), d] split router weight (bf16 x)
   int64_t T;
   int d, E, k;
   int score;                  // moe_score
@@ -163,7 +164,14 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_losses(const LossArgs& a, hipStream_t s);
 
-// router tile (tokens per router workgroup), shared by launcher and host sizing
-constexpr int kRouteTokens = 32;
+// router tile (tokens per router workgroup), shared by launcher and host
+// sizing; partial-sum arrays are sized for the smallest tile
+constexpr int kRouteTokens = 32;     // float32 router and routing from logits
+constexpr int kMinRouteTile = 16;
+__host__ __device__ inline int route_tile_tokens(int E, int dtype, bool from_x) {
+  if (!from_x || dtype != MOE_BF16) return kRouteTokens;
+  if (E <= 32) return 16;
+  return E <= 64 ? 32 : (E <= 128 ? 64 : 32);
+}
 
 }  // namespace moe

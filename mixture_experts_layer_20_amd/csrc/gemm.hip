@@ -161,8 +161,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     const bf16_t* base = stage_x ? A : ((kGlu && wave == 2) ? B1 : B0);
     const int64_t nbytes = stage_x ? (gathered ? a.a_rows : rows_g) * K * 2
                                    : static_cast<int64_t>(N) * K * 2;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), (short)0,
-                                             static_cast<int>(nbytes), kRsrcWord3);
+    // the descriptor must live in scalar registers: pin its fields to lane 0
+    // (they are uniform; without this the compiler may not prove it and wrap
+    // every load in a loop over lanes)
+    const uint64_t bu = reinterpret_cast<uint64_t>(base);
+    const uint32_t blo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu));
+    const uint32_t bhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu >> 32));
+    const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(nbytes));
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>((static_cast<uint64_t>(bhi) << 32) | blo), (short)0, nrec, kRsrcWord3);
     // first operand row of this wave's block 0 (token rows: m0; weight rows:
     // n0, plus 128 for the second half when not SwiGLU)
     const int orow0 = stage_x ? m0 + row0 : (kGlu ? n0 : n0 + row0);

@@ -322,10 +322,142 @@ __global__ __launch_bounds__(kThreads) void route_from_logits_kernel(RouteArgs a
   workgroup_epilogue<EPL>(a, zbuf, a.E, t0, nt, red);
 }
 
+// ---------------------------------------------------------------- bf16 x: MFMA router
+// The router stays float32 (x is bf16, the weight float32): the weight is
+// split exactly into three bf16 planes, w = hi + mid + lo (each a bf16
+// rounding of what the previous ones leave; exact for 2^-110 < |w| < 2^127),
+// so every product x*hi, x*mid, x*lo is exact in the MFMA and only the
+// float32 accumulation order differs from a plain float32 dot product.
+// Planes are stored transposed, [3][Ep][d] (Ep = E rounded up to 16), so an
+// MFMA operand fragment is one 16-byte load.
+typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
+typedef float f32x4_r __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void split_router_kernel(const float* w, bf16_t* wt, int d, int E, int Ep) {
+  const int64_t n = static_cast<int64_t>(Ep) * d;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int e = static_cast<int>(i / d), k = static_cast<int>(i % d);
+    const float v = e < E ? w[static_cast<int64_t>(k) * E + e] : 0.0f;
+    const bf16_t hi = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi);
+    const bf16_t mid = f32_to_bf16(r1);
+    const bf16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    wt[i] = hi;
+    wt[n + i] = mid;
+    wt[2 * n + i] = lo;
+  }
+}
+
+// One workgroup: TB tokens x all experts.  The d-range is dealt to the four
+// wavefronts in 32-wide chunks (chunk c to wave c % 4); each computes partial
+// logits with v_mfma_f32_16x16x32_bf16 (tokens as rows, experts as columns),
+// x fragments loaded straight from memory U chunks ahead.  The four partial
+// tiles are added in wave order in LDS (deterministic), then the shared
+// per-token epilogue runs.
+template <int TB, int NB, int U>
+__global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
+  constexpr int MB = TB / 16;
+  constexpr int EPAD = NB * 16;
+  constexpr int EPL = (EPAD + kWave - 1) / kWave;
+  __shared__ __align__(16) float zbuf[TB * EPAD];
+  __shared__ double red[5 * 256];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int d = a.d;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
+  const int nt = static_cast<int>(min<int64_t>(TB, a.T - t0));
+  const bf16_t* x = static_cast<const bf16_t*>(a.x);
+  const bf16_t* wt = a.wsplit;
+  const int64_t plane = static_cast<int64_t>(EPAD) * d;
+  const int koff = 8 * (lane >> 4);
+  const bf16_t* xrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t t = min<int64_t>(t0 + mb * 16 + (lane & 15), a.T - 1);
+    xrow[mb] = x + t * d + koff;
+  }
+  const bf16_t* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wrow[nb] = wt + static_cast<int64_t>(nb * 16 + (lane & 15)) * d + koff;
+
+  f32x4_r acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_r{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nchunks = (d + 31) / 32;
+  for (int c0 = wave; c0 < nchunks; c0 += 4 * U) {
+    // all loads of the batch first (x from HBM, weight planes from L2), then
+    // the MFMAs, so one batch costs about one memory latency
+    bf16x8_r af[U][MB], bw[U][NB][3];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (c0 + 4 * u) * 32;
+      const bool ok = (c0 + 4 * u) < nchunks && k + koff < d;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        af[u][mb] = ok ? __builtin_bit_cast(bf16x8_r, *reinterpret_cast<const uint4*>(xrow[mb] + k))
+                       : __builtin_bit_cast(bf16x8_r, make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp)
+          bw[u][nb][sp] = ok ? __builtin_bit_cast(bf16x8_r, *reinterpret_cast<const uint4*>(wrow[nb] + sp * plane + k))
+                             : __builtin_bit_cast(bf16x8_r, make_uint4(0, 0, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][mb], bw[u][nb][sp], acc[mb][nb], 0, 0, 0);
+  }
+  // add the four partial tiles in wave order (logit bias first)
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tl = mb * 16 + 4 * (lane >> 4) + r;
+            const int e = nb * 16 + (lane & 15);
+            float base;
+            if (w == 0) base = (a.logit_bias && e < a.E) ? a.logit_bias[e] : 0.0f;
+            else base = zbuf[tl * EPAD + e];
+            zbuf[tl * EPAD + e] = base + acc[mb][nb][r];
+          }
+    }
+    __syncthreads();
+  }
+  workgroup_epilogue<EPL>(a, zbuf, EPAD, t0, nt, red);
+}
+
 template <typename XT>
 hipError_t dispatch_route(const RouteArgs& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((a.T + kBT - 1) / kBT);
   const int epl = (a.E + kWave - 1) / kWave;
+  if (a.x != nullptr && sizeof(XT) == 2) {
+    const int ep = (a.E + 15) / 16 * 16;
+    split_router_kernel<<<min(1024, (ep * a.d + kThreads - 1) / kThreads), kThreads, 0, s>>>(
+        a.w_router, a.wsplit, a.d, a.E, ep);
+    const int tb = route_tile_tokens(a.E, MOE_BF16, true);
+    const unsigned g = static_cast<unsigned>((a.T + tb - 1) / tb);
+    // tile tokens x expert blocks x chunks per batch: sized so one batch's
+    // fragments fit in registers beside the accumulators
+    if (a.E <= 16) route_mfma_kernel<16, 1, 8><<<g, kThreads, 0, s>>>(a);
+    else if (a.E <= 32) route_mfma_kernel<16, 2, 4><<<g, kThreads, 0, s>>>(a);
+    else if (a.E <= 64) route_mfma_kernel<32, 4, 2><<<g, kThreads, 0, s>>>(a);
+    else if (a.E <= 128) route_mfma_kernel<64, 8, 1><<<g, kThreads, 0, s>>>(a);
+    else route_mfma_kernel<32, 16, 1><<<g, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (a.x == nullptr) {
     switch (epl) {
       case 1: route_from_logits_kernel<1><<<grid, kThreads, 0, s>>>(a); break;

@@ -107,7 +107,7 @@ def test_sigmoid_key_matches_the_spec_bit_for_bit(moe):
 
 
 def test_router_logits_within_float32_dot_bound(moe):
-    for name in ('tiny_f32', 'switch_top1_skewed'):
+    for name in ('tiny_f32', 'switch_top1_skewed', 'deepseekmoe_fine'):
         w = synth.WORKLOADS[name]
         inp, ex, sh, dev = device_layer(w, moe)
         say('logits', name)
@@ -117,7 +117,7 @@ def test_router_logits_within_float32_dot_bound(moe):
         idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
         gates = torch.empty(T, k, dtype=torch.float32, device=DEV)
         moe.moe_route(cfg, dev['x'], dev['w_router'], dev['logit_bias'], None, logits, None, idx,
-                      gates, None, None)
+                      gates, None, moe.workspace(cfg, DEV))
         torch.cuda.synchronize()
         x = synth.as_f32(inp['x'])
         zr = O.router_logits(x, inp['w_router'], inp['logit_bias'])
