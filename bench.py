@@ -240,7 +240,7 @@ def cpu_baseline(w, sample_tokens, log):
         threads = max([i.get('num_threads', 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    n = sample_tokens or {'mixtral_8x_top2': 256, 'sigmoid_stress': 256}.get(w.name, min(w.T, 1024))
+    n = sample_tokens or {'mixtral_8x_top2': 2048, 'sigmoid_stress': 1024}.get(w.name, min(w.T, 4096))
     ws_ = w.with_(T=n)
     inp = synth.router_inputs(w)
     inp = dict(inp, x=inp['x'][:n])
