@@ -58,6 +58,11 @@ __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
 }
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+// SiLU from the hardware exp2 and reciprocal: a few ulps in float32, far
+// below the bf16 rounding of the bf16 path's result
+__device__ __forceinline__ float silu_fast(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
+}
 
 // Byte offset of logical 16-byte k-chunk `chunk` of tile row `row` in LDS:
 // the chunk index is XORed with the row bits above the ones that already
@@ -155,8 +160,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int lr = lane / kChunks, pc = lane % kChunks;
   const int row0 = (wave & 1) * 128;               // first tile row this wave stages
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[kLoadsPerWave];
-  int kcol[kLoadsPerWave];
+  // voff: offset of each load's 16 bytes in stage 0; pvoff: the same for the
+  // last stage, with chunks at or past K sent out of range
+  uint32_t voff[kLoadsPerWave], pvoff[kLoadsPerWave];
+  const int nk = (K + kBK - 1) / kBK;
+  const int k_last = K - (nk - 1) * kBK;          // valid k in the last stage
   {
     const bf16_t* base = stage_x ? A : ((kGlu && wave == 2) ? B1 : B0);
     const int64_t nbytes = stage_x ? (gathered ? a.a_rows : rows_g) * K * 2
@@ -177,7 +185,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < kLoadsPerWave; ++j) {
       const int trow = row0 + j * kRowsPerLoad + lr;             // tile row (sets the swizzle)
       const int c = pc ^ ((trow >> kSwzShift) & (kChunks - 1));
-      kcol[j] = c * 8;
       int orow = orow0 + j * kRowsPerLoad + lr;
       if (stage_x && gathered) {
         // gathered rows past rows_g read as zero; others come from their token
@@ -186,34 +193,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
       // weight rows past N (and token rows past rows_g) land past the
       // buffer's end and read as zero
       voff[j] = orow < 0 ? kOutOfRange : static_cast<uint32_t>(orow * K + c * 8) * 2u;
+      pvoff[j] = c * 8 < k_last ? voff[j] : kOutOfRange;
     }
   }
   uint8_t* stage_region = lds + (stage_x ? 0 : kBM * kRowBytes) + row0 * kRowBytes;
 
-  // stage kt goes to LDS buffer kt % kStages; a stage past the end (valid
-  // false) loads zeros so that every iteration has the same shape
-  // When K is a multiple of kBK no chunk passes K, so the k offset goes in
-  // the scalar offset (the bounds check sees only the row offset, which is
-  // what separates valid rows) and the per-lane offsets stay fixed.
-  const bool k_full = (K % kBK) == 0;
-  auto issue_stage = [&](int kt, bool valid) {
-    const int k0 = kt * kBK;
-    const uint32_t kb = static_cast<uint32_t>(k0) * 2u;
+  // Stage kt goes to LDS buffer kt % kStages; its k offset goes in the
+  // scalar offset, so the bounds check sees the row offset, which is what
+  // separates valid rows from the rest.  The last stage takes pvoff (zeros
+  // past K).  Every iteration issues a stage so that the wait counts are
+  // fixed: stages past the end re-read the last one into a buffer nobody
+  // multiplies.
+  auto issue = [&](int kt) {
+    const int kc = min(kt, nk - 1);
+    const bool last = kc == nk - 1;
     uint8_t* dst = stage_region + (kt % kStages) * kStageBytes;
-    if (k_full) {
-      const int soff = valid ? static_cast<int>(kb) : 0;
+    const int soff = kc * kBK * 2;
 #pragma unroll
-      for (int j = 0; j < kLoadsPerWave; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
-                                                 valid ? voff[j] : kOutOfRange, soff, 0, 0);
-    } else {
-#pragma unroll
-      for (int j = 0; j < kLoadsPerWave; ++j) {
-        const bool ok = valid && k0 + kcol[j] < K && voff[j] != kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
-                                                 ok ? voff[j] + kb : kOutOfRange, 0, 0, 0);
-      }
-    }
+    for (int j = 0; j < kLoadsPerWave; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
+                                               last ? pvoff[j] : voff[j], soff, 0, 0);
   };
 
   // ---- fragments.  A full tile: wave (wn, wm) owns 128 weight rows x 128
@@ -265,13 +264,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto mfmas = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][i], xf[slot][j], acc[i][j], 0, 0, 0);
-  };
   auto mfmas_tail = [&](int slot) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -283,58 +275,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   };
 
   // ---- pipeline: stages kt+1 .. kt+kStages-1 are in flight while stage kt
-  // is multiplied.
+  // is multiplied.  The first 16-k step of an iteration issues stage
+  // kt+kStages-1; the last waits for stage kt+1, meets the other waves at
+  // the barrier (after which nobody reads the buffer the next issue
+  // overwrites) and starts reading stage kt+1's first fragments.
   constexpr int kSteps = kBK / 16;
   static_assert(kSteps % 2 == 0, "fragment slots alternate per 16-k step");
-  const int nk = (K + kBK - 1) / kBK;
+  // A full tile spreads a stage's loads over all the iteration's steps (over
+  // the first half when only two stages exist: the last step's barrier then
+  // waits for the stage issued in the same iteration).  At that barrier the
+  // loads issued after stage kt+1's may still fly: the whole stages between
+  // and the part of stage kt+kStages-1 issued before the barrier.
+  constexpr int kLoadSteps = kStages >= 3 ? kSteps : (kSteps / 2 > 0 ? kSteps / 2 : 1);
+  static_assert(kLoadsPerWave % kLoadSteps == 0, "a stage's loads split evenly over the steps");
+  constexpr int kWaitFull = wait_vm_lgkm0(
+      kStages >= 3 ? (kStages - 3) * kLoadsPerWave + (kSteps - 1) * (kLoadsPerWave / kLoadSteps) : 0);
+  // a tail tile issues a whole stage in its first step
+  constexpr int kWaitStage = wait_vm_lgkm0((kStages - 2) * kLoadsPerWave);
 #pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) issue_stage(st, st < nk);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
+  for (int st = 0; st < kStages - 1; ++st) issue(st);
+  __builtin_amdgcn_s_waitcnt(kWaitStage);
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, 0);
   if (!tail) {
+    // a full tile runs each 16-k step as 8 fenced groups of two MFMAs, one
+    // fragment read for the next step and part of the stage's loads, so that
+    // no burst of loads or reads holds up the MFMAs
     for (int kt = 0; kt < nk; ++kt) {
-      issue_stage(kt + kStages - 1, kt + kStages - 1 < nk);
+      const int ist = kt + kStages - 1;                 // stage this iteration issues
+      const int kc = min(ist, nk - 1);
+      const bool last = kc == nk - 1;
+      uint8_t* dst = stage_region + (ist % kStages) * kStageBytes;
+      const int soff = kc * kBK * 2;
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) {
         const int cur = ks & 1;
-        if (ks + 1 < kSteps) {
-          load_frags(kt, ks + 1, cur ^ 1);
-        } else {
-          // last step of the stage: wait for stage kt+1 (own loads), make
-          // everyone's visible, start reading it, and multiply meanwhile
-          __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
+        const bool next_stage = ks + 1 == kSteps;
+        if (next_stage) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(kWaitFull);
           __builtin_amdgcn_s_barrier();
-          load_frags(kt + 1, 0, cur ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        mfmas(cur);
-        // interleave: one fragment read after each of the first 8 MFMAs
+        const uint8_t* rs = lds + ((next_stage ? kt + 1 : kt) % kStages) * kStageBytes;
+        const int rc = (next_stage ? 0 : ks + 1) * 2 + (lane >> 5);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          const int i = q >> 1, j0 = (q & 1) * 2;
+          acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0], acc[i][j0], 0, 0, 0);
+          acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0 + 1], acc[i][j0 + 1], 0, 0, 0);
+          // reads in the order the next step's groups use them: x0 x1 w0 x2 x3 w1 w2 w3
+          constexpr int kOrder[8] = {4, 5, 0, 6, 7, 1, 2, 3};
+          const int f = kOrder[q];
+          if (f < 4)
+            wf[cur ^ 1][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rs + kBM * kRowBytes + swz(wrow[f], rc)));
+          else
+            xf[cur ^ 1][f - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rs + swz(xrow[f - 4], rc)));
+          // this step's share of the stage's loads, spread over the groups
+          constexpr int kPer = kLoadsPerWave / kLoadSteps;
+          if (ks < kLoadSteps) {
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+              if ((u * 8) / kPer == q) {
+                const int j = ks * kPer + u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
+                                                         last ? pvoff[j] : voff[j], soff, 0, 0);
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
     }
   } else {
     for (int kt = 0; kt < nk; ++kt) {
-      issue_stage(kt + kStages - 1, kt + kStages - 1 < nk);
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) {
         const int cur = ks & 1;
         if (ks + 1 < kSteps) {
           load_frags(kt, ks + 1, cur ^ 1);
         } else {
-          __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kStages - 2) * kLoadsPerWave));
+          __builtin_amdgcn_s_waitcnt(kWaitStage);
           __builtin_amdgcn_s_barrier();
           load_frags(kt + 1, 0, cur ^ 1);
         }
+        if (ks == 0) issue(kt + kStages - 1);
         mfmas_tail(cur);
       }
     }
   }
-  // the last issue_stage calls loaded zeros past the end; drain them
+  // the stages issued past the end are still landing
   __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: lane holds, for block (i, j), output columns
@@ -359,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
           float x = acc[i][j][4 * q + r];
           if (ACT == 2) {
             const float up = acc[i + 2][j][4 * q + r];
-            x = silu(x) * up;
+            x = silu_fast(x) * up;
           } else {
             if (bias) x += bf16_to_f32(bias[n + r]);
             if (ACT == 1) x = gelu_erf(x);
