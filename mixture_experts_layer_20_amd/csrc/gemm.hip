@@ -29,6 +29,8 @@
 //   * Rows at or past rows[g] are never stored; their loads are clamped to a
 //     valid row.  Columns past N are clamped and not stored; k past K reads 0.
 // float32 path: a plain LDS-tiled FMA kernel (small layers only).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -36,6 +38,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kBM = 256;     // token rows per tile
@@ -274,6 +278,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     }
   };
 
+  // ---- epilogue: lane holds, for block (i, j), output columns
+  // ncol[i] + 8q + 4*(lane/32) + {0..3} of token row xrow[j] (tile-relative).
+  // Each path has its own copy, so that the accumulators of the two paths
+  // are never merged into one set of registers.
+  auto store_tile = [&](auto tail_c) __attribute__((always_inline)) {
+    constexpr bool kTail = decltype(tail_c)::value;
+    // the stages issued past the end are still landing
+    __builtin_amdgcn_s_waitcnt(0);
+    bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;
+    const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t m = m0 + xrow[j];
+      if (m >= rows_g) continue;
+#pragma unroll
+      for (int i = 0; i < (kGlu ? 2 : 4); ++i) {
+        if (kTail && i != 0 && i != kTailB) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
+          if (n >= N) continue;
+          f32x2_t v[2];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = acc[i][j][4 * q + r];
+            if (ACT == 2) {
+              x = silu_fast(x) * acc[i + 2][j][4 * q + r];
+            } else {
+              if (bias) x += bf16_to_f32(bias[n + r]);
+              if (ACT == 1) x = gelu_erf(x);
+            }
+            v[r >> 1][r & 1] = x;
+          }
+          // hardware round-to-nearest-even conversion, two values at a time
+          uint2 packed;
+          packed.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[0], bf16x2_t));
+          packed.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[1], bf16x2_t));
+          *reinterpret_cast<uint2*>(C + m * N + n) = packed;
+        }
+        // one block at a time: keeps the accumulators' copies out of the
+        // VGPRs until they are needed
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // ---- pipeline: stages kt+1 .. kt+kStages-1 are in flight while stage kt
   // is multiplied.  The first 16-k step of an iteration issues stage
   // kt+kStages-1; the last waits for stage kt+1, meets the other waves at
@@ -347,6 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         }
       }
     }
+    store_tile(std::false_type{});
   } else {
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
@@ -363,45 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         mfmas_tail(cur);
       }
     }
-  }
-  // the stages issued past the end are still landing
-  __builtin_amdgcn_s_waitcnt(0);
-
-  // epilogue: lane holds, for block (i, j), output columns
-  // nbase + 8q + 4*(lane/32) + {0..3} of token row mbase + lane%32
-  bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;
-  const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
-  constexpr int kIB = kGlu ? 2 : 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + xrow[j];
-    if (m >= rows_g) continue;
-#pragma unroll
-    for (int i = 0; i < kIB; ++i) {
-      if (tail && i != 0 && i != kTailB) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
-        if (n >= N) continue;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = acc[i][j][4 * q + r];
-          if (ACT == 2) {
-            const float up = acc[i + 2][j][4 * q + r];
-            x = silu_fast(x) * up;
-          } else {
-            if (bias) x += bf16_to_f32(bias[n + r]);
-            if (ACT == 1) x = gelu_erf(x);
-          }
-          v[r] = x;
-        }
-        uint2 packed;
-        packed.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-        packed.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-        *reinterpret_cast<uint2*>(C + m * N + n) = packed;
-      }
-    }
+    store_tile(std::true_type{});
   }
 }
 
