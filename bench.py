@@ -45,7 +45,12 @@ def parse():
     p.add_argument('--no-cpu-baseline', action='store_true')
     p.add_argument('--cpu-sample-tokens', type=int, default=0)
     p.add_argument('--phase-reps', type=int, default=10)
+    p.add_argument('--copy-calibration', action='store_true',
+                   help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
     return p.parse_args()
+
+
+COPY_BYTES = 1 << 30           # bytes read and bytes written by the calibration copy
 
 
 def main():
@@ -203,11 +208,28 @@ def main():
         log(f'phase {kk}: ' + ', '.join(f'{a}={bb:.4g}' if isinstance(bb, float) else f'{a}={bb}'
                                       for a, bb in v.items()))
     ach = ffn_flops / (med['expert_ffn'] * 1e-3) / 1e12
+    # HBM bytes per launch pair from the committed FETCH_SIZE / WRITE_SIZE
+    # counter runs, if they were taken on this version of the GEMM source
+    from mixture_experts_layer_20_amd import rocprof_summary
+    rec = rocprof_summary.read_traffic(os.path.join(ROOT, 'profiles', f'gemm_traffic_{w.name}.txt'), w.name)
     roofline = {'kernel': 'expert grouped GEMM (gate/up launch + down launch)',
                 'bound': 'mfma', 'achieved': round(ach, 2), 'peak': peak, 'unit': 'TFLOP/s',
-                'frac': round(ach / peak, 4), 'traffic': None,
+                'frac': round(ach / peak, 4),
+                'traffic': round(rec['traffic_bytes_per_pair']) if rec else None,
                 'algorithmic': f'2*kept*{mult}*d*d_ff = {ffn_flops:.4e} flop per launch pair, '
                                f'kept={n_kept}'}
+    if rec:
+        roofline['traffic_note'] = (f'HBM bytes per launch pair: fetch {rec["fetch_bytes_per_pair"]:.4g} + write '
+                                    f'{rec["write_bytes_per_pair"]:.4g}, counters scaled by a plain copy kernel '
+                                    f'(factors {rec["fetch_factor"]:.3f} / {rec["write_factor"]:.3f})')
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -240,7 +262,7 @@ def cpu_baseline(w, sample_tokens, log):
         threads = max([i.get('num_threads', 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count() or 1
-    n = sample_tokens or {'mixtral_8x_top2': 2048, 'sigmoid_stress': 1024}.get(w.name, min(w.T, 4096))
+    n = sample_tokens or {'mixtral_8x_top2': 8192, 'sigmoid_stress': 1024}.get(w.name, min(w.T, 4096))
     ws_ = w.with_(T=n)
     inp = synth.router_inputs(w)
     inp = dict(inp, x=inp['x'][:n])
