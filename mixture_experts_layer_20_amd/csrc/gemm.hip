@@ -15,10 +15,14 @@
 //   * The MFMA's first operand is the weight tile and its second the token
 //     tile, so each lane ends with four consecutive output columns of one
 //     token row: 8-byte bf16 stores.
-//   * Direct global -> LDS loads (buffer_load ... lds), kStages k-stages of
-//     kBK in flight, one barrier per stage; 16-byte chunks XOR-swizzled by row
-//     so fragment reads spread over the LDS banks.  Token rows may be
-//     gathered through a row list (the dispatch is fused into this load).
+//   * Direct global -> LDS loads (buffer_load ... lds), 16 bytes per lane:
+//     one wavefront instruction fills 8 rows x 128 bytes, i.e. whole cache
+//     lines (the load path moves about 1.7x the bytes per cycle it moves
+//     for half lines).  The token rows and the weight rows each have their
+//     own ring of stage buffers in LDS, one barrier per 64-wide k stage;
+//     16-byte chunks XOR-swizzled by row so fragment reads spread over the
+//     LDS banks.  Token rows may be gathered through a row list (the
+//     dispatch is fused into this load).
 //   * Tile order: logical tiles walk groups of 4 row tiles column by column,
 //     and 32-tile chunks of them are dealt round-robin to the 8 XCDs (blocks
 //     reach XCDs round-robin), so the ~32 tiles an XCD runs at once share 4
@@ -26,8 +30,8 @@
 //     share of every expert.
 //   * A tail tile (at most 128 valid token rows) splits the weight rows four
 //     ways across the waves and skips empty 32-row token blocks.
-//   * Rows at or past rows[g] are never stored; their loads are clamped to a
-//     valid row.  Columns past N are clamped and not stored; k past K reads 0.
+//   * Rows at or past rows[g] and columns past N read as zero through the
+//     buffer bounds and are never stored; k past K reads 0.
 // float32 path: a plain LDS-tiled FMA kernel (small layers only).
 #include <type_traits>
 
@@ -45,18 +49,30 @@ constexpr int kThreads = 256;
 constexpr int kBM = 256;     // token rows per tile
 constexpr int kBW = 256;     // weight rows per tile
 #ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 32
+#define MOE_GEMM_BK 64
 #endif
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 4
+#ifndef MOE_GEMM_NX
+#define MOE_GEMM_NX 2
+#endif
+#ifndef MOE_GEMM_NW
+#define MOE_GEMM_NW 2
+#endif
+#ifndef MOE_GEMM_LOADPOS
+#define MOE_GEMM_LOADPOS 2
 #endif
 constexpr int kBK = MOE_GEMM_BK;          // k per pipeline stage
-constexpr int kStages = MOE_GEMM_STAGES;  // LDS pipeline depth
-constexpr int kRowBytes = kBK * 2;                         // 64
+constexpr int kNX = MOE_GEMM_NX;          // token-row stages in LDS
+constexpr int kNW = MOE_GEMM_NW;          // weight-row stages in LDS
+constexpr int kRowBytes = kBK * 2;                         // 128: one full cache line per row
 constexpr int kChunks = kRowBytes / 16;                    // 16-byte k-chunks per row
-constexpr int kStageBytes = (kBM + kBW) * kRowBytes;       // 32 KiB
+constexpr int kXBytes = kBM * kRowBytes;                   // one token-row stage (32 KiB)
+constexpr int kWBytes = kBW * kRowBytes;                   // one weight-row stage (32 KiB)
+constexpr int kLdsBytes = kNX * kXBytes + kNW * kWBytes;   // 128 KiB
 constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows one wave instruction fills
-constexpr int kLoadsPerWave = (kBM + kBW) / kRowsPerLoad / 4;  // per stage
+constexpr int kLoadsPerWave = 128 / kRowsPerLoad;          // per stage: each wave stages 128 rows
+static_assert(kXBytes == kWBytes, "both rings use one buffer size");
+static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
+static_assert(kLoadsPerWave <= 32, "one bit per load in the past-K mask");
 
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
@@ -119,7 +135,7 @@ template <int ACT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr bool kGlu = ACT == 2;
   constexpr int kNOut = kGlu ? kBW / 2 : kBW;   // output columns per tile
-  __shared__ __align__(1024) uint8_t lds[kStages * kStageBytes];
+  __shared__ __align__(1024) uint8_t lds[kLdsBytes];
 
   const int N = a.N, K = a.K;
   const int ntiles = (N + kNOut - 1) / kNOut;
@@ -164,9 +180,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int lr = lane / kChunks, pc = lane % kChunks;
   const int row0 = (wave & 1) * 128;               // first tile row this wave stages
   __amdgpu_buffer_rsrc_t rsrc;
-  // voff: offset of each load's 16 bytes in stage 0; pvoff: the same for the
-  // last stage, with chunks at or past K sent out of range
-  uint32_t voff[kLoadsPerWave], pvoff[kLoadsPerWave];
+  // voff: offset of each load's 16 bytes in stage 0; past: bit j set when
+  // load j's k-chunk lies at or past K in the last stage (then bit 31 of its
+  // offset is set, which sends it past every operand: it reads zero)
+  uint32_t voff[kLoadsPerWave], past = 0;
   const int nk = (K + kBK - 1) / kBK;
   const int k_last = K - (nk - 1) * kBK;          // valid k in the last stage
   {
@@ -197,26 +214,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
       // weight rows past N (and token rows past rows_g) land past the
       // buffer's end and read as zero
       voff[j] = orow < 0 ? kOutOfRange : static_cast<uint32_t>(orow * K + c * 8) * 2u;
-      pvoff[j] = c * 8 < k_last ? voff[j] : kOutOfRange;
+      past |= (c * 8 < k_last ? 0u : 1u) << j;
     }
   }
-  uint8_t* stage_region = lds + (stage_x ? 0 : kBM * kRowBytes) + row0 * kRowBytes;
+  // the token rows' ring of kNX stage buffers, then the weight rows' ring of kNW
+  const int nring = stage_x ? kNX : kNW;
+  uint8_t* ring = lds + (stage_x ? 0 : kNX * kXBytes) + row0 * kRowBytes;
 
-  // Stage kt goes to LDS buffer kt % kStages; its k offset goes in the
-  // scalar offset, so the bounds check sees the row offset, which is what
-  // separates valid rows from the rest.  The last stage takes pvoff (zeros
-  // past K).  Every iteration issues a stage so that the wait counts are
-  // fixed: stages past the end re-read the last one into a buffer nobody
-  // multiplies.
-  auto issue = [&](int kt) {
-    const int kc = min(kt, nk - 1);
-    const bool last = kc == nk - 1;
-    uint8_t* dst = stage_region + (kt % kStages) * kStageBytes;
+  // Stage s of a wave's operand goes to buffer s % nring of its ring; its k
+  // offset goes in the scalar offset, so the bounds check sees the row
+  // offset, which is what separates valid rows from the rest.  In the last
+  // stage the loads flagged in `past` read zeros (k past K).  Stages past the end re-read the last
+  // one into a buffer nobody multiplies, so every iteration has the same
+  // shape and every wait count is a constant.
+  //
+  // Issue window.  Buffer s % nring is free once every wave has passed the
+  // barrier of iteration s - nring (the barrier sits at the start of an
+  // iteration's last 16-k step, after the step's fragments were read).  So
+  // stage s is issued over kSteps positions: position 0 is that last step
+  // of iteration s - nring, positions 1.. the first steps of iteration
+  // s - nring + 1; its loads spread evenly over the first kLoadPos positions.
+  // Each operand's loads go out in the first kLoadPos positions (measured
+  // best: early enough to land, not one burst); two stages per ring suffice
+  // (a third, within the 160 KiB of LDS, measured no faster).
+  auto issue_share = [&](int st, int j_begin, int j_end) {
+    const int kc = min(st, nk - 1);
+    const uint32_t pm = kc == nk - 1 ? past : 0u;
+    uint8_t* dst = ring + (st % nring) * kXBytes;
     const int soff = kc * kBK * 2;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j)
+    for (int j = j_begin; j < j_end; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
-                                               last ? pvoff[j] : voff[j], soff, 0, 0);
+                                               voff[j] | (((pm >> j) & 1u) << 31), soff, 0, 0);
   };
 
   // ---- fragments.  A full tile: wave (wn, wm) owns 128 weight rows x 128
@@ -248,16 +276,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int kTailB = kGlu ? 2 : 1;                 // second weight block of a tail tile
 
   bf16x8_t wf[2][4], xf[2][4];
+  auto xbuf = [&](int st) -> const uint8_t* { return lds + (st % kNX) * kXBytes; };
+  auto wbuf = [&](int st) -> const uint8_t* { return lds + kNX * kXBytes + (st % kNW) * kWBytes; };
   auto load_frags = [&](int stage, int ks, int slot) {
-    const uint8_t* s = lds + (stage % kStages) * kStageBytes;
+    const uint8_t* xs = xbuf(stage);
+    const uint8_t* ws = wbuf(stage);
     const int c = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (!tail || i == 0 || i == kTailB)
-        wf[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + kBM * kRowBytes + swz(wrow[i], c)));
+        wf[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ws + swz(wrow[i], c)));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      xf[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(s + swz(xrow[j], c)));
+      xf[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xs + swz(xrow[j], c)));
   };
 
   f32x16_t acc[4][4];
@@ -324,78 +355,83 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     }
   };
 
-  // ---- pipeline: stages kt+1 .. kt+kStages-1 are in flight while stage kt
-  // is multiplied.  The first 16-k step of an iteration issues stage
-  // kt+kStages-1; the last waits for stage kt+1, meets the other waves at
-  // the barrier (after which nobody reads the buffer the next issue
-  // overwrites) and starts reading stage kt+1's first fragments.
+  // ---- pipeline.  Iteration kt multiplies stage kt.  Its last 16-k step
+  // waits for the wave's own loads of stage kt+1, meets the other waves at
+  // the barrier, and starts reading stage kt+1's first fragments.  At that
+  // barrier the loads a wave may still have in flight are the whole stages
+  // of its operand issued after stage kt+1 (nring - 2 of them).
   constexpr int kSteps = kBK / 16;
   static_assert(kSteps % 2 == 0, "fragment slots alternate per 16-k step");
-  // A full tile spreads a stage's loads over all the iteration's steps (over
-  // the first half when only two stages exist: the last step's barrier then
-  // waits for the stage issued in the same iteration).  At that barrier the
-  // loads issued after stage kt+1's may still fly: the whole stages between
-  // and the part of stage kt+kStages-1 issued before the barrier.
-  constexpr int kLoadSteps = kStages >= 3 ? kSteps : (kSteps / 2 > 0 ? kSteps / 2 : 1);
-  static_assert(kLoadsPerWave % kLoadSteps == 0, "a stage's loads split evenly over the steps");
-  constexpr int kWaitFull = wait_vm_lgkm0(
-      kStages >= 3 ? (kStages - 3) * kLoadsPerWave + (kSteps - 1) * (kLoadsPerWave / kLoadSteps) : 0);
-  // a tail tile issues a whole stage in its first step
-  constexpr int kWaitStage = wait_vm_lgkm0((kStages - 2) * kLoadsPerWave);
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) issue(st);
-  __builtin_amdgcn_s_waitcnt(kWaitStage);
+  constexpr int kLoadPos = MOE_GEMM_LOADPOS < kSteps ? MOE_GEMM_LOADPOS : kSteps;
+  static_assert(kNX >= 2 && kNW >= 2, "two stages at least");
+  // loads of window position p: [pos_begin(p), pos_begin(p + 1))
+  auto pos_begin = [](int p) { return p >= kLoadPos ? kLoadsPerWave : (kLoadsPerWave * p) / kLoadPos; };
+  auto wait_own = [&]() {
+    if (stage_x) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kNX - 2) * kLoadsPerWave));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kNW - 2) * kLoadsPerWave));
+  };
+  // prologue: stages 0 .. nring-2 whole and position 0 of stage nring-1;
+  // then stage 0 must have landed
+  for (int st = 0; st < nring - 1; ++st) issue_share(st, 0, kLoadsPerWave);
+  issue_share(nring - 1, 0, pos_begin(1));
+  __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, 0);
   if (!tail) {
     // a full tile runs each 16-k step as 8 fenced groups of two MFMAs, one
-    // fragment read for the next step and part of the stage's loads, so that
-    // no burst of loads or reads holds up the MFMAs
+    // fragment read for the next step and part of the loads, so that no
+    // burst of loads or reads holds up the MFMAs
+    int rk = 0;                                       // kt % nring
     for (int kt = 0; kt < nk; ++kt) {
-      const int ist = kt + kStages - 1;                 // stage this iteration issues
-      const int kc = min(ist, nk - 1);
-      const bool last = kc == nk - 1;
-      uint8_t* dst = stage_region + (ist % kStages) * kStageBytes;
-      const int soff = kc * kBK * 2;
+      const int rk_prev = rk == 0 ? nring - 1 : rk - 1;
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) {
         const int cur = ks & 1;
         const bool next_stage = ks + 1 == kSteps;
         if (next_stage) {
           __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(kWaitFull);
+          wait_own();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
         }
-        const uint8_t* rs = lds + ((next_stage ? kt + 1 : kt) % kStages) * kStageBytes;
+        // loads of this step: window position p of stage ist
+        const int p = next_stage ? 0 : ks + 1;
+        const int ist = next_stage ? kt + nring : kt + nring - 1;
+        const int j0 = pos_begin(p), nload = pos_begin(p + 1) - j0;
+        const int kc = min(ist, nk - 1);
+        const uint32_t pm = kc == nk - 1 ? past : 0u;
+        // buffer ist % nring: kt % nring at position 0, (kt - 1) % nring after
+        uint8_t* dst = ring + (next_stage ? rk : rk_prev) * kXBytes;
+        const int soff = kc * kBK * 2;
+        const int rstage = next_stage ? kt + 1 : kt;
+        const uint8_t* rx = xbuf(rstage);
+        const uint8_t* rw = wbuf(rstage);
         const int rc = (next_stage ? 0 : ks + 1) * 2 + (lane >> 5);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int i = q >> 1, j0 = (q & 1) * 2;
-          acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0], acc[i][j0], 0, 0, 0);
-          acc[i][j0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0 + 1], acc[i][j0 + 1], 0, 0, 0);
+          const int i = q >> 1, j0b = (q & 1) * 2;
+          acc[i][j0b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0b], acc[i][j0b], 0, 0, 0);
+          acc[i][j0b + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0b + 1], acc[i][j0b + 1], 0, 0, 0);
           // reads in the order the next step's groups use them: x0 x1 w0 x2 x3 w1 w2 w3
           constexpr int kOrder[8] = {4, 5, 0, 6, 7, 1, 2, 3};
           const int f = kOrder[q];
           if (f < 4)
-            wf[cur ^ 1][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rs + kBM * kRowBytes + swz(wrow[f], rc)));
+            wf[cur ^ 1][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rw + swz(wrow[f], rc)));
           else
-            xf[cur ^ 1][f - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rs + swz(xrow[f - 4], rc)));
-          // this step's share of the stage's loads, spread over the groups
-          constexpr int kPer = kLoadsPerWave / kLoadSteps;
-          if (ks < kLoadSteps) {
+            xf[cur ^ 1][f - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rx + swz(xrow[f - 4], rc)));
+          // this step's loads, spread over the groups
 #pragma unroll
-            for (int u = 0; u < kPer; ++u) {
-              if ((u * 8) / kPer == q) {
-                const int j = ks * kPer + u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
-                                                         last ? pvoff[j] : voff[j], soff, 0, 0);
-              }
+          for (int u = 0; u < kLoadsPerWave; ++u) {
+            if (u < nload && (u * 8) / nload == q) {
+              const int j = j0 + u;
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
+                                                       voff[j] | (((pm >> j) & 1u) << 31), soff, 0, 0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      rk = rk + 1 == nring ? 0 : rk + 1;
     }
     store_tile(std::false_type{});
   } else {
@@ -403,14 +439,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) {
         const int cur = ks & 1;
-        if (ks + 1 < kSteps) {
+        const bool next_stage = ks + 1 == kSteps;
+        if (!next_stage) {
           load_frags(kt, ks + 1, cur ^ 1);
         } else {
-          __builtin_amdgcn_s_waitcnt(kWaitStage);
+          wait_own();
           __builtin_amdgcn_s_barrier();
           load_frags(kt + 1, 0, cur ^ 1);
         }
-        if (ks == 0) issue(kt + kStages - 1);
+        const int p = next_stage ? 0 : ks + 1;
+        issue_share(next_stage ? kt + nring : kt + nring - 1, pos_begin(p), pos_begin(p + 1));
         mfmas_tail(cur);
       }
     }

@@ -183,6 +183,9 @@ FFN_CASES = [
     (3, 600, [600, 513, 255], 512, 256, 'swiglu', 'bf16'),
     (2, 130, [130, 64], 1024, 1408, 'swiglu', 'bf16'),
     (1, 700, None, 136, 200, 'gelu', 'bf16'),
+    # K not a multiple of the 64-wide k stage: last stage 40 wide; K below one stage
+    (2, 300, [300, 211], 104, 168, 'swiglu', 'bf16'),
+    (3, 90, [90, 33, 0], 40, 24, 'gelu', 'bf16'),
     (4, 40, [40, 3, 0, 17], 32, 64, 'gelu', 'f32'),
     (2, 50, [50, 9], 24, 40, 'swiglu', 'f32'),
 ]
