@@ -140,11 +140,15 @@ def main():
     fs = w.n_shared * w.d_ff_shared
     hs = torch.empty(T, fs, dtype=dt, device=dev) if fs else None
     s_out = torch.empty(T, d, dtype=dt, device=dev) if fs else None
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    # cache flush between phase repetitions: a read of 512 MiB (twice the
+    # MALL).  Reading rather than writing leaves no dirty lines whose
+    # write-back would land inside the measured kernel.
+    flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     ph = {'route': [], 'dispatch': [], 'expert_ffn': [], 'shared_ffn': [], 'combine': []}
 
     def timed(name, fn):
-        flush.zero_()
+        torch.sum(flush, dim=0, out=flush_sink)
         a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()

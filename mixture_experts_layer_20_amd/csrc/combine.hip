@@ -12,7 +12,6 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokensPerBlock = 4;
 
 template <typename T>
 struct Vec;  // 16 bytes of storage as float32 lanes
@@ -50,101 +49,115 @@ template <> struct Vec<float> {
 
 // y_t = sum_{j kept} g_tj * ye[e_tj, s_tj] (+ shared_t), float32 in j order,
 // one rounding; fallback x_t (or 0) when nothing was kept and no shared expert.
-// A workgroup takes kTokensPerBlock tokens; their (row, gate) lists are staged
-// in LDS first, then every thread streams 16-byte chunks of two (token,
-// chunk) items at a time, loading all their kept rows before summing.
+// One wavefront per token.  Lanes j < k read choice j (one round of loads);
+// a ballot gives the kept choices, whose row index and gate every lane then
+// reads from the owning lane.  Each lane streams 16-byte chunks
+// c = lane + 64 u of the row, kChunkRounds at a time, issuing the loads of
+// every kept row (up to kRowsAtOnce of them) before summing, so that a
+// wavefront keeps kChunkRounds * kRowsAtOnce KiB in flight.
+constexpr int kChunkRounds = 4;
+constexpr int kRowsAtOnce = 4;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   constexpr int V = Vec<T>::N;
-  __shared__ int64_t rows[kTokensPerBlock][32];
-  __shared__ float gts[kTokensPerBlock][32];
-  __shared__ int nkept[kTokensPerBlock];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= a.T) return;
   const int nvec = a.d / V;
   const int64_t rowbytes = static_cast<int64_t>(a.d) * sizeof(T);
   const char* __restrict__ ye = static_cast<const char*>(a.ye);
   const char* __restrict__ x = static_cast<const char*>(a.x);
   const char* __restrict__ sh = static_cast<const char*>(a.shared_out);
   char* __restrict__ y = static_cast<char*>(a.y);
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock;
-  const int nt = static_cast<int>(min<int64_t>(kTokensPerBlock, a.T - t0));
-  if (threadIdx.x < kTokensPerBlock) {
-    const int i = threadIdx.x;
-    int n = 0;
-    if (i < nt) {
-      const int64_t tk = (t0 + i) * a.k;
-      for (int j = 0; j < a.k; ++j) {
-        // a choice counts only if it is kept and its (expert, slot) is in range
-        const int e = a.idx[tk + j];
-        const int sl = a.slot[tk + j];
-        if (a.dropped[tk + j] || e < 0 || e >= a.E || sl < 0 || sl >= a.C) continue;
-        rows[i][n] = static_cast<int64_t>(e) * a.C + sl;
-        gts[i][n] = a.gates[tk + j];
-        ++n;
-      }
-    }
-    nkept[i] = n;
+
+  // choice j on lane j: kept only if not dropped and its (expert, slot) is in range
+  int64_t myrow = 0;
+  float mygate = 0.0f;
+  bool keep = false;
+  if (lane < a.k) {
+    const int64_t tk = t * a.k + lane;
+    const int e = a.idx[tk];
+    const int sl = a.slot[tk];
+    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < a.C;
+    myrow = static_cast<int64_t>(e) * a.C + sl;
+    mygate = a.gates[tk];
   }
-  __syncthreads();
-  // work items (token i, chunk c), two per thread at a time: every row of
-  // both items is loaded before either is summed
-  const int items = nt * nvec;
-  for (int w0 = threadIdx.x; w0 < items; w0 += 2 * kThreads) {
-    int it[2], ic[2], in[2];
-    bool live[2];
-    float v[2][4][V];
+  uint64_t kept = __ballot(keep);
+  const int n = __popcll(kept);
+  char* yt = y + t * rowbytes;
+
+  if (n == 0 && sh == nullptr) {
+    // fallback: the token's own row, or zeros
+    for (int c = lane; c < nvec; c += kWave) {
+      float v[V];
+      if (a.zero_fallback) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int w = w0 + u * kThreads;
-      live[u] = w < items;
-      it[u] = live[u] ? w / nvec : 0;
-      ic[u] = live[u] ? w % nvec : 0;
-      in[u] = live[u] ? nkept[it[u]] : 0;
-      const int64_t off = static_cast<int64_t>(ic[u]) * 16;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < in[u]) Vec<T>::load(ye + rows[it[u]][j] * rowbytes + off, v[u][j]);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!live[u]) continue;
-      const int i = it[u], n = in[u];
-      const int64_t t = t0 + i;
-      const int64_t off = static_cast<int64_t>(ic[u]) * 16;
-      float acc[V];
-      if (n == 0 && sh == nullptr) {
-        if (a.zero_fallback) {
-#pragma unroll
-          for (int q = 0; q < V; ++q) acc[q] = 0.0f;
-        } else {
-          Vec<T>::load(x + t * rowbytes + off, acc);
-        }
+        for (int q = 0; q < V; ++q) v[q] = 0.0f;
       } else {
+        Vec<T>::load(x + t * rowbytes + static_cast<int64_t>(c) * 16, v);
+      }
+      Vec<T>::store(yt + static_cast<int64_t>(c) * 16, v);
+    }
+    return;
+  }
+
+  for (int c0 = 0; c0 < nvec; c0 += kChunkRounds * kWave) {
+    float acc[kChunkRounds][V];
 #pragma unroll
-        for (int q = 0; q < V; ++q) acc[q] = 0.0f;
+    for (int u = 0; u < kChunkRounds; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < n) {
-            const float g = gts[i][j];
+      for (int q = 0; q < V; ++q) acc[u][q] = 0.0f;
+    // kept choices in j order, kRowsAtOnce rows per batch
+    uint64_t rest = kept;
+    for (int b = 0; b < n; b += kRowsAtOnce) {
+      const char* src[kRowsAtOnce];
+      float g[kRowsAtOnce];
+      int nb = 0;
 #pragma unroll
-            for (int q = 0; q < V; ++q) acc[q] += g * v[u][j][q];
-          }
-        }
-        // choices beyond the fourth (k > 4), in order
-        for (int j = 4; j < n; ++j) {
-          float vv[V];
-          Vec<T>::load(ye + rows[i][j] * rowbytes + off, vv);
-          const float g = gts[i][j];
-#pragma unroll
-          for (int q = 0; q < V; ++q) acc[q] += g * vv[q];
-        }
-        if (sh) {
-          float vv[V];
-          Vec<T>::load(sh + t * rowbytes + off, vv);
-#pragma unroll
-          for (int q = 0; q < V; ++q) acc[q] += vv[q];
+      for (int r = 0; r < kRowsAtOnce; ++r) {
+        src[r] = ye;
+        g[r] = 0.0f;
+        if (rest) {
+          const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+          rest &= rest - 1;
+          src[r] = ye + __shfl(myrow, j, kWave) * rowbytes;
+          g[r] = __shfl(mygate, j, kWave);
+          nb = r + 1;
         }
       }
-      Vec<T>::store(y + t * rowbytes + off, acc);
+      // raw 16-byte chunks in flight (widened only when summed)
+      uint4 raw[kRowsAtOnce][kChunkRounds];
+#pragma unroll
+      for (int r = 0; r < kRowsAtOnce; ++r)
+#pragma unroll
+        for (int u = 0; u < kChunkRounds; ++u) {
+          const int c = c0 + lane + u * kWave;
+          if (r < nb && c < nvec) raw[r][u] = *reinterpret_cast<const uint4*>(src[r] + static_cast<int64_t>(c) * 16);
+        }
+#pragma unroll
+      for (int r = 0; r < kRowsAtOnce; ++r)
+        if (r < nb)
+#pragma unroll
+          for (int u = 0; u < kChunkRounds; ++u) {
+            float v[V];
+            Vec<T>::load(&raw[r][u], v);
+#pragma unroll
+            for (int q = 0; q < V; ++q) acc[u][q] += g[r] * v[q];
+          }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunkRounds; ++u) {
+      const int c = c0 + lane + u * kWave;
+      if (c >= nvec) continue;
+      const int64_t off = static_cast<int64_t>(c) * 16;
+      if (sh) {
+        float vv[V];
+        Vec<T>::load(sh + t * rowbytes + off, vv);
+#pragma unroll
+        for (int q = 0; q < V; ++q) acc[u][q] += vv[q];
+      }
+      Vec<T>::store(yt + off, acc[u]);
     }
   }
 }
@@ -196,6 +209,7 @@ __global__ __launch_bounds__(kThreads) void losses_kernel(LossArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  constexpr int kTokensPerBlock = kThreads / kWave;     // one wavefront per token
   const unsigned grid = static_cast<unsigned>((a.T + kTokensPerBlock - 1) / kTokensPerBlock);
   if (dtype == MOE_BF16)
     combine_kernel<bf16_t><<<grid, kThreads, 0, s>>>(a);
