@@ -103,7 +103,8 @@ struct Workspace {
   double* lse2_partial;
   int32_t* fallback_partial;
   double* psum;
-  bf16_t* wsplit;
+  bf16_t* wplanes;
+  float* zraw;
   int32_t* idx_tmp;
   float* gates_tmp;
   int32_t* row_token;
@@ -136,7 +137,8 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   w.lse2_partial = static_cast<double*>(take(sizeof(double) * n_rtiles));
   w.fallback_partial = static_cast<int32_t*>(take(sizeof(int32_t) * n_tiles));
   w.psum = static_cast<double*>(take(sizeof(double) * (c.E + 1)));
-  w.wsplit = static_cast<bf16_t*>(take(sizeof(bf16_t) * 3 * ((c.E + 15) / 16 * 16) * c.d));
+  w.wplanes = static_cast<bf16_t*>(take(sizeof(bf16_t) * 4 * c.E * c.d));
+  w.zraw = static_cast<float*>(take(sizeof(float) * router_splits(c.T, c.E, c.d) * c.T * c.E));
   w.idx_tmp = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
   w.gates_tmp = static_cast<float*>(take(sizeof(float) * c.T * c.k));
   w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * c.E * C));
@@ -157,19 +159,18 @@ RouteArgs route_args(const moe_config& c, Workspace* w) {
   r.k = c.k;
   r.score = c.score;
   r.renorm = resolved_renorm(c);
+  r.zsplits = 1;
   if (w) {
     r.p_partial = w->p_partial;
     r.lse2_partial = w->lse2_partial;
-    r.wsplit = w->wsplit;
+    r.wplanes = w->wplanes;
+    r.zraw = w->zraw;
   }
   return r;
 }
 
 // router partial sums come in one row per router workgroup
-int router_tiles(const moe_config& c, bool from_x) {
-  const int tb = route_tile_tokens(c.E, c.dtype, from_x);
-  return static_cast<int>((c.T + tb - 1) / tb);
-}
+int router_tiles(const moe_config& c) { return static_cast<int>((c.T + kRouteTokens - 1) / kRouteTokens); }
 
 CapArgs cap_args(const moe_config& c, int64_t C, const Workspace& w) {
   CapArgs a{};
@@ -279,7 +280,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router
     MOE_TRY(check_ptr(w_router, "w_router", 4));
     MOE_TRY(check_ptr(logits, "logits", 4, false));
     if (c.dtype == MOE_BF16 && !ws)
-      return fail(MOE_EINVAL, "ws must not be NULL when routing bf16 x (it holds the split router weight)");
+      return fail(MOE_EINVAL, "ws must not be NULL when routing bf16 x (it holds the split router weight "
+                              "and the logits)");
   } else {
     MOE_TRY(check_ptr(logits, "logits (input when x is NULL)", 4, needT));
   }
@@ -289,7 +291,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router
   r.w_router = w_router;
   r.logit_bias = logit_bias;
   r.select_bias = select_bias;
-  r.logits = logits;
+  r.logits = x ? nullptr : logits;
+  r.logits_out = x ? logits : nullptr;
   r.probs = probs;
   r.idx = idx;
   r.gates = gates;
@@ -415,7 +418,7 @@ moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int3
   a.p_partial = w.p_partial;
   a.lse2_partial = w.lse2_partial;
   a.psum = w.psum;
-  a.n_rtiles = router_tiles(c, false);
+  a.n_rtiles = router_tiles(c);
   MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "aux-loss counts"));
   LossArgs l = loss_args(c, C, w, w.counts_tmp);
   l.fallback_partial = nullptr;
@@ -468,7 +471,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   r.w_router = wt->w_router;
   r.logit_bias = wt->logit_bias;
   r.select_bias = wt->select_bias;
-  r.logits = out->logits;
+  r.logits_out = out->logits;
   r.probs = out->probs;
   r.idx = out->idx;
   r.gates = out->gates;
@@ -484,7 +487,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   a.p_partial = w.p_partial;
   a.lse2_partial = w.lse2_partial;
   a.psum = w.psum;
-  a.n_rtiles = router_tiles(c, true);
+  a.n_rtiles = router_tiles(c);
   // the up-projection gathers token rows straight into its tiles through
   // row_token, so no dispatched copy of x is made
   a.x = nullptr;

@@ -85,14 +85,17 @@ struct RouteArgs {
   const float* w_router;      // [d,E]
   const float* logit_bias;    // [E] | null
   const float* select_bias;   // [E] | null
-  float* logits;              // [T,E] in (x null) or out | null
+  float* logits;              // [zsplits,T,E] logits in, summed over the slabs | null
+  int zsplits;                // slabs of `logits` (routing from given logits: 1)
+  float* logits_out;          // [T,E] logits out (logit bias included) | null
   float* probs;               // [T,E] | null
   int32_t* idx;               // [T,k]
   float* gates;               // [T,k]
   float* lse;                 // [T] | null
   double* p_partial;          // [n_rtiles, E] | null
   double* lse2_partial;       // [n_rtiles] | null
-  bf16_t* wsplit;             // [3, round16(E), d] split router weight (bf16 x)
+  bf16_t* wplanes;            // [4E, d] router weight split in bf16 planes (bf16 x)
+  float* zraw;                // [S,T,E] partial logits, one slab per split of d (bf16 x)
   int64_t T;
   int d, E, k;
   int score;                  // moe_score
@@ -129,7 +132,13 @@ struct GemmArgs {
   const int32_t* rows;        // [groups] | null
   int64_t rows_per_group;
   int groups, N, K;
-  int act;                    // 0 none (bias only), 1 GELU, 2 SwiGLU (B1 = gate)
+  // bf16 path only: row strides of A and B0/B1 and per-group offsets, in
+  // elements (0: rows of K elements, groups stacked contiguously)
+  int64_t lda, ldb;
+  int64_t a_gs, b_gs, c_gs;
+  int act;                    // 0 none (bias only), 1 GELU, 2 SwiGLU (B1 = gate),
+                              // 3 router planes: float32 C [rows, N/4], the sum of
+                              // each group of 4 output columns
 };
 
 struct CombineArgs {
@@ -164,14 +173,21 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_losses(const LossArgs& a, hipStream_t s);
 
-// router tile (tokens per router workgroup), shared by launcher and host
-// sizing; partial-sum arrays are sized for the smallest tile
-constexpr int kRouteTokens = 32;     // float32 router and routing from logits
-constexpr int kMinRouteTile = 16;
-__host__ __device__ inline int route_tile_tokens(int E, int dtype, bool from_x) {
-  if (!from_x || dtype != MOE_BF16) return kRouteTokens;
-  if (E <= 32) return 16;
-  return E <= 64 ? 32 : (E <= 128 ? 64 : 32);
+// The bf16 router's logits GEMM splits d into S parts (one partial-logit
+// slab each, summed in a fixed order) when the token tiles alone would not
+// give the GPU about 256 workgroups: the smallest S in {1, 2, 4, 8} that
+// does, among those that keep each part a multiple of 8 wide.
+__host__ __device__ inline int router_splits(int64_t T, int E, int d) {
+  const int64_t tiles = ((T + 255) / 256) * ((4 * static_cast<int64_t>(E) + 255) / 256);
+  int s = 1;
+  while (s < 8 && tiles * s < 256 && d % (16 * s) == 0) s *= 2;
+  return s;
 }
+
+// router tile: tokens per workgroup of the per-token routing epilogue, one
+// row of loss partial sums each (partial-sum arrays are sized for the
+// smallest tile)
+constexpr int kRouteTokens = 32;
+constexpr int kMinRouteTile = 16;
 
 }  // namespace moe

@@ -32,6 +32,8 @@
 //     ways across the waves and skips empty 32-row token blocks.
 //   * Rows at or past rows[g] and columns past N read as zero through the
 //     buffer bounds and are never stored; k past K reads 0.
+// Router mode (ACT 3): C is float32 [rows, N/4], the sum of each group of four
+// output columns (the router weight's bf16 planes; see the router).
 // float32 path: a plain LDS-tiled FMA kernel (small layers only).
 #include <type_traits>
 
@@ -158,10 +160,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   // token rows: contiguous per group, or gathered through a.gather (then A
   // is the whole [a_rows, K] input and row m of group g is A[gather[g*rpg+m]])
   const bool gathered = a.gather != nullptr;
+  const int64_t lda = a.lda ? a.lda : K, ldb = a.ldb ? a.ldb : K;
   const bf16_t* A = static_cast<const bf16_t*>(a.A) +
-                    (gathered ? 0 : static_cast<int64_t>(tc.g) * a.rows_per_group * K);
-  const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + static_cast<int64_t>(tc.g) * N * K;
-  const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + static_cast<int64_t>(tc.g) * N * K : B0;
+                    (gathered ? 0 : static_cast<int64_t>(tc.g) * (a.a_gs ? a.a_gs : a.rows_per_group * lda));
+  const int64_t bg = static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb);
+  const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + bg;
+  const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + bg : B0;
 
   const int tid = threadIdx.x;
   // the wave index is uniform: say so, so that descriptors and LDS bases live
@@ -188,8 +192,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int k_last = K - (nk - 1) * kBK;          // valid k in the last stage
   {
     const bf16_t* base = stage_x ? A : ((kGlu && wave == 2) ? B1 : B0);
-    const int64_t nbytes = stage_x ? (gathered ? a.a_rows : rows_g) * K * 2
-                                   : static_cast<int64_t>(N) * K * 2;
+    // the operand's extent from its base: the last row ends K past its start
+    const int64_t nbytes = stage_x ? ((gathered ? a.a_rows : rows_g) - 1) * lda * 2 + K * 2
+                                   : (static_cast<int64_t>(N) - 1) * ldb * 2 + K * 2;
+    const int64_t ld = stage_x ? lda : ldb;
     // the descriptor must live in scalar registers: pin its fields to lane 0
     // (they are uniform; without this the compiler may not prove it and wrap
     // every load in a loop over lanes)
@@ -212,8 +218,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         orow = orow < rows_g ? a.gather[static_cast<int64_t>(tc.g) * a.rows_per_group + orow] : -1;
       }
       // weight rows past N (and token rows past rows_g) land past the
-      // buffer's end and read as zero
-      voff[j] = orow < 0 ? kOutOfRange : static_cast<uint32_t>(orow * K + c * 8) * 2u;
+      // operand's extent and read as zero
+      voff[j] = orow < 0 ? kOutOfRange : static_cast<uint32_t>((orow * ld + c * 8) * 2);
       past |= (c * 8 < k_last ? 0u : 1u) << j;
     }
   }
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     constexpr bool kTail = decltype(tail_c)::value;
     // the stages issued past the end are still landing
     __builtin_amdgcn_s_waitcnt(0);
-    bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;
+    bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;   // ACT 0-2
     const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -330,6 +336,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
           if (n >= N) continue;
+          if (ACT == 3) {
+            // router planes: columns n..n+3 are the three exact partial
+            // products of one expert (and a zero row); their sum is the logit
+            const float z = ((acc[i][j][4 * q] + acc[i][j][4 * q + 1]) + acc[i][j][4 * q + 2]) + acc[i][j][4 * q + 3];
+            float* Cf = static_cast<float*>(a.C) +
+                        static_cast<int64_t>(tc.g) * (a.c_gs ? a.c_gs : a.rows_per_group * (N / 4));
+            Cf[m * (N / 4) + (n >> 2)] = z;
+            continue;
+          }
           f32x2_t v[2];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -537,7 +552,8 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
     switch (a.act) {
       case 0: gemm_bf16_kernel<0><<<grid, kThreads, 0, s>>>(a); break;
       case 1: gemm_bf16_kernel<1><<<grid, kThreads, 0, s>>>(a); break;
-      default: gemm_bf16_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
+      case 2: gemm_bf16_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
+      default: gemm_bf16_kernel<3><<<grid, kThreads, 0, s>>>(a); break;
     }
   } else {
     const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kFT - 1) / kFT) *

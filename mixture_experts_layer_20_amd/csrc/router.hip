@@ -1,5 +1,7 @@
-// Fused float32 router for gfx950: logits, softmax statistics, top-k and
-// gates in one pass over x, plus per-workgroup partial sums for the losses.
+// Float32 router for gfx950: logits, softmax statistics, top-k and gates,
+// plus per-workgroup partial sums for the losses.  bf16 x: the logits come
+// from the grouped GEMM on an exact bf16 split of the weight, then the
+// per-token epilogue runs over them; float32 x: one fused pass.
 //
 // Sources: "Lab 18 -- Mixture of experts" s.1 (z = x W_r, p = softmax(z),
 // renormalised vs raw gates) and s.2 (P_i, router z-loss); "Lab 01" "Where to
@@ -7,7 +9,7 @@
 // "Mixture of experts" lecture field map, stability section (router in
 // float32) and DeepSeek-V3 notes (sigmoid affinities, selection-only bias).
 //
-// Layout: one 256-thread workgroup per 32 tokens.  Each thread owns one
+// float32 x layout: one 256-thread workgroup per 32 tokens.  Each thread owns one
 // expert column e (= tid mod EP) and one residue class g of the model
 // dimension (the quads of four consecutive d that are congruent to g mod G,
 // G = 256/EP).  x is staged through LDS as float32 rows, so one 16-byte LDS
@@ -15,6 +17,9 @@
 // held in registers, and the router weight streams from L1/L2 once per
 // workgroup.  Partial dot products of the G residue classes are summed in a
 // fixed order, so the result does not depend on scheduling.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace moe {
@@ -31,7 +36,7 @@ constexpr int kDC = 128;             // model-dimension chunk staged per step
 // degree-7 Taylor polynomial of exp(r) by Horner, scaling by 2^n, then
 // 1/(1 + exp(-z)) with IEEE division.  LN2_HI is ln 2 cut to 16 significant
 // bits so n*LN2_HI is exact.  No contraction into fused multiply-adds.
-__device__ __noinline__ float exp_key(float a) {
+__device__ __forceinline__ float exp_key(float a) {
 #pragma clang fp contract(off)
   const float kInvLn2 = static_cast<float>(1.0 / 0.6931471805599453094172321);
   const float kLn2Hi = 0.693145751953125f;
@@ -63,26 +68,48 @@ __device__ __forceinline__ float log_sigmoid(float z) {
   return z >= 0.0f ? -t : z - t;
 }
 
-// Per-token epilogue, run by one wavefront: statistics, selection, gates.
-// z: LDS row of this token's logits (logit bias included), E entries.
-template <int EPL>
-__device__ void token_epilogue(const RouteArgs& a, const float* z, int64_t t, double* pacc,
-                               double& lse2acc) {
+// Reductions over a group of G consecutive lanes (G a power of two <= 64):
+// every exchange stays inside the group.
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Per-token epilogue, run by a group of G lanes (lane l of the group holds
+// experts l, l + G, ...; EPL = ceil(E / G) of them): statistics, selection,
+// gates.  z: LDS row of this token's logits (logit bias included).
+// Selection takes k rounds: the largest remaining key of the group (a float
+// max; -0 and +0 compare equal), then, by ballot, the lowest expert index
+// holding it, which is the order of the pages' top-k (key descending, ties
+// to the lower index).
+template <int G, int EPL>
+__device__ __forceinline__ void token_epilogue(const RouteArgs& a, const float* z, const float* sbias, int64_t t,
+                               double* pacc, double& lse2acc) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int li = lane & (G - 1);                  // lane within the group
+  const int gbase = lane & ~(G - 1);              // first lane of the group
   const int E = a.E, k = a.k;
   float zv[EPL];
   float m = -__builtin_huge_valf();
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int e = lane + r * kWave;
+    const int e = li + r * G;
     zv[r] = e < E ? z[e] : -__builtin_huge_valf();
     m = fmaxf(m, zv[r]);
   }
-  m = wave_max(m);
+  m = group_max<G>(m);
   float s = 0.0f;
 #pragma unroll
-  for (int r = 0; r < EPL; ++r) s += (lane + r * kWave < E) ? expf(zv[r] - m) : 0.0f;
-  s = wave_sum(s);
+  for (int r = 0; r < EPL; ++r) s += (li + r * G < E) ? expf(zv[r] - m) : 0.0f;
+  s = group_sum<G>(s);
   const float lse = m + logf(s);
 
   // full-E probabilities (softmax) or normalised sigmoid scores (log domain)
@@ -92,107 +119,136 @@ __device__ void token_epilogue(const RouteArgs& a, const float* z, int64_t t, do
     float ls[EPL];
 #pragma unroll
     for (int r = 0; r < EPL; ++r) {
-      ls[r] = (lane + r * kWave < E) ? log_sigmoid(zv[r]) : -__builtin_huge_valf();
+      ls[r] = (li + r * G < E) ? log_sigmoid(zv[r]) : -__builtin_huge_valf();
       lm = fmaxf(lm, ls[r]);
     }
-    lm = wave_max(lm);
+    lm = group_max<G>(lm);
     float qs = 0.0f;
 #pragma unroll
     for (int r = 0; r < EPL; ++r) {
-      pv[r] = (lane + r * kWave < E) ? expf(ls[r] - lm) : 0.0f;
+      pv[r] = (li + r * G < E) ? expf(ls[r] - lm) : 0.0f;
       qs += pv[r];
     }
-    qs = wave_sum(qs);
+    qs = group_sum<G>(qs);
     const float inv = 1.0f / qs;
 #pragma unroll
     for (int r = 0; r < EPL; ++r) pv[r] *= inv;
   } else {
     const float inv = 1.0f / s;
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) pv[r] = (lane + r * kWave < E) ? expf(zv[r] - m) * inv : 0.0f;
+    for (int r = 0; r < EPL; ++r) pv[r] = (li + r * G < E) ? expf(zv[r] - m) * inv : 0.0f;
   }
 
-  // selection codes
-  uint64_t code[EPL];
+  // selection keys; experts past E and experts already chosen hold -inf
+  float key[EPL];
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int e = lane + r * kWave;
+    const int e = li + r * G;
     if (e < E) {
-      float key = a.score == MOE_SIGMOID ? sigmoid_key(zv[r]) : zv[r];
-      if (a.select_bias) key = key + a.select_bias[e];
-      code[r] = select_code(key, e);
+      float kv = a.score == MOE_SIGMOID ? sigmoid_key(zv[r]) : zv[r];
+      if (sbias) kv = kv + sbias[r];
+      key[r] = kv;
     } else {
-      code[r] = 0;
+      key[r] = -__builtin_huge_valf();
     }
   }
-  int my_sel = -1;  // lane j < k keeps the j-th choice
+  const uint64_t gmask = (G == 64 ? ~0ull : ((1ull << G) - 1)) << gbase;
+  int my_sel = -1;  // lane j < k of the group keeps the j-th choice
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    float best = -__builtin_huge_valf();
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) best = code[r] > best ? code[r] : best;
-    best = wave_max_u64(best);
-    const int e = code_expert(best);
+    for (int r = 0; r < EPL; ++r) best = fmaxf(best, key[r]);
+    best = group_max<G>(best);
+    // lowest expert index holding the best key: slice r = 0 first, then 1, ...
+    int e = -1;
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const uint64_t hit = __ballot(key[r] == best) & gmask;
+      if (e < 0 && hit) e = (__ffsll(static_cast<unsigned long long>(hit)) - 1 - gbase) + r * G;
+    }
 #pragma unroll
     for (int r = 0; r < EPL; ++r)
-      if (lane + r * kWave == e) code[r] = 0;
-    if (lane == j) my_sel = e;
+      if (li + r * G == e) key[r] = -__builtin_huge_valf();
+    if (li == j) my_sel = e;
   }
 
-  // gates, computed by lanes 0..k-1
-  const bool mine = lane < k;
+  // gates, computed by lanes 0..k-1 of the group
+  const bool mine = li < k;
   const float zs = mine ? z[my_sel] : -__builtin_huge_valf();
   float g = 0.0f;
   if (a.score == MOE_SIGMOID) {
     if (a.renorm) {
       const float l = mine ? log_sigmoid(zs) : -__builtin_huge_valf();
-      const float lmx = wave_max(l);
+      const float lmx = group_max<G>(l);
       const float ex = mine ? expf(l - lmx) : 0.0f;
-      g = ex / wave_sum(ex);
+      g = ex / group_sum<G>(ex);
     } else {
       g = mine ? 1.0f / (1.0f + expf(-zs)) : 0.0f;
     }
   } else if (a.renorm) {
-    const float zmx = wave_max(zs);
+    const float zmx = group_max<G>(zs);
     const float ex = mine ? expf(zs - zmx) : 0.0f;
-    g = ex / wave_sum(ex);
+    g = ex / group_sum<G>(ex);
   } else {
     g = mine ? expf(zs - m) / s : 0.0f;
   }
   if (mine) {
-    a.idx[t * k + lane] = my_sel;
-    a.gates[t * k + lane] = g;
+    a.idx[t * k + li] = my_sel;
+    a.gates[t * k + li] = g;
   }
-  if (a.lse && lane == 0) a.lse[t] = lse;
+  if (a.lse && li == 0) a.lse[t] = lse;
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
-    const int e = lane + r * kWave;
+    const int e = li + r * G;
     if (e < E) {
       if (a.probs) a.probs[t * E + e] = pv[r];
-      if (a.x && a.logits) a.logits[t * E + e] = zv[r];
+      if (a.logits_out) a.logits_out[t * E + e] = zv[r];
       pacc[r] += static_cast<double>(pv[r]);
     }
   }
-  lse2acc += static_cast<double>(lse) * static_cast<double>(lse);
+  if (li == 0) lse2acc += static_cast<double>(lse) * static_cast<double>(lse);
 }
 
-// Epilogue for the workgroup's tokens; zrow(t) gives the LDS logits row.
-template <int EPL>
+// Epilogue for the workgroup's tokens (zbuf row i, stride zstride): token i
+// goes to group (i mod 4*TPW) of the workgroup's 4*TPW lane groups, TPW =
+// 64/G groups per wavefront.  The loss partial sums of the groups are then
+// combined in a fixed order.
+template <int G, int EPL>
 __device__ void workgroup_epilogue(const RouteArgs& a, const float* zbuf, int zstride, int64_t t0,
                                    int nt, double* red) {
+  constexpr int TPW = kWave / G;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int li = lane & (G - 1), q = lane / G;
   double pacc[EPL];
 #pragma unroll
   for (int r = 0; r < EPL; ++r) pacc[r] = 0.0;
   double lse2 = 0.0;
-  for (int i = wave; i < nt; i += kThreads / kWave)
-    token_epilogue<EPL>(a, zbuf + i * zstride, t0 + i, pacc, lse2);
-  if (!a.p_partial) return;
-  // fixed-order combination of the four wavefronts' partial sums
-  __syncthreads();
+  // the selection bias of this lane's experts, read once
+  float sb[EPL];
+  const float* sbias = nullptr;
+  if (a.select_bias) {
 #pragma unroll
-  for (int r = 0; r < EPL; ++r) {
-    const int e = lane + r * kWave;
-    if (e < a.E) red[wave * a.E + e] = pacc[r];
+    for (int r = 0; r < EPL; ++r) sb[r] = li + r * G < a.E ? a.select_bias[li + r * G] : 0.0f;
+    sbias = sb;
+  }
+  for (int i = wave * TPW + q; i < nt; i += (kThreads / kWave) * TPW)
+    token_epilogue<G, EPL>(a, zbuf + i * zstride, sbias, t0 + i, pacc, lse2);
+  if (!a.p_partial) return;
+  // groups of a wavefront first (xor over the group-index bits, fixed order),
+  // then the four wavefronts in order
+#pragma unroll
+  for (int o = G; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) pacc[r] += __shfl_xor(pacc[r], o, kWave);
+    lse2 += __shfl_xor(lse2, o, kWave);
+  }
+  __syncthreads();
+  if (q == 0) {
+#pragma unroll
+    for (int r = 0; r < EPL; ++r) {
+      const int e = li + r * G;
+      if (e < a.E) red[wave * a.E + e] = pacc[r];
+    }
   }
   if (lane == 0) red[4 * a.E + wave] = lse2;
   __syncthreads();
@@ -216,7 +272,7 @@ constexpr int kXRow = kDC + 4;
 constexpr int kXsFloats = kBT * kXRow;                 // 4224 floats
 constexpr int kRedFloats = kThreads * kBT;             // 8192 floats (G*EP*BT)
 
-template <typename XT, int EPL>
+template <typename XT, int GE, int EPL>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ __align__(16) float xs[kXsFloats];
   __shared__ __align__(16) float red[kRedFloats];
@@ -303,174 +359,124 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     red[tt * EP + ee] = v;
   }
   __syncthreads();
-  workgroup_epilogue<EPL>(a, red, EP, t0, nt, reinterpret_cast<double*>(xs));
+  workgroup_epilogue<GE, EPL>(a, red, EP, t0, nt, reinterpret_cast<double*>(xs));
 }
 
 // Routing from given logits: same epilogue, logits rows staged from memory.
-template <int EPL>
+template <int G, int EPL>
 __global__ __launch_bounds__(kThreads) void route_from_logits_kernel(RouteArgs a) {
   __shared__ float zbuf[kBT * 256];
   __shared__ double red[5 * 256];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBT;
   const int nt = static_cast<int>(min<int64_t>(kBT, a.T - t0));
+  // the slabs summed in order, then the logit bias
+  const int64_t slab = a.T * a.E;
   for (int i = threadIdx.x; i < nt * a.E; i += kThreads) {
     float v = a.logits[t0 * a.E + i];
+    for (int sp = 1; sp < a.zsplits; ++sp) v += a.logits[sp * slab + t0 * a.E + i];
     if (a.logit_bias) v += a.logit_bias[i % a.E];
     zbuf[i] = v;
   }
   __syncthreads();
-  workgroup_epilogue<EPL>(a, zbuf, a.E, t0, nt, red);
+  workgroup_epilogue<G, EPL>(a, zbuf, a.E, t0, nt, red);
 }
 
-// ---------------------------------------------------------------- bf16 x: MFMA router
+// ---------------------------------------------------------------- bf16 x: router on the GEMM
 // The router stays float32 (x is bf16, the weight float32): the weight is
 // split exactly into three bf16 planes, w = hi + mid + lo (each a bf16
 // rounding of what the previous ones leave; exact for 2^-110 < |w| < 2^127),
-// so every product x*hi, x*mid, x*lo is exact in the MFMA and only the
-// float32 accumulation order differs from a plain float32 dot product.
-// Planes are stored transposed, [3][Ep][d] (Ep = E rounded up to 16), so an
-// MFMA operand fragment is one 16-byte load.
-typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
-typedef float f32x4_r __attribute__((ext_vector_type(4)));
-
-__global__ __launch_bounds__(kThreads) void split_router_kernel(const float* w, bf16_t* wt, int d, int E, int Ep) {
-  const int64_t n = static_cast<int64_t>(Ep) * d;
+// so every product x*hi, x*mid, x*lo is exact in the bf16 MFMA.  The planes
+// are stored as the rows of a [4E, d] matrix, row 4e + p holding plane p of
+// expert e (row 4e + 3 is zero), and the grouped GEMM computes x times its
+// transpose with float32 accumulation; its router epilogue adds each group
+// of four columns (p = 0, 1, 2, 3 in that order) into logit e.  The
+// per-token epilogue then runs on those logits as for routing from logits.
+__global__ __launch_bounds__(kThreads) void split_router_kernel(const float* w, bf16_t* wp, int d, int E) {
+  const int64_t n = static_cast<int64_t>(E) * d;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kThreads) {
     const int e = static_cast<int>(i / d), k = static_cast<int>(i % d);
-    const float v = e < E ? w[static_cast<int64_t>(k) * E + e] : 0.0f;
+    const float v = w[static_cast<int64_t>(k) * E + e];
     const bf16_t hi = f32_to_bf16(v);
     const float r1 = v - bf16_to_f32(hi);
     const bf16_t mid = f32_to_bf16(r1);
     const bf16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-    wt[i] = hi;
-    wt[n + i] = mid;
-    wt[2 * n + i] = lo;
+    bf16_t* row = wp + static_cast<int64_t>(4 * e) * d + k;
+    row[0] = hi;
+    row[d] = mid;
+    row[2 * static_cast<int64_t>(d)] = lo;
+    row[3 * static_cast<int64_t>(d)] = 0;
   }
 }
 
-// One workgroup: TB tokens x all experts.  The d-range is dealt to the four
-// wavefronts in 32-wide chunks (chunk c to wave c % 4); each computes partial
-// logits with v_mfma_f32_16x16x32_bf16 (tokens as rows, experts as columns),
-// x fragments loaded straight from memory U chunks ahead.  The four partial
-// tiles are added in wave order in LDS (deterministic), then the shared
-// per-token epilogue runs.
-template <int TB, int NB, int U>
-__global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
-  constexpr int MB = TB / 16;
-  constexpr int EPAD = NB * 16;
-  constexpr int EPL = (EPAD + kWave - 1) / kWave;
-  __shared__ __align__(16) float zbuf[TB * EPAD];
-  __shared__ double red[5 * 256];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int d = a.d;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
-  const int nt = static_cast<int>(min<int64_t>(TB, a.T - t0));
-  const bf16_t* x = static_cast<const bf16_t*>(a.x);
-  const bf16_t* wt = a.wsplit;
-  const int64_t plane = static_cast<int64_t>(EPAD) * d;
-  const int koff = 8 * (lane >> 4);
-  const bf16_t* xrow[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int64_t t = min<int64_t>(t0 + mb * 16 + (lane & 15), a.T - 1);
-    xrow[mb] = x + t * d + koff;
+// calls f(integral_constant G, integral_constant EPL) for the epilogue's
+// lane-group width and experts per lane
+template <typename F>
+void template_for_group(int E, int k, F&& f) {
+  using std::integral_constant;
+  if (E <= 8) { f(integral_constant<int, 8>{}, integral_constant<int, 1>{}); return; }
+  if (k <= 16) {
+    const int epl = (E + 15) / 16;
+    if (epl <= 1) f(integral_constant<int, 16>{}, integral_constant<int, 1>{});
+    else if (epl <= 2) f(integral_constant<int, 16>{}, integral_constant<int, 2>{});
+    else if (epl <= 4) f(integral_constant<int, 16>{}, integral_constant<int, 4>{});
+    else if (epl <= 8) f(integral_constant<int, 16>{}, integral_constant<int, 8>{});
+    else f(integral_constant<int, 16>{}, integral_constant<int, 16>{});
+    return;
   }
-  const bf16_t* wrow[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wrow[nb] = wt + static_cast<int64_t>(nb * 16 + (lane & 15)) * d + koff;
-
-  f32x4_r acc[MB][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_r{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int nchunks = (d + 31) / 32;
-  for (int c0 = wave; c0 < nchunks; c0 += 4 * U) {
-    // all loads of the batch first (x from HBM, weight planes from L2), then
-    // the MFMAs, so one batch costs about one memory latency
-    bf16x8_r af[U][MB], bw[U][NB][3];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = (c0 + 4 * u) * 32;
-      const bool ok = (c0 + 4 * u) < nchunks && k + koff < d;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[u][mb] = ok ? __builtin_bit_cast(bf16x8_r, *reinterpret_cast<const uint4*>(xrow[mb] + k))
-                       : __builtin_bit_cast(bf16x8_r, make_uint4(0, 0, 0, 0));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int sp = 0; sp < 3; ++sp)
-          bw[u][nb][sp] = ok ? __builtin_bit_cast(bf16x8_r, *reinterpret_cast<const uint4*>(wrow[nb] + sp * plane + k))
-                             : __builtin_bit_cast(bf16x8_r, make_uint4(0, 0, 0, 0));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int sp = 0; sp < 3; ++sp)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][mb], bw[u][nb][sp], acc[mb][nb], 0, 0, 0);
-  }
-  // add the four partial tiles in wave order (logit bias first)
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tl = mb * 16 + 4 * (lane >> 4) + r;
-            const int e = nb * 16 + (lane & 15);
-            float base;
-            if (w == 0) base = (a.logit_bias && e < a.E) ? a.logit_bias[e] : 0.0f;
-            else base = zbuf[tl * EPAD + e];
-            zbuf[tl * EPAD + e] = base + acc[mb][nb][r];
-          }
-    }
-    __syncthreads();
-  }
-  workgroup_epilogue<EPL>(a, zbuf, EPAD, t0, nt, red);
+  const int epl = (E + 31) / 32;
+  if (epl <= 1) f(integral_constant<int, 32>{}, integral_constant<int, 1>{});
+  else if (epl <= 2) f(integral_constant<int, 32>{}, integral_constant<int, 2>{});
+  else if (epl <= 4) f(integral_constant<int, 32>{}, integral_constant<int, 4>{});
+  else f(integral_constant<int, 32>{}, integral_constant<int, 8>{});
 }
 
 template <typename XT>
 hipError_t dispatch_route(const RouteArgs& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((a.T + kBT - 1) / kBT);
-  const int epl = (a.E + kWave - 1) / kWave;
+  RouteArgs r = a;
   if (a.x != nullptr && sizeof(XT) == 2) {
-    const int ep = (a.E + 15) / 16 * 16;
-    split_router_kernel<<<min(1024, (ep * a.d + kThreads - 1) / kThreads), kThreads, 0, s>>>(
-        a.w_router, a.wsplit, a.d, a.E, ep);
-    const int tb = route_tile_tokens(a.E, MOE_BF16, true);
-    const unsigned g = static_cast<unsigned>((a.T + tb - 1) / tb);
-    // tile tokens x expert blocks x chunks per batch: sized so one batch's
-    // fragments fit in registers beside the accumulators
-    if (a.E <= 16) route_mfma_kernel<16, 1, 8><<<g, kThreads, 0, s>>>(a);
-    else if (a.E <= 32) route_mfma_kernel<16, 2, 4><<<g, kThreads, 0, s>>>(a);
-    else if (a.E <= 64) route_mfma_kernel<32, 4, 2><<<g, kThreads, 0, s>>>(a);
-    else if (a.E <= 128) route_mfma_kernel<64, 8, 1><<<g, kThreads, 0, s>>>(a);
-    else route_mfma_kernel<32, 16, 1><<<g, kThreads, 0, s>>>(a);
-    return hipGetLastError();
-  }
-  if (a.x == nullptr) {
-    switch (epl) {
-      case 1: route_from_logits_kernel<1><<<grid, kThreads, 0, s>>>(a); break;
-      case 2: route_from_logits_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
-      default: route_from_logits_kernel<4><<<grid, kThreads, 0, s>>>(a); break;
+    const int64_t n = static_cast<int64_t>(a.E) * a.d;
+    split_router_kernel<<<static_cast<unsigned>(std::min<int64_t>(1024, (n + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
+        a.w_router, a.wplanes, a.d, a.E);
+    // logits = x [T, d] . planes [4E, d]^T: the d range split into S parts
+    // (the GEMM's groups: columns [s*dc, (s+1)*dc) of both operands, partial
+    // logits to slab s), in row blocks whose part of x stays below 2^30
+    // elements (the GEMM addresses an operand through one buffer descriptor)
+    const int S = router_splits(a.T, a.E, a.d);
+    const int dc = a.d / S;
+    const int64_t max_rows = ((int64_t{1} << 30) - 1) / a.d / 256 * 256;
+    for (int64_t r0 = 0; r0 < a.T; r0 += max_rows) {
+      GemmArgs g{};
+      g.A = static_cast<const bf16_t*>(a.x) + r0 * a.d;
+      g.B0 = a.wplanes;
+      g.C = a.zraw + r0 * a.E;
+      g.rows_per_group = std::min<int64_t>(max_rows, a.T - r0);
+      g.groups = S;
+      g.N = 4 * a.E;
+      g.K = dc;
+      g.lda = a.d;
+      g.ldb = a.d;
+      g.a_gs = dc;
+      g.b_gs = dc;
+      g.c_gs = a.T * a.E;
+      g.act = 3;
+      const hipError_t e = launch_gemm(g, MOE_BF16, s);
+      if (e != hipSuccess) return e;
     }
-  } else {
-    switch (epl) {
-      case 1: route_kernel<XT, 1><<<grid, kThreads, 0, s>>>(a); break;
-      case 2: route_kernel<XT, 2><<<grid, kThreads, 0, s>>>(a); break;
-      default: route_kernel<XT, 4><<<grid, kThreads, 0, s>>>(a); break;
-    }
+    r.logits = a.zraw;
+    r.zsplits = S;
   }
+  // per-token epilogue: one token per group of G lanes, EPL experts per lane.
+  // Small groups let one wavefront instruction serve several tokens and
+  // shorten every reduction: G = 8 for E <= 8, else 16 (32 when k > 16,
+  // since lanes j < k of a group hold the choices).
+  auto launch = [&](auto g_c, auto epl_c) {
+    constexpr int G = decltype(g_c)::value, EPL = decltype(epl_c)::value;
+    if (r.x == nullptr || sizeof(XT) == 2) route_from_logits_kernel<G, EPL><<<grid, kThreads, 0, s>>>(r);
+    else route_kernel<XT, G, EPL><<<grid, kThreads, 0, s>>>(r);
+  };
+  template_for_group(a.E, a.k, launch);
   return hipGetLastError();
 }
 
