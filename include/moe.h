@@ -115,8 +115,9 @@ MOE_API size_t moe_workspace_bytes(const moe_config* cfg);
  *   gates       [T,k] float32 gate of each selected expert        (required)
  *   lse         [T] float32 log-sum-exp of the logits, or NULL
  *   ws          workspace: required when x is bf16 (it holds the router
- *               weight split into three bf16 planes for the matrix cores);
- *               otherwise may be NULL (then no loss partials are kept) */
+ *               weight split into three bf16 planes for the matrix cores and
+ *               the float32 logits before the epilogue); otherwise may be
+ *               NULL (then no loss partials are kept) */
 MOE_API moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router,
                      const float* logit_bias, const float* select_bias, float* logits,
                      float* probs, int32_t* idx, float* gates, float* lse, void* ws,
