@@ -71,7 +71,19 @@ constexpr int kXBytes = kBM * kRowBytes;                   // one token-row stag
 constexpr int kWBytes = kBW * kRowBytes;                   // one weight-row stage (32 KiB)
 constexpr int kLdsBytes = kNX * kXBytes + kNW * kWBytes;   // 128 KiB
 constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows one wave instruction fills
-constexpr int kLoadsPerWave = 128 / kRowsPerLoad;          // per stage: each wave stages 128 rows
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+constexpr int kWaves = MOE_GEMM_WAVES;                     // wavefronts per workgroup (4 or 8)
+constexpr int kThreadsB = kWaves * 64;                     // bf16 kernel's workgroup
+constexpr int kHalf = kWaves / 2;                          // waves staging each operand
+constexpr int kSRows = 256 / kHalf;                        // tile rows one wave stages
+constexpr int kLoadsPerWave = kSRows / kRowsPerLoad;       // load instructions per stage
+constexpr int kXR = 256 / kHalf;                           // token rows of one wave's output
+constexpr int kXB = kXR / 32;                              // its 32-row token blocks
+constexpr int kPairs = 4 * kXB / 2;                        // MFMA pairs (groups) per 16-k step
+constexpr int kFrags = 4 + kXB;                            // fragment reads per 16-k step
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 wavefronts");
 static_assert(kXBytes == kWBytes, "both rings use one buffer size");
 static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
 static_assert(kLoadsPerWave <= 32, "one bit per load in the past-K mask");
@@ -133,8 +145,30 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Fragment reads of a 16-k step in the order the step's MFMA groups consume
+// them (token fragments are ids 4.., weight fragments 0..3), and the group
+// that issues read r: the reads are spread over the groups, earliest first.
+struct FragPlan {
+  int order[kFrags];
+  int group[kFrags];
+};
+constexpr FragPlan make_frag_plan() {
+  FragPlan f{};
+  bool seen[kFrags] = {};
+  int n = 0;
+  for (int q = 0; q < kPairs; ++q) {
+    const int i = (2 * q) / kXB, j0 = (2 * q) % kXB;
+    const int need[3] = {4 + j0, 4 + j0 + 1, i};
+    for (int u = 0; u < 3; ++u)
+      if (!seen[need[u]]) { seen[need[u]] = true; f.order[n++] = need[u]; }
+  }
+  for (int r = 0; r < kFrags; ++r) f.group[r] = (r * kPairs) / kFrags;
+  return f;
+}
+constexpr FragPlan kPlan = make_frag_plan();
+
 template <int ACT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreadsB, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr bool kGlu = ACT == 2;
   constexpr int kNOut = kGlu ? kBW / 2 : kBW;   // output columns per tile
   __shared__ __align__(1024) uint8_t lds[kLdsBytes];
@@ -173,16 +207,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- staging: direct global -> LDS, 16 bytes per lane, 1 KiB per
-  // wavefront instruction (kRowsPerLoad rows of kBK k).  Waves 0-1 stage the
-  // 256 token rows, waves 2-3 the 256 weight rows (for SwiGLU: wave 2 the
-  // gate rows, wave 3 the up rows).  Lane i of an instruction fills LDS bytes
+  // wavefront instruction (kRowsPerLoad rows of kBK k).  The first kHalf
+  // waves stage the 256 token rows, the others the 256 weight rows (for
+  // SwiGLU the first 128 weight rows are gate rows, the rest the matching up
+  // rows), kSRows rows each.  Lane i of an instruction fills LDS bytes
   // [16i, 16i+16) of its row block: row i/kChunks, physical chunk i%kChunks,
   // which holds logical k-chunk (i%kChunks) ^ swizzle(row).  Rows past the
   // operand's end (ragged expert rows, columns past N) and k past K read as
   // zero through the buffer bounds.
-  const bool stage_x = wave < 2;
+  const bool stage_x = wave < kHalf;
   const int lr = lane / kChunks, pc = lane % kChunks;
-  const int row0 = (wave & 1) * 128;               // first tile row this wave stages
+  const int row0 = (wave % kHalf) * kSRows;        // first tile row this wave stages
   __amdgpu_buffer_rsrc_t rsrc;
   // voff: offset of each load's 16 bytes in stage 0; past: bit j set when
   // load j's k-chunk lies at or past K in the last stage (then bit 31 of its
@@ -191,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   const int nk = (K + kBK - 1) / kBK;
   const int k_last = K - (nk - 1) * kBK;          // valid k in the last stage
   {
-    const bf16_t* base = stage_x ? A : ((kGlu && wave == 2) ? B1 : B0);
+    const bf16_t* base = stage_x ? A : ((kGlu && row0 < 128) ? B1 : B0);
     // the operand's extent from its base: the last row ends K past its start
     const int64_t nbytes = stage_x ? ((gathered ? a.a_rows : rows_g) - 1) * lda * 2 + K * 2
                                    : (static_cast<int64_t>(N) - 1) * ldb * 2 + K * 2;
@@ -205,9 +240,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
     const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(nbytes));
     rsrc = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<void*>((static_cast<uint64_t>(bhi) << 32) | blo), (short)0, nrec, kRsrcWord3);
-    // first operand row of this wave's block 0 (token rows: m0; weight rows:
-    // n0, plus 128 for the second half when not SwiGLU)
-    const int orow0 = stage_x ? m0 + row0 : (kGlu ? n0 : n0 + row0);
+    // first operand row of this wave's block 0 (token rows: m0 + row0;
+    // weight rows: n0 + row0, or for SwiGLU n0 + row0 mod 128 of its matrix)
+    const int orow0 = stage_x ? m0 + row0 : (kGlu ? n0 + (row0 & 127) : n0 + row0);
 #pragma unroll
     for (int j = 0; j < kLoadsPerWave; ++j) {
       const int trow = row0 + j * kRowsPerLoad + lr;             // tile row (sets the swizzle)
@@ -230,19 +265,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   // Stage s of a wave's operand goes to buffer s % nring of its ring; its k
   // offset goes in the scalar offset, so the bounds check sees the row
   // offset, which is what separates valid rows from the rest.  In the last
-  // stage the loads flagged in `past` read zeros (k past K).  Stages past the end re-read the last
-  // one into a buffer nobody multiplies, so every iteration has the same
-  // shape and every wait count is a constant.
+  // stage the loads flagged in `past` read zeros (k past K).  Stages past the
+  // end re-read the last one into a buffer nobody multiplies, so every
+  // iteration has the same shape and every wait count is a constant.
   //
   // Issue window.  Buffer s % nring is free once every wave has passed the
   // barrier of iteration s - nring (the barrier sits at the start of an
   // iteration's last 16-k step, after the step's fragments were read).  So
   // stage s is issued over kSteps positions: position 0 is that last step
   // of iteration s - nring, positions 1.. the first steps of iteration
-  // s - nring + 1; its loads spread evenly over the first kLoadPos positions.
-  // Each operand's loads go out in the first kLoadPos positions (measured
-  // best: early enough to land, not one burst); two stages per ring suffice
-  // (a third, within the 160 KiB of LDS, measured no faster).
+  // s - nring + 1; its loads spread evenly over the first kLoadPos positions
+  // (measured best: early enough to land, not one burst).
   auto issue_share = [&](int st, int j_begin, int j_end) {
     const int kc = min(st, nk - 1);
     const uint32_t pm = kc == nk - 1 ? past : 0u;
@@ -253,85 +286,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
                                                voff[j] | (((pm >> j) & 1u) << 31), soff, 0, 0);
   };
 
-  // ---- fragments.  A full tile: wave (wn, wm) owns 128 weight rows x 128
-  // token rows (4 x 4 MFMA blocks).  A tail tile with at most 128 valid token
-  // rows: the four waves split the weight rows four ways and all take the
-  // valid 32-row token blocks, so an expert's last, mostly empty tile costs
-  // about (valid blocks)/8 of a full one instead of all of it.
-  // Block i of a wave: weight rows wrow[i] (+ lane%32), output columns
-  // ncol[i]; for SwiGLU blocks 0-1 are gate rows, 2-3 the matching up rows.
+  // ---- fragments.  Wave (wn, wm) owns 128 weight rows (4 MFMA blocks of 32)
+  // x kXR token rows (kXB blocks of 32).  Block i: weight rows wrow[i] (+
+  // lane%32), output columns ncol[i]; for SwiGLU blocks 0-1 are gate rows,
+  // 2-3 the matching up rows.  In a partial tile (fewer than 256 valid token
+  // rows) a wave multiplies only its token blocks that hold valid rows.
   const int wn = wave & 1, wm = wave >> 1;
   const int valid_rows = static_cast<int>(min<int64_t>(rows_g - m0, kBM));
-  const bool tail = valid_rows <= 128;
-  const int mblocks = (valid_rows + 31) / 32;          // valid 32-row token blocks
-  int wrow[4], ncol[4], xrow[4];
+  const bool partial = valid_rows < kBM;
+  const int xbv = max(0, min(kXB, (valid_rows - wm * kXR + 31) / 32));   // valid blocks of this wave
+  int wrow[4], ncol[4], xrow[kXB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (!tail) {
-      ncol[i] = kGlu ? wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
-      wrow[i] = kGlu ? (i >> 1) * 128 + ncol[i] : ncol[i];
-    } else {
-      // blocks 0 and (SwiGLU: 2, else 1) are used
-      ncol[i] = kGlu ? wave * 32 : wave * 64 + (i & 1) * 32;
-      wrow[i] = kGlu ? (i >> 1) * 128 + ncol[i] : ncol[i];
-    }
-    wrow[i] += lane & 31;
+    ncol[i] = kGlu ? wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+    wrow[i] = (kGlu ? (i >> 1) * 128 + ncol[i] : ncol[i]) + (lane & 31);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) xrow[j] = (tail ? 0 : wm * 128) + j * 32 + (lane & 31);
-  constexpr int kTailB = kGlu ? 2 : 1;                 // second weight block of a tail tile
+  for (int j = 0; j < kXB; ++j) xrow[j] = wm * kXR + j * 32 + (lane & 31);
 
-  bf16x8_t wf[2][4], xf[2][4];
+  bf16x8_t wf[2][4], xf[2][kXB];
   auto xbuf = [&](int st) -> const uint8_t* { return lds + (st % kNX) * kXBytes; };
   auto wbuf = [&](int st) -> const uint8_t* { return lds + kNX * kXBytes + (st % kNW) * kWBytes; };
-  auto load_frags = [&](int stage, int ks, int slot) {
-    const uint8_t* xs = xbuf(stage);
-    const uint8_t* ws = wbuf(stage);
-    const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (!tail || i == 0 || i == kTailB)
-        wf[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ws + swz(wrow[i], c)));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      xf[slot][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xs + swz(xrow[j], c)));
+  auto read_frag = [&](const uint8_t* xs, const uint8_t* ws, int c, int slot, int f) {
+    if (f < 4)
+      wf[slot][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ws + swz(wrow[f], c)));
+    else
+      xf[slot][f - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xs + swz(xrow[f - 4], c)));
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][kXB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kXB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto mfmas_tail = [&](int slot) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < mblocks) {
-        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][0], xf[slot][j], acc[0][j], 0, 0, 0);
-        acc[kTailB][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][kTailB], xf[slot][j], acc[kTailB][j], 0, 0, 0);
-      }
-    }
-  };
-
   // ---- epilogue: lane holds, for block (i, j), output columns
   // ncol[i] + 8q + 4*(lane/32) + {0..3} of token row xrow[j] (tile-relative).
-  // Each path has its own copy, so that the accumulators of the two paths
+  // Each loop instance has its own copy, so that the accumulators of the two
   // are never merged into one set of registers.
-  auto store_tile = [&](auto tail_c) __attribute__((always_inline)) {
-    constexpr bool kTail = decltype(tail_c)::value;
+  auto store_tile = [&]() __attribute__((always_inline)) {
     // the stages issued past the end are still landing
     __builtin_amdgcn_s_waitcnt(0);
     bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;   // ACT 0-2
     const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kXB; ++j) {
       const int64_t m = m0 + xrow[j];
       if (m >= rows_g) continue;
 #pragma unroll
       for (int i = 0; i < (kGlu ? 2 : 4); ++i) {
-        if (kTail && i != 0 && i != kTailB) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
@@ -391,11 +396,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
   issue_share(nring - 1, 0, pos_begin(1));
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
-  load_frags(0, 0, 0);
-  if (!tail) {
-    // a full tile runs each 16-k step as 8 fenced groups of two MFMAs, one
-    // fragment read for the next step and part of the loads, so that no
-    // burst of loads or reads holds up the MFMAs
+  {
+    const int c0 = lane >> 5;
+#pragma unroll
+    for (int f = 0; f < kFrags; ++f) read_frag(xbuf(0), wbuf(0), c0, 0, f);
+  }
+  // Each 16-k step runs as kPairs fenced groups of two MFMAs, the step's
+  // share of the next step's fragment reads and of the loads, so that no
+  // burst of loads or reads holds up the MFMAs.  A partial tile skips the
+  // MFMAs of token blocks without valid rows.
+  auto run = [&](auto partial_c) __attribute__((always_inline)) {
+    constexpr bool kPartial = decltype(partial_c)::value;
     int rk = 0;                                       // kt % nring
     for (int kt = 0; kt < nk; ++kt) {
       const int rk_prev = rk == 0 ? nring - 1 : rk - 1;
@@ -423,21 +434,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
         const uint8_t* rw = wbuf(rstage);
         const int rc = (next_stage ? 0 : ks + 1) * 2 + (lane >> 5);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int i = q >> 1, j0b = (q & 1) * 2;
-          acc[i][j0b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0b], acc[i][j0b], 0, 0, 0);
-          acc[i][j0b + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][j0b + 1], acc[i][j0b + 1], 0, 0, 0);
-          // reads in the order the next step's groups use them: x0 x1 w0 x2 x3 w1 w2 w3
-          constexpr int kOrder[8] = {4, 5, 0, 6, 7, 1, 2, 3};
-          const int f = kOrder[q];
-          if (f < 4)
-            wf[cur ^ 1][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rw + swz(wrow[f], rc)));
-          else
-            xf[cur ^ 1][f - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rx + swz(xrow[f - 4], rc)));
+        for (int q = 0; q < kPairs; ++q) {
+          const int i = (2 * q) / kXB, jb = (2 * q) % kXB;
+          if (!kPartial || jb < xbv)
+            acc[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb], acc[i][jb], 0, 0, 0);
+          if (!kPartial || jb + 1 < xbv)
+            acc[i][jb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb + 1], acc[i][jb + 1], 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < kFrags; ++r)
+            if (kPlan.group[r] == q) read_frag(rx, rw, rc, cur ^ 1, kPlan.order[r]);
           // this step's loads, spread over the groups
 #pragma unroll
           for (int u = 0; u < kLoadsPerWave; ++u) {
-            if (u < nload && (u * 8) / nload == q) {
+            if (u < nload && (u * kPairs) / nload == q) {
               const int j = j0 + u;
               __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
                                                        voff[j] | (((pm >> j) & 1u) << 31), soff, 0, 0);
@@ -448,27 +457,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs a) {
       }
       rk = rk + 1 == nring ? 0 : rk + 1;
     }
-    store_tile(std::false_type{});
-  } else {
-    for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-      for (int ks = 0; ks < kSteps; ++ks) {
-        const int cur = ks & 1;
-        const bool next_stage = ks + 1 == kSteps;
-        if (!next_stage) {
-          load_frags(kt, ks + 1, cur ^ 1);
-        } else {
-          wait_own();
-          __builtin_amdgcn_s_barrier();
-          load_frags(kt + 1, 0, cur ^ 1);
-        }
-        const int p = next_stage ? 0 : ks + 1;
-        issue_share(next_stage ? kt + nring : kt + nring - 1, pos_begin(p), pos_begin(p + 1));
-        mfmas_tail(cur);
-      }
-    }
-    store_tile(std::true_type{});
-  }
+    store_tile();
+  };
+  if (!partial) run(std::false_type{});
+  else run(std::true_type{});
 }
 
 // ------------------------------------------------------------------ float32
@@ -550,10 +542,10 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
                           ((a.N + nout - 1) / nout);
     const unsigned grid = static_cast<unsigned>((tiles + 255) / 256 * 256);
     switch (a.act) {
-      case 0: gemm_bf16_kernel<0><<<grid, kThreads, 0, s>>>(a); break;
-      case 1: gemm_bf16_kernel<1><<<grid, kThreads, 0, s>>>(a); break;
-      case 2: gemm_bf16_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
-      default: gemm_bf16_kernel<3><<<grid, kThreads, 0, s>>>(a); break;
+      case 0: gemm_bf16_kernel<0><<<grid, kThreadsB, 0, s>>>(a); break;
+      case 1: gemm_bf16_kernel<1><<<grid, kThreadsB, 0, s>>>(a); break;
+      case 2: gemm_bf16_kernel<2><<<grid, kThreadsB, 0, s>>>(a); break;
+      default: gemm_bf16_kernel<3><<<grid, kThreadsB, 0, s>>>(a); break;
     }
   } else {
     const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kFT - 1) / kFT) *
