@@ -329,27 +329,55 @@ __global__ __launch_bounds__(kThreadsB, 1) void gemm_bf16_kernel(GemmArgs a) {
   auto store_tile = [&]() __attribute__((always_inline)) {
     // the stages issued past the end are still landing
     __builtin_amdgcn_s_waitcnt(0);
-    bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;   // ACT 0-2
+    if (ACT == 3) {
+      // router planes: columns n..n+3 are the three exact partial products
+      // of one expert (and a zero row); their sum is the logit
+      float* Cf = static_cast<float*>(a.C) +
+                  static_cast<int64_t>(tc.g) * (a.c_gs ? a.c_gs : a.rows_per_group * (N / 4));
+#pragma unroll
+      for (int j = 0; j < kXB; ++j) {
+        const int64_t m = m0 + xrow[j];
+        if (m >= rows_g) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
+            if (n >= N) continue;
+            Cf[m * (N / 4) + (n >> 2)] =
+                ((acc[i][j][4 * q] + acc[i][j][4 * q + 1]) + acc[i][j][4 * q + 2]) + acc[i][j][4 * q + 3];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return;
+    }
+    // Output through LDS, 32 token rows at a time per wave: the finished
+    // bf16 values go to the wave's own LDS region, come back row-contiguous
+    // and leave as whole row segments (16 bytes per lane, kOut*2 contiguous
+    // bytes per row).  Stored straight from the MFMA layout, one instruction
+    // would write 8 bytes into each of 32 rows, and the L2 would take many
+    // more, smaller write requests.
+    bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;
     const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
+    constexpr int kOut = kGlu ? 64 : 128;              // output columns per wave
+    constexpr int kPitch = kOut * 2 + 16;              // padded LDS row (bytes)
+    constexpr int kLanesPerRow = kOut * 2 / 16;
+    constexpr int kRowsPerInst = kWave / kLanesPerRow;
+    static_assert(kWaves * 32 * kPitch <= kLdsBytes, "epilogue staging must fit the stage buffers");
+    __syncthreads();                                   // every wave is done with the stage buffers
+    uint8_t* scr = lds + wave * 32 * kPitch;
+    const int colw = wn * kOut;                        // the wave's first tile column
 #pragma unroll
     for (int j = 0; j < kXB; ++j) {
-      const int64_t m = m0 + xrow[j];
-      if (m >= rows_g) continue;
+      const int rowbase = wm * kXR + j * 32;
+      if (m0 + rowbase >= rows_g) break;
 #pragma unroll
       for (int i = 0; i < (kGlu ? 2 : 4); ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const int col = ncol[i] - colw + 8 * q + 4 * (lane >> 5);
           const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
-          if (n >= N) continue;
-          if (ACT == 3) {
-            // router planes: columns n..n+3 are the three exact partial
-            // products of one expert (and a zero row); their sum is the logit
-            const float z = ((acc[i][j][4 * q] + acc[i][j][4 * q + 1]) + acc[i][j][4 * q + 2]) + acc[i][j][4 * q + 3];
-            float* Cf = static_cast<float*>(a.C) +
-                        static_cast<int64_t>(tc.g) * (a.c_gs ? a.c_gs : a.rows_per_group * (N / 4));
-            Cf[m * (N / 4) + (n >> 2)] = z;
-            continue;
-          }
           f32x2_t v[2];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -357,7 +385,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void gemm_bf16_kernel(GemmArgs a) {
             if (ACT == 2) {
               x = silu_fast(x) * acc[i + 2][j][4 * q + r];
             } else {
-              if (bias) x += bf16_to_f32(bias[n + r]);
+              if (bias && n + r < N) x += bf16_to_f32(bias[n + r]);
               if (ACT == 1) x = gelu_erf(x);
             }
             v[r >> 1][r & 1] = x;
@@ -366,11 +394,22 @@ __global__ __launch_bounds__(kThreadsB, 1) void gemm_bf16_kernel(GemmArgs a) {
           uint2 packed;
           packed.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[0], bf16x2_t));
           packed.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[1], bf16x2_t));
-          *reinterpret_cast<uint2*>(C + m * N + n) = packed;
+          *reinterpret_cast<uint2*>(scr + (lane & 31) * kPitch + col * 2) = packed;
         }
         // one block at a time: keeps the accumulators' copies out of the
         // VGPRs until they are needed
         __builtin_amdgcn_sched_barrier(0);
+      }
+      // the wave reads back only what it wrote itself
+#pragma unroll
+      for (int pp = 0; pp < 32 / kRowsPerInst; ++pp) {
+        const int row = pp * kRowsPerInst + lane / kLanesPerRow;
+        const int ch = lane % kLanesPerRow;
+        const uint4 v = *reinterpret_cast<const uint4*>(scr + row * kPitch + ch * 16);
+        const int64_t m = m0 + rowbase + row;
+        const int n = n0 + colw + ch * 8;
+        // N is a multiple of 8: a segment is wholly inside or wholly past it
+        if (m < rows_g && n < N) *reinterpret_cast<uint4*>(C + m * N + n) = v;
       }
     }
   };
