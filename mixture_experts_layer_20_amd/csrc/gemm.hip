@@ -7,14 +7,16 @@
 // field map, systems section (small ragged per-expert matmuls).
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 with float32 accumulation.
-//   * Workgroup tile: 256 token rows x 256 weight rows x 64 (k), 4 wavefronts,
-//     each owning 128 x 128 of the output (4 x 4 MFMA blocks, 256 float32
-//     accumulators per lane).  For SwiGLU the 256 weight rows are 128 gate
-//     rows and the 128 matching up rows, so the epilogue has g and u of the
-//     same output element in the same lane and register.
+//   * Workgroup tile: 256 token rows x 256 weight rows x 64 (k), 8 wavefronts
+//     (two per SIMD), each owning 128 weight rows x 64 token rows of the
+//     output (4 x 2 MFMA blocks, 128 float32 accumulators per lane).  For
+//     SwiGLU the 256 weight rows are 128 gate rows and the 128 matching up
+//     rows, so the epilogue has g and u of the same output element in the
+//     same lane and register.
 //   * The MFMA's first operand is the weight tile and its second the token
 //     tile, so each lane ends with four consecutive output columns of one
-//     token row: 8-byte bf16 stores.
+//     token row.  The epilogue stages the bf16 results through LDS and
+//     stores whole row segments.
 //   * Direct global -> LDS loads (buffer_load ... lds), 16 bytes per lane:
 //     one wavefront instruction fills 8 rows x 128 bytes, i.e. whole cache
 //     lines (the load path moves about 1.7x the bytes per cycle it moves
@@ -28,8 +30,8 @@
 //     reach XCDs round-robin), so the ~32 tiles an XCD runs at once share 4
 //     token panels and 8 weight panels in its L2 while every XCD gets an even
 //     share of every expert.
-//   * A tail tile (at most 128 valid token rows) splits the weight rows four
-//     ways across the waves and skips empty 32-row token blocks.
+//   * A partial tile (an expert's last, fewer than 256 valid token rows)
+//     skips the MFMAs of 32-row token blocks without valid rows.
 //   * Rows at or past rows[g] and columns past N read as zero through the
 //     buffer bounds and are never stored; k past K reads 0.
 // Router mode (ACT 3): C is float32 [rows, N/4], the sum of each group of four
@@ -71,22 +73,50 @@ constexpr int kXBytes = kBM * kRowBytes;                   // one token-row stag
 constexpr int kWBytes = kBW * kRowBytes;                   // one weight-row stage (32 KiB)
 constexpr int kLdsBytes = kNX * kXBytes + kNW * kWBytes;   // 128 KiB
 constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows one wave instruction fills
-#ifndef MOE_GEMM_WAVES
-#define MOE_GEMM_WAVES 8
-#endif
-constexpr int kWaves = MOE_GEMM_WAVES;                     // wavefronts per workgroup (4 or 8)
-constexpr int kThreadsB = kWaves * 64;                     // bf16 kernel's workgroup
-constexpr int kHalf = kWaves / 2;                          // waves staging each operand
-constexpr int kSRows = 256 / kHalf;                        // tile rows one wave stages
-constexpr int kLoadsPerWave = kSRows / kRowsPerLoad;       // load instructions per stage
-constexpr int kXR = 256 / kHalf;                           // token rows of one wave's output
-constexpr int kXB = kXR / 32;                              // its 32-row token blocks
-constexpr int kPairs = 4 * kXB / 2;                        // MFMA pairs (groups) per 16-k step
-constexpr int kFrags = 4 + kXB;                            // fragment reads per 16-k step
-static_assert(kWaves == 4 || kWaves == 8, "4 or 8 wavefronts");
+// Wavefronts per workgroup, per kernel: 8 (two per SIMD, each owning 64
+// token rows x 128 weight rows of the output) or 4 (one per SIMD, 128 x
+// 128: a third fewer LDS fragment reads per flop, but one wave per SIMD to
+// hide latency).  Measured per GEMM; see launch_gemm.
+template <int W>
+struct Geo {
+  static_assert(W == 4 || W == 8, "4 or 8 wavefronts");
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = W * 64;
+  static constexpr int kHalf = W / 2;                         // waves staging each operand
+  static constexpr int kSRows = 256 / kHalf;                  // tile rows one wave stages
+  static constexpr int kLoadsPerWave = kSRows / kRowsPerLoad; // load instructions per stage
+  static constexpr int kXR = 256 / kHalf;                     // token rows of one wave's output
+  static constexpr int kXB = kXR / 32;                        // its 32-row token blocks
+  static constexpr int kPairs = 4 * kXB / 2;                  // MFMA pairs (groups) per 16-k step
+  static constexpr int kFrags = 4 + kXB;                      // fragment reads per 16-k step
+  static_assert(kLoadsPerWave <= 32, "one bit per load in the past-K mask");
+  
+  // Fragment reads of a 16-k step in the order the step's MFMA groups
+  // consume them (token fragments are ids 4.., weight fragments 0..3), and
+  // the group that issues read r: the reads are spread over the groups,
+  // earliest first.
+  struct FragPlan {
+    int order[kFrags];
+    int group[kFrags];
+  };
+  static constexpr FragPlan frag_plan() {
+    FragPlan f{};
+    bool seen[kFrags] = {};
+    int n = 0;
+    for (int q = 0; q < kPairs; ++q) {
+      const int i = (2 * q) / kXB, j0 = (2 * q) % kXB;
+      const int need[3] = {4 + j0, 4 + j0 + 1, i};
+      for (int u = 0; u < 3; ++u)
+        if (!seen[need[u]]) { seen[need[u]] = true; f.order[n++] = need[u]; }
+    }
+    for (int r = 0; r < kFrags; ++r) f.group[r] = (r * kPairs) / kFrags;
+    return f;
+  }
+};
+template <int W>
+constexpr typename Geo<W>::FragPlan kPlanOf = Geo<W>::frag_plan();
 static_assert(kXBytes == kWBytes, "both rings use one buffer size");
 static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
-static_assert(kLoadsPerWave <= 32, "one bit per load in the past-K mask");
 
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
@@ -145,30 +175,28 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Fragment reads of a 16-k step in the order the step's MFMA groups consume
-// them (token fragments are ids 4.., weight fragments 0..3), and the group
-// that issues read r: the reads are spread over the groups, earliest first.
-struct FragPlan {
-  int order[kFrags];
-  int group[kFrags];
-};
-constexpr FragPlan make_frag_plan() {
-  FragPlan f{};
-  bool seen[kFrags] = {};
-  int n = 0;
-  for (int q = 0; q < kPairs; ++q) {
-    const int i = (2 * q) / kXB, j0 = (2 * q) % kXB;
-    const int need[3] = {4 + j0, 4 + j0 + 1, i};
-    for (int u = 0; u < 3; ++u)
-      if (!seen[need[u]]) { seen[need[u]] = true; f.order[n++] = need[u]; }
-  }
-  for (int r = 0; r < kFrags; ++r) f.group[r] = (r * kPairs) / kFrags;
-  return f;
+#ifndef MOE_GEMM_WAVES0
+#define MOE_GEMM_WAVES0 8
+#endif
+#ifndef MOE_GEMM_WAVES1
+#define MOE_GEMM_WAVES1 8
+#endif
+#ifndef MOE_GEMM_WAVES2
+#define MOE_GEMM_WAVES2 8
+#endif
+#ifndef MOE_GEMM_WAVES3
+#define MOE_GEMM_WAVES3 8
+#endif
+// wavefronts per workgroup of each bf16 kernel (by ACT)
+constexpr int waves_of(int act) {
+  return act == 0 ? MOE_GEMM_WAVES0 : act == 1 ? MOE_GEMM_WAVES1 : act == 2 ? MOE_GEMM_WAVES2 : MOE_GEMM_WAVES3;
 }
-constexpr FragPlan kPlan = make_frag_plan();
 
-template <int ACT>
-__global__ __launch_bounds__(kThreadsB, 1) void gemm_bf16_kernel(GemmArgs a) {
+template <int ACT, int W>
+__device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
+  using G = Geo<W>;
+  constexpr int kWaves = G::kWaves, kHalf = G::kHalf, kSRows = G::kSRows, kLoadsPerWave = G::kLoadsPerWave;
+  constexpr int kXR = G::kXR, kXB = G::kXB, kPairs = G::kPairs, kFrags = G::kFrags;
   constexpr bool kGlu = ACT == 2;
   constexpr int kNOut = kGlu ? kBW / 2 : kBW;   // output columns per tile
   __shared__ __align__(1024) uint8_t lds[kLdsBytes];
@@ -481,7 +509,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void gemm_bf16_kernel(GemmArgs a) {
             acc[i][jb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb + 1], acc[i][jb + 1], 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < kFrags; ++r)
-            if (kPlan.group[r] == q) read_frag(rx, rw, rc, cur ^ 1, kPlan.order[r]);
+            if (kPlanOf<W>.group[r] == q) read_frag(rx, rw, rc, cur ^ 1, kPlanOf<W>.order[r]);
           // this step's loads, spread over the groups
 #pragma unroll
           for (int u = 0; u < kLoadsPerWave; ++u) {
@@ -500,6 +528,17 @@ __global__ __launch_bounds__(kThreadsB, 1) void gemm_bf16_kernel(GemmArgs a) {
   };
   if (!partial) run(std::false_type{});
   else run(std::true_type{});
+}
+
+// The bf16 kernels, one per workgroup size (the body is a device function
+// so that the wave count is a literal in each kernel).
+template <int ACT>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_w8(GemmArgs a) {
+  gemm_bf16_body<ACT, 8>(a);
+}
+template <int ACT>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmArgs a) {
+  gemm_bf16_body<ACT, 4>(a);
 }
 
 // ------------------------------------------------------------------ float32
@@ -573,6 +612,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
 
 }  // namespace
 
+template <int ACT>
+void launch_bf16(const GemmArgs& a, unsigned grid, hipStream_t s) {
+  if constexpr (waves_of(ACT) == 8) gemm_bf16_w8<ACT><<<grid, 512, 0, s>>>(a);
+  else gemm_bf16_w4<ACT><<<grid, 256, 0, s>>>(a);
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
@@ -581,10 +626,10 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
                           ((a.N + nout - 1) / nout);
     const unsigned grid = static_cast<unsigned>((tiles + 255) / 256 * 256);
     switch (a.act) {
-      case 0: gemm_bf16_kernel<0><<<grid, kThreadsB, 0, s>>>(a); break;
-      case 1: gemm_bf16_kernel<1><<<grid, kThreadsB, 0, s>>>(a); break;
-      case 2: gemm_bf16_kernel<2><<<grid, kThreadsB, 0, s>>>(a); break;
-      default: gemm_bf16_kernel<3><<<grid, kThreadsB, 0, s>>>(a); break;
+      case 0: launch_bf16<0>(a, grid, s); break;
+      case 1: launch_bf16<1>(a, grid, s); break;
+      case 2: launch_bf16<2>(a, grid, s); break;
+      default: launch_bf16<3>(a, grid, s); break;
     }
   } else {
     const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kFT - 1) / kFT) *

@@ -12,23 +12,33 @@ of ``bench.py --copy-calibration`` and prints, per kernel, the average counter
 value per dispatch (KiB), the calibration factor that the plain copy kernel of
 known size gives (its algorithmic bytes / its counter bytes), and a JSON line
 with the expert GEMM's calibrated HBM bytes per launch pair, tagged with the
-SHA-256 of the GEMM source it was measured on.
+SHA-256 of the GEMM code (comments and whitespace removed) it was measured on.
 """
 import argparse
 import glob
 import hashlib
 import json
 import os
+import re
 import sqlite3
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCE = os.path.join(HERE, 'csrc', 'gemm.hip')
 COPY_KERNEL_TAG = 'neg_kernel'      # torch's elementwise negation, used as the plain copy
+GEMM_UP = r'gemm_bf16_w\d<2>'       # kernel-name patterns of the two expert GEMMs
+GEMM_DOWN = r'gemm_bf16_w\d<0>'
 
 
-def gemm_source_sha256():
-    with open(GEMM_SOURCE, 'rb') as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def gemm_code_sha256(path=GEMM_SOURCE):
+    """SHA-256 of the GEMM source with comments and whitespace removed, so
+    that a record stays valid across comment edits but not code edits (the
+    source has no string literal holding a comment marker)."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r'/\*.*?\*/', ' ', text, flags=re.S)
+    text = re.sub(r'//[^\n]*', ' ', text)
+    text = ' '.join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def find_db(d):
@@ -78,8 +88,8 @@ def cmd_traffic(a):
     fetch = pmc_per_kernel(a.fetch_dir, 'FETCH_SIZE')
     write = pmc_per_kernel(a.write_dir, 'WRITE_SIZE')
 
-    def pick(tab, tag):
-        hits = [(kn, v) for kn, v in tab.items() if tag in kn]
+    def pick(tab, pattern):
+        hits = [(kn, v) for kn, v in tab.items() if re.search(pattern, kn)]
         if len(hits) != 1:
             raise SystemExit(f'expected one kernel matching {tag!r}, found {[h[0] for h in hits]}')
         return hits[0][1]
@@ -87,8 +97,9 @@ def cmd_traffic(a):
     copy_f, copy_w = pick(fetch, COPY_KERNEL_TAG)[1], pick(write, COPY_KERNEL_TAG)[1]
     kib = a.copy_bytes / 1024.0
     f_fetch, f_write = kib / copy_f, kib / copy_w
-    g2f, g2w = pick(fetch, 'gemm_bf16_kernel<2>')[1], pick(write, 'gemm_bf16_kernel<2>')[1]
-    g0f, g0w = pick(fetch, 'gemm_bf16_kernel<0>')[1], pick(write, 'gemm_bf16_kernel<0>')[1]
+    # the expert GEMM kernels (either workgroup size): SwiGLU up/gate, then down
+    g2f, g2w = pick(fetch, GEMM_UP)[1], pick(write, GEMM_UP)[1]
+    g0f, g0w = pick(fetch, GEMM_DOWN)[1], pick(write, GEMM_DOWN)[1]
     print(f'HBM traffic of the expert grouped GEMM, {a.workload} workload (rocprofv3 --pmc)')
     if a.command_fetch:
         print('command (FETCH_SIZE):', a.command_fetch)
@@ -104,7 +115,7 @@ def cmd_traffic(a):
     print(f'calibration: the copy kernel moves {kib:.0f} KiB each way; counters read '
           f'FETCH {copy_f:.1f} KiB, WRITE {copy_w:.1f} KiB -> factors {f_fetch:.4f} (fetch), '
           f'{f_write:.4f} (write)')
-    rec = {'workload': a.workload, 'gemm_source_sha256': gemm_source_sha256(),
+    rec = {'workload': a.workload, 'gemm_code_sha256': gemm_code_sha256(),
            'fetch_bytes_per_pair': (g2f + g0f) * f_fetch * 1024, 'write_bytes_per_pair': (g2w + g0w) * f_write * 1024,
            'fetch_factor': f_fetch, 'write_factor': f_write}
     rec['traffic_bytes_per_pair'] = rec['fetch_bytes_per_pair'] + rec['write_bytes_per_pair']
@@ -120,7 +131,7 @@ def read_traffic(path, workload):
     for line in open(path):
         if line.startswith('json: '):
             rec = json.loads(line[6:])
-            if rec.get('workload') == workload and rec.get('gemm_source_sha256') == gemm_source_sha256():
+            if rec.get('workload') == workload and rec.get('gemm_code_sha256') == gemm_code_sha256():
                 return rec
     return None
 

@@ -14,8 +14,8 @@ sys.path.insert(0, ROOT)
 
 from mixture_experts_layer_20_amd import rocprof_summary as R  # noqa: E402
 
-G2 = 'void moe::(anonymous namespace)::gemm_bf16_kernel<2>(moe::GemmArgs)'
-G0 = 'void moe::(anonymous namespace)::gemm_bf16_kernel<0>(moe::GemmArgs)'
+G2 = 'void moe::(anonymous namespace)::gemm_bf16_w8<2>(moe::GemmArgs)'
+G0 = 'void moe::(anonymous namespace)::gemm_bf16_w4<0>(moe::GemmArgs)'
 COPY = 'void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>'
 
 
@@ -55,13 +55,24 @@ def test_traffic_calibration_and_hash_gate(tmp_path):
     assert rec['fetch_factor'] == pytest.approx(2.0) and rec['write_factor'] == pytest.approx(1.0)
     assert rec['fetch_bytes_per_pair'] == pytest.approx(1500.0 * 2.0 * 1024)
     assert rec['write_bytes_per_pair'] == pytest.approx(50.0 * 1024)
-    assert rec['gemm_source_sha256'] == R.gemm_source_sha256()
+    assert rec['gemm_code_sha256'] == R.gemm_code_sha256()
     path = tmp_path / 'summary.txt'
     path.write_text(out.stdout)
     assert R.read_traffic(str(path), 'wl')['traffic_bytes_per_pair'] == pytest.approx((3000.0 + 50.0) * 1024)
     assert R.read_traffic(str(path), 'other') is None
     # a summary taken on another version of the GEMM source is not used
-    stale = dict(rec, gemm_source_sha256='0' * 64)
+    stale = dict(rec, gemm_code_sha256='0' * 64)
     path.write_text('json: ' + json.dumps(stale) + '\n')
     assert R.read_traffic(str(path), 'wl') is None
     assert R.read_traffic(str(tmp_path / 'missing.txt'), 'wl') is None
+
+
+def test_code_hash_ignores_comments_not_code(tmp_path):
+    a = tmp_path / 'a.hip'
+    a.write_text('// header\nint f(int x) {  /* note */ return x + 1; }  // tail\n')
+    b = tmp_path / 'b.hip'
+    b.write_text('// another header\n\nint f(int x) { return x + 1; }\n')
+    c = tmp_path / 'c.hip'
+    c.write_text('int f(int x) { return x + 2; }\n')
+    assert R.gemm_code_sha256(str(a)) == R.gemm_code_sha256(str(b))
+    assert R.gemm_code_sha256(str(a)) != R.gemm_code_sha256(str(c))
