@@ -30,8 +30,9 @@
 //     reach XCDs round-robin), so the ~32 tiles an XCD runs at once share 4
 //     token panels and 8 weight panels in its L2 while every XCD gets an even
 //     share of every expert.
-//   * A partial tile (an expert's last, fewer than 256 valid token rows)
-//     skips the MFMAs of 32-row token blocks without valid rows.
+//   * A partial tile (an expert's last, fewer than 256 valid token rows, or
+//     one reaching past N) skips the MFMAs of 32-row token blocks without
+//     valid rows and of 32-row weight blocks past N.
 //   * Rows at or past rows[g] and columns past N read as zero through the
 //     buffer bounds and are never stored; k past K reads 0.
 // Router mode (ACT 3): C is float32 [rows, N/4], the sum of each group of four
@@ -318,11 +319,16 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // x kXR token rows (kXB blocks of 32).  Block i: weight rows wrow[i] (+
   // lane%32), output columns ncol[i]; for SwiGLU blocks 0-1 are gate rows,
   // 2-3 the matching up rows.  In a partial tile (fewer than 256 valid token
-  // rows) a wave multiplies only its token blocks that hold valid rows.
+  // rows, or columns past N) a wave multiplies only its blocks that hold
+  // valid token rows and weight rows below N (router logits use 4E of the
+  // 256 weight rows).
   const int wn = wave & 1, wm = wave >> 1;
   const int valid_rows = static_cast<int>(min<int64_t>(rows_g - m0, kBM));
-  const bool partial = valid_rows < kBM;
-  const int xbv = max(0, min(kXB, (valid_rows - wm * kXR + 31) / 32));   // valid blocks of this wave
+  const int xbv = max(0, min(kXB, (valid_rows - wm * kXR + 31) / 32));   // valid token blocks of this wave
+  // weight blocks of this wave with a column below N (for SwiGLU a gate
+  // block and its up block share their columns)
+  const int wbv = kGlu ? max(0, min(2, (N - n0 - wn * 64 + 31) / 32)) : max(0, min(4, (N - n0 - wn * 128 + 31) / 32));
+  const bool partial = valid_rows < kBM || n0 + kNOut > N;
   int wrow[4], ncol[4], xrow[kXB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -471,7 +477,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // Each 16-k step runs as kPairs fenced groups of two MFMAs, the step's
   // share of the next step's fragment reads and of the loads, so that no
   // burst of loads or reads holds up the MFMAs.  A partial tile skips the
-  // MFMAs of token blocks without valid rows.
+  // MFMAs of blocks without valid token rows or weight rows.
   auto run = [&](auto partial_c) __attribute__((always_inline)) {
     constexpr bool kPartial = decltype(partial_c)::value;
     int rk = 0;                                       // kt % nring
@@ -503,9 +509,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
 #pragma unroll
         for (int q = 0; q < kPairs; ++q) {
           const int i = (2 * q) / kXB, jb = (2 * q) % kXB;
-          if (!kPartial || jb < xbv)
+          const bool wvalid = (kGlu ? (i & 1) : i) < wbv;
+          if (!kPartial || (jb < xbv && wvalid))
             acc[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb], acc[i][jb], 0, 0, 0);
-          if (!kPartial || jb + 1 < xbv)
+          if (!kPartial || (jb + 1 < xbv && wvalid))
             acc[i][jb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb + 1], acc[i][jb + 1], 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < kFrags; ++r)

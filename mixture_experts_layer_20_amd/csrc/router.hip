@@ -1,7 +1,8 @@
 // Float32 router for gfx950: logits, softmax statistics, top-k and gates,
 // plus per-workgroup partial sums for the losses.  bf16 x: the logits come
-// from the grouped GEMM on an exact bf16 split of the weight, then the
-// per-token epilogue runs over them; float32 x: one fused pass.
+// from MFMAs on an exact bf16 split of the weight (a streaming kernel for at
+// most 16 experts, the grouped GEMM beyond), then the per-token epilogue
+// runs over them; float32 x: one fused pass.
 //
 // Sources: "Lab 18 -- Mixture of experts" s.1 (z = x W_r, p = softmax(z),
 // renormalised vs raw gates) and s.2 (P_i, router z-loss); "Lab 01" "Where to
@@ -369,11 +370,17 @@ __global__ __launch_bounds__(kThreads) void route_from_logits_kernel(RouteArgs a
   __shared__ double red[5 * 256];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBT;
   const int nt = static_cast<int>(min<int64_t>(kBT, a.T - t0));
-  // the slabs summed in order, then the logit bias
+  // the slabs (at most 8) summed in order, then the logit bias; all of a
+  // value's slab loads are issued before the first add
   const int64_t slab = a.T * a.E;
   for (int i = threadIdx.x; i < nt * a.E; i += kThreads) {
-    float v = a.logits[t0 * a.E + i];
-    for (int sp = 1; sp < a.zsplits; ++sp) v += a.logits[sp * slab + t0 * a.E + i];
+    float vs[8];
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp) vs[sp] = sp < a.zsplits ? a.logits[sp * slab + t0 * a.E + i] : 0.0f;
+    float v = vs[0];
+#pragma unroll
+    for (int sp = 1; sp < 8; ++sp)
+      if (sp < a.zsplits) v += vs[sp];
     if (a.logit_bias) v += a.logit_bias[i % a.E];
     zbuf[i] = v;
   }
@@ -391,21 +398,175 @@ __global__ __launch_bounds__(kThreads) void route_from_logits_kernel(RouteArgs a
 // transpose with float32 accumulation; its router epilogue adds each group
 // of four columns (p = 0, 1, 2, 3 in that order) into logit e.  The
 // per-token epilogue then runs on those logits as for routing from logits.
+// The exact three-way bf16 split of a float32 weight: hi + mid + lo == v
+// (8 + 8 + 8 significant bits cover float32's 24).
+__device__ __forceinline__ void split3(float v, bf16_t& hi, bf16_t& mid, bf16_t& lo) {
+#pragma clang fp contract(off)
+  hi = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+}
+
 __global__ __launch_bounds__(kThreads) void split_router_kernel(const float* w, bf16_t* wp, int d, int E) {
   const int64_t n = static_cast<int64_t>(E) * d;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kThreads) {
     const int e = static_cast<int>(i / d), k = static_cast<int>(i % d);
     const float v = w[static_cast<int64_t>(k) * E + e];
-    const bf16_t hi = f32_to_bf16(v);
-    const float r1 = v - bf16_to_f32(hi);
-    const bf16_t mid = f32_to_bf16(r1);
-    const bf16_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+    bf16_t hi, mid, lo;
+    split3(v, hi, mid, lo);
     bf16_t* row = wp + static_cast<int64_t>(4 * e) * d + k;
     row[0] = hi;
     row[d] = mid;
     row[2 * static_cast<int64_t>(d)] = lo;
     row[3 * static_cast<int64_t>(d)] = 0;
+  }
+}
+
+
+// ---------------------------------------------------------------- bf16 x, E <= 16
+// Router logits streamed from bf16 tokens for few experts.  The grouped
+// GEMM would spend a 256-row weight tile on 4E rows and wait out a load
+// latency per k stage; here the token rows are the streamed operand and the
+// weight planes sit in LDS.
+//
+// Workgroup: 16 wavefronts x 16 tokens = 256 tokens, one slice of the model
+// dimension (the slices' partial logits go to separate slabs, summed in a
+// fixed order by the epilogue).  The float32 weight slice is split into its
+// three exact bf16 planes in LDS, 256 k at a time (rows 4e + p; p = 3 and
+// rows past 4E are zero), double-buffered.  Each wave loads its tokens' x
+// straight into registers in the operand layout of v_mfma_f32_16x16x32_bf16
+// (lane l: token l%16, 8 consecutive k at 8*(l/16) of each 32-k step; rows
+// past T and k past the slice read zero through the buffer bounds), one
+// 256-k chunk ahead of the one it multiplies.  With the planes as the first
+// operand, lane l ends with plane rows 4*(l/16) + {0,1,2,3} of token l%16:
+// the hi, mid, lo (and zero) products of one expert, summed into its logit in
+// the same order as the grouped GEMM's router epilogue.
+constexpr int kLgWaves = 16;
+constexpr int kLgThreads = kLgWaves * 64;
+constexpr int kLgTokens = kLgWaves * 16;
+constexpr int kLgSub = 256;                  // k per LDS chunk
+constexpr int kLgSteps = kLgSub / 32;        // MFMA k-steps per chunk
+constexpr int kLgPitch = kLgSub + 8;         // plane row pitch (bf16): rows 16 B apart in the banks
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int EB>
+__global__ __launch_bounds__(kLgThreads) void router_logits_kernel(RouteArgs a, int S) {
+  constexpr int kRows = 16 * EB;             // plane rows 4e + p for e < 4*EB
+  constexpr int kWPer = kLgSub * 4 * EB / kLgThreads;   // weights each thread splits per chunk
+  static_assert(kWPer >= 1, "one weight per thread at least");
+  __shared__ __align__(16) bf16_t planes[2][kRows * kLgPitch];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = a.E, d = a.d;
+  const int64_t T = a.T;
+  const int dc = d / S;                      // the slice (a multiple of 8)
+  const int kbeg = blockIdx.y * dc, kend = kbeg + dc;
+  const int nsub = (dc + kLgSub - 1) / kLgSub;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kLgTokens + wave * 16;
+
+  // the float32 weights of chunk c: thread tid takes entries tid + j*threads
+  // of the chunk's [256 k, E] block (contiguous in w's [d, E] layout)
+  auto fetch_w = [&](float (&wv)[kWPer], int c) {
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      const int i = tid + j * kLgThreads;
+      const int kk = i / E, e = i % E;
+      const int k = kbeg + c * kLgSub + kk;
+      wv[j] = (kk < kLgSub && k < kend) ? a.w_router[static_cast<int64_t>(k) * E + e] : 0.0f;
+    }
+  };
+  auto store_w = [&](const float (&wv)[kWPer], int c) {
+    bf16_t* pl = planes[c & 1];
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      const int i = tid + j * kLgThreads;
+      const int kk = i / E, e = i % E;
+      if (kk < kLgSub) {
+        bf16_t hi, mid, lo;
+        split3(wv[j], hi, mid, lo);
+        pl[(4 * e) * kLgPitch + kk] = hi;
+        pl[(4 * e + 1) * kLgPitch + kk] = mid;
+        pl[(4 * e + 2) * kLgPitch + kk] = lo;
+      }
+    }
+  };
+  // this wave's 16 token rows through one descriptor (rows past T read zero)
+  const int64_t nrows = max<int64_t>(0, min<int64_t>(16, T - t0));
+  const uint64_t bu = reinterpret_cast<uint64_t>(static_cast<const bf16_t*>(a.x) + max<int64_t>(0, min(t0, T)) * d);
+  const uint32_t blo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu));
+  const uint32_t bhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu >> 32));
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>((static_cast<uint64_t>(bhi) << 32) | blo), (short)0,
+      __builtin_amdgcn_readfirstlane(static_cast<int>(nrows * d * 2)), 0x00020000);
+  const int row = lane & 15, q = lane >> 4;
+  auto fetch_x = [&](u32x4_t (&xv)[kLgSteps], int c) {
+#pragma unroll
+    for (int j = 0; j < kLgSteps; ++j) {
+      const int k = kbeg + c * kLgSub + 32 * j + 8 * q;
+      const uint32_t off = k < kend ? static_cast<uint32_t>((row * d + k) * 2) : 0x80000000u;
+      xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, static_cast<int>(off), 0, 0);
+    }
+  };
+  f32x4_t acc[EB];
+#pragma unroll
+  for (int b = 0; b < EB; ++b) acc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto multiply = [&](const u32x4_t (&xv)[kLgSteps], int c) {
+    const bf16_t* pl = planes[c & 1];
+#pragma unroll
+    for (int j = 0; j < kLgSteps; ++j) {
+      const bf16x8_t bx = __builtin_bit_cast(bf16x8_t, xv[j]);
+#pragma unroll
+      for (int b = 0; b < EB; ++b) {
+        const bf16x8_t aw = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(pl + (16 * b + row) * kLgPitch + 32 * j + 8 * q));
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bx, acc[b], 0, 0, 0);
+      }
+    }
+  };
+  // Two chunks in flight at all times.  Loads complete in order, so each
+  // chunk's weights are requested before its x, and a chunk's weights are
+  // split into LDS only after the previous chunk's MFMAs (the x that wait
+  // needs is the x the next MFMAs need anyway).  Plane buffer c%2 is free
+  // once every wave has passed the barrier after chunk c-1's MFMAs.
+  u32x4_t x0[kLgSteps], x1[kLgSteps];
+  float w0[kWPer], w1[kWPer];
+  fetch_w(w0, 0);
+  if (nsub > 1) fetch_w(w1, 1);
+  fetch_x(x0, 0);
+  if (nsub > 1) fetch_x(x1, 1);
+  // zero rows of both buffers (never rewritten)
+  for (int i = tid; i < 2 * kRows * kLgPitch; i += kLgThreads) {
+    const int r = (i / kLgPitch) % kRows;
+    if ((r & 3) == 3 || (r >> 2) >= E) (&planes[0][0])[i] = 0;
+  }
+  store_w(w0, 0);
+  if (nsub > 1) store_w(w1, 1);
+  __syncthreads();
+  auto step = [&](u32x4_t (&xc)[kLgSteps], float (&wc)[kWPer], const float (&wn)[kWPer], int c) {
+    multiply(xc, c);
+    if (c >= 1 && c + 1 < nsub) store_w(wn, c + 1);
+    if (c + 2 < nsub) {
+      fetch_w(wc, c + 2);
+      fetch_x(xc, c + 2);
+    }
+    __syncthreads();
+  };
+  for (int c = 0; c < nsub; c += 2) {
+    step(x0, w0, w1, c);
+    if (c + 1 < nsub) step(x1, w1, w0, c + 1);
+  }
+  // lane: token t0 + row, expert 4b + q
+  if (t0 + row < T) {
+    float* zs = a.zraw + (static_cast<int64_t>(blockIdx.y) * T + t0 + row) * E;
+#pragma unroll
+    for (int b = 0; b < EB; ++b) {
+      const int e = 4 * b + q;
+      if (e < E) zs[e] = ((acc[b][0] + acc[b][1]) + acc[b][2]) + acc[b][3];
+    }
   }
 }
 
@@ -435,7 +596,18 @@ template <typename XT>
 hipError_t dispatch_route(const RouteArgs& a, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((a.T + kBT - 1) / kBT);
   RouteArgs r = a;
-  if (a.x != nullptr && sizeof(XT) == 2) {
+  if (a.x != nullptr && sizeof(XT) == 2 && a.E <= 16) {
+    // few experts: the streamed router-logits kernel
+    const int S = router_splits(a.T, a.E, a.d);
+    const dim3 lg_grid(static_cast<unsigned>((a.T + kLgTokens - 1) / kLgTokens), static_cast<unsigned>(S));
+    const int eb = (a.E + 3) / 4;
+    if (eb == 1) router_logits_kernel<1><<<lg_grid, kLgThreads, 0, s>>>(a, S);
+    else if (eb == 2) router_logits_kernel<2><<<lg_grid, kLgThreads, 0, s>>>(a, S);
+    else if (eb == 3) router_logits_kernel<3><<<lg_grid, kLgThreads, 0, s>>>(a, S);
+    else router_logits_kernel<4><<<lg_grid, kLgThreads, 0, s>>>(a, S);
+    r.logits = a.zraw;
+    r.zsplits = S;
+  } else if (a.x != nullptr && sizeof(XT) == 2) {
     const int64_t n = static_cast<int64_t>(a.E) * a.d;
     split_router_kernel<<<static_cast<unsigned>(std::min<int64_t>(1024, (n + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
         a.w_router, a.wplanes, a.d, a.E);

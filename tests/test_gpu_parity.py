@@ -107,7 +107,7 @@ def test_sigmoid_key_matches_the_spec_bit_for_bit(moe):
 
 
 def test_router_logits_within_float32_dot_bound(moe):
-    for name in ('tiny_f32', 'switch_top1_skewed', 'deepseekmoe_fine'):
+    for name in ('tiny_f32', 'switch_top1_skewed', 'mixtral_8x_top2', 'deepseekmoe_fine'):
         w = synth.WORKLOADS[name]
         inp, ex, sh, dev = device_layer(w, moe)
         say('logits', name)
@@ -125,6 +125,42 @@ def test_router_logits_within_float32_dot_bound(moe):
             2.0 ** -24 * np.abs(zr.astype(np.float64))
         err = np.abs(np_of(logits).astype(np.float64) - zr.astype(np.float64))
         assert (err <= bound).all(), (err / bound).max()
+
+
+# bf16 tokens with at most 16 experts take the streamed logits kernel: E not
+# a multiple of 4, T not a multiple of 16 or 256, d slices that end inside a
+# 32-wide k step or a 256-wide chunk, one slice of several chunks (T large
+# enough for a single split), and a logit bias
+LOGIT_CASES = [
+    # (T, d, E, logit_bias)
+    (4097, 48, 5, ''),
+    (300, 1024, 3, 'first_two_plus2'),
+    (1000, 264, 16, ''),
+    (70001, 1032, 6, 'log_rank'),
+    (17, 8, 1, ''),
+]
+
+
+@pytest.mark.parametrize('case', LOGIT_CASES, ids=[f'T{c[0]}d{c[1]}E{c[2]}{c[3]}' for c in LOGIT_CASES])
+def test_streamed_router_logits_within_float32_dot_bound(moe, case):
+    T, d, E, lb = case
+    say('streamed logits', case)
+    w = synth.Workload('lg', T=T, d=d, E=E, k=1, d_ff=8, act='gelu', score='softmax', renormalize=-1,
+                       cf=1.0, dtype='bf16', seed=T + d + E, logit_bias=lb)
+    inp = synth.router_inputs(w)
+    cfg = moe.config_from_workload(w)
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, 1, dtype=torch.int32, device=DEV)
+    gates = torch.empty(T, 1, dtype=torch.float32, device=DEV)
+    moe.moe_route(cfg, synth.to_torch(inp['x'], DEV), synth.to_torch(inp['w_router'], DEV),
+                  synth.to_torch(inp['logit_bias'], DEV), None, logits, None, idx, gates, None,
+                  moe.workspace(cfg, DEV))
+    torch.cuda.synchronize()
+    x = synth.as_f32(inp['x'])
+    zr = O.router_logits(x, inp['w_router'], inp['logit_bias'])
+    bound = logit_error_bound(x, inp['w_router'], inp['logit_bias']) + 2.0 ** -24 * np.abs(zr.astype(np.float64))
+    err = np.abs(np_of(logits).astype(np.float64) - zr.astype(np.float64))
+    assert (err <= bound).all(), (err / bound).max()
 
 
 # ----------------------------------------------------------------------------- capacity / dispatch
