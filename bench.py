@@ -45,6 +45,8 @@ def parse():
     p.add_argument('--no-cpu-baseline', action='store_true')
     p.add_argument('--cpu-sample-tokens', type=int, default=0)
     p.add_argument('--phase-reps', type=int, default=10)
+    p.add_argument('--dropless', action='store_true',
+                   help='dropless mode: no capacity limit, expert rows packed without padding')
     p.add_argument('--copy-calibration', action='store_true',
                    help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
     return p.parse_args()
@@ -72,7 +74,7 @@ def main():
     dev = 'cuda'
     t0 = time.time()
     inp = synth.router_inputs(w)
-    cfg = moe.config_from_workload(w)
+    cfg = moe.config_from_workload(w, dropless=args.dropless)
     C = moe.moe_validate(cfg)
     x = synth.to_torch(inp['x'], dev)
     weights = dict(w_router=synth.to_torch(inp['w_router'], dev),
@@ -133,9 +135,11 @@ def main():
     slot = torch.empty_like(out['slot'])
     dropped = torch.empty_like(out['dropped'])
     counts = torch.empty_like(out['counts'])
-    row_token = torch.empty(E, C, dtype=torch.int32, device=dev)
-    h = torch.empty(E, C, F, dtype=dt, device=dev)
-    ye = torch.empty(E, C, d, dtype=dt, device=dev)
+    # expert rows: E x C (capacity), or T*k packed back to back (dropless)
+    xrows = T * k if args.dropless else E * C
+    row_token = torch.empty(xrows, dtype=torch.int32, device=dev)
+    h = torch.empty(xrows, F, dtype=dt, device=dev)
+    ye = torch.empty(xrows, d, dtype=dt, device=dev)
     y = torch.empty_like(out['y'])
     fs = w.n_shared * w.d_ff_shared
     hs = torch.empty(T, fs, dtype=dt, device=dev) if fs else None
@@ -164,7 +168,11 @@ def main():
         # token rows inside the expert GEMM, so nothing is copied here)
         timed('dispatch', lambda: moe.moe_dispatch(cfg, None, idx, slot, dropped, counts, row_token, None, ws))
         torch.clamp(counts, max=C, out=kept_rows)
-        if w.act == 'swiglu':
+        if args.dropless:
+            timed('expert_ffn', lambda: moe.moe_expert_ffn_packed(
+                cfg, w.act, E, counts, T * k, x, weights['w_in'], weights.get('w_gate'), weights.get('b_in'),
+                weights['w_out'], weights.get('b_out'), F, h, ye, gather=row_token))
+        elif w.act == 'swiglu':
             timed('expert_ffn', lambda: moe.moe_expert_ffn(cfg, 'swiglu', E, C, kept_rows, x, weights['w_in'],
                                                            weights['w_gate'], None, weights['w_out'], None,
                                                            F, h, ye, gather=row_token))
@@ -215,7 +223,8 @@ def main():
     # HBM bytes per launch pair from the committed FETCH_SIZE / WRITE_SIZE
     # counter runs, if they were taken on this version of the GEMM source
     from mixture_experts_layer_20_amd import rocprof_summary
-    rec = rocprof_summary.read_traffic(os.path.join(ROOT, 'profiles', f'gemm_traffic_{w.name}.txt'), w.name)
+    wl_key = w.name + ('_dropless' if args.dropless else '')
+    rec = rocprof_summary.read_traffic(os.path.join(ROOT, 'profiles', f'gemm_traffic_{wl_key}.txt'), wl_key)
     roofline = {'kernel': 'expert grouped GEMM (gate/up launch + down launch)',
                 'bound': 'mfma', 'achieved': round(ach, 2), 'peak': peak, 'unit': 'TFLOP/s',
                 'frac': round(ach / peak, 4),
@@ -238,7 +247,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample_tokens, log)
+        cpu = cpu_baseline(w, args.cpu_sample_tokens, log, dropless=args.dropless)
 
     line = {'metric': METRIC, 'value': round(tokens_per_s, 1), 'unit': 'tokens/s', 'n_gpus': 1,
             'steps': args.steps, 'warmup': args.warmup, 'ms_per_step': round(ms, 4),
@@ -246,7 +255,8 @@ def main():
             'data': 'synthetic (seeded; random-init weights of the named shape)',
             'config': {'workload': w.name, 'T': w.T, 'd': d, 'E': E, 'k': k, 'd_ff': F, 'act': w.act,
                        'score': w.score, 'capacity_factor': w.cf, 'capacity': C,
-                       'n_shared': w.n_shared, 'kept_assignments': kept, 'dropped_assignments': n_dropped},
+                       'n_shared': w.n_shared, 'kept_assignments': kept, 'dropped_assignments': n_dropped,
+                       'dropless': bool(args.dropless)},
             'roofline': roofline,
             'phases': {kk: {a: (round(bb, 5) if isinstance(bb, float) else bb) for a, bb in v.items()}
                        for kk, v in phases.items()},
@@ -254,7 +264,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, sample_tokens, log):
+def cpu_baseline(w, sample_tokens, log, dropless=False):
     """The oracle as it stands, on the first `sample_tokens` tokens of the same
     workload taken as a batch of their own (routing, capacity, every expert
     FFN and the combine, in float64 on the host cores)."""
@@ -273,7 +283,8 @@ def cpu_baseline(w, sample_tokens, log):
     experts = [synth.expert_weights(w, e) for e in range(w.E)]
     shared = [synth.expert_weights(w, s, shared=True) for s in range(w.n_shared)] or None
     t = time.perf_counter()
-    O.moe_forward(ws_, inp, lambda e: experts[e], (lambda s: shared[s]) if shared else None)
+    O.moe_forward(ws_, inp, lambda e: experts[e], (lambda s: shared[s]) if shared else None,
+                  dropless=dropless)
     el = time.perf_counter() - t
     log(f'cpu oracle: {n} tokens in {el:.1f}s on {threads} threads')
     return {'value': round(n / el, 2), 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',

@@ -92,7 +92,22 @@ typedef struct moe_config {
   int32_t dtype;              /* moe_dtype of x, expert weights/biases, y              */
   int32_t priority;           /* moe_priority of the capacity queue                    */
   int32_t dropped_output;     /* 0: fully dropped token -> y = x; 1: y = 0             */
+  int32_t dropless;           /* 0: capacity C as above; 1: dropless (see below)       */
 } moe_config;
+
+/* Dropless mode (dropless = 1) ["Lab 18" s.3, alternatives to dropping: a
+ * capacity high enough that nothing is dropped, or block-sparse kernels that
+ * remove the limit; "Mixture of experts" lecture, systems section: ragged
+ * per-expert matmuls without padding or dropping]:
+ *   - capacity_factor and capacity_override are ignored; moe_validate reports
+ *     C = T (no expert can receive more than T choices) and no choice is
+ *     dropped (dropped[] is all 0, the loss statistics count no drops);
+ *   - the choices of expert e occupy the rows [off_e, off_e + counts[e]) of
+ *     packed [T*k, ...] buffers, off_e = counts[0] + ... + counts[e-1], in the
+ *     same priority order as the capacity queue, with no padding;
+ *   - slot[t,j] is that packed ROW (not the position inside the expert);
+ *     row_token is [T*k], xe, h and ye are [T*k, ...];
+ *   - moe_combine reads ye[slot[t,j]]. */
 
 /* Check a configuration; on MOE_OK store the capacity C in *capacity [host]
  * (may be NULL). Runs on the host only. ["Lab 18" s.3; "Lab 01" traps] */
@@ -134,6 +149,8 @@ MOE_API moe_status moe_route(const moe_config* cfg, const void* x, const float* 
  *              expert e are left untouched), or NULL
  *   xe         [E,C,d] storage type: xe[e,slot] = x[t] for every kept choice
  *              (rows >= kept_e untouched), or NULL
+ *   (dropless mode: slot is the packed row, row_token [T*k], xe [T*k,d];
+ *   see moe_config)
  *   ws         workspace (required) */
 MOE_API moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx, int32_t* slot,
                         uint8_t* dropped, int32_t* counts, int32_t* row_token, void* xe,
@@ -172,12 +189,32 @@ MOE_API moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t gr
                                   const void* w_gate, const void* b_in, const void* w_out,
                                   const void* b_out, int32_t F, void* h, void* out, void* stream);
 
+/* The grouped expert FFN on packed rows (dropless mode): group g's rows are
+ * rows [off_g, off_g + rows[g]) of a (or of the gather list), h and out, with
+ * off_g = rows[0] + ... + rows[g-1] computed on the device (no padding)
+ * ["Mixture of experts" lecture, systems section: ragged per-expert matmuls].
+ *   rows        [groups] int32 (required), e.g. the counts of moe_dispatch
+ *   total_rows  [host] an upper bound of rows[0] + ... + rows[groups-1]
+ *               (sizes the launch; e.g. T*k), >= 0
+ *   a           [total rows, d], or with `gather` the [a_rows, d] token
+ *               matrix read through gather[off_g + m]
+ *   h, out      [total rows, F] and [total rows, d]
+ * Other arguments as for moe_expert_ffn; rows past the packed total are
+ * neither read nor written. */
+MOE_API moe_status moe_expert_ffn_packed(const moe_config* cfg, int32_t act, int32_t groups,
+                                         const int32_t* rows, int64_t total_rows, const void* a,
+                                         const int32_t* gather, int64_t a_rows, const void* w_in,
+                                         const void* w_gate, const void* b_in, const void* w_out,
+                                         const void* b_out, int32_t F, void* h, void* out,
+                                         void* stream);
+
 /* Gate-weighted combine with residual fallback ["Lab 18" s.1 layer equation
  * and s.3; "Lab 01" "Where to start" 5; "Phase 02" concept map].
  *   y_t = sum_{j not dropped} gates[t,j] * ye[idx[t,j], slot[t,j]] + shared_out[t]
  *   accumulated in float32 in j order, rounded once to the storage type.
  *   With shared_out NULL, a token with every choice dropped gets x_t (or 0).
- *   x [T,d]; ye [E,C,d]; shared_out [T,d] or NULL; y [T,d] (storage type). */
+ *   x [T,d]; ye [E,C,d] (dropless: [T*k,d], row slot[t,j]); shared_out [T,d]
+ *   or NULL; y [T,d] (storage type). */
 MOE_API moe_status moe_combine(const moe_config* cfg, const void* x, const void* ye,
                        const void* shared_out, const int32_t* idx, const float* gates,
                        const int32_t* slot, const uint8_t* dropped, void* y, void* stream);

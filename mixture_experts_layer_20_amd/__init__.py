@@ -37,7 +37,8 @@ class moe_config(ctypes.Structure):
                 ('d_ff_shared', ctypes.c_int32), ('capacity_factor', ctypes.c_double),
                 ('capacity_override', ctypes.c_int64), ('renormalize', ctypes.c_int32),
                 ('score', ctypes.c_int32), ('act', ctypes.c_int32), ('dtype', ctypes.c_int32),
-                ('priority', ctypes.c_int32), ('dropped_output', ctypes.c_int32)]
+                ('priority', ctypes.c_int32), ('dropped_output', ctypes.c_int32),
+                ('dropless', ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -66,6 +67,8 @@ def _load():
         'moe_dispatch': (st, [cfgp] + [_P] * 9),
         'moe_expert_ffn': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                 ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
+        'moe_expert_ffn_packed': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
+                                       ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
         'moe_combine': (st, [cfgp] + [_P] * 9),
         'moe_aux_losses': (st, [cfgp, _P, _P, _P, _P, _P]),
         'moe_forward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs),
@@ -96,12 +99,12 @@ def _enum(kind, v):
 
 def make_config(T, d, E, k, d_ff, *, n_shared=0, d_ff_shared=0, capacity_factor=1.25,
                 capacity_override=0, renormalize=-1, score='softmax', act='gelu', dtype='bf16',
-                priority='rank', dropped_output='residual') -> moe_config:
+                priority='rank', dropped_output='residual', dropless=False) -> moe_config:
     return moe_config(T=T, d=d, E=E, k=k, d_ff=d_ff, n_shared=n_shared, d_ff_shared=d_ff_shared,
                       capacity_factor=float(capacity_factor), capacity_override=capacity_override,
                       renormalize=renormalize, score=_enum('score', score), act=_enum('act', act),
                       dtype=_enum('dtype', dtype), priority=_enum('priority', priority),
-                      dropped_output=_enum('dropped_output', dropped_output))
+                      dropped_output=_enum('dropped_output', dropped_output), dropless=int(bool(dropless)))
 
 
 def config_from_workload(w, **over) -> moe_config:
@@ -204,6 +207,23 @@ def moe_expert_ffn(cfg, act, groups, rows_per_group, rows, a, w_in, w_gate, b_in
                                _ptr(b_in, 'b_in', dt), _ptr(w_out, 'w_out', dt),
                                _ptr(b_out, 'b_out', dt), F, _ptr(h, 'h', dt), _ptr(out, 'out', dt),
                                _stream(stream)))
+
+
+def moe_expert_ffn_packed(cfg, act, groups, rows, total_rows, a, w_in, w_gate, b_in, w_out, b_out, F,
+                          h, out, stream=None, gather=None):
+    """Packed rows (dropless mode): group g's rows start at rows[0] + ... +
+    rows[g-1]; ``total_rows`` bounds their sum.  ``gather`` (optional, int32):
+    row m of group g is a[gather[off_g + m]]; ``a`` is then the whole token
+    matrix."""
+    dt = torch_dtype(cfg)
+    a_rows = a.shape[0] if gather is not None else 0
+    _check(_lib.moe_expert_ffn_packed(ctypes.byref(cfg), _enum('act', act), groups,
+                                      _ptr(rows, 'rows', torch.int32), int(total_rows), _ptr(a, 'a', dt),
+                                      _ptr(gather, 'gather', torch.int32), a_rows,
+                                      _ptr(w_in, 'w_in', dt), _ptr(w_gate, 'w_gate', dt),
+                                      _ptr(b_in, 'b_in', dt), _ptr(w_out, 'w_out', dt),
+                                      _ptr(b_out, 'b_out', dt), F, _ptr(h, 'h', dt), _ptr(out, 'out', dt),
+                                      _stream(stream)))
 
 
 def moe_combine(cfg, x, ye, shared_out, idx, gates, slot, dropped, y, stream=None):

@@ -5,6 +5,7 @@
 // Sources: "Lab 18 -- Mixture of experts" s.3 (C = ceil(cf*T*k/E)) and "What
 // to implement" (route, load_balancing_loss, router_z_loss, capacity_mask,
 // MoE.forward); "Lab 01" "The traps" (capacity_factor < 1 must raise).
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -34,6 +35,9 @@ moe_status hip_status(hipError_t e, const char* where) {
 }
 
 int64_t capacity_of(const moe_config& c) {
+  // dropless: no expert receives more than T choices (a token picks an expert
+  // at most once), so C = T never binds
+  if (c.dropless) return c.T;
   if (c.capacity_override > 0) return c.capacity_override;
   // evaluated in IEEE double in this order, then rounded up
   return static_cast<int64_t>(ceil(c.capacity_factor * static_cast<double>(c.T) *
@@ -73,8 +77,9 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
     return fail(MOE_EINVAL, "d_ff_shared must be a positive multiple of 8 (got %d)", c.d_ff_shared);
   if (c.T * static_cast<int64_t>(c.k) >= (int64_t{1} << 31))
     return fail(MOE_EINVAL, "T*k must be < 2^31");
+  if (c.dropless != 0 && c.dropless != 1) return fail(MOE_EINVAL, "dropless must be 0 or 1");
   if (c.capacity_override < 0) return fail(MOE_EINVAL, "capacity_override must be >= 0");
-  if (c.capacity_override == 0 && !(c.capacity_factor >= 1.0))
+  if (!c.dropless && c.capacity_override == 0 && !(c.capacity_factor >= 1.0))
     return fail(MOE_EINVAL,
                 "capacity_factor must be >= 1.0 (got %g): below 1 it drops tokens even under "
                 "perfect balance",
@@ -87,7 +92,9 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
     return fail(MOE_EINVAL, "unknown priority %d", c.priority);
   if (c.dropped_output != 0 && c.dropped_output != 1) return fail(MOE_EINVAL, "dropped_output must be 0 or 1");
   const int64_t C = capacity_of(c);
-  if (C > (int64_t{1} << 31) / c.E) return fail(MOE_EINVAL, "capacity %lld too large", static_cast<long long>(C));
+  // capacity buffers hold E*C rows (dropless: T*k, bounded above)
+  if (!c.dropless && C > (int64_t{1} << 31) / c.E)
+    return fail(MOE_EINVAL, "capacity %lld too large", static_cast<long long>(C));
   if (cap) *cap = C;
   return MOE_OK;
 }
@@ -141,10 +148,12 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   w.zraw = static_cast<float*>(take(sizeof(float) * router_splits(c.T, c.E, c.d) * c.T * c.E));
   w.idx_tmp = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
   w.gates_tmp = static_cast<float*>(take(sizeof(float) * c.T * c.k));
-  w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * c.E * C));
+  // expert rows: E*C (capacity), or T*k packed (dropless)
+  const int64_t xrows = c.dropless ? c.T * c.k : c.E * C;
+  w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * xrows));
 
-  w.h = take(ds * c.E * C * c.d_ff);
-  w.ye = take(ds * c.E * C * c.d);
+  w.h = take(ds * xrows * c.d_ff);
+  w.ye = take(ds * xrows * c.d);
   w.hs = fs > 0 ? take(ds * c.T * fs) : nullptr;
   w.s = fs > 0 ? take(ds * c.T * c.d) : nullptr;
   w.bytes = off;
@@ -185,6 +194,7 @@ CapArgs cap_args(const moe_config& c, int64_t C, const Workspace& w) {
   a.n_tiles = static_cast<int>((c.T + kTileTokens - 1) / kTileTokens);
   a.n_rtiles = static_cast<int>((c.T + kRouteTokens - 1) / kRouteTokens);
   a.token_major = c.priority == MOE_TOKEN_MAJOR;
+  a.packed = c.dropless;
   return a;
 }
 
@@ -199,22 +209,27 @@ LossArgs loss_args(const moe_config& c, int64_t C, const Workspace& w, const int
   l.k = c.k;
   l.n_tiles = static_cast<int>((c.T + kTileTokens - 1) / kTileTokens);
   l.has_shared = c.n_shared > 0;
+  l.packed = c.dropless;
   return l;
 }
 
 // Expert FFN on `groups` groups of rows: h = act(a w_in^T (+ b_in)) (or the
 // SwiGLU pair), out = h w_out^T (+ b_out).  With `gather`, row m of group g
-// is row gather[g*rpg + m] of a ([a_rows, d]).
+// is row gather[base_g + m] of a ([a_rows, d]), base_g = g*rpg, or with
+// `packed` rows[0] + ... + rows[g-1] (then rpg is the bound on their sum).
 moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int32_t* rows, const void* a,
                const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate,
                const void* b_in, const void* w_out, const void* b_out, int F, void* h, void* out,
-               hipStream_t s) {
-  // each operand a GEMM launch addresses through one buffer descriptor stays
-  // below 2^30 elements (2^31 bytes)
+               hipStream_t s, bool packed = false, int64_t group_rows = 0) {
+  // each operand a GEMM launch addresses through one buffer descriptor (one
+  // group's rows) stays below 2^30 elements (2^31 bytes); packed groups hold
+  // at most group_rows rows
   const int64_t lim = int64_t{1} << 30;
-  if (rpg * c.d >= lim || rpg * F >= lim || static_cast<int64_t>(F) * c.d >= lim ||
+  const int64_t gr = packed && group_rows > 0 ? std::min(group_rows, rpg) : rpg;
+  if (gr * c.d >= lim || gr * F >= lim || static_cast<int64_t>(F) * c.d >= lim ||
       (gather && a_rows * c.d >= lim))
     return fail(MOE_EINVAL, "one expert's operands must hold < 2^30 elements");
+  if (packed && groups > 256) return fail(MOE_EINVAL, "packed rows take at most 256 groups");
   GemmArgs g1{};
   g1.A = a;
   g1.gather = gather;
@@ -225,6 +240,8 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   g1.C = h;
   g1.rows = rows;
   g1.rows_per_group = rpg;
+  g1.packed = packed;
+  g1.total_rows = packed ? rpg : 0;
   g1.groups = groups;
   g1.N = F;
   g1.K = c.d;
@@ -237,6 +254,8 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   g2.C = out;
   g2.rows = rows;
   g2.rows_per_group = rpg;
+  g2.packed = packed;
+  g2.total_rows = packed ? rpg : 0;
   g2.groups = groups;
   g2.N = c.d;
   g2.K = F;
@@ -357,6 +376,35 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups, in
              out, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_expert_ffn_packed(const moe_config* cfg, int32_t act, int32_t groups, const int32_t* rows,
+                                 int64_t total_rows, const void* a, const int32_t* gather, int64_t a_rows,
+                                 const void* w_in, const void* w_gate, const void* b_in, const void* w_out,
+                                 const void* b_out, int32_t F, void* h, void* out, void* stream) {
+  MOE_TRY(validate(cfg, nullptr));
+  const moe_config& c = *cfg;
+  if (act != MOE_GELU && act != MOE_SWIGLU) return fail(MOE_EINVAL, "unknown act %d", act);
+  if (groups < 0 || groups > 256) return fail(MOE_EINVAL, "groups must be in [0, 256] (got %d)", groups);
+  if (total_rows < 0 || total_rows >= (int64_t{1} << 31)) return fail(MOE_EINVAL, "total_rows must be in [0, 2^31)");
+  if (F < 8 || F % 8) return fail(MOE_EINVAL, "F must be a positive multiple of 8 (got %d)", F);
+  if (groups == 0 || total_rows == 0) return MOE_OK;
+  MOE_TRY(check_ptr(rows, "rows", 4));
+  MOE_TRY(check_ptr(a, "a", 16));
+  MOE_TRY(check_ptr(w_in, "w_in", 16));
+  MOE_TRY(check_ptr(w_out, "w_out", 16));
+  MOE_TRY(check_ptr(h, "h", 16));
+  MOE_TRY(check_ptr(out, "out", 16));
+  MOE_TRY(check_ptr(gather, "gather", 4, false));
+  if (gather && a_rows <= 0) return fail(MOE_EINVAL, "a_rows must be > 0 when gathering");
+  MOE_TRY(check_ptr(b_in, "b_in", dsize(c), false));
+  MOE_TRY(check_ptr(b_out, "b_out", dsize(c), false));
+  if (act == MOE_SWIGLU) {
+    MOE_TRY(check_ptr(w_gate, "w_gate", 16));
+    if (b_in) return fail(MOE_EUNSUPPORTED, "SwiGLU experts take no b_in");
+  }
+  return ffn(c, act, groups, total_rows, rows, a, gather, a_rows, w_in, w_gate, b_in, w_out, b_out, F, h, out,
+             static_cast<hipStream_t>(stream), true);
+}
+
 moe_status moe_combine(const moe_config* cfg, const void* x, const void* ye, const void* shared_out,
                        const int32_t* idx, const float* gates, const int32_t* slot, const uint8_t* dropped, void* y,
                        void* stream) {
@@ -387,6 +435,7 @@ moe_status moe_combine(const moe_config* cfg, const void* x, const void* ye, con
   a.k = c.k;
   a.E = c.E;
   a.zero_fallback = c.dropped_output;
+  a.packed = c.dropless;
   return hip_status(launch_combine(a, c.dtype, static_cast<hipStream_t>(stream)), "combine");
 }
 
@@ -494,9 +543,15 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   a.xe = nullptr;
   MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "capacity"));
 
-  if (C > 0)
+  if (c.dropless) {
+    // packed rows: expert e's rows start after the counts of the lower experts
+    if (c.T > 0)
+      MOE_TRY(ffn(c, c.act, c.E, c.T * c.k, out->counts, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in,
+                  wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T));
+  } else if (C > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, w.kept, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in, wt->w_out,
                 wt->b_out, c.d_ff, w.h, w.ye, s));
+  }
   if (c.n_shared > 0 && c.T > 0)
     MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt->ws_in, nullptr, wt->bs_in, wt->ws_out,
                 wt->bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s));
@@ -516,6 +571,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   cb.k = c.k;
   cb.E = c.E;
   cb.zero_fallback = c.dropped_output;
+  cb.packed = c.dropless;
   MOE_TRY(hip_status(launch_combine(cb, c.dtype, s), "combine"));
 
   LossArgs l = loss_args(c, C, w, out->counts);

@@ -18,6 +18,8 @@
 //   permute per tile: in-tile rank from the same ballots + the tile's offset
 //           = slot; writes slot/dropped/row_token and copies each token row
 //           once into every kept destination with 16-byte accesses.
+// Dropless mode (packed rows) keeps every choice and lays the experts' rows
+// back to back: row = (sum of the counts of lower experts) + queue position.
 #include "common.hpp"
 
 namespace moe {
@@ -137,12 +139,29 @@ template <typename XT>
 __global__ __launch_bounds__(kThreads) void permute_kernel(CapArgs a) {
   __shared__ int64_t dest[kTileTokens][32];   // row of xe per (token, choice), -1 dropped
   __shared__ int any_kept[kTileTokens];
+  __shared__ int off[kThreads];               // packed rows: first row of each expert
   const int tile = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int k = a.k;
   const int64_t t0 = static_cast<int64_t>(tile) * kTileTokens;
   const int nt = static_cast<int>(min<int64_t>(kTileTokens, a.T - t0));
+  if (a.packed) {
+    // exclusive prefix sum of the expert counts (E <= 256 = threads)
+    const int v = tid < a.E ? a.counts[tid] : 0;
+    off[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < kThreads; o <<= 1) {
+      const int u = tid >= o ? off[tid - o] : 0;
+      __syncthreads();
+      off[tid] += u;
+      __syncthreads();
+    }
+    const int incl = off[tid];
+    __syncthreads();
+    off[tid] = incl - v;
+    __syncthreads();
+  }
   if (tid < kWave) {
     const int64_t t = t0 + lane;
     const bool valid = lane < nt;
@@ -165,14 +184,16 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(CapArgs a) {
         dest[lane][j] = -1;
       } else if (valid) {
         const int64_t s = static_cast<int64_t>(a.hist[(static_cast<int64_t>(j) * a.n_tiles + tile) * a.E + code]) + rank;
-        const bool drop = s >= a.C;
-        a.slot[t * k + j] = static_cast<int32_t>(s);
+        // packed rows: nothing is dropped and the slot is the row itself
+        const bool drop = !a.packed && s >= a.C;
+        const int64_t row = a.packed ? off[code] + s : static_cast<int64_t>(code) * a.C + s;
+        a.slot[t * k + j] = static_cast<int32_t>(a.packed ? row : s);
         a.dropped[t * k + j] = drop ? 1 : 0;
         if (!drop) {
           kept_any = true;
-          if (a.row_token) a.row_token[code * a.C + s] = static_cast<int32_t>(t);
+          if (a.row_token) a.row_token[row] = static_cast<int32_t>(t);
         }
-        dest[lane][j] = drop ? -1 : static_cast<int64_t>(code) * a.C + s;
+        dest[lane][j] = drop ? -1 : row;
       }
     }
     const uint64_t fb = __ballot(valid && !kept_any);

@@ -71,7 +71,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const char* __restrict__ sh = static_cast<const char*>(a.shared_out);
   char* __restrict__ y = static_cast<char*>(a.y);
 
-  // choice j on lane j: kept only if not dropped and its (expert, slot) is in range
+  // choice j on lane j: kept only if not dropped and its (expert, slot) is in
+  // range; its row of ye is e*C + slot, or the slot itself for packed rows
   int64_t myrow = 0;
   float mygate = 0.0f;
   bool keep = false;
@@ -79,8 +80,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     const int64_t tk = t * a.k + lane;
     const int e = a.idx[tk];
     const int sl = a.slot[tk];
-    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < a.C;
-    myrow = static_cast<int64_t>(e) * a.C + sl;
+    const int64_t bound = a.packed ? a.T * a.k : a.C;
+    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < bound;
+    myrow = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
     mygate = a.gates[tk];
   }
   uint64_t kept = __ballot(keep);
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void losses_kernel(LossArgs a) {
       a.stats[0] = static_cast<int32_t>(n_kept);
       a.stats[1] = static_cast<int32_t>(total - n_kept);
       a.stats[2] = a.has_shared ? 0 : static_cast<int32_t>(fred[0]);
-      a.stats[3] = static_cast<int32_t>(static_cast<long long>(a.E) * a.C - n_kept);
+      a.stats[3] = a.packed ? 0 : static_cast<int32_t>(static_cast<long long>(a.E) * a.C - n_kept);
     }
   }
 }

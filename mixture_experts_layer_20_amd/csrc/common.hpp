@@ -119,6 +119,8 @@ struct CapArgs {
   int64_t T, C;
   int E, k, d, n_tiles, n_rtiles;
   int token_major;
+  int packed;                 // dropless: slot = packed row off_e + queue position,
+                              // row_token [T*k], xe [T*k, d]; nothing dropped
 };
 
 struct GemmArgs {
@@ -136,6 +138,10 @@ struct GemmArgs {
   // elements (0: rows of K elements, groups stacked contiguously)
   int64_t lda, ldb;
   int64_t a_gs, b_gs, c_gs;
+  int packed;                 // group g's rows start at rows[0] + ... + rows[g-1] of A
+                              // (or of gather) and C; rows required (bf16 path:
+                              // the launch covers total_rows)
+  int64_t total_rows;         // packed: upper bound of the sum of rows
   int act;                    // 0 none (bias only), 1 GELU, 2 SwiGLU (B1 = gate),
                               // 3 router planes: float32 C [rows, N/4], the sum of
                               // each group of 4 output columns
@@ -153,6 +159,7 @@ struct CombineArgs {
   int64_t T, C;
   int d, k, E;
   int zero_fallback;
+  int packed;                 // dropless: ye is [T*k, d] and slot the row
 };
 
 struct LossArgs {
@@ -164,6 +171,7 @@ struct LossArgs {
   int64_t T, C;
   int E, k, n_tiles;
   int has_shared;
+  int packed;                 // dropless: no padding in the statistics
 };
 
 // host-side launchers (defined in the kernel translation units)

@@ -168,6 +168,9 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntil
   return c;
 }
 
+// Groups of a packed-rows launch (the ABI's expert limit).
+constexpr int kMaxPackedGroups = 256;
+
 // Buffer resource word 3 for raw (unswizzled, untyped) buffers on gfx9.
 constexpr int kRsrcWord3 = 0x00020000;
 // An offset past every operand (operands are kept below 2^31 bytes), which
@@ -213,19 +216,89 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // of 256 blocks.
   const int64_t p = blockIdx.x / 8;
   const int64_t L = ((p / 32) * 8 + blockIdx.x % 8) * 32 + p % 32;
-  const TileCoord tc = decode_tile(L, mt_max, ntiles, a.groups);
-  if (!tc.valid) return;
-  const int64_t rows_g = a.rows ? min<int64_t>(a.rows[tc.g], a.rows_per_group) : a.rows_per_group;
+  TileCoord tc;
+  int64_t rows_g, row_base;   // valid rows of the tile's group, and its first row
+  if (a.packed) {
+    // Packed rows: group g's rows start at rows[0] + ... + rows[g-1] (capped
+    // so that no group reaches past total_rows).  Wave 0 lays out the
+    // groups' row starts, rows and dense tile ranges at the start of the
+    // stage buffers (a second LDS object would make the compiler order every
+    // direct-to-LDS load behind the ones before it); L numbers only the
+    // tiles that hold rows.
+    int* pk_start = reinterpret_cast<int*>(lds);
+    int* pk_rows = pk_start + kMaxPackedGroups;
+    int* pk_end = pk_rows + kMaxPackedGroups;
+    const int ln = threadIdx.x & 63;
+    if (threadIdx.x < kWave) {
+      int64_t carry_r = 0;
+      int carry_t = 0;
+      for (int c = 0; c < a.groups; c += kWave) {
+        const int g = c + ln;
+        const int64_t rg = g < a.groups ? max(a.rows[g], 0) : 0;
+        int64_t vr = rg;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int64_t u = __shfl_up(vr, o, kWave);
+          if (ln >= o) vr += u;
+        }
+        const int64_t start = min(carry_r + vr - rg, a.total_rows);
+        const int re = static_cast<int>(max<int64_t>(0, min<int64_t>(rg, a.total_rows - start)));
+        int vt = (re + kBM - 1) / kBM * ntiles;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int u = __shfl_up(vt, o, kWave);
+          if (ln >= o) vt += u;
+        }
+        if (g < a.groups) {
+          pk_start[g] = static_cast<int>(start);
+          pk_rows[g] = re;
+          pk_end[g] = carry_t + vt;
+        }
+        carry_r += __shfl(vr, kWave - 1, kWave);
+        carry_t += __shfl(vt, kWave - 1, kWave);
+      }
+    }
+    __syncthreads();
+    if (L >= pk_end[a.groups - 1]) return;
+    // the tile's group: the number of groups whose tiles end at or before L
+    int g = 0;
+    for (int c = 0; c < a.groups; c += kWave)
+      g += __popcll(__ballot(c + ln < a.groups && pk_end[c + ln] <= L));
+    const int first = g ? pk_end[g - 1] : 0;
+    const int mt_g = (pk_end[g] - first) / ntiles;
+    const int r = static_cast<int>(L) - first;
+    constexpr int kGM = 4;
+    const int band = r / (kGM * ntiles);
+    const int mt0 = band * kGM;
+    const int gm = min(kGM, mt_g - mt0);
+    const int within = r % (kGM * ntiles);
+    tc.g = g;
+    tc.mt = mt0 + within % gm;
+    tc.nt = within / gm;
+    tc.valid = true;
+    rows_g = pk_rows[g];
+    row_base = pk_start[g];
+    // every wave has read the table before the stage loads overwrite it
+    __syncthreads();
+  } else {
+    tc = decode_tile(L, mt_max, ntiles, a.groups);
+    if (!tc.valid) return;
+    rows_g = a.rows ? min<int64_t>(a.rows[tc.g], a.rows_per_group) : a.rows_per_group;
+    row_base = static_cast<int64_t>(tc.g) * a.rows_per_group;
+  }
   const int m0 = tc.mt * kBM;
   if (m0 >= rows_g) return;
   const int n0 = tc.nt * kNOut;
 
   // token rows: contiguous per group, or gathered through a.gather (then A
-  // is the whole [a_rows, K] input and row m of group g is A[gather[g*rpg+m]])
+  // is the whole [a_rows, K] input and row m of group g is A[gather[row_base
+  // + m]], row_base = g*rpg, or the packed start)
   const bool gathered = a.gather != nullptr;
   const int64_t lda = a.lda ? a.lda : K, ldb = a.ldb ? a.ldb : K;
   const bf16_t* A = static_cast<const bf16_t*>(a.A) +
-                    (gathered ? 0 : static_cast<int64_t>(tc.g) * (a.a_gs ? a.a_gs : a.rows_per_group * lda));
+                    (gathered ? 0
+                     : a.packed ? row_base * lda
+                                : static_cast<int64_t>(tc.g) * (a.a_gs ? a.a_gs : a.rows_per_group * lda));
   const int64_t bg = static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb);
   const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + bg;
   const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + bg : B0;
@@ -279,7 +352,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
       int orow = orow0 + j * kRowsPerLoad + lr;
       if (stage_x && gathered) {
         // gathered rows past rows_g read as zero; others come from their token
-        orow = orow < rows_g ? a.gather[static_cast<int64_t>(tc.g) * a.rows_per_group + orow] : -1;
+        orow = orow < rows_g ? a.gather[row_base + orow] : -1;
       }
       // weight rows past N (and token rows past rows_g) land past the
       // operand's extent and read as zero
@@ -392,7 +465,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     // bytes per row).  Stored straight from the MFMA layout, one instruction
     // would write 8 bytes into each of 32 rows, and the L2 would take many
     // more, smaller write requests.
-    bf16_t* C = static_cast<bf16_t*>(a.C) + static_cast<int64_t>(tc.g) * a.rows_per_group * N;
+    bf16_t* C = static_cast<bf16_t*>(a.C) + row_base * N;
     const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
     constexpr int kOut = kGlu ? 64 : 128;              // output columns per wave
     constexpr int kPitch = kOut * 2 + 16;              // padded LDS row (bytes)
@@ -563,12 +636,22 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
   if (g >= a.groups) return;
   const int r = static_cast<int>(L % (static_cast<int64_t>(mt_max) * ntiles));
   const int mt = r / ntiles, nt = r % ntiles;
-  const int64_t rows_g = a.rows ? min<int64_t>(a.rows[g], a.rows_per_group) : a.rows_per_group;
+  int64_t rows_g = a.rows ? min<int64_t>(a.rows[g], a.rows_per_group) : a.rows_per_group;
+  int64_t row_base = static_cast<int64_t>(g) * a.rows_per_group;
+  if (a.packed) {
+    // packed rows: the group starts after the rows of the lower groups
+    // (each capped so that none reaches past total_rows)
+    int64_t start = 0;
+    for (int h = 0; h < g; ++h) start += max(a.rows[h], 0);
+    start = min(start, a.total_rows);
+    row_base = start;
+    rows_g = max<int64_t>(0, min<int64_t>(max(a.rows[g], 0), a.total_rows - start));
+  }
   const int m0 = mt * kFT, n0 = nt * kFT;
   if (m0 >= rows_g) return;
   const bool gathered = a.gather != nullptr;
-  const float* A = static_cast<const float*>(a.A) + (gathered ? 0 : static_cast<int64_t>(g) * a.rows_per_group * K);
-  const int32_t* grow = gathered ? a.gather + static_cast<int64_t>(g) * a.rows_per_group : nullptr;
+  const float* A = static_cast<const float*>(a.A) + (gathered ? 0 : row_base * K);
+  const int32_t* grow = gathered ? a.gather + row_base : nullptr;
   const float* B0 = static_cast<const float*>(a.B0) + static_cast<int64_t>(g) * N * K;
   const float* B1 = ACT == 2 ? static_cast<const float*>(a.B1) + static_cast<int64_t>(g) * N * K : nullptr;
   const int tx = threadIdx.x % kFT, ty = threadIdx.x / kFT;   // ty 0..7
@@ -598,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
       }
     }
   }
-  float* C = static_cast<float*>(a.C) + static_cast<int64_t>(g) * a.rows_per_group * N;
+  float* C = static_cast<float*>(a.C) + row_base * N;
   const float* bias = a.bias ? static_cast<const float*>(a.bias) + static_cast<int64_t>(g) * N : nullptr;
   const int n = n0 + tx;
   if (n >= N) return;
@@ -629,8 +712,11 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
     const int nout = a.act == 2 ? kBW / 2 : kBW;
-    const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kBM - 1) / kBM) *
-                          ((a.N + nout - 1) / nout);
+    if (a.packed && a.groups > kMaxPackedGroups) return hipErrorInvalidValue;
+    // packed rows: the groups' row tiles number at most total/256 + groups
+    const int64_t row_tiles = a.packed ? (a.total_rows + kBM - 1) / kBM + a.groups
+                                       : static_cast<int64_t>(a.groups) * ((a.rows_per_group + kBM - 1) / kBM);
+    const int64_t tiles = row_tiles * ((a.N + nout - 1) / nout);
     const unsigned grid = static_cast<unsigned>((tiles + 255) / 256 * 256);
     switch (a.act) {
       case 0: launch_bf16<0>(a, grid, s); break;

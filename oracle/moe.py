@@ -252,6 +252,29 @@ def assign_capacity(idx, n_experts, C, priority='rank'):
     return slot.astype(np.int32), dropped, np.asarray(cnt, np.int64), row_token
 
 
+def dropless_rows(idx, n_experts, priority='rank'):
+    """Dropless mode: every assignment is kept, and the experts' rows are laid
+    back to back with no padding ["Lab 18" s.3, the alternatives to dropping:
+    a capacity high enough that nothing is dropped, or block-sparse kernels
+    without the limit; "Mixture of experts" lecture, systems section: ragged
+    per-expert matmuls without padding].
+
+    Row of (t, j) = (assignments routed to lower-numbered experts) + its
+    queue position in its own expert, in the capacity queue's priority order.
+    Returns row [T,k] int32, counts [E] int64, row_token [T*k] int32.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    # every expert receives at most T assignments, so a capacity of T drops none
+    pos, dropped, counts, _ = assign_capacity(idx, n_experts, max(T, 1), priority)
+    assert not dropped.any()
+    first = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    row = (first[idx] + pos).astype(np.int32)
+    row_token = np.empty(T * k, np.int32)
+    row_token[row.ravel()] = np.repeat(np.arange(T, dtype=np.int32), k)
+    return row, counts, row_token
+
+
 # ----------------------------------------------------------------------------- experts
 def gelu(u):
     """Exact GELU: u/2 (1 + erf(u/sqrt 2))  (R11)."""
@@ -312,7 +335,7 @@ def combine(routed, shared=None, x=None, any_kept=None, dropped_output='residual
 
 # ----------------------------------------------------------------------------- forward
 def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank',
-                capacity_override=0, dropped_output='residual', logits=None):
+                capacity_override=0, dropped_output='residual', logits=None, dropless=False):
     """The whole layer.
 
     w: a ``synth.Workload``-like object (T, d, E, k, act, score, renormalize,
@@ -324,6 +347,8 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     rows: optional sorted token ids; expert maths and y only for those rows
        (routing, capacity and losses always use every token).
     logits: optional given float32 logits (then x is used only for expert maths).
+    dropless: keep every assignment (capacity T); 'slot' and 'row_token' are
+       then the packed rows of ``dropless_rows``.
 
     Steps: logits -> keys -> top-k -> gates/probs -> capacity -> experts ->
     combine, with the losses beside [P3 "What to implement" 1-5; P4 build
@@ -335,8 +360,13 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
         else np.asarray(logits, np.float32)
     idx, g, probs = route(z, k, w.score, w.renormalize, inp.get('select_bias'))
     lse = logsumexp(z)
-    C = capacity(T, k, E, w.cf, capacity_override)
-    slot, dropped, counts, row_token = assign_capacity(idx, E, C, priority)
+    if dropless:
+        C = T
+        slot, counts, row_token = dropless_rows(idx, E, priority)
+        dropped = np.zeros((T, k), bool)
+    else:
+        C = capacity(T, k, E, w.cf, capacity_override)
+        slot, dropped, counts, row_token = assign_capacity(idx, E, C, priority)
     l_aux = load_balancing_loss(probs, idx, E)
     l_z = float(np.mean(lse * lse))
 
@@ -374,7 +404,7 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     n_kept = int(kept_e.sum())
     stats = dict(kept=n_kept, dropped=T * k - n_kept,
                  fallback=int((~kept.any(axis=1)).sum()) if S is None else 0,
-                 pad=E * C - n_kept)
+                 pad=0 if dropless else E * C - n_kept)
     return dict(y=y, rows=rows, logits=z, idx=idx, gates=g, probs=probs, lse=lse,
                 capacity=C, slot=slot, dropped=dropped, counts=counts,
                 row_token=row_token, l_aux=l_aux, l_z=l_z, stats=stats)

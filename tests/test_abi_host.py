@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ('moe_route', 'moe_dispatch', 'moe_expert_ffn', 'moe_combine', 'moe_forward',
-              'moe_aux_losses', 'moe_validate', 'moe_workspace_bytes', 'moe_last_error'):
+              'moe_aux_losses', 'moe_validate', 'moe_workspace_bytes', 'moe_last_error',
+              'moe_expert_ffn_packed'):
         assert n in names
 
 
@@ -62,9 +63,10 @@ def test_struct_layout_matches_header(tmp_path, moe):
 #include <stddef.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_config), offsetof(moe_config, capacity_factor),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_config), offsetof(moe_config, capacity_factor),
          offsetof(moe_config, capacity_override), offsetof(moe_config, dropped_output),
-         sizeof(moe_weights), sizeof(moe_outputs), offsetof(moe_outputs, lse));
+         offsetof(moe_config, dropless), sizeof(moe_weights), sizeof(moe_outputs),
+         offsetof(moe_outputs, lse));
   return 0;
 }
 ''')
@@ -75,7 +77,7 @@ int main(void) {
                                        check=True).stdout.split()))
     want = [ctypes.sizeof(moe.moe_config), moe.moe_config.capacity_factor.offset,
             moe.moe_config.capacity_override.offset, moe.moe_config.dropped_output.offset,
-            ctypes.sizeof(moe.moe_weights), ctypes.sizeof(moe.moe_outputs),
+            moe.moe_config.dropless.offset, ctypes.sizeof(moe.moe_weights), ctypes.sizeof(moe.moe_outputs),
             moe.moe_outputs.lse.offset]
     assert got == want
 
@@ -162,3 +164,34 @@ def test_workspace_grows_with_capacity(moe):
     b = moe.moe_workspace_bytes(cfg(moe, capacity_factor=4.0))
     assert 0 < a < b
     assert a % 256 == 0
+
+
+def test_dropless_capacity_and_workspace(moe):
+    # dropless: C = T (a token picks an expert at most once), whatever the factor
+    assert moe.moe_validate(cfg(moe, dropless=True)) == 64
+    assert moe.moe_validate(cfg(moe, dropless=True, capacity_factor=0.5)) == 64
+    assert moe.moe_validate(cfg(moe, dropless=True, capacity_override=3)) == 64
+    c = cfg(moe, dropless=True)
+    c.dropless = 2
+    with pytest.raises(ValueError, match='dropless'):
+        moe.moe_validate(c)
+    # packed expert rows: T*k of them, not E*C; for the Mixtral shape the
+    # dropless workspace is smaller than the capacity-factor-1.25 one
+    big = dict(T=8192, d=4096, E=8, k=2, d_ff=14336, dtype='bf16', act='swiglu')
+    assert moe.moe_workspace_bytes(cfg(moe, dropless=True, **big)) < moe.moe_workspace_bytes(cfg(moe, **big))
+
+
+def test_packed_ffn_rejects_bad_arguments_before_launch(moe):
+    lib = moe._lib
+    c = cfg(moe)
+    args = lambda groups, rows, total, F=64: (ctypes.byref(c), 0, groups, rows, total, 16, None, 0, 16, None, None,
+                                              16, None, F, 16, 16, None)
+    assert lib.moe_expert_ffn_packed(*args(257, 16, 100)) == moe.MOE_EINVAL
+    assert b'groups' in lib.moe_last_error()
+    assert lib.moe_expert_ffn_packed(*args(4, 16, -1)) == moe.MOE_EINVAL
+    assert b'total_rows' in lib.moe_last_error()
+    assert lib.moe_expert_ffn_packed(*args(4, None, 100)) == moe.MOE_EINVAL
+    assert b'rows' in lib.moe_last_error()
+    assert lib.moe_expert_ffn_packed(*args(4, 16, 100, F=12)) == moe.MOE_EINVAL
+    # nothing to do: no launch, no pointer needed
+    assert lib.moe_expert_ffn_packed(*args(4, None, 0)) == moe.MOE_OK

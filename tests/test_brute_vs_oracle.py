@@ -92,3 +92,52 @@ def test_oracle_matches_brute_force(case):
 def test_tiny_f32_capacity_is_40():
     w = synth.WORKLOADS['tiny_f32']
     assert O.capacity(w.T, w.k, w.E, w.cf) == 40
+
+
+def test_dropless_rows_worked_example():
+    """Rows worked out by hand from the definition: expert e's choices follow
+    the choices of lower experts, in queue order.  Choices (token: experts)
+    0: 0 1, 1: 1 2, 2: 0 2, 3: 1 0.
+    Rank-major queue: expert 0 gets t0, t2 (rank 0), t3 (rank 1) -> rows 0-2;
+    expert 1 gets t1, t3 (rank 0), t0 (rank 1) -> rows 3-5; expert 2 gets t1,
+    t2 (rank 1) -> rows 6-7.  Token-major: expert 0 t0, t2, t3; expert 1 t0,
+    t1, t3; expert 2 t1, t2."""
+    idx = np.array([[0, 1], [1, 2], [0, 2], [1, 0]])
+    row, counts, row_token = O.dropless_rows(idx, 3, 'rank')
+    np.testing.assert_array_equal(row, [[0, 5], [3, 6], [1, 7], [4, 2]])
+    np.testing.assert_array_equal(counts, [3, 3, 2])
+    np.testing.assert_array_equal(row_token, [0, 2, 3, 1, 3, 0, 1, 2])
+    row, _, row_token = O.dropless_rows(idx, 3, 'token')
+    np.testing.assert_array_equal(row, [[0, 3], [4, 6], [1, 7], [5, 2]])
+    np.testing.assert_array_equal(row_token, [0, 2, 3, 0, 1, 3, 1, 2])
+
+
+@pytest.mark.parametrize('case', [c for c in CASES if c['name'] not in ('tiny_f32',)] +
+                         [dict(name='tiny_f32_token', priority='token',
+                               wl=synth.WORKLOADS['tiny_f32'].with_(T=32))],
+                         ids=lambda c: c['name'])
+def test_dropless_oracle_matches_brute_force(case):
+    """Dropless: nothing is dropped, y is the per-token sum of every chosen
+    expert's gated output (the brute force with no capacity limit), and the
+    packed row of each choice is the count of lower experts' choices plus its
+    queue position."""
+    w = case.get('wl') or synth.WORKLOADS[case['name']]
+    inp = synth.router_inputs(w)
+    ex = synth.all_expert_weights(w)
+    sh = synth.all_expert_weights(w, shared=True) if w.n_shared else None
+    pr = case.get('priority', 'rank')
+    o = O.moe_forward(w, inp, ex, sh, priority=pr, dropless=True)
+    x, wr, lb, sb, experts, shared = _lists(w, inp, ex, sh)
+    b = brute.forward(x, wr, lb, sb, experts, shared, k=w.k, act=w.act, score=w.score,
+                      renormalize=w.renormalize, C=w.T * w.k, dtype=w.dtype, priority=pr)
+    assert not o['dropped'].any() and not np.array(b['dropped']).any()
+    assert o['stats']['dropped'] == 0 and o['stats']['pad'] == 0 and o['stats']['fallback'] == 0
+    np.testing.assert_array_equal(o['counts'], np.array(b['counts']))
+    first = np.concatenate([[0], np.cumsum(b['counts'])[:-1]])
+    bidx = np.array(b['idx'])
+    np.testing.assert_array_equal(o['slot'], first[bidx] + np.array(b['slot']))
+    assert sorted(o['row_token'].tolist()) == sorted(np.repeat(np.arange(w.T), w.k).tolist())
+    yb = np.array(b['y'])
+    tol = 1e-6 if w.dtype == 'f32' else 1e-2
+    assert np.abs(o['y'] - yb).max() <= tol * np.abs(yb).max()
+    assert np.mean(o['y'] != yb) < 0.02

@@ -210,6 +210,33 @@ def test_dispatch_bit_exact(moe, case, dtype):
         assert (xe_n[e, ke:] == 0).all()        # rows past kept_e untouched
 
 
+@pytest.mark.parametrize('case', [c for c in DISPATCH_CASES if c[0] > 1][:6],
+                         ids=[f'T{c[0]}E{c[1]}k{c[2]}{c[4]}' for c in DISPATCH_CASES if c[0] > 1][:6])
+def test_dispatch_dropless_bit_exact(moe, case):
+    T, E, k, _, pr, skew, d = case
+    say('dispatch dropless', case)
+    idx = synth.random_indices(T, E, k, seed=T * 7 + E, skew=skew)
+    w = synth.Workload('d', T=T, d=d, E=E, k=k, d_ff=8, act='gelu', score='softmax', renormalize=-1,
+                       cf=1.0, dtype='bf16', seed=T)
+    x = synth.router_inputs(w)['x']
+    cfg = moe.make_config(T, d, E, k, 8, priority=pr, dtype='bf16', dropless=True)
+    xt = synth.to_torch(x, DEV)
+    slot = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    dropped = torch.full((T, k), 9, dtype=torch.uint8, device=DEV)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    row_token = torch.full((T * k,), -1, dtype=torch.int32, device=DEV)
+    xe = torch.zeros((T * k, d), dtype=xt.dtype, device=DEV)
+    moe.moe_dispatch(cfg, xt, torch.from_numpy(idx).to(DEV), slot, dropped, counts, row_token, xe,
+                     moe.workspace(cfg, DEV))
+    torch.cuda.synchronize()
+    r_row, r_counts, r_rt = O.dropless_rows(idx, E, pr)
+    np.testing.assert_array_equal(np_of(slot), r_row)
+    assert not np_of(dropped).any()
+    np.testing.assert_array_equal(np_of(counts), r_counts)
+    np.testing.assert_array_equal(np_of(row_token), r_rt)
+    np.testing.assert_array_equal(np_of(xe), x[r_rt])
+
+
 # ----------------------------------------------------------------------------- expert FFN
 FFN_CASES = [
     # (groups, rows_per_group, rows, d, F, act, dtype)
@@ -302,6 +329,76 @@ def test_expert_ffn_parity(moe, case):
     check(f64_of(h), f64_of(out), lambda g, n: slice(g * R, g * R + n))
 
 
+PACKED_CASES = [
+    # (rows per group, d, F, act, dtype): packed back to back, total bound T*k style
+    ([0, 1, 37, 256, 300, 0, 129], 256, 384, 'gelu', 'bf16'),
+    ([900, 0, 769, 3, 300, 1, 256, 257, 900, 450, 37, 128, 511, 900], 512, 1024, 'swiglu', 'bf16'),
+    ([600, 512, 257, 0, 600, 3, 600, 450], 104, 2048, 'gelu', 'bf16'),
+    ([40, 0, 3, 17], 32, 64, 'gelu', 'f32'),
+    ([50, 9, 0], 24, 40, 'swiglu', 'f32'),
+]
+
+
+@pytest.mark.parametrize('case', PACKED_CASES, ids=[f'G{len(c[0])}d{c[1]}F{c[2]}{c[3]}{c[4]}' for c in PACKED_CASES])
+def test_expert_ffn_packed_parity(moe, case):
+    rows, d, F, act, dtype = case
+    G = len(rows)
+    R = sum(rows)
+    total = R + 5                                       # a bound above the sum
+    say('ffn packed', case)
+    w = synth.Workload('p', T=max(R, 1), d=d, E=G, k=1, d_ff=F, act=act, score='softmax', renormalize=-1,
+                       cf=1.0, dtype=dtype, seed=G * 100 + d + 1)
+    a = synth.router_inputs(w)['x']                      # [R, d]
+    ex = synth.all_expert_weights(w)
+    if act == 'gelu':
+        g = np.random.default_rng(6)
+        ex['b_in'] = (g.standard_normal(ex['b_in'].shape) * 0.1).astype(np.float32)
+        ex['b_out'] = (g.standard_normal(ex['b_out'].shape) * 0.1).astype(np.float32)
+        if dtype == 'bf16':
+            ex['b_in'] = synth.as_f32(synth.bf16_bits(ex['b_in']))
+            ex['b_out'] = synth.as_f32(synth.bf16_bits(ex['b_out']))
+    cfg = moe.make_config(max(R, 1), d, G, 1, F, act=act, dtype=dtype)
+    tt = lambda v: synth.to_torch(synth.bf16_bits(v) if (dtype == 'bf16' and v.dtype == np.float32) else v, DEV)
+    at = synth.to_torch(a, DEV)
+    rows_t = torch.tensor(rows, dtype=torch.int32, device=DEV)
+    first = np.concatenate([[0], np.cumsum(rows)[:-1]])
+    af = synth.as_f32(a).astype(np.float64)
+    refs = {}
+    for gather in (False, True):
+        h = torch.full((total, F), 7.0, dtype=at.dtype, device=DEV)
+        out = torch.full((total, d), 7.0, dtype=at.dtype, device=DEV)
+        kw = {}
+        src = at
+        order = np.arange(R)
+        if gather:
+            # rows gathered from a shuffled token matrix
+            perm = np.random.default_rng(G + R).permutation(R)
+            a_sh = np.ascontiguousarray(a[np.argsort(perm)])     # a_sh[perm[i]] = a[i]
+            src = synth.to_torch(a_sh, DEV)
+            kw = dict(gather=torch.from_numpy(perm.astype(np.int32)).to(DEV))
+        if act == 'gelu':
+            moe.moe_expert_ffn_packed(cfg, act, G, rows_t, total, src, tt(ex['w_in']), None, tt(ex['b_in']),
+                                      tt(ex['w_out']), tt(ex['b_out']), F, h, out, **kw)
+        else:
+            moe.moe_expert_ffn_packed(cfg, act, G, rows_t, total, src, tt(ex['w_up']), tt(ex['w_gate']), None,
+                                      tt(ex['w_out']), None, F, h, out, **kw)
+        torch.cuda.synchronize()
+        hn, on = f64_of(h), f64_of(out)
+        tol = 1e-5 if dtype == 'f32' else 2e-2
+        for g_ in range(G):
+            n = rows[g_]
+            if not n:
+                continue
+            if g_ not in refs:
+                wts = {kk: synth.as_f32(v[g_]) for kk, v in ex.items()}
+                refs[g_] = O.expert_ffn(af[first[g_]:first[g_] + n], wts, act, dtype)
+            rh, ro = refs[g_]
+            assert maxrel(hn[first[g_]:first[g_] + n], rh) <= tol
+            assert maxrel(on[first[g_]:first[g_] + n], ro) <= tol
+        # rows past the packed total are untouched
+        assert (hn[R:] == 7.0).all() and (on[R:] == 7.0).all()
+
+
 # ----------------------------------------------------------------------------- combine and losses
 @pytest.mark.parametrize('dtype,shared,zero', [('bf16', False, 0), ('bf16', True, 0), ('f32', False, 0),
                                                ('f32', False, 1)])
@@ -344,6 +441,32 @@ def test_combine_parity(moe, dtype, shared, zero):
         np.testing.assert_array_equal(yn[fb], 0.0 if zero else xf[fb])
 
 
+def test_combine_dropless_reads_packed_rows(moe):
+    T, E, k, d = 700, 8, 3, 256
+    say('combine dropless')
+    idx = synth.random_indices(T, E, k, seed=17, skew=0.6)
+    row, counts, _ = O.dropless_rows(idx, E, 'rank')
+    w = synth.Workload('c', T=T, d=d, E=E, k=k, d_ff=8, act='gelu', score='softmax', renormalize=-1,
+                       cf=1.0, dtype='bf16', seed=18)
+    x = synth.router_inputs(w)['x']
+    ye = synth.router_inputs(w.with_(T=T * k, seed=19))['x']             # [T*k, d] packed
+    g = np.random.default_rng(2).random((T, k)).astype(np.float32)
+    cfg = moe.make_config(T, d, E, k, 8, dtype='bf16', dropless=True)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+    moe.moe_combine(cfg, synth.to_torch(x, DEV), synth.to_torch(ye, DEV), None, torch.from_numpy(idx).to(DEV),
+                    torch.from_numpy(g).to(DEV), torch.from_numpy(row).to(DEV),
+                    torch.zeros((T, k), dtype=torch.uint8, device=DEV), y)
+    torch.cuda.synchronize()
+    yef = synth.as_f32(ye).astype(np.float64)
+    routed = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            routed[t] += float(g[t, j]) * yef[row[t, j]]
+    ref = O.round_store(O.combine(routed, None, synth.as_f32(x).astype(np.float64), np.ones(T, bool), 'residual'),
+                        'bf16')
+    assert maxrel(f64_of(y), ref) <= 2e-2
+
+
 @pytest.mark.parametrize('score', ['softmax', 'sigmoid'])
 def test_aux_losses_from_given_logits(moe, score):
     T, E, k = 5000, 64, 6
@@ -372,8 +495,9 @@ def _compare_forward(moe, w, rows=None, **over):
     cov = over.get('capacity_override', 0)
     get = (lambda e: {kk: v[e] for kk, v in ex.items()})
     gsh = None if sh is None else (lambda s: {kk: v[s] for kk, v in sh.items()})
+    dl = bool(over.get('dropless', False))
     ref = O.moe_forward(w, inp, get, gsh, rows=rows, priority=pr, capacity_override=cov,
-                        dropped_output=dout)
+                        dropped_output=dout, dropless=dl)
     x = synth.as_f32(inp['x'])
     zr = ref['logits']
     zg = np_of(out['logits'])
@@ -400,6 +524,12 @@ def _compare_forward(moe, w, rows=None, **over):
         lse_abs = np.abs(ref['lse'])
         assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z']) + 2 * float((lse_abs * dz).mean()) + float((dz * dz).mean())
         say(f'  L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}, L_z {l[1]:.6f} vs {ref["l_z"]:.6f}, max dz {dz.max():.2e}')
+    elif dl:
+        # the packed rows the GPU's own choices give
+        r_row, r_counts, _ = O.dropless_rows(gi, w.E, pr)
+        np.testing.assert_array_equal(gs, r_row)
+        np.testing.assert_array_equal(gc, r_counts)
+        assert not gd.any()
     else:
         check_capacity_valid(gi, gs, gd, gc, C, w.E, pr)
     assert_propagated(np_of(out['gates'])[same], ref['gates'][same], dz[same], what='gates')
@@ -472,6 +602,31 @@ def test_forward_k_equals_E_bf16_swiglu(moe):
                        renormalize=-1, cf=1.0, dtype='bf16', seed=31)
     cfg, out, ref = _compare_forward(moe, w)
     assert not ref['dropped'].any()
+
+
+DROPLESS_FORWARDS = [
+    ('tiny_f32', dict(), None),
+    ('tiny_f32', dict(priority='token'), None),
+    ('switch_top1_skewed', dict(), None),
+    ('deepseekmoe_fine', dict(), 'every7'),
+    ('mixtral_8x_top2', dict(), 'sample'),
+    ('sigmoid_stress', dict(), 'sample'),
+]
+
+
+@pytest.mark.parametrize('case', DROPLESS_FORWARDS, ids=[f'{c[0]}{"_" + c[1]["priority"] if c[1] else ""}'
+                                                          for c in DROPLESS_FORWARDS])
+def test_forward_dropless(moe, case):
+    name, over, rsel = case
+    w = synth.WORKLOADS[name]
+    rows = None
+    if rsel == 'every7':
+        rows = np.arange(0, w.T, 7)
+    elif rsel == 'sample':
+        rows = np.sort(np.random.default_rng(3).choice(w.T, 160, replace=False))
+    cfg, out, ref = _compare_forward(moe, w, rows=rows, dropless=True, **over)
+    assert not ref['dropped'].any()
+    assert ref['stats']['dropped'] == 0 and ref['stats']['pad'] == 0
 
 
 def test_forward_is_deterministic(moe):
