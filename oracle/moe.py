@@ -205,6 +205,49 @@ def load_balancing_loss(probs, idx, n_experts):
     return float(n_experts * np.sum(f * P))
 
 
+def sequence_aux_loss(probs, idx, n_experts, seq_len):
+    """Sequence-wise balance loss: the balance formula E * sum_i f_i P_i taken
+    within each sequence of seq_len consecutive tokens (f over the sequence's
+    seq_len*k routed choices, P the mean of its tokens' full router
+    probabilities), averaged over the sequences.  ["Lab 18" s.2, the
+    auxiliary-loss-free note: a small sequence-wise balance loss is kept;
+    "Mixture of experts" lecture, DeepSeek section: the balancing unit is
+    where the variants differ, with the same formula.]  No alpha.
+    """
+    idx = np.asarray(idx)
+    probs = np.asarray(probs, F64)
+    T, k = idx.shape
+    if seq_len <= 0 or T % seq_len:
+        raise ValueError('T must be a positive multiple of seq_len')
+    n_seq = T // seq_len
+    total = 0.0
+    for b in range(n_seq):
+        rows = slice(b * seq_len, (b + 1) * seq_len)
+        cnt = np.bincount(idx[rows].reshape(-1), minlength=n_experts).astype(F64)
+        f = cnt / (seq_len * k)
+        P = probs[rows].mean(axis=0)
+        total += n_experts * float(np.sum(f * P))
+    return total / n_seq
+
+
+def update_select_bias(select_bias, counts, gamma, T, k):
+    """Auxiliary-loss-free balancing: after a batch, lower the selection bias
+    of every overloaded expert by gamma and raise it for every underloaded
+    one; an expert exactly at the mean load T*k/E keeps its bias.  The load
+    is the number of choices routed to the expert.  Each new bias is the
+    float32 sum b_i +- gamma.  ["Lab 18" s.2 auxiliary-loss-free balancing
+    (bias for selection only, a fixed small step) and its exercise 4 (step
+    0.001); "Mixture of experts" lecture, DeepSeek section.]
+    """
+    b = np.asarray(select_bias, np.float32)
+    counts = np.asarray(counts, np.int64)
+    E = b.size
+    # sign(mean - load), compared exactly as T*k versus load*E
+    s = np.sign(T * k - counts * E).astype(F64)
+    g = float(np.float32(gamma))
+    return (b.astype(F64) + g * s).astype(np.float32)
+
+
 def router_z_loss(z32):
     """(1/T) sum_t (log sum_i exp z_ti)^2  [P3 s.2 router z-loss; P1 concept map]."""
     lse = logsumexp(z32)

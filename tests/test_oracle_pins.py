@@ -403,3 +403,51 @@ def test_sampled_rows_equal_full_rows():
     rows = np.array([0, 7, 8, 31, 49])
     part = O.moe_forward(w, inp, ex, rows=rows)
     np.testing.assert_array_equal(part['y'], full['y'][rows])
+
+
+# ----------------------------------------------------------------------------- balancing variants
+def test_sequence_loss_worked_example():
+    """Worked by hand (E = 2, k = 1, two sequences of two tokens).
+    Sequence 1: both tokens to expert 0 with p = (1, 0): f = (1, 0), P = (1, 0),
+    loss 2 * 1 = 2.  Sequence 2: one token to each expert, p = (1/2, 1/2):
+    f = P = (1/2, 1/2), loss 2 * (1/4 + 1/4) = 1.  Mean 1.5; over the whole
+    batch f = P = (3/4, 1/4) would give 2 * (9/16 + 1/16) = 1.25."""
+    probs = np.array([[1, 0], [1, 0], [0.5, 0.5], [0.5, 0.5]])
+    idx = np.array([[0], [0], [0], [1]])
+    assert O.sequence_aux_loss(probs, idx, 2, 2) == 1.5
+    assert O.sequence_aux_loss(probs, idx, 2, 4) == 1.25
+    assert O.load_balancing_loss(probs, idx, 2) == 1.25
+    with pytest.raises(ValueError):
+        O.sequence_aux_loss(probs, idx, 2, 3)
+
+
+@pytest.mark.parametrize('E,k', [(4, 1), (8, 2), (16, 4)])
+def test_sequence_loss_balanced_and_collapsed(E, k):
+    S, n = 2 * E, 3
+    # every sequence balanced on its own (uniform probabilities): exactly 1
+    idx = np.array([[(t * k + j) % E for j in range(k)] for t in range(S)] * n)
+    probs = np.full((S * n, E), 1.0 / E)
+    assert abs(O.sequence_aux_loss(probs, idx, E, S) - 1.0) < 1e-12
+    # every sequence collapsed onto one expert with probability 1: E (each
+    # sequence onto a different expert, so the batch as a whole stays balanced-ish)
+    idx = np.concatenate([np.full((S, k), b % E) for b in range(n)])
+    probs = np.zeros((S * n, E))
+    for b in range(n):
+        probs[b * S:(b + 1) * S, b % E] = 1.0
+    if k == 1:
+        assert abs(O.sequence_aux_loss(probs, idx, E, S) - E) < 1e-12
+        assert O.load_balancing_loss(probs, idx, E) < E
+
+
+def test_bias_update_hand_values():
+    """Mean load T*k/E = 8*1/4 = 2: the expert with 3 choices is overloaded
+    (bias - gamma), the one with 1 underloaded (+ gamma), the two at 2 keep
+    theirs; each result is one float32 add."""
+    b = np.array([0.1, -0.2, 0.0, 0.5], np.float32)
+    got = O.update_select_bias(b, [3, 1, 2, 2], 0.001, T=8, k=1)
+    want = np.array([np.float32(0.1) - np.float32(0.001), np.float32(-0.2) + np.float32(0.001),
+                     np.float32(0.0), np.float32(0.5)], np.float32)
+    np.testing.assert_array_equal(got, want)
+    # a non-integer mean: T*k/E = 5/2, so 2 is under and 3 over
+    got = O.update_select_bias(np.zeros(2, np.float32), [2, 3], 0.5, T=5, k=1)
+    np.testing.assert_array_equal(got, [0.5, -0.5])
