@@ -226,6 +226,31 @@ MOE_API moe_status moe_combine(const moe_config* cfg, const void* x, const void*
 MOE_API moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int32_t* idx,
                           float* losses, void* ws, void* stream);
 
+/* Sequence-wise balance loss ["Lab 18" s.2, auxiliary-loss-free note: a
+ * small sequence-wise balance loss is kept; "Mixture of experts" lecture,
+ * DeepSeek section: the same formula over a different balancing unit]:
+ *   loss[0] = (1/B) sum_b E * sum_i f_bi P_bi over the B = T/seq_len
+ *   sequences b (tokens [b*seq_len, (b+1)*seq_len)), f_bi = the sequence's
+ *   choices routed to i / (seq_len*k), P_bi = the mean of its tokens'
+ *   probs[t,i]; no alpha.  Fixed-order float64 reductions.
+ *   seq_len [host] > 0, dividing T (MOE_EINVAL otherwise; T > 0)
+ *   probs [T,E] float32 (e.g. moe_route's probs); idx [T,k] int32;
+ *   loss [1] float32; ws required */
+MOE_API moe_status moe_sequence_aux_loss(const moe_config* cfg, int64_t seq_len, const float* probs,
+                                         const int32_t* idx, float* loss, void* ws, void* stream);
+
+/* Auxiliary-loss-free balancing ["Lab 18" s.2 and its exercise 4; "Mixture
+ * of experts" lecture, DeepSeek section]: the selection bias of every
+ * expert whose load is above the mean T*k/E drops by gamma, of every expert
+ * below it rises by gamma (float32 adds); an expert at the mean keeps it.
+ * The bias enters selection only (moe_route's select_bias).
+ *   counts       [E] int32 choices routed to each expert before capacity
+ *                (moe_dispatch's or moe_forward's counts)
+ *   select_bias  [E] float32, updated in place
+ *   gamma        [host] step, finite and >= 0 (the lab uses 0.001) */
+MOE_API moe_status moe_update_select_bias(const moe_config* cfg, const int32_t* counts, float* select_bias,
+                                          float gamma, void* stream);
+
 typedef struct moe_weights {
   const float* w_router;      /* [d,E] float32                                      */
   const float* logit_bias;    /* [E] float32 or NULL                                */

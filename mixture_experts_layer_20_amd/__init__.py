@@ -69,6 +69,8 @@ def _load():
                                 ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
         'moe_expert_ffn_packed': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
                                        ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
+        'moe_sequence_aux_loss': (st, [cfgp, ctypes.c_int64, _P, _P, _P, _P, _P]),
+        'moe_update_select_bias': (st, [cfgp, _P, _P, ctypes.c_float, _P]),
         'moe_combine': (st, [cfgp] + [_P] * 9),
         'moe_aux_losses': (st, [cfgp, _P, _P, _P, _P, _P]),
         'moe_forward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs),
@@ -224,6 +226,18 @@ def moe_expert_ffn_packed(cfg, act, groups, rows, total_rows, a, w_in, w_gate, b
                                       _ptr(b_in, 'b_in', dt), _ptr(w_out, 'w_out', dt),
                                       _ptr(b_out, 'b_out', dt), F, _ptr(h, 'h', dt), _ptr(out, 'out', dt),
                                       _stream(stream)))
+
+
+def moe_sequence_aux_loss(cfg, seq_len, probs, idx, loss, ws, stream=None):
+    _check(_lib.moe_sequence_aux_loss(ctypes.byref(cfg), int(seq_len), _ptr(probs, 'probs', torch.float32),
+                                      _ptr(idx, 'idx', torch.int32), _ptr(loss, 'loss', torch.float32),
+                                      _ptr(ws, 'ws'), _stream(stream)))
+
+
+def moe_update_select_bias(cfg, counts, select_bias, gamma, stream=None):
+    _check(_lib.moe_update_select_bias(ctypes.byref(cfg), _ptr(counts, 'counts', torch.int32),
+                                       _ptr(select_bias, 'select_bias', torch.float32), float(gamma),
+                                       _stream(stream)))
 
 
 def moe_combine(cfg, x, ye, shared_out, idx, gates, slot, dropped, y, stream=None):

@@ -110,6 +110,7 @@ struct Workspace {
   double* lse2_partial;
   int32_t* fallback_partial;
   double* psum;
+  double* seq_partial;
   bf16_t* wplanes;
   float* zraw;
   int32_t* idx_tmp;
@@ -144,6 +145,7 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   w.lse2_partial = static_cast<double*>(take(sizeof(double) * n_rtiles));
   w.fallback_partial = static_cast<int32_t*>(take(sizeof(int32_t) * n_tiles));
   w.psum = static_cast<double*>(take(sizeof(double) * (c.E + 1)));
+  w.seq_partial = static_cast<double*>(take(sizeof(double) * std::max<int64_t>(c.T, 1)));
   w.wplanes = static_cast<bf16_t*>(take(sizeof(bf16_t) * 4 * c.E * c.d));
   w.zraw = static_cast<float*>(take(sizeof(float) * router_splits(c.T, c.E, c.d) * c.T * c.E));
   w.idx_tmp = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
@@ -473,6 +475,44 @@ moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int3
   l.fallback_partial = nullptr;
   l.losses = losses;
   return hip_status(launch_losses(l, s), "aux-loss finaliser");
+}
+
+moe_status moe_sequence_aux_loss(const moe_config* cfg, int64_t seq_len, const float* probs, const int32_t* idx,
+                                 float* loss, void* ws, void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  if (c.T == 0) return fail(MOE_EINVAL, "the sequence-wise loss needs T > 0");
+  if (seq_len <= 0 || c.T % seq_len)
+    return fail(MOE_EINVAL, "seq_len must be positive and divide T (T=%lld, seq_len=%lld)",
+                static_cast<long long>(c.T), static_cast<long long>(seq_len));
+  MOE_TRY(check_ptr(probs, "probs", 4));
+  MOE_TRY(check_ptr(idx, "idx", 4));
+  MOE_TRY(check_ptr(loss, "loss", 4));
+  MOE_TRY(check_ptr(ws, "ws", 256));
+  Workspace w = carve(c, C, ws);
+  SeqLossArgs a{};
+  a.probs = probs;
+  a.idx = idx;
+  a.partial = w.seq_partial;
+  a.loss = loss;
+  a.seq_len = seq_len;
+  a.n_seq = c.T / seq_len;
+  a.E = c.E;
+  a.k = c.k;
+  return hip_status(launch_seq_loss(a, static_cast<hipStream_t>(stream)), "sequence-wise loss");
+}
+
+moe_status moe_update_select_bias(const moe_config* cfg, const int32_t* counts, float* select_bias, float gamma,
+                                  void* stream) {
+  MOE_TRY(validate(cfg, nullptr));
+  const moe_config& c = *cfg;
+  if (!(gamma >= 0.0f) || gamma == __builtin_huge_valf())
+    return fail(MOE_EINVAL, "gamma must be finite and >= 0 (got %g)", static_cast<double>(gamma));
+  MOE_TRY(check_ptr(counts, "counts", 4));
+  MOE_TRY(check_ptr(select_bias, "select_bias", 4));
+  return hip_status(launch_bias_update(counts, select_bias, c.E, c.T * c.k, gamma, static_cast<hipStream_t>(stream)),
+                    "selection-bias update");
 }
 
 moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* x, moe_outputs* out, void* ws,

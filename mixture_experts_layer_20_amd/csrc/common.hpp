@@ -174,12 +174,24 @@ struct LossArgs {
   int packed;                 // dropless: no padding in the statistics
 };
 
+struct SeqLossArgs {
+  const float* probs;         // [T,E]
+  const int32_t* idx;         // [T,k]
+  double* partial;            // [n_seq] per-sequence losses (workspace)
+  float* loss;                // [1]
+  int64_t seq_len, n_seq;
+  int E, k;
+};
+
 // host-side launchers (defined in the kernel translation units)
 hipError_t launch_route(const RouteArgs& a, int dtype, hipStream_t s);
 hipError_t launch_capacity(const CapArgs& a, int dtype, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_losses(const LossArgs& a, hipStream_t s);
+hipError_t launch_seq_loss(const SeqLossArgs& a, hipStream_t s);
+hipError_t launch_bias_update(const int32_t* counts, float* select_bias, int E, int64_t Tk, float gamma,
+                              hipStream_t s);
 
 // The bf16 router's logits GEMM splits d into S parts (one partial-logit
 // slab each, summed in a fixed order) when the token tiles alone would not

@@ -195,3 +195,17 @@ def test_packed_ffn_rejects_bad_arguments_before_launch(moe):
     assert lib.moe_expert_ffn_packed(*args(4, 16, 100, F=12)) == moe.MOE_EINVAL
     # nothing to do: no launch, no pointer needed
     assert lib.moe_expert_ffn_packed(*args(4, None, 0)) == moe.MOE_OK
+
+
+def test_balancing_entry_points_reject_bad_arguments(moe):
+    lib = moe._lib
+    c = cfg(moe)                                     # T = 64
+    assert lib.moe_sequence_aux_loss(ctypes.byref(c), 48, 16, 16, 16, 256, None) == moe.MOE_EINVAL
+    assert b'seq_len' in lib.moe_last_error()
+    assert lib.moe_sequence_aux_loss(ctypes.byref(c), 0, 16, 16, 16, 256, None) == moe.MOE_EINVAL
+    assert lib.moe_sequence_aux_loss(ctypes.byref(c), 16, None, 16, 16, 256, None) == moe.MOE_EINVAL
+    assert b'probs' in lib.moe_last_error()
+    assert lib.moe_update_select_bias(ctypes.byref(c), 16, 16, ctypes.c_float(-0.001), None) == moe.MOE_EINVAL
+    assert b'gamma' in lib.moe_last_error()
+    assert lib.moe_update_select_bias(ctypes.byref(c), None, 16, ctypes.c_float(0.001), None) == moe.MOE_EINVAL
+    assert b'counts' in lib.moe_last_error()

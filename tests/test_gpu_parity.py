@@ -467,6 +467,38 @@ def test_combine_dropless_reads_packed_rows(moe):
     assert maxrel(f64_of(y), ref) <= 2e-2
 
 
+@pytest.mark.parametrize('T,E,k,S', [(64, 4, 2, 16), (4096, 16, 1, 512), (16384, 64, 6, 2048), (1000, 8, 2, 1000),
+                                     (96, 256, 32, 32)])
+def test_sequence_aux_loss_parity(moe, T, E, k, S):
+    say('sequence loss', T, E, k, S)
+    z = synth.random_logits(T, E, seed=T + E, scale=2.0)
+    idx, _, probs = O.route(z, k)
+    cfg = moe.make_config(T, 8, E, k, 8, dtype='f32')
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    moe.moe_sequence_aux_loss(cfg, S, torch.from_numpy(probs.astype(np.float32)).to(DEV),
+                              torch.from_numpy(idx.astype(np.int32)).to(DEV), loss, moe.workspace(cfg, DEV))
+    torch.cuda.synchronize()
+    ref = O.sequence_aux_loss(probs.astype(np.float32), idx, E, S)
+    assert abs(float(loss.item()) - ref) <= 1e-5 * abs(ref)
+    if S == T:
+        assert abs(ref - O.load_balancing_loss(probs.astype(np.float32), idx, E)) <= 1e-12 * ref
+
+
+@pytest.mark.parametrize('T,E,k', [(64, 4, 2), (4096, 16, 1), (65536, 128, 8), (10, 256, 3)])
+def test_select_bias_update_bit_exact(moe, T, E, k):
+    say('bias update', T, E, k)
+    g = np.random.default_rng(T + E)
+    counts = g.integers(0, 2 * T * k // E + 2, E).astype(np.int32)
+    if T * k % E == 0:
+        counts[:3] = T * k // E                       # exactly at the mean: unchanged
+    b = g.uniform(-0.1, 0.1, E).astype(np.float32)
+    cfg = moe.make_config(T, 8, E, k, 8, dtype='bf16')
+    bt = torch.from_numpy(b.copy()).to(DEV)
+    moe.moe_update_select_bias(cfg, torch.from_numpy(counts).to(DEV), bt, 0.001)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np_of(bt), O.update_select_bias(b, counts, 0.001, T, k))
+
+
 @pytest.mark.parametrize('score', ['softmax', 'sigmoid'])
 def test_aux_losses_from_given_logits(moe, score):
     T, E, k = 5000, 64, 6
