@@ -67,12 +67,14 @@ def sigmoid_key(z):
 
 
 def forward(x, w_router, logit_bias, select_bias, experts, shared, *, k, act, score,
-            renormalize, C, dtype, priority='rank', dropped_output='residual'):
+            renormalize, C, dtype, priority='rank', dropped_output='residual', routing='token'):
     """Per-token reference.  Lists of lists in, dict of lists out.
 
     x [T][d]; w_router [d][E]; experts[e] dict with lists (w_in [F][d], b_in,
     w_out [d][F], b_out) or (w_gate, w_up, w_out); shared: list of GELU expert
-    dicts (may be empty).
+    dicts (may be empty).  routing='expert': each expert takes, by repeated
+    maximum over the tokens, the C largest float32-rounded probabilities
+    (equal -> lower token), and the gate is the probability itself.
     """
     T, d, E = len(x), len(x[0]), len(w_router[0])
     # logits, one product at a time, then one float32 rounding
@@ -128,6 +130,19 @@ def forward(x, w_router, logit_bias, select_bias, experts, shared, *, k, act, sc
                 gate.append([sv[i] / tot for i in chosen])
             else:
                 gate.append([sv[i] for i in chosen])
+    if routing == 'expert':
+        picks = []                       # picks[e] = tokens chosen by expert e, ascending
+        for i in range(E):
+            mine = []
+            for _ in range(min(C, T)):
+                best = None
+                for t in range(T):
+                    if t in mine:
+                        continue
+                    if best is None or f32(probs[t][i]) > f32(probs[best][i]):
+                        best = t
+                mine.append(best)
+            picks.append(sorted(mine))
     # capacity: slot = number of earlier assignments (priority order) to the same expert
     seq = [(t, j) for j in range(k) for t in range(T)] if priority == 'rank' else \
         [(t, j) for t in range(T) for j in range(k)]
@@ -159,13 +174,13 @@ def forward(x, w_router, logit_bias, select_bias, experts, shared, *, k, act, sc
     for t in range(T):
         acc = [0.0] * d
         any_kept = False
-        for j in range(k):
-            if dropped[t][j]:
-                continue
+        mine = [(i, probs[t][i]) for i in range(E) if t in picks[i]] if routing == 'expert' else \
+            [(idx[t][j], gate[t][j]) for j in range(k) if not dropped[t][j]]
+        for i, gv in mine:
             any_kept = True
-            out = run(experts[idx[t][j]], x[t], act)
+            out = run(experts[i], x[t], act)
             for c in range(d):
-                acc[c] += gate[t][j] * out[c]
+                acc[c] += gv * out[c]
         for s_ in shared:
             out = run(s_, x[t], 'gelu')
             for c in range(d):
@@ -173,9 +188,14 @@ def forward(x, w_router, logit_bias, select_bias, experts, shared, *, k, act, sc
         if not any_kept and not shared:
             acc = list(x[t]) if dropped_output == 'residual' else [0.0] * d
         y.append([store(v, dtype) for v in acc])
-    counts = [sum(1 for t in range(T) for j in range(k) if idx[t][j] == e) for e in range(E)]
-    l_aux = E * sum((counts[i] / (T * k)) * (sum(probs[t][i] for t in range(T)) / T)
+    if routing == 'expert':
+        counts = [len(picks[e]) for e in range(E)]
+        sel = [[picks[e].index(t) if t in picks[e] else -1 for e in range(E)] for t in range(T)]
+    else:
+        counts = [sum(1 for t in range(T) for j in range(k) if idx[t][j] == e) for e in range(E)]
+        sel = None
+    l_aux = E * sum((counts[i] / sum(counts)) * (sum(probs[t][i] for t in range(T)) / T)
                     for i in range(E))
     l_z = sum(v * v for v in lse) / T
     return dict(y=y, logits=z, idx=idx, gates=gate, probs=probs, lse=lse, slot=slot,
-                dropped=dropped, counts=counts, l_aux=l_aux, l_z=l_z)
+                dropped=dropped, counts=counts, l_aux=l_aux, l_z=l_z, sel=sel)

@@ -318,6 +318,32 @@ def dropless_rows(idx, n_experts, priority='rank'):
     return row, counts, row_token
 
 
+def expert_choice(probs, C):
+    """Expert-choice routing: every expert picks the C tokens with the largest
+    router probability for it (all T tokens when T <= C), equal scores to the
+    lower token index, and holds its picks in token order.  ["Lab 18"
+    exercise 1 (each expert picks its top tokens: balance by construction, no
+    dropping) and "Common extensions"; "Mixture of experts" lecture, routing
+    families: the top of each expert's row of the token x expert score
+    matrix.]  The scores are the given float32 probabilities (the decision is
+    taken in the precision the router stores them in).
+    Returns row_token [E, min(C, T)] int32 (ascending tokens) and sel [T, E]
+    int32, the slot of token t in expert e or -1.
+    """
+    probs = np.asarray(probs, np.float32)
+    T, E = probs.shape
+    n = min(int(C), T)
+    row_token = np.empty((E, n), np.int32)
+    sel = np.full((T, E), -1, np.int32)
+    tok = np.arange(T)
+    for e in range(E):
+        order = np.lexsort((tok, -probs[:, e].astype(F64)))     # score descending, token ascending
+        picked = np.sort(order[:n])
+        row_token[e] = picked
+        sel[picked, e] = np.arange(n, dtype=np.int32)
+    return row_token, sel
+
+
 # ----------------------------------------------------------------------------- experts
 def gelu(u):
     """Exact GELU: u/2 (1 + erf(u/sqrt 2))  (R11)."""
@@ -378,7 +404,8 @@ def combine(routed, shared=None, x=None, any_kept=None, dropped_output='residual
 
 # ----------------------------------------------------------------------------- forward
 def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank',
-                capacity_override=0, dropped_output='residual', logits=None, dropless=False):
+                capacity_override=0, dropped_output='residual', logits=None, dropless=False,
+                routing='token'):
     """The whole layer.
 
     w: a ``synth.Workload``-like object (T, d, E, k, act, score, renormalize,
@@ -392,6 +419,9 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     logits: optional given float32 logits (then x is used only for expert maths).
     dropless: keep every assignment (capacity T); 'slot' and 'row_token' are
        then the packed rows of ``dropless_rows``.
+    routing: 'token' (token choice, the default) or 'expert' (expert choice:
+       every expert takes its C best tokens by float32 probability, the gate
+       is that probability).
 
     Steps: logits -> keys -> top-k -> gates/probs -> capacity -> experts ->
     combine, with the losses beside [P3 "What to implement" 1-5; P4 build
@@ -403,6 +433,9 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
         else np.asarray(logits, np.float32)
     idx, g, probs = route(z, k, w.score, w.renormalize, inp.get('select_bias'))
     lse = logsumexp(z)
+    if routing == 'expert':
+        return _expert_choice_forward(w, inp, experts, shared_experts, rows, capacity_override,
+                                      dropped_output, z, idx, g, probs, lse)
     if dropless:
         C = T
         slot, counts, row_token = dropless_rows(idx, E, priority)
@@ -451,6 +484,50 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     return dict(y=y, rows=rows, logits=z, idx=idx, gates=g, probs=probs, lse=lse,
                 capacity=C, slot=slot, dropped=dropped, counts=counts,
                 row_token=row_token, l_aux=l_aux, l_z=l_z, stats=stats)
+
+
+def _expert_choice_forward(w, inp, experts, shared_experts, rows, capacity_override, dropped_output,
+                           z, idx, g, probs, lse):
+    """The layer under expert-choice routing (see ``expert_choice``): y_t is
+    the sum over the experts that picked t of p_te * FFN_e(x_t) (+ shared
+    experts); a token no expert picked passes through (or 0) as under token
+    choice.  f_i in the balance loss counts picks: count_i / (sum of counts)."""
+    T, E, k, d = w.T, w.E, w.k, w.d
+    C = capacity(T, k, E, w.cf, capacity_override)
+    row_token, sel = expert_choice(np.asarray(probs, np.float32), C)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    sel_rows = np.zeros(T, bool)
+    sel_rows[rows] = True
+    pos = np.full(T, -1, np.int64)
+    pos[rows] = np.arange(rows.size)
+    xa = as_f32(inp['x'])
+    get = experts if callable(experts) else (lambda e: {kk: v[e] for kk, v in experts.items()})
+    routed = np.zeros((rows.size, d), F64)
+    for e in range(E):
+        t_e = row_token[e][sel_rows[row_token[e]]]
+        if t_e.size == 0:
+            continue
+        _, o = expert_ffn(xa[t_e].astype(F64), _f32_weights(get(e)), w.act, w.dtype)
+        routed[pos[t_e]] += probs[t_e, e][:, None] * o
+    S = None
+    if shared_experts is not None and getattr(w, 'n_shared', 0) > 0:
+        gs = shared_experts if callable(shared_experts) else \
+            (lambda s_: {kk: v[s_] for kk, v in shared_experts.items()})
+        S = np.zeros((rows.size, d), F64)
+        for s_ in range(w.n_shared):
+            _, o = expert_ffn(xa[rows].astype(F64), _f32_weights(gs(s_)), 'gelu', w.dtype)
+            S += o
+    picked = (sel >= 0).any(axis=1)
+    y = round_store(combine(routed, S, xa[rows], picked[rows], dropped_output), w.dtype)
+    counts = (sel >= 0).sum(axis=0).astype(np.int64)
+    f = counts / max(1, counts.sum())
+    l_aux = float(E * np.sum(f * np.asarray(probs, F64).mean(axis=0)))
+    n_kept = int(counts.sum())
+    stats = dict(kept=n_kept, dropped=0, fallback=int((~picked).sum()) if S is None else 0,
+                 pad=E * C - n_kept)
+    return dict(y=y, rows=rows, logits=z, idx=idx, gates=g, probs=probs, lse=lse, capacity=C,
+                row_token=row_token, sel=sel, counts=counts, l_aux=l_aux,
+                l_z=float(np.mean(lse * lse)), stats=stats)
 
 
 def _f32_weights(wts):

@@ -141,3 +141,112 @@ def test_dropless_oracle_matches_brute_force(case):
     tol = 1e-6 if w.dtype == 'f32' else 1e-2
     assert np.abs(o['y'] - yb).max() <= tol * np.abs(yb).max()
     assert np.mean(o['y'] != yb) < 0.02
+
+
+# ----------------------------------------------------------------------------- expert choice
+def test_expert_choice_worked_example():
+    """Picks worked out by hand: each column's C largest entries, the equal
+    0.5s of expert 0 going to the lower token, picks held in token order."""
+    p = np.array([[.5, .2], [.1, .7], [.5, .6], [.3, .1]], np.float32)
+    rt, sel = O.expert_choice(p, 2)
+    np.testing.assert_array_equal(rt, [[0, 2], [1, 2]])
+    np.testing.assert_array_equal(sel, [[0, -1], [-1, 0], [1, 1], [-1, -1]])
+    rt, sel = O.expert_choice(p, 1)
+    np.testing.assert_array_equal(rt, [[0], [1]])              # 0.5 = 0.5 -> token 0
+    rt, _ = O.expert_choice(p, 3)
+    np.testing.assert_array_equal(rt, [[0, 2, 3], [0, 1, 2]])
+    rt, sel = O.expert_choice(p, 9)                              # C > T: every token
+    np.testing.assert_array_equal(rt, [[0, 1, 2, 3]] * 2)
+    np.testing.assert_array_equal(sel, [[0, 0], [1, 1], [2, 2], [3, 3]])
+
+
+def test_expert_choice_is_best_subset():
+    """On a dyadic grid (exact sums) every expert's picks are the C-subset of
+    largest total score, and among equal totals the one whose sorted tokens
+    come first: that is what 'top C with ties to the lower token' means."""
+    import itertools
+    rng = np.random.default_rng(5)
+    for trial in range(30):
+        T, E = int(rng.integers(1, 8)), int(rng.integers(1, 4))
+        p = (rng.integers(0, 6, size=(T, E)) / 8).astype(np.float32)   # many ties
+        C = int(rng.integers(1, T + 2))
+        rt, sel = O.expert_choice(p, C)
+        n = min(C, T)
+        for e in range(E):
+            best = max(itertools.combinations(range(T), n),
+                       key=lambda s: (sum(float(p[t, e]) for t in s), [-t for t in s]))
+            assert rt[e].tolist() == list(best), (trial, e)
+            assert sorted(np.nonzero(sel[:, e] >= 0)[0].tolist()) == list(best)
+            assert [sel[t, e] for t in best] == list(range(n))
+
+
+EC_CASES = [
+    dict(name='ec_gelu_f32', wl=synth.Workload('h', T=16, d=8, E=4, k=2, d_ff=8, act='gelu',
+                                               score='softmax', renormalize=-1, cf=1.0,
+                                               dtype='f32', seed=31)),
+    dict(name='ec_swiglu_bf16_cf2', wl=synth.Workload('i', T=24, d=8, E=4, k=1, d_ff=12,
+                                                      act='swiglu', score='softmax',
+                                                      renormalize=-1, cf=2.0, dtype='bf16',
+                                                      seed=32)),
+    dict(name='ec_shared_sigmoid', wl=synth.Workload('j', T=20, d=8, E=8, k=2, d_ff=4,
+                                                     act='gelu', score='sigmoid', renormalize=1,
+                                                     cf=1.0, dtype='bf16', seed=33, n_shared=1,
+                                                     d_ff_shared=4)),
+    dict(name='ec_zero_fallback', override=3, dropped_output='zero',
+         wl=synth.Workload('k', T=12, d=4, E=3, k=1, d_ff=4, act='gelu', score='softmax',
+                           renormalize=-1, cf=1.0, dtype='f32', seed=34)),
+    dict(name='ec_capacity_over_T', override=40,
+         wl=synth.Workload('l', T=10, d=4, E=3, k=1, d_ff=4, act='gelu', score='softmax',
+                           renormalize=-1, cf=1.0, dtype='f32', seed=35)),
+]
+
+
+@pytest.mark.parametrize('case', EC_CASES, ids=[c['name'] for c in EC_CASES])
+def test_expert_choice_oracle_matches_brute_force(case):
+    """Expert choice: the picks equal the brute force's repeated maximum over
+    tokens, every expert holds exactly min(C, T) tokens, and y is the
+    per-token sum of the picking experts' outputs weighted by probability."""
+    w = case['wl']
+    inp = synth.router_inputs(w)
+    ex = synth.all_expert_weights(w)
+    sh = synth.all_expert_weights(w, shared=True) if w.n_shared else None
+    ov = case.get('override', 0)
+    dout = case.get('dropped_output', 'residual')
+    o = O.moe_forward(w, inp, ex, sh, capacity_override=ov, dropped_output=dout,
+                      routing='expert')
+    x, wr, lb, sb, experts, shared = _lists(w, inp, ex, sh)
+    b = brute.forward(x, wr, lb, sb, experts, shared, k=w.k, act=w.act, score=w.score,
+                      renormalize=w.renormalize, C=o['capacity'], dtype=w.dtype,
+                      dropped_output=dout, routing='expert')
+    n = min(o['capacity'], w.T)
+    np.testing.assert_array_equal(o['counts'], [n] * w.E)
+    np.testing.assert_array_equal(o['counts'], b['counts'])
+    np.testing.assert_array_equal(o['sel'], np.array(b['sel']))
+    assert o['stats']['pad'] == w.E * (o['capacity'] - n)
+    assert abs(o['l_aux'] - b['l_aux']) <= 1e-12 * abs(b['l_aux'])
+    yb = np.array(b['y'])
+    tol = 1e-6 if w.dtype == 'f32' else 1e-2
+    assert np.abs(o['y'] - yb).max() <= tol * np.abs(yb).max()
+    assert np.mean(o['y'] != yb) < 0.02
+
+
+def test_expert_choice_full_capacity_is_dense_mixture():
+    """With C >= T every expert takes every token, so the layer is the dense
+    soft mixture y_t = sum_e p_te FFN_e(x_t) over all experts; under softmax
+    the balance loss is then E * sum_i (1/E) P_i = 1."""
+    w = synth.Workload('m', T=12, d=8, E=4, k=1, d_ff=8, act='gelu', score='softmax',
+                       renormalize=-1, cf=1.0, dtype='f32', seed=36)
+    inp = synth.router_inputs(w)
+    ex = synth.all_expert_weights(w)
+    o = O.moe_forward(w, inp, ex, capacity_override=w.T, routing='expert')
+    xa = synth.as_f32(inp['x']).astype(np.float64)
+    z = xa @ inp['w_router'].astype(np.float64)
+    p = np.exp(z - z.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    dense = np.zeros_like(xa)
+    for e in range(w.E):
+        _, out = O.expert_ffn(xa, {kk: synth.as_f32(v[e]).astype(np.float64)
+                                   for kk, v in ex.items()}, 'gelu', 'f32')
+        dense += p[:, [e]] * out
+    np.testing.assert_allclose(o['y'], dense, rtol=1e-5, atol=1e-6)
+    assert abs(o['l_aux'] - 1.0) < 1e-12
