@@ -75,6 +75,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 typedef enum { MOE_GELU = 0, MOE_SWIGLU = 1 } moe_act;
 typedef enum { MOE_RANK_MAJOR = 0, MOE_TOKEN_MAJOR = 1 } moe_priority;
+typedef enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1 } moe_routing;
 
 typedef struct moe_config {
   int64_t T;                  /* tokens (B*S flattened by the caller)                 */
@@ -93,6 +94,7 @@ typedef struct moe_config {
   int32_t priority;           /* moe_priority of the capacity queue                    */
   int32_t dropped_output;     /* 0: fully dropped token -> y = x; 1: y = 0             */
   int32_t dropless;           /* 0: capacity C as above; 1: dropless (see below)       */
+  int32_t routing;            /* moe_routing: token choice (above) or expert choice    */
 } moe_config;
 
 /* Dropless mode (dropless = 1) ["Lab 18" s.3, alternatives to dropping: a
@@ -108,6 +110,25 @@ typedef struct moe_config {
  *   - slot[t,j] is that packed ROW (not the position inside the expert);
  *     row_token is [T*k], xe, h and ye are [T*k, ...];
  *   - moe_combine reads ye[slot[t,j]]. */
+
+/* Expert-choice routing (routing = MOE_EXPERT_CHOICE) ["Lab 18" exercise 1
+ * and "Common extensions": each expert picks its top tokens, so the load is
+ * balanced by construction and nothing is dropped, while a token may be
+ * picked by several experts or by none; "Mixture of experts" lecture,
+ * routing families: the top of each expert's row of the token x expert
+ * score matrix]:
+ *   - C is computed as above (k is then the mean number of experts a token
+ *     gets) and every expert takes n = min(C, T) tokens: those with the
+ *     largest float32 probability probs[t,e], equal values to the lower
+ *     token, held in its rows in token order (row_token [E,C], rows >= n
+ *     unused);
+ *   - sel[t,e] is token t's row inside expert e, or -1;
+ *   - y_t = sum over the experts e that picked t, in e order, of
+ *     probs[t,e] * FFN_e(x_t) (+ shared experts); a token no expert picked
+ *     gets x_t (or 0, dropped_output = 1) when there is no shared expert;
+ *   - L_aux = E * sum_i f_i P_i with f_i = counts_i / sum_j counts_j (1/E);
+ *     stats = {E*n picks, 0 dropped, unpicked tokens, E*(C - n) pad slots};
+ *   - dropless must be 0 (MOE_EINVAL otherwise). */
 
 /* Check a configuration; on MOE_OK store the capacity C in *capacity [host]
  * (may be NULL). Runs on the host only. ["Lab 18" s.3; "Lab 01" traps] */
@@ -219,6 +240,30 @@ MOE_API moe_status moe_combine(const moe_config* cfg, const void* x, const void*
                        const void* shared_out, const int32_t* idx, const float* gates,
                        const int32_t* slot, const uint8_t* dropped, void* y, void* stream);
 
+/* Expert-choice selection (routing must be MOE_EXPERT_CHOICE, else
+ * MOE_EINVAL) ["Lab 18" exercise 1; see the expert-choice block above].
+ *   probs      [T,E] float32 router probabilities (moe_route's probs)
+ *   row_token  [E,C] int32: the n = min(C,T) tokens expert e picked, in
+ *              ascending order, in row e's first n entries (the rest untouched)
+ *   sel        [T,E] int32: the row of token t inside expert e, or -1
+ *   counts     [E] int32: n for every expert
+ *   ws         workspace (required; it holds the [E,T] transposed keys)
+ * Feed row_token and counts to moe_expert_ffn (groups E, rows_per_group C,
+ * gather row_token) and sel to moe_combine_expert_choice. */
+MOE_API moe_status moe_expert_choice(const moe_config* cfg, const float* probs, int32_t* row_token, int32_t* sel,
+                                     int32_t* counts, void* ws, void* stream);
+
+/* Expert-choice combine (routing must be MOE_EXPERT_CHOICE):
+ *   y_t = sum over e with sel[t,e] >= 0, in e order, of
+ *         probs[t,e] * ye[e, sel[t,e]]  + shared_out[t],
+ *   accumulated in float32, rounded once to the storage type; a token with
+ *   no pick and no shared_out gets x_t (or 0).
+ *   x [T,d]; ye [E,C,d]; shared_out [T,d] or NULL; probs [T,E] float32;
+ *   sel [T,E] int32 (moe_expert_choice's); y [T,d]. */
+MOE_API moe_status moe_combine_expert_choice(const moe_config* cfg, const void* x, const void* ye,
+                                             const void* shared_out, const float* probs, const int32_t* sel,
+                                             void* y, void* stream);
+
 /* Auxiliary losses from given logits and choices ["Lab 18" s.2 and "What to
  * implement" 2-3; "Lab 01" traps]: losses[0] = E * sum_i f_i P_i,
  * losses[1] = mean_t logsumexp(z_t)^2 (no alpha applied).
@@ -278,11 +323,17 @@ typedef struct moe_outputs {
   float* logits;              /* [T,E] or NULL                                        */
   float* probs;               /* [T,E] or NULL                                        */
   float* lse;                 /* [T] or NULL                                          */
+  int32_t* sel;               /* [T,E] expert choice: row of t in e or -1 (required then;
+                                 ignored under token choice)                          */
 } moe_outputs;
 
 /* The whole layer: route -> capacity -> dispatch -> routed (and shared)
  * expert FFNs -> combine, with the losses beside, all on `stream`
  * ["Lab 18" "What to implement" 5: MoE.forward(x) -> (y, aux)].
+ * Expert choice: route -> expert choice -> routed (and shared) FFNs ->
+ * expert-choice combine; idx and gates then receive the router's top-k
+ * when given (they may be NULL), slot and dropped are not used, sel is
+ * required.
  * Shared experts: pass them concatenated along their hidden dimension
  * (GELU is elementwise, so the sum of the shared experts equals one MLP
  * whose hidden layer is the concatenation of theirs). */

@@ -26,6 +26,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
 MOE_RANK_MAJOR, MOE_TOKEN_MAJOR = 0, 1
+MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
 
 EXPORTS = ('moe_validate', 'moe_workspace_bytes', 'moe_route', 'moe_dispatch', 'moe_expert_ffn',
            'moe_combine', 'moe_aux_losses', 'moe_forward', 'moe_last_error')
@@ -38,7 +39,7 @@ class moe_config(ctypes.Structure):
                 ('capacity_override', ctypes.c_int64), ('renormalize', ctypes.c_int32),
                 ('score', ctypes.c_int32), ('act', ctypes.c_int32), ('dtype', ctypes.c_int32),
                 ('priority', ctypes.c_int32), ('dropped_output', ctypes.c_int32),
-                ('dropless', ctypes.c_int32)]
+                ('dropless', ctypes.c_int32), ('routing', ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -51,7 +52,7 @@ class moe_weights(ctypes.Structure):
 
 class moe_outputs(ctypes.Structure):
     _fields_ = [(n, _P) for n in ('y', 'idx', 'gates', 'slot', 'dropped', 'counts', 'losses',
-                                  'stats', 'logits', 'probs', 'lse')]
+                                  'stats', 'logits', 'probs', 'lse', 'sel')]
 
 
 def _load():
@@ -72,6 +73,8 @@ def _load():
         'moe_sequence_aux_loss': (st, [cfgp, ctypes.c_int64, _P, _P, _P, _P, _P]),
         'moe_update_select_bias': (st, [cfgp, _P, _P, ctypes.c_float, _P]),
         'moe_combine': (st, [cfgp] + [_P] * 9),
+        'moe_expert_choice': (st, [cfgp] + [_P] * 6),
+        'moe_combine_expert_choice': (st, [cfgp] + [_P] * 7),
         'moe_aux_losses': (st, [cfgp, _P, _P, _P, _P, _P]),
         'moe_forward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs),
                              _P, _P]),
@@ -92,6 +95,7 @@ _ENUMS = {
     'dtype': {'f32': MOE_F32, 'float32': MOE_F32, 'bf16': MOE_BF16, 'bfloat16': MOE_BF16},
     'priority': {'rank': MOE_RANK_MAJOR, 'token': MOE_TOKEN_MAJOR},
     'dropped_output': {'residual': 0, 'zero': 1},
+    'routing': {'token': MOE_TOKEN_CHOICE, 'expert': MOE_EXPERT_CHOICE},
 }
 
 
@@ -101,12 +105,14 @@ def _enum(kind, v):
 
 def make_config(T, d, E, k, d_ff, *, n_shared=0, d_ff_shared=0, capacity_factor=1.25,
                 capacity_override=0, renormalize=-1, score='softmax', act='gelu', dtype='bf16',
-                priority='rank', dropped_output='residual', dropless=False) -> moe_config:
+                priority='rank', dropped_output='residual', dropless=False,
+                routing='token') -> moe_config:
     return moe_config(T=T, d=d, E=E, k=k, d_ff=d_ff, n_shared=n_shared, d_ff_shared=d_ff_shared,
                       capacity_factor=float(capacity_factor), capacity_override=capacity_override,
                       renormalize=renormalize, score=_enum('score', score), act=_enum('act', act),
                       dtype=_enum('dtype', dtype), priority=_enum('priority', priority),
-                      dropped_output=_enum('dropped_output', dropped_output), dropless=int(bool(dropless)))
+                      dropped_output=_enum('dropped_output', dropped_output), dropless=int(bool(dropless)),
+                      routing=_enum('routing', routing))
 
 
 def config_from_workload(w, **over) -> moe_config:
@@ -249,6 +255,21 @@ def moe_combine(cfg, x, ye, shared_out, idx, gates, slot, dropped, y, stream=Non
                             _stream(stream)))
 
 
+def moe_expert_choice(cfg, probs, row_token, sel, counts, ws, stream=None):
+    """Expert-choice picks: row_token [E,C], sel [T,E] (row or -1), counts [E]."""
+    _check(_lib.moe_expert_choice(ctypes.byref(cfg), _ptr(probs, 'probs', torch.float32),
+                                  _ptr(row_token, 'row_token', torch.int32), _ptr(sel, 'sel', torch.int32),
+                                  _ptr(counts, 'counts', torch.int32), _ptr(ws, 'ws'), _stream(stream)))
+
+
+def moe_combine_expert_choice(cfg, x, ye, shared_out, probs, sel, y, stream=None):
+    dt = torch_dtype(cfg)
+    _check(_lib.moe_combine_expert_choice(ctypes.byref(cfg), _ptr(x, 'x', dt), _ptr(ye, 'ye', dt),
+                                          _ptr(shared_out, 'shared_out', dt),
+                                          _ptr(probs, 'probs', torch.float32), _ptr(sel, 'sel', torch.int32),
+                                          _ptr(y, 'y', dt), _stream(stream)))
+
+
 def moe_aux_losses(cfg, logits, idx, losses, ws, stream=None):
     _check(_lib.moe_aux_losses(ctypes.byref(cfg), _ptr(logits, 'logits', torch.float32),
                                _ptr(idx, 'idx', torch.int32), _ptr(losses, 'losses', torch.float32),
@@ -258,7 +279,7 @@ def moe_aux_losses(cfg, logits, idx, losses, ws, stream=None):
 _WKEYS = ('w_router', 'logit_bias', 'select_bias', 'w_in', 'w_gate', 'b_in', 'w_out', 'b_out',
           'ws_in', 'bs_in', 'ws_out', 'bs_out')
 _OKEYS = ('y', 'idx', 'gates', 'slot', 'dropped', 'counts', 'losses', 'stats', 'logits', 'probs',
-          'lse')
+          'lse', 'sel')
 
 
 def moe_forward(cfg, weights: dict, x, outputs: dict, ws, stream=None):
@@ -272,7 +293,7 @@ def moe_forward(cfg, weights: dict, x, outputs: dict, ws, stream=None):
     od = {}
     want_o = dict(y=dt, idx=torch.int32, gates=torch.float32, slot=torch.int32, dropped=torch.uint8,
                   counts=torch.int32, losses=torch.float32, stats=torch.int32, logits=torch.float32,
-                  probs=torch.float32, lse=torch.float32)
+                  probs=torch.float32, lse=torch.float32, sel=torch.int32)
     for kk in _OKEYS:
         od[kk] = _ptr(outputs.get(kk), kk, want_o[kk])
     w = moe_weights(**wd)
@@ -298,4 +319,6 @@ def alloc_outputs(cfg, device='cuda', logits=False, probs=False, lse=False) -> d
         o['probs'] = torch.empty(T, E, dtype=torch.float32, device=device)
     if lse:
         o['lse'] = torch.empty(T, dtype=torch.float32, device=device)
+    if cfg.routing == MOE_EXPERT_CHOICE:
+        o['sel'] = torch.empty(T, E, dtype=torch.int32, device=device)
     return o

@@ -78,6 +78,10 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
   if (c.T * static_cast<int64_t>(c.k) >= (int64_t{1} << 31))
     return fail(MOE_EINVAL, "T*k must be < 2^31");
   if (c.dropless != 0 && c.dropless != 1) return fail(MOE_EINVAL, "dropless must be 0 or 1");
+  if (c.routing != MOE_TOKEN_CHOICE && c.routing != MOE_EXPERT_CHOICE)
+    return fail(MOE_EINVAL, "unknown routing %d", c.routing);
+  if (c.routing == MOE_EXPERT_CHOICE && c.dropless)
+    return fail(MOE_EINVAL, "expert-choice routing has no dropless mode (no choice is ever dropped)");
   if (c.capacity_override < 0) return fail(MOE_EINVAL, "capacity_override must be >= 0");
   if (!c.dropless && c.capacity_override == 0 && !(c.capacity_factor >= 1.0))
     return fail(MOE_EINVAL,
@@ -116,6 +120,9 @@ struct Workspace {
   int32_t* idx_tmp;
   float* gates_tmp;
   int32_t* row_token;
+  uint32_t* ec_keys;
+  float* ec_probs;
+  int32_t* ec_fallback;
   void* h;
   void* ye;
   void* hs;
@@ -153,6 +160,11 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   // expert rows: E*C (capacity), or T*k packed (dropless)
   const int64_t xrows = c.dropless ? c.T * c.k : c.E * C;
   w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * xrows));
+  if (c.routing == MOE_EXPERT_CHOICE) {
+    w.ec_keys = static_cast<uint32_t*>(take(sizeof(uint32_t) * c.T * c.E));
+    w.ec_probs = static_cast<float*>(take(sizeof(float) * c.T * c.E));
+    w.ec_fallback = static_cast<int32_t*>(take(sizeof(int32_t)));
+  }
 
   w.h = take(ds * xrows * c.d_ff);
   w.ye = take(ds * xrows * c.d);
@@ -263,6 +275,57 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   g2.K = F;
   g2.act = 0;
   return hip_status(launch_gemm(g2, c.dtype, s), "expert GEMM 2");
+}
+
+// Expert choice after the router: each expert's picks, the routed FFNs on
+// the picked rows (gathered straight from x), the shared experts, the
+// probability-weighted combine and the losses.
+moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weights& wt, const void* x,
+                                 const float* probs, const moe_outputs& out, const Workspace& w, hipStream_t s) {
+  EcArgs e{};
+  e.probs = probs;
+  e.keys = w.ec_keys;
+  e.row_token = w.row_token;
+  e.sel = out.sel;
+  e.counts = out.counts;
+  e.p_partial = w.p_partial;
+  e.lse2_partial = w.lse2_partial;
+  e.psum = w.psum;
+  e.fallback_count = w.ec_fallback;
+  e.T = c.T;
+  e.C = C;
+  e.E = c.E;
+  e.n_rtiles = router_tiles(c);
+  MOE_TRY(hip_status(launch_expert_choice(e, s), "expert choice"));   // T = 0: zero counts and sums
+  if (c.T > 0) {
+    MOE_TRY(ffn(c, c.act, c.E, C, out.counts, x, w.row_token, c.T, wt.w_in, wt.w_gate, wt.b_in, wt.w_out,
+                wt.b_out, c.d_ff, w.h, w.ye, s));
+    if (c.n_shared > 0)
+      MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt.ws_in, nullptr, wt.bs_in, wt.ws_out,
+                  wt.bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s));
+    CombineArgs cb{};
+    cb.x = x;
+    cb.ye = w.ye;
+    cb.shared_out = c.n_shared > 0 ? w.s : nullptr;
+    cb.sel = out.sel;
+    cb.probs = probs;
+    cb.fallback_count = w.ec_fallback;
+    cb.y = out.y;
+    cb.T = c.T;
+    cb.C = C;
+    cb.d = c.d;
+    cb.k = c.k;
+    cb.E = c.E;
+    cb.zero_fallback = c.dropped_output;
+    MOE_TRY(hip_status(launch_combine(cb, c.dtype, s), "expert-choice combine"));
+  }
+  LossArgs l = loss_args(c, C, w, out.counts);
+  l.fallback_partial = nullptr;
+  l.ec = 1;
+  l.fallback_count = w.ec_fallback;
+  l.losses = out.losses;
+  l.stats = out.stats;
+  return hip_status(launch_losses(l, s), "loss finaliser");
 }
 
 }  // namespace
@@ -441,6 +504,61 @@ moe_status moe_combine(const moe_config* cfg, const void* x, const void* ye, con
   return hip_status(launch_combine(a, c.dtype, static_cast<hipStream_t>(stream)), "combine");
 }
 
+moe_status moe_expert_choice(const moe_config* cfg, const float* probs, int32_t* row_token, int32_t* sel,
+                             int32_t* counts, void* ws, void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  if (c.routing != MOE_EXPERT_CHOICE) return fail(MOE_EINVAL, "moe_expert_choice needs routing = MOE_EXPERT_CHOICE");
+  const bool needT = c.T > 0;
+  MOE_TRY(check_ptr(probs, "probs", 4, needT));
+  MOE_TRY(check_ptr(row_token, "row_token", 4, needT));
+  MOE_TRY(check_ptr(sel, "sel", 4, needT));
+  MOE_TRY(check_ptr(counts, "counts", 4));
+  MOE_TRY(check_ptr(ws, "ws", 256));
+  Workspace w = carve(c, C, ws);
+  EcArgs e{};
+  e.probs = probs;
+  e.keys = w.ec_keys;
+  e.row_token = row_token;
+  e.sel = sel;
+  e.counts = counts;
+  e.T = c.T;
+  e.C = C;
+  e.E = c.E;
+  return hip_status(launch_expert_choice(e, static_cast<hipStream_t>(stream)), "expert choice");
+}
+
+moe_status moe_combine_expert_choice(const moe_config* cfg, const void* x, const void* ye, const void* shared_out,
+                                     const float* probs, const int32_t* sel, void* y, void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  if (c.routing != MOE_EXPERT_CHOICE)
+    return fail(MOE_EINVAL, "moe_combine_expert_choice needs routing = MOE_EXPERT_CHOICE");
+  const bool needT = c.T > 0;
+  MOE_TRY(check_ptr(x, "x", 16, needT));
+  MOE_TRY(check_ptr(ye, "ye", 16, needT));
+  MOE_TRY(check_ptr(shared_out, "shared_out", 16, false));
+  MOE_TRY(check_ptr(probs, "probs", 4, needT));
+  MOE_TRY(check_ptr(sel, "sel", 4, needT));
+  MOE_TRY(check_ptr(y, "y", 16, needT));
+  CombineArgs a{};
+  a.x = x;
+  a.ye = ye;
+  a.shared_out = shared_out;
+  a.sel = sel;
+  a.probs = probs;
+  a.y = y;
+  a.T = c.T;
+  a.C = C;
+  a.d = c.d;
+  a.k = c.k;
+  a.E = c.E;
+  a.zero_fallback = c.dropped_output;
+  return hip_status(launch_combine(a, c.dtype, static_cast<hipStream_t>(stream)), "expert-choice combine");
+}
+
 moe_status moe_aux_losses(const moe_config* cfg, const float* logits, const int32_t* idx, float* losses, void* ws,
                           void* stream) {
   int64_t C = 0;
@@ -541,11 +659,13 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
     MOE_TRY(check_ptr(wt->bs_in, "bs_in", dsize(c), false));
     MOE_TRY(check_ptr(wt->bs_out, "bs_out", dsize(c), false));
   }
+  const bool ec = c.routing == MOE_EXPERT_CHOICE;
   MOE_TRY(check_ptr(out->y, "y", 16, needT));
-  MOE_TRY(check_ptr(out->idx, "idx", 4, needT));
-  MOE_TRY(check_ptr(out->gates, "gates", 4, needT));
-  MOE_TRY(check_ptr(out->slot, "slot", 4, needT));
-  MOE_TRY(check_ptr(out->dropped, "dropped", 1, needT));
+  MOE_TRY(check_ptr(out->idx, "idx", 4, needT && !ec));
+  MOE_TRY(check_ptr(out->gates, "gates", 4, needT && !ec));
+  MOE_TRY(check_ptr(out->slot, "slot", 4, needT && !ec));
+  MOE_TRY(check_ptr(out->dropped, "dropped", 1, needT && !ec));
+  MOE_TRY(check_ptr(out->sel, "sel", 4, needT && ec));
   MOE_TRY(check_ptr(out->counts, "counts", 4));
   MOE_TRY(check_ptr(out->losses, "losses", 4));
   MOE_TRY(check_ptr(out->stats, "stats", 4, false));
@@ -565,7 +685,14 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   r.idx = out->idx;
   r.gates = out->gates;
   r.lse = out->lse;
+  if (ec) {
+    // the top-k of the router is still formed (into idx/gates when given)
+    if (!r.probs) r.probs = w.ec_probs;
+    if (!r.idx) r.idx = w.idx_tmp;
+    if (!r.gates) r.gates = w.gates_tmp;
+  }
   MOE_TRY(hip_status(launch_route(r, c.dtype, s), "router"));
+  if (ec) return forward_expert_choice(c, C, *wt, x, r.probs, *out, w, s);
 
   CapArgs a = cap_args(c, C, w);
   a.idx = out->idx;

@@ -59,10 +59,12 @@ template <> struct Vec<float> {
 // leaves room for more resident wavefronts; the expert rows are read once,
 // with non-temporal loads (about 5-10% faster; non-temporal stores of y are
 // not).
+// Expert choice (EC): lane l reads experts l, l + 64, ... (E <= 256, so up to
+// four ballots); the picks are summed in expert order, ballot by ballot.
 constexpr int kChunkRounds = 2;
 constexpr int kRowsAtOnce = 2;
 
-template <typename T>
+template <typename T, bool EC>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x & (kWave - 1);
@@ -77,23 +79,40 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 
   // choice j on lane j: kept only if not dropped and its (expert, slot) is in
   // range; its row of ye is e*C + slot, or the slot itself for packed rows
-  int64_t myrow = 0;
-  float mygate = 0.0f;
-  bool keep = false;
-  if (lane < a.k) {
-    const int64_t tk = t * a.k + lane;
-    const int e = a.idx[tk];
-    const int sl = a.slot[tk];
-    const int64_t bound = a.packed ? a.T * a.k : a.C;
-    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < bound;
-    myrow = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
-    mygate = a.gates[tk];
+  constexpr int kBal = EC ? 4 : 1;
+  int64_t myrow[kBal];
+  float mygate[kBal];
+  uint64_t kept[kBal];
+  int n = 0;
+#pragma unroll
+  for (int b = 0; b < kBal; ++b) {
+    myrow[b] = 0;
+    mygate[b] = 0.0f;
+    bool keep = false;
+    if constexpr (EC) {
+      const int e = b * kWave + lane;
+      if (e < a.E) {
+        const int sl = a.sel[t * a.E + e];
+        keep = sl >= 0 && sl < a.C;
+        myrow[b] = static_cast<int64_t>(e) * a.C + sl;
+        mygate[b] = a.probs[t * a.E + e];
+      }
+    } else if (lane < a.k) {
+      const int64_t tk = t * a.k + lane;
+      const int e = a.idx[tk];
+      const int sl = a.slot[tk];
+      const int64_t bound = a.packed ? a.T * a.k : a.C;
+      keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < bound;
+      myrow[b] = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
+      mygate[b] = a.gates[tk];
+    }
+    kept[b] = __ballot(keep);
+    n += __popcll(kept[b]);
   }
-  uint64_t kept = __ballot(keep);
-  const int n = __popcll(kept);
   char* yt = y + t * rowbytes;
 
   if (n == 0 && sh == nullptr) {
+    if (EC && a.fallback_count && lane == 0) atomicAdd(a.fallback_count, 1);   // integer: order-free
     // fallback: the token's own row, or zeros
     for (int c = lane; c < nvec; c += kWave) {
       float v[V];
@@ -115,46 +134,49 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int q = 0; q < V; ++q) acc[u][q] = 0.0f;
     // kept choices in j order, kRowsAtOnce rows per batch
-    uint64_t rest = kept;
-    for (int b = 0; b < n; b += kRowsAtOnce) {
-      const char* src[kRowsAtOnce];
-      float g[kRowsAtOnce];
-      int nb = 0;
 #pragma unroll
-      for (int r = 0; r < kRowsAtOnce; ++r) {
-        src[r] = ye;
-        g[r] = 0.0f;
-        if (rest) {
-          const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
-          rest &= rest - 1;
-          src[r] = ye + __shfl(myrow, j, kWave) * rowbytes;
-          g[r] = __shfl(mygate, j, kWave);
-          nb = r + 1;
-        }
-      }
-      // raw 16-byte chunks in flight (widened only when summed)
-      uint4 raw[kRowsAtOnce][kChunkRounds];
+    for (int bal = 0; bal < kBal; ++bal) {
+      uint64_t rest = kept[bal];
+      while (rest) {
+        const char* src[kRowsAtOnce];
+        float g[kRowsAtOnce];
+        int nb = 0;
 #pragma unroll
-      for (int r = 0; r < kRowsAtOnce; ++r)
-#pragma unroll
-        for (int u = 0; u < kChunkRounds; ++u) {
-          const int c = c0 + lane + u * kWave;
-          if (r < nb && c < nvec) {
-            const uint4* pp = reinterpret_cast<const uint4*>(src[r] + static_cast<int64_t>(c) * 16);
-            const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pp));
-            raw[r][u] = make_uint4(q[0], q[1], q[2], q[3]);
+        for (int r = 0; r < kRowsAtOnce; ++r) {
+          src[r] = ye;
+          g[r] = 0.0f;
+          if (rest) {
+            const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+            rest &= rest - 1;
+            src[r] = ye + __shfl(myrow[bal], j, kWave) * rowbytes;
+            g[r] = __shfl(mygate[bal], j, kWave);
+            nb = r + 1;
           }
         }
+        // raw 16-byte chunks in flight (widened only when summed)
+        uint4 raw[kRowsAtOnce][kChunkRounds];
 #pragma unroll
-      for (int r = 0; r < kRowsAtOnce; ++r)
-        if (r < nb)
+        for (int r = 0; r < kRowsAtOnce; ++r)
 #pragma unroll
           for (int u = 0; u < kChunkRounds; ++u) {
-            float v[V];
-            Vec<T>::load(&raw[r][u], v);
-#pragma unroll
-            for (int q = 0; q < V; ++q) acc[u][q] += g[r] * v[q];
+            const int c = c0 + lane + u * kWave;
+            if (r < nb && c < nvec) {
+              const uint4* pp = reinterpret_cast<const uint4*>(src[r] + static_cast<int64_t>(c) * 16);
+              const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pp));
+              raw[r][u] = make_uint4(q[0], q[1], q[2], q[3]);
+            }
           }
+#pragma unroll
+        for (int r = 0; r < kRowsAtOnce; ++r)
+          if (r < nb)
+#pragma unroll
+            for (int u = 0; u < kChunkRounds; ++u) {
+              float v[V];
+              Vec<T>::load(&raw[r][u], v);
+#pragma unroll
+              for (int q = 0; q < V; ++q) acc[u][q] += g[r] * v[q];
+            }
+      }
     }
 #pragma unroll
     for (int u = 0; u < kChunkRounds; ++u) {
@@ -180,15 +202,20 @@ __global__ __launch_bounds__(kThreads) void losses_kernel(LossArgs a) {
   __shared__ long long fred[kThreads];
   const int tid = threadIdx.x;
   const double T = static_cast<double>(a.T);
+  // f_i divides by the T*k choices (token choice) or by the sum of the picks
+  // (expert choice, every expert's count being min(C, T))
+  const double fden = a.ec ? static_cast<double>(a.E) * static_cast<double>(min<int64_t>(a.C, a.T))
+                           : T * a.k;
   double fp = 0.0;
   long long kept = 0;
   for (int e = tid; e < a.E; e += kThreads) {
-    if (a.T > 0) fp += (static_cast<double>(a.counts[e]) / (T * a.k)) * (a.psum[e] / T);
+    if (a.T > 0) fp += (static_cast<double>(a.counts[e]) / fden) * (a.psum[e] / T);
     kept += min<long long>(a.counts[e], a.C);
   }
   long long fb = 0;
   if (a.fallback_partial)
     for (int r = tid; r < a.n_tiles; r += kThreads) fb += a.fallback_partial[r];
+  if (a.ec && a.fallback_count && tid == 0) fb = a.fallback_count[0];
   red[tid] = fp;
   ired[tid] = kept;
   fred[tid] = fb;
@@ -206,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void losses_kernel(LossArgs a) {
     a.losses[0] = static_cast<float>(static_cast<double>(a.E) * red[0]);
     a.losses[1] = a.T > 0 ? static_cast<float>(a.psum[a.E] / T) : 0.0f;
     if (a.stats) {
-      const long long total = a.T * a.k;
+      const long long total = a.ec ? n_kept : a.T * a.k;
       a.stats[0] = static_cast<int32_t>(n_kept);
       a.stats[1] = static_cast<int32_t>(total - n_kept);
       a.stats[2] = a.has_shared ? 0 : static_cast<int32_t>(fred[0]);
@@ -221,10 +248,16 @@ hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   constexpr int kTokensPerBlock = kThreads / kWave;     // one wavefront per token
   const unsigned grid = static_cast<unsigned>((a.T + kTokensPerBlock - 1) / kTokensPerBlock);
-  if (dtype == MOE_BF16)
-    combine_kernel<bf16_t><<<grid, kThreads, 0, s>>>(a);
-  else
-    combine_kernel<float><<<grid, kThreads, 0, s>>>(a);
+  if (a.sel) {
+    if (dtype == MOE_BF16)
+      combine_kernel<bf16_t, true><<<grid, kThreads, 0, s>>>(a);
+    else
+      combine_kernel<float, true><<<grid, kThreads, 0, s>>>(a);
+  } else if (dtype == MOE_BF16) {
+    combine_kernel<bf16_t, false><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    combine_kernel<float, false><<<grid, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -160,6 +160,12 @@ struct CombineArgs {
   int d, k, E;
   int zero_fallback;
   int packed;                 // dropless: ye is [T*k, d] and slot the row
+  // expert choice (sel != null): the picks of token t are the experts e with
+  // sel[t*E + e] >= 0, in e order, row e*C + sel, gate probs[t*E + e];
+  // idx, gates, slot and dropped are then not read
+  const int32_t* sel;         // [T,E] | null
+  const float* probs;         // [T,E] (expert choice)
+  int32_t* fallback_count;    // [1] tokens that took the fallback, added to | null
 };
 
 struct LossArgs {
@@ -172,6 +178,23 @@ struct LossArgs {
   int E, k, n_tiles;
   int has_shared;
   int packed;                 // dropless: no padding in the statistics
+  int ec;                     // expert choice: f_i = counts_i / sum counts, no drops,
+                              // fallback tokens from fallback_count
+  const int32_t* fallback_count;  // [1] (expert choice)
+};
+
+struct EcArgs {
+  const float* probs;         // [T,E] router probabilities
+  uint32_t* keys;             // [E,T] order codes (workspace)
+  int32_t* row_token;         // [E,C] picked tokens, ascending, first min(C,T) rows
+  int32_t* sel;               // [T,E] slot of t in e, or -1
+  int32_t* counts;            // [E] = min(C,T)
+  const double* p_partial;    // [n_rtiles, E] router partial sums | null
+  const double* lse2_partial; // [n_rtiles]
+  double* psum;               // [E + 1]
+  int32_t* fallback_count;    // [1] zeroed here (the combine adds to it) | null
+  int64_t T, C;
+  int E, n_rtiles;
 };
 
 struct SeqLossArgs {
@@ -189,6 +212,7 @@ hipError_t launch_capacity(const CapArgs& a, int dtype, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_losses(const LossArgs& a, hipStream_t s);
+hipError_t launch_expert_choice(const EcArgs& a, hipStream_t s);
 hipError_t launch_seq_loss(const SeqLossArgs& a, hipStream_t s);
 hipError_t launch_bias_update(const int32_t* counts, float* select_bias, int E, int64_t Tk, float gamma,
                               hipStream_t s);

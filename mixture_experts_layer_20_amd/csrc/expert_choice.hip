@@ -1,0 +1,238 @@
+// Expert-choice routing: every expert takes the C tokens with the largest
+// router probability for it.
+//
+// Sources: "Lab 18 -- Mixture of experts", exercise 1 and "Common
+// extensions" (each expert picks its top tokens instead of each token its
+// top experts: balanced by construction, nothing dropped, a token may be
+// picked by several experts or by none); "Mixture of experts" lecture,
+// routing families (the top of each expert's row of the token x expert
+// score matrix).
+//
+// Ties go to the lower token; an expert's picks sit in its rows in token
+// order.  The decision is taken on the float32 probabilities as stored.
+//
+// Kernels:
+//   ec_keys_kernel    [T,E] float32 probabilities -> [E,T] uint32 order codes
+//                     (an LDS-tiled transpose, so that each expert's column
+//                     reads contiguously)
+//   ec_select_kernel  one 1024-thread workgroup per expert: the n-th largest
+//                     code K (n = min(C, T)) by bisection over the 32-bit code
+//                     space, each step one count over the expert's codes held
+//                     in registers; then, in token order, every code above K
+//                     and the first n - #(code > K) codes equal to K are taken,
+//                     and a block-wide exclusive scan numbers the picks.
+// The count-based bisection makes no use of atomics and needs no sort: 33
+// workgroup-wide sums of per-thread counts.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+// ------------------------------------------------------------------ transpose
+constexpr int kTr = 64;          // 64 tokens x 64 experts per tile
+
+__global__ __launch_bounds__(256) void ec_keys_kernel(const float* __restrict__ probs, uint32_t* __restrict__ keys,
+                                                      int64_t T, int E) {
+  __shared__ uint32_t tile[kTr][kTr + 1];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTr;
+  const int e0 = blockIdx.y * kTr;
+  const int lane = threadIdx.x & (kTr - 1);
+  const int row = threadIdx.x / kTr;                 // 0..3
+#pragma unroll 4
+  for (int r = row; r < kTr; r += 4) {               // read along experts
+    const int64_t t = t0 + r;
+    const int e = e0 + lane;
+    if (t < T && e < E) tile[r][lane] = order_code(probs[t * E + e]);
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int r = row; r < kTr; r += 4) {               // write along tokens
+    const int e = e0 + r;
+    const int64_t t = t0 + lane;
+    if (t < T && e < E) keys[static_cast<int64_t>(e) * T + t] = tile[lane][r];
+  }
+}
+
+// ------------------------------------------------------------------ selection
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum over the workgroup; every thread gets the total.  `buf` holds two banks
+// of per-wave sums used alternately, so one barrier per call suffices: a bank
+// is rewritten only two calls later, after every thread has passed the
+// barrier of the call in between (and so finished reading it).
+__device__ __forceinline__ int block_sum(int v, int (*buf)[kSelWaves], int& bank) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  v = wave_sum_i(v);
+  if (lane == 0) buf[bank][wave] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) s += buf[bank][w];
+  bank ^= 1;
+  return s;
+}
+
+// Exclusive prefix over the workgroup in thread order.
+__device__ __forceinline__ int block_excl_scan(int v, int* wtot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == kWave - 1) wtot[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  __syncthreads();                                   // wtot is reused by the next scan
+  return base + inc - v;
+}
+
+// R > 0: thread i holds the codes of tokens [i R, i R + R) in registers
+// (T <= 1024 R).  R == 0: the same token ranges, of P = ceil(T / 1024) codes,
+// re-read from memory in every step (any T).
+template <int R>
+__global__ __launch_bounds__(kSelThreads) void ec_select_kernel(EcArgs a) {
+  __shared__ int sums[2][kSelWaves];
+  __shared__ int wtot[kSelWaves];
+  __shared__ double dred[kSelThreads];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t T = a.T;
+  const int64_t P = R > 0 ? R : (T + kSelThreads - 1) / kSelThreads;
+  const int64_t first = static_cast<int64_t>(tid) * P;
+  const int nv = static_cast<int>(max<int64_t>(0, min<int64_t>(P, T - first)));   // codes of this thread
+  const uint32_t* __restrict__ col = a.keys + static_cast<int64_t>(e) * T + first;
+  const int64_t n = min<int64_t>(a.C, T);
+
+  uint32_t reg[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) reg[j] = j < nv ? col[j] : 0u;
+  }
+  // f(j, code of token first + j) for this thread's tokens in order (the
+  // register copy is indexed only by unrolled constants)
+  auto each = [&](auto f) {
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (j < nv) f(j, reg[j]);
+    } else {
+      for (int j = 0; j < nv; ++j) f(j, col[j]);
+    }
+  };
+  auto count_ge = [&](uint64_t v) -> int {
+    int c = 0;
+    each([&](int, uint32_t k) { c += static_cast<uint64_t>(k) >= v ? 1 : 0; });
+    return c;
+  };
+
+  // K = the largest v with #(code >= v) >= n: invariant #(>= lo) >= n > #(>= hi)
+  int bank = 0;
+  uint64_t lo = 0, hi = uint64_t{1} << 32;
+  for (int it = 0; it < 32; ++it) {
+    const uint64_t mid = (lo + hi) >> 1;
+    if (block_sum(count_ge(mid), sums, bank) >= n) lo = mid;
+    else hi = mid;
+  }
+  const uint32_t K = static_cast<uint32_t>(lo);
+  const int64_t above = block_sum(count_ge(lo + 1), sums, bank);
+  const int64_t take_eq = n - above;                 // codes equal to K to take, lowest tokens first
+
+  // in token order: the equal codes before this thread's range, then the picks
+  int my_eq = 0;
+  each([&](int, uint32_t k) { my_eq += k == K ? 1 : 0; });
+  const int64_t eq_before = block_excl_scan(my_eq, wtot);
+  int my_take = 0;
+  {
+    int64_t eq = eq_before;
+    each([&](int, uint32_t k) {
+      my_take += (k > K || (k == K && eq < take_eq)) ? 1 : 0;
+      eq += k == K ? 1 : 0;
+    });
+  }
+  {
+    int64_t slot = block_excl_scan(my_take, wtot);
+    int64_t eq = eq_before;
+    int32_t* __restrict__ rt = a.row_token + static_cast<int64_t>(e) * a.C;
+    each([&](int j, uint32_t k) {
+      const bool tk = k > K || (k == K && eq < take_eq);
+      eq += k == K ? 1 : 0;
+      const int64_t t = first + j;
+      if (tk) rt[slot] = static_cast<int32_t>(t);
+      a.sel[t * a.E + e] = tk ? static_cast<int32_t>(slot) : -1;
+      slot += tk ? 1 : 0;
+    });
+  }
+  if (tid == 0) {
+    a.counts[e] = static_cast<int32_t>(n);
+    if (e == 0 && a.fallback_count) a.fallback_count[0] = 0;
+  }
+
+  // per-expert probability sums (and, in workgroup 0, the LSE^2 sum) from the
+  // router's per-workgroup partials, in a fixed order
+  if (a.p_partial) {
+    auto reduce = [&](auto load) {
+      double v = 0.0;
+      for (int r = tid; r < a.n_rtiles; r += kSelThreads) v += load(r);
+      dred[tid] = v;
+      __syncthreads();
+      for (int o = kSelThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) dred[tid] += dred[tid + o];
+        __syncthreads();
+      }
+      const double out = dred[0];
+      __syncthreads();
+      return out;
+    };
+    const double Ps = reduce([&](int r) { return a.p_partial[static_cast<int64_t>(r) * a.E + e]; });
+    if (tid == 0) a.psum[e] = Ps;
+    if (e == 0) {
+      const double z2 = reduce([&](int r) { return a.lse2_partial[r]; });
+      if (tid == 0) a.psum[a.E] = z2;
+    }
+  }
+}
+
+// T = 0: no picks; the counts, the sums and the fallback count are zero.
+__global__ __launch_bounds__(256) void ec_empty_kernel(EcArgs a) {
+  for (int e = threadIdx.x; e <= a.E; e += blockDim.x) {
+    if (e < a.E) a.counts[e] = 0;
+    if (a.p_partial) a.psum[e] = 0.0;
+  }
+  if (threadIdx.x == 0 && a.fallback_count) a.fallback_count[0] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_expert_choice(const EcArgs& a, hipStream_t s) {
+  if (a.E == 0) return hipSuccess;
+  if (a.T == 0) {
+    ec_empty_kernel<<<1, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  const dim3 tg(static_cast<unsigned>((a.T + kTr - 1) / kTr), static_cast<unsigned>((a.E + kTr - 1) / kTr));
+  ec_keys_kernel<<<tg, 256, 0, s>>>(a.probs, a.keys, a.T, a.E);
+  const unsigned grid = static_cast<unsigned>(a.E);
+  if (a.T <= int64_t{kSelThreads} * 8)
+    ec_select_kernel<8><<<grid, kSelThreads, 0, s>>>(a);
+  else if (a.T <= int64_t{kSelThreads} * 16)
+    ec_select_kernel<16><<<grid, kSelThreads, 0, s>>>(a);
+  else if (a.T <= int64_t{kSelThreads} * 64)
+    ec_select_kernel<64><<<grid, kSelThreads, 0, s>>>(a);
+  else
+    ec_select_kernel<0><<<grid, kSelThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ('moe_route', 'moe_dispatch', 'moe_expert_ffn', 'moe_combine', 'moe_forward',
               'moe_aux_losses', 'moe_validate', 'moe_workspace_bytes', 'moe_last_error',
-              'moe_expert_ffn_packed'):
+              'moe_expert_ffn_packed', 'moe_expert_choice', 'moe_combine_expert_choice'):
         assert n in names
 
 
@@ -63,10 +63,10 @@ def test_struct_layout_matches_header(tmp_path, moe):
 #include <stddef.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_config), offsetof(moe_config, capacity_factor),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_config), offsetof(moe_config, capacity_factor),
          offsetof(moe_config, capacity_override), offsetof(moe_config, dropped_output),
-         offsetof(moe_config, dropless), sizeof(moe_weights), sizeof(moe_outputs),
-         offsetof(moe_outputs, lse));
+         offsetof(moe_config, dropless), offsetof(moe_config, routing), sizeof(moe_weights),
+         sizeof(moe_outputs), offsetof(moe_outputs, lse), offsetof(moe_outputs, sel));
   return 0;
 }
 ''')
@@ -77,8 +77,8 @@ int main(void) {
                                        check=True).stdout.split()))
     want = [ctypes.sizeof(moe.moe_config), moe.moe_config.capacity_factor.offset,
             moe.moe_config.capacity_override.offset, moe.moe_config.dropped_output.offset,
-            moe.moe_config.dropless.offset, ctypes.sizeof(moe.moe_weights), ctypes.sizeof(moe.moe_outputs),
-            moe.moe_outputs.lse.offset]
+            moe.moe_config.dropless.offset, moe.moe_config.routing.offset, ctypes.sizeof(moe.moe_weights),
+            ctypes.sizeof(moe.moe_outputs), moe.moe_outputs.lse.offset, moe.moe_outputs.sel.offset]
     assert got == want
 
 
@@ -209,3 +209,33 @@ def test_balancing_entry_points_reject_bad_arguments(moe):
     assert b'gamma' in lib.moe_last_error()
     assert lib.moe_update_select_bias(ctypes.byref(c), None, 16, ctypes.c_float(0.001), None) == moe.MOE_EINVAL
     assert b'counts' in lib.moe_last_error()
+
+
+def test_expert_choice_configuration(moe):
+    # C from the same formula; the mode has no dropless variant; unknown modes fail
+    assert moe.moe_validate(cfg(moe, routing='expert')) == 40
+    assert moe.moe_validate(cfg(moe, routing='expert', capacity_override=100)) == 100
+    with pytest.raises(ValueError, match='dropless'):
+        moe.moe_validate(cfg(moe, routing='expert', dropless=True))
+    c = cfg(moe)
+    c.routing = 2
+    with pytest.raises(ValueError, match='routing'):
+        moe.moe_validate(c)
+    # the transposed keys and the probabilities take workspace
+    assert moe.moe_workspace_bytes(cfg(moe, routing='expert')) > moe.moe_workspace_bytes(cfg(moe))
+
+
+def test_expert_choice_entry_points_reject_bad_arguments(moe):
+    lib = moe._lib
+    tc, ec = cfg(moe), cfg(moe, routing='expert')
+    assert lib.moe_expert_choice(ctypes.byref(tc), 16, 16, 16, 16, 256, None) == moe.MOE_EINVAL
+    assert b'MOE_EXPERT_CHOICE' in lib.moe_last_error()
+    assert lib.moe_expert_choice(ctypes.byref(ec), None, 16, 16, 16, 256, None) == moe.MOE_EINVAL
+    assert b'probs' in lib.moe_last_error()
+    assert lib.moe_expert_choice(ctypes.byref(ec), 16, 16, None, 16, 256, None) == moe.MOE_EINVAL
+    assert b'sel' in lib.moe_last_error()
+    assert lib.moe_expert_choice(ctypes.byref(ec), 16, 16, 16, 16, None, None) == moe.MOE_EINVAL
+    assert b'ws' in lib.moe_last_error()
+    assert lib.moe_combine_expert_choice(ctypes.byref(tc), 16, 16, None, 16, 16, 16, None) == moe.MOE_EINVAL
+    assert lib.moe_combine_expert_choice(ctypes.byref(ec), 16, 16, None, 16, 2, 16, None) == moe.MOE_EINVAL
+    assert b'sel' in lib.moe_last_error()

@@ -668,3 +668,181 @@ def test_forward_is_deterministic(moe):
     _, b = forward(moe, w, dev)
     for kk in a:
         assert torch.equal(a[kk], b[kk]), kk
+
+
+# ----------------------------------------------------------------------------- expert choice
+def _ec_probs(T, E, kind, seed):
+    g = np.random.default_rng(seed)
+    if kind == 'grid':                                   # few distinct values: ties everywhere
+        return (g.integers(0, 9, size=(T, E)) / 8).astype(np.float32)
+    z = g.standard_normal((T, E))
+    p = np.exp(z - z.max(1, keepdims=True))
+    return (p / p.sum(1, keepdims=True)).astype(np.float32)
+
+
+# (T, E, C, kind): every register width of the selection kernel (T <= 8K, 16K,
+# 64K) and the streamed one (T > 64K), C > T, heavy ties, E = 256
+EC_SELECT_CASES = [(64, 4, 40, 'softmax'), (1000, 8, 313, 'softmax'), (8192, 8, 2560, 'softmax'),
+                   (12000, 16, 1000, 'grid'), (40000, 4, 25000, 'softmax'), (70001, 2, 40000, 'softmax'),
+                   (5000, 8, 1250, 'grid'), (300, 3, 1000, 'softmax'), (2048, 256, 64, 'softmax'),
+                   (1, 5, 1, 'softmax')]
+
+
+@pytest.mark.parametrize('case', EC_SELECT_CASES, ids=lambda c: f'T{c[0]}_E{c[1]}_C{c[2]}_{c[3]}')
+def test_expert_choice_select_bit_exact(moe, case):
+    T, E, C, kind = case
+    say('expert choice select', case)
+    p = _ec_probs(T, E, kind, seed=T + E)
+    rt_ref, sel_ref = O.expert_choice(p, C)
+    n = min(C, T)
+    cfg = moe.make_config(T, 8, E, 1, 8, capacity_override=C, dtype='f32', routing='expert')
+    ws = moe.workspace(cfg, DEV)
+    rt = torch.full((E, C), -7, dtype=torch.int32, device=DEV)
+    sel = torch.empty(T, E, dtype=torch.int32, device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    moe.moe_expert_choice(cfg, torch.from_numpy(p).to(DEV), rt, sel, counts, ws)
+    torch.cuda.synchronize()
+    rtn = np_of(rt)
+    np.testing.assert_array_equal(np_of(counts), [n] * E)
+    np.testing.assert_array_equal(rtn[:, :n], rt_ref)
+    assert (rtn[:, n:] == -7).all()                      # rows past n untouched
+    np.testing.assert_array_equal(np_of(sel), sel_ref)
+
+
+@pytest.mark.parametrize('E,shared,zero,dtype', [(8, False, 0, 'bf16'), (8, True, 0, 'bf16'), (130, False, 1, 'f32'),
+                                                 (256, False, 0, 'f32')])
+def test_combine_expert_choice_parity(moe, E, shared, zero, dtype):
+    """Picks from several ballots of 64 experts, summed in expert order, and the
+    fallback for tokens no expert picked."""
+    T, d = 500, 128
+    C = max(1, T // E)                                   # about one pick per token: some get none
+    say('combine expert choice', E, shared, zero, dtype)
+    p = _ec_probs(T, E, 'softmax', seed=E)
+    rt, sel = O.expert_choice(p, C)
+    w = synth.Workload('c', T=T, d=d, E=E, k=1, d_ff=8, act='gelu', score='softmax', renormalize=-1,
+                       cf=1.0, dtype=dtype, seed=41)
+    x = synth.router_inputs(w)['x']
+    ye = synth.router_inputs(w.with_(T=E * C, seed=42))['x'].reshape(E, C, d)
+    s_out = synth.router_inputs(w.with_(seed=43))['x'] if shared else None
+    cfg = moe.make_config(T, d, E, 1, 8, capacity_override=C, dtype=dtype, dropped_output=zero,
+                          n_shared=1 if shared else 0, d_ff_shared=8, routing='expert')
+    y = torch.empty(T, d, dtype=synth.to_torch(x, DEV).dtype, device=DEV)
+    moe.moe_combine_expert_choice(cfg, synth.to_torch(x, DEV), synth.to_torch(ye, DEV), synth.to_torch(s_out, DEV),
+                                  torch.from_numpy(p).to(DEV), torch.from_numpy(sel).to(DEV), y)
+    torch.cuda.synchronize()
+    yef = synth.as_f32(ye).astype(np.float64)
+    routed = np.zeros((T, d))
+    for t in range(T):
+        for e in range(E):
+            if sel[t, e] >= 0:
+                routed[t] += float(p[t, e]) * yef[e, sel[t, e]]
+    picked = (sel >= 0).any(1)
+    xf = synth.as_f32(x).astype(np.float64)
+    ref = O.round_store(O.combine(routed, None if s_out is None else synth.as_f32(s_out).astype(np.float64), xf,
+                                  picked, 'zero' if zero else 'residual'), dtype)
+    yn = f64_of(y)
+    assert maxrel(yn, ref) <= (1e-5 if dtype == 'f32' else 2e-2)
+    if not shared:
+        assert (~picked).any() and ((sel >= 0).sum(1) > 1).any()
+        np.testing.assert_array_equal(yn[~picked], 0.0 if zero else xf[~picked])
+
+
+def _compare_forward_ec(moe, w, rows=None, **over):
+    inp, ex, sh, dev = device_layer(w, moe)
+    say('forward expert choice', w.name, over)
+    cfg, out = forward(moe, w, dev, routing='expert', **over)
+    dout = 'zero' if over.get('dropped_output') == 'zero' else 'residual'
+    get = (lambda e: {kk: v[e] for kk, v in ex.items()})
+    gsh = None if sh is None else (lambda s: {kk: v[s] for kk, v in sh.items()})
+    ref = O.moe_forward(w, inp, get, gsh, rows=rows, capacity_override=over.get('capacity_override', 0),
+                        dropped_output=dout, routing='expert')
+    x = synth.as_f32(inp['x'])
+    zr, zg = ref['logits'], np_of(out['logits'])
+    bound = logit_error_bound(x, inp['w_router'], inp['logit_bias']) + 2.0 ** -24 * np.abs(zr.astype(np.float64))
+    assert (np.abs(zg.astype(np.float64) - zr) <= bound).all()
+    dz = np.abs(zg.astype(np.float64) - zr).max(axis=1)
+    gp = np_of(out['probs'])
+    assert_propagated(gp, ref['probs'], dz, what='probs')
+    T, E, C = w.T, w.E, ref['capacity']
+    n = min(C, T)
+    gsel, gc = np_of(out['sel']), np_of(out['counts'])
+    np.testing.assert_array_equal(gc, [n] * E)
+    # the GPU's picks are a valid top-n of its own probabilities: n per expert,
+    # rows numbered in token order, nothing unpicked above anything picked
+    for e in range(E):
+        pk = gsel[:, e] >= 0
+        assert pk.sum() == n
+        np.testing.assert_array_equal(gsel[pk, e], np.arange(n))
+        if n < T:
+            assert gp[pk, e].min() >= gp[~pk, e].max()
+    # and equal to the oracle's except where a probability lies within the
+    # propagated error of the expert's n-th largest one
+    rp = ref['probs']
+    diff = (gsel >= 0) != (ref['sel'] >= 0)
+    if diff.any():
+        kth = -np.sort(-rp.astype(np.float32), axis=0)[n - 1].astype(np.float64)
+        band = np.abs(rp - kth[None, :]) <= 1e-6 * np.abs(kth)[None, :] + rp * np.expm1(2 * dz)[:, None] + 1e-9
+        assert band[diff].all(), np.argwhere(diff & ~band)[:5]
+    tok_diff = diff.any(1)
+    say(f'  tokens picked differently near an expert boundary: {int(tok_diff.sum())}')
+    st = np_of(out['stats'])
+    unpicked = int((~(gsel >= 0).any(1)).sum())
+    assert st.tolist() == [E * n, 0, unpicked if w.n_shared == 0 else 0, E * (C - n)]
+    if not tok_diff.any():
+        np.testing.assert_array_equal(gsel, ref['sel'])
+        assert st[2] == ref['stats']['fallback']
+    l = np_of(out['losses']).astype(np.float64)
+    slack = 2 * float(dz.mean())
+    assert abs(l[0] - ref['l_aux']) <= (1e-5 + slack) * abs(ref['l_aux'])
+    lse_abs = np.abs(ref['lse'])
+    assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z']) + 2 * float((lse_abs * dz).mean()) + float((dz * dz).mean())
+    rws = ref['rows']
+    cmp = ~tok_diff[rws]
+    y = f64_of(out['y'])[rws]
+    tol = 1e-5 if w.dtype == 'f32' else 2e-2
+    err = maxrel(y[cmp], ref['y'][cmp])
+    say(f'  y max-rel err {err:.3e} over {int(cmp.sum())} rows; L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}')
+    assert err <= tol
+    none = ~(ref['sel'][rws] >= 0).any(1) & cmp
+    if w.n_shared == 0 and none.any():
+        want = 0.0 if dout == 'zero' else x[rws][none].astype(np.float64)
+        np.testing.assert_array_equal(y[none], want)
+    return cfg, out, ref
+
+
+EC_FORWARDS = [
+    ('tiny_f32', dict(), None),
+    ('tiny_f32', dict(capacity_override=5, dropped_output='zero'), None),
+    ('tiny_f32', dict(capacity_override=64), None),
+    ('switch_top1_skewed', dict(), 'every5'),
+    ('deepseekmoe_fine', dict(), 'every7'),
+    ('mixtral_8x_top2', dict(), 'sample'),
+    ('sigmoid_stress', dict(), 'sample'),
+]
+
+
+@pytest.mark.parametrize('case', EC_FORWARDS, ids=lambda c: c[0] + ''.join(f'_{k}{v}' for k, v in c[1].items()))
+def test_forward_expert_choice(moe, case):
+    name, over, rsel = case
+    w = synth.WORKLOADS[name]
+    rows = None
+    if rsel == 'every5':
+        rows = np.arange(0, w.T, 5)
+    elif rsel == 'every7':
+        rows = np.arange(0, w.T, 7)
+    elif rsel == 'sample':
+        rows = np.sort(np.random.default_rng(4).choice(w.T, 128, replace=False))
+    _compare_forward_ec(moe, w, rows=rows, **over)
+
+
+@pytest.mark.parametrize('T', [0, 1, 65])
+def test_forward_expert_choice_ragged_and_empty(moe, T):
+    w = synth.WORKLOADS['tiny_f32'].with_(T=T, name=f'tiny_ec_T{T}')
+    if T == 0:
+        inp, ex, sh, dev = device_layer(w.with_(T=1), moe)
+        dev['x'] = dev['x'][:0]
+        cfg, out = forward(moe, w, dev, routing='expert')
+        assert np_of(out['counts']).tolist() == [0] * w.E
+        assert np_of(out['losses']).tolist() == [0.0, 0.0]
+        return
+    _compare_forward_ec(moe, w)
