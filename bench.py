@@ -1,7 +1,8 @@
 """Benchmark of the MoE layer forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--phase-reps R]
+                    [--no-cpu-baseline] [--phase-reps R] [--dropless]
+                    [--routing token|expert]
 
 A step is one whole forward pass of the layer (router, capacity, dispatch,
 routed and shared expert FFNs, combine, losses) over one batch of T synthetic
@@ -47,6 +48,9 @@ def parse():
     p.add_argument('--phase-reps', type=int, default=10)
     p.add_argument('--dropless', action='store_true',
                    help='dropless mode: no capacity limit, expert rows packed without padding')
+    p.add_argument('--routing', choices=('token', 'expert'), default='token',
+                   help='token choice (each token its top-k experts) or expert choice (each expert its '
+                        'top-C tokens)')
     p.add_argument('--copy-calibration', action='store_true',
                    help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
     return p.parse_args()
@@ -71,10 +75,14 @@ def main():
         print('[bench]', *a, file=sys.stderr, flush=True)
 
     w = synth.WORKLOADS[args.workload]
+    ec = args.routing == 'expert'
+    if ec and args.dropless:
+        print(json.dumps({'error': 'expert-choice routing has no dropless mode'}), flush=True)
+        sys.exit(2)
     dev = 'cuda'
     t0 = time.time()
     inp = synth.router_inputs(w)
-    cfg = moe.config_from_workload(w, dropless=args.dropless)
+    cfg = moe.config_from_workload(w, dropless=args.dropless, routing=args.routing)
     C = moe.moe_validate(cfg)
     x = synth.to_torch(inp['x'], dev)
     weights = dict(w_router=synth.to_torch(inp['w_router'], dev),
@@ -150,6 +158,8 @@ def main():
     flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     flush_sink = torch.zeros((), dtype=torch.float32, device=dev)
     ph = {'route': [], 'dispatch': [], 'expert_ffn': [], 'shared_ffn': [], 'combine': []}
+    probs = torch.empty(T, E, dtype=torch.float32, device=dev) if ec else None
+    sel = torch.empty(T, E, dtype=torch.int32, device=dev) if ec else None
 
     def timed(name, fn):
         torch.sum(flush, dim=0, out=flush_sink)
@@ -163,10 +173,15 @@ def main():
     kept_rows = torch.empty(E, dtype=torch.int32, device=dev)
     for rep in range(args.phase_reps + 1):
         timed('route', lambda: moe.moe_route(cfg, x, weights['w_router'], weights['logit_bias'],
-                                             weights['select_bias'], None, None, idx, gates, None, ws))
-        # capacity slots and the token list of every expert (the layer gathers
-        # token rows inside the expert GEMM, so nothing is copied here)
-        timed('dispatch', lambda: moe.moe_dispatch(cfg, None, idx, slot, dropped, counts, row_token, None, ws))
+                                             weights['select_bias'], None, probs, idx, gates, None, ws))
+        if ec:
+            # every expert's top-C tokens (the 'dispatch' phase of expert choice)
+            timed('dispatch', lambda: moe.moe_expert_choice(cfg, probs, row_token, sel, counts, ws))
+        else:
+            # capacity slots and the token list of every expert (the layer gathers
+            # token rows inside the expert GEMM, so nothing is copied here)
+            timed('dispatch', lambda: moe.moe_dispatch(cfg, None, idx, slot, dropped, counts, row_token, None,
+                                                       ws))
         torch.clamp(counts, max=C, out=kept_rows)
         if args.dropless:
             timed('expert_ffn', lambda: moe.moe_expert_ffn_packed(
@@ -184,19 +199,29 @@ def main():
             timed('shared_ffn', lambda: moe.moe_expert_ffn(cfg, 'gelu', 1, T, None, x, weights['ws_in'], None,
                                                            weights['bs_in'], weights['ws_out'], weights['bs_out'],
                                                            fs, hs, s_out))
-        timed('combine', lambda: moe.moe_combine(cfg, x, ye, s_out, idx, gates, slot, dropped, y))
+        if ec:
+            timed('combine', lambda: moe.moe_combine_expert_choice(cfg, x, ye, s_out, probs, sel, y))
+        else:
+            timed('combine', lambda: moe.moe_combine(cfg, x, ye, s_out, idx, gates, slot, dropped, y))
     med = {kk: float(np.median(v[1:])) for kk, v in ph.items() if v}
     n_kept = int(torch.clamp(counts, max=C).sum().item())
-    any_kept = (dropped == 0).any(dim=1)
+    any_kept = (sel >= 0).any(dim=1) if ec else (dropped == 0).any(dim=1)
     n_tok_kept = int(any_kept.sum().item())
     n_fb = T - n_tok_kept
     mult = 3 if w.act == 'swiglu' else 2
     ffn_flops = 2.0 * n_kept * mult * d * F
     sh_flops = 2.0 * T * 2 * d * fs
-    bytes_route = T * d * b + d * E * 4 + T * k * 8 + ((T + 31) // 32) * (E + 1) * 8
-    # slots only: idx in; slot, dropped, row_token out (+ the tile histograms)
-    bytes_dispatch = T * k * 4 + T * k * 5 + n_kept * 4
-    bytes_combine = n_kept * d * b + (0 if fs else n_fb * d * b) + (T * d * b if fs else 0) + T * d * b + T * k * 13
+    bytes_route = T * d * b + d * E * 4 + T * k * 8 + ((T + 31) // 32) * (E + 1) * 8 + (T * E * 4 if ec else 0)
+    if ec:
+        # probabilities in; sel and the picked tokens out
+        bytes_dispatch = T * E * 4 + T * E * 4 + n_kept * 4
+        bytes_combine = (n_kept * d * b + (0 if fs else n_fb * d * b) + (T * d * b if fs else 0) + T * d * b
+                         + T * E * 8)
+    else:
+        # slots only: idx in; slot, dropped, row_token out (+ the tile histograms)
+        bytes_dispatch = T * k * 4 + T * k * 5 + n_kept * 4
+        bytes_combine = (n_kept * d * b + (0 if fs else n_fb * d * b) + (T * d * b if fs else 0) + T * d * b
+                         + T * k * 13)
     peak = PEAK_BF16_TFLOPS if w.dtype == 'bf16' else PEAK_F32_TFLOPS
 
     def gbs(nbytes, ms_):
@@ -223,7 +248,7 @@ def main():
     # HBM bytes per launch pair from the committed FETCH_SIZE / WRITE_SIZE
     # counter runs, if they were taken on this version of the GEMM source
     from mixture_experts_layer_20_amd import rocprof_summary
-    wl_key = w.name + ('_dropless' if args.dropless else '')
+    wl_key = w.name + ('_dropless' if args.dropless else '') + ('_expert_choice' if ec else '')
     rec = rocprof_summary.read_traffic(os.path.join(ROOT, 'profiles', f'gemm_traffic_{wl_key}.txt'), wl_key)
     roofline = {'kernel': 'expert grouped GEMM (gate/up launch + down launch)',
                 'bound': 'mfma', 'achieved': round(ach, 2), 'peak': peak, 'unit': 'TFLOP/s',
@@ -247,7 +272,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample_tokens, log, dropless=args.dropless)
+        cpu = cpu_baseline(w, args.cpu_sample_tokens, log, dropless=args.dropless, routing=args.routing)
 
     line = {'metric': METRIC, 'value': round(tokens_per_s, 1), 'unit': 'tokens/s', 'n_gpus': 1,
             'steps': args.steps, 'warmup': args.warmup, 'ms_per_step': round(ms, 4),
@@ -256,7 +281,7 @@ def main():
             'config': {'workload': w.name, 'T': w.T, 'd': d, 'E': E, 'k': k, 'd_ff': F, 'act': w.act,
                        'score': w.score, 'capacity_factor': w.cf, 'capacity': C,
                        'n_shared': w.n_shared, 'kept_assignments': kept, 'dropped_assignments': n_dropped,
-                       'dropless': bool(args.dropless)},
+                       'dropless': bool(args.dropless), 'routing': args.routing},
             'roofline': roofline,
             'phases': {kk: {a: (round(bb, 5) if isinstance(bb, float) else bb) for a, bb in v.items()}
                        for kk, v in phases.items()},
@@ -264,7 +289,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, sample_tokens, log, dropless=False):
+def cpu_baseline(w, sample_tokens, log, dropless=False, routing='token'):
     """The oracle as it stands, on the first `sample_tokens` tokens of the same
     workload taken as a batch of their own (routing, capacity, every expert
     FFN and the combine, in float64 on the host cores)."""
@@ -284,13 +309,13 @@ def cpu_baseline(w, sample_tokens, log, dropless=False):
     shared = [synth.expert_weights(w, s, shared=True) for s in range(w.n_shared)] or None
     t = time.perf_counter()
     O.moe_forward(ws_, inp, lambda e: experts[e], (lambda s: shared[s]) if shared else None,
-                  dropless=dropless)
+                  dropless=dropless, routing=routing)
     el = time.perf_counter() - t
     log(f'cpu oracle: {n} tokens in {el:.1f}s on {threads} threads')
     return {'value': round(n / el, 2), 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',
             'sample': f'the first {n} tokens of the {w.name} workload as one batch (T={n}, same d, E, k, '
-                      f'd_ff and capacity factor); routing, capacity, all expert FFNs and the combine '
-                      f'in float64 numpy; wall {el:.1f}s'}
+                      f'd_ff and capacity factor; {routing} choice{", dropless" if dropless else ""}); '
+                      f'routing, capacity, all expert FFNs and the combine in float64 numpy; wall {el:.1f}s'}
 
 
 if __name__ == '__main__':

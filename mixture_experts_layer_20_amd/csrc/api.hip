@@ -121,6 +121,7 @@ struct Workspace {
   float* gates_tmp;
   int32_t* row_token;
   uint32_t* ec_keys;
+  int32_t* ec_selT;
   float* ec_probs;
   int32_t* ec_fallback;
   void* h;
@@ -162,6 +163,7 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * xrows));
   if (c.routing == MOE_EXPERT_CHOICE) {
     w.ec_keys = static_cast<uint32_t*>(take(sizeof(uint32_t) * c.T * c.E));
+    w.ec_selT = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.E));
     w.ec_probs = static_cast<float*>(take(sizeof(float) * c.T * c.E));
     w.ec_fallback = static_cast<int32_t*>(take(sizeof(int32_t)));
   }
@@ -285,6 +287,7 @@ moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weigh
   EcArgs e{};
   e.probs = probs;
   e.keys = w.ec_keys;
+  e.selT = w.ec_selT;
   e.row_token = w.row_token;
   e.sel = out.sel;
   e.counts = out.counts;
@@ -520,6 +523,7 @@ moe_status moe_expert_choice(const moe_config* cfg, const float* probs, int32_t*
   EcArgs e{};
   e.probs = probs;
   e.keys = w.ec_keys;
+  e.selT = w.ec_selT;
   e.row_token = row_token;
   e.sel = sel;
   e.counts = counts;

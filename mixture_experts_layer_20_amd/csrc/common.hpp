@@ -187,6 +187,7 @@ struct EcArgs {
   const float* probs;         // [T,E] router probabilities
   uint32_t* keys;             // [E,T] order codes (workspace)
   int32_t* row_token;         // [E,C] picked tokens, ascending, first min(C,T) rows
+  int32_t* selT;              // [E,T] the same, expert-major (workspace)
   int32_t* sel;               // [T,E] slot of t in e, or -1
   int32_t* counts;            // [E] = min(C,T)
   const double* p_partial;    // [n_rtiles, E] router partial sums | null

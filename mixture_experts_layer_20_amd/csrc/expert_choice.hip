@@ -14,13 +14,17 @@
 // Kernels:
 //   ec_keys_kernel    [T,E] float32 probabilities -> [E,T] uint32 order codes
 //                     (an LDS-tiled transpose, so that each expert's column
-//                     reads contiguously)
+//                     reads contiguously); codes are at least 1, and 0 marks
+//                     "no token" in the selection kernel
 //   ec_select_kernel  one 1024-thread workgroup per expert: the n-th largest
 //                     code K (n = min(C, T)) by bisection over the 32-bit code
 //                     space, each step one count over the expert's codes held
 //                     in registers; then, in token order, every code above K
 //                     and the first n - #(code > K) codes equal to K are taken,
-//                     and a block-wide exclusive scan numbers the picks.
+//                     and a block-wide exclusive scan numbers the picks; the
+//                     rows go to an [E,T] staging array, written contiguously
+//   ec_sel_kernel     the [E,T] staging array -> sel [T,E] (LDS-tiled transpose)
+//   (for E <= 16 both transposes take one thread per token instead)
 // The count-based bisection makes no use of atomics and needs no sort: 33
 // workgroup-wide sums of per-thread counts.
 #include "common.hpp"
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(256) void ec_keys_kernel(const float* __restrict__ 
   for (int r = row; r < kTr; r += 4) {               // read along experts
     const int64_t t = t0 + r;
     const int e = e0 + lane;
-    if (t < T && e < E) tile[r][lane] = order_code(probs[t * E + e]);
+    if (t < T && e < E) tile[r][lane] = max(order_code(probs[t * E + e]), 1u);
   }
   __syncthreads();
 #pragma unroll 4
@@ -56,11 +60,56 @@ __global__ __launch_bounds__(256) void ec_keys_kernel(const float* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(256) void ec_sel_kernel(const int32_t* __restrict__ selT, int32_t* __restrict__ sel,
+                                                     int64_t T, int E) {
+  __shared__ int32_t tile[kTr][kTr + 1];
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTr;
+  const int e0 = blockIdx.y * kTr;
+  const int lane = threadIdx.x & (kTr - 1);
+  const int row = threadIdx.x / kTr;
+#pragma unroll 4
+  for (int r = row; r < kTr; r += 4) {               // read along tokens
+    const int e = e0 + r;
+    const int64_t t = t0 + lane;
+    if (t < T && e < E) tile[lane][r] = selT[static_cast<int64_t>(e) * T + t];
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int r = row; r < kTr; r += 4) {               // write along experts
+    const int64_t t = t0 + r;
+    const int e = e0 + lane;
+    if (t < T && e < E) sel[t * E + e] = tile[r][lane];
+  }
+}
+
+// E <= 16: one thread per token, E codes read along the row and written one
+// per expert row (consecutive lanes, consecutive tokens)
+__global__ __launch_bounds__(256) void ec_keys_rows_kernel(const float* __restrict__ probs,
+                                                           uint32_t* __restrict__ keys, int64_t T, int E) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  for (int e = 0; e < E; ++e) keys[static_cast<int64_t>(e) * T + t] = max(order_code(probs[t * E + e]), 1u);
+}
+
+__global__ __launch_bounds__(256) void ec_sel_rows_kernel(const int32_t* __restrict__ selT, int32_t* __restrict__ sel,
+                                                          int64_t T, int E) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  for (int e = 0; e < E; ++e) sel[t * E + e] = selT[static_cast<int64_t>(e) * T + t];
+}
+
 // ------------------------------------------------------------------ selection
+// Sum over the wavefront with DPP row shifts and row broadcasts (an inclusive
+// scan whose last lane holds the total), read back as a uniform value.  All
+// 64 lanes must be active.
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);    // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);    // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);    // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);    // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Sum over the workgroup; every thread gets the total.  `buf` holds two banks
@@ -99,13 +148,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wtot) {
 }
 
 // R > 0: thread i holds the codes of tokens [i R, i R + R) in registers
-// (T <= 1024 R).  R == 0: the same token ranges, of P = ceil(T / 1024) codes,
-// re-read from memory in every step (any T).
+// (T <= 1024 R), code 0 past the last token: every threshold tried is at
+// least 1 and K >= 1, so such entries are never counted, equal to K or taken,
+// and the counting loops need no per-entry bounds test (whose 64 masks would
+// otherwise stay live across the bisection).  R == 0: the same token ranges,
+// of P = ceil(T / 1024) codes, re-read from memory in every step (any T).
 template <int R>
 __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(EcArgs a) {
   __shared__ int sums[2][kSelWaves];
   __shared__ int wtot[kSelWaves];
   __shared__ double dred[kSelThreads];
+  __shared__ uint64_t pick_mask[R > 0 ? kSelThreads : 1];
+  __shared__ int pick_base[R > 0 ? kSelThreads : 1];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t T = a.T;
@@ -120,57 +174,96 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(EcArgs a) {
 #pragma unroll
     for (int j = 0; j < R; ++j) reg[j] = j < nv ? col[j] : 0u;
   }
-  // f(j, code of token first + j) for this thread's tokens in order (the
-  // register copy is indexed only by unrolled constants)
+  // f(code) over this thread's entries: the register copy (indexed only by
+  // unrolled constants; entries past the last token are 0), for the counts
+  // of the bisection
   auto each = [&](auto f) {
     if constexpr (R > 0) {
 #pragma unroll
-      for (int j = 0; j < R; ++j)
-        if (j < nv) f(j, reg[j]);
+      for (int j = 0; j < R; ++j) f(reg[j]);
     } else {
-      for (int j = 0; j < nv; ++j) f(j, col[j]);
+      for (int j = 0; j < nv; ++j) f(col[j]);
     }
   };
-  auto count_ge = [&](uint64_t v) -> int {
+  // f(j, code of token first + j) in token order, re-read from memory (the
+  // ordered passes of the R == 0 path)
+  auto each_in_order = [&](auto f) {
+    for (int j = 0; j < nv; ++j) f(j, col[j]);
+  };
+  // 32-bit compares (a 64-bit one would keep a widened copy of every code)
+  auto count_ge = [&](uint32_t v) -> int {
     int c = 0;
-    each([&](int, uint32_t k) { c += static_cast<uint64_t>(k) >= v ? 1 : 0; });
+    each([&](uint32_t k) { c += k >= v ? 1 : 0; });
     return c;
   };
 
-  // K = the largest v with #(code >= v) >= n: invariant #(>= lo) >= n > #(>= hi)
+  // K = the largest v with #(code >= v) >= n, by bisection: invariant
+  // #(>= lo) >= n > #(>= hi), every mid in [1, 2^32 - 1].  (Counting several
+  // thresholds a step with ballots and scalar popcounts, fewer steps and
+  // barriers, measured slower: the scalar adds serialise.)
   int bank = 0;
   uint64_t lo = 0, hi = uint64_t{1} << 32;
   for (int it = 0; it < 32; ++it) {
     const uint64_t mid = (lo + hi) >> 1;
-    if (block_sum(count_ge(mid), sums, bank) >= n) lo = mid;
+    if (block_sum(count_ge(static_cast<uint32_t>(mid)), sums, bank) >= n) lo = mid;
     else hi = mid;
   }
   const uint32_t K = static_cast<uint32_t>(lo);
-  const int64_t above = block_sum(count_ge(lo + 1), sums, bank);
+  int my_above = 0;
+  each([&](uint32_t k) { my_above += k > K ? 1 : 0; });
+  const int64_t above = block_sum(my_above, sums, bank);
   const int64_t take_eq = n - above;                 // codes equal to K to take, lowest tokens first
-
   // in token order: the equal codes before this thread's range, then the picks
   int my_eq = 0;
-  each([&](int, uint32_t k) { my_eq += k == K ? 1 : 0; });
+  each([&](uint32_t k) { my_eq += k == K ? 1 : 0; });
   const int64_t eq_before = block_excl_scan(my_eq, wtot);
-  int my_take = 0;
-  {
-    int64_t eq = eq_before;
-    each([&](int, uint32_t k) {
-      my_take += (k > K || (k == K && eq < take_eq)) ? 1 : 0;
-      eq += k == K ? 1 : 0;
-    });
-  }
-  {
+  int32_t* __restrict__ rt = a.row_token + static_cast<int64_t>(e) * a.C;
+  int32_t* __restrict__ st = a.selT + static_cast<int64_t>(e) * T;
+  if constexpr (R > 0) {
+    // this thread's picks as a bit mask (R <= 64), numbered through LDS, then
+    // written with consecutive lanes on consecutive tokens
+    uint64_t gt = 0, eqm = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      gt |= static_cast<uint64_t>(reg[j] > K) << j;
+      eqm |= static_cast<uint64_t>(reg[j] == K) << j;
+    }
+    // of the codes equal to K, the first take_eq - eq_before (if any) are taken
+    int64_t room = take_eq - eq_before;
+    uint64_t rest = eqm;
+    while (room > 0 && rest) {
+      rest &= rest - 1;
+      --room;
+    }
+    const uint64_t mask = gt | (eqm ^ rest);
+    const int base = block_excl_scan(__popcll(mask), wtot);
+    pick_mask[tid] = mask;
+    pick_base[tid] = base;
+    __syncthreads();
+    for (int64_t t = tid; t < T; t += kSelThreads) {
+      const int o = static_cast<int>(t / R), j = static_cast<int>(t % R);
+      const uint64_t w = pick_mask[o];
+      const bool tk = (w >> j) & 1u;
+      const int slot = pick_base[o] + __popcll(w & ((uint64_t{1} << j) - 1));
+      if (tk) rt[slot] = static_cast<int32_t>(t);
+      st[t] = tk ? slot : -1;
+    }
+  } else {
+    int my_take = 0;
+    {
+      int64_t eq = eq_before;
+      each_in_order([&](int, uint32_t k) {
+        my_take += (k > K || (k == K && eq < take_eq)) ? 1 : 0;
+        eq += k == K ? 1 : 0;
+      });
+    }
     int64_t slot = block_excl_scan(my_take, wtot);
     int64_t eq = eq_before;
-    int32_t* __restrict__ rt = a.row_token + static_cast<int64_t>(e) * a.C;
-    each([&](int j, uint32_t k) {
+    each_in_order([&](int j, uint32_t k) {
       const bool tk = k > K || (k == K && eq < take_eq);
       eq += k == K ? 1 : 0;
-      const int64_t t = first + j;
-      if (tk) rt[slot] = static_cast<int32_t>(t);
-      a.sel[t * a.E + e] = tk ? static_cast<int32_t>(slot) : -1;
+      if (tk) rt[slot] = static_cast<int32_t>(first + j);
+      st[first + j] = tk ? static_cast<int32_t>(slot) : -1;
       slot += tk ? 1 : 0;
     });
   }
@@ -222,7 +315,12 @@ hipError_t launch_expert_choice(const EcArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const dim3 tg(static_cast<unsigned>((a.T + kTr - 1) / kTr), static_cast<unsigned>((a.E + kTr - 1) / kTr));
-  ec_keys_kernel<<<tg, 256, 0, s>>>(a.probs, a.keys, a.T, a.E);
+  const unsigned rows_grid = static_cast<unsigned>((a.T + 255) / 256);
+  const bool by_rows = a.E <= 16;
+  if (by_rows)
+    ec_keys_rows_kernel<<<rows_grid, 256, 0, s>>>(a.probs, a.keys, a.T, a.E);
+  else
+    ec_keys_kernel<<<tg, 256, 0, s>>>(a.probs, a.keys, a.T, a.E);
   const unsigned grid = static_cast<unsigned>(a.E);
   if (a.T <= int64_t{kSelThreads} * 8)
     ec_select_kernel<8><<<grid, kSelThreads, 0, s>>>(a);
@@ -232,6 +330,10 @@ hipError_t launch_expert_choice(const EcArgs& a, hipStream_t s) {
     ec_select_kernel<64><<<grid, kSelThreads, 0, s>>>(a);
   else
     ec_select_kernel<0><<<grid, kSelThreads, 0, s>>>(a);
+  if (by_rows)
+    ec_sel_rows_kernel<<<rows_grid, 256, 0, s>>>(a.selT, a.sel, a.T, a.E);
+  else
+    ec_sel_kernel<<<tg, 256, 0, s>>>(a.selT, a.sel, a.T, a.E);
   return hipGetLastError();
 }
 
