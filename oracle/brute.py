@@ -144,12 +144,34 @@ def forward(x, w_router, logit_bias, select_bias, experts, shared, *, k, act, sc
                 mine.append(best)
             picks.append(sorted(mine))
     # capacity: slot = number of earlier assignments (priority order) to the same expert
-    seq = [(t, j) for j in range(k) for t in range(T)] if priority == 'rank' else \
-        [(t, j) for t in range(T) for j in range(k)]
+    seq = [(t, j) for t in range(T) for j in range(k)] if priority == 'token' else \
+        [(t, j) for j in range(k) for t in range(T)]
     slot = [[0] * k for _ in range(T)]
     for p, (t, j) in enumerate(seq):
         e = idx[t][j]
         slot[t][j] = sum(1 for (t2, j2) in seq[:p] if idx[t2][j2] == e)
+    if priority == 'score':
+        # per expert: keep the C largest float32 gates by repeated maximum over
+        # its queue (equal -> earlier in the queue); kept numbered first
+        for e in range(E):
+            queue = [(t, j) for (t, j) in seq if idx[t][j] == e]
+            kept = []
+            for _ in range(min(C, len(queue))):
+                best = None
+                for q in queue:
+                    if q in kept:
+                        continue
+                    if best is None or f32(gate[q[0]][q[1]]) > f32(gate[best[0]][best[1]]):
+                        best = q
+                kept.append(best)
+            nk = nd = 0
+            for (t, j) in queue:
+                if (t, j) in kept:
+                    slot[t][j] = nk
+                    nk += 1
+                else:
+                    slot[t][j] = C + nd
+                    nd += 1
     dropped = [[slot[t][j] >= C for j in range(k)] for t in range(T)]
 
     def run(wts, a, kind):

@@ -264,17 +264,25 @@ def capacity(T, k, E, cf, override=0):
     return int(math.ceil(float(cf) * T * k / E))
 
 
-def assign_capacity(idx, n_experts, C, priority='rank'):
+def assign_capacity(idx, n_experts, C, priority='rank', scores=None):
     """Queue position of every assignment in its expert; dropped iff position >= C.
 
     Rank-major: walk rank j = 0..k-1, and inside a rank tokens in order
     [P3 s.3 GShard priority; Tips: flatten rank-major, one-hot, cumulative
     sum]. Token-major walks tokens, then ranks [P4 "Where to start" 4].
+    'score': batch-prioritised routing, which ranks assignments by router
+    score [P3 s.3, the V-MoE alternative]: in each expert the C assignments
+    with the largest score (float32 ``scores`` [T,k], e.g. the gates; equal
+    scores to the earlier one in the rank-major queue) are kept and numbered
+    0.. in rank-major order; the dropped ones follow, numbered C.. in the
+    same order.
     Returns slot [T,k] int32, dropped [T,k] bool, counts [E] int64,
     row_token [E,C] int32 (-1 where empty).
     """
     idx = np.asarray(idx)
     T, k = idx.shape
+    if priority == 'score':
+        return _assign_by_score(idx, n_experts, C, np.asarray(scores, np.float32))
     cnt = [0] * n_experts
     slot = np.empty((T, k), np.int64)
     if priority == 'rank':
@@ -295,6 +303,29 @@ def assign_capacity(idx, n_experts, C, priority='rank'):
     return slot.astype(np.int32), dropped, np.asarray(cnt, np.int64), row_token
 
 
+def _assign_by_score(idx, n_experts, C, scores):
+    T, k = idx.shape
+    queue, _, counts, _ = assign_capacity(idx, n_experts, max(T, 1), 'rank')
+    slot = np.empty((T, k), np.int64)
+    dropped = np.zeros((T, k), bool)
+    for e in range(n_experts):
+        tt, jj = np.nonzero(idx == e)
+        q = queue[tt, jj]
+        order = np.argsort(q, kind='stable')             # this expert's rank-major queue
+        tt, jj, q = tt[order], jj[order], q[order]
+        sc = scores[tt, jj].astype(F64)
+        best = np.lexsort((q, -sc))[:C]                  # score descending, queue position ascending
+        keep = np.zeros(tt.size, bool)
+        keep[best] = True
+        slot[tt[keep], jj[keep]] = np.arange(int(keep.sum()))
+        slot[tt[~keep], jj[~keep]] = C + np.arange(int((~keep).sum()))
+        dropped[tt[~keep], jj[~keep]] = True
+    row_token = np.full((n_experts, C), -1, np.int32)
+    keep = ~dropped
+    row_token[idx[keep], slot[keep]] = np.nonzero(keep)[0]
+    return slot.astype(np.int32), dropped, counts, row_token
+
+
 def dropless_rows(idx, n_experts, priority='rank'):
     """Dropless mode: every assignment is kept, and the experts' rows are laid
     back to back with no padding ["Lab 18" s.3, the alternatives to dropping:
@@ -308,8 +339,10 @@ def dropless_rows(idx, n_experts, priority='rank'):
     """
     idx = np.asarray(idx)
     T, k = idx.shape
-    # every expert receives at most T assignments, so a capacity of T drops none
-    pos, dropped, counts, _ = assign_capacity(idx, n_experts, max(T, 1), priority)
+    # every expert receives at most T assignments, so a capacity of T drops none;
+    # with nothing dropped, score priority numbers its rows in rank-major order
+    pos, dropped, counts, _ = assign_capacity(idx, n_experts, max(T, 1),
+                                              'rank' if priority == 'score' else priority)
     assert not dropped.any()
     first = np.concatenate([[0], np.cumsum(counts)[:-1]])
     row = (first[idx] + pos).astype(np.int32)
@@ -442,7 +475,8 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
         dropped = np.zeros((T, k), bool)
     else:
         C = capacity(T, k, E, w.cf, capacity_override)
-        slot, dropped, counts, row_token = assign_capacity(idx, E, C, priority)
+        slot, dropped, counts, row_token = assign_capacity(idx, E, C, priority,
+                                                           scores=np.asarray(g, np.float32))
     l_aux = load_balancing_loss(probs, idx, E)
     l_z = float(np.mean(lse * lse))
 

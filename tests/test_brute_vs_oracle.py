@@ -250,3 +250,73 @@ def test_expert_choice_full_capacity_is_dense_mixture():
         dense += p[:, [e]] * out
     np.testing.assert_allclose(o['y'], dense, rtol=1e-5, atol=1e-6)
     assert abs(o['l_aux'] - 1.0) < 1e-12
+
+
+# ----------------------------------------------------------------------------- score priority
+def test_score_priority_worked_example():
+    """Batch-prioritised capacity by hand: expert 0 holds tokens 0, 1, 2 with
+    scores 0.3, 0.9, 0.5 and room for 2, so token 0 drops; the kept ones are
+    numbered in queue order (token 1, then token 2).  Equal scores go to the
+    earlier assignment in the rank-major queue (a first choice before a second
+    choice)."""
+    idx = np.array([[0], [0], [0], [1]])
+    g = np.array([[.3], [.9], [.5], [.2]], np.float32)
+    slot, dropped, counts, rt = O.assign_capacity(idx, 2, 2, 'score', g)
+    np.testing.assert_array_equal(slot[:, 0], [2, 0, 1, 0])
+    np.testing.assert_array_equal(dropped[:, 0], [True, False, False, False])
+    np.testing.assert_array_equal(counts, [3, 1])
+    np.testing.assert_array_equal(rt, [[1, 2], [3, -1]])
+    idx = np.array([[0, 1], [1, 0]])
+    g = np.full((2, 2), 0.5, np.float32)
+    slot, dropped, _, rt = O.assign_capacity(idx, 2, 1, 'score', g)
+    np.testing.assert_array_equal(dropped, [[False, True], [False, True]])   # first choices win the ties
+    np.testing.assert_array_equal(rt, [[0], [1]])
+
+
+def test_score_priority_properties():
+    """Kept scores dominate dropped ones within each expert, counts and kept
+    numbers follow C, and with room for everything the queue is the GShard one."""
+    rng = np.random.default_rng(8)
+    for trial in range(20):
+        T, E, k = int(rng.integers(1, 60)), int(rng.integers(1, 6)), 1
+        k = int(rng.integers(1, E + 1))
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+        g = (rng.integers(0, 5, size=(T, k)) / 4).astype(np.float32)
+        C = int(rng.integers(1, T + 1))
+        slot, dropped, counts, rt = O.assign_capacity(idx, E, C, 'score', g)
+        np.testing.assert_array_equal(dropped, slot >= C)
+        for e in range(E):
+            m = idx == e
+            assert sorted(slot[m].tolist()) == list(range(int(m.sum())))
+            kept, drop = g[m & ~dropped], g[m & dropped]
+            assert kept.size == min(C, int(m.sum()))
+            if kept.size and drop.size:
+                assert kept.min() >= drop.max()
+        s2, d2, _, r2 = O.assign_capacity(idx, E, T, 'score', g)
+        s3, d3, _, r3 = O.assign_capacity(idx, E, T, 'rank')
+        np.testing.assert_array_equal(s2, s3)
+        np.testing.assert_array_equal(r2, r3)
+
+
+@pytest.mark.parametrize('case', [c for c in CASES if c['name'] in ('swiglu_bf16', 'top1_raw_bias', 'shared_logrank',
+                                                                     'sigmoid_selbias', 'zero_fallback')],
+                         ids=lambda c: c['name'])
+def test_score_priority_oracle_matches_brute_force(case):
+    w = case.get('wl') or synth.WORKLOADS[case['name']]
+    inp = synth.router_inputs(w)
+    ex = synth.all_expert_weights(w)
+    sh = synth.all_expert_weights(w, shared=True) if w.n_shared else None
+    ov = case.get('override', 0) or max(1, O.capacity(w.T, w.k, w.E, w.cf) // 2)   # force drops
+    dout = case.get('dropped_output', 'residual')
+    o = O.moe_forward(w, inp, ex, sh, priority='score', capacity_override=ov, dropped_output=dout)
+    x, wr, lb, sb, experts, shared = _lists(w, inp, ex, sh)
+    b = brute.forward(x, wr, lb, sb, experts, shared, k=w.k, act=w.act, score=w.score,
+                      renormalize=w.renormalize, C=o['capacity'], dtype=w.dtype,
+                      priority='score', dropped_output=dout)
+    assert o['dropped'].any()
+    np.testing.assert_array_equal(o['slot'], np.array(b['slot']))
+    np.testing.assert_array_equal(o['dropped'], np.array(b['dropped']))
+    yb = np.array(b['y'])
+    tol = 1e-6 if w.dtype == 'f32' else 1e-2
+    assert np.abs(o['y'] - yb).max() <= tol * np.abs(yb).max()
+    assert np.mean(o['y'] != yb) < 0.02
