@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--phase-reps R] [--dropless]
-                    [--routing token|expert]
+                    [--routing token|expert] [--priority rank|token|score]
 
 A step is one whole forward pass of the layer (router, capacity, dispatch,
 routed and shared expert FFNs, combine, losses) over one batch of T synthetic
@@ -51,6 +51,9 @@ def parse():
     p.add_argument('--routing', choices=('token', 'expert'), default='token',
                    help='token choice (each token its top-k experts) or expert choice (each expert its '
                         'top-C tokens)')
+    p.add_argument('--priority', choices=('rank', 'token', 'score'), default='rank',
+                   help='capacity queue order: rank-major (GShard), token-major, or by router score '
+                        '(batch-prioritised)')
     p.add_argument('--copy-calibration', action='store_true',
                    help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
     return p.parse_args()
@@ -82,7 +85,7 @@ def main():
     dev = 'cuda'
     t0 = time.time()
     inp = synth.router_inputs(w)
-    cfg = moe.config_from_workload(w, dropless=args.dropless, routing=args.routing)
+    cfg = moe.config_from_workload(w, dropless=args.dropless, routing=args.routing, priority=args.priority)
     C = moe.moe_validate(cfg)
     x = synth.to_torch(inp['x'], dev)
     weights = dict(w_router=synth.to_torch(inp['w_router'], dev),
@@ -180,8 +183,12 @@ def main():
         else:
             # capacity slots and the token list of every expert (the layer gathers
             # token rows inside the expert GEMM, so nothing is copied here)
-            timed('dispatch', lambda: moe.moe_dispatch(cfg, None, idx, slot, dropped, counts, row_token, None,
-                                                       ws))
+            if args.priority == 'score' and not args.dropless:
+                timed('dispatch', lambda: moe.moe_dispatch_by_score(cfg, None, idx, gates, slot, dropped, counts,
+                                                                    row_token, None, ws))
+            else:
+                timed('dispatch', lambda: moe.moe_dispatch(cfg, None, idx, slot, dropped, counts, row_token,
+                                                           None, ws))
         torch.clamp(counts, max=C, out=kept_rows)
         if args.dropless:
             timed('expert_ffn', lambda: moe.moe_expert_ffn_packed(
@@ -248,7 +255,8 @@ def main():
     # HBM bytes per launch pair from the committed FETCH_SIZE / WRITE_SIZE
     # counter runs, if they were taken on this version of the GEMM source
     from mixture_experts_layer_20_amd import rocprof_summary
-    wl_key = w.name + ('_dropless' if args.dropless else '') + ('_expert_choice' if ec else '')
+    wl_key = (w.name + ('_dropless' if args.dropless else '') + ('_expert_choice' if ec else '')
+              + ('' if args.priority == 'rank' else '_' + args.priority + '_priority'))
     rec = rocprof_summary.read_traffic(os.path.join(ROOT, 'profiles', f'gemm_traffic_{wl_key}.txt'), wl_key)
     roofline = {'kernel': 'expert grouped GEMM (gate/up launch + down launch)',
                 'bound': 'mfma', 'achieved': round(ach, 2), 'peak': peak, 'unit': 'TFLOP/s',
@@ -272,7 +280,8 @@ def main():
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_sample_tokens, log, dropless=args.dropless, routing=args.routing)
+        cpu = cpu_baseline(w, args.cpu_sample_tokens, log, dropless=args.dropless, routing=args.routing,
+                           priority=args.priority)
 
     line = {'metric': METRIC, 'value': round(tokens_per_s, 1), 'unit': 'tokens/s', 'n_gpus': 1,
             'steps': args.steps, 'warmup': args.warmup, 'ms_per_step': round(ms, 4),
@@ -281,7 +290,7 @@ def main():
             'config': {'workload': w.name, 'T': w.T, 'd': d, 'E': E, 'k': k, 'd_ff': F, 'act': w.act,
                        'score': w.score, 'capacity_factor': w.cf, 'capacity': C,
                        'n_shared': w.n_shared, 'kept_assignments': kept, 'dropped_assignments': n_dropped,
-                       'dropless': bool(args.dropless), 'routing': args.routing},
+                       'dropless': bool(args.dropless), 'routing': args.routing, 'priority': args.priority},
             'roofline': roofline,
             'phases': {kk: {a: (round(bb, 5) if isinstance(bb, float) else bb) for a, bb in v.items()}
                        for kk, v in phases.items()},
@@ -289,7 +298,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, sample_tokens, log, dropless=False, routing='token'):
+def cpu_baseline(w, sample_tokens, log, dropless=False, routing='token', priority='rank'):
     """The oracle as it stands, on the first `sample_tokens` tokens of the same
     workload taken as a batch of their own (routing, capacity, every expert
     FFN and the combine, in float64 on the host cores)."""
@@ -309,7 +318,7 @@ def cpu_baseline(w, sample_tokens, log, dropless=False, routing='token'):
     shared = [synth.expert_weights(w, s, shared=True) for s in range(w.n_shared)] or None
     t = time.perf_counter()
     O.moe_forward(ws_, inp, lambda e: experts[e], (lambda s: shared[s]) if shared else None,
-                  dropless=dropless, routing=routing)
+                  dropless=dropless, routing=routing, priority=priority)
     el = time.perf_counter() - t
     log(f'cpu oracle: {n} tokens in {el:.1f}s on {threads} threads')
     return {'value': round(n / el, 2), 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',

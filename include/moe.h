@@ -74,7 +74,7 @@ typedef enum { MOE_OK = 0, MOE_EINVAL = 1, MOE_EUNSUPPORTED = 2, MOE_EHIP = 3 } 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 typedef enum { MOE_GELU = 0, MOE_SWIGLU = 1 } moe_act;
-typedef enum { MOE_RANK_MAJOR = 0, MOE_TOKEN_MAJOR = 1 } moe_priority;
+typedef enum { MOE_RANK_MAJOR = 0, MOE_TOKEN_MAJOR = 1, MOE_SCORE_PRIORITY = 2 } moe_priority;
 typedef enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1 } moe_routing;
 
 typedef struct moe_config {
@@ -96,6 +96,18 @@ typedef struct moe_config {
   int32_t dropless;           /* 0: capacity C as above; 1: dropless (see below)       */
   int32_t routing;            /* moe_routing: token choice (above) or expert choice    */
 } moe_config;
+
+/* Score priority (priority = MOE_SCORE_PRIORITY) ["Lab 18" s.3: who is
+ * dropped depends on the priority; V-MoE's batch-prioritised routing ranks
+ * assignments by router score]:
+ *   - each expert keeps the C assignments with the largest gate (float32, as
+ *     moe_route stores it), equal gates to the assignment earlier in the
+ *     rank-major queue;
+ *   - kept assignments take slots 0.. in rank-major queue order, dropped ones
+ *     C.. in the same order (so dropped iff slot >= C still holds);
+ *   - the standalone dispatch is moe_dispatch_by_score (moe_dispatch returns
+ *     MOE_EINVAL); in dropless mode nothing drops and the rows are numbered
+ *     as under rank-major priority. */
 
 /* Dropless mode (dropless = 1) ["Lab 18" s.3, alternatives to dropping: a
  * capacity high enough that nothing is dropped, or block-sparse kernels that
@@ -176,6 +188,14 @@ MOE_API moe_status moe_route(const moe_config* cfg, const void* x, const float* 
 MOE_API moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx, int32_t* slot,
                         uint8_t* dropped, int32_t* counts, int32_t* row_token, void* xe,
                         void* ws, void* stream);
+
+/* Capacity and dispatch under score priority (cfg->priority must be
+ * MOE_SCORE_PRIORITY, token choice; see above): as moe_dispatch, plus
+ *   gates   [T,k] float32 score of each choice (moe_route's gates)
+ * row_token is required when xe is given. */
+MOE_API moe_status moe_dispatch_by_score(const moe_config* cfg, const void* x, const int32_t* idx, const float* gates,
+                                         int32_t* slot, uint8_t* dropped, int32_t* counts, int32_t* row_token,
+                                         void* xe, void* ws, void* stream);
 
 /* Grouped expert FFN on bf16 MFMA (float32 FMA for MOE_F32)
  * ["Lab 18" s.1 experts, Tips (one grouped matrix multiply over all

@@ -25,7 +25,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GELU, MOE_SWIGLU = 0, 1
-MOE_RANK_MAJOR, MOE_TOKEN_MAJOR = 0, 1
+MOE_RANK_MAJOR, MOE_TOKEN_MAJOR, MOE_SCORE_PRIORITY = 0, 1, 2
 MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE = 0, 1
 
 EXPORTS = ('moe_validate', 'moe_workspace_bytes', 'moe_route', 'moe_dispatch', 'moe_expert_ffn',
@@ -66,6 +66,7 @@ def _load():
         'moe_workspace_bytes': (ctypes.c_size_t, [cfgp]),
         'moe_route': (st, [cfgp] + [_P] * 11),
         'moe_dispatch': (st, [cfgp] + [_P] * 9),
+        'moe_dispatch_by_score': (st, [cfgp] + [_P] * 10),
         'moe_expert_ffn': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                 ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
         'moe_expert_ffn_packed': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
@@ -93,7 +94,7 @@ _ENUMS = {
     'score': {'softmax': MOE_SOFTMAX, 'sigmoid': MOE_SIGMOID},
     'act': {'gelu': MOE_GELU, 'swiglu': MOE_SWIGLU},
     'dtype': {'f32': MOE_F32, 'float32': MOE_F32, 'bf16': MOE_BF16, 'bfloat16': MOE_BF16},
-    'priority': {'rank': MOE_RANK_MAJOR, 'token': MOE_TOKEN_MAJOR},
+    'priority': {'rank': MOE_RANK_MAJOR, 'token': MOE_TOKEN_MAJOR, 'score': MOE_SCORE_PRIORITY},
     'dropped_output': {'residual': 0, 'zero': 1},
     'routing': {'token': MOE_TOKEN_CHOICE, 'expert': MOE_EXPERT_CHOICE},
 }
@@ -200,6 +201,16 @@ def moe_dispatch(cfg, x, idx, slot, dropped, counts, row_token, xe, ws, stream=N
                              _ptr(counts, 'counts', torch.int32),
                              _ptr(row_token, 'row_token', torch.int32), _ptr(xe, 'xe', dt),
                              _ptr(ws, 'ws'), _stream(stream)))
+
+
+def moe_dispatch_by_score(cfg, x, idx, gates, slot, dropped, counts, row_token, xe, ws, stream=None):
+    """Capacity under score priority: each expert keeps its C highest-gated choices."""
+    dt = torch_dtype(cfg)
+    _check(_lib.moe_dispatch_by_score(ctypes.byref(cfg), _ptr(x, 'x', dt), _ptr(idx, 'idx', torch.int32),
+                                      _ptr(gates, 'gates', torch.float32), _ptr(slot, 'slot', torch.int32),
+                                      _ptr(dropped, 'dropped', torch.uint8), _ptr(counts, 'counts', torch.int32),
+                                      _ptr(row_token, 'row_token', torch.int32), _ptr(xe, 'xe', dt),
+                                      _ptr(ws, 'ws'), _stream(stream)))
 
 
 def moe_expert_ffn(cfg, act, groups, rows_per_group, rows, a, w_in, w_gate, b_in, w_out, b_out, F,

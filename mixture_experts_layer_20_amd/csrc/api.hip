@@ -92,7 +92,7 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
   if (c.score != MOE_SOFTMAX && c.score != MOE_SIGMOID) return fail(MOE_EINVAL, "unknown score %d", c.score);
   if (c.act != MOE_GELU && c.act != MOE_SWIGLU) return fail(MOE_EINVAL, "unknown act %d", c.act);
   if (c.dtype != MOE_F32 && c.dtype != MOE_BF16) return fail(MOE_EINVAL, "unknown dtype %d", c.dtype);
-  if (c.priority != MOE_RANK_MAJOR && c.priority != MOE_TOKEN_MAJOR)
+  if (c.priority != MOE_RANK_MAJOR && c.priority != MOE_TOKEN_MAJOR && c.priority != MOE_SCORE_PRIORITY)
     return fail(MOE_EINVAL, "unknown priority %d", c.priority);
   if (c.dropped_output != 0 && c.dropped_output != 1) return fail(MOE_EINVAL, "dropped_output must be 0 or 1");
   const int64_t C = capacity_of(c);
@@ -104,6 +104,12 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
 }
 
 int resolved_renorm(const moe_config& c) { return c.renormalize < 0 ? (c.k > 1) : c.renormalize; }
+
+// Batch-prioritised capacity in effect (in dropless mode nothing is dropped
+// and the kept choices are numbered in rank-major order, as without it).
+bool by_score(const moe_config& c) {
+  return c.priority == MOE_SCORE_PRIORITY && !c.dropless && c.routing == MOE_TOKEN_CHOICE;
+}
 
 // ------------------------------------------------------------------ workspace
 struct Workspace {
@@ -124,6 +130,7 @@ struct Workspace {
   int32_t* ec_selT;
   float* ec_probs;
   int32_t* ec_fallback;
+  int32_t* score_queue;
   void* h;
   void* ye;
   void* hs;
@@ -161,12 +168,15 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   // expert rows: E*C (capacity), or T*k packed (dropless)
   const int64_t xrows = c.dropless ? c.T * c.k : c.E * C;
   w.row_token = static_cast<int32_t*>(take(sizeof(int32_t) * xrows));
-  if (c.routing == MOE_EXPERT_CHOICE) {
+  if (c.routing == MOE_EXPERT_CHOICE || by_score(c)) {
     w.ec_keys = static_cast<uint32_t*>(take(sizeof(uint32_t) * c.T * c.E));
     w.ec_selT = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.E));
+  }
+  if (c.routing == MOE_EXPERT_CHOICE) {
     w.ec_probs = static_cast<float*>(take(sizeof(float) * c.T * c.E));
     w.ec_fallback = static_cast<int32_t*>(take(sizeof(int32_t)));
   }
+  if (by_score(c)) w.score_queue = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
 
   w.h = take(ds * xrows * c.d_ff);
   w.ye = take(ds * xrows * c.d);
@@ -277,6 +287,48 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   g2.K = F;
   g2.act = 0;
   return hip_status(launch_gemm(g2, c.dtype, s), "expert GEMM 2");
+}
+
+// Capacity and dispatch.  Score priority: the histogram/scan/permute pass
+// first gives every assignment its rank-major queue position with room for
+// all (into the workspace), then the kept set is chosen by score and numbered
+// (launch_score_priority); the row copy into xe, if asked for, follows.
+moe_status capacity_step(const moe_config& c, int64_t C, const Workspace& w, const CapArgs& a, const float* gates,
+                         hipStream_t s) {
+  if (!by_score(c)) return hip_status(launch_capacity(a, c.dtype, s), "capacity");
+  CapArgs q = a;
+  q.C = std::max<int64_t>(c.T, 1);
+  q.slot = w.score_queue;
+  q.row_token = nullptr;
+  q.kept = nullptr;
+  q.fallback_partial = nullptr;
+  q.x = nullptr;
+  q.xe = nullptr;
+  q.token_major = 0;
+  q.packed = 0;
+  MOE_TRY(hip_status(launch_capacity(q, c.dtype, s), "capacity queue"));
+  ScoreArgs sa{};
+  sa.idx = a.idx;
+  sa.gates = gates;
+  sa.queue = w.score_queue;
+  sa.counts = a.counts;
+  sa.keys = w.ec_keys;
+  sa.selT = w.ec_selT;
+  sa.slot = a.slot;
+  sa.dropped = a.dropped;
+  sa.row_token = a.row_token;
+  sa.kept = w.kept;
+  sa.fallback_partial = a.fallback_partial;
+  sa.T = c.T;
+  sa.C = C;
+  sa.E = c.E;
+  sa.k = c.k;
+  sa.n_tiles = a.n_tiles;
+  MOE_TRY(hip_status(launch_score_priority(sa, s), "score-priority capacity"));
+  if (a.xe && a.row_token && c.T > 0)
+    MOE_TRY(hip_status(launch_gather_rows(a.x, a.xe, a.row_token, w.kept, C, c.E, static_cast<int>(c.d * dsize(c)), s),
+                       "dispatch copy"));
+  return MOE_OK;
 }
 
 // Expert choice after the router: each expert's picks, the routed FFNs on
@@ -403,6 +455,7 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx
     MOE_TRY(check_ptr(x, "x", 16));
     MOE_TRY(check_ptr(xe, "xe", 16, C > 0));
   }
+  if (by_score(c)) return fail(MOE_EINVAL, "score priority needs the scores: call moe_dispatch_by_score");
   Workspace w = carve(c, C, ws);
   CapArgs a = cap_args(c, C, w);
   a.idx = idx;
@@ -413,6 +466,39 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx
   a.x = x;
   a.xe = xe;
   return hip_status(launch_capacity(a, c.dtype, static_cast<hipStream_t>(stream)), "capacity");
+}
+
+moe_status moe_dispatch_by_score(const moe_config* cfg, const void* x, const int32_t* idx, const float* gates,
+                                 int32_t* slot, uint8_t* dropped, int32_t* counts, int32_t* row_token, void* xe,
+                                 void* ws, void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  if (c.priority != MOE_SCORE_PRIORITY || c.routing != MOE_TOKEN_CHOICE)
+    return fail(MOE_EINVAL, "moe_dispatch_by_score needs priority = MOE_SCORE_PRIORITY under token choice");
+  const bool needT = c.T > 0;
+  MOE_TRY(check_ptr(idx, "idx", 4, needT));
+  MOE_TRY(check_ptr(gates, "gates", 4, needT));
+  MOE_TRY(check_ptr(slot, "slot", 4, needT));
+  MOE_TRY(check_ptr(dropped, "dropped", 1, needT));
+  MOE_TRY(check_ptr(counts, "counts", 4));
+  MOE_TRY(check_ptr(row_token, "row_token", 4, false));
+  MOE_TRY(check_ptr(ws, "ws", 256));
+  if ((xe || x) && needT) {
+    MOE_TRY(check_ptr(x, "x", 16));
+    MOE_TRY(check_ptr(xe, "xe", 16, C > 0));
+    if (!row_token) return fail(MOE_EINVAL, "row_token is needed to copy rows into xe under score priority");
+  }
+  Workspace w = carve(c, C, ws);
+  CapArgs a = cap_args(c, C, w);
+  a.idx = idx;
+  a.slot = slot;
+  a.dropped = dropped;
+  a.counts = counts;
+  a.row_token = row_token;
+  a.x = x;
+  a.xe = xe;
+  return capacity_step(c, C, w, a, gates, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups, int64_t rows_per_group,
@@ -712,7 +798,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   // row_token, so no dispatched copy of x is made
   a.x = nullptr;
   a.xe = nullptr;
-  MOE_TRY(hip_status(launch_capacity(a, c.dtype, s), "capacity"));
+  MOE_TRY(capacity_step(c, C, w, a, out->gates, s));
 
   if (c.dropless) {
     // packed rows: expert e's rows start after the counts of the lower experts

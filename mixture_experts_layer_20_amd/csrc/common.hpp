@@ -194,8 +194,29 @@ struct EcArgs {
   const double* lse2_partial; // [n_rtiles]
   double* psum;               // [E + 1]
   int32_t* fallback_count;    // [1] zeroed here (the combine adds to it) | null
+  // selection over lists of different lengths (batch-prioritised capacity):
+  // expert e's entries are keys[e*T + 0 .. lengths[e]); counts and row_token
+  // are then not written
+  const int32_t* lengths;     // [E] | null (every list T long)
+  int keep_before;            // entries not taken store -(taken entries before them) - 1
   int64_t T, C;
   int E, n_rtiles;
+};
+
+struct ScoreArgs {
+  const int32_t* idx;         // [T,k]
+  const float* gates;         // [T,k] the scores
+  const int32_t* queue;       // [T,k] rank-major queue position (room for all)
+  const int32_t* counts;      // [E]
+  uint32_t* keys;             // [E,T] workspace
+  int32_t* selT;              // [E,T] workspace
+  int32_t* slot;              // [T,k]
+  uint8_t* dropped;           // [T,k]
+  int32_t* row_token;         // [E,C] | null
+  int32_t* kept;              // [E] min(counts, C)
+  int32_t* fallback_partial;  // [n_tiles] | null
+  int64_t T, C;
+  int E, k, n_tiles;
 };
 
 struct SeqLossArgs {
@@ -214,6 +235,10 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
 hipError_t launch_losses(const LossArgs& a, hipStream_t s);
 hipError_t launch_expert_choice(const EcArgs& a, hipStream_t s);
+hipError_t launch_select_top(const EcArgs& a, hipStream_t s);
+hipError_t launch_score_priority(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_gather_rows(const void* x, void* xe, const int32_t* row_token, const int32_t* kept, int64_t C,
+                              int E, int row_bytes, hipStream_t s);
 hipError_t launch_seq_loss(const SeqLossArgs& a, hipStream_t s);
 hipError_t launch_bias_update(const int32_t* counts, float* select_bias, int E, int64_t Tk, float gamma,
                               hipStream_t s);

@@ -162,12 +162,13 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(EcArgs a) {
   __shared__ int pick_base[R > 0 ? kSelThreads : 1];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
-  const int64_t T = a.T;
+  const int64_t T = a.T;                             // row stride of keys and selT
+  const int64_t len = a.lengths ? a.lengths[e] : T;  // this expert's entries
   const int64_t P = R > 0 ? R : (T + kSelThreads - 1) / kSelThreads;
   const int64_t first = static_cast<int64_t>(tid) * P;
-  const int nv = static_cast<int>(max<int64_t>(0, min<int64_t>(P, T - first)));   // codes of this thread
+  const int nv = static_cast<int>(max<int64_t>(0, min<int64_t>(P, len - first)));   // codes of this thread
   const uint32_t* __restrict__ col = a.keys + static_cast<int64_t>(e) * T + first;
-  const int64_t n = min<int64_t>(a.C, T);
+  const int64_t n = min<int64_t>(a.C, len);
 
   uint32_t reg[R > 0 ? R : 1];
   if constexpr (R > 0) {
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(EcArgs a) {
   int my_eq = 0;
   each([&](uint32_t k) { my_eq += k == K ? 1 : 0; });
   const int64_t eq_before = block_excl_scan(my_eq, wtot);
-  int32_t* __restrict__ rt = a.row_token + static_cast<int64_t>(e) * a.C;
+  int32_t* __restrict__ rt = a.row_token ? a.row_token + static_cast<int64_t>(e) * a.C : nullptr;
   int32_t* __restrict__ st = a.selT + static_cast<int64_t>(e) * T;
   if constexpr (R > 0) {
     // this thread's picks as a bit mask (R <= 64), numbered through LDS, then
@@ -240,13 +241,13 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(EcArgs a) {
     pick_mask[tid] = mask;
     pick_base[tid] = base;
     __syncthreads();
-    for (int64_t t = tid; t < T; t += kSelThreads) {
+    for (int64_t t = tid; t < len; t += kSelThreads) {
       const int o = static_cast<int>(t / R), j = static_cast<int>(t % R);
       const uint64_t w = pick_mask[o];
       const bool tk = (w >> j) & 1u;
       const int slot = pick_base[o] + __popcll(w & ((uint64_t{1} << j) - 1));
-      if (tk) rt[slot] = static_cast<int32_t>(t);
-      st[t] = tk ? slot : -1;
+      if (tk && rt) rt[slot] = static_cast<int32_t>(t);
+      st[t] = tk ? slot : (a.keep_before ? -slot - 1 : -1);
     }
   } else {
     int my_take = 0;
@@ -262,13 +263,13 @@ __global__ __launch_bounds__(kSelThreads) void ec_select_kernel(EcArgs a) {
     each_in_order([&](int j, uint32_t k) {
       const bool tk = k > K || (k == K && eq < take_eq);
       eq += k == K ? 1 : 0;
-      if (tk) rt[slot] = static_cast<int32_t>(first + j);
-      st[first + j] = tk ? static_cast<int32_t>(slot) : -1;
+      if (tk && rt) rt[slot] = static_cast<int32_t>(first + j);
+      st[first + j] = tk ? static_cast<int32_t>(slot) : (a.keep_before ? static_cast<int32_t>(-slot - 1) : -1);
       slot += tk ? 1 : 0;
     });
   }
   if (tid == 0) {
-    a.counts[e] = static_cast<int32_t>(n);
+    if (a.counts) a.counts[e] = static_cast<int32_t>(n);
     if (e == 0 && a.fallback_count) a.fallback_count[0] = 0;
   }
 
@@ -308,6 +309,19 @@ __global__ __launch_bounds__(256) void ec_empty_kernel(EcArgs a) {
 
 }  // namespace
 
+hipError_t launch_select_top(const EcArgs& a, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>(a.E);
+  if (a.T <= int64_t{kSelThreads} * 8)
+    ec_select_kernel<8><<<grid, kSelThreads, 0, s>>>(a);
+  else if (a.T <= int64_t{kSelThreads} * 16)
+    ec_select_kernel<16><<<grid, kSelThreads, 0, s>>>(a);
+  else if (a.T <= int64_t{kSelThreads} * 64)
+    ec_select_kernel<64><<<grid, kSelThreads, 0, s>>>(a);
+  else
+    ec_select_kernel<0><<<grid, kSelThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_choice(const EcArgs& a, hipStream_t s) {
   if (a.E == 0) return hipSuccess;
   if (a.T == 0) {
@@ -321,15 +335,8 @@ hipError_t launch_expert_choice(const EcArgs& a, hipStream_t s) {
     ec_keys_rows_kernel<<<rows_grid, 256, 0, s>>>(a.probs, a.keys, a.T, a.E);
   else
     ec_keys_kernel<<<tg, 256, 0, s>>>(a.probs, a.keys, a.T, a.E);
-  const unsigned grid = static_cast<unsigned>(a.E);
-  if (a.T <= int64_t{kSelThreads} * 8)
-    ec_select_kernel<8><<<grid, kSelThreads, 0, s>>>(a);
-  else if (a.T <= int64_t{kSelThreads} * 16)
-    ec_select_kernel<16><<<grid, kSelThreads, 0, s>>>(a);
-  else if (a.T <= int64_t{kSelThreads} * 64)
-    ec_select_kernel<64><<<grid, kSelThreads, 0, s>>>(a);
-  else
-    ec_select_kernel<0><<<grid, kSelThreads, 0, s>>>(a);
+  const hipError_t err = launch_select_top(a, s);
+  if (err != hipSuccess) return err;
   if (by_rows)
     ec_sel_rows_kernel<<<rows_grid, 256, 0, s>>>(a.selT, a.sel, a.T, a.E);
   else

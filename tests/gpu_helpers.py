@@ -133,3 +133,29 @@ def check_capacity_valid(idx, slot, dropped, counts, C, E, priority='rank'):
         assert slot[t, j] == nxt[e]
         nxt[e] += 1
     np.testing.assert_array_equal(dropped, slot >= C)
+
+
+def check_score_capacity_valid(idx, gates, slot, dropped, counts, C, E):
+    """Properties any correct score-priority assignment has for the given
+    choices and float32 gates: per expert, min(count, C) kept, no dropped gate
+    above a kept one (equal gates: the earlier in the rank-major queue is
+    kept), kept numbered 0.. and dropped C.. in queue order."""
+    T, k = idx.shape
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    queue = [(t, j) for j in range(k) for t in range(T)]
+    per = {e: [] for e in range(E)}
+    for t, j in queue:
+        per[int(idx[t, j])].append((t, j))
+    for e, q in per.items():
+        g = np.array([gates[t, j] for t, j in q], np.float32)
+        kept = np.array([not dropped[t, j] for t, j in q], bool)
+        assert kept.sum() == min(C, len(q))
+        if kept.any() and (~kept).any():
+            assert g[kept].min() >= g[~kept].max()
+            # at equal gates the earlier entry is the kept one
+            gmin = g[kept].min()
+            if (g[~kept] == gmin).any():
+                assert np.nonzero(kept & (g == gmin))[0].max() < np.nonzero(~kept & (g == gmin))[0].min()
+        np.testing.assert_array_equal([slot[t, j] for (t, j), kk in zip(q, kept) if kk], np.arange(kept.sum()))
+        np.testing.assert_array_equal([slot[t, j] for (t, j), kk in zip(q, kept) if not kk],
+                                      C + np.arange((~kept).sum()))

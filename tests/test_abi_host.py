@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ('moe_route', 'moe_dispatch', 'moe_expert_ffn', 'moe_combine', 'moe_forward',
               'moe_aux_losses', 'moe_validate', 'moe_workspace_bytes', 'moe_last_error',
-              'moe_expert_ffn_packed', 'moe_expert_choice', 'moe_combine_expert_choice'):
+              'moe_expert_ffn_packed', 'moe_expert_choice', 'moe_combine_expert_choice',
+              'moe_dispatch_by_score'):
         assert n in names
 
 
@@ -239,3 +240,28 @@ def test_expert_choice_entry_points_reject_bad_arguments(moe):
     assert lib.moe_combine_expert_choice(ctypes.byref(tc), 16, 16, None, 16, 16, 16, None) == moe.MOE_EINVAL
     assert lib.moe_combine_expert_choice(ctypes.byref(ec), 16, 16, None, 16, 2, 16, None) == moe.MOE_EINVAL
     assert b'sel' in lib.moe_last_error()
+
+
+def test_score_priority_configuration(moe):
+    lib = moe._lib
+    sc = cfg(moe, priority='score')
+    assert moe.moe_validate(sc) == 40
+    c = cfg(moe)
+    c.priority = 3
+    with pytest.raises(ValueError, match='priority'):
+        moe.moe_validate(c)
+    # the plain dispatch cannot rank by score; the score dispatch needs score priority
+    assert lib.moe_dispatch(ctypes.byref(sc), None, 16, 16, 16, 16, None, None, 256, None) == moe.MOE_EINVAL
+    assert b'moe_dispatch_by_score' in lib.moe_last_error()
+    assert lib.moe_dispatch_by_score(ctypes.byref(cfg(moe)), None, 16, 16, 16, 16, 16, None, None, 256,
+                                     None) == moe.MOE_EINVAL
+    assert lib.moe_dispatch_by_score(ctypes.byref(sc), None, 16, None, 16, 16, 16, None, None, 256,
+                                     None) == moe.MOE_EINVAL
+    assert b'gates' in lib.moe_last_error()
+    assert lib.moe_dispatch_by_score(ctypes.byref(sc), 16, 16, 16, 16, 16, 16, None, 16, 256,
+                                     None) == moe.MOE_EINVAL
+    assert b'row_token' in lib.moe_last_error()
+    # its queue and the selection buffers take workspace
+    assert moe.moe_workspace_bytes(sc) > moe.moe_workspace_bytes(cfg(moe))
+    assert moe.moe_workspace_bytes(cfg(moe, priority='score', dropless=True)) == \
+        moe.moe_workspace_bytes(cfg(moe, dropless=True))

@@ -12,8 +12,8 @@ import torch
 import synth
 from oracle import moe as O
 
-from gpu_helpers import (DEV, assert_propagated, check_capacity_valid, device_layer, f64_of,
-                         forward, logit_error_bound, maxrel, near_tie_tokens, np_of)
+from gpu_helpers import (DEV, assert_propagated, check_capacity_valid, check_score_capacity_valid, device_layer,
+                         f64_of, forward, logit_error_bound, maxrel, near_tie_tokens, np_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -522,7 +522,7 @@ def _compare_forward(moe, w, rows=None, **over):
     inp, ex, sh, dev = device_layer(w, moe)
     say('forward', w.name, over)
     cfg, out = forward(moe, w, dev, **over)
-    pr = 'token' if over.get('priority') == 'token' else 'rank'
+    pr = over.get('priority', 'rank')
     dout = 'zero' if over.get('dropped_output') == 'zero' else 'residual'
     cov = over.get('capacity_override', 0)
     get = (lambda e: {kk: v[e] for kk, v in ex.items()})
@@ -562,6 +562,8 @@ def _compare_forward(moe, w, rows=None, **over):
         np.testing.assert_array_equal(gs, r_row)
         np.testing.assert_array_equal(gc, r_counts)
         assert not gd.any()
+    elif pr == 'score':
+        check_score_capacity_valid(gi, np_of(out['gates']), gs, gd, gc, C, w.E)
     else:
         check_capacity_valid(gi, gs, gd, gc, C, w.E, pr)
     assert_propagated(np_of(out['gates'])[same], ref['gates'][same], dz[same], what='gates')
@@ -846,3 +848,61 @@ def test_forward_expert_choice_ragged_and_empty(moe, T):
         assert np_of(out['losses']).tolist() == [0.0, 0.0]
         return
     _compare_forward_ec(moe, w)
+
+
+
+# ----------------------------------------------------------------------------- score priority
+# (T, E, k, C, kind): the selection widths (lists up to 8K, 16K, 64K entries and
+# the streamed path past 64K tokens), heavy gate ties, many drops
+SCORE_CASES = [(700, 8, 3, 100, 'uniform'), (4096, 16, 1, 256, 'uniform'), (16384, 64, 6, 1536, 'grid'),
+               (70000, 4, 2, 20000, 'uniform'), (3000, 5, 2, 400, 'grid'), (64, 4, 2, 40, 'uniform')]
+
+
+@pytest.mark.parametrize('case', SCORE_CASES, ids=lambda c: f'T{c[0]}_E{c[1]}_k{c[2]}_C{c[3]}_{c[4]}')
+def test_dispatch_by_score_bit_exact(moe, case):
+    T, E, k, C, kind = case
+    say('dispatch by score', case)
+    idx = synth.random_indices(T, E, k, seed=T + k, skew=0.5)
+    g = np.random.default_rng(T).random((T, k)).astype(np.float32)
+    if kind == 'grid':
+        g = (np.round(g * 8) / 8).astype(np.float32)
+    slot_r, dropped_r, counts_r, rt_r = O.assign_capacity(idx, E, C, 'score', g)
+    cfg = moe.make_config(T, 64, E, k, 64, capacity_override=C, dtype='bf16', priority='score')
+    ws = moe.workspace(cfg, DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    slot = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    dropped = torch.empty(T, k, dtype=torch.uint8, device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    rt = torch.full((E, C), -1, dtype=torch.int32, device=DEV)
+    w = synth.Workload('s', T=T, d=64, E=E, k=k, d_ff=8, act='gelu', score='softmax', renormalize=-1, cf=1.0,
+                       dtype='bf16', seed=5)
+    x = synth.to_torch(synth.router_inputs(w)['x'], DEV)
+    xe = torch.zeros(E, C, 64, dtype=x.dtype, device=DEV)
+    moe.moe_dispatch_by_score(cfg, x, d_idx, torch.from_numpy(g).to(DEV), slot, dropped, counts, rt, xe, ws)
+    torch.cuda.synchronize()
+    assert dropped_r.any()
+    np.testing.assert_array_equal(np_of(counts), counts_r)
+    np.testing.assert_array_equal(np_of(slot), slot_r)
+    np.testing.assert_array_equal(np_of(dropped).astype(bool), dropped_r)
+    np.testing.assert_array_equal(np_of(rt), rt_r)
+    # the copy of the kept rows
+    xn, xen = np_of(x), np_of(xe)
+    kept = np.minimum(counts_r, C)
+    for e in range(E):
+        np.testing.assert_array_equal(xen[e, :kept[e]], xn[rt_r[e, :kept[e]]])
+
+
+SCORE_FORWARDS = [('tiny_f32', dict(capacity_override=20)), ('switch_top1_skewed', dict()),
+                  ('deepseekmoe_fine', dict(capacity_override=900)), ('mixtral_8x_top2', dict(capacity_override=1800)),
+                  ('sigmoid_stress', dict(capacity_override=2500))]
+
+
+@pytest.mark.parametrize('case', SCORE_FORWARDS, ids=lambda c: c[0])
+def test_forward_score_priority(moe, case):
+    name, over = case
+    w = synth.WORKLOADS[name]
+    rows = None
+    if w.T > 5000:
+        rows = np.sort(np.random.default_rng(6).choice(w.T, 160, replace=False))
+    cfg, out, ref = _compare_forward(moe, w, rows=rows, priority='score', **over)
+    assert ref['dropped'].any()
