@@ -10,5 +10,8 @@ module both sides use is ``synth`` (seeded input tensors, no layer arithmetic).
 * ``fp32spec`` -- the float32 sigmoid selection key, step by step.
 * ``brute``  -- a pure-Python per-token loop for tiny inputs, written
   independently of ``moe`` so that each checks the other.
+* ``backward`` -- the chain rule of ``moe``'s layer (gradients of the input,
+  router and expert weights, with the balance and z-loss terms), pinned by
+  finite differences of the forward definition.
 """
 

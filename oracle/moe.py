@@ -82,7 +82,10 @@ def round_bf16(v):
 
 
 def round_store(v, dtype: str):
-    """Round to the layer's storage type ('f32' or 'bf16'), returned as float64."""
+    """Round to the layer's storage type ('f32' or 'bf16'), returned as float64.
+    'f64' stores exactly (the smooth layer that finite differences need)."""
+    if dtype == 'f64':
+        return np.asarray(v, dtype=F64)
     if dtype == 'f32':
         return np.asarray(v, dtype=F64).astype(np.float32).astype(F64)
     if dtype == 'bf16':
@@ -438,7 +441,7 @@ def combine(routed, shared=None, x=None, any_kept=None, dropped_output='residual
 # ----------------------------------------------------------------------------- forward
 def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank',
                 capacity_override=0, dropped_output='residual', logits=None, dropless=False,
-                routing='token'):
+                routing='token', exact=False):
     """The whole layer.
 
     w: a ``synth.Workload``-like object (T, d, E, k, act, score, renormalize,
@@ -455,6 +458,9 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     routing: 'token' (token choice, the default) or 'expert' (expert choice:
        every expert takes its C best tokens by float32 probability, the gate
        is that probability).
+    exact: no float32 rounding of x, the weights or the logits' values (the
+       selection still ranks the float32 keys); with w.dtype 'f64' the layer
+       is then smooth wherever no choice changes, as finite differences need.
 
     Steps: logits -> keys -> top-k -> gates/probs -> capacity -> experts ->
     combine, with the losses beside [P3 "What to implement" 1-5; P4 build
@@ -462,8 +468,13 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     """
     x = inp['x']
     T, E, k, d = w.T, w.E, w.k, w.d
-    z = router_logits(as_f32(x), inp['w_router'], inp.get('logit_bias')) if logits is None \
-        else np.asarray(logits, np.float32)
+    if exact:
+        z = np.asarray(x, F64) @ np.asarray(inp['w_router'], F64)
+        if inp.get('logit_bias') is not None:
+            z = z + np.asarray(inp['logit_bias'], F64)[None, :]
+    else:
+        z = router_logits(as_f32(x), inp['w_router'], inp.get('logit_bias')) if logits is None \
+            else np.asarray(logits, np.float32)
     idx, g, probs = route(z, k, w.score, w.renormalize, inp.get('select_bias'))
     lse = logsumexp(z)
     if routing == 'expert':
@@ -486,7 +497,9 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     pos = np.full(T, -1, np.int64)
     pos[rows] = np.arange(rows.size)
     kept = ~dropped
-    xa = as_f32(x)
+    xa = np.asarray(x, F64) if exact else as_f32(x)
+    wcast = (lambda wts: {kk: (None if v is None else np.asarray(v, F64)) for kk, v in wts.items()}) \
+        if exact else _f32_weights
     get = experts if callable(experts) else (lambda e: {kk: v[e] for kk, v in experts.items()})
     routed = np.zeros((rows.size, d), F64)
     for e in range(E):
@@ -495,7 +508,7 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
         t_e, j_e = np.nonzero((idx == e) & kept & sel[:, None])
         if t_e.size == 0:
             continue
-        _, o = expert_ffn(xa[t_e].astype(F64), _f32_weights(get(e)), w.act, w.dtype)
+        _, o = expert_ffn(xa[t_e].astype(F64), wcast(get(e)), w.act, w.dtype)
         routed[pos[t_e]] += g[t_e, j_e][:, None] * o
 
     S = None
@@ -504,7 +517,7 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
             (lambda s: {kk: v[s] for kk, v in shared_experts.items()})
         S = np.zeros((rows.size, d), F64)
         for s in range(w.n_shared):
-            _, o = expert_ffn(xa[rows].astype(F64), _f32_weights(gs(s)), 'gelu', w.dtype)
+            _, o = expert_ffn(xa[rows].astype(F64), wcast(gs(s)), 'gelu', w.dtype)
             S += o
     any_kept = kept.any(axis=1)[rows]
     y = combine(routed, S, xa[rows], any_kept, dropped_output)
