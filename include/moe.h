@@ -361,6 +361,57 @@ MOE_API moe_status moe_forward(const moe_config* cfg, const moe_weights* w, cons
                        moe_outputs* out, void* ws, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
+/* Gradients of the backward pass (storage type unless marked float32). */
+typedef struct moe_grads {
+  void* dx;                   /* [T,d]                                     (required) */
+  float* dw_router;           /* [d,E] float32                             (required) */
+  float* dlogit_bias;         /* [E] float32 or NULL                                  */
+  void* dw_in;                /* GELU: [E,F,d]; SwiGLU: the up projection  (required) */
+  void* dw_gate;              /* SwiGLU [E,F,d] (required then), else ignored         */
+  void* db_in;                /* [E,F] or NULL (GELU only)                            */
+  void* dw_out;               /* [E,d,F]                                   (required) */
+  void* db_out;               /* [E,d] or NULL                                        */
+  void* dws_in;               /* shared experts, concatenated: [n_shared*Fs, d]       */
+  void* dbs_in;               /* [n_shared*Fs] or NULL                                */
+  void* dws_out;              /* [d, n_shared*Fs]                                     */
+  void* dbs_out;              /* [d] or NULL: the gradient of EACH shared expert's
+                                 output bias (the forward adds their sum)             */
+  float* dgates;              /* [T,k] float32 or NULL                                */
+  float* dlogits;             /* [T,E] float32 or NULL                                */
+} moe_grads;
+
+/* Bytes of backward workspace for cfg (0 if cfg is invalid or not built). */
+MOE_API size_t moe_backward_workspace_bytes(const moe_config* cfg);
+
+/* Backward pass of moe_forward ["Lab 18" s.1 (gate values: with raw top-1
+ * gates the router learns through the gate) and s.2 (f_i is a count and has
+ * no gradient; the balance loss reaches the router through P_i; the z-loss);
+ * "Lab 01" "The traps"; "Mixture of experts" lecture, training a router]:
+ * the gradients of  L = <dy, y> + alpha_aux * L_aux + alpha_z * L_z.
+ *   - top-k selection and capacity are piecewise constant: no gradient; a
+ *     dropped choice's gate gets none; a token that fell back to y = x passes
+ *     dy to dx; the selection bias has no gradient;
+ *   - the float32 rounding of the logits and the storage roundings are taken
+ *     as the identity; H and Ye are the forward's stored values, the expert
+ *     pre-activations are recomputed;
+ *   - built for bf16 storage, token choice with a capacity (not dropless):
+ *     MOE_EUNSUPPORTED otherwise.
+ *   x, weights    the forward's inputs
+ *   fwd           the forward's outputs: idx, gates, slot, dropped, counts and
+ *                 logits are read (logits required)
+ *   fwd_ws        the forward's workspace, unchanged since that call (its
+ *                 expert rows, hidden activations and outputs are read)
+ *   dy            [T,d] storage type
+ *   alpha_aux, alpha_z  [host] loss weights (0 leaves a loss out)
+ *   grads         see moe_grads; weight gradients are written, not added to
+ *   bws           backward workspace of moe_backward_workspace_bytes() bytes
+ * Weight gradients contract over tokens with float32 accumulation in the
+ * matrix cores; the router-weight gradient uses the exact three-plane bf16
+ * split of dL/dz (as the router does for its weight). */
+MOE_API moe_status moe_backward(const moe_config* cfg, const moe_weights* w, const void* x,
+                                const moe_outputs* fwd, const void* fwd_ws, const void* dy, float alpha_aux,
+                                float alpha_z, moe_grads* grads, void* bws, void* stream);
+
 MOE_API const char* moe_last_error(void);
 
 #ifdef __cplusplus

@@ -55,6 +55,11 @@ class moe_outputs(ctypes.Structure):
                                   'stats', 'logits', 'probs', 'lse', 'sel')]
 
 
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ('dx', 'dw_router', 'dlogit_bias', 'dw_in', 'dw_gate', 'db_in', 'dw_out', 'db_out',
+                                  'dws_in', 'dbs_in', 'dws_out', 'dbs_out', 'dgates', 'dlogits')]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f'{LIB_PATH} is not built: run `python mixture_experts_layer_20_amd/build.py`')
@@ -79,6 +84,9 @@ def _load():
         'moe_aux_losses': (st, [cfgp, _P, _P, _P, _P, _P]),
         'moe_forward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs),
                              _P, _P]),
+        'moe_backward_workspace_bytes': (ctypes.c_size_t, [cfgp]),
+        'moe_backward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs), _P, _P,
+                              ctypes.c_float, ctypes.c_float, ctypes.POINTER(moe_grads), _P, _P]),
         'moe_last_error': (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -333,3 +341,39 @@ def alloc_outputs(cfg, device='cuda', logits=False, probs=False, lse=False) -> d
     if cfg.routing == MOE_EXPERT_CHOICE:
         o['sel'] = torch.empty(T, E, dtype=torch.int32, device=device)
     return o
+
+
+_GKEYS = ('dx', 'dw_router', 'dlogit_bias', 'dw_in', 'dw_gate', 'db_in', 'dw_out', 'db_out', 'dws_in', 'dbs_in',
+          'dws_out', 'dbs_out', 'dgates', 'dlogits')
+
+
+def backward_workspace(cfg: moe_config, device='cuda') -> torch.Tensor:
+    n = _lib.moe_backward_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise ValueError(f'moe_backward is not built for this configuration: {cfg_summary(cfg)}')
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def cfg_summary(cfg) -> str:
+    return ', '.join(f'{n}={getattr(cfg, n)}' for n, _ in cfg._fields_)
+
+
+def moe_backward(cfg, weights: dict, x, fwd_outputs: dict, fwd_ws, dy, grads: dict, bws, alpha_aux=0.0,
+                 alpha_z=0.0, stream=None):
+    """Backward pass of moe_forward: ``grads`` is a dict keyed like moe_grads;
+    ``fwd_outputs`` and ``fwd_ws`` are the forward call's outputs and workspace."""
+    dt = torch_dtype(cfg)
+    wd = {kk: _ptr(weights.get(kk), kk, torch.float32 if kk in ('w_router', 'logit_bias', 'select_bias') else dt)
+          for kk in _WKEYS}
+    want_o = dict(y=dt, idx=torch.int32, gates=torch.float32, slot=torch.int32, dropped=torch.uint8,
+                  counts=torch.int32, losses=torch.float32, stats=torch.int32, logits=torch.float32,
+                  probs=torch.float32, lse=torch.float32, sel=torch.int32)
+    od = {kk: _ptr(fwd_outputs.get(kk), kk, want_o[kk]) for kk in _OKEYS}
+    f32 = ('dw_router', 'dlogit_bias', 'dgates', 'dlogits')
+    gd = {kk: _ptr(grads.get(kk), kk, torch.float32 if kk in f32 else dt) for kk in _GKEYS}
+    w = moe_weights(**wd)
+    o = moe_outputs(**od)
+    g = moe_grads(**gd)
+    _check(_lib.moe_backward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x, 'x', dt), ctypes.byref(o),
+                             _ptr(fwd_ws, 'fwd_ws'), _ptr(dy, 'dy', dt), float(alpha_aux), float(alpha_z),
+                             ctypes.byref(g), _ptr(bws, 'bws'), _stream(stream)))

@@ -383,6 +383,147 @@ moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weigh
   return hip_status(launch_losses(l, s), "loss finaliser");
 }
 
+// ------------------------------------------------------------------ backward
+int64_t round8(int64_t v) { return (v + 7) / 8 * 8; }
+
+struct BwdWorkspace {
+  float* dgates;
+  float* dz;
+  bf16_t* dYe;
+  bf16_t* U;
+  bf16_t* U2;
+  bf16_t* dH;
+  bf16_t* dact;
+  bf16_t* dA;
+  bf16_t* woT;
+  bf16_t* wiT;
+  bf16_t* dYeT;
+  bf16_t* HT;
+  bf16_t* dactT;
+  bf16_t* AT;
+  bf16_t* xT;
+  bf16_t* planes;
+  float* slabs;
+  float* wrT;
+  bf16_t* Us;
+  bf16_t* dHs;
+  bf16_t* dUs;
+  bf16_t* dAs;
+  bf16_t* wsoT;
+  bf16_t* wsiT;
+  bf16_t* dyT;
+  bf16_t* HsT;
+  bf16_t* dUsT;
+  int S;
+  size_t bytes;
+};
+
+BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
+  const int64_t T = c.T, d = c.d, E = c.E, F = c.d_ff, Cp = round8(C), Tp = round8(T);
+  const int64_t ga = c.act == MOE_SWIGLU ? 2 : 1;
+  const int64_t Fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
+  BwdWorkspace b{};
+  size_t off = 0;
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t n) -> void* {
+    void* q = p ? p + off : nullptr;
+    off += align_up(n);
+    return q;
+  };
+  const size_t h2 = sizeof(bf16_t);
+  b.S = router_splits(d, c.E, Tp);
+  b.dgates = static_cast<float*>(take(sizeof(float) * T * c.k));
+  b.dz = static_cast<float*>(take(sizeof(float) * T * E));
+  b.dYe = static_cast<bf16_t*>(take(h2 * E * C * d));
+  b.U = static_cast<bf16_t*>(take(h2 * E * C * F));
+  b.U2 = ga == 2 ? static_cast<bf16_t*>(take(h2 * E * C * F)) : nullptr;
+  b.dH = static_cast<bf16_t*>(take(h2 * E * C * F));
+  b.dact = static_cast<bf16_t*>(take(h2 * E * C * ga * F));
+  b.dA = static_cast<bf16_t*>(take(h2 * E * C * d));
+  b.woT = static_cast<bf16_t*>(take(h2 * E * F * d));
+  b.wiT = static_cast<bf16_t*>(take(h2 * E * d * ga * F));
+  b.dYeT = static_cast<bf16_t*>(take(h2 * E * d * Cp));
+  b.HT = static_cast<bf16_t*>(take(h2 * E * F * Cp));
+  b.dactT = static_cast<bf16_t*>(take(h2 * E * ga * F * Cp));
+  b.AT = static_cast<bf16_t*>(take(h2 * E * d * Cp));
+  b.xT = static_cast<bf16_t*>(take(h2 * d * Tp));
+  b.planes = static_cast<bf16_t*>(take(h2 * 4 * E * Tp));
+  b.slabs = static_cast<float*>(take(sizeof(float) * b.S * d * E));
+  b.wrT = static_cast<float*>(take(sizeof(float) * E * d));
+  if (Fs > 0) {
+    b.Us = static_cast<bf16_t*>(take(h2 * T * Fs));
+    b.dHs = static_cast<bf16_t*>(take(h2 * T * Fs));
+    b.dUs = static_cast<bf16_t*>(take(h2 * T * Fs));
+    b.dAs = static_cast<bf16_t*>(take(h2 * T * d));
+    b.wsoT = static_cast<bf16_t*>(take(h2 * Fs * d));
+    b.wsiT = static_cast<bf16_t*>(take(h2 * d * Fs));
+    b.dyT = static_cast<bf16_t*>(take(h2 * d * Tp));
+    b.HsT = static_cast<bf16_t*>(take(h2 * Fs * Tp));
+    b.dUsT = static_cast<bf16_t*>(take(h2 * Fs * Tp));
+  }
+  b.bytes = off;
+  return b;
+}
+
+moe_status check_backward_config(const moe_config& c, int64_t C) {
+  if (c.dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the backward pass is built for bf16 storage");
+  if (c.routing != MOE_TOKEN_CHOICE || c.dropless)
+    return fail(MOE_EUNSUPPORTED, "the backward pass is built for token choice with a capacity (not dropless)");
+  const int64_t lim = int64_t{1} << 30;
+  const int64_t ga = c.act == MOE_SWIGLU ? 2 : 1;
+  const int64_t Fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
+  const int64_t Cp = round8(C), Tp = round8(c.T);
+  const int64_t big = std::max({C * c.d, C * ga * c.d_ff, static_cast<int64_t>(c.d) * Cp, ga * c.d_ff * Cp,
+                                static_cast<int64_t>(c.d) * Tp, Fs * Tp, c.T * std::max<int64_t>(Fs, c.d),
+                                static_cast<int64_t>(c.d_ff) * c.d * ga});
+  if (big >= lim) return fail(MOE_EINVAL, "one backward GEMM operand would hold 2^30 elements or more");
+  return MOE_OK;
+}
+
+// C[g] = A[g] B[g]^T (+ bias) on the bf16 grouped GEMM, operands K-contiguous.
+moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, const int32_t* gather, int64_t a_rows,
+                 const void* B, int64_t ldb, int64_t b_gs, const void* bias, void* Cout, const int32_t* rows,
+                 int64_t rpg, int groups, int N, int K, hipStream_t s) {
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.a_gs = a_gs;
+  g.gather = gather;
+  g.a_rows = a_rows;
+  g.B0 = B;
+  g.ldb = ldb;
+  g.b_gs = b_gs;
+  g.bias = bias;
+  g.C = Cout;
+  g.rows = rows;
+  g.rows_per_group = rpg;
+  g.groups = groups;
+  g.N = N;
+  g.K = K;
+  g.act = 0;
+  return hip_status(launch_gemm(g, MOE_BF16, s), what);
+}
+
+moe_status transpose(const char* what, const bf16_t* in, bf16_t* out, int G, int64_t R, int64_t Cc, int64_t Rpad,
+                     int64_t in_gs, int64_t ld_in, int64_t out_gs, int64_t ld_out, const int32_t* valid,
+                     const int32_t* gather, int64_t gather_gs, hipStream_t s) {
+  TransposeArgs t{};
+  t.in = in;
+  t.out = out;
+  t.gather = gather;
+  t.valid = valid;
+  t.R = R;
+  t.Cc = Cc;
+  t.Rpad = Rpad;
+  t.in_gs = in_gs;
+  t.ld_in = ld_in;
+  t.gather_gs = gather_gs;
+  t.out_gs = out_gs;
+  t.ld_out = ld_out;
+  t.G = G;
+  return hip_status(launch_transpose(t, s), what);
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -835,6 +976,243 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   l.losses = out->losses;
   l.stats = out->stats;
   return hip_status(launch_losses(l, s), "loss finaliser");
+}
+
+size_t moe_backward_workspace_bytes(const moe_config* cfg) {
+  int64_t C = 0;
+  if (validate(cfg, &C) != MOE_OK || check_backward_config(*cfg, C) != MOE_OK) return 0;
+  return carve_bwd(*cfg, C, nullptr).bytes;
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void* x, const moe_outputs* fwd,
+                        const void* fwd_ws, const void* dy, float alpha_aux, float alpha_z, moe_grads* gr, void* bws,
+                        void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  MOE_TRY(check_backward_config(c, C));
+  if (!wt || !fwd || !gr) return fail(MOE_EINVAL, "weights, forward outputs and gradients must not be NULL");
+  if (!(alpha_aux == alpha_aux) || !(alpha_z == alpha_z)) return fail(MOE_EINVAL, "alpha_aux and alpha_z must not be NaN");
+  const bool needT = c.T > 0;
+  const bool glu = c.act == MOE_SWIGLU;
+  const int64_t Fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
+  MOE_TRY(check_ptr(x, "x", 16, needT));
+  MOE_TRY(check_ptr(dy, "dy", 16, needT));
+  MOE_TRY(check_ptr(fwd_ws, "fwd_ws", 256));
+  MOE_TRY(check_ptr(bws, "bws", 256));
+  MOE_TRY(check_ptr(wt->w_router, "w_router", 4));
+  MOE_TRY(check_ptr(wt->w_in, "w_in", 16));
+  MOE_TRY(check_ptr(wt->w_out, "w_out", 16));
+  MOE_TRY(check_ptr(wt->b_in, "b_in", 2, false));
+  if (glu) MOE_TRY(check_ptr(wt->w_gate, "w_gate", 16));
+  if (Fs > 0) {
+    MOE_TRY(check_ptr(wt->ws_in, "ws_in", 16));
+    MOE_TRY(check_ptr(wt->ws_out, "ws_out", 16));
+    MOE_TRY(check_ptr(wt->bs_in, "bs_in", 2, false));
+  }
+  MOE_TRY(check_ptr(fwd->idx, "fwd idx", 4, needT));
+  MOE_TRY(check_ptr(fwd->gates, "fwd gates", 4, needT));
+  MOE_TRY(check_ptr(fwd->slot, "fwd slot", 4, needT));
+  MOE_TRY(check_ptr(fwd->dropped, "fwd dropped", 1, needT));
+  MOE_TRY(check_ptr(fwd->counts, "fwd counts", 4));
+  MOE_TRY(check_ptr(fwd->logits, "fwd logits", 4, needT));
+  MOE_TRY(check_ptr(gr->dx, "dx", 16, needT));
+  MOE_TRY(check_ptr(gr->dw_router, "dw_router", 4));
+  MOE_TRY(check_ptr(gr->dlogit_bias, "dlogit_bias", 4, false));
+  MOE_TRY(check_ptr(gr->dw_in, "dw_in", 16));
+  MOE_TRY(check_ptr(gr->dw_out, "dw_out", 16));
+  if (glu) MOE_TRY(check_ptr(gr->dw_gate, "dw_gate", 16));
+  MOE_TRY(check_ptr(gr->db_in, "db_in", 2, false));
+  MOE_TRY(check_ptr(gr->db_out, "db_out", 2, false));
+  if (glu && gr->db_in) return fail(MOE_EINVAL, "SwiGLU experts have no b_in (db_in must be NULL)");
+  if (Fs > 0) {
+    MOE_TRY(check_ptr(gr->dws_in, "dws_in", 16));
+    MOE_TRY(check_ptr(gr->dws_out, "dws_out", 16));
+    MOE_TRY(check_ptr(gr->dbs_in, "dbs_in", 2, false));
+    MOE_TRY(check_ptr(gr->dbs_out, "dbs_out", 2, false));
+  }
+  MOE_TRY(check_ptr(gr->dgates, "dgates", 4, false));
+  MOE_TRY(check_ptr(gr->dlogits, "dlogits", 4, false));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Workspace w = carve(c, C, const_cast<void*>(fwd_ws));
+  BwdWorkspace b = carve_bwd(c, C, bws);
+  const int64_t T = c.T, d = c.d, F = c.d_ff, Cp = round8(C), Tp = round8(T);
+  const int E = c.E;
+  const int ga = glu ? 2 : 1;
+
+  BwdArgs a{};
+  a.idx = fwd->idx;
+  a.gates = fwd->gates;
+  a.slot = fwd->slot;
+  a.dropped = fwd->dropped;
+  a.counts = fwd->counts;
+  a.logits = fwd->logits;
+  a.dy = dy;
+  a.ye = w.ye;
+  a.dYe = b.dYe;
+  a.dgates = gr->dgates ? gr->dgates : b.dgates;
+  a.dz = gr->dlogits ? gr->dlogits : b.dz;
+  a.dA = b.dA;
+  a.dAs = Fs > 0 ? b.dAs : nullptr;
+  a.wrT = b.wrT;
+  a.dx = gr->dx;
+  a.T = T;
+  a.C = C;
+  a.d = c.d;
+  a.E = E;
+  a.k = c.k;
+  a.score = c.score;
+  a.renorm = resolved_renorm(c);
+  a.zero_fallback = c.dropped_output;
+  a.alpha_aux = alpha_aux;
+  a.alpha_z = alpha_z;
+
+  // gates and logits
+  MOE_TRY(hip_status(launch_combine_bwd(a, s), "combine backward"));
+  MOE_TRY(hip_status(launch_router_bwd(a, s), "router backward"));
+  if (gr->dlogit_bias) MOE_TRY(hip_status(launch_dz_colsum(a.dz, gr->dlogit_bias, T, E, s), "logit-bias gradient"));
+  // router weight: dW_r = x^T dz on the matrix cores, dz split into exact bf16
+  // planes, K = tokens split into S slabs summed in order
+  MOE_TRY(transpose("x transpose", static_cast<const bf16_t*>(x), b.xT, 1, T, d, Tp, 0, d, 0, Tp, nullptr, nullptr,
+                    0, s));
+  MOE_TRY(hip_status(launch_router_weight_prep(a.dz, b.planes, T, Tp, E, wt->w_router, b.wrT, c.d, s),
+                     "router planes"));
+  {
+    const int S = b.S;
+    const int64_t kc = Tp / S;
+    GemmArgs g{};
+    g.A = b.xT;
+    g.B0 = b.planes;
+    g.C = b.slabs;
+    g.rows_per_group = d;
+    g.groups = S;
+    g.N = 4 * E;
+    g.K = static_cast<int>(kc);
+    g.lda = Tp;
+    g.ldb = Tp;
+    g.a_gs = kc;
+    g.b_gs = kc;
+    g.c_gs = d * E;
+    g.act = 3;
+    if (T > 0) MOE_TRY(hip_status(launch_gemm(g, MOE_BF16, s), "router weight gradient"));
+    else MOE_TRY(hip_status(launch_zero(b.slabs, sizeof(float) * S * d * E, s), "router weight gradient"));
+    MOE_TRY(hip_status(launch_slab_sum(b.slabs, gr->dw_router, d * E, S, s), "router weight slabs"));
+  }
+
+  // routed experts (rows = kept per expert, gathered from x through row_token)
+  if (C > 0 && T > 0) {
+    const int32_t* kept = w.kept;
+    const bf16_t* W_in = static_cast<const bf16_t*>(wt->w_in);
+    if (glu) {
+      MOE_TRY(bgemm("recompute gate projection", x, 0, 0, w.row_token, T, wt->w_gate, 0, 0, nullptr, b.U, kept, C, E,
+                    static_cast<int>(F), c.d, s));
+      MOE_TRY(bgemm("recompute up projection", x, 0, 0, w.row_token, T, wt->w_in, 0, 0, nullptr, b.U2, kept, C, E,
+                    static_cast<int>(F), c.d, s));
+    } else {
+      MOE_TRY(bgemm("recompute pre-activation", x, 0, 0, w.row_token, T, wt->w_in, 0, 0, wt->b_in, b.U, kept, C, E,
+                    static_cast<int>(F), c.d, s));
+    }
+    // dH = dYe W_out: W_out [E, d, F] -> [E, F, d]
+    MOE_TRY(transpose("w_out transpose", static_cast<const bf16_t*>(wt->w_out), b.woT, E, d, F, d, d * F, F, F * d, d,
+                      nullptr, nullptr, 0, s));
+    MOE_TRY(bgemm("expert hidden gradient", b.dYe, 0, 0, nullptr, 0, b.woT, 0, 0, nullptr, b.dH, kept, C, E,
+                  static_cast<int>(F), c.d, s));
+    ActBwdArgs ab{};
+    ab.dH = b.dH;
+    ab.U = b.U;
+    ab.U2 = b.U2;
+    ab.dact = b.dact;
+    ab.valid = kept;
+    ab.rpg = C;
+    ab.groups = E;
+    ab.F = static_cast<int>(F);
+    MOE_TRY(hip_status(launch_act_bwd(ab, c.act, s), "activation backward"));
+    // dA = dact W_in (SwiGLU: [dGp | dUp] [W_gate; W_up]): W -> [E, d, ga*F]
+    if (glu) {
+      MOE_TRY(transpose("w_gate transpose", static_cast<const bf16_t*>(wt->w_gate), b.wiT, E, F, d, F, F * d, d,
+                        d * 2 * F, 2 * F, nullptr, nullptr, 0, s));
+      MOE_TRY(transpose("w_up transpose", W_in, b.wiT + F, E, F, d, F, F * d, d, d * 2 * F, 2 * F, nullptr, nullptr, 0,
+                        s));
+    } else {
+      MOE_TRY(transpose("w_in transpose", W_in, b.wiT, E, F, d, F, F * d, d, d * F, F, nullptr, nullptr, 0, s));
+    }
+    MOE_TRY(bgemm("expert input gradient", b.dact, 0, 0, nullptr, 0, b.wiT, 0, 0, nullptr, b.dA, kept, C, E, c.d,
+                  static_cast<int>(ga * F), s));
+    // dW_out = dYe^T H, dW_in = dact^T A: contraction over the kept rows,
+    // zero-padded to Cp
+    MOE_TRY(transpose("dYe transpose", b.dYe, b.dYeT, E, C, d, Cp, C * d, d, d * Cp, Cp, kept, nullptr, 0, s));
+    MOE_TRY(transpose("H transpose", static_cast<const bf16_t*>(w.h), b.HT, E, C, F, Cp, C * F, F, F * Cp, Cp, kept,
+                      nullptr, 0, s));
+    MOE_TRY(bgemm("w_out gradient", b.dYeT, 0, 0, nullptr, 0, b.HT, 0, 0, nullptr, gr->dw_out, nullptr, d, E,
+                  static_cast<int>(F), static_cast<int>(Cp), s));
+    MOE_TRY(transpose("activation-gradient transpose", b.dact, b.dactT, E, C, ga * F, Cp, C * ga * F, ga * F,
+                      ga * F * Cp, Cp, kept, nullptr, 0, s));
+    MOE_TRY(transpose("token rows transpose", static_cast<const bf16_t*>(x), b.AT, E, C, d, Cp, 0, d, d * Cp, Cp, kept,
+                      w.row_token, C, s));
+    if (glu) {
+      MOE_TRY(bgemm("w_gate gradient", b.dactT, Cp, 2 * F * Cp, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_gate, nullptr,
+                    F, E, c.d, static_cast<int>(Cp), s));
+      MOE_TRY(bgemm("w_up gradient", b.dactT + F * Cp, Cp, 2 * F * Cp, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_in,
+                    nullptr, F, E, c.d, static_cast<int>(Cp), s));
+    } else {
+      MOE_TRY(bgemm("w_in gradient", b.dactT, 0, 0, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_in, nullptr, F, E, c.d,
+                    static_cast<int>(Cp), s));
+    }
+    if (gr->db_out) MOE_TRY(hip_status(launch_colsum(b.dYe, gr->db_out, kept, E, C, d, 0, s), "b_out gradient"));
+    if (gr->db_in) MOE_TRY(hip_status(launch_colsum(b.dact, gr->db_in, kept, E, C, F, 0, s), "b_in gradient"));
+  } else {
+    // no expert row: every expert-weight gradient is zero
+    const size_t ew = sizeof(bf16_t) * E * F * d;
+    MOE_TRY(hip_status(launch_zero(gr->dw_in, ew, s), "zero gradients"));
+    MOE_TRY(hip_status(launch_zero(gr->dw_out, ew, s), "zero gradients"));
+    if (glu) MOE_TRY(hip_status(launch_zero(gr->dw_gate, ew, s), "zero gradients"));
+    if (gr->db_in) MOE_TRY(hip_status(launch_zero(gr->db_in, sizeof(bf16_t) * E * F, s), "zero gradients"));
+    if (gr->db_out) MOE_TRY(hip_status(launch_zero(gr->db_out, sizeof(bf16_t) * E * d, s), "zero gradients"));
+  }
+
+  // shared experts: every token, output gradient dy itself
+  if (Fs > 0 && T > 0) {
+    MOE_TRY(bgemm("recompute shared pre-activation", x, 0, 0, nullptr, 0, wt->ws_in, 0, 0, wt->bs_in, b.Us, nullptr, T,
+                  1, static_cast<int>(Fs), c.d, s));
+    MOE_TRY(transpose("ws_out transpose", static_cast<const bf16_t*>(wt->ws_out), b.wsoT, 1, d, Fs, d, 0, Fs, 0, d,
+                      nullptr, nullptr, 0, s));
+    MOE_TRY(bgemm("shared hidden gradient", dy, 0, 0, nullptr, 0, b.wsoT, 0, 0, nullptr, b.dHs, nullptr, T, 1,
+                  static_cast<int>(Fs), c.d, s));
+    ActBwdArgs ab{};
+    ab.dH = b.dHs;
+    ab.U = b.Us;
+    ab.dact = b.dUs;
+    ab.rpg = T;
+    ab.groups = 1;
+    ab.F = static_cast<int>(Fs);
+    MOE_TRY(hip_status(launch_act_bwd(ab, MOE_GELU, s), "shared activation backward"));
+    MOE_TRY(transpose("ws_in transpose", static_cast<const bf16_t*>(wt->ws_in), b.wsiT, 1, Fs, d, Fs, 0, d, 0, Fs,
+                      nullptr, nullptr, 0, s));
+    MOE_TRY(bgemm("shared input gradient", b.dUs, 0, 0, nullptr, 0, b.wsiT, 0, 0, nullptr, b.dAs, nullptr, T, 1, c.d,
+                  static_cast<int>(Fs), s));
+    MOE_TRY(transpose("dy transpose", static_cast<const bf16_t*>(dy), b.dyT, 1, T, d, Tp, 0, d, 0, Tp, nullptr, nullptr,
+                      0, s));
+    MOE_TRY(transpose("shared H transpose", static_cast<const bf16_t*>(w.hs), b.HsT, 1, T, Fs, Tp, 0, Fs, 0, Tp,
+                      nullptr, nullptr, 0, s));
+    MOE_TRY(bgemm("ws_out gradient", b.dyT, 0, 0, nullptr, 0, b.HsT, 0, 0, nullptr, gr->dws_out, nullptr, d, 1,
+                  static_cast<int>(Fs), static_cast<int>(Tp), s));
+    MOE_TRY(transpose("shared activation-gradient transpose", b.dUs, b.dUsT, 1, T, Fs, Tp, 0, Fs, 0, Tp, nullptr,
+                      nullptr, 0, s));
+    MOE_TRY(bgemm("ws_in gradient", b.dUsT, 0, 0, nullptr, 0, b.xT, 0, 0, nullptr, gr->dws_in, nullptr, Fs, 1, c.d,
+                  static_cast<int>(Tp), s));
+    if (gr->dbs_in) MOE_TRY(hip_status(launch_colsum(b.dUs, gr->dbs_in, nullptr, 1, T, Fs, 0, s), "bs_in gradient"));
+    if (gr->dbs_out)
+      MOE_TRY(hip_status(launch_colsum(static_cast<const bf16_t*>(dy), gr->dbs_out, nullptr, 1, T, d, 0, s),
+                         "bs_out gradient"));
+  }
+  if (Fs > 0 && T == 0) {
+    const size_t sw = sizeof(bf16_t) * Fs * d;
+    MOE_TRY(hip_status(launch_zero(gr->dws_in, sw, s), "zero gradients"));
+    MOE_TRY(hip_status(launch_zero(gr->dws_out, sw, s), "zero gradients"));
+    if (gr->dbs_in) MOE_TRY(hip_status(launch_zero(gr->dbs_in, sizeof(bf16_t) * Fs, s), "zero gradients"));
+    if (gr->dbs_out) MOE_TRY(hip_status(launch_zero(gr->dbs_out, sizeof(bf16_t) * d, s), "zero gradients"));
+  }
+  return hip_status(launch_dx(a, s), "input gradient");
 }
 
 }  // extern "C"

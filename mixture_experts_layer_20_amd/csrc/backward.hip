@@ -1,0 +1,517 @@
+// Backward pass of the token-choice layer: the kernels around the grouped
+// GEMM (which the backward pass reuses with transposed operands).
+//
+// Sources: "Lab 18 -- Mixture of experts" s.1 (the layer and its gates; with
+// raw top-1 gates the router learns through the gate value) and s.2 (the
+// balance loss reaches the router only through P_i, f being a count; the
+// z-loss); "Lab 01" "The traps" (f carries no gradient); "Mixture of
+// experts" lecture, training a router.
+//
+// L = <dy, y> + alpha_aux L_aux + alpha_z L_z.  With r = (t, j) a kept
+// choice of expert e in slot s and o_r = ye[e, s] its stored output:
+//   dgate_r = <dy_t, o_r>,   dYe[e, s] = gate_r dy_t           (combine_bwd)
+//   dz_t    = the gate, balance and z-loss terms               (router_bwd)
+//   dU      = dH * gelu'(U)   or   [dGp | dUp]                 (act_bwd)
+//   dx_t    = sum_j dA[e_tj, s_tj] + shared + fallback + dz_t W_r^T (dx)
+// Transposes put every operand in the grouped GEMM's K-contiguous layout:
+// weight gradients contract over the rows of an expert, zero-padded past its
+// kept count.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTr = 64;
+
+// ------------------------------------------------------------------ transpose
+// out[g][c][r] = in_row(g, r)[c] for r < valid_g, 0 for valid_g <= r < Rpad;
+// in_row(g, r) = in + g*in_gs + r*ld_in, or in + gather[g*gather_gs + r]*ld_in.
+__global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeArgs a) {
+  __shared__ bf16_t tile[kTr][kTr + 2];
+  const int g = blockIdx.z;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTr;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kTr;
+  const int lane = threadIdx.x & (kTr - 1);
+  const int row = threadIdx.x / kTr;                 // 0..3
+  const int64_t valid = a.valid ? min<int64_t>(a.valid[g], a.R) : a.R;
+#pragma unroll 4
+  for (int i = row; i < kTr; i += 4) {               // read along c
+    const int64_t r = r0 + i, c = c0 + lane;
+    bf16_t v = 0;
+    if (r < valid && c < a.Cc) {
+      const int64_t src = a.gather ? static_cast<int64_t>(a.gather[g * a.gather_gs + r]) * a.ld_in
+                                   : g * a.in_gs + r * a.ld_in;
+      v = a.in[src + c];
+    }
+    tile[i][lane] = v;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = row; i < kTr; i += 4) {               // write along r
+    const int64_t c = c0 + i, r = r0 + lane;
+    if (c < a.Cc && r < a.Rpad) a.out[g * a.out_gs + c * a.ld_out + r] = tile[lane][i];
+  }
+}
+
+// ------------------------------------------------------------------ combine
+// One wavefront per token; lanes j < k hold choice j.  For each kept choice:
+// dgate = <dy_t, ye row> (per-lane partial sums over 16-byte chunks, then a
+// fixed butterfly), and the gate-scaled dy_t goes to the choice's dYe row.
+__global__ __launch_bounds__(kThreads) void combine_bwd_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= a.T) return;
+  int64_t myrow = 0;
+  float mygate = 0.0f;
+  bool keep = false;
+  if (lane < a.k) {
+    const int64_t tk = t * a.k + lane;
+    const int e = a.idx[tk];
+    const int sl = a.slot[tk];
+    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < a.C;
+    myrow = static_cast<int64_t>(e) * a.C + sl;
+    mygate = a.gates[tk];
+  }
+  const uint64_t kept = __ballot(keep);
+  const int nvec = a.d / 8;
+  const uint4* dy = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dy) + t * a.d);
+  float mydg = 0.0f;
+  uint64_t rest = kept;
+  while (rest) {
+    const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+    rest &= rest - 1;
+    const int64_t row = __shfl(myrow, j, kWave);
+    const float g = __shfl(mygate, j, kWave);
+    const uint4* ye = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.ye) + row * a.d);
+    uint4* dye = reinterpret_cast<uint4*>(a.dYe + row * a.d);
+    float part = 0.0f;
+    for (int c = lane; c < nvec; c += kWave) {
+      const uint4 u = dy[c], v = ye[c];
+      const uint32_t uu[4] = {u.x, u.y, u.z, u.w}, vv[4] = {v.x, v.y, v.z, v.w};
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float d0 = __uint_as_float(uu[q] << 16), d1 = __uint_as_float(uu[q] & 0xFFFF0000u);
+        const float o0 = __uint_as_float(vv[q] << 16), o1 = __uint_as_float(vv[q] & 0xFFFF0000u);
+        part += d0 * o0;
+        part += d1 * o1;
+        w[q] = static_cast<uint32_t>(f32_to_bf16(g * d0)) | (static_cast<uint32_t>(f32_to_bf16(g * d1)) << 16);
+      }
+      dye[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    part = wave_sum(part);
+    if (lane == j) mydg = part;
+  }
+  if (lane < a.k) a.dgates[t * a.k + lane] = mydg;   // dropped choices: 0
+}
+
+// ------------------------------------------------------------------ router
+// One wavefront per token, lane l holding experts l, l + 64, ... (E <= 256).
+// Sums over experts go through wave_sum in float32 after max-shifting.
+__global__ __launch_bounds__(kThreads) void router_bwd_kernel(BwdArgs a) {
+  constexpr int kPer = 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= a.T) return;
+  const int E = a.E, k = a.k;
+  float z[kPer], dz[kPer], dgv[kPer];
+  bool sel[kPer];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int e = lane + kWave * m;
+    z[m] = e < E ? a.logits[t * E + e] : -__builtin_huge_valf();
+    dz[m] = 0.0f;
+    dgv[m] = 0.0f;
+    sel[m] = false;
+  }
+  // the gate gradient of each selected expert, placed at its expert
+  for (int j = 0; j < k; ++j) {
+    const int e = a.idx[t * k + j];
+    const float g = a.dgates[t * k + j];
+#pragma unroll
+    for (int m = 0; m < kPer; ++m)
+      if (e == lane + kWave * m) {
+        sel[m] = true;
+        dgv[m] = g;
+      }
+  }
+  float zmax = -__builtin_huge_valf();
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) zmax = fmaxf(zmax, z[m]);
+  zmax = wave_max(zmax);
+  float ex[kPer], sum = 0.0f;
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    ex[m] = lane + kWave * m < E ? __expf(z[m] - zmax) : 0.0f;
+    sum += ex[m];
+  }
+  sum = wave_sum(sum);
+  float p[kPer];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) p[m] = ex[m] / sum;
+  const bool ren = a.renorm != 0;
+  if (a.score == MOE_SOFTMAX) {
+    if (ren) {
+      // g = softmax over the selected logits (shifted by their own maximum):
+      // dz_sel = g (dg - <g, dg>)
+      float smax = -__builtin_huge_valf();
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) smax = sel[m] ? fmaxf(smax, z[m]) : smax;
+      smax = wave_max(smax);
+      float w[kPer], ssum = 0.0f;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        w[m] = sel[m] ? __expf(z[m] - smax) : 0.0f;
+        ssum += w[m];
+      }
+      ssum = wave_sum(ssum);
+      float gdg = 0.0f;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) gdg += sel[m] ? (w[m] / ssum) * dgv[m] : 0.0f;
+      gdg = wave_sum(gdg);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m)
+        if (sel[m]) dz[m] = (w[m] / ssum) * (dgv[m] - gdg);
+    } else {
+      // g = p_sel: dz = p (dp - <p, dp>), dp = dg at the selected experts
+      float pdp = 0.0f;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) pdp += sel[m] ? p[m] * dgv[m] : 0.0f;
+      pdp = wave_sum(pdp);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m)
+        if (lane + kWave * m < E) dz[m] = p[m] * ((sel[m] ? dgv[m] : 0.0f) - pdp);
+    }
+  } else {
+    // sigmoid scores in the log domain (as the forward pass forms them):
+    // ls = log s(z), and 1 - s(z) = s(-z), both without cancellation
+    float ls[kPer], sm[kPer];
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      ls[m] = z[m] < 0.0f ? z[m] - log1pf(__expf(z[m])) : -log1pf(__expf(-z[m]));
+      sm[m] = 1.0f / (1.0f + __expf(z[m]));
+    }
+    if (ren) {
+      // g = softmax over the selected log s: dz_sel = g (dg - <g, dg>) s(-z)
+      float lmax = -__builtin_huge_valf();
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) lmax = sel[m] ? fmaxf(lmax, ls[m]) : lmax;
+      lmax = wave_max(lmax);
+      float w[kPer], ssum = 0.0f;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        w[m] = sel[m] ? __expf(ls[m] - lmax) : 0.0f;
+        ssum += w[m];
+      }
+      ssum = wave_sum(ssum);
+      float gdg = 0.0f;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) gdg += sel[m] ? (w[m] / ssum) * dgv[m] : 0.0f;
+      gdg = wave_sum(gdg);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m)
+        if (sel[m]) dz[m] = (w[m] / ssum) * (dgv[m] - gdg) * sm[m];
+    } else {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m)
+        if (sel[m]) dz[m] = dgv[m] * __expf(ls[m]) * sm[m];
+    }
+  }
+  // balance loss: dL/dp_ti = alpha E f_i / T, f_i = count_i / (T k)
+  if (a.alpha_aux != 0.0f) {
+    float v[kPer], q[kPer], qv = 0.0f;
+    if (a.score == MOE_SOFTMAX) {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) q[m] = p[m];
+    } else {
+      // q = the sigmoid scores normalised over all E: softmax of log s(z)
+      float lmax = -__builtin_huge_valf(), ssum = 0.0f;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        q[m] = z[m] < 0.0f ? z[m] - log1pf(__expf(z[m])) : -log1pf(__expf(-z[m]));
+        if (lane + kWave * m < E) lmax = fmaxf(lmax, q[m]);
+      }
+      lmax = wave_max(lmax);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        q[m] = lane + kWave * m < E ? __expf(q[m] - lmax) : 0.0f;
+        ssum += q[m];
+      }
+      ssum = wave_sum(ssum);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) q[m] /= ssum;
+    }
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int e = lane + kWave * m;
+      v[m] = e < E ? static_cast<float>(static_cast<double>(a.alpha_aux) * E *
+                                        (static_cast<double>(a.counts[e]) / (static_cast<double>(a.T) * k)) /
+                                        static_cast<double>(a.T))
+                   : 0.0f;
+      qv += q[m] * v[m];
+    }
+    qv = wave_sum(qv);
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      if (lane + kWave * m >= E) continue;
+      float term = q[m] * (v[m] - qv);
+      if (a.score != MOE_SOFTMAX) term *= 1.0f / (1.0f + __expf(z[m]));          // s(-z)
+      dz[m] += term;
+    }
+  }
+  // z-loss: dL_z/dz_ti = 2 LSE_t p_ti / T
+  if (a.alpha_z != 0.0f) {
+    const float lse = zmax + __logf(sum);
+    const float c = 2.0f * a.alpha_z * lse / static_cast<float>(a.T);
+#pragma unroll
+    for (int m = 0; m < kPer; ++m)
+      if (lane + kWave * m < E) dz[m] += c * p[m];
+  }
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) {
+    const int e = lane + kWave * m;
+    if (e < E) a.dz[t * E + e] = dz[m];
+  }
+}
+
+// ------------------------------------------------------------------ activations
+// GELU:   dU = dH * (Phi(U) + U phi(U))                      -> dact [rows, F]
+// SwiGLU: dGp = dH * Up * s (1 + Gp (1 - s)), dUp = dH * Gp s -> dact [rows, 2F]
+// over the first valid_g rows of each group (rows_per_group apart).
+template <int ACT>
+__global__ __launch_bounds__(kThreads) void act_bwd_kernel(ActBwdArgs a) {
+  const int g = blockIdx.y;
+  const int64_t valid = a.valid ? min<int64_t>(a.valid[g], a.rpg) : a.rpg;
+  const int64_t n = valid * a.F;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int64_t r = i / a.F, f = i % a.F;
+    const int64_t row = static_cast<int64_t>(g) * a.rpg + r;
+    const float dh = bf16_to_f32(a.dH[row * a.F + f]);
+    if (ACT == 1) {
+      const float u = bf16_to_f32(a.U[row * a.F + f]);
+      const float grad = 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * __expf(-0.5f * u * u) * 0.39894228040143268f;
+      a.dact[row * a.F + f] = f32_to_bf16(dh * grad);
+    } else {
+      const float gp = bf16_to_f32(a.U[row * a.F + f]);
+      const float up = bf16_to_f32(a.U2[row * a.F + f]);
+      const float s = 1.0f / (1.0f + __expf(-gp));
+      a.dact[row * 2 * a.F + f] = f32_to_bf16(dh * up * s * (1.0f + gp * (1.0f - s)));
+      a.dact[row * 2 * a.F + a.F + f] = f32_to_bf16(dh * gp * s);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ column sums
+// out[g*Cc + c] = sum over the first valid_g rows r of in[g*rpg + r][c],
+// float32 in row order, stored in the storage type (or float32 with f32out).
+__global__ __launch_bounds__(kThreads) void colsum_kernel(const bf16_t* __restrict__ in, void* out,
+                                                          const int32_t* valid, int64_t rpg, int64_t Cc,
+                                                          int f32out) {
+  const int g = blockIdx.y;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (c >= Cc) return;
+  const int64_t nv = valid ? min<int64_t>(valid[g], rpg) : rpg;
+  const bf16_t* p = in + static_cast<int64_t>(g) * rpg * Cc + c;
+  float s = 0.0f;
+  for (int64_t r = 0; r < nv; ++r) s += bf16_to_f32(p[r * Cc]);
+  if (f32out) static_cast<float*>(out)[g * Cc + c] = s;
+  else static_cast<bf16_t*>(out)[g * Cc + c] = f32_to_bf16(s);
+}
+
+// float32 column sums of dz [T, E] in float64, one thread per expert
+__global__ __launch_bounds__(kThreads) void dz_colsum_kernel(const float* __restrict__ dz, float* out, int64_t T,
+                                                             int E) {
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= E) return;
+  double s = 0.0;
+  for (int64_t t = 0; t < T; ++t) s += dz[t * E + e];
+  out[e] = static_cast<float>(s);
+}
+
+// dz [T, E] float32 -> its exact bf16 planes [4E, Tp] (row 4e + p: plane p of
+// expert e over the tokens, row 4e + 3 and columns past T zero)
+__global__ __launch_bounds__(kThreads) void dz_planes_kernel(const float* __restrict__ dz, bf16_t* planes,
+                                                             int64_t T, int64_t Tp, int E) {
+  const int64_t n = static_cast<int64_t>(E) * Tp;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int e = static_cast<int>(i / Tp);
+    const int64_t t = i % Tp;
+    bf16_t hi = 0, mid = 0, lo = 0;
+    if (t < T) split3(dz[t * E + e], hi, mid, lo);
+    bf16_t* row = planes + static_cast<int64_t>(4 * e) * Tp + t;
+    row[0] = hi;
+    row[Tp] = mid;
+    row[2 * Tp] = lo;
+    row[3 * Tp] = 0;
+  }
+}
+
+// out[i] = sum over s of slabs[s][i], in slab order
+__global__ __launch_bounds__(kThreads) void slab_sum_kernel(const float* __restrict__ slabs, float* out, int64_t n,
+                                                            int S) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int q = 0; q < S; ++q) s += slabs[q * n + i];
+  out[i] = s;
+}
+
+// w_r [d, E] float32 -> [E, d]
+__global__ __launch_bounds__(kThreads) void wr_transpose_kernel(const float* __restrict__ w, float* wt, int d, int E) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= static_cast<int64_t>(d) * E) return;
+  const int e = static_cast<int>(i / d), c = static_cast<int>(i % d);
+  wt[i] = w[static_cast<int64_t>(c) * E + e];
+}
+
+// ------------------------------------------------------------------ dx
+// One wavefront per token, 8 columns per lane per round:
+//   dx_t = sum_j kept dA[row_j] (j order) + dAs_t (shared) | dy_t (fallback,
+//          residual) + sum_e dz_te W_r[:, e]
+__global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= a.T) return;
+  int64_t myrow = 0;
+  bool keep = false;
+  if (lane < a.k) {
+    const int64_t tk = t * a.k + lane;
+    const int e = a.idx[tk];
+    const int sl = a.slot[tk];
+    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < a.C;
+    myrow = static_cast<int64_t>(e) * a.C + sl;
+  }
+  const uint64_t kept = __ballot(keep);
+  float dzv[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int e = lane + kWave * m;
+    dzv[m] = e < a.E ? a.dz[t * a.E + e] : 0.0f;
+  }
+  const int nvec = a.d / 8;
+  const bool fallback = kept == 0 && a.dAs == nullptr && !a.zero_fallback;
+  for (int c = lane; c < nvec; c += kWave) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    auto add_row = [&](const bf16_t* base) {
+      const uint4 u = reinterpret_cast<const uint4*>(base)[c];
+      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __uint_as_float(uu[q] << 16);
+        acc[2 * q + 1] += __uint_as_float(uu[q] & 0xFFFF0000u);
+      }
+    };
+    uint64_t rest = kept;
+    while (rest) {
+      const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+      rest &= rest - 1;
+      add_row(a.dA + __shfl(myrow, j, kWave) * a.d);
+    }
+    if (a.dAs) add_row(a.dAs + t * a.d);
+    else if (fallback) add_row(static_cast<const bf16_t*>(a.dy) + t * a.d);
+    for (int e = 0; e < a.E; ++e) {
+      const float g = __shfl(dzv[e / kWave], e % kWave, kWave);
+      const float4* w = reinterpret_cast<const float4*>(a.wrT + static_cast<int64_t>(e) * a.d + c * 8);
+      const float4 w0 = w[0], w1 = w[1];
+      acc[0] += g * w0.x; acc[1] += g * w0.y; acc[2] += g * w0.z; acc[3] += g * w0.w;
+      acc[4] += g * w1.x; acc[5] += g * w1.y; acc[6] += g * w1.z; acc[7] += g * w1.w;
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = static_cast<uint32_t>(f32_to_bf16(acc[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * q + 1])) << 16);
+    reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.dx) + t * a.d)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void zero_kernel(uint16_t* p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    p[i] = 0;
+}
+
+}  // namespace
+
+// Zero `bytes` (even) bytes with a kernel (no memset node in a captured graph).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(bytes / 2);
+  if (n == 0) return hipSuccess;
+  zero_kernel<<<static_cast<unsigned>(std::min<int64_t>(4096, (n + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
+      static_cast<uint16_t*>(p), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
+  if (a.G == 0 || a.Rpad == 0 || a.Cc == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((a.Rpad + kTr - 1) / kTr), static_cast<unsigned>((a.Cc + kTr - 1) / kTr),
+                  static_cast<unsigned>(a.G));
+  transpose_kernel<<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const BwdArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>((a.T + 3) / 4);
+  combine_bwd_kernel<<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const BwdArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>((a.T + 3) / 4);
+  router_bwd_kernel<<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_act_bwd(const ActBwdArgs& a, int act, hipStream_t s) {
+  if (a.groups == 0 || a.rpg == 0) return hipSuccess;
+  const int64_t per = a.rpg * a.F;
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>((per + kThreads - 1) / kThreads, 4096)),
+                  static_cast<unsigned>(a.groups));
+  if (act == MOE_GELU) act_bwd_kernel<1><<<grid, kThreads, 0, s>>>(a);
+  else act_bwd_kernel<2><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const bf16_t* in, void* out, const int32_t* valid, int groups, int64_t rpg, int64_t Cc,
+                         int f32out, hipStream_t s) {
+  if (groups == 0 || Cc == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((Cc + kThreads - 1) / kThreads), static_cast<unsigned>(groups));
+  colsum_kernel<<<grid, kThreads, 0, s>>>(in, out, valid, rpg, Cc, f32out);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_weight_prep(const float* dz, bf16_t* planes, int64_t T, int64_t Tp, int E,
+                                     const float* w_router, float* wrT, int d, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(E) * Tp;
+  if (n > 0)
+    dz_planes_kernel<<<static_cast<unsigned>(std::min<int64_t>(4096, (n + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
+        dz, planes, T, Tp, E);
+  const int64_t m = static_cast<int64_t>(d) * E;
+  wr_transpose_kernel<<<static_cast<unsigned>((m + kThreads - 1) / kThreads), kThreads, 0, s>>>(w_router, wrT, d, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_dz_colsum(const float* dz, float* out, int64_t T, int E, hipStream_t s) {
+  dz_colsum_kernel<<<static_cast<unsigned>((E + kThreads - 1) / kThreads), kThreads, 0, s>>>(dz, out, T, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_slab_sum(const float* slabs, float* out, int64_t n, int S, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  slab_sum_kernel<<<static_cast<unsigned>((n + kThreads - 1) / kThreads), kThreads, 0, s>>>(slabs, out, n, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx(const BwdArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  dx_kernel<<<static_cast<unsigned>((a.T + 3) / 4), kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -25,6 +25,17 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// The exact three-way bf16 split of a float32 value: hi + mid + lo == v
+// (8 + 8 + 8 significant bits cover float32's 24), so each product of a bf16
+// value with a plane is exact in the bf16 matrix cores.
+__device__ __forceinline__ void split3(float v, bf16_t& hi, bf16_t& mid, bf16_t& lo) {
+#pragma clang fp contract(off)
+  hi = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+}
+
 template <typename T> struct Storage;
 template <> struct Storage<float> {
   __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
@@ -219,6 +230,49 @@ struct ScoreArgs {
   int E, k, n_tiles;
 };
 
+// Backward pass (token choice, capacity mode, bf16 storage)
+struct TransposeArgs {
+  const bf16_t* in;           // rows of ld_in elements
+  bf16_t* out;                // out[g*out_gs + c*ld_out + r]
+  const int32_t* gather;      // [G*gather_gs] source row of (g, r) | null
+  const int32_t* valid;       // [G] rows read per group (the rest zero) | null: R
+  int64_t R, Cc, Rpad;        // rows and columns in, rows written (>= R)
+  int64_t in_gs, ld_in, gather_gs, out_gs, ld_out;
+  int G;
+};
+
+struct BwdArgs {
+  const int32_t* idx;         // [T,k]
+  const float* gates;         // [T,k]
+  const int32_t* slot;        // [T,k]
+  const uint8_t* dropped;     // [T,k]
+  const int32_t* counts;      // [E] choices per expert (before capacity)
+  const float* logits;        // [T,E]
+  const void* dy;             // [T,d]
+  const void* ye;             // [E,C,d] the forward's expert outputs
+  bf16_t* dYe;                // [E,C,d]
+  float* dgates;              // [T,k]
+  float* dz;                  // [T,E]
+  const bf16_t* dA;           // [E,C,d] input gradients of the routed experts
+  const bf16_t* dAs;          // [T,d] of the shared experts | null
+  const float* wrT;           // [E,d] the router weight, transposed
+  void* dx;                   // [T,d]
+  int64_t T, C;
+  int d, E, k;
+  int score, renorm, zero_fallback;
+  float alpha_aux, alpha_z;
+};
+
+struct ActBwdArgs {
+  const bf16_t* dH;           // [groups*rpg, F]
+  const bf16_t* U;            // GELU: pre-activation; SwiGLU: gate projection
+  const bf16_t* U2;           // SwiGLU: up projection | null
+  bf16_t* dact;               // [groups*rpg, F] (GELU) or [groups*rpg, 2F] (SwiGLU)
+  const int32_t* valid;       // [groups] | null
+  int64_t rpg;
+  int groups, F;
+};
+
 struct SeqLossArgs {
   const float* probs;         // [T,E]
   const int32_t* idx;         // [T,k]
@@ -239,6 +293,18 @@ hipError_t launch_select_top(const EcArgs& a, hipStream_t s);
 hipError_t launch_score_priority(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_gather_rows(const void* x, void* xe, const int32_t* row_token, const int32_t* kept, int64_t C,
                               int E, int row_bytes, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_combine_bwd(const BwdArgs& a, hipStream_t s);
+hipError_t launch_router_bwd(const BwdArgs& a, hipStream_t s);
+hipError_t launch_act_bwd(const ActBwdArgs& a, int act, hipStream_t s);
+hipError_t launch_colsum(const bf16_t* in, void* out, const int32_t* valid, int groups, int64_t rpg, int64_t Cc,
+                         int f32out, hipStream_t s);
+hipError_t launch_router_weight_prep(const float* dz, bf16_t* planes, int64_t T, int64_t Tp, int E,
+                                     const float* w_router, float* wrT, int d, hipStream_t s);
+hipError_t launch_dz_colsum(const float* dz, float* out, int64_t T, int E, hipStream_t s);
+hipError_t launch_slab_sum(const float* slabs, float* out, int64_t n, int S, hipStream_t s);
+hipError_t launch_dx(const BwdArgs& a, hipStream_t s);
 hipError_t launch_seq_loss(const SeqLossArgs& a, hipStream_t s);
 hipError_t launch_bias_update(const int32_t* counts, float* select_bias, int E, int64_t Tk, float gamma,
                               hipStream_t s);

@@ -398,15 +398,7 @@ __global__ __launch_bounds__(kThreads) void route_from_logits_kernel(RouteArgs a
 // transpose with float32 accumulation; its router epilogue adds each group
 // of four columns (p = 0, 1, 2, 3 in that order) into logit e.  The
 // per-token epilogue then runs on those logits as for routing from logits.
-// The exact three-way bf16 split of a float32 weight: hi + mid + lo == v
-// (8 + 8 + 8 significant bits cover float32's 24).
-__device__ __forceinline__ void split3(float v, bf16_t& hi, bf16_t& mid, bf16_t& lo) {
-#pragma clang fp contract(off)
-  hi = f32_to_bf16(v);
-  const float r1 = v - bf16_to_f32(hi);
-  mid = f32_to_bf16(r1);
-  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-}
+// (split3, the exact three-way split, is in common.hpp.)
 
 __global__ __launch_bounds__(kThreads) void split_router_kernel(const float* w, bf16_t* wp, int d, int E) {
   const int64_t n = static_cast<int64_t>(E) * d;

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     for n in ('moe_route', 'moe_dispatch', 'moe_expert_ffn', 'moe_combine', 'moe_forward',
               'moe_aux_losses', 'moe_validate', 'moe_workspace_bytes', 'moe_last_error',
               'moe_expert_ffn_packed', 'moe_expert_choice', 'moe_combine_expert_choice',
-              'moe_dispatch_by_score'):
+              'moe_dispatch_by_score', 'moe_backward', 'moe_backward_workspace_bytes'):
         assert n in names
 
 
@@ -265,3 +265,21 @@ def test_score_priority_configuration(moe):
     assert moe.moe_workspace_bytes(sc) > moe.moe_workspace_bytes(cfg(moe))
     assert moe.moe_workspace_bytes(cfg(moe, priority='score', dropless=True)) == \
         moe.moe_workspace_bytes(cfg(moe, dropless=True))
+
+
+def test_backward_configuration(moe):
+    lib = moe._lib
+    bf = dict(dtype='bf16')
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, **bf))) > 0
+    # built for bf16 token choice with a capacity
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe))) == 0             # f32
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, dropless=True, **bf))) == 0
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, routing='expert', **bf))) == 0
+    c = cfg(moe)
+    g = moe.moe_grads()
+    assert lib.moe_backward(ctypes.byref(c), None, None, None, None, None, 0.0, 0.0, ctypes.byref(g), None,
+                            None) == moe.MOE_EUNSUPPORTED
+    c = cfg(moe, **bf)
+    assert lib.moe_backward(ctypes.byref(c), None, None, None, None, None, 0.0, 0.0, ctypes.byref(g), None,
+                            None) == moe.MOE_EINVAL
+    assert b'NULL' in lib.moe_last_error()

@@ -1,0 +1,156 @@
+"""Parity of the HIP backward pass (through the C ABI) with the oracle's
+chain rule, on an MI355X.
+
+The GPU forward pass runs first (its outputs and workspace feed the backward
+pass); the oracle runs its own forward pass on the same inputs and its
+backward pass on the same dy.  Routing must come out identical on both sides
+for the comparison to be meaningful (the layers below have no near ties).
+Bar: every gradient within 2e-2 max-relative of the oracle's (the bf16 bar:
+the gradients flow through bf16-stored activations, expert outputs and
+gradient rows, each a rounding the oracle does not make).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import backward as B
+from oracle import moe as O
+
+from gpu_helpers import DEV, device_layer, f64_of, maxrel, np_of
+
+pytestmark = pytest.mark.gpu
+
+ALPHA_AUX, ALPHA_Z = 0.37, 0.11
+TOL = 2e-2
+
+
+@pytest.fixture(scope='module')
+def moe():
+    assert torch.cuda.is_available(), 'GPU tests need a GPU'
+    import mixture_experts_layer_20_amd as m
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _layer(moe, w, seed):
+    inp, ex, sh, dev = device_layer(w, moe)
+    rng = np.random.default_rng(seed)
+    if w.act == 'gelu':                                   # non-zero biases, bf16-exact
+        for kk in ('b_in', 'b_out'):
+            bits = synth.bf16_bits((0.1 * rng.standard_normal(ex[kk].shape)).astype(np.float32))
+            ex[kk] = bits
+            dev[kk] = synth.to_torch(bits, DEV)
+    if sh is not None:
+        bits = synth.bf16_bits((0.1 * rng.standard_normal(sh['b_in'].shape)).astype(np.float32))
+        sh['b_in'] = bits
+        dev['bs_in'] = synth.to_torch(np.concatenate(list(bits)), DEV)
+    dy = synth.bf16_bits(rng.standard_normal((w.T, w.d)).astype(np.float32))
+    return inp, ex, sh, dev, dy
+
+
+def _run(moe, w, seed=0, **over):
+    inp, ex, sh, dev, dy = _layer(moe, w, seed)
+    cfg = moe.config_from_workload(w, **over)
+    out = moe.alloc_outputs(cfg, DEV, logits=True)
+    ws = moe.workspace(cfg, DEV)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    moe.moe_forward(cfg, weights, dev['x'], out, ws)
+    E, F, d, T = w.E, w.d_ff, w.d, w.T
+    bf = torch.bfloat16
+    grads = dict(dx=torch.empty(T, d, dtype=bf, device=DEV), dw_router=torch.empty(d, E, device=DEV),
+                 dlogit_bias=torch.empty(E, device=DEV), dw_in=torch.empty(E, F, d, dtype=bf, device=DEV),
+                 dw_out=torch.empty(E, d, F, dtype=bf, device=DEV), db_out=None, db_in=None,
+                 dgates=torch.empty(T, w.k, device=DEV), dlogits=torch.empty(T, E, device=DEV))
+    if w.act == 'swiglu':
+        grads['dw_gate'] = torch.empty(E, F, d, dtype=bf, device=DEV)
+    else:
+        grads['db_in'] = torch.empty(E, F, dtype=bf, device=DEV)
+        grads['db_out'] = torch.empty(E, d, dtype=bf, device=DEV)
+    fs = w.n_shared * w.d_ff_shared
+    if fs:
+        grads.update(dws_in=torch.empty(fs, d, dtype=bf, device=DEV), dws_out=torch.empty(d, fs, dtype=bf, device=DEV),
+                     dbs_in=torch.empty(fs, dtype=bf, device=DEV), dbs_out=torch.empty(d, dtype=bf, device=DEV))
+    bws = moe.backward_workspace(cfg, DEV)
+    dy_t = synth.to_torch(dy, DEV)
+    moe.moe_backward(cfg, weights, dev['x'], out, ws, dy_t, grads, bws, ALPHA_AUX, ALPHA_Z)
+    torch.cuda.synchronize()
+    # the oracle on the same inputs
+    dout = 'zero' if over.get('dropped_output') == 'zero' else 'residual'
+    ov = over.get('capacity_override', 0)
+    fwd = O.moe_forward(w, inp, ex, sh, capacity_override=ov, dropped_output=dout)
+    assert (np_of(out['idx']) == fwd['idx']).all(), 'routing differs from the oracle: pick another seed'
+    np.testing.assert_array_equal(np_of(out['slot']), fwd['slot'])
+    ref = B.moe_backward(w, inp, ex, sh, fwd, synth.as_f32(dy), ALPHA_AUX, ALPHA_Z, dropped_output=dout)
+    return grads, ref, fwd
+
+
+def _check(name, got, ref):
+    err = maxrel(got, ref)
+    say(f'  {name}: max-rel {err:.2e}')
+    assert err <= TOL, (name, err)
+
+
+def _compare(w, grads, ref):
+    _check('dgates', np_of(grads['dgates']), ref['dgates'])
+    _check('dlogits', np_of(grads['dlogits']), ref['dz'])
+    _check('dx', f64_of(grads['dx']), ref['dx'])
+    _check('dw_router', np_of(grads['dw_router']), ref['dw_router'])
+    _check('dlogit_bias', np_of(grads['dlogit_bias']), ref['dlogit_bias'])
+    ex = ref['experts']
+    if w.act == 'swiglu':
+        _check('dw_gate', f64_of(grads['dw_gate']), np.stack([g['w_gate'] for g in ex]))
+        _check('dw_up', f64_of(grads['dw_in']), np.stack([g['w_up'] for g in ex]))
+    else:
+        _check('dw_in', f64_of(grads['dw_in']), np.stack([g['w_in'] for g in ex]))
+        _check('db_in', f64_of(grads['db_in']), np.stack([g['b_in'] for g in ex]))
+        _check('db_out', f64_of(grads['db_out']), np.stack([g['b_out'] for g in ex]))
+    _check('dw_out', f64_of(grads['dw_out']), np.stack([g['w_out'] for g in ex]))
+    if w.n_shared:
+        sg = ref['shared']
+        _check('dws_in', f64_of(grads['dws_in']), np.concatenate([g['w_in'] for g in sg], 0))
+        _check('dws_out', f64_of(grads['dws_out']), np.concatenate([g['w_out'] for g in sg], 1))
+        _check('dbs_in', f64_of(grads['dbs_in']), np.concatenate([g['b_in'] for g in sg]))
+        _check('dbs_out', f64_of(grads['dbs_out']), sg[0]['b_out'])
+
+
+BWD_CASES = [
+    ('gelu_renorm_drops', synth.Workload('ba', T=700, d=256, E=8, k=2, d_ff=384, act='gelu', score='softmax',
+                                         renormalize=-1, cf=1.0, dtype='bf16', seed=61), {}),
+    ('swiglu_renorm', synth.Workload('bb', T=600, d=256, E=4, k=2, d_ff=512, act='swiglu', score='softmax',
+                                     renormalize=-1, cf=1.25, dtype='bf16', seed=62), {}),
+    ('sigmoid_shared', synth.Workload('bc', T=500, d=128, E=16, k=3, d_ff=128, act='gelu', score='sigmoid',
+                                      renormalize=1, cf=1.0, dtype='bf16', seed=63, select_bias=True, n_shared=2,
+                                      d_ff_shared=128), {}),
+    ('top1_raw_fallback', synth.Workload('bd', T=1000, d=128, E=16, k=1, d_ff=256, act='gelu', score='softmax',
+                                         renormalize=-1, cf=1.0, dtype='bf16', seed=64,
+                                         logit_bias='first_two_plus2'), {}),
+    ('zero_fallback_swiglu', synth.Workload('be', T=300, d=128, E=4, k=2, d_ff=256, act='swiglu',
+                                            score='softmax', renormalize=-1, cf=1.0, dtype='bf16', seed=65),
+     dict(capacity_override=40, dropped_output='zero')),
+    ('sigmoid_raw_ragged', synth.Workload('bf', T=333, d=64, E=8, k=2, d_ff=72, act='gelu', score='sigmoid',
+                                          renormalize=0, cf=1.25, dtype='bf16', seed=66), {}),
+]
+
+
+@pytest.mark.parametrize('case', BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_backward_parity(moe, case):
+    name, w, over = case
+    say('backward', name)
+    grads, ref, fwd = _run(moe, w, **over)
+    if name in ('gelu_renorm_drops', 'top1_raw_fallback', 'zero_fallback_swiglu'):
+        assert fwd['dropped'].any()
+    _compare(w, grads, ref)
+    if name == 'top1_raw_fallback':
+        # fully dropped tokens pass dy through (plus their router term)
+        assert (~(~fwd['dropped']).any(axis=1)).any()
+
+
+def test_backward_empty_batch(moe):
+    w = synth.Workload('bz', T=1, d=64, E=4, k=2, d_ff=64, act='gelu', score='softmax', renormalize=-1, cf=1.0,
+                       dtype='bf16', seed=67)
+    grads, ref, fwd = _run(moe, w)
+    _compare(w, grads, ref)
