@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--phase-reps R] [--dropless]
-                    [--routing token|expert] [--priority rank|token|score]
+                    [--routing token|expert] [--priority rank|token|score] [--backward]
 
 A step is one whole forward pass of the layer (router, capacity, dispatch,
 routed and shared expert FFNs, combine, losses) over one batch of T synthetic
@@ -54,6 +54,8 @@ def parse():
     p.add_argument('--priority', choices=('rank', 'token', 'score'), default='rank',
                    help='capacity queue order: rank-major (GShard), token-major, or by router score '
                         '(batch-prioritised)')
+    p.add_argument('--backward', action='store_true',
+                   help='also time moe_backward (the gradients of the same layer) as a phase')
     p.add_argument('--copy-calibration', action='store_true',
                    help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
     return p.parse_args()
@@ -269,6 +271,9 @@ def main():
                                     f'{rec["write_bytes_per_pair"]:.4g}, counters scaled by a plain copy kernel '
                                     f'(factors {rec["fetch_factor"]:.3f} / {rec["write_factor"]:.3f})')
 
+    if args.backward:
+        phases['backward'] = time_backward(moe, cfg, w, weights, x, args, ffn_flops, peak, log)
+
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -296,6 +301,46 @@ def main():
                        for kk, v in phases.items()},
             'cpu_baseline': cpu}
     print(json.dumps(line), flush=True)
+
+
+def time_backward(moe, cfg, w, weights, x, args, ffn_flops, peak, log):
+    """moe_backward of the layer after one moe_forward, timed over --steps
+    calls with HIP events on the library's stream.  Algorithmic work: twice
+    the forward's expert matmul flops (input and weight gradients; the
+    backward pass also recomputes the expert pre-activations, which is not
+    counted)."""
+    import torch
+    T, d, E, F, k = w.T, w.d, w.E, w.d_ff, w.k
+    out = moe.alloc_outputs(cfg, 'cuda', logits=True)
+    ws = moe.workspace(cfg, 'cuda')
+    moe.moe_forward(cfg, weights, x, out, ws)
+    bf = moe.torch_dtype(cfg)
+    grads = dict(dx=torch.empty(T, d, dtype=bf, device='cuda'), dw_router=torch.empty(d, E, device='cuda'),
+                 dw_in=torch.empty(E, F, d, dtype=bf, device='cuda'), dw_out=torch.empty(E, d, F, dtype=bf, device='cuda'))
+    if w.act == 'swiglu':
+        grads['dw_gate'] = torch.empty(E, F, d, dtype=bf, device='cuda')
+    fs = w.n_shared * w.d_ff_shared
+    if fs:
+        grads.update(dws_in=torch.empty(fs, d, dtype=bf, device='cuda'),
+                     dws_out=torch.empty(d, fs, dtype=bf, device='cuda'))
+    bws = moe.backward_workspace(cfg, 'cuda')
+    dy = torch.randn(T, d, device='cuda', generator=torch.Generator('cuda').manual_seed(5)).to(bf)
+    for _ in range(max(1, args.warmup)):
+        moe.moe_backward(cfg, weights, x, out, ws, dy, grads, bws, 0.01, 0.001)
+    torch.cuda.synchronize()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        moe.moe_backward(cfg, weights, x, out, ws, dy, grads, bws, 0.01, 0.001)
+    z.record()
+    z.synchronize()
+    ms = a.elapsed_time(z) / max(1, args.steps)
+    flops = 2.0 * ffn_flops
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f'phase backward: ms={ms:.4g}, TFLOP/s={tf:.4g} (algorithmic 2x forward expert flops), '
+        f'workspace {bws.numel() / 2**30:.2f} GiB')
+    return {'ms': ms, 'TFLOP/s': tf, 'mfma_frac': tf / peak, 'flops': flops,
+            'workspace_bytes': int(bws.numel())}
 
 
 def cpu_baseline(w, sample_tokens, log, dropless=False, routing='token', priority='rank'):

@@ -80,7 +80,8 @@ def expert_ffn_backward(a, wts, act, dtype, d_out):
     raise ValueError(act)
 
 
-def router_backward(z, idx, dgates, score='softmax', renormalize=-1, f=None, alpha_aux=0.0, alpha_z=0.0):
+def router_backward(z, idx, dgates, score='softmax', renormalize=-1, f=None, alpha_aux=0.0, alpha_z=0.0,
+                    n_tokens=None):
     """d L / d z for the logits z [T,E] (float64 values), given the gradient of
     the k gates of every token (0 for dropped ones), plus the balance and
     z-loss terms.
@@ -90,15 +91,17 @@ def router_backward(z, idx, dgates, score='softmax', renormalize=-1, f=None, alp
     g = softmax(log sigma(z_sel)); raw sigmoid g = sigma(z_sel).
     Balance loss: dL_aux/dp_ti = E f_i / T, through p = softmax(z) (or the
     normalised sigmoid scores softmax(log sigma(z))).  z-loss:
-    dL_z/dz_ti = 2 LSE_t softmax(z)_ti / T.
+    dL_z/dz_ti = 2 LSE_t softmax(z)_ti / T.  ``n_tokens`` is the batch size T
+    when z holds only some of the batch's rows (both losses are batch means).
     """
     z = np.asarray(z, F64)
     idx = np.asarray(idx)
     dg = np.asarray(dgates, F64)
-    T, E = z.shape
+    rows, E = z.shape
+    T = rows if n_tokens is None else int(n_tokens)
     k = idx.shape[1]
     ren = (k > 1) if renormalize < 0 else bool(renormalize)
-    dz = np.zeros((T, E), F64)
+    dz = np.zeros((rows, E), F64)
     zs = np.take_along_axis(z, idx, axis=1)
     if score == 'softmax':
         if ren:
@@ -107,7 +110,7 @@ def router_backward(z, idx, dgates, score='softmax', renormalize=-1, f=None, alp
             np.put_along_axis(dz, idx, dzs, axis=1)
         else:
             p = softmax(z)
-            dp = np.zeros((T, E), F64)
+            dp = np.zeros((rows, E), F64)
             np.put_along_axis(dp, idx, dg, axis=1)
             dz += p * (dp - (p * dp).sum(axis=1, keepdims=True))
     elif score == 'sigmoid':

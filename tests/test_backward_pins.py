@@ -161,3 +161,20 @@ def test_activation_derivatives():
     np.testing.assert_allclose(B.gelu_grad(u), (O.gelu(u + h) - O.gelu(u - h)) / (2 * h), rtol=1e-7, atol=1e-9)
     np.testing.assert_allclose(B.silu_grad(u), (O.silu(u + h) - O.silu(u - h)) / (2 * h), rtol=1e-7, atol=1e-9)
     assert B.gelu_grad(np.array([0.0]))[0] == 0.5 and B.silu_grad(np.array([0.0]))[0] == 0.5
+
+
+@pytest.mark.parametrize('score,ren', [('softmax', -1), ('softmax', 0), ('sigmoid', 1), ('sigmoid', 0)])
+def test_router_backward_on_some_rows_equals_those_rows_of_the_batch(score, ren):
+    """The per-row terms depend only on the row, the batch size enters as 1/T:
+    evaluating a subset of rows with n_tokens = T gives those rows of the
+    whole-batch result."""
+    rng = np.random.default_rng(11)
+    T, E, k = 40, 6, 2
+    z = rng.standard_normal((T, E))
+    idx = np.argsort(-z, axis=1)[:, :k]
+    dg = rng.standard_normal((T, k))
+    f = rng.random(E)
+    full = B.router_backward(z, idx, dg, score, ren, f, 0.3, 0.2)
+    rows = np.array([0, 7, 8, 31, 39])
+    part = B.router_backward(z[rows], idx[rows], dg[rows], score, ren, f, 0.3, 0.2, n_tokens=T)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-14, atol=1e-17)

@@ -149,8 +149,75 @@ def test_backward_parity(moe, case):
         assert (~(~fwd['dropped']).any(axis=1)).any()
 
 
-def test_backward_empty_batch(moe):
+def test_backward_single_token(moe):
     w = synth.Workload('bz', T=1, d=64, E=4, k=2, d_ff=64, act='gelu', score='softmax', renormalize=-1, cf=1.0,
                        dtype='bf16', seed=67)
     grads, ref, fwd = _run(moe, w)
     _compare(w, grads, ref)
+
+
+def test_backward_mixtral_sampled(moe):
+    """The Mixtral-shaped layer at full size (T=8192, d=4096, E=8, k=2, SwiGLU
+    d_ff=14336): the gate, logit and input gradients of 48 sampled tokens, and
+    sampled rows/columns of the expert weight gradients (each a sum over all of
+    an expert's kept rows), against the oracle computed for just those."""
+    w = synth.WORKLOADS['mixtral_8x_top2']
+    say('backward mixtral sampled')
+    inp, ex, sh, dev = device_layer(w, moe)
+    rng = np.random.default_rng(9)
+    dy = synth.bf16_bits(rng.standard_normal((w.T, w.d)).astype(np.float32))
+    cfg = moe.config_from_workload(w)
+    out = moe.alloc_outputs(cfg, DEV, logits=True)
+    ws = moe.workspace(cfg, DEV)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    moe.moe_forward(cfg, weights, dev['x'], out, ws)
+    E, F, d, T, k = w.E, w.d_ff, w.d, w.T, w.k
+    bf = torch.bfloat16
+    grads = dict(dx=torch.empty(T, d, dtype=bf, device=DEV), dw_router=torch.empty(d, E, device=DEV),
+                 dw_in=torch.empty(E, F, d, dtype=bf, device=DEV), dw_gate=torch.empty(E, F, d, dtype=bf, device=DEV),
+                 dw_out=torch.empty(E, d, F, dtype=bf, device=DEV), dgates=torch.empty(T, k, device=DEV),
+                 dlogits=torch.empty(T, E, device=DEV))
+    bws = moe.backward_workspace(cfg, DEV)
+    moe.moe_backward(cfg, weights, dev['x'], out, ws, synth.to_torch(dy, DEV), grads, bws, ALPHA_AUX, ALPHA_Z)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(T, 48, replace=False))
+    get = (lambda e: {kk: v[e] for kk, v in ex.items()})
+    fwd = O.moe_forward(w, inp, get, None, rows=rows)
+    gi = np_of(out['idx'])
+    assert (gi == fwd['idx']).all() and (np_of(out['slot']) == fwd['slot']).all()
+    x = synth.as_f32(inp['x']).astype(np.float64)
+    dyf = synth.as_f32(dy).astype(np.float64)
+    kept = ~fwd['dropped']
+    wts = [{kk: synth.as_f32(v).astype(np.float64) for kk, v in get(e).items()} for e in range(E)]
+    # per sampled token: gate gradients, its experts' input gradients, dz and dx
+    dg = np.zeros((rows.size, k))
+    dxe = np.zeros((rows.size, d))
+    for i, t in enumerate(rows):
+        for j in range(k):
+            if not kept[t, j]:
+                continue
+            e = fwd['idx'][t, j]
+            _, o = O.expert_ffn(x[t][None], wts[e], 'swiglu', 'bf16')
+            dg[i, j] = float((dyf[t] * o[0]).sum())
+            da, _ = B.expert_ffn_backward(x[t][None], wts[e], 'swiglu', 'bf16', fwd['gates'][t, j] * dyf[t][None])
+            dxe[i] += da[0]
+    counts = np.bincount(fwd['idx'].ravel(), minlength=E)
+    dz = B.router_backward(fwd['logits'][rows], fwd['idx'][rows], dg, w.score, w.renormalize, counts / (T * k),
+                           ALPHA_AUX, ALPHA_Z, n_tokens=T)
+    dx = dxe + dz @ np.asarray(inp['w_router'], np.float64).T
+    _check('dgates (sampled tokens)', np_of(grads['dgates'])[rows], dg)
+    _check('dlogits (sampled tokens)', np_of(grads['dlogits'])[rows], dz)
+    _check('dx (sampled tokens)', f64_of(grads['dx'])[rows], dx)
+    # weight gradients: for expert e and hidden unit f, over all its kept rows
+    gw_up, gw_gate, gw_out = f64_of(grads['dw_in']), f64_of(grads['dw_gate']), f64_of(grads['dw_out'])
+    for e, f in [(0, 5), (3, 14335), (7, 7000)]:
+        t_e, j_e = np.nonzero((fwd['idx'] == e) & kept)
+        a = x[t_e]
+        gp = a @ wts[e]['w_gate'][f]
+        up = a @ wts[e]['w_up'][f]
+        h = O.round_store(O.silu(gp) * up, 'bf16')
+        d_out = fwd['gates'][t_e, j_e][:, None] * dyf[t_e]
+        dh = d_out @ wts[e]['w_out'][:, f]
+        _check(f'dw_out[{e}][:, {f}]', gw_out[e][:, f], d_out.T @ h)
+        _check(f'dw_up[{e}][{f}]', gw_up[e][f], (dh * O.silu(gp)) @ a)
+        _check(f'dw_gate[{e}][{f}]', gw_gate[e][f], (dh * up * B.silu_grad(gp)) @ a)
