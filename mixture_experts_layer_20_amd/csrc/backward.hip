@@ -27,30 +27,52 @@ constexpr int kTr = 64;
 // ------------------------------------------------------------------ transpose
 // out[g][c][r] = in_row(g, r)[c] for r < valid_g, 0 for valid_g <= r < Rpad;
 // in_row(g, r) = in + g*in_gs + r*ld_in, or in + gather[g*gather_gs + r]*ld_in.
-__global__ __launch_bounds__(kThreads) void transpose_kernel(TransposeArgs a) {
-  __shared__ bf16_t tile[kTr][kTr + 2];
+// 64 x 64 tiles through LDS with 16-byte accesses (8 bf16) on both sides:
+// every row length, stride and the padded row count are multiples of 8.  LDS
+// rows are 66 elements (33 words) apart, so the 8-row column reads of a
+// wavefront fall in distinct banks.
+constexpr int kTrPitch = kTr + 2;
+
+__global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs a) {
+  __shared__ uint32_t tile[kTr * kTrPitch / 2];
   const int g = blockIdx.z;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kTr;
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kTr;
-  const int lane = threadIdx.x & (kTr - 1);
-  const int row = threadIdx.x / kTr;                 // 0..3
+  const int tid = threadIdx.x;
   const int64_t valid = a.valid ? min<int64_t>(a.valid[g], a.R) : a.R;
-#pragma unroll 4
-  for (int i = row; i < kTr; i += 4) {               // read along c
-    const int64_t r = r0 + i, c = c0 + lane;
-    bf16_t v = 0;
-    if (r < valid && c < a.Cc) {
-      const int64_t src = a.gather ? static_cast<int64_t>(a.gather[g * a.gather_gs + r]) * a.ld_in
-                                   : g * a.in_gs + r * a.ld_in;
-      v = a.in[src + c];
+  {
+    const int tr = tid / 8, tc = tid % 8;            // 32 rows x 8 chunks per pass
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int i = tr + 32 * p;
+      const int64_t r = r0 + i, c = c0 + tc * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < valid && c < a.Cc) {
+        const int64_t src = a.gather ? static_cast<int64_t>(a.gather[g * a.gather_gs + r]) * a.ld_in
+                                     : g * a.in_gs + r * a.ld_in;
+        v = *reinterpret_cast<const uint4*>(a.in + src + c);
+      }
+      uint32_t* t = tile + (i * kTrPitch + tc * 8) / 2;
+      t[0] = v.x;
+      t[1] = v.y;
+      t[2] = v.z;
+      t[3] = v.w;
     }
-    tile[i][lane] = v;
   }
   __syncthreads();
-#pragma unroll 4
-  for (int i = row; i < kTr; i += 4) {               // write along r
-    const int64_t c = c0 + i, r = r0 + lane;
-    if (c < a.Cc && r < a.Rpad) a.out[g * a.out_gs + c * a.ld_out + r] = tile[lane][i];
+  const bf16_t* tl = reinterpret_cast<const bf16_t*>(tile);
+  const int wr = tid % 8, wc = tid / 8;              // 8 row chunks x 32 columns per pass
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int j = wc + 32 * p;
+    const int64_t c = c0 + j, r = r0 + wr * 8;
+    if (c >= a.Cc || r >= a.Rpad) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = static_cast<uint32_t>(tl[(wr * 8 + 2 * q) * kTrPitch + j]) |
+             (static_cast<uint32_t>(tl[(wr * 8 + 2 * q + 1) * kTrPitch + j]) << 16);
+    *reinterpret_cast<uint4*>(a.out + g * a.out_gs + c * a.ld_out + r) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -450,7 +472,11 @@ hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
   if (a.G == 0 || a.Rpad == 0 || a.Cc == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((a.Rpad + kTr - 1) / kTr), static_cast<unsigned>((a.Cc + kTr - 1) / kTr),
                   static_cast<unsigned>(a.G));
-  transpose_kernel<<<grid, kThreads, 0, s>>>(a);
+  const bool wide = a.Cc % 8 == 0 && a.Rpad % 8 == 0 && a.ld_in % 8 == 0 && a.ld_out % 8 == 0 && a.in_gs % 8 == 0 &&
+                    a.out_gs % 8 == 0 && reinterpret_cast<uintptr_t>(a.in) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(a.out) % 16 == 0;
+  if (!wide) return hipErrorInvalidValue;
+  transpose16_kernel<<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
