@@ -1,6 +1,8 @@
 /*
- * moe.h -- C ABI of the token-choice mixture-of-experts forward pass for
- * AMD Instinct MI355X (gfx950).
+ * moe.h -- C ABI of a mixture-of-experts layer for AMD Instinct MI355X
+ * (gfx950): the token-choice forward pass below, and beside it dropless and
+ * score-priority capacity, expert-choice routing, the balancing variants and
+ * the backward pass (each documented at its entry point).
  *
  * The layer (page titles and sections of the sources it follows):
  *   "Lab 18 -- Mixture of experts" s.1 (layer equation, gate values),
