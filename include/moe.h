@@ -97,6 +97,9 @@ typedef struct moe_config {
   int32_t dropped_output;     /* 0: fully dropped token -> y = x; 1: y = 0             */
   int32_t dropless;           /* 0: capacity C as above; 1: dropless (see below)       */
   int32_t routing;            /* moe_routing: token choice (above) or expert choice    */
+  int32_t save_preact;        /* 1: moe_forward also keeps the expert pre-activations in
+                                 its workspace, so moe_backward need not recompute them
+                                 (bf16 token choice with a capacity only)             */
 } moe_config;
 
 /* Score priority (priority = MOE_SCORE_PRIORITY) ["Lab 18" s.3: who is
@@ -395,7 +398,9 @@ MOE_API size_t moe_backward_workspace_bytes(const moe_config* cfg);
  *     dy to dx; the selection bias has no gradient;
  *   - the float32 rounding of the logits and the storage roundings are taken
  *     as the identity; H and Ye are the forward's stored values, the expert
- *     pre-activations are recomputed;
+ *     pre-activations are recomputed, or read from the forward's workspace
+ *     when cfg->save_preact is 1 (bit-identical values: the same products
+ *     summed in the same order);
  *   - built for bf16 storage, token choice with a capacity (not dropless):
  *     MOE_EUNSUPPORTED otherwise.
  *   x, weights    the forward's inputs

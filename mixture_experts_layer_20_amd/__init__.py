@@ -39,7 +39,7 @@ class moe_config(ctypes.Structure):
                 ('capacity_override', ctypes.c_int64), ('renormalize', ctypes.c_int32),
                 ('score', ctypes.c_int32), ('act', ctypes.c_int32), ('dtype', ctypes.c_int32),
                 ('priority', ctypes.c_int32), ('dropped_output', ctypes.c_int32),
-                ('dropless', ctypes.c_int32), ('routing', ctypes.c_int32)]
+                ('dropless', ctypes.c_int32), ('routing', ctypes.c_int32), ('save_preact', ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -115,13 +115,13 @@ def _enum(kind, v):
 def make_config(T, d, E, k, d_ff, *, n_shared=0, d_ff_shared=0, capacity_factor=1.25,
                 capacity_override=0, renormalize=-1, score='softmax', act='gelu', dtype='bf16',
                 priority='rank', dropped_output='residual', dropless=False,
-                routing='token') -> moe_config:
+                routing='token', save_preact=False) -> moe_config:
     return moe_config(T=T, d=d, E=E, k=k, d_ff=d_ff, n_shared=n_shared, d_ff_shared=d_ff_shared,
                       capacity_factor=float(capacity_factor), capacity_override=capacity_override,
                       renormalize=renormalize, score=_enum('score', score), act=_enum('act', act),
                       dtype=_enum('dtype', dtype), priority=_enum('priority', priority),
                       dropped_output=_enum('dropped_output', dropped_output), dropless=int(bool(dropless)),
-                      routing=_enum('routing', routing))
+                      routing=_enum('routing', routing), save_preact=int(bool(save_preact)))
 
 
 def config_from_workload(w, **over) -> moe_config:
@@ -347,8 +347,12 @@ _GKEYS = ('dx', 'dw_router', 'dlogit_bias', 'dw_in', 'dw_gate', 'db_in', 'dw_out
           'dws_out', 'dbs_out', 'dgates', 'dlogits')
 
 
+def moe_backward_workspace_bytes(cfg: moe_config) -> int:
+    return int(_lib.moe_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
 def backward_workspace(cfg: moe_config, device='cuda') -> torch.Tensor:
-    n = _lib.moe_backward_workspace_bytes(ctypes.byref(cfg))
+    n = moe_backward_workspace_bytes(cfg)
     if n == 0:
         raise ValueError(f'moe_backward is not built for this configuration: {cfg_summary(cfg)}')
     return torch.empty(n, dtype=torch.uint8, device=device)

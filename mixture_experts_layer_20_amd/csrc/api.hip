@@ -82,6 +82,9 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
     return fail(MOE_EINVAL, "unknown routing %d", c.routing);
   if (c.routing == MOE_EXPERT_CHOICE && c.dropless)
     return fail(MOE_EINVAL, "expert-choice routing has no dropless mode (no choice is ever dropped)");
+  if (c.save_preact != 0 && c.save_preact != 1) return fail(MOE_EINVAL, "save_preact must be 0 or 1");
+  if (c.save_preact && (c.dtype != MOE_BF16 || c.routing != MOE_TOKEN_CHOICE || c.dropless))
+    return fail(MOE_EINVAL, "save_preact is built for bf16 token choice with a capacity (the backward pass's mode)");
   if (c.capacity_override < 0) return fail(MOE_EINVAL, "capacity_override must be >= 0");
   if (!c.dropless && c.capacity_override == 0 && !(c.capacity_factor >= 1.0))
     return fail(MOE_EINVAL,
@@ -131,6 +134,9 @@ struct Workspace {
   float* ec_probs;
   int32_t* ec_fallback;
   int32_t* score_queue;
+  void* pre0;
+  void* pre1;
+  void* pres;
   void* h;
   void* ye;
   void* hs;
@@ -178,6 +184,11 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
   }
   if (by_score(c)) w.score_queue = static_cast<int32_t*>(take(sizeof(int32_t) * c.T * c.k));
 
+  if (c.save_preact) {
+    w.pre0 = take(ds * xrows * c.d_ff);
+    if (c.act == MOE_SWIGLU) w.pre1 = take(ds * xrows * c.d_ff);
+    if (fs > 0) w.pres = take(ds * c.T * fs);
+  }
   w.h = take(ds * xrows * c.d_ff);
   w.ye = take(ds * xrows * c.d);
   w.hs = fs > 0 ? take(ds * c.T * fs) : nullptr;
@@ -246,7 +257,8 @@ LossArgs loss_args(const moe_config& c, int64_t C, const Workspace& w, const int
 moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int32_t* rows, const void* a,
                const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate,
                const void* b_in, const void* w_out, const void* b_out, int F, void* h, void* out,
-               hipStream_t s, bool packed = false, int64_t group_rows = 0) {
+               hipStream_t s, bool packed = false, int64_t group_rows = 0, void* pre0 = nullptr,
+               void* pre1 = nullptr) {
   // each operand a GEMM launch addresses through one buffer descriptor (one
   // group's rows) stays below 2^30 elements (2^31 bytes); packed groups hold
   // at most group_rows rows
@@ -272,6 +284,8 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   g1.N = F;
   g1.K = c.d;
   g1.act = act == MOE_SWIGLU ? 2 : 1;
+  g1.pre0 = pre0;
+  g1.pre1 = pre1;
   MOE_TRY(hip_status(launch_gemm(g1, c.dtype, s), "expert GEMM 1"));
   GemmArgs g2{};
   g2.A = h;
@@ -435,8 +449,10 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   b.dgates = static_cast<float*>(take(sizeof(float) * T * c.k));
   b.dz = static_cast<float*>(take(sizeof(float) * T * E));
   b.dYe = static_cast<bf16_t*>(take(h2 * E * C * d));
-  b.U = static_cast<bf16_t*>(take(h2 * E * C * F));
-  b.U2 = ga == 2 ? static_cast<bf16_t*>(take(h2 * E * C * F)) : nullptr;
+  if (!c.save_preact) {
+    b.U = static_cast<bf16_t*>(take(h2 * E * C * F));
+    b.U2 = ga == 2 ? static_cast<bf16_t*>(take(h2 * E * C * F)) : nullptr;
+  }
   b.dH = static_cast<bf16_t*>(take(h2 * E * C * F));
   b.dact = static_cast<bf16_t*>(take(h2 * E * C * ga * F));
   b.dA = static_cast<bf16_t*>(take(h2 * E * C * d));
@@ -451,7 +467,7 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   b.slabs = static_cast<float*>(take(sizeof(float) * b.S * d * E));
   b.wrT = static_cast<float*>(take(sizeof(float) * E * d));
   if (Fs > 0) {
-    b.Us = static_cast<bf16_t*>(take(h2 * T * Fs));
+    if (!c.save_preact) b.Us = static_cast<bf16_t*>(take(h2 * T * Fs));
     b.dHs = static_cast<bf16_t*>(take(h2 * T * Fs));
     b.dUs = static_cast<bf16_t*>(take(h2 * T * Fs));
     b.dAs = static_cast<bf16_t*>(take(h2 * T * d));
@@ -948,11 +964,11 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
                   wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T));
   } else if (C > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, w.kept, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in, wt->w_out,
-                wt->b_out, c.d_ff, w.h, w.ye, s));
+                wt->b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1));
   }
   if (c.n_shared > 0 && c.T > 0)
     MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt->ws_in, nullptr, wt->bs_in, wt->ws_out,
-                wt->bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s));
+                wt->bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s, false, 0, w.pres));
 
   CombineArgs cb{};
   cb.x = x;
@@ -1103,7 +1119,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
   if (C > 0 && T > 0) {
     const int32_t* kept = w.kept;
     const bf16_t* W_in = static_cast<const bf16_t*>(wt->w_in);
-    if (glu) {
+    if (c.save_preact) {
+      // the forward pass kept them
+    } else if (glu) {
       MOE_TRY(bgemm("recompute gate projection", x, 0, 0, w.row_token, T, wt->w_gate, 0, 0, nullptr, b.U, kept, C, E,
                     static_cast<int>(F), c.d, s));
       MOE_TRY(bgemm("recompute up projection", x, 0, 0, w.row_token, T, wt->w_in, 0, 0, nullptr, b.U2, kept, C, E,
@@ -1119,8 +1137,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
                   static_cast<int>(F), c.d, s));
     ActBwdArgs ab{};
     ab.dH = b.dH;
-    ab.U = b.U;
-    ab.U2 = b.U2;
+    ab.U = c.save_preact ? static_cast<const bf16_t*>(w.pre0) : b.U;
+    ab.U2 = c.save_preact ? static_cast<const bf16_t*>(w.pre1) : b.U2;
     ab.dact = b.dact;
     ab.valid = kept;
     ab.rpg = C;
@@ -1172,15 +1190,16 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
 
   // shared experts: every token, output gradient dy itself
   if (Fs > 0 && T > 0) {
-    MOE_TRY(bgemm("recompute shared pre-activation", x, 0, 0, nullptr, 0, wt->ws_in, 0, 0, wt->bs_in, b.Us, nullptr, T,
-                  1, static_cast<int>(Fs), c.d, s));
+    if (!c.save_preact)
+      MOE_TRY(bgemm("recompute shared pre-activation", x, 0, 0, nullptr, 0, wt->ws_in, 0, 0, wt->bs_in, b.Us, nullptr,
+                    T, 1, static_cast<int>(Fs), c.d, s));
     MOE_TRY(transpose("ws_out transpose", static_cast<const bf16_t*>(wt->ws_out), b.wsoT, 1, d, Fs, d, 0, Fs, 0, d,
                       nullptr, nullptr, 0, s));
     MOE_TRY(bgemm("shared hidden gradient", dy, 0, 0, nullptr, 0, b.wsoT, 0, 0, nullptr, b.dHs, nullptr, T, 1,
                   static_cast<int>(Fs), c.d, s));
     ActBwdArgs ab{};
     ab.dH = b.dHs;
-    ab.U = b.Us;
+    ab.U = c.save_preact ? static_cast<const bf16_t*>(w.pres) : b.Us;
     ab.dact = b.dUs;
     ab.rpg = T;
     ab.groups = 1;

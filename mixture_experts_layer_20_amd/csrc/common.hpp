@@ -156,6 +156,11 @@ struct GemmArgs {
   int act;                    // 0 none (bias only), 1 GELU, 2 SwiGLU (B1 = gate),
                               // 3 router planes: float32 C [rows, N/4], the sum of
                               // each group of 4 output columns
+  // bf16 path, ACT 1/2: the pre-activations too, laid out like C (kept for a
+  // backward pass): pre0 = A B0^T + bias (GELU) or the gate projection
+  // (SwiGLU), pre1 = the up projection (SwiGLU) | null
+  void* pre0;
+  void* pre1;
 };
 
 struct CombineArgs {

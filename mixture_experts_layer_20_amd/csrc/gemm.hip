@@ -465,7 +465,6 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     // bytes per row).  Stored straight from the MFMA layout, one instruction
     // would write 8 bytes into each of 32 rows, and the L2 would take many
     // more, smaller write requests.
-    bf16_t* C = static_cast<bf16_t*>(a.C) + row_base * N;
     const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
     constexpr int kOut = kGlu ? 64 : 128;              // output columns per wave
     constexpr int kPitch = kOut * 2 + 16;              // padded LDS row (bytes)
@@ -475,49 +474,60 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     __syncthreads();                                   // every wave is done with the stage buffers
     uint8_t* scr = lds + wave * 32 * kPitch;
     const int colw = wn * kOut;                        // the wave's first tile column
+    // what = 0: the activated output into C; 1: the pre-activation (GELU:
+    // a w^T + b; SwiGLU: the gate projection) into pre0; 2: the SwiGLU up
+    // projection into pre1 (outputs kept for a backward pass)
+    auto emit = [&](bf16_t* dst, int what) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < kXB; ++j) {
-      const int rowbase = wm * kXR + j * 32;
-      if (m0 + rowbase >= rows_g) break;
+      for (int j = 0; j < kXB; ++j) {
+        const int rowbase = wm * kXR + j * 32;
+        if (m0 + rowbase >= rows_g) break;
 #pragma unroll
-      for (int i = 0; i < (kGlu ? 2 : 4); ++i) {
+        for (int i = 0; i < (kGlu ? 2 : 4); ++i) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = ncol[i] - colw + 8 * q + 4 * (lane >> 5);
-          const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
-          f32x2_t v[2];
+          for (int q = 0; q < 4; ++q) {
+            const int col = ncol[i] - colw + 8 * q + 4 * (lane >> 5);
+            const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
+            f32x2_t v[2];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x = acc[i][j][4 * q + r];
-            if (ACT == 2) {
-              x = silu_fast(x) * acc[i + 2][j][4 * q + r];
-            } else {
-              if (bias && n + r < N) x += bf16_to_f32(bias[n + r]);
-              if (ACT == 1) x = gelu_erf(x);
+            for (int r = 0; r < 4; ++r) {
+              float x = acc[i][j][4 * q + r];
+              if (ACT == 2) {
+                if (what == 0) x = silu_fast(x) * acc[i + 2][j][4 * q + r];
+                else if (what == 2) x = acc[i + 2][j][4 * q + r];
+              } else {
+                if (bias && n + r < N) x += bf16_to_f32(bias[n + r]);
+                if (ACT == 1 && what == 0) x = gelu_erf(x);
+              }
+              v[r >> 1][r & 1] = x;
             }
-            v[r >> 1][r & 1] = x;
+            // hardware round-to-nearest-even conversion, two values at a time
+            uint2 packed;
+            packed.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[0], bf16x2_t));
+            packed.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[1], bf16x2_t));
+            *reinterpret_cast<uint2*>(scr + (lane & 31) * kPitch + col * 2) = packed;
           }
-          // hardware round-to-nearest-even conversion, two values at a time
-          uint2 packed;
-          packed.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[0], bf16x2_t));
-          packed.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[1], bf16x2_t));
-          *reinterpret_cast<uint2*>(scr + (lane & 31) * kPitch + col * 2) = packed;
+          // one block at a time: keeps the accumulators' copies out of the
+          // VGPRs until they are needed
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // one block at a time: keeps the accumulators' copies out of the
-        // VGPRs until they are needed
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the wave reads back only what it wrote itself
+        // the wave reads back only what it wrote itself
 #pragma unroll
-      for (int pp = 0; pp < 32 / kRowsPerInst; ++pp) {
-        const int row = pp * kRowsPerInst + lane / kLanesPerRow;
-        const int ch = lane % kLanesPerRow;
-        const uint4 v = *reinterpret_cast<const uint4*>(scr + row * kPitch + ch * 16);
-        const int64_t m = m0 + rowbase + row;
-        const int n = n0 + colw + ch * 8;
-        // N is a multiple of 8: a segment is wholly inside or wholly past it
-        if (m < rows_g && n < N) *reinterpret_cast<uint4*>(C + m * N + n) = v;
+        for (int pp = 0; pp < 32 / kRowsPerInst; ++pp) {
+          const int row = pp * kRowsPerInst + lane / kLanesPerRow;
+          const int ch = lane % kLanesPerRow;
+          const uint4 v = *reinterpret_cast<const uint4*>(scr + row * kPitch + ch * 16);
+          const int64_t m = m0 + rowbase + row;
+          const int n = n0 + colw + ch * 8;
+          // N is a multiple of 8: a segment is wholly inside or wholly past it
+          if (m < rows_g && n < N) *reinterpret_cast<uint4*>(dst + m * N + n) = v;
+        }
       }
+    };
+    emit(static_cast<bf16_t*>(a.C) + row_base * N, 0);
+    if (ACT != 0 && a.pre0) {
+      emit(static_cast<bf16_t*>(a.pre0) + row_base * N, 1);
+      if (ACT == 2) emit(static_cast<bf16_t*>(a.pre1) + row_base * N, 2);
     }
   };
 

@@ -64,10 +64,11 @@ def test_struct_layout_matches_header(tmp_path, moe):
 #include <stddef.h>
 #include "moe.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_config), offsetof(moe_config, capacity_factor),
-         offsetof(moe_config, capacity_override), offsetof(moe_config, dropped_output),
-         offsetof(moe_config, dropless), offsetof(moe_config, routing), sizeof(moe_weights),
-         sizeof(moe_outputs), offsetof(moe_outputs, lse), offsetof(moe_outputs, sel));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_config),
+         offsetof(moe_config, capacity_factor), offsetof(moe_config, capacity_override),
+         offsetof(moe_config, dropped_output), offsetof(moe_config, dropless), offsetof(moe_config, routing),
+         offsetof(moe_config, save_preact), sizeof(moe_weights), sizeof(moe_outputs), offsetof(moe_outputs, lse),
+         offsetof(moe_outputs, sel), sizeof(moe_grads));
   return 0;
 }
 ''')
@@ -78,8 +79,9 @@ int main(void) {
                                        check=True).stdout.split()))
     want = [ctypes.sizeof(moe.moe_config), moe.moe_config.capacity_factor.offset,
             moe.moe_config.capacity_override.offset, moe.moe_config.dropped_output.offset,
-            moe.moe_config.dropless.offset, moe.moe_config.routing.offset, ctypes.sizeof(moe.moe_weights),
-            ctypes.sizeof(moe.moe_outputs), moe.moe_outputs.lse.offset, moe.moe_outputs.sel.offset]
+            moe.moe_config.dropless.offset, moe.moe_config.routing.offset, moe.moe_config.save_preact.offset,
+            ctypes.sizeof(moe.moe_weights), ctypes.sizeof(moe.moe_outputs), moe.moe_outputs.lse.offset,
+            moe.moe_outputs.sel.offset, ctypes.sizeof(moe.moe_grads)]
     assert got == want
 
 
@@ -283,3 +285,15 @@ def test_backward_configuration(moe):
     assert lib.moe_backward(ctypes.byref(c), None, None, None, None, None, 0.0, 0.0, ctypes.byref(g), None,
                             None) == moe.MOE_EINVAL
     assert b'NULL' in lib.moe_last_error()
+
+
+def test_save_preact_configuration(moe):
+    bf = dict(dtype='bf16')
+    assert moe.moe_validate(cfg(moe, save_preact=True, **bf)) == 40
+    for bad in (dict(), dict(dropless=True, **bf), dict(routing='expert', **bf)):     # f32, dropless, expert choice
+        with pytest.raises(ValueError, match='save_preact'):
+            moe.moe_validate(cfg(moe, save_preact=True, **bad))
+    # the forward keeps them, the backward need not
+    assert moe.moe_workspace_bytes(cfg(moe, save_preact=True, **bf)) > moe.moe_workspace_bytes(cfg(moe, **bf))
+    assert moe.moe_backward_workspace_bytes(cfg(moe, save_preact=True, **bf)) < \
+        moe.moe_backward_workspace_bytes(cfg(moe, **bf))

@@ -221,3 +221,45 @@ def test_backward_mixtral_sampled(moe):
         _check(f'dw_out[{e}][:, {f}]', gw_out[e][:, f], d_out.T @ h)
         _check(f'dw_up[{e}][{f}]', gw_up[e][f], (dh * O.silu(gp)) @ a)
         _check(f'dw_gate[{e}][{f}]', gw_gate[e][f], (dh * up * B.silu_grad(gp)) @ a)
+
+
+def _gpu_pass(moe, w, dev, dy, **over):
+    cfg = moe.config_from_workload(w, **over)
+    out = moe.alloc_outputs(cfg, DEV, logits=True)
+    ws = moe.workspace(cfg, DEV)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    moe.moe_forward(cfg, weights, dev['x'], out, ws)
+    E, F, d, T = w.E, w.d_ff, w.d, w.T
+    bf = torch.bfloat16
+    grads = dict(dx=torch.empty(T, d, dtype=bf, device=DEV), dw_router=torch.empty(d, E, device=DEV),
+                 dw_in=torch.empty(E, F, d, dtype=bf, device=DEV), dw_out=torch.empty(E, d, F, dtype=bf, device=DEV),
+                 dgates=torch.empty(T, w.k, device=DEV), dlogits=torch.empty(T, E, device=DEV))
+    if w.act == 'swiglu':
+        grads['dw_gate'] = torch.empty(E, F, d, dtype=bf, device=DEV)
+    else:
+        grads['db_in'] = torch.empty(E, F, dtype=bf, device=DEV)
+    fs = w.n_shared * w.d_ff_shared
+    if fs:
+        grads.update(dws_in=torch.empty(fs, d, dtype=bf, device=DEV), dws_out=torch.empty(d, fs, dtype=bf, device=DEV))
+    bws = moe.backward_workspace(cfg, DEV)
+    moe.moe_backward(cfg, weights, dev['x'], out, ws, synth.to_torch(dy, DEV), grads, bws, ALPHA_AUX, ALPHA_Z)
+    torch.cuda.synchronize()
+    return out, grads
+
+
+@pytest.mark.parametrize('case', [c for c in BWD_CASES if c[0] in ('gelu_renorm_drops', 'swiglu_renorm',
+                                                                   'sigmoid_shared')], ids=lambda c: c[0])
+def test_saved_preactivations_equal_recomputation(moe, case):
+    """With save_preact the forward pass keeps the expert (and shared)
+    pre-activations and the backward pass reads them instead of recomputing:
+    the forward outputs and every gradient are bit-identical either way (the
+    same products summed in the same order)."""
+    name, w, over = case
+    say('save_preact', name)
+    inp, ex, sh, dev, dy = _layer(moe, w, 0)
+    out0, g0 = _gpu_pass(moe, w, dev, dy, **over)
+    out1, g1 = _gpu_pass(moe, w, dev, dy, save_preact=True, **over)
+    for kk in out0:
+        assert torch.equal(out0[kk], out1[kk]), kk
+    for kk in g0:
+        assert torch.equal(g0[kk], g1[kk]), kk
