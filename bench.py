@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--phase-reps R] [--dropless]
                     [--routing token|expert] [--priority rank|token|score] [--backward]
+                    [--save-preact]
 
 A step is one whole forward pass of the layer (router, capacity, dispatch,
 routed and shared expert FFNs, combine, losses) over one batch of T synthetic
@@ -56,6 +57,8 @@ def parse():
                         '(batch-prioritised)')
     p.add_argument('--backward', action='store_true',
                    help='also time moe_backward (the gradients of the same layer) as a phase')
+    p.add_argument('--save-preact', action='store_true',
+                   help='the forward pass keeps the expert pre-activations for the backward pass')
     p.add_argument('--copy-calibration', action='store_true',
                    help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
     return p.parse_args()
@@ -87,7 +90,8 @@ def main():
     dev = 'cuda'
     t0 = time.time()
     inp = synth.router_inputs(w)
-    cfg = moe.config_from_workload(w, dropless=args.dropless, routing=args.routing, priority=args.priority)
+    cfg = moe.config_from_workload(w, dropless=args.dropless, routing=args.routing, priority=args.priority,
+                                   save_preact=args.save_preact)
     C = moe.moe_validate(cfg)
     x = synth.to_torch(inp['x'], dev)
     weights = dict(w_router=synth.to_torch(inp['w_router'], dev),
@@ -295,7 +299,8 @@ def main():
             'config': {'workload': w.name, 'T': w.T, 'd': d, 'E': E, 'k': k, 'd_ff': F, 'act': w.act,
                        'score': w.score, 'capacity_factor': w.cf, 'capacity': C,
                        'n_shared': w.n_shared, 'kept_assignments': kept, 'dropped_assignments': n_dropped,
-                       'dropless': bool(args.dropless), 'routing': args.routing, 'priority': args.priority},
+                       'dropless': bool(args.dropless), 'routing': args.routing, 'priority': args.priority,
+                       'save_preact': bool(args.save_preact)},
             'roofline': roofline,
             'phases': {kk: {a: (round(bb, 5) if isinstance(bb, float) else bb) for a, bb in v.items()}
                        for kk, v in phases.items()},
