@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--phase-reps R] [--dropless]
                     [--routing token|expert] [--priority rank|token|score] [--backward]
-                    [--save-preact]
+                    [--save-preact] [--graph]
 
 A step is one whole forward pass of the layer (router, capacity, dispatch,
 routed and shared expert FFNs, combine, losses) over one batch of T synthetic
@@ -59,6 +59,8 @@ def parse():
                    help='also time moe_backward (the gradients of the same layer) as a phase')
     p.add_argument('--save-preact', action='store_true',
                    help='the forward pass keeps the expert pre-activations for the backward pass')
+    p.add_argument('--graph', action='store_true',
+                   help='capture one moe_forward into a HIP graph and time its replays')
     p.add_argument('--copy-calibration', action='store_true',
                    help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
     return p.parse_args()
@@ -130,12 +132,24 @@ def main():
     log(f'inputs ready in {time.time() - t0:.1f}s: {w.name} T={w.T} d={d} E={E} k={w.k} F={F} C={C}')
 
     # ---------------------------------------------------------------- headline
+    step = lambda: moe.moe_forward(cfg, weights, x, out, ws)
+    if args.graph:
+        # the library enqueues kernels only, so one call captures whole
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            moe.moe_forward(cfg, weights, x, out, ws, stream=gs)
+        torch.cuda.current_stream().wait_stream(gs)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            moe.moe_forward(cfg, weights, x, out, ws, stream=gs)
+        step = graph.replay
     for _ in range(args.warmup):
-        moe.moe_forward(cfg, weights, x, out, ws)
+        step()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        moe.moe_forward(cfg, weights, x, out, ws)
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms = 1e3 * elapsed / max(1, args.steps)
@@ -300,7 +314,7 @@ def main():
                        'score': w.score, 'capacity_factor': w.cf, 'capacity': C,
                        'n_shared': w.n_shared, 'kept_assignments': kept, 'dropped_assignments': n_dropped,
                        'dropless': bool(args.dropless), 'routing': args.routing, 'priority': args.priority,
-                       'save_preact': bool(args.save_preact)},
+                       'save_preact': bool(args.save_preact), 'graph': bool(args.graph)},
             'roofline': roofline,
             'phases': {kk: {a: (round(bb, 5) if isinstance(bb, float) else bb) for a, bb in v.items()}
                        for kk, v in phases.items()},

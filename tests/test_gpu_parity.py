@@ -906,3 +906,42 @@ def test_forward_score_priority(moe, case):
         rows = np.sort(np.random.default_rng(6).choice(w.T, 160, replace=False))
     cfg, out, ref = _compare_forward(moe, w, rows=rows, priority='score', **over)
     assert ref['dropped'].any()
+
+
+# ----------------------------------------------------------------------------- graph capture
+@pytest.mark.parametrize('over', [dict(), dict(priority='score', capacity_override=900), dict(routing='expert'),
+                                  dict(dropless=True)], ids=['rank', 'score', 'expert_choice', 'dropless'])
+def test_forward_replays_from_a_captured_graph(moe, over):
+    """moe_forward enqueues kernels only (no memset, copy or allocation), so
+    it can be captured into a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager call bit for bit."""
+    w = synth.WORKLOADS['deepseekmoe_fine'].with_(T=3000, name='graph')
+    say('graph capture', over)
+    inp, ex, sh, dev = device_layer(w, moe)
+    cfg = moe.config_from_workload(w, **over)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    ref = moe.alloc_outputs(cfg, DEV, logits=True, probs=True, lse=True)
+    ws_ref = moe.workspace(cfg, DEV)
+    moe.moe_forward(cfg, weights, dev['x'], ref, ws_ref)
+    torch.cuda.synchronize()
+    out = moe.alloc_outputs(cfg, DEV, logits=True, probs=True, lse=True)
+    ws = moe.workspace(cfg, DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                         # warm the stream once outside capture
+        moe.moe_forward(cfg, weights, dev['x'], out, ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_forward(cfg, weights, dev['x'], out, ws, stream=s)
+    for rep in range(3):
+        for t in out.values():                         # scribble between replays
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for kk in ref:
+            if over.get('routing') == 'expert' and kk in ('slot', 'dropped'):
+                continue                               # not written under expert choice
+            assert torch.equal(out[kk], ref[kk]), (rep, kk)
