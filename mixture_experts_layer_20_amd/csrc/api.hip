@@ -108,6 +108,25 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
 
 int resolved_renorm(const moe_config& c) { return c.renormalize < 0 ? (c.k > 1) : c.renormalize; }
 
+// Parts of the k range for the expert down projection when its tiles would
+// not fill the GPU (few experts' rows, a narrow model): enough parts to reach
+// about 256 workgroups, each part at least 512 wide and a multiple of 64.
+// The weights are then streamed by every CU instead of a few.
+struct KSplit {
+  int parts;
+  int64_t slice;
+};
+KSplit down_ksplit(int64_t groups, int64_t rpg, int64_t N, int64_t K) {
+  const int64_t tiles = groups * ((rpg + 255) / 256) * ((N + 255) / 256);
+  KSplit k{1, K};
+  if (tiles >= 192 || tiles == 0) return k;
+  const int64_t want = std::min<int64_t>({8, (256 + tiles - 1) / tiles, K / 512});
+  if (want <= 1) return k;
+  k.slice = ((K + want - 1) / want + 63) / 64 * 64;
+  k.parts = static_cast<int>((K + k.slice - 1) / k.slice);
+  return k;
+}
+
 // Batch-prioritised capacity in effect (in dropless mode nothing is dropped
 // and the kept choices are numbered in rank-major order, as without it).
 bool by_score(const moe_config& c) {
@@ -137,6 +156,7 @@ struct Workspace {
   void* pre0;
   void* pre1;
   void* pres;
+  float* kpart;
   void* h;
   void* ye;
   void* hs;
@@ -188,6 +208,10 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
     w.pre0 = take(ds * xrows * c.d_ff);
     if (c.act == MOE_SWIGLU) w.pre1 = take(ds * xrows * c.d_ff);
     if (fs > 0) w.pres = take(ds * c.T * fs);
+  }
+  if (!c.dropless && c.dtype == MOE_BF16) {
+    const KSplit ksp = down_ksplit(c.E, C, c.d, c.d_ff);
+    if (ksp.parts > 1) w.kpart = static_cast<float*>(take(sizeof(float) * ksp.parts * c.E * C * c.d));
   }
   w.h = take(ds * xrows * c.d_ff);
   w.ye = take(ds * xrows * c.d);
@@ -258,7 +282,7 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
                const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate,
                const void* b_in, const void* w_out, const void* b_out, int F, void* h, void* out,
                hipStream_t s, bool packed = false, int64_t group_rows = 0, void* pre0 = nullptr,
-               void* pre1 = nullptr) {
+               void* pre1 = nullptr, float* kpart = nullptr) {
   // each operand a GEMM launch addresses through one buffer descriptor (one
   // group's rows) stays below 2^30 elements (2^31 bytes); packed groups hold
   // at most group_rows rows
@@ -300,6 +324,15 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   g2.N = c.d;
   g2.K = F;
   g2.act = 0;
+  if (kpart && !packed && c.dtype == MOE_BF16) {
+    const KSplit ksp = down_ksplit(groups, rpg, c.d, F);
+    if (ksp.parts > 1) {
+      g2.ksplit = ksp.parts;
+      g2.kslice = ksp.slice;
+      g2.kpart = kpart;
+      g2.kpart_stride = static_cast<int64_t>(groups) * rpg * c.d;
+    }
+  }
   return hip_status(launch_gemm(g2, c.dtype, s), "expert GEMM 2");
 }
 
@@ -368,7 +401,7 @@ moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weigh
   MOE_TRY(hip_status(launch_expert_choice(e, s), "expert choice"));   // T = 0: zero counts and sums
   if (c.T > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, out.counts, x, w.row_token, c.T, wt.w_in, wt.w_gate, wt.b_in, wt.w_out,
-                wt.b_out, c.d_ff, w.h, w.ye, s));
+                wt.b_out, c.d_ff, w.h, w.ye, s, false, 0, nullptr, nullptr, w.kpart));
     if (c.n_shared > 0)
       MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt.ws_in, nullptr, wt.bs_in, wt.ws_out,
                   wt.bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s));
@@ -964,7 +997,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
                   wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T));
   } else if (C > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, w.kept, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in, wt->w_out,
-                wt->b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1));
+                wt->b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart));
   }
   if (c.n_shared > 0 && c.T > 0)
     MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt->ws_in, nullptr, wt->bs_in, wt->ws_out,

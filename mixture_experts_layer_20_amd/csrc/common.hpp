@@ -161,6 +161,14 @@ struct GemmArgs {
   // (SwiGLU), pre1 = the up projection (SwiGLU) | null
   void* pre0;
   void* pre1;
+  // bf16 path, ACT 0, not packed: split the k range into ksplit parts of
+  // kslice (a multiple of 64), float32 partial sums in kpart [ksplit,
+  // groups*rows_per_group, N] (kpart_stride elements apart), then summed in
+  // part order with the bias into C.  ksplit <= 1: no split.
+  int ksplit;
+  int64_t kslice;
+  float* kpart;
+  int64_t kpart_stride;
 };
 
 struct CombineArgs {

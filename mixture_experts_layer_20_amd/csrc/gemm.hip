@@ -205,7 +205,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   constexpr int kNOut = kGlu ? kBW / 2 : kBW;   // output columns per tile
   __shared__ __align__(1024) uint8_t lds[kLdsBytes];
 
-  const int N = a.N, K = a.K;
+  const int N = a.N;
   const int ntiles = (N + kNOut - 1) / kNOut;
   const int mt_max = static_cast<int>((a.rows_per_group + kBM - 1) / kBM);
   // blocks are dealt round-robin to the 8 XCDs: block b runs on XCD b%8 as
@@ -215,7 +215,16 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // and every XCD gets an even share of every expert.  The grid is a multiple
   // of 256 blocks.
   const int64_t p = blockIdx.x / 8;
-  const int64_t L = ((p / 32) * 8 + blockIdx.x % 8) * 32 + p % 32;
+  int64_t L = ((p / 32) * 8 + blockIdx.x % 8) * 32 + p % 32;
+  // split k (bias-only GEMMs with too few tiles to fill the GPU): part ks of
+  // the k range, float32 partial sums to kpart, summed by ksum_kernel
+  int ks = 0;
+  if (ACT == 0 && a.ksplit > 1) {
+    const int64_t per_split = static_cast<int64_t>(a.groups) * mt_max * ntiles;
+    ks = static_cast<int>(L / per_split);
+    if (ks >= a.ksplit) return;
+    L %= per_split;
+  }
   TileCoord tc;
   int64_t rows_g, row_base;   // valid rows of the tile's group, and its first row
   if (a.packed) {
@@ -294,12 +303,15 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // is the whole [a_rows, K] input and row m of group g is A[gather[row_base
   // + m]], row_base = g*rpg, or the packed start)
   const bool gathered = a.gather != nullptr;
-  const int64_t lda = a.lda ? a.lda : K, ldb = a.ldb ? a.ldb : K;
-  const bf16_t* A = static_cast<const bf16_t*>(a.A) +
+  const int64_t lda = a.lda ? a.lda : a.K, ldb = a.ldb ? a.ldb : a.K;
+  // this tile's k range: [k0, k0 + K) of the operands' rows
+  const int64_t k0 = static_cast<int64_t>(ks) * a.kslice;
+  const int K = ACT == 0 && a.ksplit > 1 ? static_cast<int>(min<int64_t>(a.kslice, a.K - k0)) : a.K;
+  const bf16_t* A = static_cast<const bf16_t*>(a.A) + k0 +
                     (gathered ? 0
                      : a.packed ? row_base * lda
                                 : static_cast<int64_t>(tc.g) * (a.a_gs ? a.a_gs : a.rows_per_group * lda));
-  const int64_t bg = static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb);
+  const int64_t bg = static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb) + k0;
   const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + bg;
   const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + bg : B0;
 
@@ -453,6 +465,27 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
             if (n >= N) continue;
             Cf[m * (N / 4) + (n >> 2)] =
                 ((acc[i][j][4 * q] + acc[i][j][4 * q + 1]) + acc[i][j][4 * q + 2]) + acc[i][j][4 * q + 3];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return;
+    }
+    if (ACT == 0 && a.ksplit > 1) {
+      // split k: this part's float32 sums, four consecutive columns a lane
+      float* P = a.kpart + static_cast<int64_t>(ks) * a.kpart_stride + row_base * N;
+#pragma unroll
+      for (int j = 0; j < kXB; ++j) {
+        const int64_t m = m0 + xrow[j];
+        if (m >= rows_g) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
+            if (n >= N) continue;
+            *reinterpret_cast<float4*>(P + m * N + n) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -718,6 +751,37 @@ void launch_bf16(const GemmArgs& a, unsigned grid, hipStream_t s) {
   else gemm_bf16_w4<ACT><<<grid, 256, 0, s>>>(a);
 }
 
+namespace {
+// Split k: C[row] = bf16(sum over the parts, in order, of kpart + bias) for
+// the valid rows of every group, 8 columns a thread.
+__global__ __launch_bounds__(kThreads) void ksum_kernel(GemmArgs a) {
+  const int64_t c8 = a.N / 8;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (item >= static_cast<int64_t>(a.groups) * a.rows_per_group * c8) return;
+  const int64_t row = item / c8, c = (item % c8) * 8;
+  const int g = static_cast<int>(row / a.rows_per_group);
+  const int64_t r = row % a.rows_per_group;
+  if (a.rows && r >= a.rows[g]) return;
+  float v[8] = {};
+  for (int s = 0; s < a.ksplit; ++s) {
+    const float4* q = reinterpret_cast<const float4*>(a.kpart + s * a.kpart_stride + row * a.N + c);
+    const float4 x0 = q[0], x1 = q[1];
+    v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+    v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+  }
+  if (a.bias) {
+    const bf16_t* b = static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(g) * a.N + c;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += bf16_to_f32(b[q]);
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    w[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
+  *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.C) + row * a.N + c) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+}  // namespace
+
 hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
@@ -726,13 +790,18 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
     // packed rows: the groups' row tiles number at most total/256 + groups
     const int64_t row_tiles = a.packed ? (a.total_rows + kBM - 1) / kBM + a.groups
                                        : static_cast<int64_t>(a.groups) * ((a.rows_per_group + kBM - 1) / kBM);
-    const int64_t tiles = row_tiles * ((a.N + nout - 1) / nout);
+    const bool split = a.act == 0 && a.ksplit > 1 && !a.packed;
+    const int64_t tiles = row_tiles * ((a.N + nout - 1) / nout) * (split ? a.ksplit : 1);
     const unsigned grid = static_cast<unsigned>((tiles + 255) / 256 * 256);
     switch (a.act) {
       case 0: launch_bf16<0>(a, grid, s); break;
       case 1: launch_bf16<1>(a, grid, s); break;
       case 2: launch_bf16<2>(a, grid, s); break;
       default: launch_bf16<3>(a, grid, s); break;
+    }
+    if (split) {
+      const int64_t items = static_cast<int64_t>(a.groups) * a.rows_per_group * (a.N / 8);
+      ksum_kernel<<<static_cast<unsigned>((items + kThreads - 1) / kThreads), kThreads, 0, s>>>(a);
     }
   } else {
     const int64_t tiles = static_cast<int64_t>(a.groups) * ((a.rows_per_group + kFT - 1) / kFT) *

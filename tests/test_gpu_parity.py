@@ -945,3 +945,16 @@ def test_forward_replays_from_a_captured_graph(moe, over):
             if over.get('routing') == 'expert' and kk in ('slot', 'dropped'):
                 continue                               # not written under expert choice
             assert torch.equal(out[kk], ref[kk]), (rep, kk)
+
+
+# ----------------------------------------------------------------------------- split-k down projection
+@pytest.mark.parametrize('act', ['gelu', 'swiglu'])
+def test_forward_with_split_k_down_projection(moe, act):
+    """Few experts' rows and a narrow model leave the down projection with
+    too few tiles to fill the GPU; moe_forward then splits its k range (here
+    4 tiles, d_ff 2048 -> 4 parts of 512) and sums the float32 parts in order
+    with the bias.  The layer still matches the oracle."""
+    w = synth.Workload('sk', T=300, d=256, E=4, k=1, d_ff=2048, act=act, score='softmax', renormalize=-1,
+                       cf=1.0, dtype='bf16', seed=71)
+    cfg, out, ref = _compare_forward(moe, w)
+    assert ref['dropped'].any() or ref['capacity'] * w.E >= w.T
