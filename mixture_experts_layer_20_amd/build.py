@@ -67,7 +67,29 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError('link failed:\n' + r.stderr)
     os.replace(tmp, OUT)
+    build_examples(verbose)
     return OUT
+
+
+EXAMPLE = os.path.join(PKG, 'examples', 'forward_from_c.c')
+
+
+def build_examples(verbose=False):
+    """The plain-C consumer of the ABI (examples/forward_from_c.c), as a
+    shared object for the tests and as a program, linked against libmoe.so
+    and the HIP runtime only."""
+    rocm = os.environ.get('ROCM_PATH', '/opt/rocm')
+    base = ['gcc', '-std=c11', '-O2', '-Wall', '-D__HIP_PLATFORM_AMD__', '-I', os.path.join(rocm, 'include'),
+            '-I', os.path.join(ROOT, 'include'), EXAMPLE, '-L', PKG, '-lmoe', '-L', os.path.join(rocm, 'lib'),
+            '-lamdhip64', '-Wl,-rpath,$ORIGIN/..', '-Wl,-rpath,' + os.path.join(rocm, 'lib')]
+    outdir = os.path.dirname(EXAMPLE)
+    for extra, name in ((['-fPIC', '-shared'], 'libforward_from_c.so'), (['-DMOE_EXAMPLE_MAIN'], 'forward_from_c')):
+        cmd = base[:1] + extra + base[1:] + ['-o', os.path.join(outdir, name)]
+        if verbose:
+            print(' '.join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f'building {name} failed:\n{r.stderr}')
 
 
 if __name__ == '__main__':
