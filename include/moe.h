@@ -99,7 +99,7 @@ typedef struct moe_config {
   int32_t routing;            /* moe_routing: token choice (above) or expert choice    */
   int32_t save_preact;        /* 1: moe_forward also keeps the expert pre-activations in
                                  its workspace, so moe_backward need not recompute them
-                                 (bf16 token choice with a capacity only)             */
+                                 (bf16 token choice only)                             */
 } moe_config;
 
 /* Score priority (priority = MOE_SCORE_PRIORITY) ["Lab 18" s.3: who is
@@ -401,8 +401,8 @@ MOE_API size_t moe_backward_workspace_bytes(const moe_config* cfg);
  *     pre-activations are recomputed, or read from the forward's workspace
  *     when cfg->save_preact is 1 (bit-identical values: the same products
  *     summed in the same order);
- *   - built for bf16 storage, token choice with a capacity (not dropless):
- *     MOE_EUNSUPPORTED otherwise.
+ *   - built for bf16 storage and token choice, with a capacity or dropless
+ *     (packed rows): MOE_EUNSUPPORTED otherwise.
  *   x, weights    the forward's inputs
  *   fwd           the forward's outputs: idx, gates, slot, dropped, counts and
  *                 logits are read (logits required)

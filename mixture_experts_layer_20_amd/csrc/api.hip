@@ -83,8 +83,8 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
   if (c.routing == MOE_EXPERT_CHOICE && c.dropless)
     return fail(MOE_EINVAL, "expert-choice routing has no dropless mode (no choice is ever dropped)");
   if (c.save_preact != 0 && c.save_preact != 1) return fail(MOE_EINVAL, "save_preact must be 0 or 1");
-  if (c.save_preact && (c.dtype != MOE_BF16 || c.routing != MOE_TOKEN_CHOICE || c.dropless))
-    return fail(MOE_EINVAL, "save_preact is built for bf16 token choice with a capacity (the backward pass's mode)");
+  if (c.save_preact && (c.dtype != MOE_BF16 || c.routing != MOE_TOKEN_CHOICE))
+    return fail(MOE_EINVAL, "save_preact is built for bf16 token choice (the backward pass's mode)");
   if (c.capacity_override < 0) return fail(MOE_EINVAL, "capacity_override must be >= 0");
   if (!c.dropless && c.capacity_override == 0 && !(c.capacity_factor >= 1.0))
     return fail(MOE_EINVAL,
@@ -461,6 +461,9 @@ struct BwdWorkspace {
   bf16_t* dyT;
   bf16_t* HsT;
   bf16_t* dUsT;
+  int32_t* pstart;
+  int32_t* prow;
+  int32_t* pxrow;
   int S;
   size_t bytes;
 };
@@ -481,14 +484,20 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   b.S = router_splits(d, c.E, Tp);
   b.dgates = static_cast<float*>(take(sizeof(float) * T * c.k));
   b.dz = static_cast<float*>(take(sizeof(float) * T * E));
-  b.dYe = static_cast<bf16_t*>(take(h2 * E * C * d));
+  const int64_t R = c.dropless ? T * c.k : E * C;   // rows of the expert buffers (packed when dropless)
+  b.dYe = static_cast<bf16_t*>(take(h2 * R * d));
   if (!c.save_preact) {
-    b.U = static_cast<bf16_t*>(take(h2 * E * C * F));
-    b.U2 = ga == 2 ? static_cast<bf16_t*>(take(h2 * E * C * F)) : nullptr;
+    b.U = static_cast<bf16_t*>(take(h2 * R * F));
+    b.U2 = ga == 2 ? static_cast<bf16_t*>(take(h2 * R * F)) : nullptr;
   }
-  b.dH = static_cast<bf16_t*>(take(h2 * E * C * F));
-  b.dact = static_cast<bf16_t*>(take(h2 * E * C * ga * F));
-  b.dA = static_cast<bf16_t*>(take(h2 * E * C * d));
+  b.dH = static_cast<bf16_t*>(take(h2 * R * F));
+  b.dact = static_cast<bf16_t*>(take(h2 * R * ga * F));
+  b.dA = static_cast<bf16_t*>(take(h2 * R * d));
+  if (c.dropless) {
+    b.pstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+    b.prow = static_cast<int32_t*>(take(sizeof(int32_t) * E * Cp));
+    b.pxrow = static_cast<int32_t*>(take(sizeof(int32_t) * E * Cp));
+  }
   b.woT = static_cast<bf16_t*>(take(h2 * E * F * d));
   b.wiT = static_cast<bf16_t*>(take(h2 * E * d * ga * F));
   b.dYeT = static_cast<bf16_t*>(take(h2 * E * d * Cp));
@@ -516,8 +525,8 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
 
 moe_status check_backward_config(const moe_config& c, int64_t C) {
   if (c.dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the backward pass is built for bf16 storage");
-  if (c.routing != MOE_TOKEN_CHOICE || c.dropless)
-    return fail(MOE_EUNSUPPORTED, "the backward pass is built for token choice with a capacity (not dropless)");
+  if (c.routing != MOE_TOKEN_CHOICE)
+    return fail(MOE_EUNSUPPORTED, "the backward pass is built for token choice (capacity or dropless)");
   const int64_t lim = int64_t{1} << 30;
   const int64_t ga = c.act == MOE_SWIGLU ? 2 : 1;
   const int64_t Fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
@@ -532,7 +541,8 @@ moe_status check_backward_config(const moe_config& c, int64_t C) {
 // C[g] = A[g] B[g]^T (+ bias) on the bf16 grouped GEMM, operands K-contiguous.
 moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, const int32_t* gather, int64_t a_rows,
                  const void* B, int64_t ldb, int64_t b_gs, const void* bias, void* Cout, const int32_t* rows,
-                 int64_t rpg, int groups, int N, int K, hipStream_t s) {
+                 int64_t rpg, int groups, int N, int K, hipStream_t s, const int32_t* kvar = nullptr,
+                 bool packed = false) {
   GemmArgs g{};
   g.A = A;
   g.lda = lda;
@@ -550,6 +560,9 @@ moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, con
   g.N = N;
   g.K = K;
   g.act = 0;
+  g.kvar = kvar;
+  g.packed = packed;
+  g.total_rows = packed ? rpg : 0;
   return hip_status(launch_gemm(g, MOE_BF16, s), what);
 }
 
@@ -994,7 +1007,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
     // packed rows: expert e's rows start after the counts of the lower experts
     if (c.T > 0)
       MOE_TRY(ffn(c, c.act, c.E, c.T * c.k, out->counts, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in,
-                  wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T));
+                  wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T, w.pre0, w.pre1));
   } else if (C > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, w.kept, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in, wt->w_out,
                 wt->b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart));
@@ -1113,6 +1126,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
   a.score = c.score;
   a.renorm = resolved_renorm(c);
   a.zero_fallback = c.dropped_output;
+  a.packed = c.dropless;
   a.alpha_aux = alpha_aux;
   a.alpha_z = alpha_z;
 
@@ -1148,34 +1162,39 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     MOE_TRY(hip_status(launch_slab_sum(b.slabs, gr->dw_router, d * E, S, s), "router weight slabs"));
   }
 
-  // routed experts (rows = kept per expert, gathered from x through row_token)
+  // routed experts: rows = kept per expert in [E, C] slabs, or (dropless)
+  // every choice in packed rows; gathered from x through row_token
   if (C > 0 && T > 0) {
-    const int32_t* kept = w.kept;
+    const bool dl = c.dropless != 0;
+    const int32_t* rows = dl ? fwd->counts : w.kept;   // rows of each expert
+    const int64_t R = dl ? T * c.k : E * C;            // rows of the expert buffers
+    const int64_t rpg = dl ? R : C;                    // GEMM rows per group (packed: the bound)
     const bf16_t* W_in = static_cast<const bf16_t*>(wt->w_in);
+    // the GEMMs over the expert rows: slabs, or packed rows
+    auto rgemm = [&](const char* what, const void* A, const int32_t* gather, int64_t a_rows, const void* B,
+                     const void* bias, void* out, int N, int K) -> moe_status {
+      return bgemm(what, A, 0, 0, gather, a_rows, B, 0, 0, bias, out, rows, rpg, E, N, K, s, nullptr, dl);
+    };
     if (c.save_preact) {
       // the forward pass kept them
     } else if (glu) {
-      MOE_TRY(bgemm("recompute gate projection", x, 0, 0, w.row_token, T, wt->w_gate, 0, 0, nullptr, b.U, kept, C, E,
-                    static_cast<int>(F), c.d, s));
-      MOE_TRY(bgemm("recompute up projection", x, 0, 0, w.row_token, T, wt->w_in, 0, 0, nullptr, b.U2, kept, C, E,
-                    static_cast<int>(F), c.d, s));
+      MOE_TRY(rgemm("recompute gate projection", x, w.row_token, T, wt->w_gate, nullptr, b.U, static_cast<int>(F), c.d));
+      MOE_TRY(rgemm("recompute up projection", x, w.row_token, T, wt->w_in, nullptr, b.U2, static_cast<int>(F), c.d));
     } else {
-      MOE_TRY(bgemm("recompute pre-activation", x, 0, 0, w.row_token, T, wt->w_in, 0, 0, wt->b_in, b.U, kept, C, E,
-                    static_cast<int>(F), c.d, s));
+      MOE_TRY(rgemm("recompute pre-activation", x, w.row_token, T, wt->w_in, wt->b_in, b.U, static_cast<int>(F), c.d));
     }
     // dH = dYe W_out: W_out [E, d, F] -> [E, F, d]
     MOE_TRY(transpose("w_out transpose", static_cast<const bf16_t*>(wt->w_out), b.woT, E, d, F, d, d * F, F, F * d, d,
                       nullptr, nullptr, 0, s));
-    MOE_TRY(bgemm("expert hidden gradient", b.dYe, 0, 0, nullptr, 0, b.woT, 0, 0, nullptr, b.dH, kept, C, E,
-                  static_cast<int>(F), c.d, s));
+    MOE_TRY(rgemm("expert hidden gradient", b.dYe, nullptr, 0, b.woT, nullptr, b.dH, static_cast<int>(F), c.d));
     ActBwdArgs ab{};
     ab.dH = b.dH;
     ab.U = c.save_preact ? static_cast<const bf16_t*>(w.pre0) : b.U;
     ab.U2 = c.save_preact ? static_cast<const bf16_t*>(w.pre1) : b.U2;
     ab.dact = b.dact;
-    ab.valid = kept;
-    ab.rpg = C;
-    ab.groups = E;
+    ab.valid = dl ? nullptr : rows;                    // packed rows are all valid
+    ab.rpg = dl ? R : C;
+    ab.groups = dl ? 1 : E;
     ab.F = static_cast<int>(F);
     MOE_TRY(hip_status(launch_act_bwd(ab, c.act, s), "activation backward"));
     // dA = dact W_in (SwiGLU: [dGp | dUp] [W_gate; W_up]): W -> [E, d, ga*F]
@@ -1187,30 +1206,41 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     } else {
       MOE_TRY(transpose("w_in transpose", W_in, b.wiT, E, F, d, F, F * d, d, d * F, F, nullptr, nullptr, 0, s));
     }
-    MOE_TRY(bgemm("expert input gradient", b.dact, 0, 0, nullptr, 0, b.wiT, 0, 0, nullptr, b.dA, kept, C, E, c.d,
-                  static_cast<int>(ga * F), s));
-    // dW_out = dYe^T H, dW_in = dact^T A: contraction over the kept rows,
-    // zero-padded to Cp
-    MOE_TRY(transpose("dYe transpose", b.dYe, b.dYeT, E, C, d, Cp, C * d, d, d * Cp, Cp, kept, nullptr, 0, s));
-    MOE_TRY(transpose("H transpose", static_cast<const bf16_t*>(w.h), b.HT, E, C, F, Cp, C * F, F, F * Cp, Cp, kept,
-                      nullptr, 0, s));
+    MOE_TRY(rgemm("expert input gradient", b.dact, nullptr, 0, b.wiT, nullptr, b.dA, c.d, static_cast<int>(ga * F)));
+    // dW_out = dYe^T H, dW_in = dact^T A: contraction over each expert's rows
+    // (its own extent, kvar), the transposed copies zero-padded to Cp
+    // (dropless: C = T); packed rows reach the transposes through row lists
+    const int32_t* plist = nullptr;
+    const int32_t* xlist = w.row_token;
+    if (dl) {
+      MOE_TRY(hip_status(launch_packed_lists(rows, b.pstart, w.row_token, b.prow, b.pxrow, E, Cp, s), "row lists"));
+      plist = b.prow;
+      xlist = b.pxrow;
+    }
+    const int64_t lgs = dl ? Cp : C;                   // row-list stride per group
+    MOE_TRY(transpose("dYe transpose", b.dYe, b.dYeT, E, C, d, Cp, C * d, d, d * Cp, Cp, rows, plist, lgs, s));
+    MOE_TRY(transpose("H transpose", static_cast<const bf16_t*>(w.h), b.HT, E, C, F, Cp, C * F, F, F * Cp, Cp, rows,
+                      plist, lgs, s));
     MOE_TRY(bgemm("w_out gradient", b.dYeT, 0, 0, nullptr, 0, b.HT, 0, 0, nullptr, gr->dw_out, nullptr, d, E,
-                  static_cast<int>(F), static_cast<int>(Cp), s));
+                  static_cast<int>(F), static_cast<int>(Cp), s, rows));
     MOE_TRY(transpose("activation-gradient transpose", b.dact, b.dactT, E, C, ga * F, Cp, C * ga * F, ga * F,
-                      ga * F * Cp, Cp, kept, nullptr, 0, s));
-    MOE_TRY(transpose("token rows transpose", static_cast<const bf16_t*>(x), b.AT, E, C, d, Cp, 0, d, d * Cp, Cp, kept,
-                      w.row_token, C, s));
+                      ga * F * Cp, Cp, rows, plist, lgs, s));
+    MOE_TRY(transpose("token rows transpose", static_cast<const bf16_t*>(x), b.AT, E, C, d, Cp, 0, d, d * Cp, Cp, rows,
+                      xlist, lgs, s));
     if (glu) {
       MOE_TRY(bgemm("w_gate gradient", b.dactT, Cp, 2 * F * Cp, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_gate, nullptr,
-                    F, E, c.d, static_cast<int>(Cp), s));
+                    F, E, c.d, static_cast<int>(Cp), s, rows));
       MOE_TRY(bgemm("w_up gradient", b.dactT + F * Cp, Cp, 2 * F * Cp, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_in,
-                    nullptr, F, E, c.d, static_cast<int>(Cp), s));
+                    nullptr, F, E, c.d, static_cast<int>(Cp), s, rows));
     } else {
       MOE_TRY(bgemm("w_in gradient", b.dactT, 0, 0, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_in, nullptr, F, E, c.d,
-                    static_cast<int>(Cp), s));
+                    static_cast<int>(Cp), s, rows));
     }
-    if (gr->db_out) MOE_TRY(hip_status(launch_colsum(b.dYe, gr->db_out, kept, E, C, d, 0, s), "b_out gradient"));
-    if (gr->db_in) MOE_TRY(hip_status(launch_colsum(b.dact, gr->db_in, kept, E, C, F, 0, s), "b_in gradient"));
+    const int32_t* starts = dl ? b.pstart : nullptr;
+    if (gr->db_out)
+      MOE_TRY(hip_status(launch_colsum(b.dYe, gr->db_out, rows, E, rpg, d, 0, s, starts), "b_out gradient"));
+    if (gr->db_in)
+      MOE_TRY(hip_status(launch_colsum(b.dact, gr->db_in, rows, E, rpg, F, 0, s, starts), "b_in gradient"));
   } else {
     // no expert row: every expert-weight gradient is zero
     const size_t ew = sizeof(bf16_t) * E * F * d;

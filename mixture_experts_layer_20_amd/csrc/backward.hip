@@ -91,8 +91,9 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(BwdArgs a) {
     const int64_t tk = t * a.k + lane;
     const int e = a.idx[tk];
     const int sl = a.slot[tk];
-    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < a.C;
-    myrow = static_cast<int64_t>(e) * a.C + sl;
+    // dropless: the slot is the packed row itself
+    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < (a.packed ? a.T * a.k : a.C);
+    myrow = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
     mygate = a.gates[tk];
   }
   const uint64_t kept = __ballot(keep);
@@ -329,13 +330,14 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(ActBwdArgs a) {
 // out[g*Cc + c] = sum over the first valid_g rows r of in[g*rpg + r][c],
 // float32 in row order, stored in the storage type (or float32 with f32out).
 __global__ __launch_bounds__(kThreads) void colsum_kernel(const bf16_t* __restrict__ in, void* out,
-                                                          const int32_t* valid, int64_t rpg, int64_t Cc,
-                                                          int f32out) {
+                                                          const int32_t* valid, const int32_t* start, int64_t rpg,
+                                                          int64_t Cc, int f32out) {
   const int g = blockIdx.y;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (c >= Cc) return;
   const int64_t nv = valid ? min<int64_t>(valid[g], rpg) : rpg;
-  const bf16_t* p = in + static_cast<int64_t>(g) * rpg * Cc + c;
+  // group g's rows: from g*rpg, or (packed) from start[g]
+  const bf16_t* p = in + (start ? static_cast<int64_t>(start[g]) : static_cast<int64_t>(g) * rpg) * Cc + c;
   float s = 0.0f;
   for (int64_t r = 0; r < nv; ++r) s += bf16_to_f32(p[r * Cc]);
   if (f32out) static_cast<float*>(out)[g * Cc + c] = s;
@@ -403,8 +405,9 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
     const int64_t tk = t * a.k + lane;
     const int e = a.idx[tk];
     const int sl = a.slot[tk];
-    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < a.C;
-    myrow = static_cast<int64_t>(e) * a.C + sl;
+    // dropless: the slot is the packed row itself
+    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < (a.packed ? a.T * a.k : a.C);
+    myrow = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
   }
   const uint64_t kept = __ballot(keep);
   float dzv[4];
@@ -451,6 +454,40 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
   }
 }
 
+// Dropless rows: start[g] = counts[0] + ... + counts[g-1] (one workgroup, E
+// <= 256), then the row lists of the weight-gradient transposes:
+// rows[g*kmax + r] = start[g] + r and xrows[g*kmax + r] = row_token[start[g]
+// + r] for r < counts[g].
+__global__ __launch_bounds__(kThreads) void packed_starts_kernel(const int32_t* __restrict__ counts,
+                                                                 int32_t* start, int E) {
+  __shared__ int v[kThreads];
+  const int tid = threadIdx.x;
+  const int c = tid < E ? counts[tid] : 0;
+  v[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int u = tid >= o ? v[tid - o] : 0;
+    __syncthreads();
+    v[tid] += u;
+    __syncthreads();
+  }
+  if (tid < E) start[tid] = v[tid] - c;
+  if (tid == E - 1) start[E] = v[tid];
+}
+
+__global__ __launch_bounds__(kThreads) void packed_lists_kernel(const int32_t* __restrict__ counts,
+                                                                const int32_t* __restrict__ start,
+                                                                const int32_t* __restrict__ row_token, int32_t* rows,
+                                                                int32_t* xrows, int64_t kmax) {
+  const int g = blockIdx.y;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (r >= kmax) return;
+  const int n = counts[g];
+  const int64_t p = static_cast<int64_t>(start[g]) + r;
+  rows[g * kmax + r] = r < n ? static_cast<int32_t>(p) : 0;
+  xrows[g * kmax + r] = r < n ? row_token[p] : 0;
+}
+
 __global__ __launch_bounds__(kThreads) void zero_kernel(uint16_t* p, int64_t n) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kThreads)
@@ -465,6 +502,15 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   if (n == 0) return hipSuccess;
   zero_kernel<<<static_cast<unsigned>(std::min<int64_t>(4096, (n + kThreads - 1) / kThreads)), kThreads, 0, s>>>(
       static_cast<uint16_t*>(p), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_packed_lists(const int32_t* counts, int32_t* start, const int32_t* row_token, int32_t* rows,
+                               int32_t* xrows, int E, int64_t kmax, hipStream_t s) {
+  packed_starts_kernel<<<1, kThreads, 0, s>>>(counts, start, E);
+  if (kmax == 0) return hipGetLastError();
+  const dim3 grid(static_cast<unsigned>((kmax + kThreads - 1) / kThreads), static_cast<unsigned>(E));
+  packed_lists_kernel<<<grid, kThreads, 0, s>>>(counts, start, row_token, rows, xrows, kmax);
   return hipGetLastError();
 }
 
@@ -505,10 +551,10 @@ hipError_t launch_act_bwd(const ActBwdArgs& a, int act, hipStream_t s) {
 }
 
 hipError_t launch_colsum(const bf16_t* in, void* out, const int32_t* valid, int groups, int64_t rpg, int64_t Cc,
-                         int f32out, hipStream_t s) {
+                         int f32out, hipStream_t s, const int32_t* start) {
   if (groups == 0 || Cc == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((Cc + kThreads - 1) / kThreads), static_cast<unsigned>(groups));
-  colsum_kernel<<<grid, kThreads, 0, s>>>(in, out, valid, rpg, Cc, f32out);
+  colsum_kernel<<<grid, kThreads, 0, s>>>(in, out, valid, start, rpg, Cc, f32out);
   return hipGetLastError();
 }
 

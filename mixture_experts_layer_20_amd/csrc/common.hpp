@@ -169,6 +169,10 @@ struct GemmArgs {
   int64_t kslice;
   float* kpart;
   int64_t kpart_stride;
+  // bf16 path, not packed: group g contracts over its first kvar[g] k only
+  // (rounded up to 8, at least 8; the operands must be zero from there to the
+  // rounded extent), e.g. a weight gradient over an expert's kept rows | null
+  const int32_t* kvar;
 };
 
 struct CombineArgs {
@@ -273,6 +277,7 @@ struct BwdArgs {
   int64_t T, C;
   int d, E, k;
   int score, renorm, zero_fallback;
+  int packed;                 // dropless: slot is the packed row of ye, dYe and dA
   float alpha_aux, alpha_z;
 };
 
@@ -312,7 +317,9 @@ hipError_t launch_combine_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_router_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_act_bwd(const ActBwdArgs& a, int act, hipStream_t s);
 hipError_t launch_colsum(const bf16_t* in, void* out, const int32_t* valid, int groups, int64_t rpg, int64_t Cc,
-                         int f32out, hipStream_t s);
+                         int f32out, hipStream_t s, const int32_t* start = nullptr);
+hipError_t launch_packed_lists(const int32_t* counts, int32_t* start, const int32_t* row_token, int32_t* rows,
+                               int32_t* xrows, int E, int64_t kmax, hipStream_t s);
 hipError_t launch_router_weight_prep(const float* dz, bf16_t* planes, int64_t T, int64_t Tp, int E,
                                      const float* w_router, float* wrT, int d, hipStream_t s);
 hipError_t launch_dz_colsum(const float* dz, float* out, int64_t T, int E, hipStream_t s);

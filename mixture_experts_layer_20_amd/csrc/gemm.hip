@@ -306,7 +306,11 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   const int64_t lda = a.lda ? a.lda : a.K, ldb = a.ldb ? a.ldb : a.K;
   // this tile's k range: [k0, k0 + K) of the operands' rows
   const int64_t k0 = static_cast<int64_t>(ks) * a.kslice;
-  const int K = ACT == 0 && a.ksplit > 1 ? static_cast<int>(min<int64_t>(a.kslice, a.K - k0)) : a.K;
+  // (or, with kvar, the group's own k extent: its count rounded up to 8, the
+  // operands being zero there; at least 8 so that an empty group sums zeros)
+  const int K = ACT == 0 && a.ksplit > 1 ? static_cast<int>(min<int64_t>(a.kslice, a.K - k0))
+                : a.kvar ? max(8, min(a.K, (max(a.kvar[tc.g], 0) + 7) / 8 * 8))
+                         : a.K;
   const bf16_t* A = static_cast<const bf16_t*>(a.A) + k0 +
                     (gathered ? 0
                      : a.packed ? row_base * lda

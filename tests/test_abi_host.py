@@ -275,7 +275,7 @@ def test_backward_configuration(moe):
     assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, **bf))) > 0
     # built for bf16 token choice with a capacity
     assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe))) == 0             # f32
-    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, dropless=True, **bf))) == 0
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, dropless=True, **bf))) > 0
     assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, routing='expert', **bf))) == 0
     c = cfg(moe)
     g = moe.moe_grads()
@@ -290,7 +290,8 @@ def test_backward_configuration(moe):
 def test_save_preact_configuration(moe):
     bf = dict(dtype='bf16')
     assert moe.moe_validate(cfg(moe, save_preact=True, **bf)) == 40
-    for bad in (dict(), dict(dropless=True, **bf), dict(routing='expert', **bf)):     # f32, dropless, expert choice
+    assert moe.moe_validate(cfg(moe, save_preact=True, dropless=True, **bf)) == 64
+    for bad in (dict(), dict(routing='expert', **bf)):                                  # f32, expert choice
         with pytest.raises(ValueError, match='save_preact'):
             moe.moe_validate(cfg(moe, save_preact=True, **bad))
     # the forward keeps them, the backward need not

@@ -81,7 +81,8 @@ def _run(moe, w, seed=0, **over):
     # the oracle on the same inputs
     dout = 'zero' if over.get('dropped_output') == 'zero' else 'residual'
     ov = over.get('capacity_override', 0)
-    fwd = O.moe_forward(w, inp, ex, sh, capacity_override=ov, dropped_output=dout)
+    fwd = O.moe_forward(w, inp, ex, sh, capacity_override=ov, dropped_output=dout,
+                        dropless=bool(over.get('dropless', False)))
     assert (np_of(out['idx']) == fwd['idx']).all(), 'routing differs from the oracle: pick another seed'
     np.testing.assert_array_equal(np_of(out['slot']), fwd['slot'])
     ref = B.moe_backward(w, inp, ex, sh, fwd, synth.as_f32(dy), ALPHA_AUX, ALPHA_Z, dropped_output=dout)
@@ -259,6 +260,30 @@ def test_saved_preactivations_equal_recomputation(moe, case):
     inp, ex, sh, dev, dy = _layer(moe, w, 0)
     out0, g0 = _gpu_pass(moe, w, dev, dy, **over)
     out1, g1 = _gpu_pass(moe, w, dev, dy, save_preact=True, **over)
+    for kk in out0:
+        assert torch.equal(out0[kk], out1[kk]), kk
+    for kk in g0:
+        assert torch.equal(g0[kk], g1[kk]), kk
+
+
+@pytest.mark.parametrize('case', [c for c in BWD_CASES if c[0] in ('gelu_renorm_drops', 'swiglu_renorm', 'sigmoid_shared',
+                                                                   'sigmoid_raw_ragged')], ids=lambda c: c[0])
+def test_backward_dropless(moe, case):
+    """Dropless mode: every choice kept in packed rows; the expert GEMMs run on
+    the packed rows and the weight gradients contract over each expert's own
+    row count (reached through per-expert row lists)."""
+    name, w, over = case
+    say('backward dropless', name)
+    grads, ref, fwd = _run(moe, w, dropless=True)
+    assert not fwd['dropped'].any()
+    _compare(w, grads, ref)
+
+
+def test_saved_preactivations_equal_recomputation_dropless(moe):
+    name, w, over = BWD_CASES[1]
+    inp, ex, sh, dev, dy = _layer(moe, w, 0)
+    out0, g0 = _gpu_pass(moe, w, dev, dy, dropless=True)
+    out1, g1 = _gpu_pass(moe, w, dev, dy, dropless=True, save_preact=True)
     for kk in out0:
         assert torch.equal(out0[kk], out1[kk]), kk
     for kk in g0:
