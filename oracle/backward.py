@@ -140,6 +140,83 @@ def router_backward(z, idx, dgates, score='softmax', renormalize=-1, f=None, alp
     return dz
 
 
+def probs_backward(z, dp, score='softmax'):
+    """d/dz of <dp, p> for the full router probabilities p (softmax, or the
+    sigmoid scores normalised over all experts, softmax of log sigma(z))."""
+    z = np.asarray(z, F64)
+    dp = np.asarray(dp, F64)
+    if score == 'softmax':
+        p = softmax(z)
+        return p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    q = softmax(log_sigmoid(z))
+    dls = q * (dp - (q * dp).sum(axis=1, keepdims=True))
+    return dls * np.exp(log_sigmoid(-z))                             # d log sigma(z)/dz = sigma(-z)
+
+
+def moe_backward_expert_choice(w, inp, experts, shared_experts, fwd, dy, alpha_aux=0.0, alpha_z=0.0,
+                               dropped_output='residual', exact=False):
+    """Gradients under expert-choice routing (``oracle.moe.expert_choice``):
+    y_t = sum over the experts e that picked t of p_te FFN_e(x_t); the gate
+    is the router probability itself, so the gate gradient of a pick lands on
+    p_te and reaches z through the probabilities' Jacobian.  The picks are
+    piecewise constant (no gradient); f_i = count_i / sum of counts.
+    Returns the same keys as ``moe_backward``, with dgates replaced by
+    dprobs [T,E] (the gradient of each picked probability, 0 elsewhere)."""
+    T, E, d = w.T, w.E, w.d
+    assert fwd['rows'].size == T, 'the backward pass needs the forward over every token'
+    dy = np.asarray(dy, F64)
+    x = np.asarray(inp['x'], F64) if exact else as_f32(inp['x']).astype(F64)
+    cast = (lambda wts: {kk: (None if v is None else np.asarray(v, F64)) for kk, v in wts.items()}) if exact \
+        else (lambda wts: {kk: (None if v is None else as_f32(v).astype(F64)) for kk, v in wts.items()})
+    get = experts if callable(experts) else (lambda e: {kk: v[e] for kk, v in experts.items()})
+    p = np.asarray(fwd['probs'], F64)
+    sel = fwd['sel']
+    dx = np.zeros((T, d), F64)
+    dp = np.zeros((T, E), F64)
+    grads = []
+    for e in range(E):
+        wts = cast(get(e))
+        t_e = np.nonzero(sel[:, e] >= 0)[0]
+        if t_e.size == 0:
+            grads.append({kk: np.zeros_like(np.asarray(v, F64)) for kk, v in wts.items() if v is not None})
+            continue
+        a = x[t_e]
+        _, o = expert_ffn(a, wts, w.act, w.dtype)
+        dp[t_e, e] = (dy[t_e] * o).sum(axis=1)
+        da, ge = expert_ffn_backward(a, wts, w.act, w.dtype, p[t_e, e][:, None] * dy[t_e])
+        np.add.at(dx, t_e, da)
+        if w.act == 'swiglu':
+            ge = {kk: ge[kk] for kk in ('w_gate', 'w_up', 'w_out')}
+        else:
+            ge = {kk: ge[kk] if wts.get(kk) is not None else None for kk in ('w_in', 'b_in', 'w_out', 'b_out')}
+        grads.append(ge)
+    sgrads = []
+    if shared_experts is not None and getattr(w, 'n_shared', 0) > 0:
+        gs = shared_experts if callable(shared_experts) else \
+            (lambda s: {kk: v[s] for kk, v in shared_experts.items()})
+        for s_ in range(w.n_shared):
+            da, ge = expert_ffn_backward(x, cast(gs(s_)), 'gelu', w.dtype, dy)
+            dx += da
+            sgrads.append(ge)
+    elif dropped_output == 'residual':
+        fb = ~(sel >= 0).any(axis=1)
+        dx[fb] += dy[fb]
+    z = np.asarray(fwd['logits'], F64)
+    counts = (sel >= 0).sum(axis=0).astype(F64)
+    v = np.zeros(E, F64)
+    if alpha_aux:
+        v = alpha_aux * E * (counts / max(1.0, counts.sum())) / T            # dL_aux/dp_ti
+    dz = probs_backward(z, dp + v[None, :], w.score)
+    if alpha_z:
+        m = z.max(axis=1, keepdims=True)
+        lse = m[:, 0] + np.log(np.exp(z - m).sum(axis=1))
+        dz += alpha_z * 2.0 * lse[:, None] * softmax(z) / T
+    wr = np.asarray(inp['w_router'], F64)
+    dx += dz @ wr.T
+    return dict(dx=dx, dw_router=x.T @ dz, dlogit_bias=dz.sum(axis=0), dprobs=dp, dz=dz, experts=grads,
+                shared=sgrads)
+
+
 def moe_backward(w, inp, experts, shared_experts, fwd, dy, alpha_aux=0.0, alpha_z=0.0,
                  dropped_output='residual', exact=False):
     """Gradients of L = <dy, y> + alpha_aux L_aux + alpha_z L_z for the layer

@@ -479,7 +479,7 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
     lse = logsumexp(z)
     if routing == 'expert':
         return _expert_choice_forward(w, inp, experts, shared_experts, rows, capacity_override,
-                                      dropped_output, z, idx, g, probs, lse)
+                                      dropped_output, z, idx, g, probs, lse, exact)
     if dropless:
         C = T
         slot, counts, row_token = dropless_rows(idx, E, priority)
@@ -534,7 +534,7 @@ def moe_forward(w, inp, experts, shared_experts=None, rows=None, priority='rank'
 
 
 def _expert_choice_forward(w, inp, experts, shared_experts, rows, capacity_override, dropped_output,
-                           z, idx, g, probs, lse):
+                           z, idx, g, probs, lse, exact=False):
     """The layer under expert-choice routing (see ``expert_choice``): y_t is
     the sum over the experts that picked t of p_te * FFN_e(x_t) (+ shared
     experts); a token no expert picked passes through (or 0) as under token
@@ -547,14 +547,16 @@ def _expert_choice_forward(w, inp, experts, shared_experts, rows, capacity_overr
     sel_rows[rows] = True
     pos = np.full(T, -1, np.int64)
     pos[rows] = np.arange(rows.size)
-    xa = as_f32(inp['x'])
+    xa = np.asarray(inp['x'], F64) if exact else as_f32(inp['x'])
+    wcast = (lambda wts: {kk: (None if v is None else np.asarray(v, F64)) for kk, v in wts.items()}) \
+        if exact else _f32_weights
     get = experts if callable(experts) else (lambda e: {kk: v[e] for kk, v in experts.items()})
     routed = np.zeros((rows.size, d), F64)
     for e in range(E):
         t_e = row_token[e][sel_rows[row_token[e]]]
         if t_e.size == 0:
             continue
-        _, o = expert_ffn(xa[t_e].astype(F64), _f32_weights(get(e)), w.act, w.dtype)
+        _, o = expert_ffn(xa[t_e].astype(F64), wcast(get(e)), w.act, w.dtype)
         routed[pos[t_e]] += probs[t_e, e][:, None] * o
     S = None
     if shared_experts is not None and getattr(w, 'n_shared', 0) > 0:
@@ -562,7 +564,7 @@ def _expert_choice_forward(w, inp, experts, shared_experts, rows, capacity_overr
             (lambda s_: {kk: v[s_] for kk, v in shared_experts.items()})
         S = np.zeros((rows.size, d), F64)
         for s_ in range(w.n_shared):
-            _, o = expert_ffn(xa[rows].astype(F64), _f32_weights(gs(s_)), 'gelu', w.dtype)
+            _, o = expert_ffn(xa[rows].astype(F64), wcast(gs(s_)), 'gelu', w.dtype)
             S += o
     picked = (sel >= 0).any(axis=1)
     y = round_store(combine(routed, S, xa[rows], picked[rows], dropped_output), w.dtype)

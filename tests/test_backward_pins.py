@@ -178,3 +178,60 @@ def test_router_backward_on_some_rows_equals_those_rows_of_the_batch(score, ren)
     rows = np.array([0, 7, 8, 31, 39])
     part = B.router_backward(z[rows], idx[rows], dg[rows], score, ren, f, 0.3, 0.2, n_tokens=T)
     np.testing.assert_allclose(part, full[rows], rtol=1e-14, atol=1e-17)
+
+
+EC_FD_CASES = [
+    ('ec_gelu_softmax', synth.Workload('ea', T=24, d=8, E=4, k=2, d_ff=12, act='gelu', score='softmax',
+                                       renormalize=-1, cf=1.0, dtype='f64', seed=91), {}),
+    ('ec_swiglu_sigmoid', synth.Workload('eb', T=20, d=8, E=5, k=2, d_ff=8, act='swiglu', score='sigmoid',
+                                         renormalize=1, cf=1.0, dtype='f64', seed=92), {}),
+    ('ec_shared', synth.Workload('ec', T=16, d=8, E=4, k=1, d_ff=8, act='gelu', score='softmax', renormalize=-1,
+                                 cf=1.0, dtype='f64', seed=93, n_shared=1, d_ff_shared=8), {}),
+    ('ec_fallback', synth.Workload('ed', T=16, d=8, E=4, k=1, d_ff=8, act='gelu', score='softmax', renormalize=-1,
+                                   cf=1.0, dtype='f64', seed=94), dict(capacity_override=2)),
+]
+
+
+@pytest.mark.parametrize('case', EC_FD_CASES, ids=[c[0] for c in EC_FD_CASES])
+def test_expert_choice_backward_matches_finite_differences(case):
+    """Expert choice: the gate of a pick is the router probability itself; a
+    central difference of the forward definition (picks held fixed inside
+    +-h) matches the analytic gradient of every parameter."""
+    name, w, over = case
+    over = dict(over, routing='expert')
+    inp, ex, sh, dy = _layer(w)
+    L0, f0 = _loss(w, inp, ex, sh, dy, over)
+    g = B.moe_backward_expert_choice(w, inp, ex, sh, f0, dy, ALPHA_AUX, ALPHA_Z, exact=True)
+    rng = np.random.default_rng(17)
+    h = 1e-6
+
+    def check(kind, get_param, set_param, grad):
+        p0 = get_param()
+        v = rng.standard_normal(p0.shape)
+        set_param(p0 + h * v)
+        Lp, fp = _loss(w, inp, ex, sh, dy, over)
+        set_param(p0 - h * v)
+        Lm, fm = _loss(w, inp, ex, sh, dy, over)
+        set_param(p0)
+        for ff in (fp, fm):
+            assert (ff['sel'] == f0['sel']).all(), kind
+        fd = (Lp - Lm) / (2 * h)
+        an = float((np.asarray(grad) * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (kind, fd, an)
+
+    def setter(d_, key):
+        def s_(val):
+            d_[key] = val
+        return s_
+
+    check('x', lambda: inp['x'].copy(), setter(inp, 'x'), g['dx'])
+    check('w_router', lambda: np.asarray(inp['w_router'], np.float64).copy(), setter(inp, 'w_router'), g['dw_router'])
+    for kk in ex:
+        check('expert ' + kk, lambda kk=kk: ex[kk].copy(), setter(ex, kk), np.stack([g['experts'][e][kk]
+                                                                                      for e in range(w.E)]))
+    if sh is not None:
+        for kk in sh:
+            check('shared ' + kk, lambda kk=kk: sh[kk].copy(), setter(sh, kk),
+                  np.stack([g['shared'][s_][kk] for s_ in range(w.n_shared)]))
+    if name == 'ec_fallback':
+        assert (~(f0['sel'] >= 0).any(axis=1)).any()                     # some token is picked by no expert
