@@ -99,7 +99,7 @@ typedef struct moe_config {
   int32_t routing;            /* moe_routing: token choice (above) or expert choice    */
   int32_t save_preact;        /* 1: moe_forward also keeps the expert pre-activations in
                                  its workspace, so moe_backward need not recompute them
-                                 (bf16 token choice only)                             */
+                                 (bf16 only)                                          */
 } moe_config;
 
 /* Score priority (priority = MOE_SCORE_PRIORITY) ["Lab 18" s.3: who is
@@ -381,7 +381,8 @@ typedef struct moe_grads {
   void* dws_out;              /* [d, n_shared*Fs]                                     */
   void* dbs_out;              /* [d] or NULL: the gradient of EACH shared expert's
                                  output bias (the forward adds their sum)             */
-  float* dgates;              /* [T,k] float32 or NULL                                */
+  float* dgates;              /* [T,k] float32 or NULL; expert choice: [T,E], the
+                                 gradient of each picked probability (0 elsewhere)    */
   float* dlogits;             /* [T,E] float32 or NULL                                */
 } moe_grads;
 
@@ -401,11 +402,16 @@ MOE_API size_t moe_backward_workspace_bytes(const moe_config* cfg);
  *     pre-activations are recomputed, or read from the forward's workspace
  *     when cfg->save_preact is 1 (bit-identical values: the same products
  *     summed in the same order);
- *   - built for bf16 storage and token choice, with a capacity or dropless
- *     (packed rows): MOE_EUNSUPPORTED otherwise.
+ *   - expert choice ["Lab 18" exercise 1 and "Common extensions"]: the gate
+ *     of a pick is the router probability itself, so its gradient reaches
+ *     the logits through the probabilities' Jacobian (softmax, or the
+ *     sigmoid scores normalised over all experts); the picks carry none;
+ *   - built for bf16 storage: token choice with a capacity or dropless
+ *     (packed rows), or expert choice; MOE_EUNSUPPORTED otherwise.
  *   x, weights    the forward's inputs
  *   fwd           the forward's outputs: idx, gates, slot, dropped, counts and
- *                 logits are read (logits required)
+ *                 logits are read (logits required); expert choice: sel,
+ *                 counts, logits, and probs when the forward was given it
  *   fwd_ws        the forward's workspace, unchanged since that call (its
  *                 expert rows, hidden activations and outputs are read)
  *   dy            [T,d] storage type

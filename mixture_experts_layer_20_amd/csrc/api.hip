@@ -83,8 +83,8 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
   if (c.routing == MOE_EXPERT_CHOICE && c.dropless)
     return fail(MOE_EINVAL, "expert-choice routing has no dropless mode (no choice is ever dropped)");
   if (c.save_preact != 0 && c.save_preact != 1) return fail(MOE_EINVAL, "save_preact must be 0 or 1");
-  if (c.save_preact && (c.dtype != MOE_BF16 || c.routing != MOE_TOKEN_CHOICE))
-    return fail(MOE_EINVAL, "save_preact is built for bf16 token choice (the backward pass's mode)");
+  if (c.save_preact && c.dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "save_preact is built for bf16 storage (the backward pass's mode)");
   if (c.capacity_override < 0) return fail(MOE_EINVAL, "capacity_override must be >= 0");
   if (!c.dropless && c.capacity_override == 0 && !(c.capacity_factor >= 1.0))
     return fail(MOE_EINVAL,
@@ -401,10 +401,10 @@ moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weigh
   MOE_TRY(hip_status(launch_expert_choice(e, s), "expert choice"));   // T = 0: zero counts and sums
   if (c.T > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, out.counts, x, w.row_token, c.T, wt.w_in, wt.w_gate, wt.b_in, wt.w_out,
-                wt.b_out, c.d_ff, w.h, w.ye, s, false, 0, nullptr, nullptr, w.kpart));
+                wt.b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart));
     if (c.n_shared > 0)
       MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt.ws_in, nullptr, wt.bs_in, wt.ws_out,
-                  wt.bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s));
+                  wt.bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s, false, 0, w.pres));
     CombineArgs cb{};
     cb.x = x;
     cb.ye = w.ye;
@@ -482,7 +482,9 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   };
   const size_t h2 = sizeof(bf16_t);
   b.S = router_splits(d, c.E, Tp);
-  b.dgates = static_cast<float*>(take(sizeof(float) * T * c.k));
+  // expert choice: the gate gradients are those of the probabilities, [T,E]
+  const int64_t ng = c.routing == MOE_EXPERT_CHOICE ? E : c.k;
+  b.dgates = static_cast<float*>(take(sizeof(float) * T * ng));
   b.dz = static_cast<float*>(take(sizeof(float) * T * E));
   const int64_t R = c.dropless ? T * c.k : E * C;   // rows of the expert buffers (packed when dropless)
   b.dYe = static_cast<bf16_t*>(take(h2 * R * d));
@@ -525,8 +527,6 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
 
 moe_status check_backward_config(const moe_config& c, int64_t C) {
   if (c.dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the backward pass is built for bf16 storage");
-  if (c.routing != MOE_TOKEN_CHOICE)
-    return fail(MOE_EUNSUPPORTED, "the backward pass is built for token choice (capacity or dropless)");
   const int64_t lim = int64_t{1} << 30;
   const int64_t ga = c.act == MOE_SWIGLU ? 2 : 1;
   const int64_t Fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
@@ -1072,10 +1072,13 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     MOE_TRY(check_ptr(wt->ws_out, "ws_out", 16));
     MOE_TRY(check_ptr(wt->bs_in, "bs_in", 2, false));
   }
-  MOE_TRY(check_ptr(fwd->idx, "fwd idx", 4, needT));
-  MOE_TRY(check_ptr(fwd->gates, "fwd gates", 4, needT));
-  MOE_TRY(check_ptr(fwd->slot, "fwd slot", 4, needT));
-  MOE_TRY(check_ptr(fwd->dropped, "fwd dropped", 1, needT));
+  const bool ec = c.routing == MOE_EXPERT_CHOICE;
+  MOE_TRY(check_ptr(fwd->idx, "fwd idx", 4, needT && !ec));
+  MOE_TRY(check_ptr(fwd->gates, "fwd gates", 4, needT && !ec));
+  MOE_TRY(check_ptr(fwd->slot, "fwd slot", 4, needT && !ec));
+  MOE_TRY(check_ptr(fwd->dropped, "fwd dropped", 1, needT && !ec));
+  MOE_TRY(check_ptr(fwd->sel, "fwd sel", 4, needT && ec));
+  MOE_TRY(check_ptr(fwd->probs, "fwd probs", 4, false));
   MOE_TRY(check_ptr(fwd->counts, "fwd counts", 4));
   MOE_TRY(check_ptr(fwd->logits, "fwd logits", 4, needT));
   MOE_TRY(check_ptr(gr->dx, "dx", 16, needT));
@@ -1122,9 +1125,17 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
   a.C = C;
   a.d = c.d;
   a.E = E;
-  a.k = c.k;
+  a.k = ec ? 0 : c.k;
   a.score = c.score;
   a.renorm = resolved_renorm(c);
+  if (ec) {
+    // the forward kept the probabilities in the caller's buffer when given,
+    // else in its workspace; every expert picked min(C, T) tokens
+    a.sel = fwd->sel;
+    a.probs = fwd->probs ? fwd->probs : w.ec_probs;
+    a.dprobs = a.dgates;
+    a.fden = static_cast<int64_t>(E) * std::min<int64_t>(C, T);
+  }
   a.zero_fallback = c.dropped_output;
   a.packed = c.dropless;
   a.alpha_aux = alpha_aux;
@@ -1162,11 +1173,12 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     MOE_TRY(hip_status(launch_slab_sum(b.slabs, gr->dw_router, d * E, S, s), "router weight slabs"));
   }
 
-  // routed experts: rows = kept per expert in [E, C] slabs, or (dropless)
-  // every choice in packed rows; gathered from x through row_token
+  // routed experts: rows = kept (expert choice: picked) per expert in [E, C]
+  // slabs, or (dropless) every choice in packed rows; gathered from x
+  // through row_token
   if (C > 0 && T > 0) {
     const bool dl = c.dropless != 0;
-    const int32_t* rows = dl ? fwd->counts : w.kept;   // rows of each expert
+    const int32_t* rows = dl || ec ? fwd->counts : w.kept;   // rows of each expert
     const int64_t R = dl ? T * c.k : E * C;            // rows of the expert buffers
     const int64_t rpg = dl ? R : C;                    // GEMM rows per group (packed: the bound)
     const bf16_t* W_in = static_cast<const bf16_t*>(wt->w_in);

@@ -80,32 +80,66 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs a) 
 // One wavefront per token; lanes j < k hold choice j.  For each kept choice:
 // dgate = <dy_t, ye row> (per-lane partial sums over 16-byte chunks, then a
 // fixed butterfly), and the gate-scaled dy_t goes to the choice's dYe row.
+// The choices of token t on the lanes of its wavefront.  Token choice: lane
+// j < k holds choice j (kBal = 1).  Expert choice: lane l holds experts l,
+// l + 64, ... (kBal = 4 ballots, E <= 256).
+template <bool EC>
+struct Picks {
+  static constexpr int kBal = EC ? 4 : 1;
+  int64_t row[kBal];
+  float gate[kBal];
+  uint64_t kept[kBal];
+  __device__ Picks(const BwdArgs& a, int64_t t, int lane) {
+#pragma unroll
+    for (int b = 0; b < kBal; ++b) {
+      row[b] = 0;
+      gate[b] = 0.0f;
+      bool keep = false;
+      if constexpr (EC) {
+        const int e = b * kWave + lane;
+        if (e < a.E) {
+          const int sl = a.sel[t * a.E + e];
+          keep = sl >= 0 && sl < a.C;
+          row[b] = static_cast<int64_t>(e) * a.C + sl;
+          gate[b] = a.probs[t * a.E + e];
+        }
+      } else if (lane < a.k) {
+        const int64_t tk = t * a.k + lane;
+        const int e = a.idx[tk];
+        const int sl = a.slot[tk];
+        // dropless: the slot is the packed row itself
+        keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < (a.packed ? a.T * a.k : a.C);
+        row[b] = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
+        gate[b] = a.gates[tk];
+      }
+      kept[b] = __ballot(keep);
+    }
+  }
+  __device__ bool any() const {
+    uint64_t m = 0;
+#pragma unroll
+    for (int b = 0; b < kBal; ++b) m |= kept[b];
+    return m != 0;
+  }
+};
+
+template <bool EC>
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(BwdArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
   if (t >= a.T) return;
-  int64_t myrow = 0;
-  float mygate = 0.0f;
-  bool keep = false;
-  if (lane < a.k) {
-    const int64_t tk = t * a.k + lane;
-    const int e = a.idx[tk];
-    const int sl = a.slot[tk];
-    // dropless: the slot is the packed row itself
-    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < (a.packed ? a.T * a.k : a.C);
-    myrow = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
-    mygate = a.gates[tk];
-  }
-  const uint64_t kept = __ballot(keep);
+  const Picks<EC> pk(a, t, lane);
   const int nvec = a.d / 8;
   const uint4* dy = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.dy) + t * a.d);
-  float mydg = 0.0f;
-  uint64_t rest = kept;
+  float mydg[Picks<EC>::kBal] = {};
+#pragma unroll
+  for (int bal = 0; bal < Picks<EC>::kBal; ++bal) {
+  uint64_t rest = pk.kept[bal];
   while (rest) {
     const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
     rest &= rest - 1;
-    const int64_t row = __shfl(myrow, j, kWave);
-    const float g = __shfl(mygate, j, kWave);
+    const int64_t row = __shfl(pk.row[bal], j, kWave);
+    const float g = __shfl(pk.gate[bal], j, kWave);
     const uint4* ye = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.ye) + row * a.d);
     uint4* dye = reinterpret_cast<uint4*>(a.dYe + row * a.d);
     float part = 0.0f;
@@ -124,9 +158,18 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(BwdArgs a) {
       dye[c] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     part = wave_sum(part);
-    if (lane == j) mydg = part;
+    if (lane == j) mydg[bal] = part;
   }
-  if (lane < a.k) a.dgates[t * a.k + lane] = mydg;   // dropped choices: 0
+  }
+  if constexpr (EC) {
+#pragma unroll
+    for (int bal = 0; bal < Picks<EC>::kBal; ++bal) {
+      const int e = bal * kWave + lane;
+      if (e < a.E) a.dprobs[t * a.E + e] = mydg[bal];  // not picked: 0
+    }
+  } else if (lane < a.k) {
+    a.dgates[t * a.k + lane] = mydg[0];               // dropped choices: 0
+  }
 }
 
 // ------------------------------------------------------------------ router
@@ -174,7 +217,53 @@ __global__ __launch_bounds__(kThreads) void router_bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = 0; m < kPer; ++m) p[m] = ex[m] / sum;
   const bool ren = a.renorm != 0;
-  if (a.score == MOE_SOFTMAX) {
+  if (a.sel) {
+    // expert choice: the gates are the probabilities themselves, so the pick
+    // gradients and the balance term both go through the probabilities'
+    // Jacobian: dz = q (u - <q, u>) [x s(-z) for sigmoid scores], u = dprobs + v
+    float q[kPer], u[kPer], qu = 0.0f;
+    if (a.score == MOE_SOFTMAX) {
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) q[m] = p[m];
+    } else {
+      float lmax = -__builtin_huge_valf(), ssum = 0.0f;
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        q[m] = z[m] < 0.0f ? z[m] - log1pf(__expf(z[m])) : -log1pf(__expf(-z[m]));
+        if (lane + kWave * m < E) lmax = fmaxf(lmax, q[m]);
+      }
+      lmax = wave_max(lmax);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) {
+        q[m] = lane + kWave * m < E ? __expf(q[m] - lmax) : 0.0f;
+        ssum += q[m];
+      }
+      ssum = wave_sum(ssum);
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) q[m] /= ssum;
+    }
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int e = lane + kWave * m;
+      u[m] = 0.0f;
+      if (e < E) {
+        u[m] = a.dprobs[t * E + e];
+        if (a.alpha_aux != 0.0f)
+          u[m] += static_cast<float>(static_cast<double>(a.alpha_aux) * E *
+                                     (static_cast<double>(a.counts[e]) / static_cast<double>(a.fden)) /
+                                     static_cast<double>(a.T));
+      }
+      qu += q[m] * u[m];
+    }
+    qu = wave_sum(qu);
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      if (lane + kWave * m >= E) continue;
+      float term = q[m] * (u[m] - qu);
+      if (a.score != MOE_SOFTMAX) term *= 1.0f / (1.0f + __expf(z[m]));    // s(-z)
+      dz[m] = term;
+    }
+  } else if (a.score == MOE_SOFTMAX) {
     if (ren) {
       // g = softmax over the selected logits (shifted by their own maximum):
       // dz_sel = g (dg - <g, dg>)
@@ -242,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void router_bwd_kernel(BwdArgs a) {
     }
   }
   // balance loss: dL/dp_ti = alpha E f_i / T, f_i = count_i / (T k)
-  if (a.alpha_aux != 0.0f) {
+  if (a.alpha_aux != 0.0f && !a.sel) {
     float v[kPer], q[kPer], qv = 0.0f;
     if (a.score == MOE_SOFTMAX) {
 #pragma unroll
@@ -395,21 +484,12 @@ __global__ __launch_bounds__(kThreads) void wr_transpose_kernel(const float* __r
 // One wavefront per token, 8 columns per lane per round:
 //   dx_t = sum_j kept dA[row_j] (j order) + dAs_t (shared) | dy_t (fallback,
 //          residual) + sum_e dz_te W_r[:, e]
+template <bool EC>
 __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave;
   if (t >= a.T) return;
-  int64_t myrow = 0;
-  bool keep = false;
-  if (lane < a.k) {
-    const int64_t tk = t * a.k + lane;
-    const int e = a.idx[tk];
-    const int sl = a.slot[tk];
-    // dropless: the slot is the packed row itself
-    keep = !a.dropped[tk] && e >= 0 && e < a.E && sl >= 0 && sl < (a.packed ? a.T * a.k : a.C);
-    myrow = a.packed ? static_cast<int64_t>(sl) : static_cast<int64_t>(e) * a.C + sl;
-  }
-  const uint64_t kept = __ballot(keep);
+  const Picks<EC> pk(a, t, lane);
   float dzv[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -417,12 +497,17 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
     dzv[m] = e < a.E ? a.dz[t * a.E + e] : 0.0f;
   }
   const int nvec = a.d / 8;
-  const bool fallback = kept == 0 && a.dAs == nullptr && !a.zero_fallback;
-  for (int c = lane; c < nvec; c += kWave) {
+  const bool fallback = !pk.any() && a.dAs == nullptr && !a.zero_fallback;
+  // every lane runs every round (the shuffles below read all lanes); the
+  // loads and the store are those of the lanes whose column c is in the row
+  for (int c0 = 0; c0 < nvec; c0 += kWave) {
+    const int c = c0 + lane;
+    const bool on = c < nvec;
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
     auto add_row = [&](const bf16_t* base) {
+      if (!on) return;
       const uint4 u = reinterpret_cast<const uint4*>(base)[c];
       const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -431,16 +516,20 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
         acc[2 * q + 1] += __uint_as_float(uu[q] & 0xFFFF0000u);
       }
     };
-    uint64_t rest = kept;
-    while (rest) {
-      const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
-      rest &= rest - 1;
-      add_row(a.dA + __shfl(myrow, j, kWave) * a.d);
+#pragma unroll
+    for (int bal = 0; bal < Picks<EC>::kBal; ++bal) {
+      uint64_t rest = pk.kept[bal];
+      while (rest) {
+        const int j = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+        rest &= rest - 1;
+        add_row(a.dA + __shfl(pk.row[bal], j, kWave) * a.d);
+      }
     }
     if (a.dAs) add_row(a.dAs + t * a.d);
     else if (fallback) add_row(static_cast<const bf16_t*>(a.dy) + t * a.d);
     for (int e = 0; e < a.E; ++e) {
       const float g = __shfl(dzv[e / kWave], e % kWave, kWave);
+      if (!on) continue;
       const float4* w = reinterpret_cast<const float4*>(a.wrT + static_cast<int64_t>(e) * a.d + c * 8);
       const float4 w0 = w[0], w1 = w[1];
       acc[0] += g * w0.x; acc[1] += g * w0.y; acc[2] += g * w0.z; acc[3] += g * w0.w;
@@ -450,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       o[q] = static_cast<uint32_t>(f32_to_bf16(acc[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * q + 1])) << 16);
-    reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.dx) + t * a.d)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    if (on) reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.dx) + t * a.d)[c] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -529,7 +618,10 @@ hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
 hipError_t launch_combine_bwd(const BwdArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const unsigned grid = static_cast<unsigned>((a.T + 3) / 4);
-  combine_bwd_kernel<<<grid, kThreads, 0, s>>>(a);
+  if (a.sel)
+    combine_bwd_kernel<true><<<grid, kThreads, 0, s>>>(a);
+  else
+    combine_bwd_kernel<false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -582,7 +674,10 @@ hipError_t launch_slab_sum(const float* slabs, float* out, int64_t n, int S, hip
 
 hipError_t launch_dx(const BwdArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  dx_kernel<<<static_cast<unsigned>((a.T + 3) / 4), kThreads, 0, s>>>(a);
+  if (a.sel)
+    dx_kernel<true><<<static_cast<unsigned>((a.T + 3) / 4), kThreads, 0, s>>>(a);
+  else
+    dx_kernel<false><<<static_cast<unsigned>((a.T + 3) / 4), kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

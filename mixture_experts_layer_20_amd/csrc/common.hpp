@@ -279,6 +279,13 @@ struct BwdArgs {
   int score, renorm, zero_fallback;
   int packed;                 // dropless: slot is the packed row of ye, dYe and dA
   float alpha_aux, alpha_z;
+  // expert choice (sel != null): the picks of token t are the experts e with
+  // sel[t*E + e] >= 0 (row e*C + sel), gate probs[t*E + e]; the gate
+  // gradients go to dprobs [T,E] (0 where not picked) instead of dgates
+  const int32_t* sel;
+  const float* probs;
+  float* dprobs;
+  int64_t fden;               // expert choice: the sum of the picks (f_i = counts_i / fden)
 };
 
 struct ActBwdArgs {

@@ -273,10 +273,10 @@ def test_backward_configuration(moe):
     lib = moe._lib
     bf = dict(dtype='bf16')
     assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, **bf))) > 0
-    # built for bf16 token choice with a capacity
+    # built for bf16: token choice with a capacity or dropless, expert choice
     assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe))) == 0             # f32
     assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, dropless=True, **bf))) > 0
-    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, routing='expert', **bf))) == 0
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(cfg(moe, routing='expert', **bf))) > 0
     c = cfg(moe)
     g = moe.moe_grads()
     assert lib.moe_backward(ctypes.byref(c), None, None, None, None, None, 0.0, 0.0, ctypes.byref(g), None,
@@ -291,9 +291,9 @@ def test_save_preact_configuration(moe):
     bf = dict(dtype='bf16')
     assert moe.moe_validate(cfg(moe, save_preact=True, **bf)) == 40
     assert moe.moe_validate(cfg(moe, save_preact=True, dropless=True, **bf)) == 64
-    for bad in (dict(), dict(routing='expert', **bf)):                                  # f32, expert choice
-        with pytest.raises(ValueError, match='save_preact'):
-            moe.moe_validate(cfg(moe, save_preact=True, **bad))
+    assert moe.moe_validate(cfg(moe, save_preact=True, routing='expert', **bf)) > 0
+    with pytest.raises(ValueError, match='save_preact'):
+        moe.moe_validate(cfg(moe, save_preact=True))                                    # f32
     # the forward keeps them, the backward need not
     assert moe.moe_workspace_bytes(cfg(moe, save_preact=True, **bf)) > moe.moe_workspace_bytes(cfg(moe, **bf))
     assert moe.moe_backward_workspace_bytes(cfg(moe, save_preact=True, **bf)) < \

@@ -134,6 +134,10 @@ BWD_CASES = [
      dict(capacity_override=40, dropped_output='zero')),
     ('sigmoid_raw_ragged', synth.Workload('bf', T=333, d=64, E=8, k=2, d_ff=72, act='gelu', score='sigmoid',
                                           renormalize=0, cf=1.25, dtype='bf16', seed=66), {}),
+    # more experts than 16-byte column chunks of a row (E > d/8): the input
+    # gradient's router term reads dL/dz of every expert from every lane
+    ('narrow_rows_many_experts', synth.Workload('bg', T=256, d=64, E=48, k=4, d_ff=64, act='gelu',
+                                                score='softmax', renormalize=-1, cf=1.0, dtype='bf16', seed=68), {}),
 ]
 
 
@@ -256,7 +260,7 @@ def test_backward_full_size_sampled(moe, name):
             _check(f'dw_in[{e}][{f}]', g_in[e][f], (dh * B.gelu_grad(u)) @ a)
         _check(f'dw_out[{e}][:, {f}]', g_out[e][:, f], d_out.T @ h)
 
-def _gpu_pass(moe, w, dev, dy, **over):
+def _gpu_pass(moe, w, dev, dy, k_grads=None, **over):
     cfg = moe.config_from_workload(w, **over)
     out = moe.alloc_outputs(cfg, DEV, logits=True)
     ws = moe.workspace(cfg, DEV)
@@ -266,7 +270,7 @@ def _gpu_pass(moe, w, dev, dy, **over):
     bf = torch.bfloat16
     grads = dict(dx=torch.empty(T, d, dtype=bf, device=DEV), dw_router=torch.empty(d, E, device=DEV),
                  dw_in=torch.empty(E, F, d, dtype=bf, device=DEV), dw_out=torch.empty(E, d, F, dtype=bf, device=DEV),
-                 dgates=torch.empty(T, w.k, device=DEV), dlogits=torch.empty(T, E, device=DEV))
+                 dgates=torch.empty(T, k_grads or w.k, device=DEV), dlogits=torch.empty(T, E, device=DEV))
     if w.act == 'swiglu':
         grads['dw_gate'] = torch.empty(E, F, d, dtype=bf, device=DEV)
     else:
@@ -318,5 +322,108 @@ def test_saved_preactivations_equal_recomputation_dropless(moe):
     out1, g1 = _gpu_pass(moe, w, dev, dy, dropless=True, save_preact=True)
     for kk in out0:
         assert torch.equal(out0[kk], out1[kk]), kk
+    for kk in g0:
+        assert torch.equal(g0[kk], g1[kk]), kk
+
+
+# ----------------------------------------------------------------------------- expert choice
+EC_BWD_CASES = [
+    ('ec_gelu_fallback', synth.Workload('ea', T=600, d=128, E=8, k=2, d_ff=256, act='gelu', score='softmax',
+                                        renormalize=-1, cf=1.0, dtype='bf16', seed=71), {}),
+    ('ec_swiglu_sigmoid', synth.Workload('eb', T=400, d=256, E=16, k=2, d_ff=128, act='swiglu', score='sigmoid',
+                                         renormalize=1, cf=1.25, dtype='bf16', seed=72), {}),
+    ('ec_gelu_shared', synth.Workload('ec', T=300, d=128, E=8, k=2, d_ff=128, act='gelu', score='softmax',
+                                      renormalize=-1, cf=1.0, dtype='bf16', seed=73, n_shared=1,
+                                      d_ff_shared=128), {}),
+    ('ec_zero_fallback', synth.Workload('ed', T=256, d=64, E=4, k=1, d_ff=64, act='gelu', score='softmax',
+                                        renormalize=-1, cf=1.0, dtype='bf16', seed=74),
+     dict(capacity_override=24, dropped_output='zero')),
+    ('ec_wide_160', synth.Workload('ee', T=320, d=64, E=160, k=4, d_ff=64, act='gelu', score='softmax',
+                                   renormalize=-1, cf=1.0, dtype='bf16', seed=75), {}),
+    ('ec_all_tokens', synth.Workload('ef', T=40, d=64, E=4, k=2, d_ff=64, act='swiglu', score='softmax',
+                                     renormalize=-1, cf=1.0, dtype='bf16', seed=76), dict(capacity_override=64)),
+]
+
+
+def _run_ec(moe, w, seed=0, **over):
+    """GPU forward + backward under expert choice, and the oracle's forward and
+    backward on the same inputs; the picks must come out identical."""
+    inp, ex, sh, dev, dy = _layer(moe, w, seed)
+    cfg = moe.config_from_workload(w, routing='expert', **over)
+    out = moe.alloc_outputs(cfg, DEV, logits=True)
+    ws = moe.workspace(cfg, DEV)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    moe.moe_forward(cfg, weights, dev['x'], out, ws)
+    E, F, d, T = w.E, w.d_ff, w.d, w.T
+    bf = torch.bfloat16
+    grads = dict(dx=torch.empty(T, d, dtype=bf, device=DEV), dw_router=torch.empty(d, E, device=DEV),
+                 dlogit_bias=torch.empty(E, device=DEV), dw_in=torch.empty(E, F, d, dtype=bf, device=DEV),
+                 dw_out=torch.empty(E, d, F, dtype=bf, device=DEV), db_out=None, db_in=None,
+                 dgates=torch.empty(T, E, device=DEV), dlogits=torch.empty(T, E, device=DEV))
+    if w.act == 'swiglu':
+        grads['dw_gate'] = torch.empty(E, F, d, dtype=bf, device=DEV)
+    else:
+        grads['db_in'] = torch.empty(E, F, dtype=bf, device=DEV)
+        grads['db_out'] = torch.empty(E, d, dtype=bf, device=DEV)
+    fs = w.n_shared * w.d_ff_shared
+    if fs:
+        grads.update(dws_in=torch.empty(fs, d, dtype=bf, device=DEV), dws_out=torch.empty(d, fs, dtype=bf, device=DEV),
+                     dbs_in=torch.empty(fs, dtype=bf, device=DEV), dbs_out=torch.empty(d, dtype=bf, device=DEV))
+    bws = moe.backward_workspace(cfg, DEV)
+    moe.moe_backward(cfg, weights, dev['x'], out, ws, synth.to_torch(dy, DEV), grads, bws, ALPHA_AUX, ALPHA_Z)
+    torch.cuda.synchronize()
+    dout = 'zero' if over.get('dropped_output') == 'zero' else 'residual'
+    fwd = O.moe_forward(w, inp, ex, sh, capacity_override=over.get('capacity_override', 0), dropped_output=dout,
+                        routing='expert')
+    np.testing.assert_array_equal(np_of(out['sel']), fwd['sel'], 'picks differ from the oracle: pick another seed')
+    ref = B.moe_backward_expert_choice(w, inp, ex, sh, fwd, synth.as_f32(dy), ALPHA_AUX, ALPHA_Z,
+                                       dropped_output=dout)
+    return out, grads, ref, fwd
+
+
+@pytest.mark.parametrize('case', EC_BWD_CASES, ids=[c[0] for c in EC_BWD_CASES])
+def test_backward_expert_choice_parity(moe, case):
+    """Expert choice: the gate of a pick is the router probability, so dprobs
+    [T,E] (0 where not picked) reaches the logits through the probabilities'
+    Jacobian; unpicked tokens pass dy to dx unless shared experts or the zero
+    output take their place."""
+    name, w, over = case
+    say('backward expert choice', name)
+    out, grads, ref, fwd = _run_ec(moe, w, **over)
+    picked = (fwd['sel'] >= 0)
+    if name in ('ec_gelu_fallback', 'ec_zero_fallback'):
+        assert (~picked.any(axis=1)).any()                 # tokens no expert picked
+    if name == 'ec_all_tokens':
+        assert picked.all()
+    dp = np_of(grads['dgates'])
+    assert (dp[~picked] == 0).all()
+    _check('dprobs', dp, ref['dprobs'])
+    _check('dlogits', np_of(grads['dlogits']), ref['dz'])
+    _check('dx', f64_of(grads['dx']), ref['dx'])
+    _check('dw_router', np_of(grads['dw_router']), ref['dw_router'])
+    _check('dlogit_bias', np_of(grads['dlogit_bias']), ref['dlogit_bias'])
+    ex = ref['experts']
+    if w.act == 'swiglu':
+        _check('dw_gate', f64_of(grads['dw_gate']), np.stack([g['w_gate'] for g in ex]))
+        _check('dw_up', f64_of(grads['dw_in']), np.stack([g['w_up'] for g in ex]))
+    else:
+        _check('dw_in', f64_of(grads['dw_in']), np.stack([g['w_in'] for g in ex]))
+        _check('db_in', f64_of(grads['db_in']), np.stack([g['b_in'] for g in ex]))
+        _check('db_out', f64_of(grads['db_out']), np.stack([g['b_out'] for g in ex]))
+    _check('dw_out', f64_of(grads['dw_out']), np.stack([g['w_out'] for g in ex]))
+    if w.n_shared:
+        sg = ref['shared']
+        _check('dws_in', f64_of(grads['dws_in']), np.concatenate([g['w_in'] for g in sg], 0))
+        _check('dws_out', f64_of(grads['dws_out']), np.concatenate([g['w_out'] for g in sg], 1))
+
+
+def test_backward_expert_choice_saved_preactivations(moe):
+    name, w, over = EC_BWD_CASES[2]
+    inp, ex, sh, dev, dy = _layer(moe, w, 0)
+    out0, g0 = _gpu_pass(moe, w, dev, dy, routing='expert', k_grads=w.E)
+    out1, g1 = _gpu_pass(moe, w, dev, dy, routing='expert', k_grads=w.E, save_preact=True)
+    for kk in out0:
+        if kk not in ('slot', 'dropped'):                 # not written under expert choice
+            assert torch.equal(out0[kk], out1[kk]), kk
     for kk in g0:
         assert torch.equal(g0[kk], g1[kk]), kk
