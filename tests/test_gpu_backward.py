@@ -427,3 +427,98 @@ def test_backward_expert_choice_saved_preactivations(moe):
             assert torch.equal(out0[kk], out1[kk]), kk
     for kk in g0:
         assert torch.equal(g0[kk], g1[kk]), kk
+
+
+@pytest.mark.parametrize('name', ['mixtral_8x_top2', 'deepseekmoe_fine', 'sigmoid_stress'])
+def test_backward_expert_choice_full_size_sampled(moe, name):
+    """Expert choice at full size: the probability, logit and input gradients
+    of 48 sampled tokens, and sampled rows/columns of the expert weight
+    gradients (sums over all of an expert's picks), against the oracle
+    computed for just those.  Tokens whose picks differ from the oracle's
+    (probabilities within rounding of an expert's n-th largest) and experts
+    whose pick sets differ are left out; there must be few."""
+    w = synth.WORKLOADS[name]
+    say('backward expert choice full size', name)
+    inp, ex, sh, dev = device_layer(w, moe)
+    rng = np.random.default_rng(19)
+    dy = synth.bf16_bits(rng.standard_normal((w.T, w.d)).astype(np.float32))
+    cfg = moe.config_from_workload(w, routing='expert')
+    out = moe.alloc_outputs(cfg, DEV, logits=True)
+    ws = moe.workspace(cfg, DEV)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    moe.moe_forward(cfg, weights, dev['x'], out, ws)
+    E, F, d, T = w.E, w.d_ff, w.d, w.T
+    glu = w.act == 'swiglu'
+    bf = torch.bfloat16
+    grads = dict(dx=torch.empty(T, d, dtype=bf, device=DEV), dw_router=torch.empty(d, E, device=DEV),
+                 dw_in=torch.empty(E, F, d, dtype=bf, device=DEV), dw_out=torch.empty(E, d, F, dtype=bf, device=DEV),
+                 dgates=torch.empty(T, E, device=DEV), dlogits=torch.empty(T, E, device=DEV))
+    if glu:
+        grads['dw_gate'] = torch.empty(E, F, d, dtype=bf, device=DEV)
+    fs = w.n_shared * w.d_ff_shared
+    if fs:
+        grads.update(dws_in=torch.empty(fs, d, dtype=bf, device=DEV), dws_out=torch.empty(d, fs, dtype=bf, device=DEV))
+    bws = moe.backward_workspace(cfg, DEV)
+    moe.moe_backward(cfg, weights, dev['x'], out, ws, synth.to_torch(dy, DEV), grads, bws, ALPHA_AUX, ALPHA_Z)
+    torch.cuda.synchronize()
+    rows = np.unique(rng.choice(T, 48, replace=False))
+    get = (lambda e: {kk: v[e] for kk, v in ex.items()})
+    gsh = None if sh is None else (lambda s_: {kk: v[s_] for kk, v in sh.items()})
+    fwd = O.moe_forward(w, inp, get, gsh, rows=rows, routing='expert')
+    gsel = np_of(out['sel'])
+    gp, rp = gsel >= 0, fwd['sel'] >= 0
+    same = (gp == rp).all(axis=1)
+    assert same.mean() > 0.995, int((~same).sum())
+    rows = rows[same[rows]]
+    p = np.asarray(fwd['probs'], np.float64)
+    x = synth.as_f32(inp['x']).astype(np.float64)
+    dyf = synth.as_f32(dy).astype(np.float64)
+    wts = [{kk: synth.as_f32(v).astype(np.float64) for kk, v in get(e).items()} for e in range(E)]
+    swts = [{kk: synth.as_f32(v).astype(np.float64) for kk, v in gsh(s_).items()} for s_ in range(w.n_shared)]
+    dp = np.zeros((rows.size, E))
+    dxe = np.zeros((rows.size, d))
+    for i, t in enumerate(rows):
+        for e in np.nonzero(rp[t])[0]:
+            _, o = O.expert_ffn(x[t][None], wts[e], w.act, 'bf16')
+            dp[i, e] = float((dyf[t] * o[0]).sum())
+            da, _ = B.expert_ffn_backward(x[t][None], wts[e], w.act, 'bf16', p[t, e] * dyf[t][None])
+            dxe[i] += da[0]
+        for sw in swts:
+            da, _ = B.expert_ffn_backward(x[t][None], sw, 'gelu', 'bf16', dyf[t][None])
+            dxe[i] += da[0]
+        if not swts and not rp[t].any():
+            dxe[i] += dyf[t]                                 # residual fallback
+    counts = rp.sum(axis=0).astype(np.float64)
+    v = ALPHA_AUX * E * (counts / counts.sum()) / T
+    z = np.asarray(fwd['logits'], np.float64)[rows]
+    dz = B.probs_backward(z, dp + v[None, :], w.score)
+    m = z.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(z - m).sum(axis=1))
+    dz += ALPHA_Z * 2.0 * lse[:, None] * O.softmax(z) / T
+    dx = dxe + dz @ np.asarray(inp['w_router'], np.float64).T
+    _check('dprobs (sampled tokens)', np_of(grads['dgates'])[rows], dp)
+    _check('dlogits (sampled tokens)', np_of(grads['dlogits'])[rows], dz)
+    _check('dx (sampled tokens)', f64_of(grads['dx'])[rows], dx)
+    g_in, g_out = f64_of(grads['dw_in']), f64_of(grads['dw_out'])
+    g_gate = f64_of(grads['dw_gate']) if glu else None
+    checked = 0
+    for e, f in [(0, 5), (E - 1, F - 1), (E // 2, F // 3)]:
+        if not (gp[:, e] == rp[:, e]).all():
+            continue
+        checked += 1
+        t_e = np.nonzero(rp[:, e])[0]
+        a = x[t_e]
+        d_out = p[t_e, e][:, None] * dyf[t_e]
+        dh = d_out @ wts[e]['w_out'][:, f]
+        if glu:
+            gpre = a @ wts[e]['w_gate'][f]
+            up = a @ wts[e]['w_up'][f]
+            h = O.round_store(O.silu(gpre) * up, 'bf16')
+            _check(f'dw_up[{e}][{f}]', g_in[e][f], (dh * O.silu(gpre)) @ a)
+            _check(f'dw_gate[{e}][{f}]', g_gate[e][f], (dh * up * B.silu_grad(gpre)) @ a)
+        else:
+            u = a @ wts[e]['w_in'][f] + (wts[e]['b_in'][f] if wts[e].get('b_in') is not None else 0.0)
+            h = O.round_store(O.gelu(u), 'bf16')
+            _check(f'dw_in[{e}][{f}]', g_in[e][f], (dh * B.gelu_grad(u)) @ a)
+        _check(f'dw_out[{e}][:, {f}]', g_out[e][:, f], d_out.T @ h)
+    assert checked > 0
