@@ -393,24 +393,55 @@ __global__ __launch_bounds__(kThreads) void router_bwd_kernel(BwdArgs a) {
 // over the first valid_g rows of each group (rows_per_group apart).
 template <int ACT>
 __global__ __launch_bounds__(kThreads) void act_bwd_kernel(ActBwdArgs a) {
+  // eight consecutive columns per thread and step (F is a multiple of 8 and
+  // every row starts 16-byte aligned): 16-byte loads and stores
   const int g = blockIdx.y;
   const int64_t valid = a.valid ? min<int64_t>(a.valid[g], a.rpg) : a.rpg;
-  const int64_t n = valid * a.F;
+  const int F8 = a.F / 8;
+  const int64_t n = valid * F8;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const int64_t r = i / a.F, f = i % a.F;
+    const int64_t r = i / F8;
+    const int c8 = static_cast<int>(i - r * F8) * 8;
     const int64_t row = static_cast<int64_t>(g) * a.rpg + r;
-    const float dh = bf16_to_f32(a.dH[row * a.F + f]);
+    const uint4 dh4 = *reinterpret_cast<const uint4*>(a.dH + row * a.F + c8);
+    const uint4 u4 = *reinterpret_cast<const uint4*>(a.U + row * a.F + c8);
+    const uint32_t dh[4] = {dh4.x, dh4.y, dh4.z, dh4.w}, uu[4] = {u4.x, u4.y, u4.z, u4.w};
+    uint32_t o0[4], o1[4];
     if (ACT == 1) {
-      const float u = bf16_to_f32(a.U[row * a.F + f]);
-      const float grad = 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * __expf(-0.5f * u * u) * 0.39894228040143268f;
-      a.dact[row * a.F + f] = f32_to_bf16(dh * grad);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float d = __uint_as_float(h ? dh[q] & 0xFFFF0000u : dh[q] << 16);
+          const float u = __uint_as_float(h ? uu[q] & 0xFFFF0000u : uu[q] << 16);
+          const float grad = 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * __expf(-0.5f * u * u) * 0.39894228040143268f;
+          w |= static_cast<uint32_t>(f32_to_bf16(d * grad)) << (16 * h);
+        }
+        o0[q] = w;
+      }
+      *reinterpret_cast<uint4*>(a.dact + row * a.F + c8) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
     } else {
-      const float gp = bf16_to_f32(a.U[row * a.F + f]);
-      const float up = bf16_to_f32(a.U2[row * a.F + f]);
-      const float s = 1.0f / (1.0f + __expf(-gp));
-      a.dact[row * 2 * a.F + f] = f32_to_bf16(dh * up * s * (1.0f + gp * (1.0f - s)));
-      a.dact[row * 2 * a.F + a.F + f] = f32_to_bf16(dh * gp * s);
+      const uint4 v4 = *reinterpret_cast<const uint4*>(a.U2 + row * a.F + c8);
+      const uint32_t vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float d = __uint_as_float(h ? dh[q] & 0xFFFF0000u : dh[q] << 16);
+          const float gp = __uint_as_float(h ? uu[q] & 0xFFFF0000u : uu[q] << 16);
+          const float up = __uint_as_float(h ? vv[q] & 0xFFFF0000u : vv[q] << 16);
+          const float s = 1.0f / (1.0f + __expf(-gp));
+          w0 |= static_cast<uint32_t>(f32_to_bf16(d * up * s * (1.0f + gp * (1.0f - s)))) << (16 * h);
+          w1 |= static_cast<uint32_t>(f32_to_bf16(d * gp * s)) << (16 * h);
+        }
+        o0[q] = w0;
+        o1[q] = w1;
+      }
+      *reinterpret_cast<uint4*>(a.dact + row * 2 * a.F + c8) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+      *reinterpret_cast<uint4*>(a.dact + row * 2 * a.F + a.F + c8) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
     }
   }
 }
@@ -634,7 +665,8 @@ hipError_t launch_router_bwd(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_act_bwd(const ActBwdArgs& a, int act, hipStream_t s) {
   if (a.groups == 0 || a.rpg == 0) return hipSuccess;
-  const int64_t per = a.rpg * a.F;
+  if (a.F % 8) return hipErrorInvalidValue;
+  const int64_t per = a.rpg * (a.F / 8);
   const dim3 grid(static_cast<unsigned>(std::min<int64_t>((per + kThreads - 1) / kThreads, 4096)),
                   static_cast<unsigned>(a.groups));
   if (act == MOE_GELU) act_bwd_kernel<1><<<grid, kThreads, 0, s>>>(a);
