@@ -70,17 +70,45 @@ __device__ __forceinline__ float log_sigmoid(float z) {
 }
 
 // Reductions over a group of G consecutive lanes (G a power of two <= 64):
-// every exchange stays inside the group.
+// every exchange stays inside the group, and every lane of the group ends
+// with the same bits.  Groups of 8 and 16 exchange through DPP (a VALU
+// operand modifier, no LDS round trip): the 16-lane row mirror (lane i with
+// 15 - i), the 8-lane half-row mirror (i with 7 - i), then the quad swaps i^2
+// and i^1; each step pairs lanes symmetrically, so the partial sums of the
+// two lanes of a pair are the same float additions.  Larger groups use the
+// xor butterfly through the cross-lane permute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141;
+constexpr int kDppQuadSwap2 = 2 | (3 << 2) | (0 << 4) | (1 << 6);   // quad_perm [2,3,0,1]
+constexpr int kDppQuadSwap1 = 1 | (0 << 2) | (3 << 4) | (2 << 6);   // quad_perm [1,0,3,2]
+
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
+  if constexpr (G == 8 || G == 16) {
+    if constexpr (G == 16) v = fmaxf(v, dpp_f<kDppRowMirror>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+  } else {
 #pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  }
   return v;
 }
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G == 8 || G == 16) {
+    if constexpr (G == 16) v += dpp_f<kDppRowMirror>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppQuadSwap2>(v);
+    v += dpp_f<kDppQuadSwap1>(v);
+  } else {
 #pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  }
   return v;
 }
 
