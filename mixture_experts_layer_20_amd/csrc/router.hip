@@ -398,19 +398,33 @@ __global__ __launch_bounds__(kThreads) void route_from_logits_kernel(RouteArgs a
   __shared__ double red[5 * 256];
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kBT;
   const int nt = static_cast<int>(min<int64_t>(kBT, a.T - t0));
-  // the slabs (at most 8) summed in order, then the logit bias; all of a
-  // value's slab loads are issued before the first add
+  // the slabs (at most 8) summed in order, then the logit bias; the slab
+  // loads of four values are all issued before the first add, so the logit
+  // rows of many experts take a quarter of the load round trips (up to 8
+  // experts, G = 8, every thread has at most one value)
+  constexpr int kU = G == 8 ? 1 : 4;
   const int64_t slab = a.T * a.E;
-  for (int i = threadIdx.x; i < nt * a.E; i += kThreads) {
-    float vs[8];
+  const int n = nt * a.E;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kThreads * kU) {
+    float vs[kU][8];
 #pragma unroll
-    for (int sp = 0; sp < 8; ++sp) vs[sp] = sp < a.zsplits ? a.logits[sp * slab + t0 * a.E + i] : 0.0f;
-    float v = vs[0];
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * kThreads;
 #pragma unroll
-    for (int sp = 1; sp < 8; ++sp)
-      if (sp < a.zsplits) v += vs[sp];
-    if (a.logit_bias) v += a.logit_bias[i % a.E];
-    zbuf[i] = v;
+      for (int sp = 0; sp < 8; ++sp)
+        vs[u][sp] = (sp < a.zsplits && i < n) ? a.logits[sp * slab + t0 * a.E + i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * kThreads;
+      if (i >= n) continue;
+      float v = vs[u][0];
+#pragma unroll
+      for (int sp = 1; sp < 8; ++sp)
+        if (sp < a.zsplits) v += vs[u][sp];
+      if (a.logit_bias) v += a.logit_bias[i % a.E];
+      zbuf[i] = v;
+    }
   }
   __syncthreads();
   workgroup_epilogue<G, EPL>(a, zbuf, a.E, t0, nt, red);
