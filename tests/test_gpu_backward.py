@@ -82,7 +82,7 @@ def _run(moe, w, seed=0, **over):
     dout = 'zero' if over.get('dropped_output') == 'zero' else 'residual'
     ov = over.get('capacity_override', 0)
     fwd = O.moe_forward(w, inp, ex, sh, capacity_override=ov, dropped_output=dout,
-                        dropless=bool(over.get('dropless', False)))
+                        dropless=bool(over.get('dropless', False)), priority=over.get('priority', 'rank'))
     assert (np_of(out['idx']) == fwd['idx']).all(), 'routing differs from the oracle: pick another seed'
     np.testing.assert_array_equal(np_of(out['slot']), fwd['slot'])
     ref = B.moe_backward(w, inp, ex, sh, fwd, synth.as_f32(dy), ALPHA_AUX, ALPHA_Z, dropped_output=dout)
@@ -152,6 +152,17 @@ def test_backward_parity(moe, case):
     if name == 'top1_raw_fallback':
         # fully dropped tokens pass dy through (plus their router term)
         assert (~(~fwd['dropped']).any(axis=1)).any()
+
+
+@pytest.mark.parametrize('priority', ['token', 'score'])
+def test_backward_capacity_priorities(moe, priority):
+    """The backward pass reads the forward's slots and drops whatever queue
+    order decided them: token-major and batch-prioritised (score) capacity."""
+    name, w, over = BWD_CASES[0]
+    say('backward priority', priority)
+    grads, ref, fwd = _run(moe, w, priority=priority)
+    assert fwd['dropped'].any()
+    _compare(w, grads, ref)
 
 
 def test_backward_single_token(moe):
