@@ -533,3 +533,50 @@ def test_backward_expert_choice_full_size_sampled(moe, name):
             _check(f'dw_in[{e}][{f}]', g_in[e][f], (dh * B.gelu_grad(u)) @ a)
         _check(f'dw_out[{e}][:, {f}]', g_out[e][:, f], d_out.T @ h)
     assert checked > 0
+
+
+@pytest.mark.parametrize('over', [dict(), dict(save_preact=True), dict(routing='expert')],
+                         ids=['recompute', 'save_preact', 'expert_choice'])
+def test_training_step_replays_from_a_captured_graph(moe, over):
+    """moe_forward followed by moe_backward enqueues kernels only (zero fills
+    are kernels), so a whole training step of the layer captures into one HIP
+    graph: every replay, with eager scribbling and synchronisations between
+    replays, gives the eager call's outputs and gradients bit for bit."""
+    name, w, _ = BWD_CASES[2]                          # sigmoid scores, shared experts
+    say('graph capture of forward + backward', over)
+    inp, ex, sh, dev, dy = _layer(moe, w, 0)
+    ec = over.get('routing') == 'expert'
+    out0, g0 = _gpu_pass(moe, w, dev, dy, k_grads=w.E if ec else None, **over)
+    cfg = moe.config_from_workload(w, **over)
+    out = moe.alloc_outputs(cfg, DEV, logits=True)
+    ws = moe.workspace(cfg, DEV)
+    grads = {kk: torch.empty_like(v) for kk, v in g0.items()}
+    bws = moe.backward_workspace(cfg, DEV)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    dy_t = synth.to_torch(dy, DEV)
+    s = torch.cuda.Stream()
+
+    def step():
+        moe.moe_forward(cfg, weights, dev['x'], out, ws, stream=s)
+        moe.moe_backward(cfg, weights, dev['x'], out, ws, dy_t, grads, bws, ALPHA_AUX, ALPHA_Z, stream=s)
+
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                         # warm the stream once outside capture
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(3):
+        for t in list(out.values()) + list(grads.values()):   # scribble between replays
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for kk in out0:
+            if ec and kk in ('slot', 'dropped'):
+                continue                               # not written under expert choice
+            assert torch.equal(out[kk], out0[kk]), (rep, kk)
+        for kk in g0:
+            assert torch.equal(grads[kk], g0[kk]), (rep, kk)
