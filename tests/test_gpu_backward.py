@@ -580,3 +580,35 @@ def test_training_step_replays_from_a_captured_graph(moe, over):
             assert torch.equal(out[kk], out0[kk]), (rep, kk)
         for kk in g0:
             assert torch.equal(grads[kk], g0[kk]), (rep, kk)
+
+
+@pytest.mark.parametrize('routing', ['token', 'expert'])
+def test_backward_empty_batch(moe, routing):
+    """T = 0: every weight gradient is zero (written, not left as it was)."""
+    name, w1, _ = BWD_CASES[2]                         # shared experts, GELU biases
+    w = w1.with_(T=0, name='empty')
+    inp, ex, sh, dev, dy = _layer(moe, w1.with_(T=1, name='one'), 0)
+    dev['x'] = dev['x'][:0]
+    cfg = moe.config_from_workload(w, routing=routing)
+    out = moe.alloc_outputs(cfg, DEV, logits=True)
+    ws = moe.workspace(cfg, DEV)
+    weights = {kk: v for kk, v in dev.items() if kk != 'x'}
+    moe.moe_forward(cfg, weights, dev['x'], out, ws)
+    E, F, d = w.E, w.d_ff, w.d
+    fs = w.n_shared * w.d_ff_shared
+    bf = torch.bfloat16
+    grads = dict(dx=torch.empty(0, d, dtype=bf, device=DEV), dw_router=torch.empty(d, E, device=DEV),
+                 dlogit_bias=torch.empty(E, device=DEV), dw_in=torch.empty(E, F, d, dtype=bf, device=DEV),
+                 dw_out=torch.empty(E, d, F, dtype=bf, device=DEV), db_in=torch.empty(E, F, dtype=bf, device=DEV),
+                 db_out=torch.empty(E, d, dtype=bf, device=DEV), dws_in=torch.empty(fs, d, dtype=bf, device=DEV),
+                 dws_out=torch.empty(d, fs, dtype=bf, device=DEV), dbs_in=torch.empty(fs, dtype=bf, device=DEV),
+                 dbs_out=torch.empty(d, dtype=bf, device=DEV))
+    for t in grads.values():
+        t.view(torch.uint8).fill_(0xA5)
+    bws = moe.backward_workspace(cfg, DEV)
+    moe.moe_backward(cfg, weights, dev['x'], out, ws, torch.empty(0, d, dtype=bf, device=DEV), grads, bws,
+                     ALPHA_AUX, ALPHA_Z)
+    torch.cuda.synchronize()
+    for kk, t in grads.items():
+        if t.numel():
+            assert (t.float() == 0).all(), kk
