@@ -25,7 +25,8 @@
 //     16-byte chunks XOR-swizzled by row so fragment reads spread over the
 //     LDS banks.  Token rows may be gathered through a row list (the
 //     dispatch is fused into this load).
-//   * Tile order: logical tiles walk groups of 4 row tiles column by column,
+//   * Tile order: logical tiles walk bands of 4 row tiles (2 for narrow
+//     outputs) column by column,
 //     and 32-tile chunks of them are dealt round-robin to the 8 XCDs (blocks
 //     reach XCDs round-robin), so the ~32 tiles an XCD runs at once share 4
 //     token panels and 8 weight panels in its L2 while every XCD gets an even
@@ -149,8 +150,14 @@ struct TileCoord {
   bool valid;
 };
 
-// logical tile -> (group, row tile, column tile): groups of 4 row tiles,
-// walked column by column
+// Row tiles per band of the tile walk: 4, or 2 when the output has at most
+// four column tiles (narrow GEMMs of fine-grained experts: 32-tile chunks
+// then span fewer of an expert's mostly empty capacity tiles; 5% faster on
+// the 64-expert layer, the same elsewhere).
+__device__ __forceinline__ int band_rows(int ntiles) { return ntiles <= 4 ? 2 : 4; }
+
+// logical tile -> (group, row tile, column tile): bands of band_rows row
+// tiles, walked column by column
 __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntiles, int groups) {
   TileCoord c;
   const int64_t per_group = static_cast<int64_t>(mt_max) * ntiles;
@@ -158,7 +165,7 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntil
   if (!c.valid) { c.g = c.mt = c.nt = 0; return c; }
   c.g = static_cast<int>(L / per_group);
   const int r = static_cast<int>(L % per_group);
-  constexpr int kGM = 4;
+  const int kGM = band_rows(ntiles);
   const int band = r / (kGM * ntiles);
   const int first = band * kGM;
   const int gm = min(kGM, mt_max - first);
@@ -276,7 +283,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     const int first = g ? pk_end[g - 1] : 0;
     const int mt_g = (pk_end[g] - first) / ntiles;
     const int r = static_cast<int>(L) - first;
-    constexpr int kGM = 4;
+    const int kGM = band_rows(ntiles);
     const int band = r / (kGM * ntiles);
     const int mt0 = band * kGM;
     const int gm = min(kGM, mt_g - mt0);
