@@ -374,6 +374,13 @@ def moe_backward(cfg, weights: dict, x, fwd_outputs: dict, fwd_ws, dy, grads: di
                   probs=torch.float32, lse=torch.float32, sel=torch.int32)
     od = {kk: _ptr(fwd_outputs.get(kk), kk, want_o[kk]) for kk in _OKEYS}
     f32 = ('dw_router', 'dlogit_bias', 'dgates', 'dlogits')
+    # the per-token gradients the library writes in full: [T,k] gate
+    # gradients ([T,E] under expert choice) and [T,E] logit gradients
+    ng = cfg.E if cfg.routing == MOE_EXPERT_CHOICE else cfg.k
+    for kk, n in (('dgates', cfg.T * ng), ('dlogits', cfg.T * cfg.E)):
+        t = grads.get(kk)
+        if t is not None and t.numel() != n:
+            raise ValueError(f'{kk} must hold {n} float32 values for this configuration, not {t.numel()}')
     gd = {kk: _ptr(grads.get(kk), kk, torch.float32 if kk in f32 else dt) for kk in _GKEYS}
     w = moe_weights(**wd)
     o = moe_outputs(**od)

@@ -298,3 +298,15 @@ def test_save_preact_configuration(moe):
     assert moe.moe_workspace_bytes(cfg(moe, save_preact=True, **bf)) > moe.moe_workspace_bytes(cfg(moe, **bf))
     assert moe.moe_backward_workspace_bytes(cfg(moe, save_preact=True, **bf)) < \
         moe.moe_backward_workspace_bytes(cfg(moe, **bf))
+
+
+def test_backward_binding_checks_the_per_token_gradient_sizes(moe):
+    """The gate gradients are [T,k] under token choice and [T,E] under expert
+    choice; a buffer of the other size is refused before the library runs."""
+    import torch
+    for routing, bad in (('token', (64, 4)), ('expert', (64, 2))):
+        c = cfg(moe, dtype='bf16', routing=routing)
+        with pytest.raises(ValueError, match='dgates'):
+            moe.moe_backward(c, {}, None, {}, None, None, {'dgates': torch.empty(*bad)}, None)
+    with pytest.raises(ValueError, match='dlogits'):
+        moe.moe_backward(cfg(moe, dtype='bf16'), {}, None, {}, None, None, {'dlogits': torch.empty(64, 2)}, None)
