@@ -39,9 +39,13 @@ int64_t capacity_of(const moe_config& c) {
   // at most once), so C = T never binds
   if (c.dropless) return c.T;
   if (c.capacity_override > 0) return c.capacity_override;
-  // evaluated in IEEE double in this order, then rounded up
-  return static_cast<int64_t>(ceil(c.capacity_factor * static_cast<double>(c.T) *
-                                   static_cast<double>(c.k) / static_cast<double>(c.E)));
+  // evaluated in IEEE double in this order, then rounded up; a value that is
+  // not a finite non-negative number below 2^62 (an infinite or huge
+  // capacity_factor) gives -1, which validation rejects before any use
+  const double v = ceil(c.capacity_factor * static_cast<double>(c.T) * static_cast<double>(c.k) /
+                        static_cast<double>(c.E));
+  if (!(v >= 0.0 && v < 4.611686018427387904e18)) return -1;
+  return static_cast<int64_t>(v);
 }
 
 size_t dsize(const moe_config& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
@@ -100,6 +104,9 @@ moe_status validate(const moe_config* cfg, int64_t* cap) {
   if (c.dropped_output != 0 && c.dropped_output != 1) return fail(MOE_EINVAL, "dropped_output must be 0 or 1");
   const int64_t C = capacity_of(c);
   // capacity buffers hold E*C rows (dropless: T*k, bounded above)
+  if (!c.dropless && C < 0)
+    return fail(MOE_EINVAL, "capacity_factor %g gives no finite capacity for T=%lld, k=%d, E=%d",
+                c.capacity_factor, static_cast<long long>(c.T), c.k, c.E);
   if (!c.dropless && C > (int64_t{1} << 31) / c.E)
     return fail(MOE_EINVAL, "capacity %lld too large", static_cast<long long>(C));
   if (cap) *cap = C;

@@ -61,7 +61,7 @@ constexpr int kBW = 256;     // weight rows per tile
 #define MOE_GEMM_NX 2
 #endif
 #ifndef MOE_GEMM_NW
-#define MOE_GEMM_NW 2
+#define MOE_GEMM_NW 3
 #endif
 #ifndef MOE_GEMM_LOADPOS
 #define MOE_GEMM_LOADPOS 2
@@ -234,13 +234,15 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   }
   TileCoord tc;
   int64_t rows_g, row_base;   // valid rows of the tile's group, and its first row
-  if (a.packed) {
-    // Packed rows: group g's rows start at rows[0] + ... + rows[g-1] (capped
-    // so that no group reaches past total_rows).  Wave 0 lays out the
-    // groups' row starts, rows and dense tile ranges at the start of the
-    // stage buffers (a second LDS object would make the compiler order every
-    // direct-to-LDS load behind the ones before it); L numbers only the
-    // tiles that hold rows.
+  if (a.packed || a.rows) {
+    // Row counts on the device (the experts' kept rows; packed: laid back to
+    // back).  Wave 0 lays out every group's first row, valid rows and dense
+    // range of tiles at the start of the stage buffers (a second LDS object
+    // would make the compiler order every direct-to-LDS load behind the ones
+    // before it); L numbers only the tiles that hold rows, so the blocks of
+    // empty tiles sit at the end of the grid instead of between the chunks
+    // dealt to the XCDs.  Packed: group g's rows start at rows[0] + ... +
+    // rows[g-1] (capped so that no group reaches past total_rows).
     int* pk_start = reinterpret_cast<int*>(lds);
     int* pk_rows = pk_start + kMaxPackedGroups;
     int* pk_end = pk_rows + kMaxPackedGroups;
@@ -257,8 +259,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
           const int64_t u = __shfl_up(vr, o, kWave);
           if (ln >= o) vr += u;
         }
-        const int64_t start = min(carry_r + vr - rg, a.total_rows);
-        const int re = static_cast<int>(max<int64_t>(0, min<int64_t>(rg, a.total_rows - start)));
+        const int64_t start = a.packed ? min(carry_r + vr - rg, a.total_rows) : static_cast<int64_t>(g) * a.rows_per_group;
+        const int re = static_cast<int>(a.packed ? max<int64_t>(0, min<int64_t>(rg, a.total_rows - start))
+                                                 : min<int64_t>(rg, a.rows_per_group));
         int vt = (re + kBM - 1) / kBM * ntiles;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
@@ -266,7 +269,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
           if (ln >= o) vt += u;
         }
         if (g < a.groups) {
-          pk_start[g] = static_cast<int>(start);
+          pk_start[g] = static_cast<int>(a.packed ? start : 0);
           pk_rows[g] = re;
           pk_end[g] = carry_t + vt;
         }
@@ -293,13 +296,13 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     tc.nt = within / gm;
     tc.valid = true;
     rows_g = pk_rows[g];
-    row_base = pk_start[g];
+    row_base = a.packed ? static_cast<int64_t>(pk_start[g]) : static_cast<int64_t>(g) * a.rows_per_group;
     // every wave has read the table before the stage loads overwrite it
     __syncthreads();
   } else {
     tc = decode_tile(L, mt_max, ntiles, a.groups);
     if (!tc.valid) return;
-    rows_g = a.rows ? min<int64_t>(a.rows[tc.g], a.rows_per_group) : a.rows_per_group;
+    rows_g = a.rows_per_group;
     row_base = static_cast<int64_t>(tc.g) * a.rows_per_group;
   }
   const int m0 = tc.mt * kBM;
@@ -797,7 +800,7 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
     const int nout = a.act == 2 ? kBW / 2 : kBW;
-    if (a.packed && a.groups > kMaxPackedGroups) return hipErrorInvalidValue;
+    if ((a.packed || a.rows) && a.groups > kMaxPackedGroups) return hipErrorInvalidValue;
     // packed rows: the groups' row tiles number at most total/256 + groups
     const int64_t row_tiles = a.packed ? (a.total_rows + kBM - 1) / kBM + a.groups
                                        : static_cast<int64_t>(a.groups) * ((a.rows_per_group + kBM - 1) / kBM);

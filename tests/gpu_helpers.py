@@ -2,20 +2,18 @@
 calls through the C ABI, and the comparison rules.
 
 Comparison rules (the bar the tests hold the HIP path to):
-  * integer and index outputs (idx, slot, dropped, counts, row_token, stats):
-    bit-exact, given identical float32 logits;
+  * integer and index outputs (idx, slot, dropped, counts, row_token, sel,
+    stats): bit-exact, given identical float32 logits (or probabilities);
   * float32 outputs: max-relative error ||a - b||_inf / ||b||_inf <= 1e-5;
   * bf16 layer output y: max-relative error <= 2e-2;
   * losses: |a - b| / |b| <= 1e-5;
-  * end to end (logits computed on both sides): the GPU logits must lie within
-    the float32 dot-product error bound of the oracle's; tokens whose ordered
-    top-(k+1) keys have an adjacent gap below max(1e-5, what the observed logit
-    difference can move a key) are "near-tie" tokens and may route
-    differently; probabilities, gates and LSE get the float32 tolerance plus
-    the change the observed logit difference propagates into them.
+  * end to end, the oracle runs twice: on its own logits, which the GPU's must
+    match within the float32 dot-product error bound and which must give the
+    same choices for every token that is not near a tie (an adjacent gap among
+    its top-(k+1) keys below max(1e-5, what the observed logit difference can
+    move a key)); and on the GPU's logits, against which every output is held
+    to the bars above over all tokens.
 """
-import math
-
 import numpy as np
 import torch
 
@@ -107,55 +105,3 @@ def near_tie_tokens(z_ref, z_gpu, k, score, select_bias):
     ulps = 8 * 2.0 ** -24 * np.maximum(np.abs(srt[:, 0]), 1.0)
     thr = np.maximum(1e-5, 2 * lip * dz + ulps)
     return (gaps < thr[:, None]).any(axis=1)
-
-
-def assert_propagated(got, ref, dz, rel=1e-5, what=''):
-    """|got - ref| <= rel * max|ref| + |ref| * (exp(2 dz_t) - 1), row-wise: the
-    float32 tolerance plus what a logit difference of at most dz_t in row t can
-    move a (log-)softmax-derived value (log-softmax is 2-Lipschitz in max norm)."""
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    dzr = np.asarray(dz, np.float64).reshape((-1,) + (1,) * (ref.ndim - 1))
-    allowed = rel * np.abs(ref).max() + np.abs(ref) * np.expm1(2 * dzr)
-    bad = np.abs(got - ref) > allowed
-    assert not bad.any(), (what, np.argwhere(bad)[:5], float((np.abs(got - ref) / np.maximum(allowed, 1e-300)).max()))
-
-
-def check_capacity_valid(idx, slot, dropped, counts, C, E, priority='rank'):
-    """Properties any correct slot assignment has for the given choices."""
-    T, k = idx.shape
-    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
-    order = [(t, j) for j in range(k) for t in range(T)] if priority == 'rank' else \
-        [(t, j) for t in range(T) for j in range(k)]
-    nxt = np.zeros(E, np.int64)
-    for t, j in order:
-        e = idx[t, j]
-        assert slot[t, j] == nxt[e]
-        nxt[e] += 1
-    np.testing.assert_array_equal(dropped, slot >= C)
-
-
-def check_score_capacity_valid(idx, gates, slot, dropped, counts, C, E):
-    """Properties any correct score-priority assignment has for the given
-    choices and float32 gates: per expert, min(count, C) kept, no dropped gate
-    above a kept one (equal gates: the earlier in the rank-major queue is
-    kept), kept numbered 0.. and dropped C.. in queue order."""
-    T, k = idx.shape
-    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
-    queue = [(t, j) for j in range(k) for t in range(T)]
-    per = {e: [] for e in range(E)}
-    for t, j in queue:
-        per[int(idx[t, j])].append((t, j))
-    for e, q in per.items():
-        g = np.array([gates[t, j] for t, j in q], np.float32)
-        kept = np.array([not dropped[t, j] for t, j in q], bool)
-        assert kept.sum() == min(C, len(q))
-        if kept.any() and (~kept).any():
-            assert g[kept].min() >= g[~kept].max()
-            # at equal gates the earlier entry is the kept one
-            gmin = g[kept].min()
-            if (g[~kept] == gmin).any():
-                assert np.nonzero(kept & (g == gmin))[0].max() < np.nonzero(~kept & (g == gmin))[0].min()
-        np.testing.assert_array_equal([slot[t, j] for (t, j), kk in zip(q, kept) if kk], np.arange(kept.sum()))
-        np.testing.assert_array_equal([slot[t, j] for (t, j), kk in zip(q, kept) if not kk],
-                                      C + np.arange((~kept).sum()))

@@ -108,6 +108,12 @@ def test_capacity_values(moe):
 @pytest.mark.parametrize('kw,msg', [
     (dict(capacity_factor=0.99), 'capacity_factor'),
     (dict(capacity_factor=float('nan')), 'capacity_factor'),
+    # a capacity with no finite value, or one past the int64 range, is refused
+    # before any integer conversion (it would otherwise wrap negative)
+    (dict(capacity_factor=float('inf')), 'capacity_factor'),
+    (dict(capacity_factor=1e300), 'capacity_factor'),
+    (dict(capacity_factor=1e300, routing='expert'), 'capacity_factor'),
+    (dict(capacity_factor=1e9), 'too large'),
     (dict(k=5), 'k must be'),
     (dict(k=0), 'k must be'),
     (dict(E=257, k=2), 'E must be'),

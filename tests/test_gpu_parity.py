@@ -12,8 +12,7 @@ import torch
 import synth
 from oracle import moe as O
 
-from gpu_helpers import (DEV, assert_propagated, check_capacity_valid, check_score_capacity_valid, device_layer,
-                         f64_of, forward, logit_error_bound, maxrel, near_tie_tokens, np_of)
+from gpu_helpers import DEV, device_layer, f64_of, forward, logit_error_bound, maxrel, near_tie_tokens, np_of
 
 pytestmark = pytest.mark.gpu
 
@@ -519,6 +518,21 @@ def test_aux_losses_from_given_logits(moe, score):
 
 # ----------------------------------------------------------------------------- end to end
 def _compare_forward(moe, w, rows=None, **over):
+    """The whole layer against the oracle, in two runs of the oracle.
+
+    1. The oracle's own float32 logits: the GPU's must lie within the float32
+       dot-product bound of them, and every token that is not near a tie must
+       choose the same experts (only near-tie tokens may route differently).
+    2. The oracle run on the GPU's logits (the routing steps, capacity, experts,
+       combine and losses from identical float32 logits): choices, slots, drops,
+       counts and statistics bit-exact over all T; gates, probabilities and LSE
+       within 1e-5 max-relative; L_aux and L_z within 1e-5 relative; y on every
+       sampled row within 1e-5 (float32) or 2e-2 (bf16).
+    Under score priority the kept set is decided by comparing float32 gates, so
+    the slots are held bit-exact to the oracle's capacity step run on the GPU's
+    own gates, and rows the oracle keeps differently only because its gates
+    differ from the GPU's in the last bits are left out of the y comparison.
+    """
     inp, ex, sh, dev = device_layer(w, moe)
     say('forward', w.name, over)
     cfg, out = forward(moe, w, dev, **over)
@@ -528,55 +542,64 @@ def _compare_forward(moe, w, rows=None, **over):
     get = (lambda e: {kk: v[e] for kk, v in ex.items()})
     gsh = None if sh is None else (lambda s: {kk: v[s] for kk, v in sh.items()})
     dl = bool(over.get('dropless', False))
-    ref = O.moe_forward(w, inp, get, gsh, rows=rows, priority=pr, capacity_override=cov,
-                        dropped_output=dout, dropless=dl)
     x = synth.as_f32(inp['x'])
-    zr = ref['logits']
     zg = np_of(out['logits'])
+
+    # 1. the GPU's logits against the oracle's, and the choices they make
+    zr = O.router_logits(x, inp['w_router'], inp['logit_bias'])
     bound = logit_error_bound(x, inp['w_router'], inp['logit_bias']) + 2.0 ** -24 * np.abs(zr.astype(np.float64))
     assert (np.abs(zg.astype(np.float64) - zr) <= bound).all()
     near = near_tie_tokens(zr, zg, w.k, w.score, inp['select_bias'])
-    dz = np.abs(zg.astype(np.float64) - zr).max(axis=1)
+    idx_own = O.route(zr, w.k, w.score, w.renormalize, inp['select_bias'])[0]
     gi = np_of(out['idx'])
-    same = (gi == ref['idx']).all(axis=1)
+    same = (gi == idx_own).all(axis=1)
     assert same[~near].all(), np.nonzero(~same & ~near)[0][:10]
-    say(f'  near-tie tokens {int(near.sum())}, routed differently {int((~same).sum())}')
-    gs, gd, gc = np_of(out['slot']), np_of(out['dropped']).astype(bool), np_of(out['counts'])
+    say(f'  near-tie tokens {int(near.sum())}, routed differently from the oracle\'s own logits {int((~same).sum())}')
+
+    # 2. the oracle on the GPU's logits
+    ref = O.moe_forward(w, inp, get, gsh, rows=rows, priority=pr, capacity_override=cov,
+                        dropped_output=dout, dropless=dl, logits=zg)
     C = ref['capacity']
-    if same.all():
+    np.testing.assert_array_equal(gi, ref['idx'])
+    gs, gd, gc = np_of(out['slot']), np_of(out['dropped']).astype(bool), np_of(out['counts'])
+    np.testing.assert_array_equal(gc, ref['counts'])
+    rws = ref['rows']
+    cmp = np.ones(rws.size, bool)
+    if pr == 'score' and not dl:
+        ggpu = np_of(out['gates'])
+        s_g, d_g, _, _ = O.assign_capacity(gi, w.E, C, 'score', scores=ggpu)
+        np.testing.assert_array_equal(gs, s_g)
+        np.testing.assert_array_equal(gd, d_g)
+        flip = gd != ref['dropped']
+        moved = flip.any(axis=1)
+        # a choice the oracle keeps differently must have its gate within the
+        # float32 tolerance of its expert's C-th largest gate (the kept set
+        # hinged on a last-bit difference between the two sides' gates)
+        for t, j in zip(*np.nonzero(flip)):
+            ge = ggpu[gi == gi[t, j]].astype(np.float64)
+            kth = -np.sort(-ge)[C - 1]
+            assert abs(float(ggpu[t, j]) - kth) <= 1e-5 * abs(kth), (t, j, float(ggpu[t, j]), kth)
+        cmp = ~moved[rws]
+        say(f'  score-priority rows kept differently through last-bit gate differences: {int(moved.sum())}')
+    else:
         np.testing.assert_array_equal(gs, ref['slot'])
         np.testing.assert_array_equal(gd, ref['dropped'])
-        np.testing.assert_array_equal(gc, ref['counts'])
-        st = np_of(out['stats'])
-        assert st.tolist() == [ref['stats'][kk] for kk in ('kept', 'dropped', 'fallback', 'pad')]
-        l = np_of(out['losses']).astype(np.float64)
-        # P_i and LSE^2 move with the logits: first-order propagation of dz
-        slack = 2 * float(dz.mean())
-        assert abs(l[0] - ref['l_aux']) <= (1e-5 + slack) * abs(ref['l_aux'])
-        lse_abs = np.abs(ref['lse'])
-        assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z']) + 2 * float((lse_abs * dz).mean()) + float((dz * dz).mean())
-        say(f'  L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}, L_z {l[1]:.6f} vs {ref["l_z"]:.6f}, max dz {dz.max():.2e}')
-    elif dl:
-        # the packed rows the GPU's own choices give
-        r_row, r_counts, _ = O.dropless_rows(gi, w.E, pr)
-        np.testing.assert_array_equal(gs, r_row)
-        np.testing.assert_array_equal(gc, r_counts)
-        assert not gd.any()
-    elif pr == 'score':
-        check_score_capacity_valid(gi, np_of(out['gates']), gs, gd, gc, C, w.E)
-    else:
-        check_capacity_valid(gi, gs, gd, gc, C, w.E, pr)
-    assert_propagated(np_of(out['gates'])[same], ref['gates'][same], dz[same], what='gates')
-    assert_propagated(np_of(out['probs']), ref['probs'], dz, what='probs')
-    lse_g = np_of(out['lse']).astype(np.float64)
-    assert (np.abs(lse_g - ref['lse']) <= 1e-5 * np.abs(ref['lse']).max() + dz).all()
-    rws = ref['rows']
-    # rows whose routing and drops match the oracle's are compared
-    cmp = same[rws] & (gd[rws] == ref['dropped'][rws]).all(1)
+    st = np_of(out['stats']).tolist()
+    want = [ref['stats'][kk] for kk in ('kept', 'dropped', 'fallback', 'pad')]
+    assert st[:2] == want[:2] and st[3] == want[3]
+    if pr != 'score' or dl or not moved.any():
+        assert st[2] == want[2]
+    l = np_of(out['losses']).astype(np.float64)
+    assert abs(l[0] - ref['l_aux']) <= 1e-5 * abs(ref['l_aux'])
+    assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z'])
+    say(f'  L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}, L_z {l[1]:.6f} vs {ref["l_z"]:.6f}')
+    for name in ('gates', 'probs', 'lse'):
+        err = maxrel(np_of(out[name]), ref[name])
+        assert err <= 1e-5, (name, err)
     y = f64_of(out['y'])[rws]
     tol = 1e-5 if w.dtype == 'f32' else 2e-2
     err = maxrel(y[cmp], ref['y'][cmp])
-    say(f'  y max-rel err {err:.3e} over {int(cmp.sum())} rows')
+    say(f'  y max-rel err {err:.3e} over {int(cmp.sum())} of {rws.size} rows')
     assert err <= tol
     fb = ~(~ref['dropped'][rws]).any(1) & cmp
     if w.n_shared == 0 and fb.any():
@@ -750,60 +773,69 @@ def test_combine_expert_choice_parity(moe, E, shared, zero, dtype):
 
 
 def _compare_forward_ec(moe, w, rows=None, **over):
+    """The whole layer under expert choice against the oracle.
+
+    The GPU's logits must lie within the float32 dot-product bound of the
+    oracle's own.  Given the GPU's float32 probabilities, its picks must be
+    exactly the oracle's selection (n per expert, equal probabilities to the
+    lower token, rows numbered in token order).  The oracle run on the GPU's
+    logits gives the references at the stated bar: top-k choices bit-exact;
+    gates, probabilities and LSE within 1e-5 max-relative; L_aux and L_z
+    within 1e-5; statistics exact; y on the sampled rows within 1e-5 / 2e-2.
+    That run forms its probabilities from the same logits with its own exp, so
+    its picks may differ from the GPU's only where an expert's n-th and
+    (n+1)-th probabilities differ in the last bits; such tokens are counted and
+    left out of the y comparison.
+    """
     inp, ex, sh, dev = device_layer(w, moe)
     say('forward expert choice', w.name, over)
     cfg, out = forward(moe, w, dev, routing='expert', **over)
     dout = 'zero' if over.get('dropped_output') == 'zero' else 'residual'
     get = (lambda e: {kk: v[e] for kk, v in ex.items()})
     gsh = None if sh is None else (lambda s: {kk: v[s] for kk, v in sh.items()})
-    ref = O.moe_forward(w, inp, get, gsh, rows=rows, capacity_override=over.get('capacity_override', 0),
-                        dropped_output=dout, routing='expert')
     x = synth.as_f32(inp['x'])
-    zr, zg = ref['logits'], np_of(out['logits'])
+    zg = np_of(out['logits'])
+    zr = O.router_logits(x, inp['w_router'], inp['logit_bias'])
     bound = logit_error_bound(x, inp['w_router'], inp['logit_bias']) + 2.0 ** -24 * np.abs(zr.astype(np.float64))
     assert (np.abs(zg.astype(np.float64) - zr) <= bound).all()
-    dz = np.abs(zg.astype(np.float64) - zr).max(axis=1)
-    gp = np_of(out['probs'])
-    assert_propagated(gp, ref['probs'], dz, what='probs')
+
+    ref = O.moe_forward(w, inp, get, gsh, rows=rows, capacity_override=over.get('capacity_override', 0),
+                        dropped_output=dout, routing='expert', logits=zg)
     T, E, C = w.T, w.E, ref['capacity']
     n = min(C, T)
+    gp = np_of(out['probs'])
     gsel, gc = np_of(out['sel']), np_of(out['counts'])
+    # the picks, bit-exact given identical float32 probabilities
+    rt_g, sel_g = O.expert_choice(gp, C)
+    np.testing.assert_array_equal(gsel, sel_g)
     np.testing.assert_array_equal(gc, [n] * E)
-    # the GPU's picks are a valid top-n of its own probabilities: n per expert,
-    # rows numbered in token order, nothing unpicked above anything picked
-    for e in range(E):
-        pk = gsel[:, e] >= 0
-        assert pk.sum() == n
-        np.testing.assert_array_equal(gsel[pk, e], np.arange(n))
-        if n < T:
-            assert gp[pk, e].min() >= gp[~pk, e].max()
-    # and equal to the oracle's except where a probability lies within the
-    # propagated error of the expert's n-th largest one
+    np.testing.assert_array_equal(np_of(out['idx']), ref['idx'])
+    for name in ('gates', 'probs', 'lse'):
+        err = maxrel(np_of(out[name]), ref[name])
+        assert err <= 1e-5, (name, err)
+    # the oracle's own picks from its own probabilities of the same logits
     rp = ref['probs']
     diff = (gsel >= 0) != (ref['sel'] >= 0)
     if diff.any():
         kth = -np.sort(-rp.astype(np.float32), axis=0)[n - 1].astype(np.float64)
-        band = np.abs(rp - kth[None, :]) <= 1e-6 * np.abs(kth)[None, :] + rp * np.expm1(2 * dz)[:, None] + 1e-9
+        band = np.abs(rp - kth[None, :]) <= 1e-5 * np.abs(kth)[None, :]
         assert band[diff].all(), np.argwhere(diff & ~band)[:5]
     tok_diff = diff.any(1)
-    say(f'  tokens picked differently near an expert boundary: {int(tok_diff.sum())}')
+    say(f'  tokens the oracle picks differently through last-bit probability differences: {int(tok_diff.sum())}')
     st = np_of(out['stats'])
     unpicked = int((~(gsel >= 0).any(1)).sum())
     assert st.tolist() == [E * n, 0, unpicked if w.n_shared == 0 else 0, E * (C - n)]
     if not tok_diff.any():
-        np.testing.assert_array_equal(gsel, ref['sel'])
         assert st[2] == ref['stats']['fallback']
     l = np_of(out['losses']).astype(np.float64)
-    slack = 2 * float(dz.mean())
-    assert abs(l[0] - ref['l_aux']) <= (1e-5 + slack) * abs(ref['l_aux'])
-    lse_abs = np.abs(ref['lse'])
-    assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z']) + 2 * float((lse_abs * dz).mean()) + float((dz * dz).mean())
+    assert abs(l[0] - ref['l_aux']) <= 1e-5 * abs(ref['l_aux'])
+    assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z'])
     rws = ref['rows']
     cmp = ~tok_diff[rws]
     y = f64_of(out['y'])[rws]
     tol = 1e-5 if w.dtype == 'f32' else 2e-2
     err = maxrel(y[cmp], ref['y'][cmp])
-    say(f'  y max-rel err {err:.3e} over {int(cmp.sum())} rows; L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}')
+    say(f'  y max-rel err {err:.3e} over {int(cmp.sum())} of {rws.size} rows; L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}')
     assert err <= tol
     none = ~(ref['sel'][rws] >= 0).any(1) & cmp
     if w.n_shared == 0 and none.any():
