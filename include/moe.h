@@ -194,6 +194,21 @@ MOE_API moe_status moe_dispatch(const moe_config* cfg, const void* x, const int3
                         uint8_t* dropped, int32_t* counts, int32_t* row_token, void* xe,
                         void* ws, void* stream);
 
+/* moe_dispatch without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as moe_dispatch, minus ws.
+ * Its scratch (the capacity histograms, k*ceil(T/64)*E int32, plus E and
+ * ceil(T/64) int32, 256-byte aligned pieces) lives in a fixed 16 MiB device
+ * array inside the library, one per GPU, held until the process ends; a
+ * configuration needing more returns MOE_EINVAL before any launch.  Nothing
+ * in the scratch needs to start at zero.  Calls that overlap on one GPU (two
+ * streams, or two threads) race on that array: serialise them.  The first
+ * call on a device looks the array's address up (MOE_EHIP if that fails);
+ * no call allocates or frees memory. */
+MOE_API moe_status moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int32_t* idx, int32_t* slot,
+                                        uint8_t* dropped, int32_t* counts, int32_t* row_token, void* xe,
+                                        void* stream);
+
 /* Capacity and dispatch under score priority (cfg->priority must be
  * MOE_SCORE_PRIORITY, token choice; see above): as moe_dispatch, plus
  *   gates   [T,k] float32 score of each choice (moe_route's gates)

@@ -72,6 +72,7 @@ def _load():
         'moe_route': (st, [cfgp] + [_P] * 11),
         'moe_dispatch': (st, [cfgp] + [_P] * 9),
         'moe_dispatch_by_score': (st, [cfgp] + [_P] * 10),
+        'moe_dispatch_noalloc': (st, [cfgp] + [_P] * 8),
         'moe_expert_ffn': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
                                 ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
         'moe_expert_ffn_packed': (st, [cfgp, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, _P,
@@ -209,6 +210,16 @@ def moe_dispatch(cfg, x, idx, slot, dropped, counts, row_token, xe, ws, stream=N
                              _ptr(counts, 'counts', torch.int32),
                              _ptr(row_token, 'row_token', torch.int32), _ptr(xe, 'xe', dt),
                              _ptr(ws, 'ws'), _stream(stream)))
+
+
+def moe_dispatch_noalloc(cfg, x, idx, slot, dropped, counts, row_token, xe, stream=None):
+    """moe_dispatch with no workspace: the library's fixed per-GPU scratch."""
+    dt = torch_dtype(cfg)
+    _check(_lib.moe_dispatch_noalloc(ctypes.byref(cfg), _ptr(x, 'x', dt), _ptr(idx, 'idx', torch.int32),
+                                     _ptr(slot, 'slot', torch.int32), _ptr(dropped, 'dropped', torch.uint8),
+                                     _ptr(counts, 'counts', torch.int32),
+                                     _ptr(row_token, 'row_token', torch.int32), _ptr(xe, 'xe', dt),
+                                     _stream(stream)))
 
 
 def moe_dispatch_by_score(cfg, x, idx, gates, slot, dropped, counts, row_token, xe, ws, stream=None):

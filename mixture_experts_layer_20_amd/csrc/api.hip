@@ -10,6 +10,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
@@ -593,6 +594,60 @@ moe_status transpose(const char* what, const bf16_t* in, bf16_t* out, int G, int
   return hip_status(launch_transpose(t, s), what);
 }
 
+// ------------------------------------------------------------------ no-alloc
+// Scratch of the entry point that allocates nothing (moe_dispatch_noalloc):
+// the capacity histograms, kept counts and fallback partials live in this
+// file-scope device array instead of a caller workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never
+// uses the array's name as an address: its device address is looked up once
+// per device (hipGetSymbolAddress with that device current) and kept here.
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  MOE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EUNSUPPORTED, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p) return fail(MOE_EHIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The dispatch scratch: histograms [k, ceil(T/64), E], kept [E] and fallback
+// partials [ceil(T/64)], 256-byte aligned pieces from `base` (NULL: sizes only).
+struct DispatchScratch {
+  int32_t* hist;
+  int32_t* kept;
+  int32_t* fallback_partial;
+  size_t bytes;
+};
+DispatchScratch carve_dispatch(const moe_config& c, void* base) {
+  const int64_t n_tiles = (c.T + kTileTokens - 1) / kTileTokens;
+  DispatchScratch d{};
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t n) -> void* {
+    void* p = b ? b + off : nullptr;
+    off += align_up(n);
+    return p;
+  };
+  d.hist = static_cast<int32_t*>(take(sizeof(int32_t) * c.k * n_tiles * c.E));
+  d.kept = static_cast<int32_t*>(take(sizeof(int32_t) * c.E));
+  d.fallback_partial = static_cast<int32_t*>(take(sizeof(int32_t) * std::max<int64_t>(n_tiles, 1)));
+  d.bytes = off;
+  return d;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -668,6 +723,54 @@ moe_status moe_dispatch(const moe_config* cfg, const void* x, const int32_t* idx
   if (by_score(c)) return fail(MOE_EINVAL, "score priority needs the scores: call moe_dispatch_by_score");
   Workspace w = carve(c, C, ws);
   CapArgs a = cap_args(c, C, w);
+  a.idx = idx;
+  a.slot = slot;
+  a.dropped = dropped;
+  a.counts = counts;
+  a.row_token = row_token;
+  a.x = x;
+  a.xe = xe;
+  return hip_status(launch_capacity(a, c.dtype, static_cast<hipStream_t>(stream)), "capacity");
+}
+
+moe_status moe_dispatch_noalloc(const moe_config* cfg, const void* x, const int32_t* idx, int32_t* slot,
+                                uint8_t* dropped, int32_t* counts, int32_t* row_token, void* xe, void* stream) {
+  int64_t C = 0;
+  MOE_TRY(validate(cfg, &C));
+  const moe_config& c = *cfg;
+  const bool needT = c.T > 0;
+  MOE_TRY(check_ptr(idx, "idx", 4, needT));
+  MOE_TRY(check_ptr(slot, "slot", 4, needT));
+  MOE_TRY(check_ptr(dropped, "dropped", 1, needT));
+  MOE_TRY(check_ptr(counts, "counts", 4));
+  MOE_TRY(check_ptr(row_token, "row_token", 4, false));
+  if ((xe || x) && needT) {
+    MOE_TRY(check_ptr(x, "x", 16));
+    MOE_TRY(check_ptr(xe, "xe", 16, C > 0));
+  }
+  if (by_score(c)) return fail(MOE_EINVAL, "score priority needs the scores: call moe_dispatch_by_score");
+  const size_t need = carve_dispatch(c, nullptr).bytes;
+  if (need > kNoAllocScratchBytes)
+    return fail(MOE_EINVAL,
+                "moe_dispatch_noalloc: this configuration needs %zu bytes of scratch (k*ceil(T/64)*E*4 plus "
+                "E*4 and ceil(T/64)*4, 256-byte aligned), more than its fixed %zu; use moe_dispatch with a workspace",
+                need, kNoAllocScratchBytes);
+  void* base = nullptr;
+  MOE_TRY(scratch_address(&base));
+  const DispatchScratch d = carve_dispatch(c, base);
+  CapArgs a{};
+  a.hist = d.hist;
+  a.kept = d.kept;
+  a.fallback_partial = d.fallback_partial;
+  a.T = c.T;
+  a.C = C;
+  a.E = c.E;
+  a.k = c.k;
+  a.d = c.d;
+  a.n_tiles = static_cast<int>((c.T + kTileTokens - 1) / kTileTokens);
+  a.n_rtiles = static_cast<int>((c.T + kRouteTokens - 1) / kRouteTokens);
+  a.token_major = c.priority == MOE_TOKEN_MAJOR;
+  a.packed = c.dropless;
   a.idx = idx;
   a.slot = slot;
   a.dropped = dropped;

@@ -316,3 +316,18 @@ def test_backward_binding_checks_the_per_token_gradient_sizes(moe):
             moe.moe_backward(c, {}, None, {}, None, None, {'dgates': torch.empty(*bad)}, None)
     with pytest.raises(ValueError, match='dlogits'):
         moe.moe_backward(cfg(moe, dtype='bf16'), {}, None, {}, None, None, {'dlogits': torch.empty(64, 2)}, None)
+
+
+def test_noalloc_dispatch_rejects_oversized_configurations_before_launch(moe):
+    # 200,000 tokens x k 8 x 256 experts need 25 MB of histograms: more than
+    # the fixed 16 MiB scratch; refused on the host (no device is touched)
+    c = cfg(moe, T=200000, E=256, k=8, d=64, dtype='bf16')
+    lib = moe._lib
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.moe_dispatch_noalloc(ctypes.byref(c), None, fake, fake, fake, fake, None, None, None)
+    assert st == moe.MOE_EINVAL
+    msg = lib.moe_last_error()
+    assert b'noalloc' in msg and b'scratch' in msg
+    # invalid configurations are refused as by moe_dispatch
+    bad = cfg(moe, capacity_factor=0.5)
+    assert lib.moe_dispatch_noalloc(ctypes.byref(bad), None, fake, fake, fake, fake, None, None, None) == moe.MOE_EINVAL
