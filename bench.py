@@ -10,18 +10,22 @@ routed and shared expert FFNs, combine, losses) over one batch of T synthetic
 tokens that are already resident in HBM, through moe_forward on torch's
 current stream.  `value` is tokens per second over the K timed steps.
 
-Besides the headline line, the run times each phase of the same layer
-through the public entry points (moe_route, moe_dispatch, moe_expert_ffn,
-moe_combine) with HIP events recorded on the stream the kernels run on, after
-flushing the caches, and reports
+After the headline loop, K more steps run through moe_forward_events, which
+records HIP events on the library's stream at the boundaries of each phase of
+the same forward pass; their per-step durations (`phases_live`, caches warm
+as in the layer) give
   * roofline: the expert grouped GEMM (the dominant kernel: its gate/up and
     down launches) against the bf16 MFMA peak, from algorithmic FLOPs
-    2 * kept_assignments * (3 or 2) * d * d_ff (+ shared experts);
-  * phases: router, dispatch and combine against the HBM peak, from their
-    algorithmic bytes;
+    2 * kept_assignments * (3 or 2) * d * d_ff, averaged over the K steps.
+The run also times each phase through the public entry points (moe_route,
+moe_dispatch, moe_expert_ffn, moe_combine) after flushing L2 and the MALL
+(`phases`, cold caches), giving router, dispatch and combine against the HBM
+peak from their algorithmic bytes, and
   * cpu_baseline: the CPU oracle (tests' reference implementation) timed on a
-    bounded sample of the same workload.
-Prints ONE JSON line.
+    bounded sample of the same workload, with the host's core count and model.
+Prints ONE JSON line.  `--cpu-baseline-all` instead times the oracle on every
+workload (bounded samples) and the pure-Python brute force on the tiny one,
+and prints a table.
 """
 import argparse
 import json
@@ -63,7 +67,49 @@ def parse():
                    help='capture one moe_forward into a HIP graph and time its replays')
     p.add_argument('--copy-calibration', action='store_true',
                    help='finish with a plain copy kernel of known size (for calibrating HBM byte counters)')
+    p.add_argument('--cpu-baseline-all', action='store_true',
+                   help='time the CPU oracle on every workload (bounded samples) and the brute force on the '
+                        'tiny one; no GPU work')
     return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded (the library
+    records them on its stream)."""
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open('/proc/self/maps') as f:
+            for line in f:
+                if 'libamdhip64' in line:
+                    path = line.split()[-1]
+                    break
+        self.ct = ctypes
+        self.lib = ctypes.CDLL(path or 'libamdhip64.so')
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self):
+        h = self.ct.c_void_p()
+        if self.lib.hipEventCreate(self.ct.byref(h)) != 0:
+            raise RuntimeError('hipEventCreate failed')
+        self.made.append(h.value)
+        return h.value
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        if self.lib.hipEventElapsedTime(self.ct.byref(out), a, b) != 0:
+            raise RuntimeError('hipEventElapsedTime failed')
+        return float(out.value)
+
+    def close(self):
+        for h in self.made:
+            self.lib.hipEventDestroy(h)
+        self.made = []
 
 
 COPY_BYTES = 1 << 30           # bytes read and bytes written by the calibration copy
@@ -71,6 +117,9 @@ COPY_BYTES = 1 << 30           # bytes read and bytes written by the calibration
 
 def main():
     args = parse()
+    if args.cpu_baseline_all:
+        cpu_baseline_all()
+        return
     if args.gpus != 1:
         print(json.dumps({'error': 'this build runs on one GPU only: the MoE layer is measured on a '
                                    'single MI355X; --gpus must be 1'}), flush=True)
@@ -158,6 +207,23 @@ def main():
     kept, n_dropped, fallback, pad = stats
     log(f'forward: {ms:.3f} ms/step, {tokens_per_s:,.0f} tokens/s, kept {kept}, dropped {n_dropped}, '
         f'fallback {fallback}')
+
+    # ---------------------------------------------------------------- live phases
+    # K more forward passes, each recording events at its phase boundaries
+    live_names = ('route', 'dispatch', 'expert_ffn', 'shared_ffn', 'combine', 'losses')
+    hev = HipEvents()
+    evs = [[hev.create() for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_live = time.perf_counter()
+    for sev in evs:
+        moe.moe_forward(cfg, weights, x, out, ws, events=sev)
+    torch.cuda.synchronize()
+    live_ms_step = 1e3 * (time.perf_counter() - t_live) / max(1, args.steps)
+    live = {nm: [hev.ms(sev[i], sev[i + 1]) for sev in evs] for i, nm in enumerate(live_names)}
+    live['kernels'] = [hev.ms(sev[0], sev[6]) for sev in evs]
+    hev.close()
+    log(f'live: {live_ms_step:.3f} ms/step; ' + ', '.join(
+        f'{nm} {np.mean(v):.4g} ms' for nm, v in live.items()))
 
     # ---------------------------------------------------------------- phases
     T, k = w.T, w.k
@@ -271,7 +337,10 @@ def main():
     for kk, v in phases.items():
         log(f'phase {kk}: ' + ', '.join(f'{a}={bb:.4g}' if isinstance(bb, float) else f'{a}={bb}'
                                       for a, bb in v.items()))
-    ach = ffn_flops / (med['expert_ffn'] * 1e-3) / 1e12
+    # the dominant kernel's time: the live expert-FFN phase of the timed
+    # forward passes (both grouped GEMM launches), averaged over the K steps
+    ffn_live_ms = float(np.mean(live['expert_ffn']))
+    ach = ffn_flops / (ffn_live_ms * 1e-3) / 1e12
     # HBM bytes per launch pair from the committed FETCH_SIZE / WRITE_SIZE
     # counter runs, if they were taken on this version of the GEMM source
     from mixture_experts_layer_20_amd import rocprof_summary
@@ -281,6 +350,9 @@ def main():
     roofline = {'kernel': 'expert grouped GEMM (gate/up launch + down launch)',
                 'bound': 'mfma', 'achieved': round(ach, 2), 'peak': peak, 'unit': 'TFLOP/s',
                 'frac': round(ach / peak, 4),
+                'ms_per_launch_pair': round(ffn_live_ms, 5),
+                'timing': f'HIP events around the expert FFN inside each of the {args.steps} timed forward '
+                          f'passes (moe_forward_events), mean',
                 'traffic': round(rec['traffic_bytes_per_pair']) if rec else None,
                 'algorithmic': f'2*kept*{mult}*d*d_ff = {ffn_flops:.4e} flop per launch pair, '
                                f'kept={n_kept}'}
@@ -288,6 +360,20 @@ def main():
         roofline['traffic_note'] = (f'HBM bytes per launch pair: fetch {rec["fetch_bytes_per_pair"]:.4g} + write '
                                     f'{rec["write_bytes_per_pair"]:.4g}, counters scaled by a plain copy kernel '
                                     f'(factors {rec["fetch_factor"]:.3f} / {rec["write_factor"]:.3f})')
+
+    live_bytes = {'route': bytes_route, 'dispatch': bytes_dispatch, 'combine': bytes_combine}
+    live_phases = {'ms_per_step': round(live_ms_step, 4),
+                   'kernels_ms_per_step': round(float(np.mean(live['kernels'])), 5)}
+    for nm in live_names:
+        ms_ = float(np.mean(live[nm]))
+        ent = {'ms': round(ms_, 5)}
+        if nm in live_bytes and ms_ > 0:
+            ent['GB/s'] = round(gbs(live_bytes[nm], ms_), 2)
+            ent['hbm_frac'] = round(gbs(live_bytes[nm], ms_) / PEAK_HBM_GBS, 5)
+        if nm == 'expert_ffn':
+            ent['TFLOP/s'] = round(ach, 2)
+            ent['mfma_frac'] = round(ach / peak, 5)
+        live_phases[nm] = ent
 
     if args.backward:
         phases['backward'] = time_backward(moe, cfg, w, weights, x, args, ffn_flops, peak, log)
@@ -318,6 +404,7 @@ def main():
             'roofline': roofline,
             'phases': {kk: {a: (round(bb, 5) if isinstance(bb, float) else bb) for a, bb in v.items()}
                        for kk, v in phases.items()},
+            'phases_live': live_phases,
             'cpu_baseline': cpu}
     print(json.dumps(line), flush=True)
 
@@ -384,11 +471,81 @@ def cpu_baseline(w, sample_tokens, log, dropless=False, routing='token', priorit
     O.moe_forward(ws_, inp, lambda e: experts[e], (lambda s: shared[s]) if shared else None,
                   dropless=dropless, routing=routing, priority=priority)
     el = time.perf_counter() - t
-    log(f'cpu oracle: {n} tokens in {el:.1f}s on {threads} threads')
+    host = host_info()
+    log(f'cpu oracle: {n} tokens in {el:.1f}s on {threads} threads ({host["nproc"]} logical CPUs, '
+        f'{host["cpu_model"]})')
     return {'value': round(n / el, 2), 'unit': 'tokens/s', 'cores': threads, 'kind': 'oracle',
+            'nproc': host['nproc'], 'cpu_model': host['cpu_model'],
             'sample': f'the first {n} tokens of the {w.name} workload as one batch (T={n}, same d, E, k, '
                       f'd_ff and capacity factor; {routing} choice{", dropless" if dropless else ""}); '
-                      f'routing, capacity, all expert FFNs and the combine in float64 numpy; wall {el:.1f}s'}
+                      f'routing, capacity, all expert FFNs and the combine in float64 numpy on {threads} '
+                      f'BLAS threads; wall {el:.1f}s'}
+
+
+def host_info():
+    """Logical CPUs this process may use and the CPU model name."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except Exception:
+        nproc = os.cpu_count() or 1
+    model = 'unknown'
+    try:
+        with open('/proc/cpuinfo') as f:
+            for line in f:
+                if line.startswith('model name'):
+                    model = line.split(':', 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {'nproc': nproc, 'cpu_model': model}
+
+
+# bounded samples for the all-workload oracle table: the first n tokens of each
+# workload as a batch of its own (the 128-expert stress layer on 1,024 tokens)
+CPU_SAMPLES = {'tiny_f32': 64, 'switch_top1_skewed': 4096, 'mixtral_8x_top2': 8192,
+               'deepseekmoe_fine': 16384, 'sigmoid_stress': 1024}
+
+
+def cpu_baseline_all():
+    """The oracle (float64 numpy) on every workload, median of 3 where a run
+    takes under 20 s, and the pure-Python brute force on the tiny layer; one
+    line per workload, then a JSON summary."""
+    import numpy as np
+    import synth
+    from oracle import brute as B
+    host = host_info()
+    print(f'host: {host["nproc"]} logical CPUs, {host["cpu_model"]}', flush=True)
+    rows = {}
+    for name, n in CPU_SAMPLES.items():
+        w = synth.WORKLOADS[name]
+        reps = []
+        for _ in range(3):
+            r = cpu_baseline(w, n, lambda *a: None)
+            reps.append(r)
+            if float(r['sample'].rsplit('wall ', 1)[1].rstrip('s')) > 20:
+                break
+        vals = sorted(r['value'] for r in reps)
+        rows[name] = {'tokens_per_s': vals[len(vals) // 2], 'runs': len(reps), 'sample_tokens': n,
+                      'of_T': w.T, 'threads': reps[0]['cores']}
+        print(f'{name:22s} oracle {vals[len(vals) // 2]:>12,.1f} tokens/s  (first {n} of {w.T} tokens, '
+              f'median of {len(reps)}, {reps[0]["cores"]} BLAS threads)', flush=True)
+    from oracle import moe as O
+    w = synth.WORKLOADS['tiny_f32']
+    inp = synth.router_inputs(w)
+    ex = synth.all_expert_weights(w)
+    tol = (lambda v: synth.as_f32(v).astype(np.float64).tolist())
+    x = tol(inp['x'])
+    wr = inp['w_router'].astype(np.float64).tolist()
+    experts = [{kk: tol(v[e]) for kk, v in ex.items()} for e in range(w.E)]
+    C = O.capacity(w.T, w.k, w.E, w.cf)
+    t = time.perf_counter()
+    B.forward(x, wr, None, None, experts, [], k=w.k, act=w.act, score=w.score, renormalize=w.renormalize,
+              C=C, dtype=w.dtype)
+    el = time.perf_counter() - t
+    rows['tiny_f32_brute_force'] = {'seconds': round(el, 3), 'tokens_per_s': round(w.T / el, 1)}
+    print(f'{"tiny_f32":22s} brute force (pure Python, one thread): {el:.3f} s = {w.T / el:,.1f} tokens/s',
+          flush=True)
+    print(json.dumps({'host': host, 'oracle': rows}), flush=True)
 
 
 if __name__ == '__main__':

@@ -380,7 +380,19 @@ typedef struct moe_outputs {
 MOE_API moe_status moe_forward(const moe_config* cfg, const moe_weights* w, const void* x,
                        moe_outputs* out, void* ws, void* stream);
 
-/* Message for the calling thread's last non-OK status ("" if none). */
+/* moe_forward, recording the caller's HIP events (hipEvent_t handles) on
+ * `stream` at the boundaries of its phases, so that a caller can time each
+ * phase of a real forward pass (a measurement hook; the pass itself is the
+ * same).  n_events must be 7 (MOE_EINVAL otherwise); an entry may be NULL
+ * (not recorded).  events[0] before the router, [1] after it, [2] after
+ * capacity (or the expert-choice selection), [3] after the routed expert FFN
+ * (its two grouped GEMM launches), [4] after the shared experts, [5] after
+ * the combine, [6] after the losses.  The library creates, waits on and
+ * destroys no event. */
+MOE_API moe_status moe_forward_events(const moe_config* cfg, const moe_weights* w, const void* x,
+                                      moe_outputs* out, void* ws, void* stream, void* const* events,
+                                      int32_t n_events);
+
 /* Gradients of the backward pass (storage type unless marked float32). */
 typedef struct moe_grads {
   void* dx;                   /* [T,d]                                     (required) */
@@ -440,6 +452,7 @@ MOE_API moe_status moe_backward(const moe_config* cfg, const moe_weights* w, con
                                 const moe_outputs* fwd, const void* fwd_ws, const void* dy, float alpha_aux,
                                 float alpha_z, moe_grads* grads, void* bws, void* stream);
 
+/* Message for the calling thread's last non-OK status ("" if none). */
 MOE_API const char* moe_last_error(void);
 
 #ifdef __cplusplus

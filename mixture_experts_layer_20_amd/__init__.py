@@ -85,6 +85,8 @@ def _load():
         'moe_aux_losses': (st, [cfgp, _P, _P, _P, _P, _P]),
         'moe_forward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs),
                              _P, _P]),
+        'moe_forward_events': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs),
+                                    _P, _P, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         'moe_backward_workspace_bytes': (ctypes.c_size_t, [cfgp]),
         'moe_backward': (st, [cfgp, ctypes.POINTER(moe_weights), _P, ctypes.POINTER(moe_outputs), _P, _P,
                               ctypes.c_float, ctypes.c_float, ctypes.POINTER(moe_grads), _P, _P]),
@@ -312,8 +314,10 @@ _OKEYS = ('y', 'idx', 'gates', 'slot', 'dropped', 'counts', 'losses', 'stats', '
           'lse', 'sel')
 
 
-def moe_forward(cfg, weights: dict, x, outputs: dict, ws, stream=None):
-    """The whole layer.  ``weights``/``outputs``: dicts keyed like the C structs."""
+def moe_forward(cfg, weights: dict, x, outputs: dict, ws, stream=None, events=None):
+    """The whole layer.  ``weights``/``outputs``: dicts keyed like the C structs.
+    ``events`` (optional): 7 hipEvent_t handles (ints) recorded at the phase
+    boundaries (moe_forward_events)."""
     dt = torch_dtype(cfg)
     wd = {}
     for kk in _WKEYS:
@@ -328,8 +332,13 @@ def moe_forward(cfg, weights: dict, x, outputs: dict, ws, stream=None):
         od[kk] = _ptr(outputs.get(kk), kk, want_o[kk])
     w = moe_weights(**wd)
     o = moe_outputs(**od)
-    _check(_lib.moe_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x, 'x', dt), ctypes.byref(o),
-                            _ptr(ws, 'ws'), _stream(stream)))
+    if events is None:
+        _check(_lib.moe_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x, 'x', dt), ctypes.byref(o),
+                                _ptr(ws, 'ws'), _stream(stream)))
+    else:
+        ev = (ctypes.c_void_p * len(events))(*events)
+        _check(_lib.moe_forward_events(ctypes.byref(cfg), ctypes.byref(w), _ptr(x, 'x', dt), ctypes.byref(o),
+                                       _ptr(ws, 'ws'), _stream(stream), ev, len(events)))
 
 
 def alloc_outputs(cfg, device='cuda', logits=False, probs=False, lse=False) -> dict:

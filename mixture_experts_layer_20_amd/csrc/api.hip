@@ -165,6 +165,7 @@ struct Workspace {
   void* pre1;
   void* pres;
   float* kpart;
+  float* tailpart;
   void* h;
   void* ye;
   void* hs;
@@ -221,6 +222,7 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
     const KSplit ksp = down_ksplit(c.E, C, c.d, c.d_ff);
     if (ksp.parts > 1) w.kpart = static_cast<float*>(take(sizeof(float) * ksp.parts * c.E * C * c.d));
   }
+  if (!c.dropless && c.dtype == MOE_BF16) w.tailpart = static_cast<float*>(take(kTailPartBytes));
   w.h = take(ds * xrows * c.d_ff);
   w.ye = take(ds * xrows * c.d);
   w.hs = fs > 0 ? take(ds * c.T * fs) : nullptr;
@@ -290,7 +292,7 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
                const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate,
                const void* b_in, const void* w_out, const void* b_out, int F, void* h, void* out,
                hipStream_t s, bool packed = false, int64_t group_rows = 0, void* pre0 = nullptr,
-               void* pre1 = nullptr, float* kpart = nullptr) {
+               void* pre1 = nullptr, float* kpart = nullptr, float* tail_part = nullptr) {
   // each operand a GEMM launch addresses through one buffer descriptor (one
   // group's rows) stays below 2^30 elements (2^31 bytes); packed groups hold
   // at most group_rows rows
@@ -341,6 +343,12 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
       g2.kpart_stride = static_cast<int64_t>(groups) * rpg * c.d;
     }
   }
+  // a last, mostly empty round of tiles split along k (the launch decides on
+  // the device, from the row counts)
+  if (tail_part && !packed && rows && g2.ksplit <= 1 && c.dtype == MOE_BF16) {
+    g2.tail_part = tail_part;
+    g2.tail_parts = 8;
+  }
   return hip_status(launch_gemm(g2, c.dtype, s), "expert GEMM 2");
 }
 
@@ -389,8 +397,23 @@ moe_status capacity_step(const moe_config& c, int64_t C, const Workspace& w, con
 // Expert choice after the router: each expert's picks, the routed FFNs on
 // the picked rows (gathered straight from x), the shared experts, the
 // probability-weighted combine and the losses.
+// Phase boundaries of one forward pass, for moe_forward_events: 0 start,
+// 1 routed, 2 capacity (or expert-choice selection) done, 3 routed expert
+// FFN done (both grouped GEMM launches), 4 shared experts done, 5 combined,
+// 6 losses done.
+constexpr int kForwardEvents = 7;
+struct PhaseMarks {
+  void* const* ev;
+  hipStream_t s;
+  moe_status mark(int i) const {
+    if (!ev || !ev[i]) return MOE_OK;
+    return hip_status(hipEventRecord(static_cast<hipEvent_t>(ev[i]), s), "hipEventRecord");
+  }
+};
+
 moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weights& wt, const void* x,
-                                 const float* probs, const moe_outputs& out, const Workspace& w, hipStream_t s) {
+                                 const float* probs, const moe_outputs& out, const Workspace& w, hipStream_t s,
+                                 const PhaseMarks& pm) {
   EcArgs e{};
   e.probs = probs;
   e.keys = w.ec_keys;
@@ -407,12 +430,15 @@ moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weigh
   e.E = c.E;
   e.n_rtiles = router_tiles(c);
   MOE_TRY(hip_status(launch_expert_choice(e, s), "expert choice"));   // T = 0: zero counts and sums
+  MOE_TRY(pm.mark(2));
   if (c.T > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, out.counts, x, w.row_token, c.T, wt.w_in, wt.w_gate, wt.b_in, wt.w_out,
-                wt.b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart));
+                wt.b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart, w.tailpart));
+    MOE_TRY(pm.mark(3));
     if (c.n_shared > 0)
       MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt.ws_in, nullptr, wt.bs_in, wt.ws_out,
                   wt.bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s, false, 0, w.pres));
+    MOE_TRY(pm.mark(4));
     CombineArgs cb{};
     cb.x = x;
     cb.ye = w.ye;
@@ -428,14 +454,19 @@ moe_status forward_expert_choice(const moe_config& c, int64_t C, const moe_weigh
     cb.E = c.E;
     cb.zero_fallback = c.dropped_output;
     MOE_TRY(hip_status(launch_combine(cb, c.dtype, s), "expert-choice combine"));
+  } else {
+    MOE_TRY(pm.mark(3));
+    MOE_TRY(pm.mark(4));
   }
+  MOE_TRY(pm.mark(5));
   LossArgs l = loss_args(c, C, w, out.counts);
   l.fallback_partial = nullptr;
   l.ec = 1;
   l.fallback_count = w.ec_fallback;
   l.losses = out.losses;
   l.stats = out.stats;
-  return hip_status(launch_losses(l, s), "loss finaliser");
+  MOE_TRY(hip_status(launch_losses(l, s), "loss finaliser"));
+  return pm.mark(6);
 }
 
 // ------------------------------------------------------------------ backward
@@ -1036,8 +1067,8 @@ moe_status moe_update_select_bias(const moe_config* cfg, const int32_t* counts, 
                     "selection-bias update");
 }
 
-moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* x, moe_outputs* out, void* ws,
-                       void* stream) {
+static moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, const void* x, moe_outputs* out, void* ws,
+                               void* stream, void* const* events) {
   int64_t C = 0;
   MOE_TRY(validate(cfg, &C));
   const moe_config& c = *cfg;
@@ -1077,6 +1108,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   MOE_TRY(check_ptr(out->lse, "lse", 4, false));
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace w = carve(c, C, ws);
+  const PhaseMarks pm{events, s};
+  MOE_TRY(pm.mark(0));
 
   RouteArgs r = route_args(c, &w);
   r.x = x;
@@ -1095,7 +1128,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
     if (!r.gates) r.gates = w.gates_tmp;
   }
   MOE_TRY(hip_status(launch_route(r, c.dtype, s), "router"));
-  if (ec) return forward_expert_choice(c, C, *wt, x, r.probs, *out, w, s);
+  MOE_TRY(pm.mark(1));
+  if (ec) return forward_expert_choice(c, C, *wt, x, r.probs, *out, w, s, pm);
 
   CapArgs a = cap_args(c, C, w);
   a.idx = out->idx;
@@ -1112,6 +1146,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   a.x = nullptr;
   a.xe = nullptr;
   MOE_TRY(capacity_step(c, C, w, a, out->gates, s));
+  MOE_TRY(pm.mark(2));
 
   if (c.dropless) {
     // packed rows: expert e's rows start after the counts of the lower experts
@@ -1120,11 +1155,13 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
                   wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T, w.pre0, w.pre1));
   } else if (C > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, w.kept, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in, wt->w_out,
-                wt->b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart));
+                wt->b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart, w.tailpart));
   }
+  MOE_TRY(pm.mark(3));
   if (c.n_shared > 0 && c.T > 0)
     MOE_TRY(ffn(c, MOE_GELU, 1, c.T, nullptr, x, nullptr, 0, wt->ws_in, nullptr, wt->bs_in, wt->ws_out,
                 wt->bs_out, c.n_shared * c.d_ff_shared, w.hs, w.s, s, false, 0, w.pres));
+  MOE_TRY(pm.mark(4));
 
   CombineArgs cb{};
   cb.x = x;
@@ -1143,11 +1180,25 @@ moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void*
   cb.zero_fallback = c.dropped_output;
   cb.packed = c.dropless;
   MOE_TRY(hip_status(launch_combine(cb, c.dtype, s), "combine"));
+  MOE_TRY(pm.mark(5));
 
   LossArgs l = loss_args(c, C, w, out->counts);
   l.losses = out->losses;
   l.stats = out->stats;
-  return hip_status(launch_losses(l, s), "loss finaliser");
+  MOE_TRY(hip_status(launch_losses(l, s), "loss finaliser"));
+  return pm.mark(6);
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_weights* wt, const void* x, moe_outputs* out, void* ws,
+                       void* stream) {
+  return forward_impl(cfg, wt, x, out, ws, stream, nullptr);
+}
+
+moe_status moe_forward_events(const moe_config* cfg, const moe_weights* wt, const void* x, moe_outputs* out,
+                              void* ws, void* stream, void* const* events, int32_t n_events) {
+  if (n_events != kForwardEvents || !events)
+    return fail(MOE_EINVAL, "moe_forward_events takes %d event handles (got %d)", kForwardEvents, n_events);
+  return forward_impl(cfg, wt, x, out, ws, stream, events);
 }
 
 size_t moe_backward_workspace_bytes(const moe_config* cfg) {

@@ -173,7 +173,15 @@ struct GemmArgs {
   // (rounded up to 8, at least 8; the operands must be zero from there to the
   // rounded extent), e.g. a weight gradient over an expert's kept rows | null
   const int32_t* kvar;
+  // bf16 path, ACT 0, device row counts (rows), not packed, no ksplit: a
+  // float32 workspace of 256 partial tiles of 256 x 256, in which the tiles
+  // of a last, at most half-full round of the GPU are split along k into at
+  // most tail_parts parts and then summed in part order | null (no split)
+  float* tail_part;
+  int tail_parts;
 };
+// bytes of the tail-split workspace (GemmArgs.tail_part)
+constexpr size_t kTailPartBytes = size_t{256} * 256 * 256 * sizeof(float);
 
 struct CombineArgs {
   const void* x;              // [T,d]

@@ -178,6 +178,91 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntil
 // Groups of a packed-rows launch (the ABI's expert limit).
 constexpr int kMaxPackedGroups = 256;
 
+// Dense tile table for row counts read on the device (a.rows; packed: rows
+// laid back to back).  Wave 0 of the workgroup fills, for every group, its
+// first row (packed), valid rows and the end of its range of tiles in the
+// dense numbering (only tiles that hold rows); the caller synchronises.
+__device__ __forceinline__ void build_tile_table(const GemmArgs& a, int ntiles, int* pk_start, int* pk_rows,
+                                                 int* pk_end) {
+  const int ln = threadIdx.x & 63;
+  if (threadIdx.x >= kWave) return;
+  int64_t carry_r = 0;
+  int carry_t = 0;
+  for (int c = 0; c < a.groups; c += kWave) {
+    const int g = c + ln;
+    const int64_t rg = g < a.groups ? max(a.rows[g], 0) : 0;
+    int64_t vr = rg;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int64_t u = __shfl_up(vr, o, kWave);
+      if (ln >= o) vr += u;
+    }
+    const int64_t start = a.packed ? min(carry_r + vr - rg, a.total_rows) : static_cast<int64_t>(g) * a.rows_per_group;
+    const int re = static_cast<int>(a.packed ? max<int64_t>(0, min<int64_t>(rg, a.total_rows - start))
+                                             : min<int64_t>(rg, a.rows_per_group));
+    int vt = (re + kBM - 1) / kBM * ntiles;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(vt, o, kWave);
+      if (ln >= o) vt += u;
+    }
+    if (g < a.groups) {
+      pk_start[g] = static_cast<int>(a.packed ? start : 0);
+      pk_rows[g] = re;
+      pk_end[g] = carry_t + vt;
+    }
+    carry_r += __shfl(vr, kWave - 1, kWave);
+    carry_t += __shfl(vt, kWave - 1, kWave);
+  }
+}
+
+// Dense tile L (below the table's total) -> (group, row tile, column tile):
+// within a group, bands of band_rows row tiles walked column by column.
+__device__ __forceinline__ TileCoord decode_dense(int L, int groups, int ntiles, const int* pk_end) {
+  const int ln = threadIdx.x & 63;
+  int g = 0;
+  for (int c = 0; c < groups; c += kWave) g += __popcll(__ballot(c + ln < groups && pk_end[c + ln] <= L));
+  const int first = g ? pk_end[g - 1] : 0;
+  const int mt_g = (pk_end[g] - first) / ntiles;
+  const int r = L - first;
+  const int kGM = band_rows(ntiles);
+  const int band = r / (kGM * ntiles);
+  const int mt0 = band * kGM;
+  const int gm = min(kGM, mt_g - mt0);
+  const int within = r % (kGM * ntiles);
+  TileCoord tc;
+  tc.g = g;
+  tc.mt = mt0 + within % gm;
+  tc.nt = within / gm;
+  tc.valid = true;
+  return tc;
+}
+
+// Tail split (bias-only GEMMs with device row counts and a partial-sum
+// workspace): when the dense tiles fill a last round of the GPU's 256
+// compute units at most half, that round's R tiles are split along k into P
+// parts (P*R <= 256, parts of at least 512 k), written as float32 partial
+// tiles and summed in part order by tail_sum_kernel.  F = tiles before the
+// tail (all tiles when nothing is split).
+constexpr int kCUs = 256;
+struct TailPlan {
+  int F, R, P;
+  int kslice;
+};
+__device__ __forceinline__ TailPlan tail_plan(int NT, int K, int max_parts) {
+  TailPlan t{NT, 0, 1, K};
+  const int R = NT % kCUs;
+  if (NT < kCUs || R == 0 || R > kCUs / 2) return t;
+  const int P = min(min(max_parts, kCUs / R), K / 512);
+  if (P < 2) return t;
+  t.kslice = ((K + P - 1) / P + 63) / 64 * 64;
+  t.P = (K + t.kslice - 1) / t.kslice;
+  if (t.P < 2) return TailPlan{NT, 0, 1, K};
+  t.F = NT - R;
+  t.R = R;
+  return t;
+}
+
 // Buffer resource word 3 for raw (unswizzled, untyped) buffers on gfx9.
 constexpr int kRsrcWord3 = 0x00020000;
 // An offset past every operand (operands are kept below 2^31 bytes), which
@@ -234,69 +319,37 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   }
   TileCoord tc;
   int64_t rows_g, row_base;   // valid rows of the tile's group, and its first row
+  // tail split: this block's part of its tile's k range and its partial tile
+  int tail_slot = -1, kpart0 = 0, kpart_len = 0;
   if (a.packed || a.rows) {
     // Row counts on the device (the experts' kept rows; packed: laid back to
-    // back).  Wave 0 lays out every group's first row, valid rows and dense
-    // range of tiles at the start of the stage buffers (a second LDS object
-    // would make the compiler order every direct-to-LDS load behind the ones
-    // before it); L numbers only the tiles that hold rows, so the blocks of
-    // empty tiles sit at the end of the grid instead of between the chunks
-    // dealt to the XCDs.  Packed: group g's rows start at rows[0] + ... +
-    // rows[g-1] (capped so that no group reaches past total_rows).
+    // back).  The table sits at the start of the stage buffers (a second LDS
+    // object would make the compiler order every direct-to-LDS load behind
+    // the ones before it); L numbers only the tiles that hold rows, so the
+    // blocks of empty tiles sit at the end of the grid instead of between the
+    // chunks dealt to the XCDs.
     int* pk_start = reinterpret_cast<int*>(lds);
     int* pk_rows = pk_start + kMaxPackedGroups;
     int* pk_end = pk_rows + kMaxPackedGroups;
-    const int ln = threadIdx.x & 63;
-    if (threadIdx.x < kWave) {
-      int64_t carry_r = 0;
-      int carry_t = 0;
-      for (int c = 0; c < a.groups; c += kWave) {
-        const int g = c + ln;
-        const int64_t rg = g < a.groups ? max(a.rows[g], 0) : 0;
-        int64_t vr = rg;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int64_t u = __shfl_up(vr, o, kWave);
-          if (ln >= o) vr += u;
-        }
-        const int64_t start = a.packed ? min(carry_r + vr - rg, a.total_rows) : static_cast<int64_t>(g) * a.rows_per_group;
-        const int re = static_cast<int>(a.packed ? max<int64_t>(0, min<int64_t>(rg, a.total_rows - start))
-                                                 : min<int64_t>(rg, a.rows_per_group));
-        int vt = (re + kBM - 1) / kBM * ntiles;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const int u = __shfl_up(vt, o, kWave);
-          if (ln >= o) vt += u;
-        }
-        if (g < a.groups) {
-          pk_start[g] = static_cast<int>(a.packed ? start : 0);
-          pk_rows[g] = re;
-          pk_end[g] = carry_t + vt;
-        }
-        carry_r += __shfl(vr, kWave - 1, kWave);
-        carry_t += __shfl(vt, kWave - 1, kWave);
-      }
-    }
+    build_tile_table(a, ntiles, pk_start, pk_rows, pk_end);
     __syncthreads();
-    if (L >= pk_end[a.groups - 1]) return;
-    // the tile's group: the number of groups whose tiles end at or before L
-    int g = 0;
-    for (int c = 0; c < a.groups; c += kWave)
-      g += __popcll(__ballot(c + ln < a.groups && pk_end[c + ln] <= L));
-    const int first = g ? pk_end[g - 1] : 0;
-    const int mt_g = (pk_end[g] - first) / ntiles;
-    const int r = static_cast<int>(L) - first;
-    const int kGM = band_rows(ntiles);
-    const int band = r / (kGM * ntiles);
-    const int mt0 = band * kGM;
-    const int gm = min(kGM, mt_g - mt0);
-    const int within = r % (kGM * ntiles);
-    tc.g = g;
-    tc.mt = mt0 + within % gm;
-    tc.nt = within / gm;
-    tc.valid = true;
-    rows_g = pk_rows[g];
-    row_base = a.packed ? static_cast<int64_t>(pk_start[g]) : static_cast<int64_t>(g) * a.rows_per_group;
+    const int NT = pk_end[a.groups - 1];
+    int Lt = static_cast<int>(L);
+    if (ACT == 0 && a.tail_part) {
+      const TailPlan tp = tail_plan(NT, a.K, a.tail_parts);
+      if (L >= tp.F + static_cast<int64_t>(tp.R) * tp.P) return;
+      if (L >= tp.F) {
+        tail_slot = static_cast<int>(L) - tp.F;
+        Lt = tp.F + tail_slot / tp.P;
+        kpart0 = (tail_slot % tp.P) * tp.kslice;
+        kpart_len = min(tp.kslice, a.K - kpart0);
+      }
+    } else if (L >= NT) {
+      return;
+    }
+    tc = decode_dense(Lt, a.groups, ntiles, pk_end);
+    rows_g = pk_rows[tc.g];
+    row_base = a.packed ? static_cast<int64_t>(pk_start[tc.g]) : static_cast<int64_t>(tc.g) * a.rows_per_group;
     // every wave has read the table before the stage loads overwrite it
     __syncthreads();
   } else {
@@ -315,10 +368,11 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   const bool gathered = a.gather != nullptr;
   const int64_t lda = a.lda ? a.lda : a.K, ldb = a.ldb ? a.ldb : a.K;
   // this tile's k range: [k0, k0 + K) of the operands' rows
-  const int64_t k0 = static_cast<int64_t>(ks) * a.kslice;
+  const int64_t k0 = tail_slot >= 0 ? kpart0 : static_cast<int64_t>(ks) * a.kslice;
   // (or, with kvar, the group's own k extent: its count rounded up to 8, the
   // operands being zero there; at least 8 so that an empty group sums zeros)
-  const int K = ACT == 0 && a.ksplit > 1 ? static_cast<int>(min<int64_t>(a.kslice, a.K - k0))
+  const int K = tail_slot >= 0 ? kpart_len
+                : ACT == 0 && a.ksplit > 1 ? static_cast<int>(min<int64_t>(a.kslice, a.K - k0))
                 : a.kvar ? max(8, min(a.K, (max(a.kvar[tc.g], 0) + 7) / 8 * 8))
                          : a.K;
   const bf16_t* A = static_cast<const bf16_t*>(a.A) + k0 +
@@ -479,6 +533,27 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
             if (n >= N) continue;
             Cf[m * (N / 4) + (n >> 2)] =
                 ((acc[i][j][4 * q] + acc[i][j][4 * q + 1]) + acc[i][j][4 * q + 2]) + acc[i][j][4 * q + 3];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return;
+    }
+    if (ACT == 0 && tail_slot >= 0) {
+      // tail split: this part's float32 sums as a [256 x 256] partial tile
+      float* P = a.tail_part + static_cast<int64_t>(tail_slot) * (kBM * kBW);
+#pragma unroll
+      for (int j = 0; j < kXB; ++j) {
+        const int m = xrow[j];
+        if (m0 + m >= rows_g) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = ncol[i] + 8 * q + 4 * (lane >> 5);
+            if (n0 + n >= N) continue;
+            *reinterpret_cast<float4*>(P + m * kBW + n) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -794,9 +869,58 @@ __global__ __launch_bounds__(kThreads) void ksum_kernel(GemmArgs a) {
     w[q] = static_cast<uint32_t>(f32_to_bf16(v[2 * q])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * q + 1])) << 16);
   *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.C) + row * a.N + c) = make_uint4(w[0], w[1], w[2], w[3]);
 }
+
+// Tail split: tile F + blockIdx.x of the tail = bf16(sum over its parts, in
+// order, of the float32 partial tiles + bias), for its valid rows and
+// columns; the plan is recomputed from the same device row counts.
+__global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
+  __shared__ int tab[3 * kMaxPackedGroups];
+  int* pk_start = tab;
+  int* pk_rows = tab + kMaxPackedGroups;
+  int* pk_end = tab + 2 * kMaxPackedGroups;
+  const int N = a.N;
+  const int ntiles = (N + kBW - 1) / kBW;
+  build_tile_table(a, ntiles, pk_start, pk_rows, pk_end);
+  __syncthreads();
+  const TailPlan tp = tail_plan(pk_end[a.groups - 1], a.K, a.tail_parts);
+  const int t = blockIdx.x;
+  if (t >= tp.R) return;
+  const TileCoord tc = decode_dense(tp.F + t, a.groups, ntiles, pk_end);
+  const int m0 = tc.mt * kBM, n0 = tc.nt * kBW;
+  const int vr = min(kBM, pk_rows[tc.g] - m0), vc = min(kBW, N - n0);
+  const int64_t row_base = static_cast<int64_t>(tc.g) * a.rows_per_group;
+  const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N + n0 : nullptr;
+  bf16_t* C = static_cast<bf16_t*>(a.C) + (row_base + m0) * N + n0;
+  for (int i = threadIdx.x; i < kBM * (kBW / 8); i += kThreads) {
+    const int r = i / (kBW / 8), c = (i % (kBW / 8)) * 8;
+    if (r >= vr || c >= vc) continue;
+    float v[8] = {};
+    for (int p = 0; p < tp.P; ++p) {
+      const float4* q = reinterpret_cast<const float4*>(
+          a.tail_part + (static_cast<int64_t>(t) * tp.P + p) * (kBM * kBW) + r * kBW + c);
+      const float4 x0 = q[0], x1 = q[1];
+      v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+      v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+    }
+    if (bias) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] += bf16_to_f32(bias[c + u]);
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      w[u] = static_cast<uint32_t>(f32_to_bf16(v[2 * u])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * u + 1])) << 16);
+    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(r) * N + c) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
+  GemmArgs a = a_in;
+  // the tail split applies to bias-only bf16 GEMMs over device row counts
+  const bool tail = dtype == MOE_BF16 && a.act == 0 && a.tail_part != nullptr && a.rows != nullptr && !a.packed &&
+                    !(a.ksplit > 1) && a.tail_parts >= 2;
+  if (!tail) a.tail_part = nullptr;
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
     const int nout = a.act == 2 ? kBW / 2 : kBW;
@@ -806,13 +930,15 @@ hipError_t launch_gemm(const GemmArgs& a, int dtype, hipStream_t s) {
                                        : static_cast<int64_t>(a.groups) * ((a.rows_per_group + kBM - 1) / kBM);
     const bool split = a.act == 0 && a.ksplit > 1 && !a.packed;
     const int64_t tiles = row_tiles * ((a.N + nout - 1) / nout) * (split ? a.ksplit : 1);
-    const unsigned grid = static_cast<unsigned>((tiles + 255) / 256 * 256);
+    // (tail split: up to 256 more blocks for the parts of the last round's tiles)
+    const unsigned grid = static_cast<unsigned>((tiles + 255) / 256 * 256 + (tail ? kCUs : 0));
     switch (a.act) {
       case 0: launch_bf16<0>(a, grid, s); break;
       case 1: launch_bf16<1>(a, grid, s); break;
       case 2: launch_bf16<2>(a, grid, s); break;
       default: launch_bf16<3>(a, grid, s); break;
     }
+    if (tail) tail_sum_kernel<<<kCUs / 2, kThreads, 0, s>>>(a);
     if (split) {
       const int64_t items = static_cast<int64_t>(a.groups) * a.rows_per_group * (a.N / 8);
       ksum_kernel<<<static_cast<unsigned>((items + kThreads - 1) / kThreads), kThreads, 0, s>>>(a);

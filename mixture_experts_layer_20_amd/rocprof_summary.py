@@ -6,7 +6,11 @@ library.
     python -m mixture_experts_layer_20_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \
         --workload NAME --copy-bytes N [--command-fetch C] [--command-write C]
 
-``trace`` prints the per-kernel table of a ``--kernel-trace --stats`` run.
+``trace`` prints the per-kernel table of a ``--kernel-trace --stats`` run;
+with ``--skip W --take N`` it adds, for the expert GEMM launches (gate/up,
+down, and the tail sum of a split last round), the median and mean duration
+over their dispatches W .. W+N-1 in launch order (the timed forward passes of
+``bench.py``, after its W warm-up passes and before its phase loop).
 ``traffic`` takes one ``--pmc FETCH_SIZE`` run and one ``--pmc WRITE_SIZE`` run
 of ``bench.py --copy-calibration`` and prints, per kernel, the average counter
 value per dispatch (KiB), the calibration factor that the plain copy kernel of
@@ -72,6 +76,34 @@ def pmc_per_kernel(d, counter):
     return {kn: (len(v), sum(v.values()) / len(v)) for kn, v in per.items()}
 
 
+GEMM_UP_ANY = r'gemm_bf16_w\d<[12]>'    # gate/up launch, GELU or SwiGLU
+STEP_KERNELS = ((GEMM_UP_ANY, 'expert GEMM gate/up'),
+                (GEMM_DOWN, 'expert GEMM down'),
+                (r'tail_sum_kernel', 'tail sum of the down GEMM'))
+
+
+def dispatch_durations(d, pattern):
+    """Durations (microseconds) of the dispatches whose kernel name matches
+    `pattern`, in launch order."""
+    con = sqlite3.connect(find_db(d))
+    rows = con.execute('select name, start, "end" from kernels order by start').fetchall()
+    return [(e - b) / 1000.0 for n, b, e in rows if re.search(pattern, n)]
+
+
+def step_table(d, skip, take, per_step=1):
+    """{label: (dispatches, median_us, mean_us)} over dispatches
+    [skip*per_step, (skip+take)*per_step) of each expert-GEMM kernel."""
+    out = {}
+    for pat, label in STEP_KERNELS:
+        v = dispatch_durations(d, pat)[skip * per_step:(skip + take) * per_step]
+        if v:
+            srt = sorted(v)
+            out[label] = (len(v), srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] +
+                                                                                 srt[len(srt) // 2]),
+                          sum(v) / len(v))
+    return out
+
+
 def cmd_trace(a):
     rows = kernel_table(a.dir)
     print(a.title)
@@ -82,6 +114,21 @@ def cmd_trace(a):
     print(f'{"kernel":72s} {"calls":>6s} {"total_us":>12s} {"avg_us":>10s} {"pct":>6s}')
     for name, calls, total, avg, pct in rows:
         print(f'{short(name):72s} {calls:6d} {total:12.1f} {avg:10.2f} {pct:6.2f}')
+    if a.take:
+        tab = step_table(a.dir, a.skip, a.take)
+        print()
+        print(f'timed forward passes only: dispatches {a.skip} .. {a.skip + a.take - 1} of each kernel '
+              f'(after {a.skip} warm-up passes; the phase loop excluded)')
+        print(f'{"kernel":40s} {"dispatches":>10s} {"median_us":>10s} {"mean_us":>10s}')
+        tot_med = tot_mean = 0.0
+        for label, (n, med, mean) in tab.items():
+            print(f'{label:40s} {n:10d} {med:10.2f} {mean:10.2f}')
+            tot_med += med
+            tot_mean += mean
+        print(f'{"expert FFN per forward pass (sum)":40s} {"":10s} {tot_med:10.2f} {tot_mean:10.2f}')
+        print('json:', json.dumps({'step_kernels_us': {k: {'n': v[0], 'median': v[1], 'mean': v[2]}
+                                                      for k, v in tab.items()},
+                                   'expert_ffn_us_median': tot_med, 'expert_ffn_us_mean': tot_mean}))
 
 
 def cmd_traffic(a):
@@ -143,6 +190,8 @@ def main():
     t.add_argument('dir')
     t.add_argument('--title', default='rocprofv3 kernel trace')
     t.add_argument('--command', default='')
+    t.add_argument('--skip', type=int, default=0, help='warm-up forward passes before the timed ones')
+    t.add_argument('--take', type=int, default=0, help='timed forward passes (0: no per-step section)')
     f = sub.add_parser('traffic')
     f.add_argument('fetch_dir')
     f.add_argument('write_dir')

@@ -641,6 +641,24 @@ def test_forward_sigmoid_stress_sampled(moe):
     _compare_forward(moe, w, rows=rows)
 
 
+def test_forward_splits_the_last_round_of_the_down_projection(moe):
+    # 8 experts each filled to a capacity of 9 row tiles, d = 2048 (8 column
+    # tiles): the down projection has 576 tiles, a last round of 64 on 256
+    # compute units, which the launch splits along k (d_ff = 1024: 2 parts of
+    # 512); compared on tokens routed to the last expert, whose tiles form that
+    # round, and on others
+    w = synth.Workload('tail_round', T=12000, d=2048, E=8, k=2, d_ff=1024, act='gelu', score='softmax',
+                       renormalize=-1, cf=1.25, dtype='bf16', seed=41)
+    inp = synth.router_inputs(w)
+    z = O.router_logits(synth.as_f32(inp['x']), inp['w_router'], inp['logit_bias'])
+    idx = O.route(z, w.k, w.score, w.renormalize, inp['select_bias'])[0]
+    on7 = np.nonzero((idx == 7).any(axis=1))[0]
+    g = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([g.choice(on7, 120, replace=False), g.choice(w.T, 40, replace=False)]))
+    cfg, out, ref = _compare_forward(moe, w, rows=rows, capacity_override=2304)
+    assert (ref['counts'] >= 2304).all()        # every expert holds 9 full row tiles
+
+
 @pytest.mark.parametrize('T', [1, 63, 65, 0])
 def test_forward_ragged_and_empty(moe, T):
     w = synth.WORKLOADS['tiny_f32'].with_(T=T, name=f'tiny_T{T}')
@@ -684,6 +702,46 @@ def test_forward_dropless(moe, case):
     cfg, out, ref = _compare_forward(moe, w, rows=rows, dropless=True, **over)
     assert not ref['dropped'].any()
     assert ref['stats']['dropped'] == 0 and ref['stats']['pad'] == 0
+
+
+def test_forward_events_records_the_phases_of_the_same_pass(moe):
+    # moe_forward_events gives the same outputs bit for bit and records its 7
+    # events in order on the stream (the phases' durations add up to the pass)
+    import ctypes
+    w = synth.WORKLOADS['deepseekmoe_fine'].with_(T=3000, name='events')
+    inp, ex, sh, dev = device_layer(w, moe)
+    _, a = forward(moe, w, dev)
+    path = [ln.split()[-1] for ln in open('/proc/self/maps') if 'libamdhip64' in ln][0]
+    hip = ctypes.CDLL(path)
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(7):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        evs.append(h.value)
+    cfg = moe.config_from_workload(w)
+    b = moe.alloc_outputs(cfg, DEV, logits=True, probs=True, lse=True)
+    moe.moe_forward(cfg, {kk: v for kk, v in dev.items() if kk != 'x'}, dev['x'], b, moe.workspace(cfg, DEV),
+                    events=evs)
+    torch.cuda.synchronize()
+    for kk in a:
+        assert torch.equal(a[kk], b[kk]), kk
+    ms = []
+    for i in range(6):
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), evs[i], evs[i + 1]) == 0
+        ms.append(f.value)
+    tot = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(tot), evs[0], evs[6]) == 0
+    assert all(v >= 0 for v in ms) and ms[2] > 0          # the expert FFN phase takes time
+    assert abs(sum(ms) - tot.value) <= 1e-3 * max(1.0, tot.value) + 1e-3
+    for h in evs:
+        hip.hipEventDestroy(h)
+    with pytest.raises(ValueError, match='7 event'):
+        moe.moe_forward(cfg, {kk: v for kk, v in dev.items() if kk != 'x'}, dev['x'], b,
+                        moe.workspace(cfg, DEV), events=evs[:3])
 
 
 def test_forward_is_deterministic(moe):

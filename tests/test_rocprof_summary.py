@@ -76,3 +76,25 @@ def test_code_hash_ignores_comments_not_code(tmp_path):
     c.write_text('int f(int x) { return x + 2; }\n')
     assert R.gemm_code_sha256(str(a)) == R.gemm_code_sha256(str(b))
     assert R.gemm_code_sha256(str(a)) != R.gemm_code_sha256(str(c))
+
+
+def test_timed_steps_take_the_dispatches_between_warmup_and_phase_loop(tmp_path):
+    d = tmp_path / 't'
+    os.makedirs(d)
+    con = sqlite3.connect(os.path.join(d, 'run_results.db'))
+    con.execute('create table kernels (name text, start int, "end" int)')
+    con.execute('create table top_kernels (name text, total_calls int, total_duration real, average real, percentage real)')
+    up = 'void moe::(anonymous namespace)::gemm_bf16_w8<2>(moe::GemmArgs)'
+    down = 'void moe::(anonymous namespace)::gemm_bf16_w8<0>(moe::GemmArgs)'
+    t = 0
+    # 2 warm-up passes (slow), 3 timed passes, then a phase call (cold, slow)
+    for dur_up, dur_dn in [(9000, 5000), (8000, 4000), (3500, 2000), (3600, 2100), (3400, 1900), (7000, 3000)]:
+        con.execute('insert into kernels values (?,?,?)', (up, t, t + dur_up * 1000))
+        t += dur_up * 1000 + 10
+        con.execute('insert into kernels values (?,?,?)', (down, t, t + dur_dn * 1000))
+        t += dur_dn * 1000 + 10
+    con.commit()
+    con.close()
+    tab = R.step_table(str(d), 2, 3)
+    assert tab['expert GEMM gate/up'] == (3, 3500.0, 3500.0)
+    assert tab['expert GEMM down'] == (3, 2000.0, 2000.0)
