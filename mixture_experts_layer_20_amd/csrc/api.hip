@@ -501,14 +501,23 @@ struct BwdWorkspace {
   bf16_t* HsT;
   bf16_t* dUsT;
   int32_t* pstart;
-  int32_t* prow;
-  int32_t* pxrow;
+  int32_t* kstart;
+  int64_t Kw;                 // columns of the transposed expert operands (packed along k)
   int S;
   size_t bytes;
 };
 
+// Upper bound of the expert rows the backward pass contracts over: kept
+// (capacity), routed (dropless) or picked (expert choice) choices.
+int64_t expert_rows_bound(const moe_config& c, int64_t C) {
+  const int64_t Tk = c.T * c.k;
+  if (c.routing == MOE_EXPERT_CHOICE) return static_cast<int64_t>(c.E) * std::min<int64_t>(C, c.T);
+  if (c.dropless) return Tk;
+  return std::min<int64_t>(Tk, static_cast<int64_t>(c.E) * C);
+}
+
 BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
-  const int64_t T = c.T, d = c.d, E = c.E, F = c.d_ff, Cp = round8(C), Tp = round8(T);
+  const int64_t T = c.T, d = c.d, E = c.E, F = c.d_ff, Tp = round8(T);
   const int64_t ga = c.act == MOE_SWIGLU ? 2 : 1;
   const int64_t Fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
   BwdWorkspace b{};
@@ -534,17 +543,17 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   b.dH = static_cast<bf16_t*>(take(h2 * R * F));
   b.dact = static_cast<bf16_t*>(take(h2 * R * ga * F));
   b.dA = static_cast<bf16_t*>(take(h2 * R * d));
-  if (c.dropless) {
-    b.pstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
-    b.prow = static_cast<int32_t*>(take(sizeof(int32_t) * E * Cp));
-    b.pxrow = static_cast<int32_t*>(take(sizeof(int32_t) * E * Cp));
-  }
+  if (c.dropless) b.pstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+  b.kstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+  // the transposed expert operands of the weight gradients, packed along k:
+  // expert e's max(8, round8(rows_e)) columns start at kstart[e]
+  b.Kw = round8(expert_rows_bound(c, C)) + 8 * E;
   b.woT = static_cast<bf16_t*>(take(h2 * E * F * d));
   b.wiT = static_cast<bf16_t*>(take(h2 * E * d * ga * F));
-  b.dYeT = static_cast<bf16_t*>(take(h2 * E * d * Cp));
-  b.HT = static_cast<bf16_t*>(take(h2 * E * F * Cp));
-  b.dactT = static_cast<bf16_t*>(take(h2 * E * ga * F * Cp));
-  b.AT = static_cast<bf16_t*>(take(h2 * E * d * Cp));
+  b.dYeT = static_cast<bf16_t*>(take(h2 * d * b.Kw));
+  b.HT = static_cast<bf16_t*>(take(h2 * F * b.Kw));
+  b.dactT = static_cast<bf16_t*>(take(h2 * ga * F * b.Kw));
+  b.AT = static_cast<bf16_t*>(take(h2 * d * b.Kw));
   b.xT = static_cast<bf16_t*>(take(h2 * d * Tp));
   b.planes = static_cast<bf16_t*>(take(h2 * 4 * E * Tp));
   b.slabs = static_cast<float*>(take(sizeof(float) * b.S * d * E));
@@ -569,6 +578,7 @@ moe_status check_backward_config(const moe_config& c, int64_t C) {
   const int64_t lim = int64_t{1} << 30;
   const int64_t ga = c.act == MOE_SWIGLU ? 2 : 1;
   const int64_t Fs = static_cast<int64_t>(c.n_shared) * c.d_ff_shared;
+  // (one expert's transposed block: [cols, round8(C)] at most; dropless C = T)
   const int64_t Cp = round8(C), Tp = round8(c.T);
   const int64_t big = std::max({C * c.d, C * ga * c.d_ff, static_cast<int64_t>(c.d) * Cp, ga * c.d_ff * Cp,
                                 static_cast<int64_t>(c.d) * Tp, Fs * Tp, c.T * std::max<int64_t>(Fs, c.d),
@@ -581,7 +591,7 @@ moe_status check_backward_config(const moe_config& c, int64_t C) {
 moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, const int32_t* gather, int64_t a_rows,
                  const void* B, int64_t ldb, int64_t b_gs, const void* bias, void* Cout, const int32_t* rows,
                  int64_t rpg, int groups, int N, int K, hipStream_t s, const int32_t* kvar = nullptr,
-                 bool packed = false) {
+                 bool packed = false, const int32_t* koff = nullptr) {
   GemmArgs g{};
   g.A = A;
   g.lda = lda;
@@ -600,6 +610,7 @@ moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, con
   g.K = K;
   g.act = 0;
   g.kvar = kvar;
+  g.koff = koff;
   g.packed = packed;
   g.total_rows = packed ? rpg : 0;
   return hip_status(launch_gemm(g, MOE_BF16, s), what);
@@ -607,7 +618,8 @@ moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, con
 
 moe_status transpose(const char* what, const bf16_t* in, bf16_t* out, int G, int64_t R, int64_t Cc, int64_t Rpad,
                      int64_t in_gs, int64_t ld_in, int64_t out_gs, int64_t ld_out, const int32_t* valid,
-                     const int32_t* gather, int64_t gather_gs, hipStream_t s) {
+                     const int32_t* gather, int64_t gather_gs, hipStream_t s, const int32_t* ocol = nullptr,
+                     const int32_t* gstart = nullptr) {
   TransposeArgs t{};
   t.in = in;
   t.out = out;
@@ -622,6 +634,8 @@ moe_status transpose(const char* what, const bf16_t* in, bf16_t* out, int G, int
   t.out_gs = out_gs;
   t.ld_out = ld_out;
   t.G = G;
+  t.ocol = ocol;
+  t.gstart = gstart;
   return hip_status(launch_transpose(t, s), what);
 }
 
@@ -1262,7 +1276,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   Workspace w = carve(c, C, const_cast<void*>(fwd_ws));
   BwdWorkspace b = carve_bwd(c, C, bws);
-  const int64_t T = c.T, d = c.d, F = c.d_ff, Cp = round8(C), Tp = round8(T);
+  const int64_t T = c.T, d = c.d, F = c.d_ff, Tp = round8(T);
   const int E = c.E;
   const int ga = glu ? 2 : 1;
 
@@ -1381,33 +1395,37 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     }
     MOE_TRY(rgemm("expert input gradient", b.dact, nullptr, 0, b.wiT, nullptr, b.dA, c.d, static_cast<int>(ga * F)));
     // dW_out = dYe^T H, dW_in = dact^T A: contraction over each expert's rows
-    // (its own extent, kvar), the transposed copies zero-padded to Cp
-    // (dropless: C = T); packed rows reach the transposes through row lists
-    const int32_t* plist = nullptr;
-    const int32_t* xlist = w.row_token;
-    if (dl) {
-      MOE_TRY(hip_status(launch_packed_lists(rows, b.pstart, w.row_token, b.prow, b.pxrow, E, Cp, s), "row lists"));
-      plist = b.prow;
-      xlist = b.pxrow;
-    }
-    const int64_t lgs = dl ? Cp : C;                   // row-list stride per group
-    MOE_TRY(transpose("dYe transpose", b.dYe, b.dYeT, E, C, d, Cp, C * d, d, d * Cp, Cp, rows, plist, lgs, s));
-    MOE_TRY(transpose("H transpose", static_cast<const bf16_t*>(w.h), b.HT, E, C, F, Cp, C * F, F, F * Cp, Cp, rows,
-                      plist, lgs, s));
-    MOE_TRY(bgemm("w_out gradient", b.dYeT, 0, 0, nullptr, 0, b.HT, 0, 0, nullptr, gr->dw_out, nullptr, d, E,
-                  static_cast<int>(F), static_cast<int>(Cp), s, rows));
-    MOE_TRY(transpose("activation-gradient transpose", b.dact, b.dactT, E, C, ga * F, Cp, C * ga * F, ga * F,
-                      ga * F * Cp, Cp, rows, plist, lgs, s));
-    MOE_TRY(transpose("token rows transpose", static_cast<const bf16_t*>(x), b.AT, E, C, d, Cp, 0, d, d * Cp, Cp, rows,
-                      xlist, lgs, s));
+    // (its own extent, kvar).  The transposed copies are per-expert blocks
+    // packed one after another: expert e's block is [cols, n_e], n_e =
+    // max(8, round8(rows_e)) (zero past rows_e), starting kstart[e]*cols
+    // elements in; dropless rows are read from each expert's packed start
+    // (and x through row_token from there)
+    MOE_TRY(hip_status(launch_group_starts(rows, b.kstart, E, 1, s), "packed columns"));
+    if (dl) MOE_TRY(hip_status(launch_group_starts(rows, b.pstart, E, 0, s), "packed rows"));
+    const int32_t* gst = dl ? b.pstart : nullptr;
+    const int64_t Kw = b.Kw;
+    const int64_t rmax = dl ? T : C;                   // rows of one expert at most
+    MOE_TRY(transpose("dYe transpose", b.dYe, b.dYeT, E, rmax, d, round8(rmax), C * d, d, 0, Kw, rows, nullptr, 0, s,
+                      b.kstart, gst));
+    MOE_TRY(transpose("H transpose", static_cast<const bf16_t*>(w.h), b.HT, E, rmax, F, round8(rmax), C * F, F, 0, Kw,
+                      rows, nullptr, 0, s, b.kstart, gst));
+    MOE_TRY(bgemm("w_out gradient", b.dYeT, Kw, 0, nullptr, 0, b.HT, Kw, 0, nullptr, gr->dw_out, nullptr, d, E,
+                  static_cast<int>(F), static_cast<int>(Kw), s, rows, false, b.kstart));
+    // (SwiGLU: the gate and up halves of the activation gradient as two block
+    // sets, the up set F*Kw elements in)
+    for (int h = 0; h < ga; ++h)
+      MOE_TRY(transpose("activation-gradient transpose", b.dact + h * F, b.dactT + h * F * Kw, E, rmax, F,
+                        round8(rmax), C * ga * F, ga * F, 0, Kw, rows, nullptr, 0, s, b.kstart, gst));
+    MOE_TRY(transpose("token rows transpose", static_cast<const bf16_t*>(x), b.AT, E, rmax, d, round8(rmax), 0, d, 0,
+                      Kw, rows, w.row_token, C, s, b.kstart, gst));
     if (glu) {
-      MOE_TRY(bgemm("w_gate gradient", b.dactT, Cp, 2 * F * Cp, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_gate, nullptr,
-                    F, E, c.d, static_cast<int>(Cp), s, rows));
-      MOE_TRY(bgemm("w_up gradient", b.dactT + F * Cp, Cp, 2 * F * Cp, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_in,
-                    nullptr, F, E, c.d, static_cast<int>(Cp), s, rows));
+      MOE_TRY(bgemm("w_gate gradient", b.dactT, Kw, 0, nullptr, 0, b.AT, Kw, 0, nullptr, gr->dw_gate, nullptr, F, E,
+                    c.d, static_cast<int>(Kw), s, rows, false, b.kstart));
+      MOE_TRY(bgemm("w_up gradient", b.dactT + F * Kw, Kw, 0, nullptr, 0, b.AT, Kw, 0, nullptr, gr->dw_in, nullptr,
+                    F, E, c.d, static_cast<int>(Kw), s, rows, false, b.kstart));
     } else {
-      MOE_TRY(bgemm("w_in gradient", b.dactT, 0, 0, nullptr, 0, b.AT, 0, 0, nullptr, gr->dw_in, nullptr, F, E, c.d,
-                    static_cast<int>(Cp), s, rows));
+      MOE_TRY(bgemm("w_in gradient", b.dactT, Kw, 0, nullptr, 0, b.AT, Kw, 0, nullptr, gr->dw_in, nullptr, F, E, c.d,
+                    static_cast<int>(Kw), s, rows, false, b.kstart));
     }
     const int32_t* starts = dl ? b.pstart : nullptr;
     if (gr->db_out)

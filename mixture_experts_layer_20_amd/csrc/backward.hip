@@ -40,6 +40,11 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs a) 
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kTr;
   const int tid = threadIdx.x;
   const int64_t valid = a.valid ? min<int64_t>(a.valid[g], a.R) : a.R;
+  // rows written: Rpad, or with packed output columns the group's own
+  // max(8, round8(valid)) (the zero padding a k-varying GEMM contracts over)
+  const int64_t rpad = a.ocol ? max<int64_t>(8, (valid + 7) / 8 * 8) : a.Rpad;
+  if (r0 >= rpad) return;
+  const int64_t src0 = a.gstart ? a.gstart[g] : 0;
   {
     const int tr = tid / 8, tc = tid % 8;            // 32 rows x 8 chunks per pass
 #pragma unroll
@@ -48,8 +53,10 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs a) 
       const int64_t r = r0 + i, c = c0 + tc * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (r < valid && c < a.Cc) {
-        const int64_t src = a.gather ? static_cast<int64_t>(a.gather[g * a.gather_gs + r]) * a.ld_in
-                                     : g * a.in_gs + r * a.ld_in;
+        const int64_t src =
+            a.gather ? static_cast<int64_t>(a.gather[(a.gstart ? src0 : g * a.gather_gs) + r]) * a.ld_in
+            : a.gstart ? (src0 + r) * a.ld_in
+                       : g * a.in_gs + r * a.ld_in;
         v = *reinterpret_cast<const uint4*>(a.in + src + c);
       }
       uint32_t* t = tile + (i * kTrPitch + tc * 8) / 2;
@@ -66,13 +73,16 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs a) 
   for (int p = 0; p < 2; ++p) {
     const int j = wc + 32 * p;
     const int64_t c = c0 + j, r = r0 + wr * 8;
-    if (c >= a.Cc || r >= a.Rpad) continue;
+    if (c >= a.Cc || r >= rpad) continue;
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       w[q] = static_cast<uint32_t>(tl[(wr * 8 + 2 * q) * kTrPitch + j]) |
              (static_cast<uint32_t>(tl[(wr * 8 + 2 * q + 1) * kTrPitch + j]) << 16);
-    *reinterpret_cast<uint4*>(a.out + g * a.out_gs + c * a.ld_out + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    // packed: group g's block [Cc][rpad] starts ocol[g]*Cc elements in
+    bf16_t* o = a.ocol ? a.out + static_cast<int64_t>(a.ocol[g]) * a.Cc + c * rpad + r
+                       : a.out + g * a.out_gs + c * a.ld_out + r;
+    *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -574,15 +584,16 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(BwdArgs a) {
   }
 }
 
-// Dropless rows: start[g] = counts[0] + ... + counts[g-1] (one workgroup, E
-// <= 256), then the row lists of the weight-gradient transposes:
-// rows[g*kmax + r] = start[g] + r and xrows[g*kmax + r] = row_token[start[g]
-// + r] for r < counts[g].
-__global__ __launch_bounds__(kThreads) void packed_starts_kernel(const int32_t* __restrict__ counts,
-                                                                 int32_t* start, int E) {
+// Group starts (one workgroup, E <= 256): start[g] = n[0] + ... + n[g-1] and
+// start[E] = the total, with n = counts, or with pad8 n = max(8, round8(counts))
+// (the columns of a group in operands packed along k for the weight-gradient
+// GEMMs; an empty group keeps 8 zero columns).
+__global__ __launch_bounds__(kThreads) void group_starts_kernel(const int32_t* __restrict__ counts, int32_t* start,
+                                                                int E, int pad8) {
   __shared__ int v[kThreads];
   const int tid = threadIdx.x;
-  const int c = tid < E ? counts[tid] : 0;
+  int c = tid < E ? max(counts[tid], 0) : 0;
+  if (pad8 && tid < E) c = max(8, (c + 7) / 8 * 8);
   v[tid] = c;
   __syncthreads();
   for (int o = 1; o < kThreads; o <<= 1) {
@@ -593,19 +604,6 @@ __global__ __launch_bounds__(kThreads) void packed_starts_kernel(const int32_t* 
   }
   if (tid < E) start[tid] = v[tid] - c;
   if (tid == E - 1) start[E] = v[tid];
-}
-
-__global__ __launch_bounds__(kThreads) void packed_lists_kernel(const int32_t* __restrict__ counts,
-                                                                const int32_t* __restrict__ start,
-                                                                const int32_t* __restrict__ row_token, int32_t* rows,
-                                                                int32_t* xrows, int64_t kmax) {
-  const int g = blockIdx.y;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (r >= kmax) return;
-  const int n = counts[g];
-  const int64_t p = static_cast<int64_t>(start[g]) + r;
-  rows[g * kmax + r] = r < n ? static_cast<int32_t>(p) : 0;
-  xrows[g * kmax + r] = r < n ? row_token[p] : 0;
 }
 
 __global__ __launch_bounds__(kThreads) void zero_kernel(uint16_t* p, int64_t n) {
@@ -625,12 +623,8 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_packed_lists(const int32_t* counts, int32_t* start, const int32_t* row_token, int32_t* rows,
-                               int32_t* xrows, int E, int64_t kmax, hipStream_t s) {
-  packed_starts_kernel<<<1, kThreads, 0, s>>>(counts, start, E);
-  if (kmax == 0) return hipGetLastError();
-  const dim3 grid(static_cast<unsigned>((kmax + kThreads - 1) / kThreads), static_cast<unsigned>(E));
-  packed_lists_kernel<<<grid, kThreads, 0, s>>>(counts, start, row_token, rows, xrows, kmax);
+hipError_t launch_group_starts(const int32_t* counts, int32_t* start, int E, int pad8, hipStream_t s) {
+  group_starts_kernel<<<1, kThreads, 0, s>>>(counts, start, E, pad8);
   return hipGetLastError();
 }
 

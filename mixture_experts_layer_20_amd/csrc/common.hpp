@@ -179,6 +179,12 @@ struct GemmArgs {
   // most tail_parts parts and then summed in part order | null (no split)
   float* tail_part;
   int tail_parts;
+  // bf16 path, with kvar: the operands are per-group blocks packed one
+  // after another (e.g. transposed expert rows): group g's A is the
+  // [rows_per_group, K_g] block at A + koff[g]*rows_per_group and its B the
+  // [N, K_g] block at B0 + koff[g]*N, both with row stride K_g (its kvar
+  // extent, rounded up to 8, at least 8) | null
+  const int32_t* koff;
 };
 // bytes of the tail-split workspace (GemmArgs.tail_part)
 constexpr size_t kTailPartBytes = size_t{256} * 256 * 256 * sizeof(float);
@@ -258,10 +264,16 @@ struct ScoreArgs {
 // Backward pass (token choice, capacity mode, bf16 storage)
 struct TransposeArgs {
   const bf16_t* in;           // rows of ld_in elements
-  bf16_t* out;                // out[g*out_gs + c*ld_out + r]
-  const int32_t* gather;      // [G*gather_gs] source row of (g, r) | null
+  bf16_t* out;                // out[g*out_gs + c*ld_out + r], or packed: group g's block
+                              // [Cc][n_g] at out + ocol[g]*Cc, n_g = max(8, round8(valid[g]))
+  const int32_t* gather;      // [..] source row of (g, r): gather[g*gather_gs + r] or
+                              // gather[gstart[g] + r] | null
   const int32_t* valid;       // [G] rows read per group (the rest zero) | null: R
-  int64_t R, Cc, Rpad;        // rows and columns in, rows written (>= R)
+  const int32_t* ocol;        // [G] the sum of n_h over the groups h < g (packed blocks;
+                              // group g then writes its n_g rows) | null: Rpad rows
+  const int32_t* gstart;      // [G] first source row (or gather index) of group g | null
+  int64_t R, Cc, Rpad;        // rows and columns in, rows written (>= R), an upper bound
+                              // of the rows written with ocol
   int64_t in_gs, ld_in, gather_gs, out_gs, ld_out;
   int G;
 };
@@ -333,8 +345,7 @@ hipError_t launch_router_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_act_bwd(const ActBwdArgs& a, int act, hipStream_t s);
 hipError_t launch_colsum(const bf16_t* in, void* out, const int32_t* valid, int groups, int64_t rpg, int64_t Cc,
                          int f32out, hipStream_t s, const int32_t* start = nullptr);
-hipError_t launch_packed_lists(const int32_t* counts, int32_t* start, const int32_t* row_token, int32_t* rows,
-                               int32_t* xrows, int E, int64_t kmax, hipStream_t s);
+hipError_t launch_group_starts(const int32_t* counts, int32_t* start, int E, int pad8, hipStream_t s);
 hipError_t launch_router_weight_prep(const float* dz, bf16_t* planes, int64_t T, int64_t Tp, int E,
                                      const float* w_router, float* wrT, int d, hipStream_t s);
 hipError_t launch_dz_colsum(const float* dz, float* out, int64_t T, int E, hipStream_t s);

@@ -366,7 +366,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // is the whole [a_rows, K] input and row m of group g is A[gather[row_base
   // + m]], row_base = g*rpg, or the packed start)
   const bool gathered = a.gather != nullptr;
-  const int64_t lda = a.lda ? a.lda : a.K, ldb = a.ldb ? a.ldb : a.K;
+
   // this tile's k range: [k0, k0 + K) of the operands' rows
   const int64_t k0 = tail_slot >= 0 ? kpart0 : static_cast<int64_t>(ks) * a.kslice;
   // (or, with kvar, the group's own k extent: its count rounded up to 8, the
@@ -375,11 +375,15 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
                 : ACT == 0 && a.ksplit > 1 ? static_cast<int>(min<int64_t>(a.kslice, a.K - k0))
                 : a.kvar ? max(8, min(a.K, (max(a.kvar[tc.g], 0) + 7) / 8 * 8))
                          : a.K;
+  // row strides (per-group packed blocks: the group's own k extent)
+  const int64_t lda = a.koff ? K : a.lda ? a.lda : a.K, ldb = a.koff ? K : a.ldb ? a.ldb : a.K;
   const bf16_t* A = static_cast<const bf16_t*>(a.A) + k0 +
-                    (gathered ? 0
+                    (a.koff ? static_cast<int64_t>(a.koff[tc.g]) * a.rows_per_group
+                     : gathered ? 0
                      : a.packed ? row_base * lda
                                 : static_cast<int64_t>(tc.g) * (a.a_gs ? a.a_gs : a.rows_per_group * lda));
-  const int64_t bg = static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb) + k0;
+  const int64_t bg = (a.koff ? static_cast<int64_t>(a.koff[tc.g]) * N
+                             : static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb)) + k0;
   const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + bg;
   const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + bg : B0;
 
