@@ -112,6 +112,32 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Largest 64-bit value over a group of G lanes (same lane pairing as
+// group_max: DPP for 8 and 16 lanes, the xor butterfly beyond); every lane of
+// the group ends with it.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF, false));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <int G>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  if constexpr (G == 8 || G == 16) {
+    if constexpr (G == 16) v = mx(v, dpp_u64<kDppRowMirror>(v));
+    v = mx(v, dpp_u64<kDppHalfMirror>(v));
+    v = mx(v, dpp_u64<kDppQuadSwap2>(v));
+    v = mx(v, dpp_u64<kDppQuadSwap1>(v));
+  } else {
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) v = mx(v, __shfl_xor(v, o, kWave));
+  }
+  return v;
+}
+
 // Per-token epilogue, run by a group of G lanes (lane l of the group holds
 // experts l, l + G, ...; EPL = ceil(E / G) of them): statistics, selection,
 // gates.  z: LDS row of this token's logits (logit bias included).
@@ -124,7 +150,6 @@ __device__ __forceinline__ void token_epilogue(const RouteArgs& a, const float* 
                                double* pacc, double& lse2acc) {
   const int lane = threadIdx.x & (kWave - 1);
   const int li = lane & (G - 1);                  // lane within the group
-  const int gbase = lane & ~(G - 1);              // first lane of the group
   const int E = a.E, k = a.k;
   float zv[EPL];
   float m = -__builtin_huge_valf();
@@ -136,69 +161,84 @@ __device__ __forceinline__ void token_epilogue(const RouteArgs& a, const float* 
   }
   m = group_max<G>(m);
   float s = 0.0f;
+  float ex[EPL];
 #pragma unroll
-  for (int r = 0; r < EPL; ++r) s += (li + r * G < E) ? expf(zv[r] - m) : 0.0f;
+  for (int r = 0; r < EPL; ++r) {
+    ex[r] = (li + r * G < E) ? expf(zv[r] - m) : 0.0f;
+    s += ex[r];
+  }
   s = group_sum<G>(s);
   const float lse = m + logf(s);
 
-  // full-E probabilities (softmax) or normalised sigmoid scores (log domain)
-  float pv[EPL];
+  // selection keys (experts past E hold no key) and the full-E probabilities:
+  // softmax, or the sigmoid scores normalised over all E.  The sigmoid key
+  // before its bias is the float32 sigmoid, so the scores are divided by their
+  // sum directly; only a token whose every score underflows (a row of logits
+  // below about -87) takes the log domain (a softmax of log sigmoid).
+  float key[EPL], pv[EPL];
   if (a.score == MOE_SIGMOID) {
-    float lm = -__builtin_huge_valf();
-    float ls[EPL];
-#pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-      ls[r] = (li + r * G < E) ? log_sigmoid(zv[r]) : -__builtin_huge_valf();
-      lm = fmaxf(lm, ls[r]);
-    }
-    lm = group_max<G>(lm);
     float qs = 0.0f;
 #pragma unroll
     for (int r = 0; r < EPL; ++r) {
-      pv[r] = (li + r * G < E) ? expf(ls[r] - lm) : 0.0f;
-      qs += pv[r];
+      key[r] = (li + r * G < E) ? sigmoid_key(zv[r]) : 0.0f;
+      qs += key[r];
     }
     qs = group_sum<G>(qs);
-    const float inv = 1.0f / qs;
+    if (qs > 1e-30f) {
+      const float inv = 1.0f / qs;
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) pv[r] *= inv;
+      for (int r = 0; r < EPL; ++r) pv[r] = key[r] * inv;
+    } else {
+      float lm = -__builtin_huge_valf();
+      float ls[EPL];
+#pragma unroll
+      for (int r = 0; r < EPL; ++r) {
+        ls[r] = (li + r * G < E) ? log_sigmoid(zv[r]) : -__builtin_huge_valf();
+        lm = fmaxf(lm, ls[r]);
+      }
+      lm = group_max<G>(lm);
+      float q2 = 0.0f;
+#pragma unroll
+      for (int r = 0; r < EPL; ++r) {
+        pv[r] = (li + r * G < E) ? expf(ls[r] - lm) : 0.0f;
+        q2 += pv[r];
+      }
+      q2 = group_sum<G>(q2);
+      const float inv = 1.0f / q2;
+#pragma unroll
+      for (int r = 0; r < EPL; ++r) pv[r] *= inv;
+    }
   } else {
     const float inv = 1.0f / s;
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) pv[r] = (li + r * G < E) ? expf(zv[r] - m) * inv : 0.0f;
+    for (int r = 0; r < EPL; ++r) {
+      pv[r] = ex[r] * inv;
+      key[r] = zv[r];
+    }
   }
 
-  // selection keys; experts past E and experts already chosen hold -inf
-  float key[EPL];
+  // top-k on packed codes: order code of the key (plus any selection bias)
+  // above the complement of the expert index, so the largest code is the
+  // largest key and, among equal keys (-0 == +0), the lowest index; code 0
+  // marks no candidate.  Each round takes the group's largest code.
+  uint64_t code[EPL];
 #pragma unroll
   for (int r = 0; r < EPL; ++r) {
     const int e = li + r * G;
-    if (e < E) {
-      float kv = a.score == MOE_SIGMOID ? sigmoid_key(zv[r]) : zv[r];
-      if (sbias) kv = kv + sbias[r];
-      key[r] = kv;
-    } else {
-      key[r] = -__builtin_huge_valf();
-    }
+    float kv = key[r];
+    if (sbias) kv = kv + sbias[r];
+    code[r] = e < E ? select_code(kv, e) : 0ull;
   }
-  const uint64_t gmask = (G == 64 ? ~0ull : ((1ull << G) - 1)) << gbase;
   int my_sel = -1;  // lane j < k of the group keeps the j-th choice
   for (int j = 0; j < k; ++j) {
-    float best = -__builtin_huge_valf();
+    uint64_t best = 0;
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) best = fmaxf(best, key[r]);
-    best = group_max<G>(best);
-    // lowest expert index holding the best key: slice r = 0 first, then 1, ...
-    int e = -1;
-#pragma unroll
-    for (int r = 0; r < EPL; ++r) {
-      const uint64_t hit = __ballot(key[r] == best) & gmask;
-      if (e < 0 && hit) e = (__ffsll(static_cast<unsigned long long>(hit)) - 1 - gbase) + r * G;
-    }
+    for (int r = 0; r < EPL; ++r) best = code[r] > best ? code[r] : best;
+    best = group_max_u64<G>(best);
 #pragma unroll
     for (int r = 0; r < EPL; ++r)
-      if (li + r * G == e) key[r] = -__builtin_huge_valf();
-    if (li == j) my_sel = e;
+      if (code[r] == best) code[r] = 0;
+    if (li == j) my_sel = code_expert(best);
   }
 
   // gates, computed by lanes 0..k-1 of the group
