@@ -284,24 +284,14 @@ LossArgs loss_args(const moe_config& c, int64_t C, const Workspace& w, const int
   return l;
 }
 
-// Expert FFN on `groups` groups of rows: h = act(a w_in^T (+ b_in)) (or the
-// SwiGLU pair), out = h w_out^T (+ b_out).  With `gather`, row m of group g
-// is row gather[base_g + m] of a ([a_rows, d]), base_g = g*rpg, or with
-// `packed` rows[0] + ... + rows[g-1] (then rpg is the bound on their sum).
-moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int32_t* rows, const void* a,
-               const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate,
-               const void* b_in, const void* w_out, const void* b_out, int F, void* h, void* out,
-               hipStream_t s, bool packed = false, int64_t group_rows = 0, void* pre0 = nullptr,
-               void* pre1 = nullptr, float* kpart = nullptr, float* tail_part = nullptr) {
-  // each operand a GEMM launch addresses through one buffer descriptor (one
-  // group's rows) stays below 2^30 elements (2^31 bytes); packed groups hold
-  // at most group_rows rows
-  const int64_t lim = int64_t{1} << 30;
-  const int64_t gr = packed && group_rows > 0 ? std::min(group_rows, rpg) : rpg;
-  if (gr * c.d >= lim || gr * F >= lim || static_cast<int64_t>(F) * c.d >= lim ||
-      (gather && a_rows * c.d >= lim))
-    return fail(MOE_EINVAL, "one expert's operands must hold < 2^30 elements");
-  if (packed && groups > 256) return fail(MOE_EINVAL, "packed rows take at most 256 groups");
+// The gate/up launch of the expert FFN (h = act(a w_in^T + b_in), or the
+// SwiGLU pair, with the pre-activations into pre0/pre1 when given).  The
+// backward pass recomputes pre-activations with exactly this launch, so that
+// they equal the forward's bit for bit (same tiles, same k order, the same
+// split of a last round when tail_part is given).
+GemmArgs up_args(const moe_config& c, int act, int groups, int64_t rpg, const int32_t* rows, const void* a,
+                 const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate, const void* b_in, int F,
+                 void* h, bool packed, void* pre0, void* pre1, float* tail_part) {
   GemmArgs g1{};
   g1.A = a;
   g1.gather = gather;
@@ -320,6 +310,35 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   g1.act = act == MOE_SWIGLU ? 2 : 1;
   g1.pre0 = pre0;
   g1.pre1 = pre1;
+  // a last, mostly empty round of tiles split along k (the launch decides on
+  // the device, from the row counts)
+  if (tail_part && !packed && rows && c.dtype == MOE_BF16) {
+    g1.tail_part = tail_part;
+    g1.tail_parts = 8;
+  }
+  return g1;
+}
+
+// Expert FFN on `groups` groups of rows: h = act(a w_in^T (+ b_in)) (or the
+// SwiGLU pair), out = h w_out^T (+ b_out).  With `gather`, row m of group g
+// is row gather[base_g + m] of a ([a_rows, d]), base_g = g*rpg, or with
+// `packed` rows[0] + ... + rows[g-1] (then rpg is the bound on their sum).
+moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int32_t* rows, const void* a,
+               const int32_t* gather, int64_t a_rows, const void* w_in, const void* w_gate,
+               const void* b_in, const void* w_out, const void* b_out, int F, void* h, void* out,
+               hipStream_t s, bool packed = false, int64_t group_rows = 0, void* pre0 = nullptr,
+               void* pre1 = nullptr, float* kpart = nullptr, float* tail_part = nullptr) {
+  // each operand a GEMM launch addresses through one buffer descriptor (one
+  // group's rows) stays below 2^30 elements (2^31 bytes); packed groups hold
+  // at most group_rows rows
+  const int64_t lim = int64_t{1} << 30;
+  const int64_t gr = packed && group_rows > 0 ? std::min(group_rows, rpg) : rpg;
+  if (gr * c.d >= lim || gr * F >= lim || static_cast<int64_t>(F) * c.d >= lim ||
+      (gather && a_rows * c.d >= lim))
+    return fail(MOE_EINVAL, "one expert's operands must hold < 2^30 elements");
+  if (packed && groups > 256) return fail(MOE_EINVAL, "packed rows take at most 256 groups");
+  const GemmArgs g1 = up_args(c, act, groups, rpg, rows, a, gather, a_rows, w_in, w_gate, b_in, F, h, packed, pre0,
+                              pre1, tail_part);
   MOE_TRY(hip_status(launch_gemm(g1, c.dtype, s), "expert GEMM 1"));
   GemmArgs g2{};
   g2.A = h;
@@ -502,6 +521,7 @@ struct BwdWorkspace {
   bf16_t* dUsT;
   int32_t* pstart;
   int32_t* kstart;
+  float* tailpart;
   int64_t Kw;                 // columns of the transposed expert operands (packed along k)
   int S;
   size_t bytes;
@@ -543,6 +563,7 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   b.dH = static_cast<bf16_t*>(take(h2 * R * F));
   b.dact = static_cast<bf16_t*>(take(h2 * R * ga * F));
   b.dA = static_cast<bf16_t*>(take(h2 * R * d));
+  if (!c.dropless) b.tailpart = static_cast<float*>(take(kTailPartBytes));
   if (c.dropless) b.pstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
   b.kstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
   // the transposed expert operands of the weight gradients, packed along k:
@@ -1362,13 +1383,12 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
                      const void* bias, void* out, int N, int K) -> moe_status {
       return bgemm(what, A, 0, 0, gather, a_rows, B, 0, 0, bias, out, rows, rpg, E, N, K, s, nullptr, dl);
     };
-    if (c.save_preact) {
-      // the forward pass kept them
-    } else if (glu) {
-      MOE_TRY(rgemm("recompute gate projection", x, w.row_token, T, wt->w_gate, nullptr, b.U, static_cast<int>(F), c.d));
-      MOE_TRY(rgemm("recompute up projection", x, w.row_token, T, wt->w_in, nullptr, b.U2, static_cast<int>(F), c.d));
-    } else {
-      MOE_TRY(rgemm("recompute pre-activation", x, w.row_token, T, wt->w_in, wt->b_in, b.U, static_cast<int>(F), c.d));
+    if (!c.save_preact) {
+      // the forward's gate/up launch again, with its activations into the dH
+      // buffer (scratch until dH is formed) and the pre-activations kept
+      const GemmArgs g1 = up_args(c, c.act, E, rpg, rows, x, w.row_token, T, wt->w_in, wt->w_gate, wt->b_in,
+                                  static_cast<int>(F), b.dH, dl, b.U, glu ? b.U2 : nullptr, b.tailpart);
+      MOE_TRY(hip_status(launch_gemm(g1, MOE_BF16, s), "recompute pre-activations"));
     }
     // dH = dYe W_out: W_out [E, d, F] -> [E, F, d]
     MOE_TRY(transpose("w_out transpose", static_cast<const bf16_t*>(wt->w_out), b.woT, E, d, F, d, d * F, F, F * d, d,

@@ -238,13 +238,15 @@ __device__ __forceinline__ TileCoord decode_dense(int L, int groups, int ntiles,
   return tc;
 }
 
-// Tail split (bias-only GEMMs with device row counts and a partial-sum
-// workspace): when the dense tiles fill a last round of the GPU's 256
-// compute units at most half, that round's R tiles are split along k into P
-// parts (P*R <= 256, parts of at least 512 k), written as float32 partial
-// tiles and summed in part order by tail_sum_kernel.  F = tiles before the
-// tail (all tiles when nothing is split).
+// Tail split (GEMMs with device row counts and a partial-sum workspace):
+// when the dense tiles fill a last round of the GPU's 256 compute units at
+// most half, that round's R tiles are split along k into P parts (P*R <= 256,
+// parts of at least kTailMinK: shorter tiles lose more to the extra pass than
+// the idle compute units cost), written as float32 partial tiles and summed
+// in part order by tail_sum_kernel.  F = tiles before the tail (all tiles
+// when nothing is split).
 constexpr int kCUs = 256;
+constexpr int kTailMinK = 2048;
 struct TailPlan {
   int F, R, P;
   int kslice;
@@ -253,7 +255,7 @@ __device__ __forceinline__ TailPlan tail_plan(int NT, int K, int max_parts) {
   TailPlan t{NT, 0, 1, K};
   const int R = NT % kCUs;
   if (NT < kCUs || R == 0 || R > kCUs / 2) return t;
-  const int P = min(min(max_parts, kCUs / R), K / 512);
+  const int P = min(min(max_parts, kCUs / R), K / kTailMinK);
   if (P < 2) return t;
   t.kslice = ((K + P - 1) / P + 63) / 64 * 64;
   t.P = (K + t.kslice - 1) / t.kslice;
@@ -335,7 +337,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     __syncthreads();
     const int NT = pk_end[a.groups - 1];
     int Lt = static_cast<int>(L);
-    if (ACT == 0 && a.tail_part) {
+    if (ACT != 3 && a.tail_part) {
       const TailPlan tp = tail_plan(NT, a.K, a.tail_parts);
       if (L >= tp.F + static_cast<int64_t>(tp.R) * tp.P) return;
       if (L >= tp.F) {
@@ -543,8 +545,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
       }
       return;
     }
-    if (ACT == 0 && tail_slot >= 0) {
-      // tail split: this part's float32 sums as a [256 x 256] partial tile
+    if (ACT != 3 && tail_slot >= 0) {
+      // tail split: this part's float32 sums as a [256 x 256] partial tile,
+      // column = the tile's weight row (SwiGLU: gate rows 0..127, up rows
+      // 128..255); no bias or activation yet
       float* P = a.tail_part + static_cast<int64_t>(tail_slot) * (kBM * kBW);
 #pragma unroll
       for (int j = 0; j < kXB; ++j) {
@@ -556,7 +560,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
           for (int q = 0; q < 4; ++q) {
             const int n = ncol[i] + 8 * q + 4 * (lane >> 5);
             if (n0 + n >= N) continue;
-            *reinterpret_cast<float4*>(P + m * kBW + n) =
+            const int wr = (kGlu ? (i >> 1) * 128 : 0) + n;
+            *reinterpret_cast<float4*>(P + m * kBW + wr) =
                 make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -874,47 +879,67 @@ __global__ __launch_bounds__(kThreads) void ksum_kernel(GemmArgs a) {
   *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.C) + row * a.N + c) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Tail split: tile F + blockIdx.x of the tail = bf16(sum over its parts, in
-// order, of the float32 partial tiles + bias), for its valid rows and
-// columns; the plan is recomputed from the same device row counts.
+// Tail split: tile F + blockIdx.x of the tail = act(sum over its parts, in
+// part order, of the float32 partial tiles + bias), rounded to bf16, for its
+// valid rows and columns (with the pre-activations when kept); the plan is
+// recomputed from the same device row counts.
+template <int ACT>
 __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
+  constexpr bool kGlu = ACT == 2;
+  constexpr int kNOut = kGlu ? kBW / 2 : kBW;
   __shared__ int tab[3 * kMaxPackedGroups];
   int* pk_start = tab;
   int* pk_rows = tab + kMaxPackedGroups;
   int* pk_end = tab + 2 * kMaxPackedGroups;
   const int N = a.N;
-  const int ntiles = (N + kBW - 1) / kBW;
+  const int ntiles = (N + kNOut - 1) / kNOut;
   build_tile_table(a, ntiles, pk_start, pk_rows, pk_end);
   __syncthreads();
   const TailPlan tp = tail_plan(pk_end[a.groups - 1], a.K, a.tail_parts);
   const int t = blockIdx.x;
   if (t >= tp.R) return;
   const TileCoord tc = decode_dense(tp.F + t, a.groups, ntiles, pk_end);
-  const int m0 = tc.mt * kBM, n0 = tc.nt * kBW;
-  const int vr = min(kBM, pk_rows[tc.g] - m0), vc = min(kBW, N - n0);
+  const int m0 = tc.mt * kBM, n0 = tc.nt * kNOut;
+  const int vr = min(kBM, pk_rows[tc.g] - m0), vc = min(kNOut, N - n0);
   const int64_t row_base = static_cast<int64_t>(tc.g) * a.rows_per_group;
   const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N + n0 : nullptr;
-  bf16_t* C = static_cast<bf16_t*>(a.C) + (row_base + m0) * N + n0;
-  for (int i = threadIdx.x; i < kBM * (kBW / 8); i += kThreads) {
-    const int r = i / (kBW / 8), c = (i % (kBW / 8)) * 8;
-    if (r >= vr || c >= vc) continue;
-    float v[8] = {};
-    for (int p = 0; p < tp.P; ++p) {
-      const float4* q = reinterpret_cast<const float4*>(
-          a.tail_part + (static_cast<int64_t>(t) * tp.P + p) * (kBM * kBW) + r * kBW + c);
-      const float4 x0 = q[0], x1 = q[1];
-      v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
-      v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
-    }
-    if (bias) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] += bf16_to_f32(bias[c + u]);
-    }
+  const int64_t obase = (row_base + m0) * N + n0;
+  auto pack = [](const float (&v)[8]) {
     uint32_t w[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       w[u] = static_cast<uint32_t>(f32_to_bf16(v[2 * u])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * u + 1])) << 16);
-    *reinterpret_cast<uint4*>(C + static_cast<int64_t>(r) * N + c) = make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  for (int i = threadIdx.x; i < kBM * (kNOut / 8); i += kThreads) {
+    const int r = i / (kNOut / 8), c = (i % (kNOut / 8)) * 8;
+    if (r >= vr || c >= vc) continue;
+    float v[8] = {}, u[8] = {};
+    for (int p = 0; p < tp.P; ++p) {
+      const float* src = a.tail_part + (static_cast<int64_t>(t) * tp.P + p) * (kBM * kBW) + r * kBW + c;
+      const float4 x0 = reinterpret_cast<const float4*>(src)[0], x1 = reinterpret_cast<const float4*>(src)[1];
+      v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
+      v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
+      if (kGlu) {
+        const float4 y0 = reinterpret_cast<const float4*>(src + 128)[0], y1 = reinterpret_cast<const float4*>(src + 128)[1];
+        u[0] += y0.x; u[1] += y0.y; u[2] += y0.z; u[3] += y0.w;
+        u[4] += y1.x; u[5] += y1.y; u[6] += y1.z; u[7] += y1.w;
+      }
+    }
+    if (!kGlu && bias) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += bf16_to_f32(bias[c + q]);
+    }
+    const int64_t o = obase + static_cast<int64_t>(r) * N + c;
+    if (ACT != 0 && a.pre0) {
+      *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.pre0) + o) = pack(v);
+      if (kGlu) *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.pre1) + o) = pack(u);
+    }
+    float out[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      out[q] = ACT == 2 ? silu_fast(v[q]) * u[q] : ACT == 1 ? gelu_erf(v[q]) : v[q];
+    *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.C) + o) = pack(out);
   }
 }
 }  // namespace
@@ -922,7 +947,7 @@ __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
 hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
   GemmArgs a = a_in;
   // the tail split applies to bias-only bf16 GEMMs over device row counts
-  const bool tail = dtype == MOE_BF16 && a.act == 0 && a.tail_part != nullptr && a.rows != nullptr && !a.packed &&
+  const bool tail = dtype == MOE_BF16 && a.act != 3 && a.tail_part != nullptr && a.rows != nullptr && !a.packed &&
                     !(a.ksplit > 1) && a.tail_parts >= 2;
   if (!tail) a.tail_part = nullptr;
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
@@ -942,7 +967,11 @@ hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
       case 2: launch_bf16<2>(a, grid, s); break;
       default: launch_bf16<3>(a, grid, s); break;
     }
-    if (tail) tail_sum_kernel<<<kCUs / 2, kThreads, 0, s>>>(a);
+    if (tail) {
+      if (a.act == 0) tail_sum_kernel<0><<<kCUs / 2, kThreads, 0, s>>>(a);
+      else if (a.act == 1) tail_sum_kernel<1><<<kCUs / 2, kThreads, 0, s>>>(a);
+      else tail_sum_kernel<2><<<kCUs / 2, kThreads, 0, s>>>(a);
+    }
     if (split) {
       const int64_t items = static_cast<int64_t>(a.groups) * a.rows_per_group * (a.N / 8);
       ksum_kernel<<<static_cast<unsigned>((items + kThreads - 1) / kThreads), kThreads, 0, s>>>(a);

@@ -326,6 +326,29 @@ def test_backward_dropless(moe, case):
     _compare(w, grads, ref)
 
 
+@pytest.mark.parametrize('name', ['deepseekmoe_fine', 'swiglu_tail'])
+def test_saved_preactivations_equal_recomputation_with_a_split_last_round(moe, name):
+    # the 64-expert layer at full size, and a SwiGLU layer of 8 experts filled
+    # to 9 row tiles whose gate/up launch (d = 4096, 8 x 9 x 8 = 576 tiles)
+    # splits its last round of 64 tiles along k: the backward's recomputation
+    # repeats the forward's launch, so saved and recomputed pre-activations,
+    # and every gradient, are the same bits
+    if name == 'deepseekmoe_fine':
+        w, over = synth.WORKLOADS['deepseekmoe_fine'], {}
+    else:
+        w = synth.Workload('swiglu_tail', T=12000, d=4096, E=8, k=2, d_ff=1024, act='swiglu', score='softmax',
+                           renormalize=-1, cf=1.25, dtype='bf16', seed=66)
+        over = dict(capacity_override=2304)
+    say('save_preact with a split last round', name)
+    inp, ex, sh, dev, dy = _layer(moe, w, 0)
+    out0, g0 = _gpu_pass(moe, w, dev, dy, **over)
+    out1, g1 = _gpu_pass(moe, w, dev, dy, save_preact=True, **over)
+    for kk in out0:
+        assert torch.equal(out0[kk], out1[kk]), kk
+    for kk in g0:
+        assert torch.equal(g0[kk], g1[kk]), kk
+
+
 def test_saved_preactivations_equal_recomputation_dropless(moe):
     name, w, over = BWD_CASES[1]
     inp, ex, sh, dev, dy = _layer(moe, w, 0)

@@ -644,10 +644,10 @@ def test_forward_sigmoid_stress_sampled(moe):
 def test_forward_splits_the_last_round_of_the_down_projection(moe):
     # 8 experts each filled to a capacity of 9 row tiles, d = 2048 (8 column
     # tiles): the down projection has 576 tiles, a last round of 64 on 256
-    # compute units, which the launch splits along k (d_ff = 1024: 2 parts of
-    # 512); compared on tokens routed to the last expert, whose tiles form that
-    # round, and on others
-    w = synth.Workload('tail_round', T=12000, d=2048, E=8, k=2, d_ff=1024, act='gelu', score='softmax',
+    # compute units, which the launch splits along k (d_ff = 4096: 2 parts of
+    # 2048); compared on tokens routed to the last expert, whose tiles form
+    # that round, and on others
+    w = synth.Workload('tail_round', T=12000, d=2048, E=8, k=2, d_ff=4096, act='gelu', score='softmax',
                        renormalize=-1, cf=1.25, dtype='bf16', seed=41)
     inp = synth.router_inputs(w)
     z = O.router_logits(synth.as_f32(inp['x']), inp['w_router'], inp['logit_bias'])
