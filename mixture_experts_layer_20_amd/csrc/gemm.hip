@@ -21,16 +21,22 @@
 //     one wavefront instruction fills 8 rows x 128 bytes, i.e. whole cache
 //     lines (the load path moves about 1.7x the bytes per cycle it moves
 //     for half lines).  The token rows and the weight rows each have their
-//     own ring of stage buffers in LDS, one barrier per 64-wide k stage;
+//     own ring of stage buffers in LDS (2 token stages, 3 weight stages:
+//     160 KiB), one barrier per 64-wide k stage;
 //     16-byte chunks XOR-swizzled by row so fragment reads spread over the
 //     LDS banks.  Token rows may be gathered through a row list (the
 //     dispatch is fused into this load).
-//   * Tile order: logical tiles walk bands of 4 row tiles (2 for narrow
-//     outputs) column by column,
-//     and 32-tile chunks of them are dealt round-robin to the 8 XCDs (blocks
+//   * Tile order: with row counts on the device, only tiles that hold rows
+//     are numbered (so no empty tile sits between the chunks below); tiles
+//     walk bands of 4 row tiles (2 for narrow outputs) column by column, and
+//     32-tile chunks of them are dealt round-robin to the 8 XCDs (blocks
 //     reach XCDs round-robin), so the ~32 tiles an XCD runs at once share 4
 //     token panels and 8 weight panels in its L2 while every XCD gets an even
 //     share of every expert.
+//   * Tail split: a last round of tiles that would leave more than half of
+//     the 256 compute units idle is split along k into float32 partial tiles
+//     (a workspace), summed in part order by a small kernel that applies the
+//     bias and activation.
 //   * A partial tile (an expert's last, fewer than 256 valid token rows, or
 //     one reaching past N) skips the MFMAs of 32-row token blocks without
 //     valid rows and of 32-row weight blocks past N.
@@ -54,34 +60,24 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kBM = 256;     // token rows per tile
 constexpr int kBW = 256;     // weight rows per tile
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-#ifndef MOE_GEMM_NX
-#define MOE_GEMM_NX 2
-#endif
-#ifndef MOE_GEMM_NW
-#define MOE_GEMM_NW 3
-#endif
-#ifndef MOE_GEMM_LOADPOS
-#define MOE_GEMM_LOADPOS 2
-#endif
-constexpr int kBK = MOE_GEMM_BK;          // k per pipeline stage
-constexpr int kNX = MOE_GEMM_NX;          // token-row stages in LDS
-constexpr int kNW = MOE_GEMM_NW;          // weight-row stages in LDS
+constexpr int kBK = 64;      // k per pipeline stage
+constexpr int kNX = 2;       // token-row stages in LDS
+constexpr int kNW = 3;       // weight-row stages in LDS (one more in flight: the
+                             // weight panels are the operand that misses L2)
+constexpr int kLoadPositions = 2;   // 16-k steps a stage's loads are spread over
 constexpr int kRowBytes = kBK * 2;                         // 128: one full cache line per row
 constexpr int kChunks = kRowBytes / 16;                    // 16-byte k-chunks per row
 constexpr int kXBytes = kBM * kRowBytes;                   // one token-row stage (32 KiB)
 constexpr int kWBytes = kBW * kRowBytes;                   // one weight-row stage (32 KiB)
-constexpr int kLdsBytes = kNX * kXBytes + kNW * kWBytes;   // 128 KiB
+constexpr int kLdsBytes = kNX * kXBytes + kNW * kWBytes;   // 160 KiB
 constexpr int kRowsPerLoad = 1024 / kRowBytes;             // rows one wave instruction fills
-// Wavefronts per workgroup, per kernel: 8 (two per SIMD, each owning 64
-// token rows x 128 weight rows of the output) or 4 (one per SIMD, 128 x
-// 128: a third fewer LDS fragment reads per flop, but one wave per SIMD to
-// hide latency).  Measured per GEMM; see launch_gemm.
+// Wavefronts per workgroup: 8, two per SIMD, each owning 64 token rows x 128
+// weight rows of the output (measured against 4 waves of 128 x 128, which
+// need 256 accumulators a lane and spill or lose the second wave per SIMD
+// that hides latency).
 template <int W>
 struct Geo {
-  static_assert(W == 4 || W == 8, "4 or 8 wavefronts");
+  static_assert(W == 8, "8 wavefronts");
   static constexpr int kWaves = W;
   static constexpr int kThreads = W * 64;
   static constexpr int kHalf = W / 2;                         // waves staging each operand
@@ -272,23 +268,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-#ifndef MOE_GEMM_WAVES0
-#define MOE_GEMM_WAVES0 8
-#endif
-#ifndef MOE_GEMM_WAVES1
-#define MOE_GEMM_WAVES1 8
-#endif
-#ifndef MOE_GEMM_WAVES2
-#define MOE_GEMM_WAVES2 8
-#endif
-#ifndef MOE_GEMM_WAVES3
-#define MOE_GEMM_WAVES3 8
-#endif
-// wavefronts per workgroup of each bf16 kernel (by ACT)
-constexpr int waves_of(int act) {
-  return act == 0 ? MOE_GEMM_WAVES0 : act == 1 ? MOE_GEMM_WAVES1 : act == 2 ? MOE_GEMM_WAVES2 : MOE_GEMM_WAVES3;
-}
 
 template <int ACT, int W>
 __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
@@ -669,7 +648,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // of its operand issued after stage kt+1 (nring - 2 of them).
   constexpr int kSteps = kBK / 16;
   static_assert(kSteps % 2 == 0, "fragment slots alternate per 16-k step");
-  constexpr int kLoadPos = MOE_GEMM_LOADPOS < kSteps ? MOE_GEMM_LOADPOS : kSteps;
+  constexpr int kLoadPos = kLoadPositions < kSteps ? kLoadPositions : kSteps;
   static_assert(kNX >= 2 && kNW >= 2, "two stages at least");
   // loads of window position p: [pos_begin(p), pos_begin(p + 1))
   auto pos_begin = [](int p) { return p >= kLoadPos ? kLoadsPerWave : (kLoadsPerWave * p) / kLoadPos; };
@@ -751,15 +730,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   else run(std::true_type{});
 }
 
-// The bf16 kernels, one per workgroup size (the body is a device function
-// so that the wave count is a literal in each kernel).
+// The bf16 kernel: 8 wavefronts, one workgroup per compute unit (LDS).
 template <int ACT>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_w8(GemmArgs a) {
   gemm_bf16_body<ACT, 8>(a);
-}
-template <int ACT>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_w4(GemmArgs a) {
-  gemm_bf16_body<ACT, 4>(a);
 }
 
 // ------------------------------------------------------------------ float32
@@ -845,8 +819,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
 
 template <int ACT>
 void launch_bf16(const GemmArgs& a, unsigned grid, hipStream_t s) {
-  if constexpr (waves_of(ACT) == 8) gemm_bf16_w8<ACT><<<grid, 512, 0, s>>>(a);
-  else gemm_bf16_w4<ACT><<<grid, 256, 0, s>>>(a);
+  gemm_bf16_w8<ACT><<<grid, 512, 0, s>>>(a);
 }
 
 namespace {
