@@ -2,8 +2,8 @@
 //
 // Sources: "Lab 18 -- Mixture of experts" s.1 (y = sum of gated expert
 // outputs), s.2 (Switch loss E * sum f_i P_i with f over the T*k assignments;
-// router z-loss) and s.3 (a dropped slot contributes nothing; a token whose
-// every assignment was dropped reaches the next layer unchanged); "Lab 01"
+// router z-loss) and s.3 (dropped slots add nothing; a token left with no
+// kept assignment passes its input through); "Lab 01"
 // "Where to start" 5 (the residual fallback) and "The traps" (f divides by
 // T*k); "Phase 02" concept map (shared expert for every token).
 #include "common.hpp"

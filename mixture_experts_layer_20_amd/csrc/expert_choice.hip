@@ -2,11 +2,11 @@
 // router probability for it.
 //
 // Sources: "Lab 18 -- Mixture of experts", exercise 1 and "Common
-// extensions" (each expert picks its top tokens instead of each token its
-// top experts: balanced by construction, nothing dropped, a token may be
-// picked by several experts or by none); "Mixture of experts" lecture,
-// routing families (the top of each expert's row of the token x expert
-// score matrix).
+// extensions" (the selection runs per expert over the tokens rather than per
+// token over the experts, so the load is even by construction, no choice is
+// dropped, and a token can receive several experts or none); "Mixture of
+// experts" lecture, routing families (selection along the expert axis of the
+// token x expert score matrix).
 //
 // Ties go to the lower token; an expert's picks sit in its rows in token
 // order.  The decision is taken on the float32 probabilities as stored.
