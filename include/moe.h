@@ -129,11 +129,10 @@ typedef struct moe_config {
  *   - moe_combine reads ye[slot[t,j]]. */
 
 /* Expert-choice routing (routing = MOE_EXPERT_CHOICE) ["Lab 18" exercise 1
- * and "Common extensions": each expert picks its top tokens, so the load is
- * balanced by construction and nothing is dropped, while a token may be
- * picked by several experts or by none; "Mixture of experts" lecture,
- * routing families: the top of each expert's row of the token x expert
- * score matrix]:
+ * and "Common extensions": selection per expert over the tokens, which
+ * evens the load by construction and drops nothing, while a token can get
+ * several experts or none; "Mixture of experts" lecture, routing families:
+ * selection along the expert axis of the token x expert score matrix]:
  *   - C is computed as above (k is then the mean number of experts a token
  *     gets) and every expert takes n = min(C, T) tokens: those with the
  *     largest float32 probability probs[t,e], equal values to the lower
