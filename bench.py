@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--phase-reps R] [--dropless]
                     [--routing token|expert] [--priority rank|token|score] [--backward]
-                    [--save-preact] [--graph]
+                    [--save-preact | --no-save-preact] [--graph]
 
 A step is one whole forward pass of the layer (router, capacity, dispatch,
 routed and shared expert FFNs, combine, losses) over one batch of T synthetic
@@ -62,7 +62,10 @@ def parse():
     p.add_argument('--backward', action='store_true',
                    help='also time moe_backward (the gradients of the same layer) as a phase')
     p.add_argument('--save-preact', action='store_true',
-                   help='the forward pass keeps the expert pre-activations for the backward pass')
+                   help='the forward pass keeps the expert pre-activations for the backward pass '
+                        '(the default with --backward)')
+    p.add_argument('--no-save-preact', action='store_true',
+                   help='with --backward: recompute the pre-activations in the backward pass instead')
     p.add_argument('--graph', action='store_true',
                    help='capture one moe_forward into a HIP graph and time its replays')
     p.add_argument('--copy-calibration', action='store_true',
@@ -70,7 +73,44 @@ def parse():
     p.add_argument('--cpu-baseline-all', action='store_true',
                    help='time the CPU oracle on every workload (bounded samples) and the brute force on the '
                         'tiny one; no GPU work')
-    return p.parse_args()
+    p.add_argument('--yardstick-shapes', default=None,
+                   help='with --vendor-yardstick: comma-separated MxNxK shapes')
+    p.add_argument('--vendor-yardstick', action='store_true',
+                   help='time the vendor dense GEMM (through torch) on the Mixtral-shaped expert GEMMs, for '
+                        'comparison only; no MoE layer')
+    args = p.parse_args()
+    if args.save_preact and args.no_save_preact:
+        p.error('--save-preact and --no-save-preact exclude each other')
+    # a training step keeps the pre-activations unless asked not to
+    args.save_preact = args.save_preact or (args.backward and not args.no_save_preact)
+    return args
+
+
+YARDSTICK_SHAPES = '16384x28672x4096,16384x4096x14336,2048x28672x4096,2048x4096x14336'
+
+
+def vendor_yardstick(steps, shapes=YARDSTICK_SHAPES):
+    """torch's dense bf16 GEMM (the vendor library) on the shapes of the
+    Mixtral-shaped layer's expert GEMMs (M x N x K): all 16,384 kept rows at
+    once, and one expert's 2,048 rows; random normal operands, steady state."""
+    import torch
+    for M, N, K in (tuple(int(v) for v in sh.split('x')) for sh in shapes.split(',')):
+        g = torch.Generator('cuda').manual_seed(7)
+        a = torch.randn(M, K, device='cuda', dtype=torch.bfloat16, generator=g)
+        b = (torch.randn(N, K, device='cuda', dtype=torch.bfloat16, generator=g) / 64).contiguous()
+        for _ in range(5):
+            c = a @ b.t()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            c = a @ b.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        print(f'vendor GEMM {M}x{N}x{K}: {ms:.3f} ms, {2 * M * N * K / ms / 1e9:.1f} TFLOP/s '
+              f'({2 * M * N * K / ms / 1e9 / PEAK_BF16_TFLOPS:.3f} of peak)', flush=True)
+        del a, b, c
 
 
 class HipEvents:
@@ -119,6 +159,9 @@ def main():
     args = parse()
     if args.cpu_baseline_all:
         cpu_baseline_all()
+        return
+    if args.vendor_yardstick:
+        vendor_yardstick(max(1, args.steps), args.yardstick_shapes or YARDSTICK_SHAPES)
         return
     if args.gpus != 1:
         print(json.dumps({'error': 'this build runs on one GPU only: the MoE layer is measured on a '

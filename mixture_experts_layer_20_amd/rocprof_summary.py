@@ -11,6 +11,10 @@ with ``--skip W --take N`` it adds, for the expert GEMM launches (gate/up,
 down, and the tail sum of a split last round), the median and mean duration
 over their dispatches W .. W+N-1 in launch order (the timed forward passes of
 ``bench.py``, after its W warm-up passes and before its phase loop).
+``counters`` takes a ``--pmc ... --kernel-trace`` run and prints, per kernel,
+the mean over its dispatches of each counter and of the duration, with the
+shader clock (GRBM_GUI_ACTIVE cycles per microsecond of the dispatch) and, when
+collected, MFMA busy (MfmaUtil) and bf16 matrix-core work (MOPS x 512 flop).
 ``traffic`` takes one ``--pmc FETCH_SIZE`` run and one ``--pmc WRITE_SIZE`` run
 of ``bench.py --copy-calibration`` and prints, per kernel, the average counter
 value per dispatch (KiB), the calibration factor that the plain copy kernel of
@@ -131,6 +135,58 @@ def cmd_trace(a):
                                    'expert_ffn_us_median': tot_med, 'expert_ffn_us_mean': tot_mean}))
 
 
+def counters_per_kernel(d, skip_pattern=r'reduce_kernel|FillFunctor|copyBuffer|fillBuffer|elementwise'):
+    """{kernel: {'n': dispatches, 'duration_us': mean, counter: mean per dispatch}}."""
+    con = sqlite3.connect(find_db(d))
+    try:
+        dur = {did: (n, (e - b) / 1000.0) for did, n, b, e in
+               con.execute('select dispatch_id, name, start, "end" from kernels')}
+    except sqlite3.Error:           # counters without a kernel trace
+        dur = {}
+    vals = {}
+    for did, kn, cn, v in con.execute('select dispatch_id, kernel_name, counter_name, value from counters_collection'):
+        vals.setdefault(kn, {}).setdefault(did, {}).setdefault(cn, 0.0)
+        vals[kn][did][cn] += v
+    out = {}
+    for kn, per in vals.items():
+        if re.search(skip_pattern, kn):
+            continue
+        ds = [dur[did][1] for did in per if did in dur]
+        row = {'n': len(per), 'duration_us': sum(ds) / len(ds) if ds else float('nan')}
+        names = sorted({cn for v in per.values() for cn in v})
+        for cn in names:
+            xs = [v[cn] for v in per.values() if cn in v]
+            row[cn] = sum(xs) / len(xs)
+        out[kn] = row
+    return out
+
+
+def cmd_counters(a):
+    tab = counters_per_kernel(a.dir)
+    print(a.title)
+    if a.command:
+        print('command:', a.command)
+    print()
+    for kn, row in sorted(tab.items(), key=lambda kv: -kv[1]['duration_us'] * kv[1]['n']):
+        print(f'{short(kn, 100)}')
+        t = row['duration_us']
+        line = [f'dispatches {row["n"]}', f'mean duration {t:.1f} us']
+        if 'GRBM_GUI_ACTIVE' in row and t > 0:
+            line.append(f'shader clock {row["GRBM_GUI_ACTIVE"] / t / 1000:.3f} GHz (GRBM_GUI_ACTIVE / duration)')
+        if 'MfmaUtil' in row:
+            line.append(f'MFMA busy {row["MfmaUtil"] / 100:.3f} of SIMD cycles (MfmaUtil)')
+        if 'SQ_INSTS_VALU_MFMA_MOPS_BF16' in row and t > 0:
+            fl = row['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512
+            line.append(f'bf16 matrix work {fl:.4g} flop = {fl / t / 1e6:.1f} TFLOP/s')
+        if 'TCC_HIT_sum' in row and 'TCC_MISS_sum' in row:
+            h, m = row['TCC_HIT_sum'], row['TCC_MISS_sum']
+            line.append(f'L2 hit rate {h / max(1.0, h + m):.3f}')
+        for cn, v in row.items():
+            if cn not in ('n', 'duration_us'):
+                line.append(f'{cn} {v:.6g}')
+        print('    ' + '; '.join(line))
+
+
 def cmd_traffic(a):
     fetch = pmc_per_kernel(a.fetch_dir, 'FETCH_SIZE')
     write = pmc_per_kernel(a.write_dir, 'WRITE_SIZE')
@@ -138,7 +194,7 @@ def cmd_traffic(a):
     def pick(tab, pattern):
         hits = [(kn, v) for kn, v in tab.items() if re.search(pattern, kn)]
         if len(hits) != 1:
-            raise SystemExit(f'expected one kernel matching {tag!r}, found {[h[0] for h in hits]}')
+            raise SystemExit(f'expected one kernel matching {pattern!r}, found {[h[0] for h in hits]}')
         return hits[0][1]
 
     copy_f, copy_w = pick(fetch, COPY_KERNEL_TAG)[1], pick(write, COPY_KERNEL_TAG)[1]
@@ -147,6 +203,12 @@ def cmd_traffic(a):
     # the expert GEMM kernels (either workgroup size): SwiGLU up/gate, then down
     g2f, g2w = pick(fetch, GEMM_UP)[1], pick(write, GEMM_UP)[1]
     g0f, g0w = pick(fetch, GEMM_DOWN)[1], pick(write, GEMM_DOWN)[1]
+    # the ordered sum of split last rounds belongs to the launch it finishes;
+    # per pair it runs as often as the GEMMs (dispatch-weighted mean)
+    n_pair = pick(fetch, GEMM_DOWN)[0]
+    tf = sum(n * v for kn, (n, v) in fetch.items() if re.search(r'tail_sum_kernel', kn)) / max(1, n_pair)
+    tw = sum(n * v for kn, (n, v) in write.items() if re.search(r'tail_sum_kernel', kn)) / max(1, n_pair)
+    g0f, g0w = g0f + tf, g0w + tw
     print(f'HBM traffic of the expert grouped GEMM, {a.workload} workload (rocprofv3 --pmc)')
     if a.command_fetch:
         print('command (FETCH_SIZE):', a.command_fetch)
@@ -192,6 +254,10 @@ def main():
     t.add_argument('--command', default='')
     t.add_argument('--skip', type=int, default=0, help='warm-up forward passes before the timed ones')
     t.add_argument('--take', type=int, default=0, help='timed forward passes (0: no per-step section)')
+    cc = sub.add_parser('counters')
+    cc.add_argument('dir')
+    cc.add_argument('--title', default='rocprofv3 counters')
+    cc.add_argument('--command', default='')
     f = sub.add_parser('traffic')
     f.add_argument('fetch_dir')
     f.add_argument('write_dir')
@@ -200,7 +266,7 @@ def main():
     f.add_argument('--command-fetch', default='')
     f.add_argument('--command-write', default='')
     a = p.parse_args()
-    cmd_trace(a) if a.cmd == 'trace' else cmd_traffic(a)
+    {'trace': cmd_trace, 'counters': cmd_counters, 'traffic': cmd_traffic}[a.cmd](a)
 
 
 if __name__ == '__main__':
