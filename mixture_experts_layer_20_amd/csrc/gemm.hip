@@ -921,7 +921,8 @@ hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
   GemmArgs a = a_in;
   // the tail split applies to bias-only bf16 GEMMs over device row counts
   const bool tail = dtype == MOE_BF16 && a.act != 3 && a.tail_part != nullptr && a.rows != nullptr && !a.packed &&
-                    !(a.ksplit > 1) && a.tail_parts >= 2;
+                    !(a.ksplit > 1) && a.tail_parts >= 2 && a.K / kTailMinK >= 2;
+  // (a K below two minimum parts never splits: no extra blocks, no sum launch)
   if (!tail) a.tail_part = nullptr;
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {

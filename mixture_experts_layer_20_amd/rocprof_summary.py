@@ -8,9 +8,10 @@ library.
 
 ``trace`` prints the per-kernel table of a ``--kernel-trace --stats`` run;
 with ``--skip W --take N`` it adds, for the expert GEMM launches (gate/up,
-down, and the tail sum of a split last round), the median and mean duration
-over their dispatches W .. W+N-1 in launch order (the timed forward passes of
-``bench.py``, after its W warm-up passes and before its phase loop).
+down, and the tail sums of split last rounds), the median and mean duration
+over the dispatches of forward passes W .. W+N-1 in launch order (the timed
+passes of ``bench.py``, after its W warm-up passes and before its phase
+loop); ``--shared`` reports the shared experts' launches apart.
 ``counters`` takes a ``--pmc ... --kernel-trace`` run and prints, per kernel,
 the mean over its dispatches of each counter and of the duration, with the
 shader clock (GRBM_GUI_ACTIVE cycles per microsecond of the dispatch) and, when
@@ -83,7 +84,9 @@ def pmc_per_kernel(d, counter):
 GEMM_UP_ANY = r'gemm_bf16_w\d<[12]>'    # gate/up launch, GELU or SwiGLU
 STEP_KERNELS = ((GEMM_UP_ANY, 'expert GEMM gate/up'),
                 (GEMM_DOWN, 'expert GEMM down'),
-                (r'tail_sum_kernel', 'tail sum of the down GEMM'))
+                (r'tail_sum_kernel<[12]>', 'tail sum of the gate/up GEMM'),
+                (r'tail_sum_kernel<0>', 'tail sum of the down GEMM'),
+                (r'ksum_kernel', 'k-split sum of the down GEMM'))
 
 
 def dispatch_durations(d, pattern):
@@ -94,17 +97,37 @@ def dispatch_durations(d, pattern):
     return [(e - b) / 1000.0 for n, b, e in rows if re.search(pattern, n)]
 
 
-def step_table(d, skip, take, per_step=1):
-    """{label: (dispatches, median_us, mean_us)} over dispatches
-    [skip*per_step, (skip+take)*per_step) of each expert-GEMM kernel."""
+def _median(v):
+    srt = sorted(v)
+    n = len(srt)
+    return srt[n // 2] if n % 2 else 0.5 * (srt[n // 2 - 1] + srt[n // 2])
+
+
+def step_table(d, skip, take, shared=False):
+    """{label: (dispatches, median_us, mean_us)} over the dispatches of each
+    expert-GEMM kernel made by forward passes skip .. skip+take-1.  With
+    shared experts a pass launches each GEMM kernel twice, the routed experts'
+    launch first and the shared experts' second (no tail split there: they
+    are one group of T rows), so the dispatches alternate and are reported
+    apart."""
     out = {}
     for pat, label in STEP_KERNELS:
-        v = dispatch_durations(d, pat)[skip * per_step:(skip + take) * per_step]
-        if v:
-            srt = sorted(v)
-            out[label] = (len(v), srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] +
-                                                                                 srt[len(srt) // 2]),
-                          sum(v) / len(v))
+        if not shared:
+            v = dispatch_durations(d, pat)[skip:skip + take]
+            if v:
+                out[label] = (len(v), _median(v), sum(v) / len(v))
+            continue
+        v = dispatch_durations(d, pat)
+        if 'sum_kernel' in pat:
+            # a tail or k-split sum belongs to the routed launch only
+            v = v[skip:skip + take]
+            parts = ((label, v),)
+        else:
+            v = v[2 * skip:2 * (skip + take)]
+            parts = ((label + ' (routed)', v[0::2]), (label + ' (shared)', v[1::2]))
+        for lab, vv in parts:
+            if vv:
+                out[lab] = (len(vv), _median(vv), sum(vv) / len(vv))
     return out
 
 
@@ -119,7 +142,7 @@ def cmd_trace(a):
     for name, calls, total, avg, pct in rows:
         print(f'{short(name):72s} {calls:6d} {total:12.1f} {avg:10.2f} {pct:6.2f}')
     if a.take:
-        tab = step_table(a.dir, a.skip, a.take)
+        tab = step_table(a.dir, a.skip, a.take, a.shared)
         print()
         print(f'timed forward passes only: dispatches {a.skip} .. {a.skip + a.take - 1} of each kernel '
               f'(after {a.skip} warm-up passes; the phase loop excluded)')
@@ -129,10 +152,46 @@ def cmd_trace(a):
             print(f'{label:40s} {n:10d} {med:10.2f} {mean:10.2f}')
             tot_med += med
             tot_mean += mean
-        print(f'{"expert FFN per forward pass (sum)":40s} {"":10s} {tot_med:10.2f} {tot_mean:10.2f}')
+        print(f'{"expert FFNs per forward pass (sum)":40s} {"":10s} {tot_med:10.2f} {tot_mean:10.2f}')
         print('json:', json.dumps({'step_kernels_us': {k: {'n': v[0], 'median': v[1], 'mean': v[2]}
                                                       for k, v in tab.items()},
                                    'expert_ffn_us_median': tot_med, 'expert_ffn_us_mean': tot_mean}))
+        if a.bench_log:
+            print_agreement(tab, a.bench_log)
+
+
+def bench_line(path):
+    """The last bench.py JSON line in a log (stdout and the profiler's lines mixed)."""
+    rec = None
+    for line in open(path, errors='replace'):
+        if line.startswith('{"metric"'):
+            rec = json.loads(line)
+    if rec is None:
+        raise SystemExit(f'no bench.py JSON line in {path}')
+    return rec
+
+
+def print_agreement(tab, log):
+    """Trace sums of the timed passes against the live phase times (HIP
+    events inside the same passes) that the bench line of the same run reports."""
+    rec = bench_line(log)
+    live = rec.get('phases_live', {})
+    routed = sum(v[2] for k, v in tab.items() if '(shared)' not in k)
+    shared = sum(v[2] for k, v in tab.items() if '(shared)' in k)
+    print()
+    print('agreement with the bench line of the same run (its JSON line in the profiled command\'s output):')
+    ev = live.get('expert_ffn', {}).get('ms')
+    if ev:
+        print(f'  routed expert FFN: live phase (HIP events) {ev * 1000:.1f} us per pass, trace mean '
+              f'{routed:.1f} us: {abs(ev * 1000 - routed) / routed * 100:.1f}% apart')
+    if shared and live.get('shared_ffn', {}).get('ms'):
+        sv = live['shared_ffn']['ms']
+        print(f'  shared expert FFN: live phase {sv * 1000:.1f} us per pass, trace mean {shared:.1f} us: '
+              f'{abs(sv * 1000 - shared) / shared * 100:.1f}% apart')
+    rf = rec.get('roofline', {})
+    if rf:
+        print(f'  roofline.achieved {rf.get("achieved")} {rf.get("unit")} = {rf.get("frac")} of {rf.get("peak")}; '
+              f'ms_per_step {rec.get("ms_per_step")}, live pass {live.get("ms_per_step")} ms')
 
 
 def counters_per_kernel(d, skip_pattern=r'reduce_kernel|FillFunctor|copyBuffer|fillBuffer|elementwise'):
@@ -254,6 +313,10 @@ def main():
     t.add_argument('--command', default='')
     t.add_argument('--skip', type=int, default=0, help='warm-up forward passes before the timed ones')
     t.add_argument('--take', type=int, default=0, help='timed forward passes (0: no per-step section)')
+    t.add_argument('--bench-log', default='',
+                   help="the profiled bench.py run's output, for the agreement of trace and live phases")
+    t.add_argument('--shared', action='store_true',
+                   help='the layer has shared experts (each pass launches every GEMM kernel twice)')
     cc = sub.add_parser('counters')
     cc.add_argument('dir')
     cc.add_argument('--title', default='rocprofv3 counters')

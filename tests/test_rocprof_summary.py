@@ -98,3 +98,41 @@ def test_timed_steps_take_the_dispatches_between_warmup_and_phase_loop(tmp_path)
     tab = R.step_table(str(d), 2, 3)
     assert tab['expert GEMM gate/up'] == (3, 3500.0, 3500.0)
     assert tab['expert GEMM down'] == (3, 2000.0, 2000.0)
+
+
+def test_timed_steps_report_shared_expert_launches_apart(tmp_path):
+    d = tmp_path / 's'
+    os.makedirs(d)
+    con = sqlite3.connect(os.path.join(d, 'run_results.db'))
+    con.execute('create table kernels (name text, start int, "end" int)')
+    con.execute('create table top_kernels (name text, total_calls int, total_duration real, average real, percentage real)')
+    up = 'void moe::(anonymous namespace)::gemm_bf16_w8<1>(moe::GemmArgs)'
+    down = 'void moe::(anonymous namespace)::gemm_bf16_w8<0>(moe::GemmArgs)'
+    t = 0
+    # per pass: routed gate/up, routed down, shared gate/up, shared down;
+    # 1 warm-up pass (slow), then 2 timed passes
+    for scale in (3, 1, 1):
+        for name, dur in ((up, 130), (down, 110), (up, 60), (down, 55)):
+            con.execute('insert into kernels values (?,?,?)', (name, t, t + scale * dur * 1000))
+            t += scale * dur * 1000 + 10
+    con.commit()
+    con.close()
+    tab = R.step_table(str(d), 1, 2, shared=True)
+    assert tab['expert GEMM gate/up (routed)'] == (2, 130.0, 130.0)
+    assert tab['expert GEMM gate/up (shared)'] == (2, 60.0, 60.0)
+    assert tab['expert GEMM down (routed)'] == (2, 110.0, 110.0)
+    assert tab['expert GEMM down (shared)'] == (2, 55.0, 55.0)
+
+
+def test_agreement_reads_the_last_bench_line_of_a_mixed_log(tmp_path, capsys):
+    log = tmp_path / 'run.log'
+    rec = {'metric': 'm', 'ms_per_step': 0.6, 'phases_live': {'ms_per_step': 0.61, 'expert_ffn': {'ms': 0.242},
+                                                             'shared_ffn': {'ms': 0.115}},
+           'roofline': {'achieved': 400.0, 'unit': 'TFLOP/s', 'frac': 0.16, 'peak': 2500.0}}
+    log.write_text('W profiler line\n{"metric": "old"}\n' + json.dumps(rec) + '\nW profiler end\n')
+    tab = {'expert GEMM gate/up (routed)': (2, 130.0, 130.0), 'expert GEMM down (routed)': (2, 110.0, 110.0),
+           'expert GEMM gate/up (shared)': (2, 60.0, 60.0), 'expert GEMM down (shared)': (2, 55.0, 55.0)}
+    R.print_agreement(tab, str(log))
+    out = capsys.readouterr().out
+    assert 'live phase (HIP events) 242.0 us per pass, trace mean 240.0 us: 0.8% apart' in out
+    assert 'shared expert FFN: live phase 115.0 us per pass, trace mean 115.0 us: 0.0% apart' in out
