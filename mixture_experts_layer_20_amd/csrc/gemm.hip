@@ -243,6 +243,7 @@ __device__ __forceinline__ TileCoord decode_dense(int L, int groups, int ntiles,
 // when nothing is split).
 constexpr int kCUs = 256;
 constexpr int kTailMinK = 2048;
+constexpr int kMaxTailParts = 8;
 struct TailPlan {
   int F, R, P;
   int kslice;
@@ -852,10 +853,14 @@ __global__ __launch_bounds__(kThreads) void ksum_kernel(GemmArgs a) {
   *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.C) + row * a.N + c) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Tail split: tile F + blockIdx.x of the tail = act(sum over its parts, in
-// part order, of the float32 partial tiles + bias), rounded to bf16, for its
-// valid rows and columns (with the pre-activations when kept); the plan is
-// recomputed from the same device row counts.
+// Tail split: tile F + t of the tail = act(sum over its parts, in part order,
+// of the float32 partial tiles + bias), rounded to bf16, for its valid rows
+// and columns (with the pre-activations when kept); the plan is recomputed
+// from the same device row counts.  Block b sums rows
+// [(b % kTailSlices) * 32, + 32) of tail tile t = b / kTailSlices, so the
+// partial tiles stream through many compute units; each thread issues the
+// loads of every part before the first add.
+constexpr int kTailSlices = kBM / 32;
 template <int ACT>
 __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
   constexpr bool kGlu = ACT == 2;
@@ -869,7 +874,8 @@ __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
   build_tile_table(a, ntiles, pk_start, pk_rows, pk_end);
   __syncthreads();
   const TailPlan tp = tail_plan(pk_end[a.groups - 1], a.K, a.tail_parts);
-  const int t = blockIdx.x;
+  const int t = blockIdx.x / kTailSlices;
+  const int r0 = (blockIdx.x % kTailSlices) * 32;
   if (t >= tp.R) return;
   const TileCoord tc = decode_dense(tp.F + t, a.groups, ntiles, pk_end);
   const int m0 = tc.mt * kBM, n0 = tc.nt * kNOut;
@@ -884,19 +890,34 @@ __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
       w[u] = static_cast<uint32_t>(f32_to_bf16(v[2 * u])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * u + 1])) << 16);
     return make_uint4(w[0], w[1], w[2], w[3]);
   };
-  for (int i = threadIdx.x; i < kBM * (kNOut / 8); i += kThreads) {
-    const int r = i / (kNOut / 8), c = (i % (kNOut / 8)) * 8;
+  constexpr int kMaxParts = kMaxTailParts;  // launch_gemm clamps the parts to it
+  for (int i = threadIdx.x; i < 32 * (kNOut / 8); i += kThreads) {
+    const int r = r0 + i / (kNOut / 8), c = (i % (kNOut / 8)) * 8;
     if (r >= vr || c >= vc) continue;
+    const float* src0 = a.tail_part + static_cast<int64_t>(t) * tp.P * (kBM * kBW) + r * kBW + c;
+    float4 x[kMaxParts][2], y[kMaxParts][2];
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p) {
+      if (p < tp.P) {
+        const float* src = src0 + static_cast<int64_t>(p) * (kBM * kBW);
+        x[p][0] = reinterpret_cast<const float4*>(src)[0];
+        x[p][1] = reinterpret_cast<const float4*>(src)[1];
+        if (kGlu) {
+          y[p][0] = reinterpret_cast<const float4*>(src + 128)[0];
+          y[p][1] = reinterpret_cast<const float4*>(src + 128)[1];
+        }
+      }
+    }
     float v[8] = {}, u[8] = {};
-    for (int p = 0; p < tp.P; ++p) {
-      const float* src = a.tail_part + (static_cast<int64_t>(t) * tp.P + p) * (kBM * kBW) + r * kBW + c;
-      const float4 x0 = reinterpret_cast<const float4*>(src)[0], x1 = reinterpret_cast<const float4*>(src)[1];
-      v[0] += x0.x; v[1] += x0.y; v[2] += x0.z; v[3] += x0.w;
-      v[4] += x1.x; v[5] += x1.y; v[6] += x1.z; v[7] += x1.w;
-      if (kGlu) {
-        const float4 y0 = reinterpret_cast<const float4*>(src + 128)[0], y1 = reinterpret_cast<const float4*>(src + 128)[1];
-        u[0] += y0.x; u[1] += y0.y; u[2] += y0.z; u[3] += y0.w;
-        u[4] += y1.x; u[5] += y1.y; u[6] += y1.z; u[7] += y1.w;
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p) {
+      if (p < tp.P) {
+        v[0] += x[p][0].x; v[1] += x[p][0].y; v[2] += x[p][0].z; v[3] += x[p][0].w;
+        v[4] += x[p][1].x; v[5] += x[p][1].y; v[6] += x[p][1].z; v[7] += x[p][1].w;
+        if (kGlu) {
+          u[0] += y[p][0].x; u[1] += y[p][0].y; u[2] += y[p][0].z; u[3] += y[p][0].w;
+          u[4] += y[p][1].x; u[5] += y[p][1].y; u[6] += y[p][1].z; u[7] += y[p][1].w;
+        }
       }
     }
     if (!kGlu && bias) {
@@ -924,6 +945,7 @@ hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
                     !(a.ksplit > 1) && a.tail_parts >= 2 && a.K / kTailMinK >= 2;
   // (a K below two minimum parts never splits: no extra blocks, no sum launch)
   if (!tail) a.tail_part = nullptr;
+  a.tail_parts = min(a.tail_parts, kMaxTailParts);
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
   if (dtype == MOE_BF16) {
     const int nout = a.act == 2 ? kBW / 2 : kBW;
@@ -942,9 +964,10 @@ hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
       default: launch_bf16<3>(a, grid, s); break;
     }
     if (tail) {
-      if (a.act == 0) tail_sum_kernel<0><<<kCUs / 2, kThreads, 0, s>>>(a);
-      else if (a.act == 1) tail_sum_kernel<1><<<kCUs / 2, kThreads, 0, s>>>(a);
-      else tail_sum_kernel<2><<<kCUs / 2, kThreads, 0, s>>>(a);
+      const unsigned tgrid = kCUs / 2 * kTailSlices;  // tail_plan keeps R <= kCUs / 2
+      if (a.act == 0) tail_sum_kernel<0><<<tgrid, kThreads, 0, s>>>(a);
+      else if (a.act == 1) tail_sum_kernel<1><<<tgrid, kThreads, 0, s>>>(a);
+      else tail_sum_kernel<2><<<tgrid, kThreads, 0, s>>>(a);
     }
     if (split) {
       const int64_t items = static_cast<int64_t>(a.groups) * a.rows_per_group * (a.N / 8);
