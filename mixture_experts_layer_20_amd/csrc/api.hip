@@ -500,11 +500,7 @@ struct BwdWorkspace {
   bf16_t* dH;
   bf16_t* dact;
   bf16_t* dA;
-  bf16_t* woT;
   bf16_t* wiT;
-  bf16_t* dYeT;
-  bf16_t* HT;
-  bf16_t* dactT;
   bf16_t* AT;
   bf16_t* xT;
   bf16_t* planes;
@@ -514,11 +510,6 @@ struct BwdWorkspace {
   bf16_t* dHs;
   bf16_t* dUs;
   bf16_t* dAs;
-  bf16_t* wsoT;
-  bf16_t* wsiT;
-  bf16_t* dyT;
-  bf16_t* HsT;
-  bf16_t* dUsT;
   int32_t* pstart;
   int32_t* kstart;
   float* tailpart;
@@ -569,11 +560,8 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   // the transposed expert operands of the weight gradients, packed along k:
   // expert e's max(8, round8(rows_e)) columns start at kstart[e]
   b.Kw = round8(expert_rows_bound(c, C)) + 8 * E;
-  b.woT = static_cast<bf16_t*>(take(h2 * E * F * d));
-  b.wiT = static_cast<bf16_t*>(take(h2 * E * d * ga * F));
-  b.dYeT = static_cast<bf16_t*>(take(h2 * d * b.Kw));
-  b.HT = static_cast<bf16_t*>(take(h2 * F * b.Kw));
-  b.dactT = static_cast<bf16_t*>(take(h2 * ga * F * b.Kw));
+  // (SwiGLU with F not a multiple of 64: the input-gradient weights transposed)
+  if (ga == 2 && F % 64 != 0) b.wiT = static_cast<bf16_t*>(take(h2 * E * d * ga * F));
   b.AT = static_cast<bf16_t*>(take(h2 * d * b.Kw));
   b.xT = static_cast<bf16_t*>(take(h2 * d * Tp));
   b.planes = static_cast<bf16_t*>(take(h2 * 4 * E * Tp));
@@ -584,11 +572,6 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
     b.dHs = static_cast<bf16_t*>(take(h2 * T * Fs));
     b.dUs = static_cast<bf16_t*>(take(h2 * T * Fs));
     b.dAs = static_cast<bf16_t*>(take(h2 * T * d));
-    b.wsoT = static_cast<bf16_t*>(take(h2 * Fs * d));
-    b.wsiT = static_cast<bf16_t*>(take(h2 * d * Fs));
-    b.dyT = static_cast<bf16_t*>(take(h2 * d * Tp));
-    b.HsT = static_cast<bf16_t*>(take(h2 * Fs * Tp));
-    b.dUsT = static_cast<bf16_t*>(take(h2 * Fs * Tp));
   }
   b.bytes = off;
   return b;
@@ -631,6 +614,40 @@ moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, con
   g.K = K;
   g.act = 0;
   g.kvar = kvar;
+  g.koff = koff;
+  g.packed = packed;
+  g.total_rows = packed ? rpg : 0;
+  return hip_status(launch_gemm(g, MOE_BF16, s), what);
+}
+
+// C[g] = A[g] B[g]^T on the bf16 grouped GEMM with k-major operands (kmaj
+// bit 0: A is [K, M] per group, row length lda; bit 1: B is [K, N], row
+// length ldb, or B0 for k < b_split and B1 from there), read through the LDS
+// transpose loads instead of transposed copies.  A K-contiguous operand
+// takes its usual strides (0: K).
+moe_status kgemm(const char* what, int kmaj, const void* A, int64_t lda, int64_t a_gs, const void* B0,
+                 const void* B1, int64_t b_split, int64_t ldb, int64_t b_gs, void* Cout, const int32_t* rows,
+                 int64_t rpg, int groups, int N, int K, hipStream_t s, const int32_t* kvar = nullptr,
+                 const int32_t* kstart = nullptr, bool packed = false, const int32_t* koff = nullptr) {
+  GemmArgs g{};
+  g.kmaj = kmaj;
+  g.A = A;
+  g.lda = lda;
+  g.a_gs = a_gs;
+  g.B0 = B0;
+  g.B1 = B1;
+  g.b_split = b_split;
+  g.ldb = ldb;
+  g.b_gs = b_gs;
+  g.C = Cout;
+  g.rows = rows;
+  g.rows_per_group = rpg;
+  g.groups = groups;
+  g.N = N;
+  g.K = K;
+  g.act = 0;
+  g.kvar = kvar;
+  g.kstart = kstart;
   g.koff = koff;
   g.packed = packed;
   g.total_rows = packed ? rpg : 0;
@@ -1390,10 +1407,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
                                   static_cast<int>(F), b.dH, dl, b.U, glu ? b.U2 : nullptr, b.tailpart);
       MOE_TRY(hip_status(launch_gemm(g1, MOE_BF16, s), "recompute pre-activations"));
     }
-    // dH = dYe W_out: W_out [E, d, F] -> [E, F, d]
-    MOE_TRY(transpose("w_out transpose", static_cast<const bf16_t*>(wt->w_out), b.woT, E, d, F, d, d * F, F, F * d, d,
-                      nullptr, nullptr, 0, s));
-    MOE_TRY(rgemm("expert hidden gradient", b.dYe, nullptr, 0, b.woT, nullptr, b.dH, static_cast<int>(F), c.d));
+    // dH = dYe W_out, W_out [E, d, F] read k-major (k = d)
+    MOE_TRY(kgemm("expert hidden gradient", 2, b.dYe, 0, 0, wt->w_out, nullptr, 0, F, d * F, b.dH, rows, rpg, E,
+                  static_cast<int>(F), c.d, s, nullptr, nullptr, dl));
     ActBwdArgs ab{};
     ab.dH = b.dH;
     ab.U = c.save_preact ? static_cast<const bf16_t*>(w.pre0) : b.U;
@@ -1404,48 +1420,46 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     ab.groups = dl ? 1 : E;
     ab.F = static_cast<int>(F);
     MOE_TRY(hip_status(launch_act_bwd(ab, c.act, s), "activation backward"));
-    // dA = dact W_in (SwiGLU: [dGp | dUp] [W_gate; W_up]): W -> [E, d, ga*F]
-    if (glu) {
+    // dA = dact W_in (SwiGLU: [dGp | dUp] [W_gate; W_up]), the weights read
+    // k-major (k = F; SwiGLU: the gate matrix for k < F, the up matrix from
+    // there, which needs F to be a multiple of the 64-k stage; otherwise they
+    // are transposed into [E, d, 2F] first)
+    if (!glu) {
+      MOE_TRY(kgemm("expert input gradient", 2, b.dact, 0, 0, W_in, nullptr, 0, d, F * d, b.dA, rows, rpg, E, c.d,
+                    static_cast<int>(F), s, nullptr, nullptr, dl));
+    } else if (F % 64 == 0) {
+      MOE_TRY(kgemm("expert input gradient", 2, b.dact, 0, 0, wt->w_gate, W_in, F, d, F * d, b.dA, rows, rpg, E,
+                    c.d, static_cast<int>(2 * F), s, nullptr, nullptr, dl));
+    } else {
       MOE_TRY(transpose("w_gate transpose", static_cast<const bf16_t*>(wt->w_gate), b.wiT, E, F, d, F, F * d, d,
                         d * 2 * F, 2 * F, nullptr, nullptr, 0, s));
       MOE_TRY(transpose("w_up transpose", W_in, b.wiT + F, E, F, d, F, F * d, d, d * 2 * F, 2 * F, nullptr, nullptr, 0,
                         s));
-    } else {
-      MOE_TRY(transpose("w_in transpose", W_in, b.wiT, E, F, d, F, F * d, d, d * F, F, nullptr, nullptr, 0, s));
+      MOE_TRY(rgemm("expert input gradient", b.dact, nullptr, 0, b.wiT, nullptr, b.dA, c.d, static_cast<int>(2 * F)));
     }
-    MOE_TRY(rgemm("expert input gradient", b.dact, nullptr, 0, b.wiT, nullptr, b.dA, c.d, static_cast<int>(ga * F)));
-    // dW_out = dYe^T H, dW_in = dact^T A: contraction over each expert's rows
-    // (its own extent, kvar).  The transposed copies are per-expert blocks
-    // packed one after another: expert e's block is [cols, n_e], n_e =
-    // max(8, round8(rows_e)) (zero past rows_e), starting kstart[e]*cols
-    // elements in; dropless rows are read from each expert's packed start
-    // (and x through row_token from there)
+    // dW_out = dYe^T H and dW_in = dact^T A: contractions over each expert's
+    // own rows (kvar).  dYe, H and dact are read k-major from the expert
+    // buffers (dropless: from each expert's packed start); the token rows,
+    // gathered through row_token, are transposed into per-expert blocks
+    // packed one after another: expert e's block is [d, n_e], n_e = max(8,
+    // round8(rows_e)) (zero past rows_e), kstart[e]*d elements in
     MOE_TRY(hip_status(launch_group_starts(rows, b.kstart, E, 1, s), "packed columns"));
     if (dl) MOE_TRY(hip_status(launch_group_starts(rows, b.pstart, E, 0, s), "packed rows"));
     const int32_t* gst = dl ? b.pstart : nullptr;
     const int64_t Kw = b.Kw;
     const int64_t rmax = dl ? T : C;                   // rows of one expert at most
-    MOE_TRY(transpose("dYe transpose", b.dYe, b.dYeT, E, rmax, d, round8(rmax), C * d, d, 0, Kw, rows, nullptr, 0, s,
-                      b.kstart, gst));
-    MOE_TRY(transpose("H transpose", static_cast<const bf16_t*>(w.h), b.HT, E, rmax, F, round8(rmax), C * F, F, 0, Kw,
-                      rows, nullptr, 0, s, b.kstart, gst));
-    MOE_TRY(bgemm("w_out gradient", b.dYeT, Kw, 0, nullptr, 0, b.HT, Kw, 0, nullptr, gr->dw_out, nullptr, d, E,
-                  static_cast<int>(F), static_cast<int>(Kw), s, rows, false, b.kstart));
-    // (SwiGLU: the gate and up halves of the activation gradient as two block
-    // sets, the up set F*Kw elements in)
-    for (int h = 0; h < ga; ++h)
-      MOE_TRY(transpose("activation-gradient transpose", b.dact + h * F, b.dactT + h * F * Kw, E, rmax, F,
-                        round8(rmax), C * ga * F, ga * F, 0, Kw, rows, nullptr, 0, s, b.kstart, gst));
+    const int Kmax = static_cast<int>(std::max<int64_t>(8, round8(rmax)));
+    MOE_TRY(kgemm("w_out gradient", 3, b.dYe, d, dl ? 0 : C * d, w.h, nullptr, 0, F, dl ? 0 : C * F, gr->dw_out,
+                  nullptr, d, E, static_cast<int>(F), Kmax, s, rows, gst));
     MOE_TRY(transpose("token rows transpose", static_cast<const bf16_t*>(x), b.AT, E, rmax, d, round8(rmax), 0, d, 0,
                       Kw, rows, w.row_token, C, s, b.kstart, gst));
-    if (glu) {
-      MOE_TRY(bgemm("w_gate gradient", b.dactT, Kw, 0, nullptr, 0, b.AT, Kw, 0, nullptr, gr->dw_gate, nullptr, F, E,
-                    c.d, static_cast<int>(Kw), s, rows, false, b.kstart));
-      MOE_TRY(bgemm("w_up gradient", b.dactT + F * Kw, Kw, 0, nullptr, 0, b.AT, Kw, 0, nullptr, gr->dw_in, nullptr,
-                    F, E, c.d, static_cast<int>(Kw), s, rows, false, b.kstart));
-    } else {
-      MOE_TRY(bgemm("w_in gradient", b.dactT, Kw, 0, nullptr, 0, b.AT, Kw, 0, nullptr, gr->dw_in, nullptr, F, E, c.d,
-                    static_cast<int>(Kw), s, rows, false, b.kstart));
+    // (SwiGLU: the gate half of the activation gradient, then the up half, F
+    // columns in)
+    for (int h = 0; h < ga; ++h) {
+      void* dw = glu && h == 0 ? gr->dw_gate : gr->dw_in;
+      MOE_TRY(kgemm(glu ? (h == 0 ? "w_gate gradient" : "w_up gradient") : "w_in gradient", 1, b.dact + h * F,
+                    ga * F, dl ? 0 : C * ga * F, b.AT, nullptr, 0, 0, 0, dw, nullptr, F, E, c.d,
+                    static_cast<int>(Kw), s, rows, gst, false, b.kstart));
     }
     const int32_t* starts = dl ? b.pstart : nullptr;
     if (gr->db_out)
@@ -1467,9 +1481,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     if (!c.save_preact)
       MOE_TRY(bgemm("recompute shared pre-activation", x, 0, 0, nullptr, 0, wt->ws_in, 0, 0, wt->bs_in, b.Us, nullptr,
                     T, 1, static_cast<int>(Fs), c.d, s));
-    MOE_TRY(transpose("ws_out transpose", static_cast<const bf16_t*>(wt->ws_out), b.wsoT, 1, d, Fs, d, 0, Fs, 0, d,
-                      nullptr, nullptr, 0, s));
-    MOE_TRY(bgemm("shared hidden gradient", dy, 0, 0, nullptr, 0, b.wsoT, 0, 0, nullptr, b.dHs, nullptr, T, 1,
+    // the shared weights and the activations read k-major: no transposed copies
+    MOE_TRY(kgemm("shared hidden gradient", 2, dy, 0, 0, wt->ws_out, nullptr, 0, Fs, 0, b.dHs, nullptr, T, 1,
                   static_cast<int>(Fs), c.d, s));
     ActBwdArgs ab{};
     ab.dH = b.dHs;
@@ -1479,20 +1492,12 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     ab.groups = 1;
     ab.F = static_cast<int>(Fs);
     MOE_TRY(hip_status(launch_act_bwd(ab, MOE_GELU, s), "shared activation backward"));
-    MOE_TRY(transpose("ws_in transpose", static_cast<const bf16_t*>(wt->ws_in), b.wsiT, 1, Fs, d, Fs, 0, d, 0, Fs,
-                      nullptr, nullptr, 0, s));
-    MOE_TRY(bgemm("shared input gradient", b.dUs, 0, 0, nullptr, 0, b.wsiT, 0, 0, nullptr, b.dAs, nullptr, T, 1, c.d,
+    MOE_TRY(kgemm("shared input gradient", 2, b.dUs, 0, 0, wt->ws_in, nullptr, 0, d, 0, b.dAs, nullptr, T, 1, c.d,
                   static_cast<int>(Fs), s));
-    MOE_TRY(transpose("dy transpose", static_cast<const bf16_t*>(dy), b.dyT, 1, T, d, Tp, 0, d, 0, Tp, nullptr, nullptr,
-                      0, s));
-    MOE_TRY(transpose("shared H transpose", static_cast<const bf16_t*>(w.hs), b.HsT, 1, T, Fs, Tp, 0, Fs, 0, Tp,
-                      nullptr, nullptr, 0, s));
-    MOE_TRY(bgemm("ws_out gradient", b.dyT, 0, 0, nullptr, 0, b.HsT, 0, 0, nullptr, gr->dws_out, nullptr, d, 1,
-                  static_cast<int>(Fs), static_cast<int>(Tp), s));
-    MOE_TRY(transpose("shared activation-gradient transpose", b.dUs, b.dUsT, 1, T, Fs, Tp, 0, Fs, 0, Tp, nullptr,
-                      nullptr, 0, s));
-    MOE_TRY(bgemm("ws_in gradient", b.dUsT, 0, 0, nullptr, 0, b.xT, 0, 0, nullptr, gr->dws_in, nullptr, Fs, 1, c.d,
-                  static_cast<int>(Tp), s));
+    MOE_TRY(kgemm("ws_out gradient", 3, dy, d, 0, w.hs, nullptr, 0, Fs, 0, gr->dws_out, nullptr, d, 1,
+                  static_cast<int>(Fs), static_cast<int>(T), s));
+    MOE_TRY(kgemm("ws_in gradient", 3, b.dUs, Fs, 0, x, nullptr, 0, d, 0, gr->dws_in, nullptr, Fs, 1, c.d,
+                  static_cast<int>(T), s));
     if (gr->dbs_in) MOE_TRY(hip_status(launch_colsum(b.dUs, gr->dbs_in, nullptr, 1, T, Fs, 0, s), "bs_in gradient"));
     if (gr->dbs_out)
       MOE_TRY(hip_status(launch_colsum(static_cast<const bf16_t*>(dy), gr->dbs_out, nullptr, 1, T, d, 0, s),

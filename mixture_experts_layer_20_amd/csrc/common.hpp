@@ -185,6 +185,20 @@ struct GemmArgs {
   // [N, K_g] block at B0 + koff[g]*N, both with row stride K_g (its kvar
   // extent, rounded up to 8, at least 8) | null
   const int32_t* koff;
+  // bf16 path, ACT 0, not packed; no gather, ksplit, tail split or koff:
+  // operands stored k-major, as [K, rows] matrices with their rows
+  // contiguous, which the kernel reads through the LDS transpose loads
+  // instead of a transposed copy.  kmaj bit 0: element (m, k) of group g's A
+  // is A[off_g + k * lda + m]; bit 1: element (n, k) of its B is
+  // B0[off_g + k * ldb + n], or with B1, for k >= b_split, B1[off_g +
+  // (k - b_split) * ldb + n] (two matrices stacked along k; b_split a
+  // multiple of 64).  off_g = kstart[g] * ld when kstart is given (packed
+  // rows), else g * a_gs (A) or g * b_gs (B).  With kvar the k-major
+  // operands are read up to kvar[g] exactly (zeros past it, whatever the
+  // memory holds).  0: both operands K-contiguous.
+  int kmaj;
+  int64_t b_split;
+  const int32_t* kstart;
 };
 // bytes of the tail-split workspace (GemmArgs.tail_part)
 constexpr size_t kTailPartBytes = size_t{256} * 256 * 256 * sizeof(float);

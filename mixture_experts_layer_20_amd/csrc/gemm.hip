@@ -270,8 +270,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int ACT, int W>
+template <int ACT, int W, int KM = 0>
 __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
+  static_assert(KM == 0 || ACT == 0, "k-major operands: bias-only GEMMs");
+  constexpr bool kAkm = (KM & 1) != 0, kBkm = (KM & 2) != 0;
   using G = Geo<W>;
   constexpr int kWaves = G::kWaves, kHalf = G::kHalf, kSRows = G::kSRows, kLoadsPerWave = G::kLoadsPerWave;
   constexpr int kXR = G::kXR, kXB = G::kXB, kPairs = G::kPairs, kFrags = G::kFrags;
@@ -357,17 +359,27 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
                 : ACT == 0 && a.ksplit > 1 ? static_cast<int>(min<int64_t>(a.kslice, a.K - k0))
                 : a.kvar ? max(8, min(a.K, (max(a.kvar[tc.g], 0) + 7) / 8 * 8))
                          : a.K;
-  // row strides (per-group packed blocks: the group's own k extent)
-  const int64_t lda = a.koff ? K : a.lda ? a.lda : a.K, ldb = a.koff ? K : a.ldb ? a.ldb : a.K;
-  const bf16_t* A = static_cast<const bf16_t*>(a.A) + k0 +
-                    (a.koff ? static_cast<int64_t>(a.koff[tc.g]) * a.rows_per_group
-                     : gathered ? 0
-                     : a.packed ? row_base * lda
-                                : static_cast<int64_t>(tc.g) * (a.a_gs ? a.a_gs : a.rows_per_group * lda));
-  const int64_t bg = (a.koff ? static_cast<int64_t>(a.koff[tc.g]) * N
-                             : static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb)) + k0;
+  // row strides (per-group packed blocks: the group's own k extent; a
+  // k-major operand: the length of its k rows)
+  const int64_t lda = kAkm ? a.lda : a.koff ? K : a.lda ? a.lda : a.K;
+  const int64_t ldb = kBkm ? a.ldb : a.koff ? K : a.ldb ? a.ldb : a.K;
+  // k rows of a k-major operand holding data (zeros from there)
+  const int kdata = KM && a.kvar ? min(K, max(a.kvar[tc.g], 0)) : K;
+  const bf16_t* A = static_cast<const bf16_t*>(a.A) +
+                    (kAkm ? (a.kstart ? static_cast<int64_t>(a.kstart[tc.g]) * lda
+                                      : static_cast<int64_t>(tc.g) * a.a_gs)
+                     : k0 + (a.koff ? static_cast<int64_t>(a.koff[tc.g]) * a.rows_per_group
+                             : gathered ? 0
+                             : a.packed ? row_base * lda
+                                        : static_cast<int64_t>(tc.g) * (a.a_gs ? a.a_gs : a.rows_per_group * lda)));
+  const int64_t bg = kBkm ? (a.kstart ? static_cast<int64_t>(a.kstart[tc.g]) * ldb
+                                      : static_cast<int64_t>(tc.g) * a.b_gs)
+                          : (a.koff ? static_cast<int64_t>(a.koff[tc.g]) * N
+                                    : static_cast<int64_t>(tc.g) * (a.b_gs ? a.b_gs : N * ldb)) + k0;
   const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + bg;
-  const bf16_t* B1 = kGlu ? static_cast<const bf16_t*>(a.B1) + bg : B0;
+  const bf16_t* B1 = kGlu || (kBkm && a.B1) ? static_cast<const bf16_t*>(a.B1) + bg : B0;
+  // k-major B stacked along k: stages at or past k row b_split read B1
+  const int b_split = kBkm && a.B1 ? static_cast<int>(a.b_split) : 1 << 30;
 
   const int tid = threadIdx.x;
   // the wave index is uniform: say so, so that descriptors and LDS bases live
@@ -384,33 +396,64 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // operand's end (ragged expert rows, columns past N) and k past K read as
   // zero through the buffer bounds.
   const bool stage_x = wave < kHalf;
+  // this wave's operand is k-major (bit 0: the token-row operand A, bit 1: B)
+  const bool km = stage_x ? kAkm : kBkm;
   const int lr = lane / kChunks, pc = lane % kChunks;
   const int row0 = (wave % kHalf) * kSRows;        // first tile row this wave stages
-  __amdgpu_buffer_rsrc_t rsrc;
+  __amdgpu_buffer_rsrc_t rsrc, rsrc1;
   // voff: offset of each load's 16 bytes in stage 0; past: bit j set when
   // load j's k-chunk lies at or past K in the last stage (then bit 31 of its
   // offset is set, which sends it past every operand: it reads zero)
   uint32_t voff[kLoadsPerWave], past = 0;
   const int nk = (K + kBK - 1) / kBK;
   const int k_last = K - (nk - 1) * kBK;          // valid k in the last stage
+  // k-major: k rows with data in the last stage
+  const int kd_last = kdata - (nk - 1) * kBK;
   {
     const bf16_t* base = stage_x ? A : ((kGlu && row0 < 128) ? B1 : B0);
-    // the operand's extent from its base: the last row ends K past its start
-    const int64_t nbytes = stage_x ? ((gathered ? a.a_rows : rows_g) - 1) * lda * 2 + K * 2
-                                   : (static_cast<int64_t>(N) - 1) * ldb * 2 + K * 2;
     const int64_t ld = stage_x ? lda : ldb;
+    // rows of the operand (k-major: the contiguous dimension)
+    const int64_t ext = stage_x ? (gathered ? a.a_rows : rows_g) : static_cast<int64_t>(N);
+    // the operand's extent from its base: the last row ends K past its start
+    // (k-major: the last k row with data ends ext past its start; a second
+    // matrix stacked along k holds the rows from b_split on)
+    const int64_t kd0 = km ? min(kdata, b_split) : 0, kd1 = km ? kdata - kd0 : 0;
+    const int64_t nbytes = km ? (kd0 > 0 ? ((kd0 - 1) * ld + ext) * 2 : 0) : (ext - 1) * ld * 2 + K * 2;
+    const int64_t nbytes1 = kd1 > 0 ? ((kd1 - 1) * ld + ext) * 2 : 0;
     // the descriptor must live in scalar registers: pin its fields to lane 0
     // (they are uniform; without this the compiler may not prove it and wrap
     // every load in a loop over lanes)
-    const uint64_t bu = reinterpret_cast<uint64_t>(base);
-    const uint32_t blo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu));
-    const uint32_t bhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu >> 32));
-    const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(nbytes));
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>((static_cast<uint64_t>(bhi) << 32) | blo), (short)0, nrec, kRsrcWord3);
+    auto make = [&](const bf16_t* b, int64_t n) {
+      const uint64_t bu = reinterpret_cast<uint64_t>(b);
+      const uint32_t blo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu));
+      const uint32_t bhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bu >> 32));
+      const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(n));
+      return __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>((static_cast<uint64_t>(bhi) << 32) | blo), (short)0, nrec, kRsrcWord3);
+    };
+    rsrc = make(base, nbytes);
+    rsrc1 = kBkm && !stage_x ? make(B1, nbytes1) : rsrc;
     // first operand row of this wave's block 0 (token rows: m0 + row0;
     // weight rows: n0 + row0, or for SwiGLU n0 + row0 mod 128 of its matrix)
     const int orow0 = stage_x ? m0 + row0 : (kGlu ? n0 + (row0 & 127) : n0 + row0);
+    if (KM && km) {
+      // k-major: the wave stages k rows [kw0, kw0 + 16) of each stage (16 x
+      // 512 bytes, the same LDS bytes as its 64 tile rows otherwise).  Lane i
+      // of instruction j fills k row kw0 + 2j + i/32, physical 16-byte chunk
+      // i%32, which holds logical chunk (i%32) ^ ((k row & 3) << 2): tile
+      // rows 8c .. 8c+7 of that k row.  Rows past the operand's end and k
+      // rows past the data (last stage) read zero.
+      const int kw0 = (wave % kHalf) * (kSRows / 4);
+      const int rb = stage_x ? m0 : n0;
+#pragma unroll
+      for (int j = 0; j < kLoadsPerWave; ++j) {
+        const int kk = kw0 + 2 * j + (lane >> 5);
+        const int c = (lane & 31) ^ ((kk & 3) << 2);
+        const int64_t orow = rb + c * 8;
+        voff[j] = orow < ext ? static_cast<uint32_t>((kk * ld + orow) * 2) : kOutOfRange;
+        past |= (kk < kd_last ? 0u : 1u) << j;
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < kLoadsPerWave; ++j) {
       const int trow = row0 + j * kRowsPerLoad + lr;             // tile row (sets the swizzle)
@@ -425,7 +468,22 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
       voff[j] = orow < 0 ? kOutOfRange : static_cast<uint32_t>((orow * ld + c * 8) * 2);
       past |= (c * 8 < k_last ? 0u : 1u) << j;
     }
+    }
   }
+  // bytes between consecutive stages of this wave's operand (the k offset
+  // rides in the scalar offset), and the descriptor and scalar offset of
+  // stage kc (a k-major B stacked along k switches matrix at b_split)
+  const int64_t ld_w = stage_x ? lda : ldb;
+  const int kstep = KM && km ? static_cast<int>(kBK * ld_w * 2) : kBK * 2;
+  auto stage_src = [&](int kc, __amdgpu_buffer_rsrc_t& rs, int& so) __attribute__((always_inline)) {
+    if (kBkm && !stage_x && kc * kBK >= b_split) {
+      rs = rsrc1;
+      so = (kc - b_split / kBK) * kstep;
+    } else {
+      rs = rsrc;
+      so = kc * kstep;
+    }
+  };
   // the token rows' ring of kNX stage buffers, then the weight rows' ring of kNW
   const int nring = stage_x ? kNX : kNW;
   uint8_t* ring = lds + (stage_x ? 0 : kNX * kXBytes) + row0 * kRowBytes;
@@ -448,9 +506,11 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     const int kc = min(st, nk - 1);
     const uint32_t pm = kc == nk - 1 ? past : 0u;
     uint8_t* dst = ring + (st % nring) * kXBytes;
-    const int soff = kc * kBK * 2;
+    __amdgpu_buffer_rsrc_t rs;
+    int soff;
+    stage_src(kc, rs, soff);
     for (int j = j_begin; j < j_end; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 1024), 16,
                                                voff[j] | (((pm >> j) & 1u) << 31), soff, 0, 0);
   };
 
@@ -480,11 +540,69 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   bf16x8_t wf[2][4], xf[2][kXB];
   auto xbuf = [&](int st) -> const uint8_t* { return lds + (st % kNX) * kXBytes; };
   auto wbuf = [&](int st) -> const uint8_t* { return lds + kNX * kXBytes + (st % kNW) * kWBytes; };
+  // k-major stage: lane l of a 16-lane group g supplies the address of 4
+  // consecutive tile rows of one k row, and the transpose load hands each
+  // lane 4 consecutive k of its own row: with k row 8c + 4h + kmo and rows
+  // rb + rco .. +3, lane l gets row rb + l%32, k 8c + 4h .. +3 (h = 0, 1:
+  // the fragment's 8 k).  The rows' 16-byte chunk is swizzled by k row & 3
+  // (= kmo) as the stage was written, so the 32 lanes served together hit
+  // four distinct 64-byte bank windows.
+  const int kmo = (lane & 15) >> 2, rco = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // (The two reads wait for themselves in the same asm block: through the
+  // builtin the compiler cannot tell them from reads of the stage the
+  // direct-to-LDS loads are filling and waits for every load in flight first.)
+  auto kread = [&](const uint8_t* buf, int rb, int c) __attribute__((always_inline)) {
+    const int rowc = rb + rco;
+    const int off = (8 * c + kmo) * (2 * kBM) + ((((rowc >> 3) ^ (kmo << 2))) << 4) + (rowc & 7) * 2;
+    const uint32_t addr =
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(buf + off)));
+    uint2 lo, hi;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo), "=&v"(hi)
+        : "v"(addr)
+        : "memory");
+    return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+  };
+  // all four weight fragments of a k-major B at once (eight transpose reads,
+  // one wait), written to wf[slot]
+  auto kread_w4 = [&](const uint8_t* buf, int c, int slot) __attribute__((always_inline)) {
+    uint32_t ad[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int rowc = wrow[f] - (lane & 31) + rco;
+      const int off = (8 * c + kmo) * (2 * kBM) + ((((rowc >> 3) ^ (kmo << 2))) << 4) + (rowc & 7) * 2;
+      ad[f] = static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(buf + off)));
+    }
+    uint2 r[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      wf[slot][f] = __builtin_bit_cast(bf16x8_t, make_uint4(r[2 * f].x, r[2 * f].y, r[2 * f + 1].x, r[2 * f + 1].y));
+  };
   auto read_frag = [&](const uint8_t* xs, const uint8_t* ws, int c, int slot, int f) {
-    if (f < 4)
-      wf[slot][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ws + swz(wrow[f], c)));
-    else
-      xf[slot][f - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xs + swz(xrow[f - 4], c)));
+    if (f < 4) {
+      if (kBkm) wf[slot][f] = kread(ws, wrow[f] - (lane & 31), c);
+      else wf[slot][f] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(ws + swz(wrow[f], c)));
+    } else {
+      if (kAkm) xf[slot][f - 4] = kread(xs, xrow[f - 4] - (lane & 31), c);
+      else xf[slot][f - 4] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(xs + swz(xrow[f - 4], c)));
+    }
   };
 
   f32x16_t acc[4][kXB];
@@ -695,7 +813,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
         const uint32_t pm = kc == nk - 1 ? past : 0u;
         // buffer ist % nring: kt % nring at position 0, (kt - 1) % nring after
         uint8_t* dst = ring + (next_stage ? rk : rk_prev) * kXBytes;
-        const int soff = kc * kBK * 2;
+        __amdgpu_buffer_rsrc_t rs;
+        int soff;
+        stage_src(kc, rs, soff);
         const int rstage = next_stage ? kt + 1 : kt;
         const uint8_t* rx = xbuf(rstage);
         const uint8_t* rw = wbuf(rstage);
@@ -708,15 +828,18 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
             acc[i][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb], acc[i][jb], 0, 0, 0);
           if (!kPartial || (jb + 1 < xbv && wvalid))
             acc[i][jb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb + 1], acc[i][jb + 1], 0, 0, 0);
+          // (a k-major B: its four fragments at once, in the first group)
+          if (kBkm && q == 0) kread_w4(rw, rc, cur ^ 1);
 #pragma unroll
           for (int r = 0; r < kFrags; ++r)
-            if (kPlanOf<W>.group[r] == q) read_frag(rx, rw, rc, cur ^ 1, kPlanOf<W>.order[r]);
+            if (kPlanOf<W>.group[r] == q && !(kBkm && kPlanOf<W>.order[r] < 4))
+              read_frag(rx, rw, rc, cur ^ 1, kPlanOf<W>.order[r]);
           // this step's loads, spread over the groups
 #pragma unroll
           for (int u = 0; u < kLoadsPerWave; ++u) {
             if (u < nload && (u * kPairs) / nload == q) {
               const int j = j0 + u;
-              __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(dst + j * 1024), 16,
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 1024), 16,
                                                        voff[j] | (((pm >> j) & 1u) << 31), soff, 0, 0);
             }
           }
@@ -735,6 +858,11 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
 template <int ACT>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_w8(GemmArgs a) {
   gemm_bf16_body<ACT, 8>(a);
+}
+// The same, bias only, with k-major operands (GemmArgs.kmaj = KM).
+template <int KM>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_km(GemmArgs a) {
+  gemm_bf16_body<0, 8, KM>(a);
 }
 
 // ------------------------------------------------------------------ float32
@@ -820,7 +948,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs a) {
 
 template <int ACT>
 void launch_bf16(const GemmArgs& a, unsigned grid, hipStream_t s) {
-  gemm_bf16_w8<ACT><<<grid, 512, 0, s>>>(a);
+  if (ACT == 0 && a.kmaj == 1) gemm_bf16_km<1><<<grid, 512, 0, s>>>(a);
+  else if (ACT == 0 && a.kmaj == 2) gemm_bf16_km<2><<<grid, 512, 0, s>>>(a);
+  else if (ACT == 0 && a.kmaj == 3) gemm_bf16_km<3><<<grid, 512, 0, s>>>(a);
+  else gemm_bf16_w8<ACT><<<grid, 512, 0, s>>>(a);
 }
 
 namespace {
@@ -942,11 +1073,22 @@ hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
   GemmArgs a = a_in;
   // the tail split applies to bias-only bf16 GEMMs over device row counts
   const bool tail = dtype == MOE_BF16 && a.act != 3 && a.tail_part != nullptr && a.rows != nullptr && !a.packed &&
-                    !(a.ksplit > 1) && a.tail_parts >= 2 && a.K / kTailMinK >= 2;
+                    !(a.ksplit > 1) && a.tail_parts >= 2 && a.K / kTailMinK >= 2 && !a.kmaj;
   // (a K below two minimum parts never splits: no extra blocks, no sum launch)
   if (!tail) a.tail_part = nullptr;
   a.tail_parts = min(a.tail_parts, kMaxTailParts);
   if (a.groups <= 0 || a.rows_per_group <= 0 || a.N <= 0) return hipSuccess;
+  if (a.kmaj) {
+    // k-major operands: bias-only bf16; a k-major A neither packed nor
+    // gathered; per-group blocks (koff) only for a K-contiguous B; row
+    // lengths given; a stacked B switching matrix at a stage boundary
+    if (dtype != MOE_BF16 || a.act != 0 || a.kmaj > 3 || ((a.kmaj & 1) && (a.packed || a.gather)) ||
+        a.ksplit > 1 || (a.koff && a.kmaj != 1) ||
+        ((a.kmaj & 1) && a.lda <= 0) || ((a.kmaj & 2) && a.ldb <= 0) ||
+        ((a.kmaj & 2) && a.B1 && (a.b_split <= 0 || a.b_split % kBK != 0)) || a.N % 8 != 0 ||
+        ((a.kmaj & 1) && a.rows_per_group % 8 != 0))
+      return hipErrorInvalidValue;
+  }
   if (dtype == MOE_BF16) {
     const int nout = a.act == 2 ? kBW / 2 : kBW;
     if ((a.packed || a.rows) && a.groups > kMaxPackedGroups) return hipErrorInvalidValue;

@@ -134,6 +134,10 @@ BWD_CASES = [
      dict(capacity_override=40, dropped_output='zero')),
     ('sigmoid_raw_ragged', synth.Workload('bf', T=333, d=64, E=8, k=2, d_ff=72, act='gelu', score='sigmoid',
                                           renormalize=0, cf=1.25, dtype='bf16', seed=66), {}),
+    # SwiGLU width not a multiple of the 64-k stage: the input gradient takes
+    # the transposed [W_gate; W_up] copy instead of the two k-major matrices
+    ('swiglu_width_off_stage', synth.Workload('bh', T=300, d=64, E=4, k=2, d_ff=200, act='swiglu',
+                                              score='softmax', renormalize=-1, cf=1.25, dtype='bf16', seed=69), {}),
     # more experts than 16-byte column chunks of a row (E > d/8): the input
     # gradient's router term reads dL/dz of every expert from every lane
     ('narrow_rows_many_experts', synth.Workload('bg', T=256, d=64, E=48, k=4, d_ff=64, act='gelu',
