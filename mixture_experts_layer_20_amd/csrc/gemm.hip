@@ -595,6 +595,32 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     for (int f = 0; f < 4; ++f)
       wf[slot][f] = __builtin_bit_cast(bf16x8_t, make_uint4(r[2 * f].x, r[2 * f].y, r[2 * f + 1].x, r[2 * f + 1].y));
   };
+  // both token fragments of a k-major A at once (four transpose reads, one
+  // wait), written to xf[slot]
+  auto kread_x2 = [&](const uint8_t* buf, int c, int slot) __attribute__((always_inline)) {
+    static_assert(kXB == 2, "two token fragments a step");
+    uint32_t ad[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int rowc = xrow[f] - (lane & 31) + rco;
+      const int off = (8 * c + kmo) * (2 * kBM) + ((((rowc >> 3) ^ (kmo << 2))) << 4) + (rowc & 7) * 2;
+      ad[f] = static_cast<uint32_t>(
+          reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(buf + off)));
+    }
+    uint2 r[4];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %5\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(ad[0]), "v"(ad[1])
+        : "memory");
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      xf[slot][f] = __builtin_bit_cast(bf16x8_t, make_uint4(r[2 * f].x, r[2 * f].y, r[2 * f + 1].x, r[2 * f + 1].y));
+  };
   auto read_frag = [&](const uint8_t* xs, const uint8_t* ws, int c, int slot, int f) {
     if (f < 4) {
       if (kBkm) wf[slot][f] = kread(ws, wrow[f] - (lane & 31), c);
@@ -829,10 +855,12 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
           if (!kPartial || (jb + 1 < xbv && wvalid))
             acc[i][jb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][i], xf[cur][jb + 1], acc[i][jb + 1], 0, 0, 0);
           // (a k-major B: its four fragments at once, in the first group)
+          // (and a k-major A: its two, in the last group)
           if (kBkm && q == 0) kread_w4(rw, rc, cur ^ 1);
+          if (kAkm && q == kPairs - 1) kread_x2(rx, rc, cur ^ 1);
 #pragma unroll
           for (int r = 0; r < kFrags; ++r)
-            if (kPlanOf<W>.group[r] == q && !(kBkm && kPlanOf<W>.order[r] < 4))
+            if (kPlanOf<W>.group[r] == q && !(kBkm && kPlanOf<W>.order[r] < 4) && !(kAkm && kPlanOf<W>.order[r] >= 4))
               read_frag(rx, rw, rc, cur ^ 1, kPlanOf<W>.order[r]);
           // this step's loads, spread over the groups
 #pragma unroll
