@@ -36,6 +36,7 @@ GEMM_SOURCE = os.path.join(HERE, 'csrc', 'gemm.hip')
 COPY_KERNEL_TAG = 'neg_kernel'      # torch's elementwise negation, used as the plain copy
 GEMM_UP = r'gemm_bf16_w\d<2>'       # kernel-name patterns of the two expert GEMMs
 GEMM_DOWN = r'gemm_bf16_w\d<0>'
+XCDS = 8                            # GRBM_GUI_ACTIVE is summed over the XCDs
 
 
 def gemm_code_sha256(path=GEMM_SOURCE):
@@ -231,7 +232,8 @@ def cmd_counters(a):
         t = row['duration_us']
         line = [f'dispatches {row["n"]}', f'mean duration {t:.1f} us']
         if 'GRBM_GUI_ACTIVE' in row and t > 0:
-            line.append(f'shader clock {row["GRBM_GUI_ACTIVE"] / t / 1000:.3f} GHz (GRBM_GUI_ACTIVE / duration)')
+            line.append(f'shader clock {row["GRBM_GUI_ACTIVE"] / XCDS / t / 1000:.3f} GHz '
+                        f'(GRBM_GUI_ACTIVE over the {XCDS} XCDs / duration)')
         if 'MfmaUtil' in row:
             line.append(f'MFMA busy {row["MfmaUtil"] / 100:.3f} of SIMD cycles (MfmaUtil)')
         if 'SQ_INSTS_VALU_MFMA_MOPS_BF16' in row and t > 0:
@@ -240,6 +242,9 @@ def cmd_counters(a):
         if 'TCC_HIT_sum' in row and 'TCC_MISS_sum' in row:
             h, m = row['TCC_HIT_sum'], row['TCC_MISS_sum']
             line.append(f'L2 hit rate {h / max(1.0, h + m):.3f}')
+        if 'TCP_TCC_READ_REQ_LATENCY_sum' in row and row.get('TCP_TCC_READ_REQ_sum'):
+            line.append(f'L1->L2 read latency {row["TCP_TCC_READ_REQ_LATENCY_sum"] / row["TCP_TCC_READ_REQ_sum"]:.0f} '
+                        f'cycles per request')
         for cn, v in row.items():
             if cn not in ('n', 'duration_us'):
                 line.append(f'{cn} {v:.6g}')
