@@ -231,11 +231,16 @@ MOE_API moe_status moe_dispatch_by_score(const moe_config* cfg, const void* x, c
  *   gather          [groups*rows_per_group] int32 or NULL: row m of group g
  *                   is a[gather[g*rows_per_group + m]] (e.g. the row_token
  *                   of moe_dispatch), read straight into the GEMM tiles so
- *                   no dispatched copy of x is needed; entries at or past
- *                   rows[g] are not read
- *   a_rows          rows of a when gathered (ignored otherwise)
+ *                   no dispatched copy of x is needed (this is how
+ *                   moe_forward dispatches); entries at or past rows[g] are
+ *                   not read.  NULL gives the plain form on dispatched rows.
+ *   a_rows          rows of a when gathered (ignored otherwise; bounds the
+ *                   gathered reads)
  *   act             moe_act: GELU  h = GELU(a w_in^T + b_in), out = h w_out^T + b_out
  *                            SwiGLU h = SiLU(a w_gate^T) * (a w_in^T), out = h w_out^T
+ *                   (an argument rather than cfg->act, so that one config drives
+ *                   both the routed experts, whose act is cfg->act, and the
+ *                   shared experts, which are GELU MLPs)
  *   w_in            [groups,F,d] (GELU: w_in; SwiGLU: the up projection)
  *   w_gate          [groups,F,d] SwiGLU gate projection, NULL for GELU
  *   b_in            [groups,F] or NULL;   w_out [groups,d,F];  b_out [groups,d] or NULL
@@ -344,7 +349,8 @@ typedef struct moe_weights {
   const void* b_in;           /* [E,F] or NULL                                      */
   const void* w_out;          /* [E,d,F]                                            */
   const void* b_out;          /* [E,d] or NULL                                      */
-  const void* ws_in;          /* shared experts concatenated: [n_shared*Fs, d]      */
+  /* shared experts are GELU MLPs (no gate matrix), concatenated:          */
+  const void* ws_in;          /* [n_shared*Fs, d]                                   */
   const void* bs_in;          /* [n_shared*Fs] or NULL                              */
   const void* ws_out;         /* [d, n_shared*Fs]                                   */
   const void* bs_out;         /* [d] (sum of the shared experts' output biases) or NULL */
