@@ -164,8 +164,8 @@ def main():
         vendor_yardstick(max(1, args.steps), args.yardstick_shapes or YARDSTICK_SHAPES)
         return
     if args.gpus != 1:
-        print(json.dumps({'error': 'this build runs on one GPU only: the MoE layer is measured on a '
-                                   'single MI355X; --gpus must be 1'}), flush=True)
+        print(json.dumps({'error': 'one GPU only: the MoE layer is measured on a single MI355X (the '
+                                   'multi-GPU sharding is designed, not built); --gpus must be 1'}), flush=True)
         sys.exit(2)
     import numpy as np
     import torch
