@@ -222,7 +222,7 @@ Workspace carve(const moe_config& c, int64_t C, void* base) {
     const KSplit ksp = down_ksplit(c.E, C, c.d, c.d_ff);
     if (ksp.parts > 1) w.kpart = static_cast<float*>(take(sizeof(float) * ksp.parts * c.E * C * c.d));
   }
-  if (!c.dropless && c.dtype == MOE_BF16) w.tailpart = static_cast<float*>(take(kTailPartBytes));
+  if (c.dtype == MOE_BF16) w.tailpart = static_cast<float*>(take(kTailPartBytes));
   w.h = take(ds * xrows * c.d_ff);
   w.ye = take(ds * xrows * c.d);
   w.hs = fs > 0 ? take(ds * c.T * fs) : nullptr;
@@ -312,7 +312,7 @@ GemmArgs up_args(const moe_config& c, int act, int groups, int64_t rpg, const in
   g1.pre1 = pre1;
   // a last, mostly empty round of tiles split along k (the launch decides on
   // the device, from the row counts)
-  if (tail_part && !packed && rows && c.dtype == MOE_BF16) {
+  if (tail_part && rows && c.dtype == MOE_BF16) {
     g1.tail_part = tail_part;
     g1.tail_parts = 8;
   }
@@ -364,7 +364,7 @@ moe_status ffn(const moe_config& c, int act, int groups, int64_t rpg, const int3
   }
   // a last, mostly empty round of tiles split along k (the launch decides on
   // the device, from the row counts)
-  if (tail_part && !packed && rows && g2.ksplit <= 1 && c.dtype == MOE_BF16) {
+  if (tail_part && rows && g2.ksplit <= 1 && c.dtype == MOE_BF16) {
     g2.tail_part = tail_part;
     g2.tail_parts = 8;
   }
@@ -554,7 +554,7 @@ BwdWorkspace carve_bwd(const moe_config& c, int64_t C, void* base) {
   b.dH = static_cast<bf16_t*>(take(h2 * R * F));
   b.dact = static_cast<bf16_t*>(take(h2 * R * ga * F));
   b.dA = static_cast<bf16_t*>(take(h2 * R * d));
-  if (!c.dropless) b.tailpart = static_cast<float*>(take(kTailPartBytes));
+  b.tailpart = static_cast<float*>(take(kTailPartBytes));
   if (c.dropless) b.pstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
   b.kstart = static_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
   // the transposed expert operands of the weight gradients, packed along k:
@@ -1204,7 +1204,7 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, con
     // packed rows: expert e's rows start after the counts of the lower experts
     if (c.T > 0)
       MOE_TRY(ffn(c, c.act, c.E, c.T * c.k, out->counts, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in,
-                  wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T, w.pre0, w.pre1));
+                  wt->w_out, wt->b_out, c.d_ff, w.h, w.ye, s, true, c.T, w.pre0, w.pre1, nullptr, w.tailpart));
   } else if (C > 0) {
     MOE_TRY(ffn(c, c.act, c.E, C, w.kept, x, w.row_token, c.T, wt->w_in, wt->w_gate, wt->b_in, wt->w_out,
                 wt->b_out, c.d_ff, w.h, w.ye, s, false, 0, w.pre0, w.pre1, w.kpart, w.tailpart));

@@ -173,8 +173,8 @@ struct GemmArgs {
   // (rounded up to 8, at least 8; the operands must be zero from there to the
   // rounded extent), e.g. a weight gradient over an expert's kept rows | null
   const int32_t* kvar;
-  // bf16 path, ACT 0, device row counts (rows), not packed, no ksplit: a
-  // float32 workspace of 256 partial tiles of 256 x 256, in which the tiles
+  // bf16 path, ACT 0-2, device row counts (rows; slabs or packed), no
+  // ksplit: a float32 workspace of 256 partial tiles of 256 x 256, in which the tiles
   // of a last, at most half-full round of the GPU are split along k into at
   // most tail_parts parts and then summed in part order | null (no split)
   float* tail_part;

@@ -1039,7 +1039,7 @@ __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
   const TileCoord tc = decode_dense(tp.F + t, a.groups, ntiles, pk_end);
   const int m0 = tc.mt * kBM, n0 = tc.nt * kNOut;
   const int vr = min(kBM, pk_rows[tc.g] - m0), vc = min(kNOut, N - n0);
-  const int64_t row_base = static_cast<int64_t>(tc.g) * a.rows_per_group;
+  const int64_t row_base = a.packed ? static_cast<int64_t>(pk_start[tc.g]) : static_cast<int64_t>(tc.g) * a.rows_per_group;
   const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N + n0 : nullptr;
   const int64_t obase = (row_base + m0) * N + n0;
   auto pack = [](const float (&v)[8]) {
@@ -1100,7 +1100,7 @@ __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
 hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
   GemmArgs a = a_in;
   // the tail split applies to bias-only bf16 GEMMs over device row counts
-  const bool tail = dtype == MOE_BF16 && a.act != 3 && a.tail_part != nullptr && a.rows != nullptr && !a.packed &&
+  const bool tail = dtype == MOE_BF16 && a.act != 3 && a.tail_part != nullptr && a.rows != nullptr &&
                     !(a.ksplit > 1) && a.tail_parts >= 2 && a.K / kTailMinK >= 2 && !a.kmaj;
   // (a K below two minimum parts never splits: no extra blocks, no sum launch)
   if (!tail) a.tail_part = nullptr;

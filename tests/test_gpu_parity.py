@@ -659,6 +659,24 @@ def test_forward_splits_the_last_round_of_the_down_projection(moe):
     assert (ref['counts'] >= 2304).all()        # every expert holds 9 full row tiles
 
 
+def test_forward_dropless_splits_the_last_round_of_the_down_projection(moe):
+    # dropless, packed rows: 8 experts of 2,922-3,099 rows give 98 row tiles,
+    # so the down projection (d = 2048: 8 column tiles) has 784 tiles and a
+    # last round of 16, split along k (d_ff = 4096: 2 parts); those tiles
+    # belong to the last expert, so its tokens are compared, and others
+    w = synth.Workload('tail_round_dl', T=12000, d=2048, E=8, k=2, d_ff=4096, act='gelu', score='softmax',
+                       renormalize=-1, cf=1.25, dtype='bf16', seed=41)
+    inp = synth.router_inputs(w)
+    z = O.router_logits(synth.as_f32(inp['x']), inp['w_router'], inp['logit_bias'])
+    idx = O.route(z, w.k, w.score, w.renormalize, inp['select_bias'])[0]
+    counts = np.bincount(idx.ravel(), minlength=w.E)
+    assert sum((int(c) + 255) // 256 for c in counts) * 8 % 256 == 16     # the split round
+    on7 = np.nonzero((idx == 7).any(axis=1))[0]
+    g = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([g.choice(on7, 120, replace=False), g.choice(w.T, 40, replace=False)]))
+    _compare_forward(moe, w, rows=rows, dropless=True)
+
+
 @pytest.mark.parametrize('T', [1, 63, 65, 0])
 def test_forward_ragged_and_empty(moe, T):
     w = synth.WORKLOADS['tiny_f32'].with_(T=T, name=f'tiny_T{T}')
