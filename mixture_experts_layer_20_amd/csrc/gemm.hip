@@ -152,6 +152,29 @@ struct TileCoord {
 // the 64-expert layer, the same elsewhere).
 __device__ __forceinline__ int band_rows(int ntiles) { return ntiles <= 4 ? 2 : 4; }
 
+// Tile r of a group of mt row tiles (r < mt * ntiles) -> (row tile, column
+// tile): floor(mt / band) bands (at least one), the first taking the
+// remainder rows, each walked column by column.
+__device__ __forceinline__ void band_walk(int r, int mt, int ntiles, int& rt, int& ct) {
+  const int kGM = band_rows(ntiles);
+  const int nb = max(1, mt / kGM);
+  const int base = mt / nb, extra = mt % nb;                  // the first `extra` bands are one taller
+  const int tall = extra * (base + 1) * ntiles;               // tiles in the taller bands
+  int first, gm, within;
+  if (r < tall) {
+    gm = base + 1;
+    first = (r / (gm * ntiles)) * gm;
+    within = r % (gm * ntiles);
+  } else {
+    gm = base;
+    const int r2 = r - tall;
+    first = extra * (base + 1) + (r2 / (gm * ntiles)) * gm;
+    within = r2 % (gm * ntiles);
+  }
+  rt = first + within % gm;
+  ct = within / gm;
+}
+
 // logical tile -> (group, row tile, column tile): bands of band_rows row
 // tiles, walked column by column
 __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntiles, int groups) {
@@ -160,14 +183,7 @@ __device__ __forceinline__ TileCoord decode_tile(int64_t L, int mt_max, int ntil
   c.valid = L < per_group * groups;
   if (!c.valid) { c.g = c.mt = c.nt = 0; return c; }
   c.g = static_cast<int>(L / per_group);
-  const int r = static_cast<int>(L % per_group);
-  const int kGM = band_rows(ntiles);
-  const int band = r / (kGM * ntiles);
-  const int first = band * kGM;
-  const int gm = min(kGM, mt_max - first);
-  const int within = r % (kGM * ntiles);
-  c.mt = first + within % gm;
-  c.nt = within / gm;
+  band_walk(static_cast<int>(L % per_group), mt_max, ntiles, c.mt, c.nt);
   return c;
 }
 
@@ -220,16 +236,9 @@ __device__ __forceinline__ TileCoord decode_dense(int L, int groups, int ntiles,
   for (int c = 0; c < groups; c += kWave) g += __popcll(__ballot(c + ln < groups && pk_end[c + ln] <= L));
   const int first = g ? pk_end[g - 1] : 0;
   const int mt_g = (pk_end[g] - first) / ntiles;
-  const int r = L - first;
-  const int kGM = band_rows(ntiles);
-  const int band = r / (kGM * ntiles);
-  const int mt0 = band * kGM;
-  const int gm = min(kGM, mt_g - mt0);
-  const int within = r % (kGM * ntiles);
   TileCoord tc;
   tc.g = g;
-  tc.mt = mt0 + within % gm;
-  tc.nt = within / gm;
+  band_walk(L - first, mt_g, ntiles, tc.mt, tc.nt);
   tc.valid = true;
   return tc;
 }
