@@ -1,6 +1,7 @@
 """Host tests of the rocprofv3 summary helper: the per-kernel counter
 averages, the copy-kernel calibration, and the source-hash gate that keeps
 stale traffic numbers out of the bench line."""
+import argparse
 import json
 import os
 import sqlite3
@@ -136,3 +137,35 @@ def test_agreement_reads_the_last_bench_line_of_a_mixed_log(tmp_path, capsys):
     out = capsys.readouterr().out
     assert 'live phase (HIP events) 242.0 us per pass, trace mean 240.0 us: 0.8% apart' in out
     assert 'shared expert FFN: live phase 115.0 us per pass, trace mean 115.0 us: 0.0% apart' in out
+
+
+def test_counters_per_kernel_sum_instances_and_derive_rates(tmp_path, capsys):
+    # two dispatches of one kernel, counters split over instances (summed per
+    # dispatch, then averaged over dispatches), durations from the trace
+    d = tmp_path / 'c'
+    os.makedirs(d)
+    con = sqlite3.connect(os.path.join(d, 'run_results.db'))
+    con.execute('create table counters_collection (dispatch_id int, kernel_name text, counter_name text, value real)')
+    con.execute('create table kernels (dispatch_id int, name text, start int, "end" int)')
+    k = 'void moe::(anonymous namespace)::gemm_bf16_w8<2>(moe::GemmArgs)'
+    for did, us in ((1, 1000), (2, 3000)):
+        con.execute('insert into kernels values (?,?,?,?)', (did, k, 0, us * 1000))
+        for _ in range(8):                             # 8 XCD instances
+            con.execute('insert into counters_collection values (?,?,?,?)', (did, k, 'GRBM_GUI_ACTIVE', 200.0 * us))
+        con.execute('insert into counters_collection values (?,?,?,?)', (did, k, 'TCC_HIT_sum', 75.0))
+        con.execute('insert into counters_collection values (?,?,?,?)', (did, k, 'TCC_MISS_sum', 25.0))
+        con.execute('insert into counters_collection values (?,?,?,?)', (did, k, 'SQ_INSTS_VALU_MFMA_MOPS_BF16', 1e9))
+        con.execute('insert into counters_collection values (?,?,?,?)', (did, k, 'TCP_TCC_READ_REQ_LATENCY_sum', 3e5))
+        con.execute('insert into counters_collection values (?,?,?,?)', (did, k, 'TCP_TCC_READ_REQ_sum', 1e3))
+    con.commit()
+    con.close()
+    tab = R.counters_per_kernel(str(d))
+    row = tab[k]
+    assert row['n'] == 2 and row['duration_us'] == pytest.approx(2000.0)
+    assert row['GRBM_GUI_ACTIVE'] == pytest.approx(8 * 200.0 * 2000)
+    R.cmd_counters(argparse.Namespace(dir=str(d), title='t', command=''))
+    out = capsys.readouterr().out
+    assert 'shader clock 0.200 GHz' in out                     # 200 cycles per us on each XCD
+    assert 'L2 hit rate 0.750' in out
+    assert 'L1->L2 read latency 300 cycles per request' in out
+    assert 'bf16 matrix work 5.12e+11 flop = 256.0 TFLOP/s' in out
