@@ -55,7 +55,7 @@ class Workload:
     seed: int
     n_shared: int = 0
     d_ff_shared: int = 0
-    logit_bias: str = ''   # '' | 'first_two_plus2' | 'log_rank'
+    logit_bias: str = ''   # '' | 'first_two_plus2' | 'log_rank' | 'last_minus30'
     select_bias: bool = False
     extreme_frac: float = 0.0
     extreme_scale: float = 0.0
@@ -191,6 +191,10 @@ def router_inputs(w: Workload) -> dict:
         logit_bias[:2] = 2.0
     elif w.logit_bias == 'log_rank':
         logit_bias = (-0.5 * np.log1p(np.arange(w.E, dtype=np.float64))).astype(np.float32)
+    elif w.logit_bias == 'last_minus30':
+        # the last expert is never chosen (an expert without rows)
+        logit_bias = np.zeros(w.E, np.float32)
+        logit_bias[-1] = -30.0
     select_bias = None
     if w.select_bias:
         g = np.random.Generator(np.random.PCG64(r['select_bias']))

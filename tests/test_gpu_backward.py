@@ -138,11 +138,28 @@ BWD_CASES = [
     # the transposed [W_gate; W_up] copy instead of the two k-major matrices
     ('swiglu_width_off_stage', synth.Workload('bh', T=300, d=64, E=4, k=2, d_ff=200, act='swiglu',
                                               score='softmax', renormalize=-1, cf=1.25, dtype='bf16', seed=69), {}),
+    # an expert no token picks: its rows are empty, so the k-major weight
+    # gradients contract over nothing (exact zeros), SwiGLU and GELU
+    ('empty_expert_swiglu', synth.Workload('bi', T=400, d=128, E=8, k=2, d_ff=128, act='swiglu', score='softmax',
+                                           renormalize=-1, cf=1.25, dtype='bf16', seed=67,
+                                           logit_bias='last_minus30'), {}),
+    ('empty_expert_gelu_dropless', synth.Workload('bj', T=400, d=128, E=8, k=2, d_ff=192, act='gelu',
+                                                  score='softmax', renormalize=-1, cf=1.25, dtype='bf16', seed=67,
+                                                  logit_bias='last_minus30'), dict(dropless=True)),
     # more experts than 16-byte column chunks of a row (E > d/8): the input
     # gradient's router term reads dL/dz of every expert from every lane
     ('narrow_rows_many_experts', synth.Workload('bg', T=256, d=64, E=48, k=4, d_ff=64, act='gelu',
                                                 score='softmax', renormalize=-1, cf=1.0, dtype='bf16', seed=68), {}),
 ]
+
+
+def test_backward_gives_an_empty_expert_zero_weight_gradients(moe):
+    name, w, over = [c for c in BWD_CASES if c[0] == 'empty_expert_swiglu'][0]
+    grads, ref, fwd = _run(moe, w, seed=3, **over)
+    assert not (fwd['idx'] == w.E - 1).any()
+    for kk in ('dw_gate', 'dw_in', 'dw_out'):
+        assert not np_of(grads[kk])[w.E - 1].any(), kk          # exactly zero
+    _compare(w, grads, ref)
 
 
 @pytest.mark.parametrize('case', BWD_CASES, ids=[c[0] for c in BWD_CASES])
