@@ -536,7 +536,11 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   // weight blocks of this wave with a column below N (for SwiGLU a gate
   // block and its up block share their columns)
   const int wbv = kGlu ? max(0, min(2, (N - n0 - wn * 64 + 31) / 32)) : max(0, min(4, (N - n0 - wn * 128 + 31) / 32));
-  const bool partial = valid_rows < kBM || n0 + kNOut > N;
+  // the predicated loop instance only for a wave that has blocks without
+  // valid rows or columns: in a partial tile the waves whose blocks are all
+  // valid run the plain loop (its MFMAs on rows past the valid ones would
+  // only add zeros, and its stores stop at the valid rows anyway)
+  const bool partial = xbv < kXB || wbv < (kGlu ? 2 : 4);
   int wrow[4], ncol[4], xrow[kXB];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
