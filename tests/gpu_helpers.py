@@ -14,6 +14,8 @@ Comparison rules (the bar the tests hold the HIP path to):
     move a key)); and on the GPU's logits, against which every output is held
     to the bars above over all tokens.
 """
+import os
+
 import numpy as np
 import torch
 
@@ -21,6 +23,17 @@ import synth
 from oracle import moe as O
 
 DEV = 'cuda'
+
+# The errors the comparisons measured: per test (pytest's id of the running
+# test) and quantity, the worst value seen.  conftest prints them as a table
+# at the end of the session, so a drift towards a bar shows before it fails.
+PARITY = {}
+
+
+def record(quantity, err):
+    test = os.environ.get('PYTEST_CURRENT_TEST', '?').split(' ')[0]
+    row = PARITY.setdefault(test, {})
+    row[quantity] = max(row.get(quantity, 0.0), float(err))
 
 
 def maxrel(a, b):

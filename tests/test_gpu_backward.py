@@ -17,7 +17,7 @@ import synth
 from oracle import backward as B
 from oracle import moe as O
 
-from gpu_helpers import DEV, device_layer, f64_of, maxrel, np_of
+from gpu_helpers import DEV, device_layer, f64_of, maxrel, np_of, record
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,7 @@ def _run(moe, w, seed=0, **over):
 def _check(name, got, ref):
     err = maxrel(got, ref)
     say(f'  {name}: max-rel {err:.2e}')
+    record(name.split('[')[0].split(' (')[0], err)
     assert err <= TOL, (name, err)
 
 

@@ -12,7 +12,7 @@ import torch
 import synth
 from oracle import moe as O
 
-from gpu_helpers import DEV, device_layer, f64_of, forward, logit_error_bound, maxrel, near_tie_tokens, np_of
+from gpu_helpers import DEV, device_layer, f64_of, forward, logit_error_bound, maxrel, near_tie_tokens, np_of, record
 
 pytestmark = pytest.mark.gpu
 
@@ -305,8 +305,10 @@ def test_expert_ffn_parity(moe, case):
                     wts = {kk: synth.as_f32(v[g]) for kk, v in ex.items()}
                     refs[g] = O.expert_ffn(af[src_rows(g, n)], wts, act, dtype)
                 rh, ro = refs[g]
-                assert maxrel(hn[g * R:g * R + n], rh) <= tol
-                assert maxrel(on[g * R:g * R + n], ro) <= tol
+                eh, eo = maxrel(hn[g * R:g * R + n], rh), maxrel(on[g * R:g * R + n], ro)
+                record('H', eh)
+                record('out', eo)
+                assert eh <= tol and eo <= tol, (g, eh, eo)
             assert (hn[g * R + n:(g + 1) * R] == 7.0).all() and (on[g * R + n:(g + 1) * R] == 7.0).all()
     check(hn, on, lambda g, n: slice(g * R, g * R + n))
     # the same FFN with rows gathered from a shuffled token matrix
@@ -433,6 +435,7 @@ def test_combine_parity(moe, dtype, shared, zero):
                     (~dropped).any(1), 'zero' if zero else 'residual')
     ref = O.round_store(ref, dtype)
     yn = f64_of(y)
+    record('y', maxrel(yn, ref))
     assert maxrel(yn, ref) <= (1e-5 if dtype == 'f32' else 2e-2)
     fb = ~(~dropped).any(1)
     if not shared:
@@ -590,15 +593,19 @@ def _compare_forward(moe, w, rows=None, **over):
     if pr != 'score' or dl or not moved.any():
         assert st[2] == want[2]
     l = np_of(out['losses']).astype(np.float64)
+    record('L_aux', maxrel(l[0], ref['l_aux']))
+    record('L_z', maxrel(l[1], ref['l_z']))
     assert abs(l[0] - ref['l_aux']) <= 1e-5 * abs(ref['l_aux'])
     assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z'])
     say(f'  L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}, L_z {l[1]:.6f} vs {ref["l_z"]:.6f}')
     for name in ('gates', 'probs', 'lse'):
         err = maxrel(np_of(out[name]), ref[name])
+        record(name, err)
         assert err <= 1e-5, (name, err)
     y = f64_of(out['y'])[rws]
     tol = 1e-5 if w.dtype == 'f32' else 2e-2
     err = maxrel(y[cmp], ref['y'][cmp])
+    record('y', err)
     say(f'  y max-rel err {err:.3e} over {int(cmp.sum())} of {rws.size} rows')
     assert err <= tol
     fb = ~(~ref['dropped'][rws]).any(1) & cmp
@@ -888,6 +895,7 @@ def _compare_forward_ec(moe, w, rows=None, **over):
     np.testing.assert_array_equal(np_of(out['idx']), ref['idx'])
     for name in ('gates', 'probs', 'lse'):
         err = maxrel(np_of(out[name]), ref[name])
+        record(name, err)
         assert err <= 1e-5, (name, err)
     # the oracle's own picks from its own probabilities of the same logits
     rp = ref['probs']
@@ -904,6 +912,8 @@ def _compare_forward_ec(moe, w, rows=None, **over):
     if not tok_diff.any():
         assert st[2] == ref['stats']['fallback']
     l = np_of(out['losses']).astype(np.float64)
+    record('L_aux', maxrel(l[0], ref['l_aux']))
+    record('L_z', maxrel(l[1], ref['l_z']))
     assert abs(l[0] - ref['l_aux']) <= 1e-5 * abs(ref['l_aux'])
     assert abs(l[1] - ref['l_z']) <= 1e-5 * abs(ref['l_z'])
     rws = ref['rows']
@@ -911,6 +921,7 @@ def _compare_forward_ec(moe, w, rows=None, **over):
     y = f64_of(out['y'])[rws]
     tol = 1e-5 if w.dtype == 'f32' else 2e-2
     err = maxrel(y[cmp], ref['y'][cmp])
+    record('y', err)
     say(f'  y max-rel err {err:.3e} over {int(cmp.sum())} of {rws.size} rows; L_aux {l[0]:.7f} vs {ref["l_aux"]:.7f}')
     assert err <= tol
     none = ~(ref['sel'][rws] >= 0).any(1) & cmp
