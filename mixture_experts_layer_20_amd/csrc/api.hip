@@ -624,11 +624,13 @@ moe_status bgemm(const char* what, const void* A, int64_t lda, int64_t a_gs, con
 // bit 0: A is [K, M] per group, row length lda; bit 1: B is [K, N], row
 // length ldb, or B0 for k < b_split and B1 from there), read through the LDS
 // transpose loads instead of transposed copies.  A K-contiguous operand
-// takes its usual strides (0: K).
+// takes its usual strides (0: K).  With tail_part (k-major B only, device
+// row counts) a sparse last round of tiles is split along k.
 moe_status kgemm(const char* what, int kmaj, const void* A, int64_t lda, int64_t a_gs, const void* B0,
                  const void* B1, int64_t b_split, int64_t ldb, int64_t b_gs, void* Cout, const int32_t* rows,
                  int64_t rpg, int groups, int N, int K, hipStream_t s, const int32_t* kvar = nullptr,
-                 const int32_t* kstart = nullptr, bool packed = false, const int32_t* koff = nullptr) {
+                 const int32_t* kstart = nullptr, bool packed = false, const int32_t* koff = nullptr,
+                 float* tail_part = nullptr) {
   GemmArgs g{};
   g.kmaj = kmaj;
   g.A = A;
@@ -651,6 +653,10 @@ moe_status kgemm(const char* what, int kmaj, const void* A, int64_t lda, int64_t
   g.koff = koff;
   g.packed = packed;
   g.total_rows = packed ? rpg : 0;
+  if (tail_part && rows) {
+    g.tail_part = tail_part;
+    g.tail_parts = 8;
+  }
   return hip_status(launch_gemm(g, MOE_BF16, s), what);
 }
 
@@ -1409,7 +1415,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     }
     // dH = dYe W_out, W_out [E, d, F] read k-major (k = d)
     MOE_TRY(kgemm("expert hidden gradient", 2, b.dYe, 0, 0, wt->w_out, nullptr, 0, F, d * F, b.dH, rows, rpg, E,
-                  static_cast<int>(F), c.d, s, nullptr, nullptr, dl));
+                  static_cast<int>(F), c.d, s, nullptr, nullptr, dl, nullptr, b.tailpart));
     ActBwdArgs ab{};
     ab.dH = b.dH;
     ab.U = c.save_preact ? static_cast<const bf16_t*>(w.pre0) : b.U;
@@ -1426,10 +1432,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
     // are transposed into [E, d, 2F] first)
     if (!glu) {
       MOE_TRY(kgemm("expert input gradient", 2, b.dact, 0, 0, W_in, nullptr, 0, d, F * d, b.dA, rows, rpg, E, c.d,
-                    static_cast<int>(F), s, nullptr, nullptr, dl));
+                    static_cast<int>(F), s, nullptr, nullptr, dl, nullptr, b.tailpart));
     } else if (F % 64 == 0) {
       MOE_TRY(kgemm("expert input gradient", 2, b.dact, 0, 0, wt->w_gate, W_in, F, d, F * d, b.dA, rows, rpg, E,
-                    c.d, static_cast<int>(2 * F), s, nullptr, nullptr, dl));
+                    c.d, static_cast<int>(2 * F), s, nullptr, nullptr, dl, nullptr, b.tailpart));
     } else {
       MOE_TRY(transpose("w_gate transpose", static_cast<const bf16_t*>(wt->w_gate), b.wiT, E, F, d, F, F * d, d,
                         d * 2 * F, 2 * F, nullptr, nullptr, 0, s));

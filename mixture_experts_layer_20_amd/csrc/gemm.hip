@@ -388,7 +388,19 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
   const bf16_t* B0 = static_cast<const bf16_t*>(a.B0) + bg;
   const bf16_t* B1 = kGlu || (kBkm && a.B1) ? static_cast<const bf16_t*>(a.B1) + bg : B0;
   // k-major B stacked along k: stages at or past k row b_split read B1
-  const int b_split = kBkm && a.B1 ? static_cast<int>(a.b_split) : 1 << 30;
+  int b_split = kBkm && a.B1 ? static_cast<int>(a.b_split) : 1 << 30;
+  if (kBkm && k0 > 0) {
+    // a tail part's k range starts k0 rows in (a multiple of the stage, as
+    // b_split is): the matrix holding row k0 starts there, and a stacked B
+    // switches matrix b_split - k0 rows in (or holds B1 only)
+    if (k0 < b_split) {
+      B0 += k0 * ldb;
+      b_split -= static_cast<int>(k0);
+    } else {
+      B1 += (k0 - b_split) * ldb;
+      b_split = 0;
+    }
+  }
 
   const int tid = threadIdx.x;
   // the wave index is uniform: say so, so that descriptors and LDS bases live
@@ -1112,9 +1124,12 @@ __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
 
 hipError_t launch_gemm(const GemmArgs& a_in, int dtype, hipStream_t s) {
   GemmArgs a = a_in;
-  // the tail split applies to bias-only bf16 GEMMs over device row counts
+  // the tail split applies to bf16 GEMMs over device row counts (k-major:
+  // only B, read from the part's first k row on, with every group's k range
+  // the full K)
   const bool tail = dtype == MOE_BF16 && a.act != 3 && a.tail_part != nullptr && a.rows != nullptr &&
-                    !(a.ksplit > 1) && a.tail_parts >= 2 && a.K / kTailMinK >= 2 && !a.kmaj;
+                    !(a.ksplit > 1) && a.tail_parts >= 2 && a.K / kTailMinK >= 2 &&
+                    (a.kmaj == 0 || (a.kmaj == 2 && !a.kvar && !a.kstart));
   // (a K below two minimum parts never splits: no extra blocks, no sum launch)
   if (!tail) a.tail_part = nullptr;
   a.tail_parts = min(a.tail_parts, kMaxTailParts);
