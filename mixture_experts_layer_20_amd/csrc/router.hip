@@ -146,7 +146,7 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
 // holding it, which is the order of the pages' top-k (key descending, ties
 // to the lower index).
 template <int G, int EPL>
-__device__ __forceinline__ void token_epilogue(const RouteArgs& a, const float* z, const float* sbias, int64_t t,
+__device__ __forceinline__ void token_epilogue(const RouteArgs& a, const float* z, const float (&sbias)[EPL], int64_t t,
                                double* pacc, double& lse2acc) {
   const int lane = threadIdx.x & (kWave - 1);
   const int li = lane & (G - 1);                  // lane within the group
@@ -226,7 +226,7 @@ __device__ __forceinline__ void token_epilogue(const RouteArgs& a, const float* 
   for (int r = 0; r < EPL; ++r) {
     const int e = li + r * G;
     float kv = key[r];
-    if (sbias) kv = kv + sbias[r];
+    if (a.select_bias) kv = kv + sbias[r];
     code[r] = e < E ? select_code(kv, e) : 0ull;
   }
   int my_sel = -1;  // lane j < k of the group keeps the j-th choice
@@ -292,16 +292,14 @@ __device__ void workgroup_epilogue(const RouteArgs& a, const float* zbuf, int zs
 #pragma unroll
   for (int r = 0; r < EPL; ++r) pacc[r] = 0.0;
   double lse2 = 0.0;
-  // the selection bias of this lane's experts, read once
+  // the selection bias of this lane's experts, read once (in registers: the
+  // array goes by reference into the inlined per-token code; through a
+  // pointer it lived in scratch memory)
   float sb[EPL];
-  const float* sbias = nullptr;
-  if (a.select_bias) {
 #pragma unroll
-    for (int r = 0; r < EPL; ++r) sb[r] = li + r * G < a.E ? a.select_bias[li + r * G] : 0.0f;
-    sbias = sb;
-  }
+  for (int r = 0; r < EPL; ++r) sb[r] = (a.select_bias && li + r * G < a.E) ? a.select_bias[li + r * G] : 0.0f;
   for (int i = wave * TPW + q; i < nt; i += (kThreads / kWave) * TPW)
-    token_epilogue<G, EPL>(a, zbuf + i * zstride, sbias, t0 + i, pacc, lse2);
+    token_epilogue<G, EPL>(a, zbuf + i * zstride, sb, t0 + i, pacc, lse2);
   if (!a.p_partial) return;
   // groups of a wavefront first (xor over the group-index bits, fixed order),
   // then the four wavefronts in order

@@ -129,7 +129,8 @@ def test_router_logits_within_float32_dot_bound(moe):
 # bf16 tokens with at most 16 experts take the streamed logits kernel: E not
 # a multiple of 4, T not a multiple of 16 or 256, d slices that end inside a
 # 32-wide k step or a 256-wide chunk, one slice of several chunks (T large
-# enough for a single split), and a logit bias
+# enough for a single split), a slice count of 8 with several chunks each, and
+# a logit bias
 LOGIT_CASES = [
     # (T, d, E, logit_bias)
     (4097, 48, 5, ''),
@@ -137,6 +138,8 @@ LOGIT_CASES = [
     (1000, 264, 16, ''),
     (70001, 1032, 6, 'log_rank'),
     (17, 8, 1, ''),
+    (257, 2568, 7, 'log_rank'),
+    (8192, 4096, 12, ''),
 ]
 
 
@@ -160,6 +163,55 @@ def test_streamed_router_logits_within_float32_dot_bound(moe, case):
     bound = logit_error_bound(x, inp['w_router'], inp['logit_bias']) + 2.0 ** -24 * np.abs(zr.astype(np.float64))
     err = np.abs(np_of(logits).astype(np.float64) - zr.astype(np.float64))
     assert (err <= bound).all(), (err / bound).max()
+
+
+# the router from bf16 tokens end to end (logits kernel, then the epilogue on
+# its partial logits): its choices must be the oracle's on the logits it
+# wrote, bit for bit, and its gates, probabilities and log-sum-exp within
+# 1e-5; E from 1 to 16 (the streamed logits kernel) and 20 (the GEMM path),
+# tokens scaled to logits near 1000 and duplicated tokens included
+ROUTE_OWN_CASES = [
+    # (T, d, E, k, score, renorm, select_bias)
+    (1000, 264, 3, 2, 'softmax', -1, False),
+    (4097, 1032, 8, 2, 'softmax', -1, True),
+    (777, 520, 13, 4, 'sigmoid', 1, True),
+    (2049, 2568, 16, 16, 'sigmoid', 0, False),
+    (65, 64, 16, 1, 'softmax', 1, False),
+    (5, 8, 1, 1, 'softmax', -1, False),
+    (3000, 1024, 20, 3, 'sigmoid', 1, True),
+]
+
+
+@pytest.mark.parametrize('case', ROUTE_OWN_CASES, ids=lambda c: f'T{c[0]}d{c[1]}E{c[2]}k{c[3]}{c[4]}{c[5]}')
+def test_router_routes_its_own_logits_like_the_oracle(moe, case):
+    T, d, E, k, score, ren, sb = case
+    say('router on its own logits', case)
+    w = synth.Workload('op', T=T, d=d, E=E, k=k, d_ff=8, act='gelu', score=score, renormalize=ren,
+                       cf=1.0, dtype='bf16', seed=T + d + E, select_bias=sb,
+                       extreme_frac=0.02, extreme_scale=400.0, dup_frac=0.05)
+    inp = synth.router_inputs(w)
+    cfg = moe.config_from_workload(w)
+    logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    gates = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    probs = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    lse = torch.empty(T, dtype=torch.float32, device=DEV)
+    moe.moe_route(cfg, synth.to_torch(inp['x'], DEV), synth.to_torch(inp['w_router'], DEV), None,
+                  synth.to_torch(inp['select_bias'], DEV), logits, probs, idx, gates, lse,
+                  moe.workspace(cfg, DEV))
+    torch.cuda.synchronize()
+    z = np_of(logits)
+    x = synth.as_f32(inp['x'])
+    zr = O.router_logits(x, inp['w_router'])
+    bound = logit_error_bound(x, inp['w_router']) + 2.0 ** -24 * np.abs(zr.astype(np.float64))
+    assert (np.abs(z.astype(np.float64) - zr.astype(np.float64)) <= bound).all()
+    r_idx, r_g, r_p = O.route(z, k, score, ren, inp['select_bias'])
+    np.testing.assert_array_equal(np_of(idx), r_idx)
+    errs = dict(gates=maxrel(np_of(gates), r_g), probs=maxrel(np_of(probs), r_p),
+                lse=maxrel(np_of(lse), O.logsumexp(z)))
+    for q, e in errs.items():
+        record(q, e)
+    assert max(errs.values()) <= 1e-5, errs
 
 
 # ----------------------------------------------------------------------------- capacity / dispatch
