@@ -119,6 +119,24 @@ static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
 }
+// GELU for the bf16 epilogues: v * Phi(v) with the normal tail 0.5 erfc(z),
+// z = |v| / sqrt(2), from Hastings' approximation as tabulated by Abramowitz
+// & Stegun (formula 7.1.26: erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2),
+// t = 1 / (1 + p z), absolute error at most 1.5e-7), evaluated with the
+// hardware reciprocal and exp2: about 4e-7 absolute in the float32 result
+// (far below the bf16 rounding of the stored output) for a third of the
+// instructions of erff; float32 layers keep gelu_erf
+__device__ __forceinline__ float gelu_fast(float v) {
+  const float z = fabsf(v) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float y = fmaf(1.061405429f, t, -1.453152027f);
+  y = fmaf(y, t, 1.421413741f);
+  y = fmaf(y, t, -0.284496736f);
+  y = fmaf(y, t, 0.254829592f);
+  // exp(-z^2) = 2^(-v^2 log2(e) / 2)
+  const float c = 0.5f * (y * t) * __builtin_amdgcn_exp2f(v * v * -0.72134752044448170368f);
+  return v * (v >= 0.0f ? 1.0f - c : c);
+}
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 // SiLU from the hardware exp2 and reciprocal: a few ulps in float32, far
 // below the bf16 rounding of the bf16 path's result
@@ -746,6 +764,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     // would write 8 bytes into each of 32 rows, and the L2 would take many
     // more, smaller write requests.
     const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
+    const bool bias_v8 = (reinterpret_cast<uintptr_t>(bias) & 7) == 0;
     constexpr int kOut = kGlu ? 64 : 128;              // output columns per wave
     constexpr int kPitch = kOut * 2 + 16;              // padded LDS row (bytes)
     constexpr int kLanesPerRow = kOut * 2 / 16;
@@ -768,6 +787,22 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
           for (int q = 0; q < 4; ++q) {
             const int col = ncol[i] - colw + 8 * q + 4 * (lane >> 5);
             const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
+            // the bias of columns n .. n+3 (N is a multiple of 8 and n of
+            // 4, so the four are all below N or all past it): one 8-byte
+            // load when the bias is 8-byte aligned, else four 2-byte loads
+            float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (!kGlu && bias && n < N) {
+              if (bias_v8) {
+                const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
+                bb[0] = __uint_as_float(u.x << 16);
+                bb[1] = __uint_as_float(u.x & 0xFFFF0000u);
+                bb[2] = __uint_as_float(u.y << 16);
+                bb[3] = __uint_as_float(u.y & 0xFFFF0000u);
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bb[r] = bf16_to_f32(bias[n + r]);
+              }
+            }
             f32x2_t v[2];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -776,8 +811,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
                 if (what == 0) x = silu_fast(x) * acc[i + 2][j][4 * q + r];
                 else if (what == 2) x = acc[i + 2][j][4 * q + r];
               } else {
-                if (bias && n + r < N) x += bf16_to_f32(bias[n + r]);
-                if (ACT == 1 && what == 0) x = gelu_erf(x);
+                x += bb[r];
+                if (ACT == 1 && what == 0) x = gelu_fast(x);
               }
               v[r >> 1][r & 1] = x;
             }
@@ -1116,7 +1151,7 @@ __global__ __launch_bounds__(kThreads) void tail_sum_kernel(GemmArgs a) {
     float out[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      out[q] = ACT == 2 ? silu_fast(v[q]) * u[q] : ACT == 1 ? gelu_erf(v[q]) : v[q];
+      out[q] = ACT == 2 ? silu_fast(v[q]) * u[q] : ACT == 1 ? gelu_fast(v[q]) : v[q];
     *reinterpret_cast<uint4*>(static_cast<bf16_t*>(a.C) + o) = pack(out);
   }
 }
