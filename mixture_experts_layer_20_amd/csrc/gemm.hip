@@ -862,10 +862,12 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kNW - 2) * kLoadsPerWave));
   };
   // prologue: stages 0 .. nring-2 whole and position 0 of stage nring-1;
-  // then stage 0 must have landed
+  // then stage 0 must have landed: each wave waits for its own stage-0 loads
+  // only (loads complete in order; the later stages stay in flight)
   for (int st = 0; st < nring - 1; ++st) issue_share(st, 0, kLoadsPerWave);
   issue_share(nring - 1, 0, pos_begin(1));
-  __builtin_amdgcn_s_waitcnt(0);
+  if (stage_x) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kNX - 2) * kLoadsPerWave + pos_begin(1)));
+  else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((kNW - 2) * kLoadsPerWave + pos_begin(1)));
   __builtin_amdgcn_s_barrier();
   {
     const int c0 = lane >> 5;
