@@ -426,7 +426,10 @@ __global__ __launch_bounds__(kThreads) void act_bwd_kernel(ActBwdArgs a) {
         for (int h = 0; h < 2; ++h) {
           const float d = __uint_as_float(h ? dh[q] & 0xFFFF0000u : dh[q] << 16);
           const float u = __uint_as_float(h ? uu[q] & 0xFFFF0000u : uu[q] << 16);
-          const float grad = 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * __expf(-0.5f * u * u) * 0.39894228040143268f;
+          // Phi(u) + u phi(u), both from normal_tail's approximation
+          float e;
+          const float c = normal_tail(u, e);
+          const float grad = (u >= 0.0f ? 1.0f - c : c) + u * e * 0.39894228040143268f;
           w |= static_cast<uint32_t>(f32_to_bf16(d * grad)) << (16 * h);
         }
         o0[q] = w;

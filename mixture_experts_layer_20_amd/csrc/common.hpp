@@ -36,6 +36,24 @@ __device__ __forceinline__ void split3(float v, bf16_t& hi, bf16_t& mid, bf16_t&
   lo = f32_to_bf16(r1 - bf16_to_f32(mid));
 }
 
+// The standard normal tail Q(|v|) = 0.5 erfc(|v| / sqrt(2)) for the bf16
+// GELU paths, from Hastings' approximation as tabulated by Abramowitz &
+// Stegun (formula 7.1.26: erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2),
+// t = 1 / (1 + p z), absolute error at most 1.5e-7), evaluated with the
+// hardware reciprocal and exp2; also returns e = exp(-v^2 / 2), so that
+// Phi(v) = v >= 0 ? 1 - Q : Q and phi(v) = e / sqrt(2 pi).
+__device__ __forceinline__ float normal_tail(float v, float& e) {
+  const float z = fabsf(v) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float y = fmaf(1.061405429f, t, -1.453152027f);
+  y = fmaf(y, t, 1.421413741f);
+  y = fmaf(y, t, -0.284496736f);
+  y = fmaf(y, t, 0.254829592f);
+  // exp(-v^2 / 2) = 2^(-v^2 log2(e) / 2)
+  e = __builtin_amdgcn_exp2f(v * v * -0.72134752044448170368f);
+  return 0.5f * (y * t) * e;
+}
+
 template <typename T> struct Storage;
 template <> struct Storage<float> {
   __device__ static __forceinline__ float load(const float* p, int64_t i) { return p[i]; }

@@ -119,22 +119,13 @@ static_assert(kLdsBytes <= 160 * 1024, "gfx950 LDS");
 __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
 }
-// GELU for the bf16 epilogues: v * Phi(v) with the normal tail 0.5 erfc(z),
-// z = |v| / sqrt(2), from Hastings' approximation as tabulated by Abramowitz
-// & Stegun (formula 7.1.26: erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2),
-// t = 1 / (1 + p z), absolute error at most 1.5e-7), evaluated with the
-// hardware reciprocal and exp2: about 4e-7 absolute in the float32 result
-// (far below the bf16 rounding of the stored output) for a third of the
+// GELU for the bf16 epilogues: v * Phi(v) with the normal tail of
+// normal_tail (common.hpp): about 4e-7 absolute in the float32 result (far
+// below the bf16 rounding of the stored output) for a third of the
 // instructions of erff; float32 layers keep gelu_erf
 __device__ __forceinline__ float gelu_fast(float v) {
-  const float z = fabsf(v) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float y = fmaf(1.061405429f, t, -1.453152027f);
-  y = fmaf(y, t, 1.421413741f);
-  y = fmaf(y, t, -0.284496736f);
-  y = fmaf(y, t, 0.254829592f);
-  // exp(-z^2) = 2^(-v^2 log2(e) / 2)
-  const float c = 0.5f * (y * t) * __builtin_amdgcn_exp2f(v * v * -0.72134752044448170368f);
+  float e;
+  const float c = normal_tail(v, e);
   return v * (v >= 0.0f ? 1.0f - c : c);
 }
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
