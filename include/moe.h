@@ -34,7 +34,8 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked [host]. Tensors are dense,
- *     row-major, and at least 16-byte aligned.
+ *     row-major, and at least 16-byte aligned (expert biases included: the
+ *     expert GEMMs read them 8 bytes at a time; validation refuses others).
  *   - Storage type of x, expert weights, expert biases and y: MOE_F32 or
  *     MOE_BF16 (raw bf16 bits). The router weight, biases of the router,
  *     logits, probabilities, gates and losses are always float32.

@@ -922,8 +922,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t act, int32_t groups, in
   MOE_TRY(check_ptr(rows, "rows", 4, false));
   MOE_TRY(check_ptr(gather, "gather", 4, false));
   if (gather && a_rows <= 0) return fail(MOE_EINVAL, "a_rows must be > 0 when gathering");
-  MOE_TRY(check_ptr(b_in, "b_in", dsize(c), false));
-  MOE_TRY(check_ptr(b_out, "b_out", dsize(c), false));
+  MOE_TRY(check_ptr(b_in, "b_in", 16, false));
+  MOE_TRY(check_ptr(b_out, "b_out", 16, false));
   if (act == MOE_SWIGLU) {
     MOE_TRY(check_ptr(w_gate, "w_gate", 16));
     if (b_in) return fail(MOE_EUNSUPPORTED, "SwiGLU experts take no b_in");
@@ -951,8 +951,8 @@ moe_status moe_expert_ffn_packed(const moe_config* cfg, int32_t act, int32_t gro
   MOE_TRY(check_ptr(out, "out", 16));
   MOE_TRY(check_ptr(gather, "gather", 4, false));
   if (gather && a_rows <= 0) return fail(MOE_EINVAL, "a_rows must be > 0 when gathering");
-  MOE_TRY(check_ptr(b_in, "b_in", dsize(c), false));
-  MOE_TRY(check_ptr(b_out, "b_out", dsize(c), false));
+  MOE_TRY(check_ptr(b_in, "b_in", 16, false));
+  MOE_TRY(check_ptr(b_out, "b_out", 16, false));
   if (act == MOE_SWIGLU) {
     MOE_TRY(check_ptr(w_gate, "w_gate", 16));
     if (b_in) return fail(MOE_EUNSUPPORTED, "SwiGLU experts take no b_in");
@@ -1139,8 +1139,8 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, con
   MOE_TRY(check_ptr(wt->select_bias, "select_bias", 4, false));
   MOE_TRY(check_ptr(wt->w_in, "w_in", 16));
   MOE_TRY(check_ptr(wt->w_out, "w_out", 16));
-  MOE_TRY(check_ptr(wt->b_in, "b_in", dsize(c), false));
-  MOE_TRY(check_ptr(wt->b_out, "b_out", dsize(c), false));
+  MOE_TRY(check_ptr(wt->b_in, "b_in", 16, false));
+  MOE_TRY(check_ptr(wt->b_out, "b_out", 16, false));
   if (c.act == MOE_SWIGLU) {
     MOE_TRY(check_ptr(wt->w_gate, "w_gate", 16));
     if (wt->b_in) return fail(MOE_EUNSUPPORTED, "SwiGLU experts take no b_in");
@@ -1148,8 +1148,8 @@ static moe_status forward_impl(const moe_config* cfg, const moe_weights* wt, con
   if (c.n_shared > 0) {
     MOE_TRY(check_ptr(wt->ws_in, "ws_in", 16));
     MOE_TRY(check_ptr(wt->ws_out, "ws_out", 16));
-    MOE_TRY(check_ptr(wt->bs_in, "bs_in", dsize(c), false));
-    MOE_TRY(check_ptr(wt->bs_out, "bs_out", dsize(c), false));
+    MOE_TRY(check_ptr(wt->bs_in, "bs_in", 16, false));
+    MOE_TRY(check_ptr(wt->bs_out, "bs_out", 16, false));
   }
   const bool ec = c.routing == MOE_EXPERT_CHOICE;
   MOE_TRY(check_ptr(out->y, "y", 16, needT));
@@ -1284,12 +1284,12 @@ moe_status moe_backward(const moe_config* cfg, const moe_weights* wt, const void
   MOE_TRY(check_ptr(wt->w_router, "w_router", 4));
   MOE_TRY(check_ptr(wt->w_in, "w_in", 16));
   MOE_TRY(check_ptr(wt->w_out, "w_out", 16));
-  MOE_TRY(check_ptr(wt->b_in, "b_in", 2, false));
+  MOE_TRY(check_ptr(wt->b_in, "b_in", 16, false));
   if (glu) MOE_TRY(check_ptr(wt->w_gate, "w_gate", 16));
   if (Fs > 0) {
     MOE_TRY(check_ptr(wt->ws_in, "ws_in", 16));
     MOE_TRY(check_ptr(wt->ws_out, "ws_out", 16));
-    MOE_TRY(check_ptr(wt->bs_in, "bs_in", 2, false));
+    MOE_TRY(check_ptr(wt->bs_in, "bs_in", 16, false));
   }
   const bool ec = c.routing == MOE_EXPERT_CHOICE;
   MOE_TRY(check_ptr(fwd->idx, "fwd idx", 4, needT && !ec));

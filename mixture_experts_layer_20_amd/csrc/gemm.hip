@@ -755,7 +755,6 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
     // would write 8 bytes into each of 32 rows, and the L2 would take many
     // more, smaller write requests.
     const bf16_t* bias = a.bias ? static_cast<const bf16_t*>(a.bias) + static_cast<int64_t>(tc.g) * N : nullptr;
-    const bool bias_v8 = (reinterpret_cast<uintptr_t>(bias) & 7) == 0;
     constexpr int kOut = kGlu ? 64 : 128;              // output columns per wave
     constexpr int kPitch = kOut * 2 + 16;              // padded LDS row (bytes)
     constexpr int kLanesPerRow = kOut * 2 / 16;
@@ -778,21 +777,16 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& a) {
           for (int q = 0; q < 4; ++q) {
             const int col = ncol[i] - colw + 8 * q + 4 * (lane >> 5);
             const int n = n0 + ncol[i] + 8 * q + 4 * (lane >> 5);
-            // the bias of columns n .. n+3 (N is a multiple of 8 and n of
-            // 4, so the four are all below N or all past it): one 8-byte
-            // load when the bias is 8-byte aligned, else four 2-byte loads
+            // the bias of columns n .. n+3 in one 8-byte load (N is a
+            // multiple of 8 and n of 4, so the four are all below N or all
+            // past it; the entry points require 16-byte aligned biases)
             float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (!kGlu && bias && n < N) {
-              if (bias_v8) {
-                const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
-                bb[0] = __uint_as_float(u.x << 16);
-                bb[1] = __uint_as_float(u.x & 0xFFFF0000u);
-                bb[2] = __uint_as_float(u.y << 16);
-                bb[3] = __uint_as_float(u.y & 0xFFFF0000u);
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) bb[r] = bf16_to_f32(bias[n + r]);
-              }
+              const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
+              bb[0] = __uint_as_float(u.x << 16);
+              bb[1] = __uint_as_float(u.x & 0xFFFF0000u);
+              bb[2] = __uint_as_float(u.y << 16);
+              bb[3] = __uint_as_float(u.y & 0xFFFF0000u);
             }
             f32x2_t v[2];
 #pragma unroll

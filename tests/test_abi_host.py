@@ -166,6 +166,12 @@ def test_null_and_misaligned_pointers_rejected_before_launch(moe):
     st = lib.moe_expert_ffn(ctypes.byref(c), 1, 4, 40, None, 16, 16, 0, 16, None, None, 16, None, 64,
                             16, 16, None)
     assert st == moe.MOE_EINVAL and b'a_rows' in lib.moe_last_error()
+    # biases, like every tensor, must be 16-byte aligned (the GEMM epilogue
+    # reads four bf16 bias values per 8-byte load)
+    for b_in, b_out, name in ((18, None, b'b_in'), (None, 24, b'b_out')):
+        st = lib.moe_expert_ffn(ctypes.byref(c), 1, 4, 40, None, 16, None, 0, 16, None, b_in, 16, b_out,
+                                64, 16, 16, None)
+        assert st == moe.MOE_EINVAL and name + b' must be 16-byte aligned' in lib.moe_last_error()
 
 
 def test_workspace_grows_with_capacity(moe):
