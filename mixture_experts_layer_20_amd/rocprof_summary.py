@@ -34,7 +34,8 @@ import sqlite3
 HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCE = os.path.join(HERE, 'csrc', 'gemm.hip')
 COPY_KERNEL_TAG = 'neg_kernel'      # torch's elementwise negation, used as the plain copy
-GEMM_UP = r'gemm_bf16_w\d<2>'       # kernel-name patterns of the two expert GEMMs
+GEMM_UP_ANY = r'gemm_bf16_w\d<[12]>'   # kernel-name patterns of the two expert GEMMs: gate/up
+                                      # (GELU or SwiGLU) and down
 GEMM_DOWN = r'gemm_bf16_w\d<0>'
 XCDS = 8                            # GRBM_GUI_ACTIVE is summed over the XCDs
 
@@ -82,7 +83,6 @@ def pmc_per_kernel(d, counter):
     return {kn: (len(v), sum(v.values()) / len(v)) for kn, v in per.items()}
 
 
-GEMM_UP_ANY = r'gemm_bf16_w\d<[12]>'    # gate/up launch, GELU or SwiGLU
 STEP_KERNELS = ((GEMM_UP_ANY, 'expert GEMM gate/up'),
                 (GEMM_DOWN, 'expert GEMM down'),
                 (r'tail_sum_kernel<[12]>', 'tail sum of the gate/up GEMM'),
@@ -264,14 +264,17 @@ def cmd_traffic(a):
     copy_f, copy_w = pick(fetch, COPY_KERNEL_TAG)[1], pick(write, COPY_KERNEL_TAG)[1]
     kib = a.copy_bytes / 1024.0
     f_fetch, f_write = kib / copy_f, kib / copy_w
-    # the expert GEMM kernels (either workgroup size): SwiGLU up/gate, then down
-    g2f, g2w = pick(fetch, GEMM_UP)[1], pick(write, GEMM_UP)[1]
+    # the expert GEMM kernels: the up (or gate/up) launch, GELU or SwiGLU,
+    # then down
+    g2f, g2w = pick(fetch, GEMM_UP_ANY)[1], pick(write, GEMM_UP_ANY)[1]
     g0f, g0w = pick(fetch, GEMM_DOWN)[1], pick(write, GEMM_DOWN)[1]
-    # the ordered sum of split last rounds belongs to the launch it finishes;
-    # per pair it runs as often as the GEMMs (dispatch-weighted mean)
+    # the ordered sums of split last rounds and of a k-split down launch
+    # belong to the launch they finish; per pair they run as often as the
+    # GEMMs (dispatch-weighted mean)
     n_pair = pick(fetch, GEMM_DOWN)[0]
-    tf = sum(n * v for kn, (n, v) in fetch.items() if re.search(r'tail_sum_kernel', kn)) / max(1, n_pair)
-    tw = sum(n * v for kn, (n, v) in write.items() if re.search(r'tail_sum_kernel', kn)) / max(1, n_pair)
+    sums = r'tail_sum_kernel|ksum_kernel'
+    tf = sum(n * v for kn, (n, v) in fetch.items() if re.search(sums, kn)) / max(1, n_pair)
+    tw = sum(n * v for kn, (n, v) in write.items() if re.search(sums, kn)) / max(1, n_pair)
     g0f, g0w = g0f + tf, g0w + tw
     print(f'HBM traffic of the expert grouped GEMM, {a.workload} workload (rocprofv3 --pmc)')
     if a.command_fetch:

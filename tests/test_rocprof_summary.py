@@ -68,6 +68,24 @@ def test_traffic_calibration_and_hash_gate(tmp_path):
     assert R.read_traffic(str(tmp_path / 'missing.txt'), 'wl') is None
 
 
+def test_traffic_of_a_gelu_layer_counts_its_k_split_sum(tmp_path):
+    """A GELU layer's up launch is gemm_bf16_w8<1>; the k-split down launch's
+    ordered sum (ksum_kernel) is part of the down launch's traffic."""
+    g1 = 'void moe::(anonymous namespace)::gemm_bf16_w8<1>(moe::GemmArgs)'
+    g0 = 'void moe::(anonymous namespace)::gemm_bf16_w8<0>(moe::GemmArgs)'
+    ks = 'moe::(anonymous namespace)::ksum_kernel(moe::GemmArgs)'
+    kib = (1 << 30) / 1024
+    make_db(str(tmp_path / 'f'), 'FETCH_SIZE', [(1, COPY, kib), (2, g1, 700.0), (3, g0, 600.0), (4, ks, 90.0)])
+    make_db(str(tmp_path / 'w'), 'WRITE_SIZE', [(1, COPY, kib), (2, g1, 30.0), (3, g0, 80.0), (4, ks, 20.0)])
+    out = subprocess.run([sys.executable, '-m', 'mixture_experts_layer_20_amd.rocprof_summary', 'traffic',
+                          str(tmp_path / 'f'), str(tmp_path / 'w'), '--workload', 'wl',
+                          '--copy-bytes', str(1 << 30)], cwd=ROOT, capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    rec = json.loads([ln for ln in out.stdout.splitlines() if ln.startswith('json: ')][0][6:])
+    assert rec['fetch_bytes_per_pair'] == pytest.approx((700.0 + 600.0 + 90.0) * 1024)
+    assert rec['write_bytes_per_pair'] == pytest.approx((30.0 + 80.0 + 20.0) * 1024)
+
+
 def test_code_hash_ignores_comments_not_code(tmp_path):
     a = tmp_path / 'a.hip'
     a.write_text('// header\nint f(int x) {  /* note */ return x + 1; }  // tail\n')
