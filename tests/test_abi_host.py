@@ -181,6 +181,23 @@ def test_workspace_grows_with_capacity(moe):
     assert a % 256 == 0
 
 
+def test_mixtral_workspace_is_its_expert_buffers_plus_a_few_mib(moe):
+    """The forward workspace of the Mixtral-shaped layer: H [E*C, d_ff] and
+    Ye [E*C, d] in bf16 (C = 2,560), the 64 MiB of float32 partial tiles of
+    the tail split, and routing scratch of under 3 MiB; no dispatched copy
+    of x."""
+    import synth
+    w = synth.WORKLOADS['mixtral_8x_top2']
+    cfg = moe.config_from_workload(w)
+    C = moe.moe_validate(cfg)
+    assert C == 2560
+    rows = w.E * C
+    big = 2 * rows * w.d_ff + 2 * rows * w.d + (64 << 20)
+    got = moe.moe_workspace_bytes(cfg)
+    assert big <= got < big + (3 << 20)
+    assert abs(got / 2**20 - 786.6) < 0.05
+
+
 def test_dropless_capacity_and_workspace(moe):
     # dropless: C = T (a token picks an expert at most once), whatever the factor
     assert moe.moe_validate(cfg(moe, dropless=True)) == 64
