@@ -16,7 +16,7 @@ sys.path.insert(0, ROOT)
 from mixture_experts_layer_20_amd import rocprof_summary as R  # noqa: E402
 
 G2 = 'void moe::(anonymous namespace)::gemm_bf16_w8<2>(moe::GemmArgs)'
-G0 = 'void moe::(anonymous namespace)::gemm_bf16_w4<0>(moe::GemmArgs)'
+G0 = 'void moe::(anonymous namespace)::gemm_bf16_w8<0>(moe::GemmArgs)'
 COPY = 'void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>'
 
 
