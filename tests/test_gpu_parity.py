@@ -179,6 +179,7 @@ ROUTE_OWN_CASES = [
     (65, 64, 16, 1, 'softmax', 1, False),
     (5, 8, 1, 1, 'softmax', -1, False),
     (3000, 1024, 20, 3, 'sigmoid', 1, True),
+    (600, 264, 256, 32, 'sigmoid', 1, True),      # the expert and choice limits
 ]
 
 
@@ -754,6 +755,28 @@ def test_forward_k_equals_E_bf16_swiglu(moe):
                        renormalize=-1, cf=1.0, dtype='bf16', seed=31)
     cfg, out, ref = _compare_forward(moe, w)
     assert not ref['dropped'].any()
+
+
+LIMIT_FORWARDS = [
+    # (score, renormalize, select_bias, dropless)
+    ('softmax', -1, False, False),
+    ('sigmoid', 1, True, True),
+]
+
+
+@pytest.mark.parametrize('case', LIMIT_FORWARDS, ids=lambda c: f'{c[0]}{"_dropless" if c[3] else ""}')
+def test_forward_at_the_expert_and_choice_limits(moe, case):
+    """E = 256 experts and k = 32 choices, the largest the configuration
+    admits: the router's GEMM path over 1,024 plane rows, 32 ranks of
+    capacity, 256 expert groups (the packed mode's limit when dropless) and a
+    32-way combine."""
+    score, renorm, sb, dl = case
+    w = synth.Workload('limits', T=300, d=64, E=256, k=32, d_ff=64, act='gelu', score=score,
+                       renormalize=renorm, cf=1.25, dtype='bf16', seed=41, select_bias=sb)
+    cfg, out, ref = _compare_forward(moe, w, dropless=dl)
+    if dl:
+        assert not ref['dropped'].any()
+    assert int(np_of(out['counts']).sum()) == w.T * w.k
 
 
 DROPLESS_FORWARDS = [
