@@ -151,6 +151,15 @@ BWD_CASES = [
     # gradient's router term reads dL/dz of every expert from every lane
     ('narrow_rows_many_experts', synth.Workload('bg', T=256, d=64, E=48, k=4, d_ff=64, act='gelu',
                                                 score='softmax', renormalize=-1, cf=1.0, dtype='bf16', seed=68), {}),
+    # the configuration's limits: 256 experts (four per lane in the router
+    # backward, 256 expert groups in the GEMMs) and 32 choices per token;
+    # seeds whose 32nd and 33rd keys are at least 3e-5 apart, so that both
+    # sides route alike
+    ('limits_E256_k32', synth.Workload('bl', T=300, d=64, E=256, k=32, d_ff=64, act='gelu', score='softmax',
+                                       renormalize=-1, cf=1.25, dtype='bf16', seed=49), {}),
+    ('limits_E256_k32_sigmoid_dropless', synth.Workload('bm', T=300, d=64, E=256, k=32, d_ff=64, act='gelu',
+                                                        score='sigmoid', renormalize=1, cf=1.25, dtype='bf16',
+                                                        seed=41, select_bias=True), dict(dropless=True)),
 ]
 
 
